@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs shared by the HIP path's tests/bench and the oracle.
+
+This module only *makes bytes*: normal draws, rounding to binary16, and
+packing draws into the 32-value q8_0 / q4_0 block formats that the cache is
+stored in.  It holds none of the attention arithmetic and no dequantiser; the
+oracle and the HIP library each read the bytes with their own code.
+
+Cache layout (both sides read it through explicit byte strides): one tensor
+per K and per V, position-major ``[n_keys][n_kv_heads][row]`` where a row is
+the ``head_dim`` values of one (position, KV head) in the storage type.
+
+Block formats ("F5 M6 -- PolyKV", S0 and the tier-family table): a block is
+32 consecutive values along head_dim; q8_0 = binary16 scale + 32 signed bytes
+(34 B); q4_0 = binary16 scale + 16 bytes of 4-bit codes (18 B), element i < 16
+in the low nibble of byte i and element i >= 16 in the high nibble of byte
+i - 16.  The quantiser rule used to *generate* blocks from normal draws is not
+given by the pages; the one here (amax/127 for q8_0, signed-max/-8 for q4_0,
+scale stored round-to-nearest-even) only shapes the test data.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+F32, F16, Q8_0, Q4_0 = 0, 1, 2, 3
+TYPE_NAMES = {F32: "f32", F16: "f16", Q8_0: "q8_0", Q4_0: "q4_0"}
+TYPE_BY_NAME = {v: k for k, v in TYPE_NAMES.items()}
+
+
+def row_bytes(dtype: int, head_dim: int) -> int:
+    """Bytes of one (position, KV head) row of ``head_dim`` values."""
+    if dtype == F32:
+        return 4 * head_dim
+    if dtype == F16:
+        return 2 * head_dim
+    if head_dim % 32:
+        raise ValueError("block types need head_dim % 32 == 0")
+    if dtype == Q8_0:
+        return head_dim // 32 * 34
+    if dtype == Q4_0:
+        return head_dim // 32 * 18
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+def stream_seed(base: int, tensor_id: int, layer: int = 0) -> int:
+    """Independent seed per (configuration, tensor, layer)."""
+    x = (base * 0x9E3779B1 + tensor_id * 0x85EBCA77 + layer * 0xC2B2AE3D + 0x27D4EB2F) & 0x7FFFFFFFFFFFFFFF
+    x ^= x >> 29
+    x = (x * 0xBF58476D1CE4E5B9) & 0x7FFFFFFFFFFFFFFF
+    x ^= x >> 32
+    return x
+
+
+def generator(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def normal(shape, seed: int, device="cpu") -> torch.Tensor:
+    """i.i.d. N(0,1) float32 draws."""
+    return torch.randn(*shape, generator=generator(seed, device), device=device, dtype=torch.float32)
+
+
+def _round_half_away(x: torch.Tensor) -> torch.Tensor:
+    return torch.sign(x) * torch.floor(x.abs() + 0.5)
+
+
+def pack_q8_0(x: torch.Tensor) -> torch.Tensor:
+    """Pack float32 draws [..., D] into q8_0 blocks -> uint8 [..., D/32*34]."""
+    *lead, d = x.shape
+    xb = x.reshape(-1, 32).to(torch.float32)
+    amax = xb.abs().amax(dim=1)
+    scale = amax / 127.0
+    inv = torch.where(scale > 0, 1.0 / torch.where(scale > 0, scale, torch.ones_like(scale)), torch.zeros_like(scale))
+    q = _round_half_away(xb * inv[:, None]).clamp_(-127, 127).to(torch.int8)
+    out = torch.empty(xb.shape[0], 34, dtype=torch.uint8, device=x.device)
+    out[:, 0:2] = scale.to(torch.float16).view(torch.uint8).reshape(-1, 2)
+    out[:, 2:] = q.view(torch.uint8)
+    return out.reshape(*lead, d // 32 * 34)
+
+
+def pack_q4_0(x: torch.Tensor) -> torch.Tensor:
+    """Pack float32 draws [..., D] into q4_0 blocks -> uint8 [..., D/32*18]."""
+    *lead, d = x.shape
+    xb = x.reshape(-1, 32).to(torch.float32)
+    idx = xb.abs().argmax(dim=1, keepdim=True)
+    m = torch.gather(xb, 1, idx).squeeze(1)
+    scale = m / -8.0
+    inv = torch.where(scale != 0, 1.0 / torch.where(scale != 0, scale, torch.ones_like(scale)), torch.zeros_like(scale))
+    n = torch.clamp(torch.trunc(xb * inv[:, None] + 8.5), 0, 15).to(torch.uint8)
+    out = torch.empty(xb.shape[0], 18, dtype=torch.uint8, device=x.device)
+    out[:, 0:2] = scale.to(torch.float16).view(torch.uint8).reshape(-1, 2)
+    out[:, 2:] = n[:, :16] | (n[:, 16:] << 4)
+    return out.reshape(*lead, d // 32 * 18)
+
+
+def encode(x: torch.Tensor, dtype: int) -> torch.Tensor:
+    """Store float32 draws [..., D] in ``dtype``; returns the storage tensor
+    ([..., D] float32 / float16, or [..., row_bytes] uint8 for block types)."""
+    if dtype == F32:
+        return x.to(torch.float32).contiguous()
+    if dtype == F16:
+        return x.to(torch.float16).contiguous()
+    if dtype == Q8_0:
+        return pack_q8_0(x)
+    if dtype == Q4_0:
+        return pack_q4_0(x)
+    raise ValueError(dtype)
+
+
+@dataclass
+class Cache:
+    """One K or V tensor, position-major [n_keys][n_kv_heads][row]."""
+
+    data: torch.Tensor
+    dtype: int
+    n_keys: int
+    n_kv_heads: int
+    head_dim: int
+
+    @property
+    def row_bytes(self) -> int:
+        return row_bytes(self.dtype, self.head_dim)
+
+    @property
+    def head_stride(self) -> int:
+        return self.row_bytes
+
+    @property
+    def pos_stride(self) -> int:
+        return self.n_kv_heads * self.row_bytes
+
+    def to(self, device) -> "Cache":
+        return Cache(self.data.to(device), self.dtype, self.n_keys, self.n_kv_heads, self.head_dim)
+
+    def ptr(self, pos: int = 0) -> int:
+        return self.data.data_ptr() + pos * self.pos_stride
+
+
+def make_cache(n_keys: int, n_kv_heads: int, head_dim: int, dtype: int, seed: int, device="cpu",
+               outlier_channels: int = 0, outlier_gain: float = 8.0, chunk_keys: int = 1 << 16,
+               channels_seed: int | None = None, pinned: bool = False) -> Cache:
+    """A cache tensor of N(0,1) draws stored in ``dtype``.
+
+    ``outlier_channels`` (kv_head, d) channels, chosen without replacement from
+    ``channels_seed`` (default ``seed``), are multiplied by ``outlier_gain``
+    after rounding to the storage type (exact for a power of two gain on
+    binary16 data).  Draws are made in key chunks to bound peak memory; the
+    chunk size is part of the recipe (the same seed and chunk give the same
+    bytes on the same device type).  ``pinned`` places the result in pinned
+    host memory (device must be "cpu").
+    """
+    rb = row_bytes(dtype, head_dim)
+    shape_tail = (n_kv_heads, head_dim) if dtype in (F32, F16) else (n_kv_heads, rb)
+    tdtype = {F32: torch.float32, F16: torch.float16}.get(dtype, torch.uint8)
+    out = torch.empty((n_keys,) + shape_tail, dtype=tdtype, device=device, pin_memory=pinned)
+    g = generator(seed, device)
+    for c0 in range(0, n_keys, chunk_keys):
+        c1 = min(n_keys, c0 + chunk_keys)
+        x = torch.randn(c1 - c0, n_kv_heads, head_dim, generator=g, device=device, dtype=torch.float32)
+        out[c0:c1] = encode(x, dtype)
+        del x
+    if outlier_channels:
+        if dtype not in (F32, F16):
+            raise ValueError("outlier channels are defined for float storage only")
+        gc = generator(seed if channels_seed is None else channels_seed, "cpu")
+        sel = torch.randperm(n_kv_heads * head_dim, generator=gc)[:outlier_channels]
+        hh, dd = (sel // head_dim).tolist(), (sel % head_dim).tolist()
+        for h, d in zip(hh, dd):
+            out[:, h, d] *= outlier_gain
+    return Cache(out, dtype, n_keys, n_kv_heads, head_dim)
+
+
+def make_query(n_seq: int, n_q_heads: int, head_dim: int, seed: int, device="cpu") -> torch.Tensor:
+    """Query [n_seq][n_q_heads][head_dim] float32 N(0,1)."""
+    return normal((n_seq, n_q_heads, head_dim), seed, device)

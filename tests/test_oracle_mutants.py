@@ -1,0 +1,60 @@
+"""Each plausible mistake planted in a copy of oracle.c fails some pin.
+
+The mutants are built on the CPU from a temporary copy of the source; the
+real oracle is never modified.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {
+    "f16_subnormal_scale": ("ldexp((double)m, -24)", "ldexp((double)m, -25)"),
+    "f16_exponent_bias": ("e - 25", "e - 24"),
+    "q8_unsigned": ("int8_t q = (int8_t)blk[2 + i];", "int q = blk[2 + i];"),
+    "q4_offset": ("(double)(n - 8)", "(double)(n - 7)"),
+    "q4_nibble_order": ("(i < 16) ? (byte & 0x0f) : (byte >> 4)", "(i < 16) ? (byte >> 4) : (byte & 0x0f)"),
+    "q4_byte_index": ("blk[2 + (i & 15)]", "blk[2 + (i >> 1)]"),
+    "q8_block_stride": ("row + 34 * (i / 32)", "row + 32 * (i / 32)"),
+    "scale_dropped": ("s[t] = scale * dot;", "s[t] = dot;"),
+    "softcap_outer_factor": ("softcap * tanh(s[t] / softcap)", "tanh(s[t] / softcap)"),
+    "lse_log2": ("lse[r] = mx + log(z);", "lse[r] = mx + log2(z);"),
+    "no_normalise": ("for (d = 0; d < head_dim; ++d) acc[d] /= z;", ""),
+    "head_map_modulo": ("q_to_kv[h] : h / (n_q_heads / n_kv_heads)", "q_to_kv[h] : h % n_kv_heads"),
+    "pos_head_stride_swap": ("kb + j * w->k_pos_stride", "kb + j * w->k_head_stride"),
+    "v_read_as_k_type": ("dequant_row(w->v_type", "dequant_row(w->k_type"),
+    "combine_weight_sign": ("exp(lse_parts[t][r] - mx)", "exp(mx - lse_parts[t][r])"),
+    "combine_no_normalise": ("for (d = 0; d < head_dim; ++d) o_out[r * head_dim + d] /= z;", ""),
+    "seq_stride_ignored": ("(int64_t)b * w->k_seq_stride", "(int64_t)0 * w->k_seq_stride"),
+    "dot_index_shift": ("qd[d] * kv[d]", "qd[d] * kv[(d + 1) % head_dim]"),
+    "combine_lse_drops_max": ("lse_out[r] = mx + log(z);", "lse_out[r] = log(z);"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("mutants")
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, mutant_dir):
+    old, new = MUTANTS[name]
+    src = open(oracle.SRC_PATH).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    path = os.path.join(mutant_dir, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    so = os.path.join(mutant_dir, f"lib{name}.so")
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", so, path, "-lm"])
+    mut = oracle.Oracle(so)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mut)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+            break
+    assert caught, f"mutant {name} passed every pin"
