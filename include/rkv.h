@@ -1,0 +1,234 @@
+/*
+ * rkv.h -- C ABI of the position-split decode-attention library (librkv.so).
+ *
+ * The method ("F5 M7 -- Rolling KV: position-windowed KV residency", header
+ * note): one layer's KV cache is divided by KEY POSITION into a
+ * device-resident window [0, wc) and a tail [wc, n_kv).  Each part is
+ * attended on its own with flash attention that also emits the per-head
+ * log-sum-exp, and an online-softmax combine merges the parts into exactly
+ * the attention of the unsplit cache ("Implementation decomposition,
+ * refined", S2: lse_t = m_t + log d_t; O = sum_t O_t e^{lse_t - M} /
+ * sum_t e^{lse_t - M}, M = max_t lse_t, in F32).  Quantised K/V blocks are
+ * read in registers inside the attention loop (section "2026-07-12 -- #582-P2
+ * SHIPPED: position-axis mixed KV": window and tail each read in-register at
+ * its own type, no whole-cache f16 materialise).  A tail held in
+ * pinned host memory is streamed through a B-slot device ring on a copy
+ * stream with per-slot copy_done / compute_done events ("Architecture",
+ * "CUDA stream graph"; and the page "Rolling-KV: step/graph-level tail
+ * prefetch (design)", section "The fix: a persistent, step-spanning
+ * tail-prefetch ring").
+ *
+ * Conventions for every entry point:
+ *  - The return value is a status code (RKV_OK = 0, negative on error).  No
+ *    call aborts the process.  Arguments are validated on the host before
+ *    anything is enqueued; on an error nothing is enqueued and
+ *    rkv_last_error() gives a thread-local message.  A fault inside a kernel
+ *    is asynchronous and surfaces at the caller's next synchronisation.
+ *  - Device buffers are owned by the caller.  The compute entry points
+ *    allocate nothing and create no events or streams, so they may be
+ *    enqueued on any stream, including under stream capture.
+ *  - Work is enqueued on the stream argument (NULL = the legacy default
+ *    stream); calls return without waiting for it.
+ *  - Floating-point outputs are IEEE binary32.  LSE values are natural-log.
+ */
+#ifndef RKV_H
+#define RKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+/* ---- status ------------------------------------------------------------ */
+enum {
+    RKV_OK = 0,
+    RKV_E_INVAL = -1,       /* bad argument: null pointer, bad size, stride, host pointer where device memory is needed */
+    RKV_E_UNSUPPORTED = -2, /* valid but not implemented: (type, head_dim) pair, too many heads / parts */
+    RKV_E_HIP = -3,         /* a HIP runtime call failed (message has the HIP error string) */
+    RKV_E_NOMEM = -4,       /* device or host allocation failed (ring creation only) */
+    RKV_E_STATE = -5        /* ring call out of order: layer not next in the plan, step not begun / not finished */
+};
+
+/* Static name of a status code. */
+const char *rkv_status_string(int status);
+/* Message of the last failing call on this thread ("" if none). */
+const char *rkv_last_error(void);
+
+/* ---- cache storage types ------------------------------------------------
+ * Blocks follow "F5 M6 -- PolyKV", section "S0 -- Bootstrap" and the
+ * tier-family table (1.062 and 0.562 bytes per value): 32 consecutive values
+ * along head_dim share one binary16 scale d.
+ *   RKV_Q8_0: 34 bytes = d, then 32 signed bytes q_i;           x_i = d * q_i
+ *   RKV_Q4_0: 18 bytes = d, then 16 bytes of 4-bit codes n_i;   x_i = d * (n_i - 8)
+ *             element i < 16 is the low nibble of byte i, element i >= 16
+ *             the high nibble of byte i - 16.
+ * Block types need head_dim % 32 == 0; a row of head_dim values is
+ * head_dim/32 blocks back to back. */
+typedef enum rkv_dtype { RKV_F32 = 0, RKV_F16 = 1, RKV_Q8_0 = 2, RKV_Q4_0 = 3 } rkv_dtype;
+
+/* Bytes of one row of head_dim values of a type (0 if invalid). */
+int64_t rkv_row_bytes(int32_t dtype, int32_t head_dim);
+
+/* ---- a segment of the KV cache -------------------------------------------
+ * One view is one segment: a window, a tail, a tile of the tail, a shared
+ * prefix or a private suffix.  Its positions [0, n_keys) are relative to the
+ * view.  Row (position p, KV head g, sequence b) of K starts at byte
+ *     k + b * k_seq_stride + p * k_pos_stride + g * k_head_stride
+ * (likewise V).  k_seq_stride = 0 means one segment shared by every sequence
+ * (its keys are read once for all of them).  n_keys = 0 is a legal, empty
+ * segment.  Pointers, strides and row sizes must be multiples of the row's
+ * load width (16 bytes for f32/f16 rows, 8 for block rows whose size is a
+ * multiple of 8, else 4).  The result does not depend on the order of
+ * positions inside a view (softmax attention is invariant to a joint
+ * permutation of the (k, v) pairs). */
+typedef struct rkv_kv_view {
+    const void *k;
+    const void *v;
+    int32_t k_type;
+    int32_t v_type;
+    int64_t n_keys;
+    int64_t k_pos_stride, v_pos_stride;
+    int64_t k_head_stride, v_head_stride;
+    int64_t k_seq_stride, v_seq_stride;
+} rkv_kv_view;
+
+/* ---- the attention problem ------------------------------------------------
+ * Decode: one query token per sequence.  Query head h of a sequence attends
+ * KV head q_to_kv[h] (NULL: contiguous groups h / (n_q_heads / n_kv_heads),
+ * which needs n_q_heads % n_kv_heads == 0).  Scores are
+ *     s_j = scale * (q . k_j),  then  s_j = softcap * tanh(s_j / softcap)  if softcap > 0,
+ * and the softmax and LSE are taken over the final s_j.  Limits:
+ * head_dim in {64, 128, 256, 512}; n_q_heads <= 256; n_kv_heads <= 64;
+ * n_seq * n_q_heads <= 65535. */
+typedef struct rkv_attn_desc {
+    int32_t n_seq;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    float scale;
+    float softcap;          /* 0 = off */
+    const int32_t *q_to_kv; /* host array of n_q_heads, or NULL */
+} rkv_attn_desc;
+
+/* Workspace bytes rkv_attend_segment needs for this problem and segment
+ * (written to *bytes; 0 for an empty segment). */
+int rkv_attend_workspace_bytes(const rkv_attn_desc *desc, const rkv_kv_view *seg, size_t *bytes);
+
+/*
+ * rkv_attend_segment -- normalised attention output and LSE of one segment.
+ *
+ *   q    [n_seq][n_q_heads][head_dim] binary32, device.
+ *   seg  the segment (device memory).
+ *   o    [n_seq][n_q_heads][head_dim] binary32, device (written).
+ *   lse  [n_seq][n_q_heads] binary32 natural-log LSE, device (written).
+ *   ws   device workspace of at least rkv_attend_workspace_bytes bytes.
+ *
+ * An empty segment gives o = 0 and lse = -inf (combine weight 0).  The result
+ * is deterministic: the same inputs give the same bits on every run.
+ * Errors: RKV_E_INVAL (null / host pointers, misaligned strides, small
+ * workspace, bad head map), RKV_E_UNSUPPORTED (type / head_dim / head
+ * counts outside the limits).
+ */
+int rkv_attend_segment(const rkv_attn_desc *desc, const float *q, const rkv_kv_view *seg,
+                       float *o, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * rkv_lse_combine -- merge per-segment results ("F5 M7 -- Rolling KV",
+ * "Implementation decomposition, refined", S2):
+ *     M = max_t lse_t;  w_t = e^{lse_t - M};
+ *     o = sum_t w_t o_t / sum_t w_t;  lse = M + ln sum_t w_t.
+ *
+ *   o_parts[t]   [n_rows][head_dim] binary32, device;  lse_parts[t] [n_rows], device.
+ *   o_parts and lse_parts are HOST arrays of n_parts device pointers.
+ *
+ * A part with lse = -inf has weight 0.  When every part of a row is empty the
+ * row gets o = 0, lse = -inf (and the call succeeds).  A row with a single
+ * non-empty part gets that part's values bit for bit.  o_out may alias
+ * o_parts[0] and lse_out may alias lse_parts[0].  1 <= n_parts <= 64.
+ */
+int rkv_lse_combine(int n_parts, const float *const *o_parts, const float *const *lse_parts,
+                    int64_t n_rows, int32_t head_dim, float *o_out, float *lse_out, hipStream_t stream);
+
+/*
+ * rkv_dequant_q8_0 / rkv_dequant_q4_0 -- blocks (device) to n_values binary32
+ * values (device), bit-exact: the products d*q and d*(n-8) are exact in
+ * binary32.  n_values % 32 != 0 -> RKV_E_INVAL.  Not used by the attention
+ * path (which reads blocks in registers); provided for checking and tools.
+ */
+int rkv_dequant_q8_0(const void *blocks, int64_t n_values, float *out, hipStream_t stream);
+int rkv_dequant_q4_0(const void *blocks, int64_t n_values, float *out, hipStream_t stream);
+
+/* ---- streamed tail --------------------------------------------------------
+ * A ring of n_slots device staging slots, each holding one tile of K and one
+ * of V, filled from pinned host memory by asynchronous copies on a copy
+ * stream.  The copy into a slot waits for the slot's compute_done event; the
+ * attention of a tile waits for its slot's copy_done event ("F5 M7 -- Rolling
+ * KV", "CUDA stream graph").  The order of copies is one flat sequence over
+ * (layer, tile) for a whole decode step, kept n_slots ahead of compute
+ * across layer boundaries ("Rolling-KV: step/graph-level tail prefetch
+ * (design)", "The fix: a persistent, step-spanning tail-prefetch ring"), so a
+ * layer's tail can load while earlier layers compute.
+ */
+typedef struct rkv_ring rkv_ring;
+
+/* Create a ring.  n_slots >= 2 (<= 16).  slot_k_bytes / slot_v_bytes: bytes
+ * of one tile of K / V (tile_keys * pos_stride of the tail views).
+ * copy_stream: NULL makes the ring create and own a non-blocking stream.
+ * The ring owns its slots, its events (created here, timing disabled) and a
+ * stream it created.  Errors: RKV_E_INVAL, RKV_E_NOMEM, RKV_E_HIP. */
+int rkv_ring_create(int n_slots, size_t slot_k_bytes, size_t slot_v_bytes, hipStream_t copy_stream,
+                    rkv_ring **out);
+/* Wait for the ring's work to finish, then free it.  NULL is a no-op. */
+int rkv_ring_destroy(rkv_ring *ring);
+
+/* Plan one step: the tails of n_layers layers (host_tails[l], each in pinned
+ * host memory, one sequence or shared by all sequences), cut into tiles of
+ * tile_keys keys (the last tile of a layer may be partial; an empty tail has
+ * no tiles).  Enqueues the first n_slots copies.  The host buffers must stay
+ * alive and unchanged until the step's attention has completed.
+ * Errors: RKV_E_INVAL (device pointer, tile larger than a slot, misaligned),
+ * RKV_E_STATE (previous step not ended). */
+int rkv_ring_begin_step(rkv_ring *ring, int n_layers, const rkv_kv_view *host_tails, int64_t tile_keys);
+
+/* Workspace bytes rkv_stream_tail needs for a layer of the current plan. */
+int rkv_stream_tail_workspace_bytes(const rkv_ring *ring, int layer, const rkv_attn_desc *desc, size_t *bytes);
+
+/*
+ * rkv_stream_tail -- attention over layer `layer`'s tail, tile by tile from
+ * the ring, merged with the window's result.
+ *
+ * For each tile: the compute stream waits copy_done of its slot, attends the
+ * slot, records compute_done; then the refill of that slot with the item
+ * n_slots further on in the flat order is enqueued on the copy stream.
+ * Finally (o_window, lse_window) and the tiles' results are merged with
+ * rkv_lse_combine in the order window, tile 0, tile 1, ...  lse_window may be
+ * NULL (no window; o_window is then ignored).  The result equals, bit for
+ * bit, rkv_attend_segment on each tile resident in device memory followed by
+ * that combine, whatever n_slots is.  Layers must be consumed in plan order.
+ * Errors: RKV_E_STATE (layer out of order / no step), RKV_E_INVAL.
+ */
+int rkv_stream_tail(rkv_ring *ring, int layer, const rkv_attn_desc *desc, const float *q,
+                    const float *o_window, const float *lse_window, float *o, float *lse,
+                    void *ws, size_t ws_bytes, hipStream_t compute_stream);
+
+/* End the step: every planned layer must have been consumed (else
+ * RKV_E_STATE).  Does not wait for the GPU. */
+int rkv_ring_end_step(rkv_ring *ring);
+
+/* Pure host logic of the schedule, for checking: with n_slots slots and
+ * tiles_per_layer[l] tiles per layer, item j of the flat order goes to slot
+ * j % n_slots and its copy waits for the compute of item j - n_slots.
+ * Writes, for each item j < n_items: layer_of[j], tile_of[j], slot_of[j],
+ * waits_on[j] (item index or -1).  Returns the number of items, or a
+ * negative status.  Any output pointer may be NULL. */
+int64_t rkv_ring_schedule(int n_layers, const int64_t *tiles_per_layer, int n_slots, int64_t max_items,
+                          int32_t *layer_of, int64_t *tile_of, int32_t *slot_of, int64_t *waits_on);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RKV_H */

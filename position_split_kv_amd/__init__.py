@@ -1,0 +1,262 @@
+"""Python binding of librkv.so (position-split decode attention for MI355X).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+The functions carry the names of the C entry points in include/rkv.h and
+take torch tensors (device memory, or pinned host memory for streamed
+tails) plus an optional torch stream.  There is no fallback: if the library
+is not built, importing a function raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librkv.so")
+
+RKV_F32, RKV_F16, RKV_Q8_0, RKV_Q4_0 = 0, 1, 2, 3
+RKV_OK, RKV_E_INVAL, RKV_E_UNSUPPORTED, RKV_E_HIP, RKV_E_NOMEM, RKV_E_STATE = 0, -1, -2, -3, -4, -5
+
+# every symbol include/rkv.h declares
+EXPORTS = (
+    "rkv_status_string", "rkv_last_error", "rkv_row_bytes", "rkv_attend_workspace_bytes", "rkv_attend_segment",
+    "rkv_lse_combine", "rkv_dequant_q8_0", "rkv_dequant_q4_0", "rkv_ring_create", "rkv_ring_destroy",
+    "rkv_ring_begin_step", "rkv_stream_tail_workspace_bytes", "rkv_stream_tail", "rkv_ring_end_step",
+    "rkv_ring_schedule",
+)
+
+
+class RkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_status_name(code)}: {msg}")
+        self.code = code
+
+
+class rkv_kv_view(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("k_type", ctypes.c_int32), ("v_type", ctypes.c_int32),
+        ("n_keys", ctypes.c_int64),
+        ("k_pos_stride", ctypes.c_int64), ("v_pos_stride", ctypes.c_int64),
+        ("k_head_stride", ctypes.c_int64), ("v_head_stride", ctypes.c_int64),
+        ("k_seq_stride", ctypes.c_int64), ("v_seq_stride", ctypes.c_int64),
+    ]
+
+
+class rkv_attn_desc(ctypes.Structure):
+    _fields_ = [
+        ("n_seq", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
+        ("q_to_kv", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with position_split_kv_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.rkv_status_string.restype = ctypes.c_char_p
+        L.rkv_status_string.argtypes = [ctypes.c_int]
+        L.rkv_last_error.restype = ctypes.c_char_p
+        L.rkv_last_error.argtypes = []
+        L.rkv_row_bytes.restype = i64
+        L.rkv_row_bytes.argtypes = [i32, i32]
+        L.rkv_attend_workspace_bytes.argtypes = [ctypes.POINTER(rkv_attn_desc), ctypes.POINTER(rkv_kv_view),
+                                                 ctypes.POINTER(sz)]
+        L.rkv_attend_segment.argtypes = [ctypes.POINTER(rkv_attn_desc), vp, ctypes.POINTER(rkv_kv_view), vp, vp, vp,
+                                         sz, vp]
+        L.rkv_lse_combine.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i32, vp, vp, vp]
+        L.rkv_dequant_q8_0.argtypes = [vp, i64, vp, vp]
+        L.rkv_dequant_q4_0.argtypes = [vp, i64, vp, vp]
+        L.rkv_ring_create.argtypes = [ctypes.c_int, sz, sz, vp, ctypes.POINTER(vp)]
+        L.rkv_ring_destroy.argtypes = [vp]
+        L.rkv_ring_begin_step.argtypes = [vp, ctypes.c_int, ctypes.POINTER(rkv_kv_view), i64]
+        L.rkv_stream_tail_workspace_bytes.argtypes = [vp, ctypes.c_int, ctypes.POINTER(rkv_attn_desc),
+                                                      ctypes.POINTER(sz)]
+        L.rkv_stream_tail.argtypes = [vp, ctypes.c_int, ctypes.POINTER(rkv_attn_desc), vp, vp, vp, vp, vp, vp, sz, vp]
+        L.rkv_ring_end_step.argtypes = [vp]
+        L.rkv_ring_schedule.restype = i64
+        L.rkv_ring_schedule.argtypes = [ctypes.c_int, ctypes.POINTER(i64), ctypes.c_int, i64, vp, vp, vp, vp]
+        for name in EXPORTS:
+            if name not in ("rkv_status_string", "rkv_last_error", "rkv_row_bytes", "rkv_ring_schedule"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _status_name(code: int) -> str:
+    try:
+        return lib().rkv_status_string(code).decode()
+    except Exception:
+        return str(code)
+
+
+def _check(code: int) -> None:
+    if code != RKV_OK:
+        raise RkvError(code, lib().rkv_last_error().decode())
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _addr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def row_bytes(dtype: int, head_dim: int) -> int:
+    return lib().rkv_row_bytes(dtype, head_dim)
+
+
+def make_view(k, v, k_type: int, v_type: int, n_keys: int, k_pos_stride: int, v_pos_stride: int,
+              k_head_stride: int, v_head_stride: int, k_seq_stride: int = 0, v_seq_stride: int = 0) -> rkv_kv_view:
+    """A segment view; k / v are tensors or raw addresses (bytes)."""
+    return rkv_kv_view(_addr(k), _addr(v), k_type, v_type, n_keys, k_pos_stride, v_pos_stride,
+                       k_head_stride, v_head_stride, k_seq_stride, v_seq_stride)
+
+
+class Desc:
+    """rkv_attn_desc plus the storage of its head map."""
+
+    def __init__(self, n_seq: int, n_q_heads: int, n_kv_heads: int, head_dim: int, scale: float,
+                 softcap: float = 0.0, q_to_kv=None):
+        self._map = None
+        mp = None
+        if q_to_kv is not None:
+            self._map = (ctypes.c_int32 * n_q_heads)(*[int(x) for x in q_to_kv])
+            mp = ctypes.cast(self._map, ctypes.POINTER(ctypes.c_int32))
+        self.c = rkv_attn_desc(n_seq, n_q_heads, n_kv_heads, head_dim, scale, softcap, mp)
+
+    @property
+    def n_rows(self) -> int:
+        return self.c.n_seq * self.c.n_q_heads
+
+
+def rkv_attend_workspace_bytes(desc: Desc, seg: rkv_kv_view) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().rkv_attend_workspace_bytes(ctypes.byref(desc.c), ctypes.byref(seg), ctypes.byref(out)))
+    return out.value
+
+
+def rkv_attend_segment(desc: Desc, q: torch.Tensor, seg: rkv_kv_view, o: torch.Tensor, lse: torch.Tensor,
+                       ws: torch.Tensor | None, stream=None) -> None:
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().rkv_attend_segment(ctypes.byref(desc.c), _addr(q), ctypes.byref(seg), _addr(o), _addr(lse),
+                                    _addr(ws), ws_bytes, _stream(stream)))
+
+
+def rkv_lse_combine(o_parts, lse_parts, o_out: torch.Tensor, lse_out: torch.Tensor, head_dim: int,
+                    stream=None) -> None:
+    n = len(o_parts)
+    op = (ctypes.c_void_p * n)(*[_addr(t) for t in o_parts])
+    lp = (ctypes.c_void_p * n)(*[_addr(t) for t in lse_parts])
+    n_rows = lse_out.numel()
+    _check(lib().rkv_lse_combine(n, op, lp, n_rows, head_dim, _addr(o_out), _addr(lse_out), _stream(stream)))
+
+
+def rkv_dequant_q8_0(blocks: torch.Tensor, n_values: int, out: torch.Tensor, stream=None) -> None:
+    _check(lib().rkv_dequant_q8_0(_addr(blocks), n_values, _addr(out), _stream(stream)))
+
+
+def rkv_dequant_q4_0(blocks: torch.Tensor, n_values: int, out: torch.Tensor, stream=None) -> None:
+    _check(lib().rkv_dequant_q4_0(_addr(blocks), n_values, _addr(out), _stream(stream)))
+
+
+def rkv_ring_schedule(tiles_per_layer, n_slots: int):
+    """Pure host schedule: lists (layer, tile, slot, waits_on) per item."""
+    n = len(tiles_per_layer)
+    tl = (ctypes.c_int64 * max(1, n))(*tiles_per_layer)
+    total = sum(tiles_per_layer)
+    lay = (ctypes.c_int32 * max(1, total))()
+    til = (ctypes.c_int64 * max(1, total))()
+    slo = (ctypes.c_int32 * max(1, total))()
+    wai = (ctypes.c_int64 * max(1, total))()
+    got = lib().rkv_ring_schedule(n, tl, n_slots, total, lay, til, slo, wai)
+    if got < 0:
+        raise RkvError(int(got), lib().rkv_last_error().decode())
+    return [(lay[j], til[j], slo[j], wai[j]) for j in range(got)]
+
+
+class Ring:
+    """rkv_ring_* lifecycle: a B-slot device staging ring on a copy stream."""
+
+    def __init__(self, n_slots: int, slot_k_bytes: int, slot_v_bytes: int, copy_stream=None):
+        h = ctypes.c_void_p(0)
+        cs = None if copy_stream is None else _stream(copy_stream)
+        _check(lib().rkv_ring_create(n_slots, slot_k_bytes, slot_v_bytes, cs, ctypes.byref(h)))
+        self.h = h
+        self._tails = None
+
+    def close(self) -> None:
+        if self.h:
+            _check(lib().rkv_ring_destroy(self.h))
+            self.h = ctypes.c_void_p(0)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def rkv_ring_begin_step(self, host_tails, tile_keys: int) -> None:
+        arr = (rkv_kv_view * max(1, len(host_tails)))(*host_tails)
+        self._tails = arr
+        _check(lib().rkv_ring_begin_step(self.h, len(host_tails), arr, tile_keys))
+
+    def rkv_stream_tail_workspace_bytes(self, layer: int, desc: Desc) -> int:
+        out = ctypes.c_size_t(0)
+        _check(lib().rkv_stream_tail_workspace_bytes(self.h, layer, ctypes.byref(desc.c), ctypes.byref(out)))
+        return out.value
+
+    def rkv_stream_tail(self, layer: int, desc: Desc, q, o_window, lse_window, o, lse, ws: torch.Tensor,
+                        stream=None) -> None:
+        ws_bytes = ws.numel() * ws.element_size()
+        _check(lib().rkv_stream_tail(self.h, layer, ctypes.byref(desc.c), _addr(q), _addr(o_window),
+                                     _addr(lse_window), _addr(o), _addr(lse), _addr(ws), ws_bytes,
+                                     _stream(stream)))
+
+    def rkv_ring_end_step(self) -> None:
+        _check(lib().rkv_ring_end_step(self.h))
+
+
+def view_of_cache(kc, vc, start: int = 0, stop: int | None = None, k_seq_stride: int = 0,
+                  v_seq_stride: int = 0) -> rkv_kv_view:
+    """View of positions [start, stop) of a pair of position-major caches
+    (objects with .data, .dtype, .pos_stride, .head_stride, .n_keys)."""
+    stop = kc.n_keys if stop is None else stop
+    return make_view(kc.data.data_ptr() + start * kc.pos_stride, vc.data.data_ptr() + start * vc.pos_stride,
+                     kc.dtype, vc.dtype, stop - start, kc.pos_stride, vc.pos_stride, kc.head_stride,
+                     vc.head_stride, k_seq_stride, v_seq_stride)
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A device workspace of at least nbytes (torch allocations are 256-byte aligned)."""
+    return torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
+
+
+def attend(desc: Desc, q: torch.Tensor, seg: rkv_kv_view, stream=None, ws: torch.Tensor | None = None):
+    """Allocate outputs (and workspace if none given) and run rkv_attend_segment."""
+    S, Hq, D = desc.c.n_seq, desc.c.n_q_heads, desc.c.head_dim
+    o = torch.empty(S, Hq, D, dtype=torch.float32, device=q.device)
+    lse = torch.empty(S, Hq, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(rkv_attend_workspace_bytes(desc, seg), q.device)
+    rkv_attend_segment(desc, q, seg, o, lse, ws, stream)
+    return o, lse

@@ -1,0 +1,612 @@
+// api.hip -- the C ABI (rkv.h): validation, work planning, and the
+// streamed-tail ring.  Every entry point validates its arguments on the host
+// before enqueuing anything and reports errors through status codes and a
+// thread-local message; nothing here aborts.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+using namespace rkv;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(RKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define RKV_HIP(call)                                  \
+    do {                                               \
+        hipError_t e_ = (call);                        \
+        if (e_ != hipSuccess) return hip_fail(e_, #call); \
+    } while (0)
+
+// Memory kind of a pointer: 2 device, 1 pinned host, 0 unknown / pageable.
+int mem_kind(const void *p)
+{
+    hipPointerAttribute_t a;
+    memset(&a, 0, sizeof a);
+    const hipError_t e = hipPointerGetAttributes(&a, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (a.type == hipMemoryTypeDevice || a.isManaged) return 2;
+    if (a.type == hipMemoryTypeHost) return 1;
+    return 0;
+}
+
+bool valid_type(int t) { return t >= RKV_F32 && t <= RKV_Q4_0; }
+bool valid_d(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
+int check_desc(const rkv_attn_desc *d)
+{
+    if (!d) return fail(RKV_E_INVAL, "desc is NULL");
+    if (d->n_seq < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
+        return fail(RKV_E_INVAL, "n_seq, n_q_heads, n_kv_heads must be >= 1");
+    if (!valid_d(d->head_dim)) return fail(RKV_E_UNSUPPORTED, "head_dim %d not in {64,128,256,512}", d->head_dim);
+    if (d->n_q_heads > 256 || d->n_kv_heads > kMaxKvHeads)
+        return fail(RKV_E_UNSUPPORTED, "n_q_heads <= 256 and n_kv_heads <= %d", kMaxKvHeads);
+    if ((int64_t)d->n_seq * d->n_q_heads > 65535) return fail(RKV_E_UNSUPPORTED, "n_seq * n_q_heads > 65535");
+    if (!(d->scale == d->scale) || !(d->softcap >= 0.f) || d->softcap == INFINITY)
+        return fail(RKV_E_INVAL, "scale must be a number and softcap finite >= 0");
+    if (d->q_to_kv) {
+        for (int h = 0; h < d->n_q_heads; ++h)
+            if (d->q_to_kv[h] < 0 || d->q_to_kv[h] >= d->n_kv_heads)
+                return fail(RKV_E_INVAL, "q_to_kv[%d] = %d out of range", h, d->q_to_kv[h]);
+    } else if (d->n_q_heads % d->n_kv_heads) {
+        return fail(RKV_E_INVAL, "n_q_heads %% n_kv_heads != 0 needs an explicit q_to_kv");
+    }
+    return RKV_OK;
+}
+
+int kv_of(const rkv_attn_desc *d, int h)
+{
+    return d->q_to_kv ? d->q_to_kv[h] : h / (d->n_q_heads / d->n_kv_heads);
+}
+
+// Host-side checks of a view's fields (no pointer-kind checks).
+int check_view_fields(const rkv_attn_desc *d, const rkv_kv_view *v)
+{
+    if (!v) return fail(RKV_E_INVAL, "view is NULL");
+    if (!valid_type(v->k_type) || !valid_type(v->v_type)) return fail(RKV_E_INVAL, "bad K/V type");
+    if (v->n_keys < 0) return fail(RKV_E_INVAL, "n_keys < 0");
+    if (v->n_keys > ((int64_t)1 << 40)) return fail(RKV_E_UNSUPPORTED, "n_keys too large");
+    if (v->n_keys == 0) return RKV_OK;
+    if (!v->k || !v->v) return fail(RKV_E_INVAL, "K or V pointer is NULL");
+    const int D = d->head_dim;
+    const int64_t rbk = row_bytes_of(v->k_type, D), rbv = row_bytes_of(v->v_type, D);
+    const int64_t wk = load_width_of(v->k_type, D), wv = load_width_of(v->v_type, D);
+    if (v->k_pos_stride <= 0 || v->v_pos_stride <= 0 || v->k_head_stride < 0 || v->v_head_stride < 0 ||
+        v->k_seq_stride < 0 || v->v_seq_stride < 0)
+        return fail(RKV_E_INVAL, "strides must be non-negative (position strides positive)");
+    if (v->k_pos_stride > (1 << 24) || v->v_pos_stride > (1 << 24))
+        return fail(RKV_E_UNSUPPORTED, "position strides above 16 MiB");
+    if ((uintptr_t)v->k % wk || v->k_pos_stride % wk || v->k_head_stride % wk || v->k_seq_stride % wk)
+        return fail(RKV_E_INVAL, "K pointer/strides must be multiples of %lld bytes", (long long)wk);
+    if ((uintptr_t)v->v % wv || v->v_pos_stride % wv || v->v_head_stride % wv || v->v_seq_stride % wv)
+        return fail(RKV_E_INVAL, "V pointer/strides must be multiples of %lld bytes", (long long)wv);
+    if (d->n_kv_heads > 1 && (v->k_head_stride < rbk || v->v_head_stride < rbv))
+        return fail(RKV_E_INVAL, "head stride smaller than a row");
+    const bool k_shared = v->k_seq_stride == 0, v_shared = v->v_seq_stride == 0;
+    if (d->n_seq > 1 && k_shared != v_shared)
+        return fail(RKV_E_INVAL, "K and V must both be shared (seq stride 0) or both per sequence");
+    return RKV_OK;
+}
+
+const int kRtSet[] = {1, 2, 4, 5, 8, 16};
+
+// Cut a segment into waves: row groups per KV head and key ranges.
+int make_plan(const rkv_attn_desc *d, const rkv_kv_view *v, SplitPlan *pl, SplitParams *prm)
+{
+    const int S = d->n_seq, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim;
+    const bool shared = S == 1 || (v->k_seq_stride == 0 && v->v_seq_stride == 0);
+    std::vector<std::vector<int>> rows(Hkv);
+    for (int b = 0; b < (shared ? S : 1); ++b)
+        for (int h = 0; h < Hq; ++h) rows[kv_of(d, h)].push_back(b * Hq + h);
+    int rmax = 0;
+    for (auto &r : rows) rmax = std::max(rmax, (int)r.size());
+    if ((int64_t)rmax * Hkv > kMaxRowTable)
+        return fail(RKV_E_UNSUPPORTED, "rows per KV head x KV heads = %d > %d", rmax * Hkv, kMaxRowTable);
+    int rt = 16;
+    for (int c : kRtSet)
+        if (c >= rmax) {
+            rt = c;
+            break;
+        }
+    pl->rt = rt;
+    pl->n_rg = (rmax + rt - 1) / rt;
+    pl->rows_per_g = rmax;
+    pl->z = shared ? 1 : S;
+    pl->n_rows_total = (int64_t)S * Hq;
+    const int64_t n_tiles = (v->n_keys + kTile - 1) / kTile;
+    const int64_t units = (int64_t)Hkv * pl->n_rg * pl->z;
+    const int64_t want = 2048;
+    int64_t n_splits = std::max<int64_t>(1, std::min<int64_t>(n_tiles, (want + units - 1) / units));
+    int64_t tps = std::max<int64_t>((n_tiles + n_splits - 1) / n_splits, std::min<int64_t>(4, n_tiles));
+    if (tps * kTile > (1 << 30)) tps = (1 << 30) / kTile;
+    n_splits = n_tiles ? (n_tiles + tps - 1) / tps : 0;
+    if (n_splits > 65535) return fail(RKV_E_UNSUPPORTED, "segment too long for one launch");
+    pl->n_splits = (int)n_splits;
+    pl->keys_per_split = (int)(tps * kTile);
+    const size_t acc_bytes = (size_t)n_splits * pl->n_rows_total * D * sizeof(float);
+    pl->ws_bytes = n_tiles ? ((acc_bytes + 255) & ~(size_t)255) + (size_t)n_splits * pl->n_rows_total * sizeof(float2)
+                           : 0;
+    if (prm) {
+        memset(prm, 0, sizeof *prm);
+        prm->k_pos = v->k_pos_stride;
+        prm->v_pos = v->v_pos_stride;
+        prm->k_head = v->k_head_stride;
+        prm->v_head = v->v_head_stride;
+        prm->k_seq = shared ? 0 : v->k_seq_stride;
+        prm->v_seq = shared ? 0 : v->v_seq_stride;
+        prm->n_keys = v->n_keys;
+        prm->keys_per_split = pl->keys_per_split;
+        prm->n_splits = pl->n_splits;
+        prm->n_rg = pl->n_rg;
+        prm->rows_per_g = rmax;
+        prm->n_rows_total = (int32_t)pl->n_rows_total;
+        prm->z_row_step = shared ? 0 : Hq;
+        prm->scale = d->scale;
+        prm->scale_log2 = d->scale * 1.4426950408889634f;
+        prm->softcap = d->softcap;
+        for (int g = 0; g < Hkv; ++g) {
+            prm->rowcnt[g] = (uint16_t)rows[g].size();
+            for (size_t i = 0; i < rows[g].size(); ++i) prm->rowtab[g * rmax + i] = (uint16_t)rows[g][i];
+        }
+    }
+    return RKV_OK;
+}
+
+// Enqueue one segment (arguments already validated).
+int attend_impl(const rkv_attn_desc *d, const float *q, const rkv_kv_view *v, float *o, float *lse, void *ws,
+                size_t ws_bytes, hipStream_t stream)
+{
+    const int64_t n_rows = (int64_t)d->n_seq * d->n_q_heads;
+    if (v->n_keys == 0) {
+        RKV_HIP(launch_fill_empty(d->head_dim, n_rows, o, lse, stream));
+        return RKV_OK;
+    }
+    SplitPlan pl;
+    SplitParams prm;
+    int rc = make_plan(d, v, &pl, &prm);
+    if (rc) return rc;
+    if (ws_bytes < pl.ws_bytes || !ws)
+        return fail(RKV_E_INVAL, "workspace too small: %zu < %zu", ws_bytes, pl.ws_bytes);
+    if (!split_supported(v->k_type, v->v_type, d->head_dim, pl.rt))
+        return fail(RKV_E_UNSUPPORTED, "no kernel for this (type, head_dim, rows)");
+    float *part_acc = (float *)ws;
+    const size_t acc_bytes = (size_t)pl.n_splits * pl.n_rows_total * d->head_dim * sizeof(float);
+    float2 *part_ml = (float2 *)((char *)ws + ((acc_bytes + 255) & ~(size_t)255));
+    const dim3 grid((unsigned)pl.n_splits, (unsigned)(d->n_kv_heads * pl.n_rg), (unsigned)pl.z);
+    RKV_HIP(launch_split(v->k_type, v->v_type, d->head_dim, pl.rt, grid, q, (const uint8_t *)v->k,
+                         (const uint8_t *)v->v, part_acc, part_ml, prm, stream));
+    RKV_HIP(launch_reduce(d->head_dim, n_rows, pl.n_splits, part_acc, part_ml, o, lse, stream));
+    return RKV_OK;
+}
+
+int check_attend_args(const rkv_attn_desc *d, const float *q, const rkv_kv_view *v, float *o, float *lse)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    rc = check_view_fields(d, v);
+    if (rc) return rc;
+    if (!q || !o || !lse) return fail(RKV_E_INVAL, "q, o and lse must not be NULL");
+    if ((uintptr_t)q % 16 || (uintptr_t)o % 16 || (uintptr_t)lse % 4)
+        return fail(RKV_E_INVAL, "q and o must be 16-byte aligned, lse 4-byte aligned");
+    return RKV_OK;
+}
+
+int check_device(const void *p, const char *name)
+{
+    if (mem_kind(p) != 2) return fail(RKV_E_INVAL, "%s is not device memory", name);
+    return RKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rkv_status_string(int s)
+{
+    switch (s) {
+    case RKV_OK: return "RKV_OK";
+    case RKV_E_INVAL: return "RKV_E_INVAL";
+    case RKV_E_UNSUPPORTED: return "RKV_E_UNSUPPORTED";
+    case RKV_E_HIP: return "RKV_E_HIP";
+    case RKV_E_NOMEM: return "RKV_E_NOMEM";
+    case RKV_E_STATE: return "RKV_E_STATE";
+    default: return "RKV_E_UNKNOWN";
+    }
+}
+
+const char *rkv_last_error(void) { return g_err.c_str(); }
+
+int64_t rkv_row_bytes(int32_t dtype, int32_t head_dim)
+{
+    if (!valid_type(dtype) || head_dim <= 0) return 0;
+    if ((dtype == RKV_Q8_0 || dtype == RKV_Q4_0) && head_dim % 32) return 0;
+    return row_bytes_of(dtype, head_dim);
+}
+
+int rkv_attend_workspace_bytes(const rkv_attn_desc *desc, const rkv_kv_view *seg, size_t *bytes)
+{
+    if (!bytes) return fail(RKV_E_INVAL, "bytes is NULL");
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    rc = check_view_fields(desc, seg);
+    if (rc) return rc;
+    if (seg->n_keys == 0) {
+        *bytes = 0;
+        return RKV_OK;
+    }
+    SplitPlan pl;
+    rc = make_plan(desc, seg, &pl, nullptr);
+    if (rc) return rc;
+    *bytes = pl.ws_bytes;
+    return RKV_OK;
+}
+
+int rkv_attend_segment(const rkv_attn_desc *desc, const float *q, const rkv_kv_view *seg, float *o, float *lse,
+                       void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc = check_attend_args(desc, q, seg, o, lse);
+    if (rc) return rc;
+    if ((rc = check_device(q, "q")) || (rc = check_device(o, "o")) || (rc = check_device(lse, "lse"))) return rc;
+    if (seg->n_keys > 0) {
+        if ((rc = check_device(seg->k, "K")) || (rc = check_device(seg->v, "V"))) return rc;
+        if (ws && (rc = check_device(ws, "workspace"))) return rc;
+    }
+    return attend_impl(desc, q, seg, o, lse, ws, ws_bytes, stream);
+}
+
+int rkv_lse_combine(int n_parts, const float *const *o_parts, const float *const *lse_parts, int64_t n_rows,
+                    int32_t head_dim, float *o_out, float *lse_out, hipStream_t stream)
+{
+    if (n_parts < 1 || n_parts > kMaxParts) return fail(RKV_E_INVAL, "n_parts must be in [1, %d]", kMaxParts);
+    if (!o_parts || !lse_parts || !o_out || !lse_out) return fail(RKV_E_INVAL, "NULL argument");
+    if (n_rows < 0 || n_rows > 0x7fffffff) return fail(RKV_E_INVAL, "bad n_rows");
+    if (head_dim < 1 || head_dim > 4096) return fail(RKV_E_INVAL, "bad head_dim");
+    CombineParts parts;
+    memset(&parts, 0, sizeof parts);
+    for (int t = 0; t < n_parts; ++t) {
+        if (!o_parts[t] || !lse_parts[t]) return fail(RKV_E_INVAL, "part %d is NULL", t);
+        parts.o[t] = o_parts[t];
+        parts.lse[t] = lse_parts[t];
+    }
+    if (n_rows == 0) return RKV_OK;
+    int rc;
+    for (int t = 0; t < n_parts; ++t)
+        if ((rc = check_device(parts.o[t], "o_parts[t]")) || (rc = check_device(parts.lse[t], "lse_parts[t]")))
+            return rc;
+    if ((rc = check_device(o_out, "o_out")) || (rc = check_device(lse_out, "lse_out"))) return rc;
+    RKV_HIP(launch_combine(n_parts, parts, n_rows, head_dim, o_out, lse_out, stream));
+    return RKV_OK;
+}
+
+static int dequant_common(const void *blocks, int64_t n, float *out)
+{
+    if (n < 0 || n % 32) return fail(RKV_E_INVAL, "n_values must be a non-negative multiple of 32");
+    if (n == 0) return RKV_OK;
+    if (!blocks || !out) return fail(RKV_E_INVAL, "NULL argument");
+    int rc;
+    if ((rc = check_device(blocks, "blocks")) || (rc = check_device(out, "out"))) return rc;
+    return RKV_OK;
+}
+
+int rkv_dequant_q8_0(const void *blocks, int64_t n_values, float *out, hipStream_t stream)
+{
+    int rc = dequant_common(blocks, n_values, out);
+    if (rc || n_values == 0) return rc;
+    RKV_HIP(launch_dequant_q8_0(blocks, n_values, out, stream));
+    return RKV_OK;
+}
+
+int rkv_dequant_q4_0(const void *blocks, int64_t n_values, float *out, hipStream_t stream)
+{
+    int rc = dequant_common(blocks, n_values, out);
+    if (rc || n_values == 0) return rc;
+    RKV_HIP(launch_dequant_q4_0(blocks, n_values, out, stream));
+    return RKV_OK;
+}
+
+// ---------------------------------------------------------------- ring
+
+int64_t rkv_ring_schedule(int n_layers, const int64_t *tiles_per_layer, int n_slots, int64_t max_items,
+                          int32_t *layer_of, int64_t *tile_of, int32_t *slot_of, int64_t *waits_on)
+{
+    if (n_layers < 0 || (n_layers > 0 && !tiles_per_layer)) return fail(RKV_E_INVAL, "bad layers");
+    if (n_slots < 2 || n_slots > 16) return fail(RKV_E_INVAL, "n_slots must be in [2, 16]");
+    int64_t j = 0;
+    for (int l = 0; l < n_layers; ++l) {
+        if (tiles_per_layer[l] < 0) return fail(RKV_E_INVAL, "negative tile count");
+        for (int64_t t = 0; t < tiles_per_layer[l]; ++t, ++j) {
+            if (j >= max_items) continue;
+            if (layer_of) layer_of[j] = l;
+            if (tile_of) tile_of[j] = t;
+            if (slot_of) slot_of[j] = (int32_t)(j % n_slots);
+            if (waits_on) waits_on[j] = j >= n_slots ? j - n_slots : -1;
+        }
+    }
+    return j;
+}
+
+}  // extern "C"
+
+struct rkv_ring {
+    int B = 0;
+    int device = 0;
+    size_t slot_k = 0, slot_v = 0;
+    void *sk[16] = {}, *sv[16] = {};
+    hipStream_t copy = nullptr;
+    bool own_copy = false;
+    hipEvent_t copy_done[16] = {}, compute_done[16] = {};
+    // plan of the current step
+    bool in_step = false;
+    std::vector<rkv_kv_view> tails;
+    int64_t tile_keys = 0;
+    struct Item {
+        int layer;
+        int64_t k0, nk;
+    };
+    std::vector<Item> items;
+    std::vector<int64_t> first_item;  // per layer, plus end
+    int next_layer = 0;
+};
+
+namespace {
+
+int enqueue_copy(rkv_ring *r, int64_t j)
+{
+    const rkv_ring::Item &it = r->items[j];
+    const rkv_kv_view &t = r->tails[it.layer];
+    const int s = (int)(j % r->B);
+    RKV_HIP(hipStreamWaitEvent(r->copy, r->compute_done[s], 0));
+    const size_t kb = (size_t)(it.nk * t.k_pos_stride), vb = (size_t)(it.nk * t.v_pos_stride);
+    RKV_HIP(hipMemcpyAsync(r->sk[s], (const char *)t.k + it.k0 * t.k_pos_stride, kb, hipMemcpyHostToDevice, r->copy));
+    RKV_HIP(hipMemcpyAsync(r->sv[s], (const char *)t.v + it.k0 * t.v_pos_stride, vb, hipMemcpyHostToDevice, r->copy));
+    RKV_HIP(hipEventRecord(r->copy_done[s], r->copy));
+    return RKV_OK;
+}
+
+void ring_free(rkv_ring *r)
+{
+    for (int i = 0; i < 16; ++i) {
+        if (r->sk[i]) (void)hipFree(r->sk[i]);
+        if (r->sv[i]) (void)hipFree(r->sv[i]);
+        if (r->copy_done[i]) (void)hipEventDestroy(r->copy_done[i]);
+        if (r->compute_done[i]) (void)hipEventDestroy(r->compute_done[i]);
+    }
+    if (r->own_copy && r->copy) (void)hipStreamDestroy(r->copy);
+    delete r;
+}
+
+// Bytes of the tile partials kept in the stream_tail workspace.
+size_t tile_parts_bytes(int64_t n_tiles, int64_t n_rows, int D)
+{
+    return (((size_t)n_tiles * n_rows * (D + 1) * sizeof(float)) + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rkv_ring_create(int n_slots, size_t slot_k_bytes, size_t slot_v_bytes, hipStream_t copy_stream, rkv_ring **out)
+{
+    if (!out) return fail(RKV_E_INVAL, "out is NULL");
+    *out = nullptr;
+    if (n_slots < 2 || n_slots > 16) return fail(RKV_E_INVAL, "n_slots must be in [2, 16]");
+    if (slot_k_bytes == 0 || slot_v_bytes == 0) return fail(RKV_E_INVAL, "slot sizes must be > 0");
+    rkv_ring *r = new (std::nothrow) rkv_ring;
+    if (!r) return fail(RKV_E_NOMEM, "host allocation failed");
+    r->B = n_slots;
+    r->slot_k = slot_k_bytes;
+    r->slot_v = slot_v_bytes;
+    hipError_t e = hipGetDevice(&r->device);
+    if (e != hipSuccess) {
+        ring_free(r);
+        return hip_fail(e, "hipGetDevice");
+    }
+    for (int i = 0; i < n_slots; ++i) {
+        if (hipMalloc(&r->sk[i], slot_k_bytes) != hipSuccess || hipMalloc(&r->sv[i], slot_v_bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            ring_free(r);
+            return fail(RKV_E_NOMEM, "slot allocation failed");
+        }
+        if ((e = hipEventCreateWithFlags(&r->copy_done[i], hipEventDisableTiming)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&r->compute_done[i], hipEventDisableTiming)) != hipSuccess) {
+            ring_free(r);
+            return hip_fail(e, "hipEventCreateWithFlags");
+        }
+    }
+    if (copy_stream) {
+        r->copy = copy_stream;
+    } else {
+        if ((e = hipStreamCreateWithFlags(&r->copy, hipStreamNonBlocking)) != hipSuccess) {
+            r->copy = nullptr;
+            ring_free(r);
+            return hip_fail(e, "hipStreamCreateWithFlags");
+        }
+        r->own_copy = true;
+    }
+    *out = r;
+    return RKV_OK;
+}
+
+int rkv_ring_destroy(rkv_ring *r)
+{
+    if (!r) return RKV_OK;
+    hipError_t e = hipStreamSynchronize(r->copy);
+    for (int i = 0; i < r->B && e == hipSuccess; ++i) e = hipEventSynchronize(r->compute_done[i]);
+    ring_free(r);
+    if (e != hipSuccess) return hip_fail(e, "ring destroy synchronisation");
+    return RKV_OK;
+}
+
+int rkv_ring_begin_step(rkv_ring *r, int n_layers, const rkv_kv_view *tails, int64_t tile_keys)
+{
+    if (!r) return fail(RKV_E_INVAL, "ring is NULL");
+    if (r->in_step) return fail(RKV_E_STATE, "previous step not ended");
+    if (n_layers < 0 || (n_layers > 0 && !tails)) return fail(RKV_E_INVAL, "bad layers");
+    if (tile_keys < 1) return fail(RKV_E_INVAL, "tile_keys must be >= 1");
+    std::vector<rkv_ring::Item> items;
+    std::vector<int64_t> first(n_layers + 1, 0);
+    for (int l = 0; l < n_layers; ++l) {
+        const rkv_kv_view &t = tails[l];
+        first[l] = (int64_t)items.size();
+        if (t.n_keys < 0) return fail(RKV_E_INVAL, "tail %d: n_keys < 0", l);
+        if (t.n_keys == 0) continue;
+        if (!t.k || !t.v || t.k_pos_stride <= 0 || t.v_pos_stride <= 0)
+            return fail(RKV_E_INVAL, "tail %d: bad pointers or strides", l);
+        if ((size_t)(std::min(tile_keys, t.n_keys) * t.k_pos_stride) > r->slot_k ||
+            (size_t)(std::min(tile_keys, t.n_keys) * t.v_pos_stride) > r->slot_v)
+            return fail(RKV_E_INVAL, "tail %d: a tile does not fit a slot", l);
+        if (mem_kind(t.k) != 1 || mem_kind(t.v) != 1)
+            return fail(RKV_E_INVAL, "tail %d must be pinned host memory", l);
+        for (int64_t k0 = 0; k0 < t.n_keys; k0 += tile_keys)
+            items.push_back({l, k0, std::min(tile_keys, t.n_keys - k0)});
+        if ((int64_t)items.size() - first[l] > kMaxParts - 1)
+            return fail(RKV_E_UNSUPPORTED, "tail %d: more than %d tiles", l, kMaxParts - 1);
+    }
+    first[n_layers] = (int64_t)items.size();
+    r->tails.assign(tails, tails + n_layers);
+    r->items.swap(items);
+    r->first_item.swap(first);
+    r->tile_keys = tile_keys;
+    r->next_layer = 0;
+    r->in_step = true;
+    const int64_t n = std::min<int64_t>(r->B, (int64_t)r->items.size());
+    for (int64_t j = 0; j < n; ++j) {
+        int rc = enqueue_copy(r, j);
+        if (rc) {
+            r->in_step = false;
+            return rc;
+        }
+    }
+    return RKV_OK;
+}
+
+int rkv_stream_tail_workspace_bytes(const rkv_ring *r, int layer, const rkv_attn_desc *desc, size_t *bytes)
+{
+    if (!r || !bytes) return fail(RKV_E_INVAL, "NULL argument");
+    if (!r->in_step) return fail(RKV_E_STATE, "no step begun");
+    if (layer < 0 || layer >= (int)r->tails.size()) return fail(RKV_E_INVAL, "layer out of range");
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    const int64_t n_tiles = r->first_item[layer + 1] - r->first_item[layer];
+    const int64_t n_rows = (int64_t)desc->n_seq * desc->n_q_heads;
+    size_t attend = 0;
+    if (n_tiles > 0) {
+        rkv_kv_view v = r->tails[layer];
+        v.n_keys = std::min<int64_t>(r->tile_keys, v.n_keys);
+        v.k = r->sk[0];
+        v.v = r->sv[0];
+        if ((rc = rkv_attend_workspace_bytes(desc, &v, &attend))) return rc;
+    }
+    *bytes = tile_parts_bytes(n_tiles, n_rows, desc->head_dim) + attend;
+    return RKV_OK;
+}
+
+int rkv_stream_tail(rkv_ring *r, int layer, const rkv_attn_desc *desc, const float *q, const float *o_window,
+                    const float *lse_window, float *o, float *lse, void *ws, size_t ws_bytes, hipStream_t cs)
+{
+    if (!r) return fail(RKV_E_INVAL, "ring is NULL");
+    if (!r->in_step) return fail(RKV_E_STATE, "no step begun");
+    if (layer != r->next_layer) return fail(RKV_E_STATE, "layer %d consumed out of order (next is %d)", layer, r->next_layer);
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (!q || !o || !lse) return fail(RKV_E_INVAL, "q, o and lse must not be NULL");
+    if (lse_window && !o_window) return fail(RKV_E_INVAL, "o_window is NULL");
+    const int D = desc->head_dim;
+    const int64_t n_rows = (int64_t)desc->n_seq * desc->n_q_heads;
+    const int64_t j0 = r->first_item[layer], j1 = r->first_item[layer + 1];
+    const int64_t n_tiles = j1 - j0;
+    const rkv_kv_view &tail = r->tails[layer];
+    if (n_tiles > 0) {
+        if (desc->n_seq > 1 && (tail.k_seq_stride != 0 || tail.v_seq_stride != 0))
+            return fail(RKV_E_UNSUPPORTED, "a streamed tail must be shared by all sequences or n_seq == 1");
+        const int64_t rbk = row_bytes_of(tail.k_type, D), rbv = row_bytes_of(tail.v_type, D);
+        if ((desc->n_kv_heads - 1) * tail.k_head_stride + rbk > tail.k_pos_stride ||
+            (desc->n_kv_heads - 1) * tail.v_head_stride + rbv > tail.v_pos_stride)
+            return fail(RKV_E_INVAL, "tail rows of one position must fit in its position stride");
+    }
+    size_t need = 0;
+    if ((rc = rkv_stream_tail_workspace_bytes(r, layer, desc, &need))) return rc;
+    if (!ws || ws_bytes < need) return fail(RKV_E_INVAL, "workspace too small: %zu < %zu", ws_bytes, need);
+    if ((rc = check_device(q, "q")) || (rc = check_device(o, "o")) || (rc = check_device(lse, "lse")) ||
+        (rc = check_device(ws, "workspace")))
+        return rc;
+    if (lse_window && ((rc = check_device(o_window, "o_window")) || (rc = check_device(lse_window, "lse_window"))))
+        return rc;
+
+    float *tile_o = (float *)ws;
+    float *tile_lse = tile_o + n_tiles * n_rows * D;
+    char *attend_ws = (char *)ws + tile_parts_bytes(n_tiles, n_rows, D);
+    const size_t attend_bytes = ws_bytes - tile_parts_bytes(n_tiles, n_rows, D);
+    for (int64_t j = j0; j < j1; ++j) {
+        const int s = (int)(j % r->B);
+        rkv_kv_view v = tail;
+        v.k = r->sk[s];
+        v.v = r->sv[s];
+        v.n_keys = r->items[j].nk;
+        v.k_seq_stride = 0;
+        v.v_seq_stride = 0;
+        if ((rc = check_view_fields(desc, &v))) return rc;
+        RKV_HIP(hipStreamWaitEvent(cs, r->copy_done[s], 0));
+        if ((rc = attend_impl(desc, q, &v, tile_o + (j - j0) * n_rows * D, tile_lse + (j - j0) * n_rows, attend_ws,
+                              attend_bytes, cs)))
+            return rc;
+        RKV_HIP(hipEventRecord(r->compute_done[s], cs));
+        if (j + r->B < (int64_t)r->items.size())
+            if ((rc = enqueue_copy(r, j + r->B))) return rc;
+    }
+    CombineParts parts;
+    memset(&parts, 0, sizeof parts);
+    int np = 0;
+    if (lse_window) {
+        parts.o[np] = o_window;
+        parts.lse[np++] = lse_window;
+    }
+    for (int64_t t = 0; t < n_tiles; ++t) {
+        parts.o[np] = tile_o + t * n_rows * D;
+        parts.lse[np++] = tile_lse + t * n_rows;
+    }
+    if (np == 0) {
+        RKV_HIP(launch_fill_empty(D, n_rows, o, lse, cs));
+    } else {
+        RKV_HIP(launch_combine(np, parts, n_rows, D, o, lse, cs));
+    }
+    r->next_layer++;
+    return RKV_OK;
+}
+
+int rkv_ring_end_step(rkv_ring *r)
+{
+    if (!r) return fail(RKV_E_INVAL, "ring is NULL");
+    if (!r->in_step) return fail(RKV_E_STATE, "no step begun");
+    r->in_step = false;
+    if (r->next_layer != (int)r->tails.size())
+        return fail(RKV_E_STATE, "step ended after %d of %d layers", r->next_layer, (int)r->tails.size());
+    return RKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// attend_inst.hip -- instances of the split kernel for one (K type, V type)
+// pair.  Built once per pair with -DRKV_KT=<t> -DRKV_VT=<t> (0 f32, 1 f16,
+// 2 q8_0, 3 q4_0) so that the instances compile in parallel.
+#include "attend_kernel.h"
+
+#if !defined(RKV_KT) || !defined(RKV_VT)
+#error "RKV_KT and RKV_VT must be defined"
+#endif
+
+#define RKV_CAT4(a, b, c, d) a##b##c##d
+#define RKV_NAME(kt, vt) RKV_CAT4(launch_split_k, kt, _v, vt)
+
+namespace rkv {
+
+template <int D, int RT>
+static hipError_t go(dim3 grid, const float *q, const uint8_t *k, const uint8_t *v, float *pa, float2 *pm,
+                     const SplitParams &p, hipStream_t stream)
+{
+    if constexpr (D == 512 && (RKV_KT == kF32 || RKV_VT == kF32)) {
+        return hipErrorInvalidValue;  // an f32 row of 512 values does not fit the LDS tile
+    } else {
+        hipLaunchKernelGGL((rkv_split_kernel<RKV_KT, RKV_VT, D, RT>), grid, dim3(64), 0, stream, q, k, v, pa, pm, p);
+        return hipGetLastError();
+    }
+}
+
+template <int D>
+static hipError_t by_rt(int rt, dim3 grid, const float *q, const uint8_t *k, const uint8_t *v, float *pa,
+                        float2 *pm, const SplitParams &p, hipStream_t s)
+{
+    switch (rt) {
+    case 1: return go<D, 1>(grid, q, k, v, pa, pm, p, s);
+    case 2: return go<D, 2>(grid, q, k, v, pa, pm, p, s);
+    case 4: return go<D, 4>(grid, q, k, v, pa, pm, p, s);
+    case 5: return go<D, 5>(grid, q, k, v, pa, pm, p, s);
+    case 8: return go<D, 8>(grid, q, k, v, pa, pm, p, s);
+    case 16: return go<D, 16>(grid, q, k, v, pa, pm, p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t RKV_NAME(RKV_KT, RKV_VT)(int d, int rt, dim3 grid, const float *q, const uint8_t *k, const uint8_t *v,
+                                    float *pa, float2 *pm, const SplitParams &p, hipStream_t s)
+{
+    switch (d) {
+    case 64: return by_rt<64>(rt, grid, q, k, v, pa, pm, p, s);
+    case 128: return by_rt<128>(rt, grid, q, k, v, pa, pm, p, s);
+    case 256: return by_rt<256>(rt, grid, q, k, v, pa, pm, p, s);
+    case 512: return by_rt<512>(rt, grid, q, k, v, pa, pm, p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace rkv

@@ -1,0 +1,80 @@
+// common.h -- internal declarations shared by the HIP translation units of
+// librkv.so (kernels, launchers and the C-ABI layer).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rkv.h"
+
+namespace rkv {
+
+constexpr int kF32 = RKV_F32, kF16 = RKV_F16, kQ8 = RKV_Q8_0, kQ4 = RKV_Q4_0;
+
+__host__ __device__ constexpr int row_bytes_of(int t, int d)
+{
+    return t == kF32 ? 4 * d : t == kF16 ? 2 * d : t == kQ8 ? (d / 32) * 34 : t == kQ4 ? (d / 32) * 18 : 0;
+}
+
+// Width in bytes of the vector loads that stage a row: the largest of 16, 8, 4
+// dividing the row size.
+__host__ __device__ constexpr int load_width_of(int t, int d)
+{
+    return row_bytes_of(t, d) % 16 == 0 ? 16 : row_bytes_of(t, d) % 8 == 0 ? 8 : 4;
+}
+
+constexpr int kTile = 64;           // keys per wave tile (one key per lane in the score phase)
+constexpr int kMaxRowTable = 1024;  // entries of the per-KV-head row table
+constexpr int kMaxKvHeads = 64;
+constexpr int kMaxParts = 64;
+
+// Launch parameters of the split (partial) attention kernel.  Byte strides.
+struct SplitParams {
+    int64_t k_pos, v_pos, k_head, v_head, k_seq, v_seq;
+    int64_t n_keys;
+    int32_t keys_per_split;
+    int32_t n_splits;
+    int32_t n_rg;          // row groups per KV head
+    int32_t rows_per_g;    // stride of rowtab between KV heads
+    int32_t n_rows_total;  // n_seq * n_q_heads
+    int32_t z_row_step;    // row offset per blockIdx.z (n_q_heads when sequences have their own keys, else 0)
+    float scale;           // score scale
+    float scale_log2;      // scale * log2(e)
+    float softcap;         // natural units, 0 = off
+    uint16_t rowcnt[kMaxKvHeads];
+    uint16_t rowtab[kMaxRowTable];
+};
+
+// How one segment is cut into work: shared by the workspace query and the launch.
+struct SplitPlan {
+    int rt;          // rows per wave (template instance)
+    int n_rg;        // row groups per KV head
+    int rows_per_g;  // max rows of a KV head
+    int z;           // grid z (sequences with own keys, or 1)
+    int n_splits;
+    int keys_per_split;
+    int64_t n_rows_total;
+    size_t ws_bytes;
+};
+
+// Kernel launchers (attend.hip / combine.hip / dequant.hip).  They enqueue on
+// `stream` and return the hipError_t of the launch.
+hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q, const uint8_t *k,
+                        const uint8_t *v, float *part_acc, float2 *part_ml, const SplitParams &p,
+                        hipStream_t stream);
+bool split_supported(int kt, int vt, int d, int rt);
+hipError_t launch_reduce(int d, int64_t n_rows, int n_splits, const float *part_acc, const float2 *part_ml,
+                         float *o, float *lse, hipStream_t stream);
+hipError_t launch_fill_empty(int d, int64_t n_rows, float *o, float *lse, hipStream_t stream);
+
+struct CombineParts {
+    const float *o[kMaxParts];
+    const float *lse[kMaxParts];
+};
+hipError_t launch_combine(int n_parts, const CombineParts &parts, int64_t n_rows, int d, float *o_out,
+                          float *lse_out, hipStream_t stream);
+
+hipError_t launch_dequant_q8_0(const void *blocks, int64_t n_values, float *out, hipStream_t stream);
+hipError_t launch_dequant_q4_0(const void *blocks, int64_t n_values, float *out, hipStream_t stream);
+
+}  // namespace rkv
