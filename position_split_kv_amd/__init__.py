@@ -14,7 +14,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librkv.so")
+LIB_PATH = os.environ.get("RKV_LIB") or os.path.join(_HERE, "librkv.so")
 
 RKV_F32, RKV_F16, RKV_Q8_0, RKV_Q4_0 = 0, 1, 2, 3
 RKV_OK, RKV_E_INVAL, RKV_E_UNSUPPORTED, RKV_E_HIP, RKV_E_NOMEM, RKV_E_STATE = 0, -1, -2, -3, -4, -5

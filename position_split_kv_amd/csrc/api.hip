@@ -138,19 +138,26 @@ int make_plan(const rkv_attn_desc *d, const rkv_kv_view *v, SplitPlan *pl, Split
     pl->rows_per_g = rmax;
     pl->z = shared ? 1 : S;
     pl->n_rows_total = (int64_t)S * Hq;
+    // Aim at about 2048 waves (two per SIMD of the chip), each with at least
+    // one 64-key tile; a workgroup of nw waves takes a whole number of tiles
+    // per wave.
     const int64_t n_tiles = (v->n_keys + kTile - 1) / kTile;
+    const int64_t nw = std::max(1, split_waves(v->k_type, v->v_type, D));
     const int64_t units = (int64_t)Hkv * pl->n_rg * pl->z;
-    const int64_t want = 2048;
-    int64_t n_splits = std::max<int64_t>(1, std::min<int64_t>(n_tiles, (want + units - 1) / units));
-    int64_t tps = std::max<int64_t>((n_tiles + n_splits - 1) / n_splits, std::min<int64_t>(4, n_tiles));
+    const int64_t want_waves = 2048;
+    int64_t n_splits = std::max<int64_t>(1, (want_waves + units * nw - 1) / (units * nw));
+    n_splits = std::min<int64_t>(n_splits, (n_tiles + nw - 1) / nw);
+    n_splits = std::max<int64_t>(n_splits, 1);
+    int64_t tps = (n_tiles + n_splits - 1) / n_splits;
+    tps = (tps + nw - 1) / nw * nw;
     if (tps * kTile > (1 << 30)) tps = (1 << 30) / kTile;
     n_splits = n_tiles ? (n_tiles + tps - 1) / tps : 0;
     if (n_splits > 65535) return fail(RKV_E_UNSUPPORTED, "segment too long for one launch");
     pl->n_splits = (int)n_splits;
     pl->keys_per_split = (int)(tps * kTile);
     const size_t acc_bytes = (size_t)n_splits * pl->n_rows_total * D * sizeof(float);
-    pl->ws_bytes = n_tiles ? ((acc_bytes + 255) & ~(size_t)255) + (size_t)n_splits * pl->n_rows_total * sizeof(float2)
-                           : 0;
+    pl->ws_bytes = n_splits > 1 ? ((acc_bytes + 255) & ~(size_t)255) + (size_t)n_splits * pl->n_rows_total * sizeof(float2)
+                                : 0;
     if (prm) {
         memset(prm, 0, sizeof *prm);
         prm->k_pos = v->k_pos_stride;
@@ -190,7 +197,7 @@ int attend_impl(const rkv_attn_desc *d, const float *q, const rkv_kv_view *v, fl
     SplitParams prm;
     int rc = make_plan(d, v, &pl, &prm);
     if (rc) return rc;
-    if (ws_bytes < pl.ws_bytes || !ws)
+    if (pl.ws_bytes && (ws_bytes < pl.ws_bytes || !ws))
         return fail(RKV_E_INVAL, "workspace too small: %zu < %zu", ws_bytes, pl.ws_bytes);
     if (!split_supported(v->k_type, v->v_type, d->head_dim, pl.rt))
         return fail(RKV_E_UNSUPPORTED, "no kernel for this (type, head_dim, rows)");
@@ -199,8 +206,8 @@ int attend_impl(const rkv_attn_desc *d, const float *q, const rkv_kv_view *v, fl
     float2 *part_ml = (float2 *)((char *)ws + ((acc_bytes + 255) & ~(size_t)255));
     const dim3 grid((unsigned)pl.n_splits, (unsigned)(d->n_kv_heads * pl.n_rg), (unsigned)pl.z);
     RKV_HIP(launch_split(v->k_type, v->v_type, d->head_dim, pl.rt, grid, q, (const uint8_t *)v->k,
-                         (const uint8_t *)v->v, part_acc, part_ml, prm, stream));
-    RKV_HIP(launch_reduce(d->head_dim, n_rows, pl.n_splits, part_acc, part_ml, o, lse, stream));
+                         (const uint8_t *)v->v, part_acc, part_ml, o, lse, prm, stream));
+    if (pl.n_splits > 1) RKV_HIP(launch_reduce(d->head_dim, n_rows, pl.n_splits, part_acc, part_ml, o, lse, stream));
     return RKV_OK;
 }
 

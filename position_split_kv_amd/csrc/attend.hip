@@ -6,8 +6,9 @@ namespace rkv {
 
 #define RKV_DECL(kt, vt)                                                                                  \
     hipError_t launch_split_k##kt##_v##vt(int d, int rt, dim3 grid, const float *q, const uint8_t *k,     \
-                                          const uint8_t *v, float *pa, float2 *pm, const SplitParams &p,  \
-                                          hipStream_t s);
+                                          const uint8_t *v, float *pa, float2 *pm, float *o, float *lse,  \
+                                          const SplitParams &p, hipStream_t s);                             \
+    int split_waves_k##kt##_v##vt(int d);
 #define RKV_DECL_K(kt) RKV_DECL(kt, 0) RKV_DECL(kt, 1) RKV_DECL(kt, 2) RKV_DECL(kt, 3)
 RKV_DECL_K(0)
 RKV_DECL_K(1)
@@ -22,11 +23,24 @@ bool split_supported(int kt, int vt, int d, int rt)
     return t && dd && r;
 }
 
+int split_waves(int kt, int vt, int d)
+{
+#define RKV_NW(kk, vv) \
+    if (kt == kk && vt == vv) return split_waves_k##kk##_v##vv(d);
+#define RKV_NW_K(kk) RKV_NW(kk, 0) RKV_NW(kk, 1) RKV_NW(kk, 2) RKV_NW(kk, 3)
+    RKV_NW_K(0)
+    RKV_NW_K(1)
+    RKV_NW_K(2)
+    RKV_NW_K(3)
+    return 0;
+}
+
 hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q, const uint8_t *k,
-                        const uint8_t *v, float *pa, float2 *pm, const SplitParams &p, hipStream_t s)
+                        const uint8_t *v, float *pa, float2 *pm, float *o, float *lse, const SplitParams &p,
+                        hipStream_t s)
 {
 #define RKV_CASE(kk, vv) \
-    if (kt == kk && vt == vv) return launch_split_k##kk##_v##vv(d, rt, grid, q, k, v, pa, pm, p, s);
+    if (kt == kk && vt == vv) return launch_split_k##kk##_v##vv(d, rt, grid, q, k, v, pa, pm, o, lse, p, s);
 #define RKV_CASE_K(kk) RKV_CASE(kk, 0) RKV_CASE(kk, 1) RKV_CASE(kk, 2) RKV_CASE(kk, 3)
     RKV_CASE_K(0)
     RKV_CASE_K(1)
@@ -35,39 +49,67 @@ hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q
     return hipErrorInvalidValue;
 }
 
-// One wave per output row: M = max m_i, L = sum l_i 2^(m_i - M),
-// o = sum acc_i 2^(m_i - M) / L, lse = (M + log2 L) ln 2.  Partials are in
-// log2 units; the loop order over ranges is fixed.
+// Merge of the per-range partials of one row (partials are in log2 units):
+// M = max_i m_i, L = sum_i l_i 2^(m_i - M), o = sum_i acc_i 2^(m_i - M) / L,
+// lse = (M + log2 L) ln 2.  One 256-thread block per row: each group of D/4
+// threads (a float4 each) takes every NG-th range, then the groups are summed
+// in a fixed order, so the result is deterministic.
 template <int D>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
 rkv_reduce_kernel(const float *__restrict__ part_acc, const float2 *__restrict__ part_ml, int n_splits,
                   int64_t n_rows, float *__restrict__ o, float *__restrict__ lse)
 {
-    constexpr int DPT = D / 64;
+    constexpr int TPC = D / 4;     // threads per copy of the row
+    constexpr int NG = 256 / TPC;  // groups
+    __shared__ float sM[256];
+    __shared__ float4 sA[NG][TPC];
+    __shared__ float sL[NG];
     const int64_t row = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int t = threadIdx.x, grp = t / TPC, c = t - grp * TPC;
     float M = -INFINITY;
-    for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, part_ml[sp * n_rows + row].x);
-    float L = 0.f, a[DPT];
-#pragma unroll
-    for (int e = 0; e < DPT; ++e) a[e] = 0.f;
-    for (int sp = 0; sp < n_splits; ++sp) {
-        const float2 ml = part_ml[sp * n_rows + row];
-        const float w = exp2f(ml.x - M);
-        L = fmaf(ml.y, w, L);
-        const float *src = part_acc + (sp * n_rows + row) * D + lane * DPT;
-#pragma unroll
-        for (int e = 0; e < DPT; ++e) a[e] = fmaf(src[e], w, a[e]);
+    for (int sp = t; sp < n_splits; sp += 256) M = fmaxf(M, part_ml[sp * n_rows + row].x);
+    sM[t] = M;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (t < off) sM[t] = fmaxf(sM[t], sM[t + off]);
+        __syncthreads();
     }
-#pragma unroll
-    for (int e = 0; e < DPT; ++e) o[row * D + lane * DPT + e] = a[e] / L;
-    if (lane == 0) lse[row] = (M + log2f(L)) * 0.69314718055994531f;
+    M = sM[0];
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
+#pragma unroll 4
+    for (int sp = grp; sp < n_splits; sp += NG) {
+        const float2 ml = part_ml[sp * n_rows + row];
+        const float wgt = exp2f(ml.x - M);
+        const float4 x = *(const float4 *)(part_acc + (sp * n_rows + row) * D + 4 * c);
+        L = fmaf(ml.y, wgt, L);
+        a.x = fmaf(x.x, wgt, a.x);
+        a.y = fmaf(x.y, wgt, a.y);
+        a.z = fmaf(x.z, wgt, a.z);
+        a.w = fmaf(x.w, wgt, a.w);
+    }
+    sA[grp][c] = a;
+    if (c == 0) sL[grp] = L;
+    __syncthreads();
+    if (grp == 0) {
+        float4 s = sA[0][c];
+        float Lt = sL[0];
+        for (int gg = 1; gg < NG; ++gg) {
+            s.x += sA[gg][c].x;
+            s.y += sA[gg][c].y;
+            s.z += sA[gg][c].z;
+            s.w += sA[gg][c].w;
+            Lt += sL[gg];
+        }
+        *(float4 *)(o + row * D + 4 * c) = make_float4(s.x / Lt, s.y / Lt, s.z / Lt, s.w / Lt);
+        if (c == 0) lse[row] = (M + log2f(Lt)) * 0.69314718055994531f;
+    }
 }
 
 hipError_t launch_reduce(int d, int64_t n_rows, int n_splits, const float *pa, const float2 *pm, float *o,
                          float *lse, hipStream_t s)
 {
-    const dim3 grid((unsigned)n_rows), block(64);
+    const dim3 grid((unsigned)n_rows), block(256);
     switch (d) {
     case 64: hipLaunchKernelGGL(rkv_reduce_kernel<64>, grid, block, 0, s, pa, pm, n_splits, n_rows, o, lse); break;
     case 128: hipLaunchKernelGGL(rkv_reduce_kernel<128>, grid, block, 0, s, pa, pm, n_splits, n_rows, o, lse); break;

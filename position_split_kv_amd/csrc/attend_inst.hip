@@ -14,40 +14,53 @@ namespace rkv {
 
 template <int D, int RT>
 static hipError_t go(dim3 grid, const float *q, const uint8_t *k, const uint8_t *v, float *pa, float2 *pm,
-                     const SplitParams &p, hipStream_t stream)
+                     float *o, float *lse, const SplitParams &p, hipStream_t stream)
 {
     if constexpr (D == 512 && (RKV_KT == kF32 || RKV_VT == kF32)) {
         return hipErrorInvalidValue;  // an f32 row of 512 values does not fit the LDS tile
     } else {
-        hipLaunchKernelGGL((rkv_split_kernel<RKV_KT, RKV_VT, D, RT>), grid, dim3(64), 0, stream, q, k, v, pa, pm, p);
+        hipLaunchKernelGGL((rkv_split_kernel<RKV_KT, RKV_VT, D, RT>), grid, dim3(64 * Shape<RKV_KT, RKV_VT, D>::NW), 0,
+                           stream, q, k, v, pa, pm, o, lse, p);
         return hipGetLastError();
     }
 }
 
 template <int D>
 static hipError_t by_rt(int rt, dim3 grid, const float *q, const uint8_t *k, const uint8_t *v, float *pa,
-                        float2 *pm, const SplitParams &p, hipStream_t s)
+                        float2 *pm, float *o, float *lse, const SplitParams &p, hipStream_t s)
 {
     switch (rt) {
-    case 1: return go<D, 1>(grid, q, k, v, pa, pm, p, s);
-    case 2: return go<D, 2>(grid, q, k, v, pa, pm, p, s);
-    case 4: return go<D, 4>(grid, q, k, v, pa, pm, p, s);
-    case 5: return go<D, 5>(grid, q, k, v, pa, pm, p, s);
-    case 8: return go<D, 8>(grid, q, k, v, pa, pm, p, s);
-    case 16: return go<D, 16>(grid, q, k, v, pa, pm, p, s);
+    case 1: return go<D, 1>(grid, q, k, v, pa, pm, o, lse, p, s);
+    case 2: return go<D, 2>(grid, q, k, v, pa, pm, o, lse, p, s);
+    case 4: return go<D, 4>(grid, q, k, v, pa, pm, o, lse, p, s);
+    case 5: return go<D, 5>(grid, q, k, v, pa, pm, o, lse, p, s);
+    case 8: return go<D, 8>(grid, q, k, v, pa, pm, o, lse, p, s);
+    case 16: return go<D, 16>(grid, q, k, v, pa, pm, o, lse, p, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t RKV_NAME(RKV_KT, RKV_VT)(int d, int rt, dim3 grid, const float *q, const uint8_t *k, const uint8_t *v,
-                                    float *pa, float2 *pm, const SplitParams &p, hipStream_t s)
+                                    float *pa, float2 *pm, float *o, float *lse, const SplitParams &p, hipStream_t s)
 {
     switch (d) {
-    case 64: return by_rt<64>(rt, grid, q, k, v, pa, pm, p, s);
-    case 128: return by_rt<128>(rt, grid, q, k, v, pa, pm, p, s);
-    case 256: return by_rt<256>(rt, grid, q, k, v, pa, pm, p, s);
-    case 512: return by_rt<512>(rt, grid, q, k, v, pa, pm, p, s);
+    case 64: return by_rt<64>(rt, grid, q, k, v, pa, pm, o, lse, p, s);
+    case 128: return by_rt<128>(rt, grid, q, k, v, pa, pm, o, lse, p, s);
+    case 256: return by_rt<256>(rt, grid, q, k, v, pa, pm, o, lse, p, s);
+    case 512: return by_rt<512>(rt, grid, q, k, v, pa, pm, o, lse, p, s);
     default: return hipErrorInvalidValue;
+    }
+}
+
+#define RKV_NAME_NW(kt, vt) RKV_CAT4(split_waves_k, kt, _v, vt)
+int RKV_NAME_NW(RKV_KT, RKV_VT)(int d)
+{
+    switch (d) {
+    case 64: return Shape<RKV_KT, RKV_VT, 64>::NW;
+    case 128: return Shape<RKV_KT, RKV_VT, 128>::NW;
+    case 256: return Shape<RKV_KT, RKV_VT, 256>::NW;
+    case 512: return Shape<RKV_KT, RKV_VT, 512>::NW;
+    default: return 0;
     }
 }
 

@@ -1,27 +1,32 @@
 // attend_kernel.h -- split-K flash-decode kernel for one segment of the cache.
 //
-// One wave (64 lanes) = one work item: a KV head g, a group of RT query rows
-// that attend g (all GQA rows of g, and for a segment shared by every
+// A workgroup of NW waves owns one work item: a KV head g, a group of RT query
+// rows that attend g (all GQA rows of g, and for a segment shared by every
 // sequence, those rows of every sequence), and a contiguous range of the
-// segment's keys.  The wave walks its range in tiles of 64 keys:
+// segment's keys.  Wave w walks tiles w, w+NW, w+2NW, ... of the range, 64
+// keys per tile:
 //
 //   1. the K rows of the tile (and V rows when they are block-quantised or
-//      wide) are copied with coalesced vector loads into LDS, row by row, at
-//      an odd dword stride so that one-row-per-lane reads hit distinct banks;
-//      f16 V rows of up to 128 values go straight to registers instead;
+//      wide) are copied with coalesced vector loads into the wave's LDS area,
+//      row by row, at a padded stride so that one-row-per-lane reads do not
+//      collide in LDS banks; f16 V rows of up to 128 values go straight to
+//      registers instead;
 //   2. scores, one key per lane: each lane reads its key's row from LDS,
 //      dequantises it in registers (f32 / f16 / q8_0 / q4_0; the q8_0 / q4_0
 //      block scale is applied once per 32-value partial dot) and takes the
 //      dot product with the RT query rows, whose values are wave-uniform and
-//      live in scalar registers; then scale and the optional softcap;
-//   3. online softmax over the tile: wave max per row, rescale of the running
-//      state, p = 2^(s - m) (scores are kept in log2 units);
+//      stream through scalar registers; then scale and the optional softcap;
+//   3. online softmax over the tile: wave max per row (DPP), rescale of the
+//      running state only when the max moved, p = 2^(s - m) (scores are kept
+//      in log2 units);
 //   4. P.V: lanes are (key-in-step, 8-dim group); each lane accumulates its 8
 //      dims for every row over the tile's keys.
 //
-// At the end of its range the wave writes its partial (m, l, acc[D]) per row;
-// a second, fixed-order pass merges the partials of all ranges (the same
-// LSE arithmetic as the segment combine), so results are deterministic.
+// At the end the NW waves merge their (m, l, acc) in LDS.  A segment handled
+// by one workgroup per item writes its normalised output and LSE directly;
+// otherwise each workgroup writes a partial and a second, fixed-order pass
+// merges them (the same LSE arithmetic as the segment combine), so the
+// results are deterministic.
 //
 // This is the in-register reading of window and tail at their own types that
 // "F5 M7 -- Rolling KV" ships (section "2026-07-12 -- #582-P2 SHIPPED"), with
@@ -35,19 +40,36 @@ namespace rkv {
 
 __host__ __device__ constexpr int odd_dwords(int n) { return (n & 1) ? n : n + 1; }
 
-__device__ __forceinline__ float wave_max(float x)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
-}
+// LDS row stride (dwords) of a staged row of rb bytes: rows that are a
+// multiple of 16 bytes keep 16-byte alignment and get 16 bytes of padding
+// (b128 reads by 16 consecutive lanes then hit distinct banks); other rows get
+// an odd dword count (b32 reads by consecutive lanes hit distinct banks).
+__host__ __device__ constexpr int lds_row_dwords(int rb) { return rb % 16 == 0 ? rb / 4 + 4 : odd_dwords(rb / 4); }
 
-__device__ __forceinline__ float wave_sum(float x)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
+__host__ __device__ constexpr bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+template <int KT, int VT, int D>
+struct Shape {
+    static constexpr int RBK = row_bytes_of(KT, D);
+    static constexpr int RBV = row_bytes_of(VT, D);
+    // f32 / f16 K rows of 128..512 bytes go global -> LDS directly (no staging
+    // registers), packed at RBK bytes with their 16-byte chunks swizzled.
+#ifdef RKV_NO_KDMA
+    static constexpr bool KDMA = false;
+#else
+    static constexpr bool KDMA = (KT == kF32 || KT == kF16) && RBK >= 128 && RBK <= 512 && is_pow2(RBK / 16);
+#endif
+    static constexpr int LSK = KDMA ? RBK / 4 : lds_row_dwords(RBK);
+    static constexpr bool V_REG = (VT == kF16 && D <= 128) || (VT == kF32 && D <= 64);
+    static constexpr int LSV = V_REG ? 0 : lds_row_dwords(RBV);
+    static constexpr int STAGE_DW = kTile * (LSK + LSV) + 8;  // per wave: K (+ V) rows plus read slack
+    // waves per workgroup: as many as fit 160 KiB of LDS with their staging
+    // and score rows (sized for 16 rows per wave)
+    static constexpr int WAVE_BYTES = STAGE_DW * 4 + 16 * kTile * 4;
+    static constexpr int NW = 4 * WAVE_BYTES <= 160 * 1024 ? 4 : 2 * WAVE_BYTES <= 160 * 1024 ? 2 : 1;
+};
+
+// ---------------------------------------------------------------- small helpers
 
 // (hi:lo) >> (8 * sh), low 32 bits.
 __device__ __forceinline__ uint32_t funnel(uint32_t lo, uint32_t hi, uint32_t sh)
@@ -64,6 +86,40 @@ __device__ __forceinline__ float sbyte(uint32_t w, int k) { return (float)(int)(
 
 __device__ __forceinline__ float nib(uint32_t w, int shift) { return (float)((int)((w >> shift) & 0xfu) - 8); }
 
+// One step of a DPP butterfly: x = op(x, x from the lane the control selects),
+// only in the rows of row_mask (other rows keep x).  The s_nop covers the
+// VALU-write-then-DPP-read hazard of the value just computed.
+#define RKV_DPP_MAX(x, ctrl, rmask) \
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 " ctrl " row_mask:" rmask " bank_mask:0xf" : "+v"(x))
+#define RKV_DPP_ADD(x, ctrl, rmask) \
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 " ctrl " row_mask:" rmask " bank_mask:0xf" : "+v"(x))
+
+// Maximum over the 64 lanes, returned wave-uniform.
+__device__ __forceinline__ float wave_max(float x)
+{
+    RKV_DPP_MAX(x, "quad_perm:[1,0,3,2]", "0xf");
+    RKV_DPP_MAX(x, "quad_perm:[2,3,0,1]", "0xf");
+    RKV_DPP_MAX(x, "row_half_mirror", "0xf");
+    RKV_DPP_MAX(x, "row_mirror", "0xf");
+    RKV_DPP_MAX(x, "row_bcast:15", "0xa");
+    RKV_DPP_MAX(x, "row_bcast:31", "0xc");
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// Sum over the 64 lanes, returned wave-uniform.
+__device__ __forceinline__ float wave_sum(float x)
+{
+    RKV_DPP_ADD(x, "quad_perm:[1,0,3,2]", "0xf");
+    RKV_DPP_ADD(x, "quad_perm:[2,3,0,1]", "0xf");
+    RKV_DPP_ADD(x, "row_half_mirror", "0xf");
+    RKV_DPP_ADD(x, "row_mirror", "0xf");
+    RKV_DPP_ADD(x, "row_bcast:15", "0xa");
+    RKV_DPP_ADD(x, "row_bcast:31", "0xc");
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// ---------------------------------------------------------------- staging
+
 // Copy the rows of a tile (row i of RB bytes at src + i*pos_stride) into LDS
 // at a stride of LS dwords, with VW-byte loads, in rounds of at most 32 loads
 // per lane that are all in flight before the round's LDS stores.  Rows past
@@ -78,13 +134,13 @@ __device__ __forceinline__ void stage_rows(const uint8_t *__restrict__ src, int 
     asm volatile("" : "+s"(pos_stride));
     constexpr int CPR = RB / VW;
     constexpr int NCH = kTile * CPR;  // a multiple of 64
-    constexpr int NW = VW / 4;
+    constexpr int NWD = VW / 4;
     constexpr int IT = NCH / 64;
     constexpr int ROUND = IT < 32 ? IT : 32;
     static_assert(NCH % 64 == 0, "tile chunks must fill whole waves");
 #pragma unroll
     for (int it0 = 0; it0 < IT; it0 += ROUND) {
-        uint32_t buf[ROUND][NW];
+        uint32_t buf[ROUND][NWD];
 #pragma unroll
         for (int i = 0; i < ROUND; ++i) {
             const int c = lane + 64 * (it0 + i);
@@ -92,10 +148,10 @@ __device__ __forceinline__ void stage_rows(const uint8_t *__restrict__ src, int 
             const int rowc = row < nk ? row : nk - 1;
             if (it0 + i < IT) {
                 const uint8_t *p = src + (uint32_t)(rowc * pos_stride + col * VW);
-                if constexpr (NW == 4) {
+                if constexpr (NWD == 4) {
                     uint4 x = *(const uint4 *)p;
                     buf[i][0] = x.x; buf[i][1] = x.y; buf[i][2] = x.z; buf[i][3] = x.w;
-                } else if constexpr (NW == 2) {
+                } else if constexpr (NWD == 2) {
                     uint2 x = *(const uint2 *)p;
                     buf[i][0] = x.x; buf[i][1] = x.y;
                 } else {
@@ -108,33 +164,171 @@ __device__ __forceinline__ void stage_rows(const uint8_t *__restrict__ src, int 
             const int c = lane + 64 * (it0 + i);
             const int row = c / CPR, col = c - (c / CPR) * CPR;
             if (it0 + i < IT) {
+                uint32_t *dst = lds + row * LS + col * NWD;
+                if constexpr (NWD == 4 && LS % 4 == 0) {
+                    *(uint4 *)dst = make_uint4(buf[i][0], buf[i][1], buf[i][2], buf[i][3]);
+                } else {
 #pragma unroll
-                for (int e = 0; e < NW; ++e) lds[row * LS + col * NW + e] = buf[i][e];
+                    for (int e = 0; e < NWD; ++e) dst[e] = buf[i][e];
+                }
             }
         }
     }
 }
 
+// The raw bytes of a tile's rows held in registers between their global
+// loads and their LDS stores: chunk c = lane + 64*i of VW bytes, row c / CPR.
+template <int RB, int VW>
+struct RowRegs {
+    static constexpr int CPR = RB / VW, NWD = VW / 4, IT = kTile * CPR / 64;
+    uint32_t d[IT][NWD];
+};
+
+// Issue the loads of a tile's rows (rows past nk repeat row nk-1, so no load
+// is predicated).
+template <int RB, int VW>
+__device__ __forceinline__ void load_rows(RowRegs<RB, VW> &R, const uint8_t *__restrict__ src, int pos_stride,
+                                          int nk, int lane)
+{
+    using T = RowRegs<RB, VW>;
+    asm volatile("" : "+s"(pos_stride));
+#pragma unroll
+    for (int i = 0; i < T::IT; ++i) {
+        const int c = lane + 64 * i;
+        const int row = c / T::CPR, col = c - (c / T::CPR) * T::CPR;
+        const int rowc = row < nk ? row : nk - 1;
+        const uint8_t *ptr = src + (uint32_t)(rowc * pos_stride + col * VW);
+        if constexpr (T::NWD == 4) {
+            const uint4 x = *(const uint4 *)ptr;
+            R.d[i][0] = x.x; R.d[i][1] = x.y; R.d[i][2] = x.z; R.d[i][3] = x.w;
+        } else if constexpr (T::NWD == 2) {
+            const uint2 x = *(const uint2 *)ptr;
+            R.d[i][0] = x.x; R.d[i][1] = x.y;
+        } else {
+            R.d[i][0] = *(const uint32_t *)ptr;
+        }
+    }
+}
+
+// Store loaded rows to LDS at a stride of LS dwords.
+template <int RB, int VW, int LS>
+__device__ __forceinline__ void store_rows(const RowRegs<RB, VW> &R, uint32_t *lds, int lane)
+{
+    using T = RowRegs<RB, VW>;
+#pragma unroll
+    for (int i = 0; i < T::IT; ++i) {
+        const int c = lane + 64 * i;
+        const int row = c / T::CPR, col = c - (c / T::CPR) * T::CPR;
+        uint32_t *dst = lds + row * LS + col * T::NWD;
+        if constexpr (T::NWD == 4 && LS % 4 == 0) {
+            *(uint4 *)dst = make_uint4(R.d[i][0], R.d[i][1], R.d[i][2], R.d[i][3]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < T::NWD; ++e) dst[e] = R.d[i][e];
+        }
+    }
+}
+
+// Chunk swizzle of a DMA-staged K row: chunk c of row j sits in slot
+// c ^ kswz(j).  It makes the 16-byte reads of one chunk by 16 consecutive
+// lanes (one row each) hit 16 distinct 4-bank groups.
+template <int RB>
+__device__ __forceinline__ int kswz(int j)
+{
+    return RB == 128 ? ((j >> 1) & 7) : (j & 15);
+}
+
+// ---------------------------------------------------------------- dma k rows
+
+// QC dims [d0, d0 + QC) of row j of a DMA-staged f32 / f16 K tile.
+template <int KT, int RB, int QC>
+__device__ __forceinline__ void k_chunk_dma(const uint32_t *tile, int j, int sw, int d0, float *k)
+{
+    constexpr int EPC = KT == kF16 ? 8 : 4;  // elements per 16-byte chunk
+    const uint32_t *row = tile + j * (RB / 4);
+    if constexpr (QC >= EPC) {
+#pragma unroll
+        for (int cc = 0; cc < QC / EPC; ++cc) {
+            const uint4 w = *(const uint4 *)(row + 4 * (((d0 / EPC) + cc) ^ sw));
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+            if constexpr (KT == kF16) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    k[cc * 8 + 2 * e] = h2f(ww[e]);
+                    k[cc * 8 + 2 * e + 1] = h2f(ww[e] >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) k[cc * 4 + e] = __builtin_bit_cast(float, ww[e]);
+            }
+        }
+    } else {
+        // part of one chunk: the dword offset inside it
+        const int inner = (d0 % EPC) / (KT == kF16 ? 2 : 1);
+        const uint32_t *cp = row + 4 * ((d0 / EPC) ^ sw) + inner;
+        if constexpr (KT == kF16) {
+            if constexpr (QC == 4) {
+                const uint2 w = *(const uint2 *)cp;
+                k[0] = h2f(w.x); k[1] = h2f(w.x >> 16); k[2] = h2f(w.y); k[3] = h2f(w.y >> 16);
+            } else if constexpr (QC == 2) {
+                const uint32_t w = *cp;
+                k[0] = h2f(w); k[1] = h2f(w >> 16);
+            } else {
+                const uint32_t w = *cp;
+                k[0] = (d0 & 1) ? h2f(w >> 16) : h2f(w);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < QC; ++e) k[e] = __builtin_bit_cast(float, cp[e]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- scores
+
 // QC consecutive dims [d0, d0 + QC) of this lane's K row in LDS as floats
 // (block types: the codes, without the block scale).  QC is 1, 2, 4 or 8 and
-// d0 a multiple of QC, so a chunk never straddles a 32-value block.
+// d0 a multiple of QC, so a chunk never straddles a 32-value block.  Rows of
+// f32 / f16 start 16-byte aligned in LDS.
 template <int KT, int QC>
 __device__ __forceinline__ void k_chunk(const uint32_t *row, int d0, float *k)
 {
     if constexpr (KT == kF32) {
+        if constexpr (QC % 4 == 0) {
 #pragma unroll
-        for (int e = 0; e < QC; ++e) k[e] = __builtin_bit_cast(float, row[d0 + e]);
-    } else if constexpr (KT == kF16) {
-        if constexpr (QC == 1) {
-            const uint32_t w = row[d0 / 2];
-            k[0] = (d0 & 1) ? h2f(w >> 16) : h2f(w);
+            for (int j = 0; j < QC / 4; ++j) {
+                const uint4 w = *(const uint4 *)(row + d0 + 4 * j);
+                k[4 * j] = __builtin_bit_cast(float, w.x);
+                k[4 * j + 1] = __builtin_bit_cast(float, w.y);
+                k[4 * j + 2] = __builtin_bit_cast(float, w.z);
+                k[4 * j + 3] = __builtin_bit_cast(float, w.w);
+            }
         } else {
 #pragma unroll
-            for (int e = 0; e < QC / 2; ++e) {
-                const uint32_t w = row[d0 / 2 + e];
-                k[2 * e] = h2f(w);
-                k[2 * e + 1] = h2f(w >> 16);
+            for (int e = 0; e < QC; ++e) k[e] = __builtin_bit_cast(float, row[d0 + e]);
+        }
+    } else if constexpr (KT == kF16) {
+        if constexpr (QC == 8) {
+            const uint4 w = *(const uint4 *)(row + d0 / 2);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                k[2 * e] = h2f(ww[e]);
+                k[2 * e + 1] = h2f(ww[e] >> 16);
             }
+        } else if constexpr (QC == 4) {
+            const uint2 w = *(const uint2 *)(row + d0 / 2);
+            k[0] = h2f(w.x);
+            k[1] = h2f(w.x >> 16);
+            k[2] = h2f(w.y);
+            k[3] = h2f(w.y >> 16);
+        } else if constexpr (QC == 2) {
+            const uint32_t w = row[d0 / 2];
+            k[0] = h2f(w);
+            k[1] = h2f(w >> 16);
+        } else {
+            const uint32_t w = row[d0 / 2];
+            k[0] = (d0 & 1) ? h2f(w >> 16) : h2f(w);
         }
     } else {
         // q8_0: element c of block bb is byte 34*bb + 2 + c.
@@ -167,18 +361,20 @@ __device__ __forceinline__ float k_scale(const uint32_t *row, int bb)
 }
 
 // QC query values of every row, dims [d0, d0 + QC), into scalar registers.
-// The offset passes through an empty asm so that the compiler treats each
+// The byte offset passes through an empty asm so that the compiler treats each
 // chunk's loads as new: without it, the loads of all RT * head_dim values are
-// hoisted out of the key loop and spill.
+// hoisted out of the key loop and spill.  (Laundering the row pointers
+// instead would hide that they point at read-only kernel-argument memory,
+// and the loads would no longer be scalar.)
 template <int RT, int QC>
-__device__ __forceinline__ void q_chunk(const float *q, const int *qoff, int d0, float (*qv)[QC])
+__device__ __forceinline__ void q_chunk(const float *const *qp, int d0, float (*qv)[QC])
 {
-    int o = d0;
-    asm volatile("" : "+s"(o));
+    uint32_t ob = 4u * (uint32_t)d0;
+    asm volatile("" : "+s"(ob));
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int e = 0; e < QC; ++e) qv[r][e] = q[qoff[r] + o + e];
+        for (int e = 0; e < QC; ++e) qv[r][e] = *(const float *)((const char *)qp[r] + ob + 4 * e);
 }
 
 // Empty asm statements that pin values in place: the compiler may not move a
@@ -202,8 +398,8 @@ __device__ __forceinline__ void pin_v(float *v)
 // loads of chunk i+1 are issued before the multiply-adds of chunk i, and the
 // pins keep at most two chunks (2 * RT * QC scalar registers) live.  Block
 // types apply their scale once per 32-value partial dot.
-template <int KT, int D, int RT>
-__device__ __forceinline__ void key_dots(const uint32_t *row, const float *q, const int *qoff, float *s)
+template <int KT, int D, int RT, bool KDMA = false>
+__device__ __forceinline__ void key_dots(const uint32_t *row, const float *const *qp, float *s, int j = 0, int sw = 0)
 {
     constexpr int QC = RT >= 16 ? 1 : RT >= 8 ? 2 : RT >= 4 ? 4 : 8;
     constexpr int CPB = 32 / QC;  // chunks per 32-value block
@@ -217,13 +413,15 @@ __device__ __forceinline__ void key_dots(const uint32_t *row, const float *q, co
         float qa[RT][QC], qb[RT][QC], ka[QC], kb[QC], t[RT];
 #pragma unroll
         for (int r = 0; r < RT; ++r) t[r] = 0.f;
-        q_chunk<RT, QC>(q, qoff, 32 * bb, qa);
-        k_chunk<KT, QC>(row, 32 * bb, ka);
+        q_chunk<RT, QC>(qp, 32 * bb, qa);
+        if constexpr (KDMA) k_chunk_dma<KT, row_bytes_of(KT, D), QC>(row, j, sw, 32 * bb, ka);
+        else k_chunk<KT, QC>(row, 32 * bb, ka);
 #pragma unroll
         for (int ci = 0; ci < CPB; ++ci) {
             if (ci + 1 < CPB) {
-                q_chunk<RT, QC>(q, qoff, 32 * bb + QC * (ci + 1), qb);
-                k_chunk<KT, QC>(row, 32 * bb + QC * (ci + 1), kb);
+                q_chunk<RT, QC>(qp, 32 * bb + QC * (ci + 1), qb);
+                if constexpr (KDMA) k_chunk_dma<KT, row_bytes_of(KT, D), QC>(row, j, sw, 32 * bb + QC * (ci + 1), kb);
+                else k_chunk<KT, QC>(row, 32 * bb + QC * (ci + 1), kb);
             }
             pin_s<RT * QC>(&qa[0][0]);
 #pragma unroll
@@ -249,21 +447,27 @@ __device__ __forceinline__ void key_dots(const uint32_t *row, const float *q, co
     }
 }
 
+// ---------------------------------------------------------------- values
+
 // 8 consecutive values (dims 8*dg .. 8*dg+7) of a V row held in LDS, as
 // floats, plus the block scale they must be multiplied by (1 for f32/f16).
 template <int VT, int D>
 __device__ __forceinline__ float v_group_lds(const uint32_t *row, int dg, float *x)
 {
     if constexpr (VT == kF32) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = __builtin_bit_cast(float, row[8 * dg + e]);
+        const uint4 a = *(const uint4 *)(row + 8 * dg), b = *(const uint4 *)(row + 8 * dg + 4);
+        x[0] = __builtin_bit_cast(float, a.x); x[1] = __builtin_bit_cast(float, a.y);
+        x[2] = __builtin_bit_cast(float, a.z); x[3] = __builtin_bit_cast(float, a.w);
+        x[4] = __builtin_bit_cast(float, b.x); x[5] = __builtin_bit_cast(float, b.y);
+        x[6] = __builtin_bit_cast(float, b.z); x[7] = __builtin_bit_cast(float, b.w);
         return 1.f;
     } else if constexpr (VT == kF16) {
+        const uint4 w = *(const uint4 *)(row + 4 * dg);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const uint32_t w = row[4 * dg + e];
-            x[2 * e] = h2f(w);
-            x[2 * e + 1] = h2f(w >> 16);
+            x[2 * e] = h2f(ww[e]);
+            x[2 * e + 1] = h2f(ww[e] >> 16);
         }
         return 1.f;
     } else if constexpr (VT == kQ8) {
@@ -300,28 +504,35 @@ __device__ __forceinline__ float v_group_lds(const uint32_t *row, int dg, float 
     }
 }
 
+// ---------------------------------------------------------------- the kernel
+
 template <int KT, int VT, int D, int RT>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__((64 * Shape<KT, VT, D>::NW))
 rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase, const uint8_t *__restrict__ vbase,
-                 float *__restrict__ part_acc, float2 *__restrict__ part_ml, const SplitParams p)
+                 float *__restrict__ part_acc, float2 *__restrict__ part_ml, float *__restrict__ o_out,
+                 float *__restrict__ lse_out, const SplitParams p)
 {
-    constexpr int RBK = row_bytes_of(KT, D);
-    constexpr int RBV = row_bytes_of(VT, D);
+    using Sh = Shape<KT, VT, D>;
+    constexpr int NW = Sh::NW;
+    constexpr int LSK = Sh::LSK, LSV = Sh::LSV;
+    constexpr bool V_REG = Sh::V_REG;
     constexpr int VWK = load_width_of(KT, D);
     constexpr int VWV = load_width_of(VT, D);
-    constexpr int LSK = odd_dwords(RBK / 4);
     constexpr int LPR = D / 8;      // lanes per V row in the P.V phase
     constexpr int KPS = 64 / LPR;   // keys per P.V step
     constexpr int NSTEP = kTile / KPS;
-    constexpr bool V_REG = (VT == kF16 && D <= 128) || (VT == kF32 && D <= 64);
-    constexpr int LSV = V_REG ? 1 : odd_dwords(RBV / 4);
     constexpr int VRW = VT == kF32 ? 8 : 4;  // dwords of one lane's 8 values, register path
+    constexpr int MERGE_DW = NW * RT * (D + 2);
+    constexpr int SMEM_DW = NW * Sh::STAGE_DW > MERGE_DW ? NW * Sh::STAGE_DW : MERGE_DW;
 
-    __shared__ uint32_t sK[kTile * LSK + 4];
-    __shared__ uint32_t sV[V_REG ? 1 : kTile * LSV + 4];
-    __shared__ float sP[RT * kTile];
+    __shared__ __attribute__((aligned(16))) uint32_t smem[SMEM_DW];
+    __shared__ float sP[NW][RT * kTile];
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    uint32_t *sK = smem + w * Sh::STAGE_DW;
+    uint32_t *sV = sK + kTile * LSK;
+
     const int g = blockIdx.y / p.n_rg;
     const int rg = blockIdx.y - g * p.n_rg;
     const int cnt = (int)p.rowcnt[g] - rg * RT;
@@ -334,12 +545,13 @@ rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase,
     const uint8_t *kg = kbase + z * p.k_seq + g * p.k_head;
     const uint8_t *vg = vbase + z * p.v_seq + g * p.v_head;
 
-    int rid[RT], qoff[RT];
+    int rid[RT];
+    const float *qp[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
         const int rr = r < nr ? r : nr - 1;  // padding rows repeat the last row; never written
         rid[r] = z * p.z_row_step + p.rowtab[g * p.rows_per_g + rg * RT + rr];
-        qoff[r] = rid[r] * D;
+        qp[r] = q + rid[r] * D;
     }
 
     float m[RT], l[RT], acc[RT][8];
@@ -357,34 +569,108 @@ rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase,
     const float cap = p.softcap;
     constexpr float kLog2e = 1.4426950408889634f;
 
-    for (int64_t t0 = kbeg; t0 < kend; t0 += kTile) {
-        const int nk = (int)(kend - t0 < kTile ? kend - t0 : kTile);
-
-        uint32_t vreg[V_REG ? NSTEP : 1][V_REG ? VRW : 1];
-        if constexpr (V_REG) {
-            int vps = (int)p.v_pos;
-            asm volatile("" : "+s"(vps));
-            const uint8_t *vt = vg + t0 * p.v_pos;
+    // Software pipelining of the tile stream: when the raw rows of a tile fit
+    // in registers, the loads of tile i+1's K (and block-type V) rows are
+    // issued once tile i's scores are done (its K rows in LDS are no longer
+    // needed after the next store), and the loads of tile i+1's register-held
+    // V rows right after tile i's P.V, so a wave keeps its next tile in
+    // flight while it computes, with at most one tile of raw rows in registers
+    // beside the P.V working set.
+    using KRegs = RowRegs<Sh::RBK, VWK>;
+    using VRegs = RowRegs<Sh::RBV, VWV>;
+    constexpr int RAW_DW = KRegs::IT * KRegs::NWD + (V_REG ? NSTEP * VRW : VRegs::IT * VRegs::NWD);
+#ifdef RKV_NO_PIPE
+    constexpr bool PIPE = false;
+#else
+    constexpr bool PIPE = !Sh::KDMA && RAW_DW <= 64;
+#endif
+    KRegs kr;
+    VRegs vr;
+    uint32_t vreg[V_REG ? NSTEP : 1][VRW];
+    int vps = (int)p.v_pos;
+    asm volatile("" : "+s"(vps));
+    auto load_vreg = [&](int64_t t, int nkk) {
+        if constexpr (!V_REG) return;
+        const uint8_t *vt = vg + t * p.v_pos;
 #pragma unroll
-            for (int st = 0; st < NSTEP; ++st) {
-                const int key = st * KPS + ks;
-                const int keyc = key < nk ? key : nk - 1;  // masked in P.V
-                const uint8_t *pv = vt + (uint32_t)(keyc * vps + dg * (VRW * 4));
-                const uint4 a = *(const uint4 *)pv;
-                vreg[st][0] = a.x; vreg[st][1] = a.y; vreg[st][2] = a.z; vreg[st][3] = a.w;
-                if constexpr (VRW == 8) {
-                    const uint4 b = *(const uint4 *)(pv + 16);
-                    vreg[st][4] = b.x; vreg[st][5] = b.y; vreg[st][6] = b.z; vreg[st][7] = b.w;
-                }
+        for (int st = 0; st < NSTEP; ++st) {
+            const int key = st * KPS + ks;
+            const int keyc = key < nkk ? key : nkk - 1;  // weight 0 in P.V, finite data
+            const uint8_t *pv = vt + (uint32_t)(keyc * vps + dg * (VRW * 4));
+            const uint4 a = *(const uint4 *)pv;
+            uint32_t *vr8 = &vreg[st][0];
+            vr8[0] = a.x; vr8[1] = a.y; vr8[2] = a.z; vr8[3] = a.w;
+            if constexpr (VRW == 8) {
+                const uint4 b = *(const uint4 *)(pv + 16);
+                vr8[4] = b.x; vr8[5] = b.y; vr8[6] = b.z; vr8[7] = b.w;
             }
         }
-        stage_rows<RBK, VWK, LSK>(kg + t0 * p.k_pos, (int)p.k_pos, nk, sK, lane);
-        if constexpr (!V_REG) stage_rows<RBV, VWV, LSV>(vg + t0 * p.v_pos, (int)p.v_pos, nk, sV, lane);
-        __syncthreads();
+    };
+    auto nk_at = [&](int64_t t) { return (int)(kend - t < kTile ? kend - t : kTile); };
+
+    constexpr bool KDMA = Sh::KDMA;
+    // Issue the direct global -> LDS loads of a tile's K rows (rows past nkk
+    // repeat row nkk-1).  Lane l of load i fills slot i*64 + l of the tile.
+    auto dma_k = [&](int64_t t, int nkk) {
+        if constexpr (KDMA) {
+            constexpr int CPR = Sh::RBK / 16;
+            constexpr int NI = kTile * Sh::RBK / 1024;
+            int kps = (int)p.k_pos;
+            asm volatile("" : "+s"(kps));
+            const uint8_t *kt = kg + t * p.k_pos;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int slot = i * 64 + lane;
+                const int j = slot / CPR, cs = slot % CPR;
+                const int c = cs ^ kswz<Sh::RBK>(j);
+                const int jc = j < nkk ? j : nkk - 1;
+#if defined(__HIP_DEVICE_COMPILE__)  // a device-only builtin: the host pass only needs the kernel's signature
+                __builtin_amdgcn_global_load_lds((const void *)(kt + (uint32_t)(jc * kps + 16 * c)),
+                                                 smem + w * Sh::STAGE_DW + i * 256, 16, 0, 0);
+#else
+                (void)jc; (void)c; (void)kt;
+#endif
+            }
+        }
+    };
+    const int sw = kswz<Sh::RBK>(lane);
+
+    int64_t t0 = kbeg + (int64_t)w * kTile;
+    if constexpr (KDMA) {
+        if (t0 < kend) {
+            dma_k(t0, nk_at(t0));
+        }
+    } else if constexpr (PIPE) {
+        if (t0 < kend) {
+            load_rows(kr, kg + t0 * p.k_pos, (int)p.k_pos, nk_at(t0), lane);
+            if constexpr (V_REG) load_vreg(t0, nk_at(t0));
+            else load_rows(vr, vg + t0 * p.v_pos, (int)p.v_pos, nk_at(t0), lane);
+        }
+    }
+    for (; t0 < kend; t0 += (int64_t)NW * kTile) {
+        const int nk = nk_at(t0);
+        const int64_t tn = t0 + (int64_t)NW * kTile;
+        if constexpr (KDMA) {
+            // K rows arrive by DMA issued one tile ahead; V rows load now and
+            // are in flight during the scores (holding two tiles of V in
+            // registers would halve the occupancy).
+            if constexpr (V_REG) load_vreg(t0, nk);
+            if constexpr (!V_REG) stage_rows<Sh::RBV, VWV, LSV>(vg + t0 * p.v_pos, (int)p.v_pos, nk, sV, lane);
+        } else if constexpr (PIPE) {
+            store_rows<Sh::RBK, VWK, LSK>(kr, sK, lane);
+            if constexpr (!V_REG) store_rows<Sh::RBV, VWV, LSV>(vr, sV, lane);
+        } else {
+            if constexpr (V_REG) load_vreg(t0, nk);
+            stage_rows<Sh::RBK, VWK, LSK>(kg + t0 * p.k_pos, (int)p.k_pos, nk, sK, lane);
+            if constexpr (!V_REG) stage_rows<Sh::RBV, VWV, LSV>(vg + t0 * p.v_pos, (int)p.v_pos, nk, sV, lane);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS stores are done
+        __builtin_amdgcn_wave_barrier();
 
         // ---- scores, one key per lane
         float s[RT];
-        key_dots<KT, D, RT>(sK + lane * LSK, q, qoff, s);
+        if constexpr (KDMA) key_dots<KT, D, RT, true>(sK, qp, s, lane, sw);
+        else key_dots<KT, D, RT>(sK + lane * LSK, qp, s);
         const bool valid = lane < nk;
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
@@ -396,26 +682,38 @@ rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase,
             s[r] = valid ? x : -INFINITY;
         }
 
-        // ---- online softmax update
+        // ---- online softmax update (rescale only when a row's max moved)
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
-            const float mt = wave_max(s[r]);
-            const float mn = fmaxf(m[r], mt);
-            const float alpha = exp2f(m[r] - mn);
-            const float pr = exp2f(s[r] - mn);
-            l[r] = l[r] * alpha + pr;
-            m[r] = mn;
+            const float mn = fmaxf(m[r], wave_max(s[r]));
+            if (mn > m[r]) {
+                const float alpha = __builtin_amdgcn_exp2f(m[r] - mn);
+                l[r] *= alpha;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
-            sP[r * kTile + lane] = pr;
+                for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+                m[r] = mn;
+            }
+            const float pr = __builtin_amdgcn_exp2f(s[r] - m[r]);
+            l[r] += pr;
+            sP[w][r * kTile + lane] = pr;
         }
-        __syncthreads();
+        // the next tile's K (and block-type V) rows load during this tile's P.V
+        if constexpr (KDMA) {
+            if (tn < kend) dma_k(tn, nk_at(tn));
+        } else if constexpr (PIPE) {
+            if (tn < kend) {
+                load_rows(kr, kg + tn * p.k_pos, (int)p.k_pos, nk_at(tn), lane);
+                if constexpr (!V_REG) load_rows(vr, vg + tn * p.v_pos, (int)p.v_pos, nk_at(tn), lane);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
 
-        // ---- P.V (fully unrolled when V sits in registers: vreg is indexed by st)
+        // ---- P.V (fully unrolled when V sits in registers: vreg is indexed by st).
+        // Keys past nk have weight 0 and finite (repeated) data.
 #pragma unroll V_REG ? NSTEP : 4
         for (int st = 0; st < NSTEP; ++st) {
             const int key = st * KPS + ks;
-            const bool kv = key < nk;
             float x[8];
             float dsc;
             if constexpr (V_REG) {
@@ -434,38 +732,75 @@ rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase,
                 dsc = v_group_lds<VT, D>(sV + key * LSV, dg, x);
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = kv ? x[e] : 0.f;
-            dsc = kv ? dsc : 0.f;
-#pragma unroll
             for (int r = 0; r < RT; ++r) {
-                const float pw = sP[r * kTile + key] * dsc;
+                const float pw = (VT == kQ8 || VT == kQ4) ? sP[w][r * kTile + key] * dsc : sP[w][r * kTile + key];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pw, x[e], acc[r][e]);
             }
         }
-        __syncthreads();
+        if constexpr (PIPE && V_REG) {
+            if (tn < kend) load_vreg(tn, nk_at(tn));
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
     }
 
-    // ---- partial of this key range
+    // ---- merge the waves of the workgroup in LDS.  Per wave and row: m, l,
+    // and acc[D] summed over the wave's key-in-step lane groups.
 #pragma unroll
     for (int r = 0; r < RT; ++r) l[r] = wave_sum(l[r]);
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-        for (int r = 0; r < RT; ++r)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[r][e] += __shfl_xor(acc[r][e], off);
-    }
-    const int64_t base = (int64_t)blockIdx.x * p.n_rows_total;
+    __syncthreads();  // every wave is done with its staging area
+    float *mA = (float *)smem;                  // [NW][RT][D]
+    float *mML = mA + NW * RT * D;              // [NW][RT][2]
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-        if (r < nr) {
-            if (ks == 0) {
-                float4 *dst = (float4 *)(part_acc + (base + rid[r]) * D + dg * 8);
-                dst[0] = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
-                dst[1] = make_float4(acc[r][4], acc[r][5], acc[r][6], acc[r][7]);
-            }
-            if (lane == 0) part_ml[base + rid[r]] = make_float2(m[r], l[r]);
+        if (ks == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mA[(w * RT + r) * D + dg * 8 + e] = acc[r][e];
+        }
+        if (lane == 0) {
+            mML[(w * RT + r) * 2] = m[r];
+            mML[(w * RT + r) * 2 + 1] = l[r];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 1; kk < KPS; ++kk) {
+        if (ks == kk) {
+#pragma unroll
+            for (int r = 0; r < RT; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) mA[(w * RT + r) * D + dg * 8 + e] += acc[r][e];
+        }
+        __syncthreads();
+    }
+    // Thread t finalises (row r, dim d) pairs; a wave with no keys has m = -inf
+    // and weight 0.
+    const bool single = p.n_splits == 1;
+    const int64_t pbase = (int64_t)blockIdx.x * p.n_rows_total;
+    for (int i = threadIdx.x; i < nr * D; i += 64 * NW) {
+        const int r = i / D, d = i - r * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mML[(ww * RT + r) * 2]);
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            const float mw = mML[(ww * RT + r) * 2];
+            const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+            L = fmaf(mML[(ww * RT + r) * 2 + 1], f, L);
+            A = fmaf(mA[(ww * RT + r) * D + d], f, A);
+        }
+        int rr = 0;
+#pragma unroll
+        for (int x = 0; x < RT; ++x)
+            if (x == r) rr = rid[x];
+        if (single) {
+            o_out[(int64_t)rr * D + d] = A / L;
+            if (d == 0) lse_out[rr] = (M + log2f(L)) * 0.69314718055994531f;
+        } else {
+            part_acc[(pbase + rr) * D + d] = A;
+            if (d == 0) part_ml[pbase + rr] = make_float2(M, L);
         }
     }
 }

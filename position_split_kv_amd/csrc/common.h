@@ -59,10 +59,14 @@ struct SplitPlan {
 
 // Kernel launchers (attend.hip / combine.hip / dequant.hip).  They enqueue on
 // `stream` and return the hipError_t of the launch.
+// One launch of the split kernel over `grid` work items.  With one split per
+// item (p.n_splits == 1) it writes o / lse directly, else the partials.
 hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q, const uint8_t *k,
-                        const uint8_t *v, float *part_acc, float2 *part_ml, const SplitParams &p,
-                        hipStream_t stream);
+                        const uint8_t *v, float *part_acc, float2 *part_ml, float *o, float *lse,
+                        const SplitParams &p, hipStream_t stream);
 bool split_supported(int kt, int vt, int d, int rt);
+// Waves per workgroup of the split kernel for a (K type, V type, head_dim).
+int split_waves(int kt, int vt, int d);
 hipError_t launch_reduce(int d, int64_t n_rows, int n_splits, const float *part_acc, const float2 *part_ml,
                          float *o, float *lse, hipStream_t stream);
 hipError_t launch_fill_empty(int d, int64_t n_rows, float *o, float *lse, hipStream_t stream);

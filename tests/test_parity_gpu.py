@@ -194,7 +194,7 @@ def test_shared_prefix_batch():
 
 
 def test_errors_on_device():
-    D, Hq, Hkv, n = 128, 8, 2, 100
+    D, Hq, Hkv, n = 128, 8, 2, 20000  # long enough to need a workspace
     kc, vc = pair(n, Hkv, D, synth.F16, synth.F16, 5, DEV)
     q = synth.make_query(1, Hq, D, 6, DEV)
     desc = P.Desc(1, Hq, Hkv, D, 0.1)
@@ -214,6 +214,7 @@ def test_errors_on_device():
         P.rkv_attend_segment(desc, q, P.view_of_cache(kh, vc), o, l, ws)
     assert e.value.code == P.RKV_E_INVAL
     # nothing was enqueued by the failing calls; a good call still works
+    assert ws.numel() > 16
     P.rkv_attend_segment(desc, q, view, o, l, ws)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all()
