@@ -115,7 +115,9 @@ typedef struct rkv_attn_desc {
 } rkv_attn_desc;
 
 /* Workspace bytes rkv_attend_segment needs for this problem and segment
- * (written to *bytes; 0 for an empty segment). */
+ * (written to *bytes; 0 when no workspace is needed).  The workspace holds
+ * per-split partial results; its contents need no initialisation.  Calls
+ * that overlap in time must not share a workspace. */
 int rkv_attend_workspace_bytes(const rkv_attn_desc *desc, const rkv_kv_view *seg, size_t *bytes);
 
 /*
@@ -135,6 +137,30 @@ int rkv_attend_workspace_bytes(const rkv_attn_desc *desc, const rkv_kv_view *seg
  */
 int rkv_attend_segment(const rkv_attn_desc *desc, const float *q, const rkv_kv_view *seg,
                        float *o, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * rkv_attend_split -- attention over the union of n_segments segments in one
+ * launch: each segment is attended by its own key splits and all partials
+ * are merged by the LSE combine of the segment results ("F5 M7 -- Rolling
+ * KV", header note: window [0, wc) and tail [wc, n_kv) attended separately
+ * and merged; the result equals softmax attention over all their keys).
+ * This is the window + tail (+ tail tiles) step of one layer as a single
+ * kernel; rkv_attend_segment is the case n_segments == 1.
+ *
+ *   segs  1..4 views sharing one K type and one V type (else
+ *         RKV_E_UNSUPPORTED: attend them separately and use rkv_lse_combine),
+ *         all shared by every sequence or all per sequence.  Empty segments
+ *         are allowed; if every segment is empty o = 0 and lse = -inf.
+ *   q, o, lse, ws, stream: as for rkv_attend_segment.
+ *
+ * The merge order is fixed, so results are deterministic; they agree with
+ * rkv_attend_segment per segment + rkv_lse_combine to rounding, not bit for
+ * bit.
+ */
+int rkv_attend_split_workspace_bytes(const rkv_attn_desc *desc, int n_segments, const rkv_kv_view *segs,
+                                     size_t *bytes);
+int rkv_attend_split(const rkv_attn_desc *desc, const float *q, int n_segments, const rkv_kv_view *segs, float *o,
+                     float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * rkv_lse_combine -- merge per-segment results ("F5 M7 -- Rolling KV",

@@ -24,7 +24,7 @@ EXPORTS = (
     "rkv_status_string", "rkv_last_error", "rkv_row_bytes", "rkv_attend_workspace_bytes", "rkv_attend_segment",
     "rkv_lse_combine", "rkv_dequant_q8_0", "rkv_dequant_q4_0", "rkv_ring_create", "rkv_ring_destroy",
     "rkv_ring_begin_step", "rkv_stream_tail_workspace_bytes", "rkv_stream_tail", "rkv_ring_end_step",
-    "rkv_ring_schedule",
+    "rkv_ring_schedule", "rkv_attend_split", "rkv_attend_split_workspace_bytes",
 )
 
 
@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
                                                  ctypes.POINTER(sz)]
         L.rkv_attend_segment.argtypes = [ctypes.POINTER(rkv_attn_desc), vp, ctypes.POINTER(rkv_kv_view), vp, vp, vp,
                                          sz, vp]
+        L.rkv_attend_split_workspace_bytes.argtypes = [ctypes.POINTER(rkv_attn_desc), ctypes.c_int,
+                                                       ctypes.POINTER(rkv_kv_view), ctypes.POINTER(sz)]
+        L.rkv_attend_split.argtypes = [ctypes.POINTER(rkv_attn_desc), vp, ctypes.c_int, ctypes.POINTER(rkv_kv_view),
+                                       vp, vp, vp, sz, vp]
         L.rkv_lse_combine.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i32, vp, vp, vp]
         L.rkv_dequant_q8_0.argtypes = [vp, i64, vp, vp]
         L.rkv_dequant_q4_0.argtypes = [vp, i64, vp, vp]
@@ -160,6 +164,26 @@ def rkv_attend_segment(desc: Desc, q: torch.Tensor, seg: rkv_kv_view, o: torch.T
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().rkv_attend_segment(ctypes.byref(desc.c), _addr(q), ctypes.byref(seg), _addr(o), _addr(lse),
                                     _addr(ws), ws_bytes, _stream(stream)))
+
+
+def _segs(segs):
+    arr = (rkv_kv_view * len(segs))(*segs)
+    return arr
+
+
+def rkv_attend_split_workspace_bytes(desc: Desc, segs) -> int:
+    out = ctypes.c_size_t(0)
+    arr = _segs(segs)
+    _check(lib().rkv_attend_split_workspace_bytes(ctypes.byref(desc.c), len(segs), arr, ctypes.byref(out)))
+    return out.value
+
+
+def rkv_attend_split(desc: Desc, q: torch.Tensor, segs, o: torch.Tensor, lse: torch.Tensor,
+                     ws: torch.Tensor | None, stream=None) -> None:
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    arr = _segs(segs)
+    _check(lib().rkv_attend_split(ctypes.byref(desc.c), _addr(q), len(segs), arr, _addr(o), _addr(lse), _addr(ws),
+                                  ws_bytes, _stream(stream)))
 
 
 def rkv_lse_combine(o_parts, lse_parts, o_out: torch.Tensor, lse_out: torch.Tensor, head_dim: int,
@@ -249,6 +273,17 @@ def view_of_cache(kc, vc, start: int = 0, stop: int | None = None, k_seq_stride:
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A device workspace of at least nbytes (torch allocations are 256-byte aligned)."""
     return torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
+
+
+def attend_split(desc: Desc, q: torch.Tensor, segs, stream=None, ws: torch.Tensor | None = None):
+    """Allocate outputs (and workspace if none given) and run rkv_attend_split."""
+    S, Hq, D = desc.c.n_seq, desc.c.n_q_heads, desc.c.head_dim
+    o = torch.empty(S, Hq, D, dtype=torch.float32, device=q.device)
+    lse = torch.empty(S, Hq, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(rkv_attend_split_workspace_bytes(desc, segs), q.device)
+    rkv_attend_split(desc, q, segs, o, lse, ws, stream)
+    return o, lse
 
 
 def attend(desc: Desc, q: torch.Tensor, seg: rkv_kv_view, stream=None, ws: torch.Tensor | None = None):

@@ -115,11 +115,16 @@ int check_view_fields(const rkv_attn_desc *d, const rkv_kv_view *v)
 
 const int kRtSet[] = {1, 2, 4, 5, 8, 16};
 
-// Cut a segment into waves: row groups per KV head and key ranges.
-int make_plan(const rkv_attn_desc *d, const rkv_kv_view *v, SplitPlan *pl, SplitParams *prm)
+// Cut a launch over n segments (same K and V types) into workgroups: row
+// groups per KV head, and key splits over all segments together.
+int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitPlan *pl, SplitParams *prm)
 {
     const int S = d->n_seq, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim;
-    const bool shared = S == 1 || (v->k_seq_stride == 0 && v->v_seq_stride == 0);
+    const int kt = v[0]->k_type, vt = v[0]->v_type;
+    bool shared = true;
+    for (int i = 0; i < n; ++i)
+        if (v[i]->n_keys > 0 && (v[i]->k_seq_stride != 0 || v[i]->v_seq_stride != 0)) shared = false;
+    shared = shared || S == 1;
     std::vector<std::vector<int>> rows(Hkv);
     for (int b = 0; b < (shared ? S : 1); ++b)
         for (int h = 0; h < Hq; ++h) rows[kv_of(d, h)].push_back(b * Hq + h);
@@ -138,36 +143,53 @@ int make_plan(const rkv_attn_desc *d, const rkv_kv_view *v, SplitPlan *pl, Split
     pl->rows_per_g = rmax;
     pl->z = shared ? 1 : S;
     pl->n_rows_total = (int64_t)S * Hq;
-    // Aim at about 2048 waves (two per SIMD of the chip), each with at least
-    // one 64-key tile; a workgroup of nw waves takes a whole number of tiles
-    // per wave.
-    const int64_t n_tiles = (v->n_keys + kTile - 1) / kTile;
-    const int64_t nw = std::max(1, split_waves(v->k_type, v->v_type, D));
+    // One round of workgroups: as many as the kernel's occupancy lets every
+    // compute unit hold at once (measured on the current device; 2 per unit
+    // on 256 units when no device answers, e.g. for a size query on a host
+    // without a GPU).  Every segment is cut into splits of the same number of
+    // 64-key tiles, a multiple of the waves per workgroup.
+    int64_t tiles_total = 0;
+    for (int i = 0; i < n; ++i) tiles_total += (v[i]->n_keys + kTile - 1) / kTile;
+    const int64_t nw = std::max(1, split_waves(kt, vt, D));
     const int64_t units = (int64_t)Hkv * pl->n_rg * pl->z;
-    const int64_t want_waves = 2048;
-    int64_t n_splits = std::max<int64_t>(1, (want_waves + units * nw - 1) / (units * nw));
-    n_splits = std::min<int64_t>(n_splits, (n_tiles + nw - 1) / nw);
-    n_splits = std::max<int64_t>(n_splits, 1);
-    int64_t tps = (n_tiles + n_splits - 1) / n_splits;
+    int occ = split_occupancy(kt, vt, D, rt);
+    int cus = compute_units();
+    if (occ <= 0) occ = 2;
+    if (cus <= 0) cus = 256;
+    const int64_t want_groups = std::max<int64_t>(1, (int64_t)occ * cus / units);
+    int64_t tps = std::max<int64_t>(1, (tiles_total + want_groups - 1) / want_groups);
     tps = (tps + nw - 1) / nw * nw;
     if (tps * kTile > (1 << 30)) tps = (1 << 30) / kTile;
-    n_splits = n_tiles ? (n_tiles + tps - 1) / tps : 0;
-    if (n_splits > 65535) return fail(RKV_E_UNSUPPORTED, "segment too long for one launch");
+    int64_t n_splits = 0;
+    if (prm) memset(prm, 0, sizeof *prm);
+    int ns = 0;
+    for (int i = 0; i < n; ++i) {
+        const int64_t tiles = (v[i]->n_keys + kTile - 1) / kTile;
+        if (tiles == 0) continue;
+        if (prm) {
+            SegParams &sp = prm->seg[ns];
+            sp.k = (const uint8_t *)v[i]->k;
+            sp.v = (const uint8_t *)v[i]->v;
+            sp.k_pos = v[i]->k_pos_stride;
+            sp.v_pos = v[i]->v_pos_stride;
+            sp.k_head = v[i]->k_head_stride;
+            sp.v_head = v[i]->v_head_stride;
+            sp.k_seq = shared ? 0 : v[i]->k_seq_stride;
+            sp.v_seq = shared ? 0 : v[i]->v_seq_stride;
+            sp.n_keys = v[i]->n_keys;
+            sp.keys_per_split = (int32_t)(tps * kTile);
+            sp.split_base = (int32_t)n_splits;
+        }
+        ++ns;
+        n_splits += (tiles + tps - 1) / tps;
+    }
+    if (n_splits > 65535) return fail(RKV_E_UNSUPPORTED, "segments too long for one launch");
     pl->n_splits = (int)n_splits;
-    pl->keys_per_split = (int)(tps * kTile);
-    const size_t acc_bytes = (size_t)n_splits * pl->n_rows_total * D * sizeof(float);
-    pl->ws_bytes = n_splits > 1 ? ((acc_bytes + 255) & ~(size_t)255) + (size_t)n_splits * pl->n_rows_total * sizeof(float2)
-                                : 0;
+    pl->acc_bytes = n_splits > 1 ? ((size_t)n_splits * pl->n_rows_total * D * sizeof(float) + 255) & ~(size_t)255 : 0;
+    pl->ml_bytes = n_splits > 1 ? (size_t)n_splits * pl->n_rows_total * sizeof(float2) : 0;
+    pl->ws_bytes = pl->acc_bytes + pl->ml_bytes;
     if (prm) {
-        memset(prm, 0, sizeof *prm);
-        prm->k_pos = v->k_pos_stride;
-        prm->v_pos = v->v_pos_stride;
-        prm->k_head = v->k_head_stride;
-        prm->v_head = v->v_head_stride;
-        prm->k_seq = shared ? 0 : v->k_seq_stride;
-        prm->v_seq = shared ? 0 : v->v_seq_stride;
-        prm->n_keys = v->n_keys;
-        prm->keys_per_split = pl->keys_per_split;
+        prm->n_segs = ns;
         prm->n_splits = pl->n_splits;
         prm->n_rg = pl->n_rg;
         prm->rows_per_g = rmax;
@@ -184,39 +206,37 @@ int make_plan(const rkv_attn_desc *d, const rkv_kv_view *v, SplitPlan *pl, Split
     return RKV_OK;
 }
 
-// Enqueue one segment (arguments already validated).
-int attend_impl(const rkv_attn_desc *d, const float *q, const rkv_kv_view *v, float *o, float *lse, void *ws,
-                size_t ws_bytes, hipStream_t stream)
+// Enqueue one launch over segments of one (K, V) type pair (arguments already
+// validated).  All segments empty: o = 0, lse = -inf.
+int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view *const *v, float *o, float *lse,
+                void *ws, size_t ws_bytes, hipStream_t stream)
 {
     const int64_t n_rows = (int64_t)d->n_seq * d->n_q_heads;
-    if (v->n_keys == 0) {
+    int64_t keys = 0;
+    for (int i = 0; i < n; ++i) keys += v[i]->n_keys;
+    if (keys == 0) {
         RKV_HIP(launch_fill_empty(d->head_dim, n_rows, o, lse, stream));
         return RKV_OK;
     }
     SplitPlan pl;
     SplitParams prm;
-    int rc = make_plan(d, v, &pl, &prm);
+    int rc = make_plan(d, n, v, &pl, &prm);
     if (rc) return rc;
     if (pl.ws_bytes && (ws_bytes < pl.ws_bytes || !ws))
         return fail(RKV_E_INVAL, "workspace too small: %zu < %zu", ws_bytes, pl.ws_bytes);
-    if (!split_supported(v->k_type, v->v_type, d->head_dim, pl.rt))
+    const int kt = v[0]->k_type, vt = v[0]->v_type;
+    if (!split_supported(kt, vt, d->head_dim, pl.rt))
         return fail(RKV_E_UNSUPPORTED, "no kernel for this (type, head_dim, rows)");
     float *part_acc = (float *)ws;
-    const size_t acc_bytes = (size_t)pl.n_splits * pl.n_rows_total * d->head_dim * sizeof(float);
-    float2 *part_ml = (float2 *)((char *)ws + ((acc_bytes + 255) & ~(size_t)255));
+    float2 *part_ml = (float2 *)((char *)ws + pl.acc_bytes);
     const dim3 grid((unsigned)pl.n_splits, (unsigned)(d->n_kv_heads * pl.n_rg), (unsigned)pl.z);
-    RKV_HIP(launch_split(v->k_type, v->v_type, d->head_dim, pl.rt, grid, q, (const uint8_t *)v->k,
-                         (const uint8_t *)v->v, part_acc, part_ml, o, lse, prm, stream));
+    RKV_HIP(launch_split(kt, vt, d->head_dim, pl.rt, grid, q, part_acc, part_ml, o, lse, prm, stream));
     if (pl.n_splits > 1) RKV_HIP(launch_reduce(d->head_dim, n_rows, pl.n_splits, part_acc, part_ml, o, lse, stream));
     return RKV_OK;
 }
 
-int check_attend_args(const rkv_attn_desc *d, const float *q, const rkv_kv_view *v, float *o, float *lse)
+int check_out_args(const float *q, float *o, float *lse)
 {
-    int rc = check_desc(d);
-    if (rc) return rc;
-    rc = check_view_fields(d, v);
-    if (rc) return rc;
     if (!q || !o || !lse) return fail(RKV_E_INVAL, "q, o and lse must not be NULL");
     if ((uintptr_t)q % 16 || (uintptr_t)o % 16 || (uintptr_t)lse % 4)
         return fail(RKV_E_INVAL, "q and o must be 16-byte aligned, lse 4-byte aligned");
@@ -226,6 +246,30 @@ int check_attend_args(const rkv_attn_desc *d, const float *q, const rkv_kv_view 
 int check_device(const void *p, const char *name)
 {
     if (mem_kind(p) != 2) return fail(RKV_E_INVAL, "%s is not device memory", name);
+    return RKV_OK;
+}
+
+// Segments of one launch must share K and V types and sequence sharing.
+int check_segs(const rkv_attn_desc *d, int n, const rkv_kv_view *segs)
+{
+    if (n < 1 || n > kMaxSegs) return fail(RKV_E_INVAL, "n_segments must be in [1, %d]", kMaxSegs);
+    if (!segs) return fail(RKV_E_INVAL, "segments is NULL");
+    int rc;
+    for (int i = 0; i < n; ++i)
+        if ((rc = check_view_fields(d, &segs[i]))) return rc;
+    int first = -1;
+    for (int i = 0; i < n; ++i) {
+        if (segs[i].n_keys == 0) continue;
+        if (first < 0) {
+            first = i;
+            continue;
+        }
+        const rkv_kv_view &a = segs[first], &b = segs[i];
+        if (a.k_type != b.k_type || a.v_type != b.v_type)
+            return fail(RKV_E_UNSUPPORTED, "segments of one launch must share K and V types");
+        if (d->n_seq > 1 && ((a.k_seq_stride == 0) != (b.k_seq_stride == 0)))
+            return fail(RKV_E_INVAL, "segments of one launch must all be shared or all per sequence");
+    }
     return RKV_OK;
 }
 
@@ -255,35 +299,63 @@ int64_t rkv_row_bytes(int32_t dtype, int32_t head_dim)
     return row_bytes_of(dtype, head_dim);
 }
 
-int rkv_attend_workspace_bytes(const rkv_attn_desc *desc, const rkv_kv_view *seg, size_t *bytes)
+int rkv_attend_split_workspace_bytes(const rkv_attn_desc *desc, int n_segments, const rkv_kv_view *segs,
+                                     size_t *bytes)
 {
     if (!bytes) return fail(RKV_E_INVAL, "bytes is NULL");
     int rc = check_desc(desc);
     if (rc) return rc;
-    rc = check_view_fields(desc, seg);
-    if (rc) return rc;
-    if (seg->n_keys == 0) {
+    if ((rc = check_segs(desc, n_segments, segs))) return rc;
+    const rkv_kv_view *vp[kMaxSegs];
+    int64_t keys = 0;
+    for (int i = 0; i < n_segments; ++i) {
+        vp[i] = &segs[i];
+        keys += segs[i].n_keys;
+    }
+    if (keys == 0) {
         *bytes = 0;
         return RKV_OK;
     }
+    // take the types from a non-empty segment
+    int nz = 0;
+    while (segs[nz].n_keys == 0) ++nz;
+    std::swap(vp[0], vp[nz]);
     SplitPlan pl;
-    rc = make_plan(desc, seg, &pl, nullptr);
+    rc = make_plan(desc, n_segments, vp, &pl, nullptr);
     if (rc) return rc;
     *bytes = pl.ws_bytes;
     return RKV_OK;
 }
 
+int rkv_attend_split(const rkv_attn_desc *desc, const float *q, int n_segments, const rkv_kv_view *segs, float *o,
+                     float *lse, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if ((rc = check_segs(desc, n_segments, segs))) return rc;
+    if ((rc = check_out_args(q, o, lse))) return rc;
+    if ((rc = check_device(q, "q")) || (rc = check_device(o, "o")) || (rc = check_device(lse, "lse"))) return rc;
+    for (int i = 0; i < n_segments; ++i)
+        if (segs[i].n_keys > 0 && ((rc = check_device(segs[i].k, "K")) || (rc = check_device(segs[i].v, "V"))))
+            return rc;
+    if (ws && (rc = check_device(ws, "workspace"))) return rc;
+    const rkv_kv_view *vp[kMaxSegs];
+    for (int i = 0; i < n_segments; ++i) vp[i] = &segs[i];
+    int nz = 0;
+    while (nz < n_segments - 1 && segs[nz].n_keys == 0) ++nz;
+    std::swap(vp[0], vp[nz]);
+    return attend_impl(desc, q, n_segments, vp, o, lse, ws, ws_bytes, stream);
+}
+
+int rkv_attend_workspace_bytes(const rkv_attn_desc *desc, const rkv_kv_view *seg, size_t *bytes)
+{
+    return rkv_attend_split_workspace_bytes(desc, 1, seg, bytes);
+}
+
 int rkv_attend_segment(const rkv_attn_desc *desc, const float *q, const rkv_kv_view *seg, float *o, float *lse,
                        void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    int rc = check_attend_args(desc, q, seg, o, lse);
-    if (rc) return rc;
-    if ((rc = check_device(q, "q")) || (rc = check_device(o, "o")) || (rc = check_device(lse, "lse"))) return rc;
-    if (seg->n_keys > 0) {
-        if ((rc = check_device(seg->k, "K")) || (rc = check_device(seg->v, "V"))) return rc;
-        if (ws && (rc = check_device(ws, "workspace"))) return rc;
-    }
-    return attend_impl(desc, q, seg, o, lse, ws, ws_bytes, stream);
+    return rkv_attend_split(desc, q, 1, seg, o, lse, ws, ws_bytes, stream);
 }
 
 int rkv_lse_combine(int n_parts, const float *const *o_parts, const float *const *lse_parts, int64_t n_rows,
@@ -579,7 +651,8 @@ int rkv_stream_tail(rkv_ring *r, int layer, const rkv_attn_desc *desc, const flo
         v.v_seq_stride = 0;
         if ((rc = check_view_fields(desc, &v))) return rc;
         RKV_HIP(hipStreamWaitEvent(cs, r->copy_done[s], 0));
-        if ((rc = attend_impl(desc, q, &v, tile_o + (j - j0) * n_rows * D, tile_lse + (j - j0) * n_rows, attend_ws,
+        const rkv_kv_view *vp = &v;
+        if ((rc = attend_impl(desc, q, 1, &vp, tile_o + (j - j0) * n_rows * D, tile_lse + (j - j0) * n_rows, attend_ws,
                               attend_bytes, cs)))
             return rc;
         RKV_HIP(hipEventRecord(r->compute_done[s], cs));

@@ -1,14 +1,15 @@
-// attend.hip -- dispatch of the split kernel, and the fixed-order merge of
-// the per-range partials into a segment's normalised output and LSE.
+// attend.hip -- dispatch of the split kernel, occupancy queries, the
+// fixed-order merge of the per-split partials, and the fill of an empty
+// segment's result.
 #include "common.h"
 
 namespace rkv {
 
 #define RKV_DECL(kt, vt)                                                                                  \
-    hipError_t launch_split_k##kt##_v##vt(int d, int rt, dim3 grid, const float *q, const uint8_t *k,     \
-                                          const uint8_t *v, float *pa, float2 *pm, float *o, float *lse,  \
-                                          const SplitParams &p, hipStream_t s);                             \
-    int split_waves_k##kt##_v##vt(int d);
+    hipError_t launch_split_k##kt##_v##vt(int d, int rt, dim3 grid, const float *q, float *pa, float2 *pm, \
+                                          float *o, float *lse, const SplitParams &p, hipStream_t s);       \
+    int split_waves_k##kt##_v##vt(int d);                                                                 \
+    int split_occupancy_k##kt##_v##vt(int d, int rt);
 #define RKV_DECL_K(kt) RKV_DECL(kt, 0) RKV_DECL(kt, 1) RKV_DECL(kt, 2) RKV_DECL(kt, 3)
 RKV_DECL_K(0)
 RKV_DECL_K(1)
@@ -35,12 +36,59 @@ int split_waves(int kt, int vt, int d)
     return 0;
 }
 
-hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q, const uint8_t *k,
-                        const uint8_t *v, float *pa, float2 *pm, float *o, float *lse, const SplitParams &p,
-                        hipStream_t s)
+int split_occupancy(int kt, int vt, int d, int rt)
+{
+    // cached per instance and device (the first query on a device may be slow)
+    static int cache[4][4][4][6][16];
+    static const int rts[6] = {1, 2, 4, 5, 8, 16};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    int ri = -1;
+    for (int i = 0; i < 6; ++i)
+        if (rts[i] == rt) ri = i;
+    const int di = d == 64 ? 0 : d == 128 ? 1 : d == 256 ? 2 : d == 512 ? 3 : -1;
+    if (ri < 0 || di < 0 || kt < 0 || kt > 3 || vt < 0 || vt > 3 || dev < 0 || dev >= 16) return 0;
+    int &c = cache[kt][vt][di][ri][dev];
+    if (c == 0) {
+#define RKV_OCC(kk, vv) \
+    if (kt == kk && vt == vv) c = split_occupancy_k##kk##_v##vv(d, rt);
+#define RKV_OCC_K(kk) RKV_OCC(kk, 0) RKV_OCC(kk, 1) RKV_OCC(kk, 2) RKV_OCC(kk, 3)
+        RKV_OCC_K(0)
+        RKV_OCC_K(1)
+        RKV_OCC_K(2)
+        RKV_OCC_K(3)
+        if (c <= 0) c = -1;
+    }
+    return c > 0 ? c : 0;
+}
+
+int compute_units()
+{
+    static int cu[16];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (cu[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = -1;
+        }
+        cu[dev] = n;
+    }
+    return cu[dev] > 0 ? cu[dev] : 0;
+}
+
+hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q, float *pa, float2 *pm, float *o,
+                        float *lse, const SplitParams &p, hipStream_t s)
 {
 #define RKV_CASE(kk, vv) \
-    if (kt == kk && vt == vv) return launch_split_k##kk##_v##vv(d, rt, grid, q, k, v, pa, pm, o, lse, p, s);
+    if (kt == kk && vt == vv) return launch_split_k##kk##_v##vv(d, rt, grid, q, pa, pm, o, lse, p, s);
 #define RKV_CASE_K(kk) RKV_CASE(kk, 0) RKV_CASE(kk, 1) RKV_CASE(kk, 2) RKV_CASE(kk, 3)
     RKV_CASE_K(0)
     RKV_CASE_K(1)

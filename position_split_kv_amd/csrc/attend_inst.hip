@@ -13,42 +13,85 @@
 namespace rkv {
 
 template <int D, int RT>
-static hipError_t go(dim3 grid, const float *q, const uint8_t *k, const uint8_t *v, float *pa, float2 *pm,
-                     float *o, float *lse, const SplitParams &p, hipStream_t stream)
+static hipError_t go(dim3 grid, const float *q, float *pa, float2 *pm, float *o, float *lse, const SplitParams &p,
+                     hipStream_t stream)
 {
     if constexpr (D == 512 && (RKV_KT == kF32 || RKV_VT == kF32)) {
         return hipErrorInvalidValue;  // an f32 row of 512 values does not fit the LDS tile
     } else {
         hipLaunchKernelGGL((rkv_split_kernel<RKV_KT, RKV_VT, D, RT>), grid, dim3(64 * Shape<RKV_KT, RKV_VT, D>::NW), 0,
-                           stream, q, k, v, pa, pm, o, lse, p);
+                           stream, q, pa, pm, o, lse, p);
         return hipGetLastError();
     }
 }
 
 template <int D>
-static hipError_t by_rt(int rt, dim3 grid, const float *q, const uint8_t *k, const uint8_t *v, float *pa,
-                        float2 *pm, float *o, float *lse, const SplitParams &p, hipStream_t s)
+static hipError_t by_rt(int rt, dim3 grid, const float *q, float *pa, float2 *pm, float *o, float *lse,
+                        const SplitParams &p, hipStream_t s)
 {
     switch (rt) {
-    case 1: return go<D, 1>(grid, q, k, v, pa, pm, o, lse, p, s);
-    case 2: return go<D, 2>(grid, q, k, v, pa, pm, o, lse, p, s);
-    case 4: return go<D, 4>(grid, q, k, v, pa, pm, o, lse, p, s);
-    case 5: return go<D, 5>(grid, q, k, v, pa, pm, o, lse, p, s);
-    case 8: return go<D, 8>(grid, q, k, v, pa, pm, o, lse, p, s);
-    case 16: return go<D, 16>(grid, q, k, v, pa, pm, o, lse, p, s);
+    case 1: return go<D, 1>(grid, q, pa, pm, o, lse, p, s);
+    case 2: return go<D, 2>(grid, q, pa, pm, o, lse, p, s);
+    case 4: return go<D, 4>(grid, q, pa, pm, o, lse, p, s);
+    case 5: return go<D, 5>(grid, q, pa, pm, o, lse, p, s);
+    case 8: return go<D, 8>(grid, q, pa, pm, o, lse, p, s);
+    case 16: return go<D, 16>(grid, q, pa, pm, o, lse, p, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t RKV_NAME(RKV_KT, RKV_VT)(int d, int rt, dim3 grid, const float *q, const uint8_t *k, const uint8_t *v,
-                                    float *pa, float2 *pm, float *o, float *lse, const SplitParams &p, hipStream_t s)
+hipError_t RKV_NAME(RKV_KT, RKV_VT)(int d, int rt, dim3 grid, const float *q, float *pa, float2 *pm, float *o,
+                                    float *lse, const SplitParams &p, hipStream_t s)
 {
     switch (d) {
-    case 64: return by_rt<64>(rt, grid, q, k, v, pa, pm, o, lse, p, s);
-    case 128: return by_rt<128>(rt, grid, q, k, v, pa, pm, o, lse, p, s);
-    case 256: return by_rt<256>(rt, grid, q, k, v, pa, pm, o, lse, p, s);
-    case 512: return by_rt<512>(rt, grid, q, k, v, pa, pm, o, lse, p, s);
+    case 64: return by_rt<64>(rt, grid, q, pa, pm, o, lse, p, s);
+    case 128: return by_rt<128>(rt, grid, q, pa, pm, o, lse, p, s);
+    case 256: return by_rt<256>(rt, grid, q, pa, pm, o, lse, p, s);
+    case 512: return by_rt<512>(rt, grid, q, pa, pm, o, lse, p, s);
     default: return hipErrorInvalidValue;
+    }
+}
+
+template <int D, int RT>
+static int occ_of()
+{
+    if constexpr (D == 512 && (RKV_KT == kF32 || RKV_VT == kF32)) {
+        return 0;
+    } else {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rkv_split_kernel<RKV_KT, RKV_VT, D, RT>,
+                                                         64 * Shape<RKV_KT, RKV_VT, D>::NW, 0) != hipSuccess) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        return n;
+    }
+}
+
+template <int D>
+static int occ_by_rt(int rt)
+{
+    switch (rt) {
+    case 1: return occ_of<D, 1>();
+    case 2: return occ_of<D, 2>();
+    case 4: return occ_of<D, 4>();
+    case 5: return occ_of<D, 5>();
+    case 8: return occ_of<D, 8>();
+    case 16: return occ_of<D, 16>();
+    default: return 0;
+    }
+}
+
+#define RKV_NAME_OCC(kt, vt) RKV_CAT4(split_occupancy_k, kt, _v, vt)
+// Workgroups of this instance that fit one compute unit (0 if unknown).
+int RKV_NAME_OCC(RKV_KT, RKV_VT)(int d, int rt)
+{
+    switch (d) {
+    case 64: return occ_by_rt<64>(rt);
+    case 128: return occ_by_rt<128>(rt);
+    case 256: return occ_by_rt<256>(rt);
+    case 512: return occ_by_rt<512>(rt);
+    default: return 0;
     }
 }
 

@@ -22,11 +22,13 @@
 //   4. P.V: lanes are (key-in-step, 8-dim group); each lane accumulates its 8
 //      dims for every row over the tile's keys.
 //
-// At the end the NW waves merge their (m, l, acc) in LDS.  A segment handled
-// by one workgroup per item writes its normalised output and LSE directly;
-// otherwise each workgroup writes a partial and a second, fixed-order pass
+// At the end the NW waves merge their (m, l, acc) in LDS.  A launch that is
+// one workgroup per work item writes its normalised output and LSE directly;
+// otherwise each workgroup writes a partial and a second, fixed-order kernel
 // merges them (the same LSE arithmetic as the segment combine), so the
-// results are deterministic.
+// results are deterministic.  (A merge by the last workgroup to finish was
+// measured slower: handing partials between workgroups inside a kernel needs
+// device-scope release fences, which write back the L2 of each XCD.)
 //
 // This is the in-register reading of window and tail at their own types that
 // "F5 M7 -- Rolling KV" ships (section "2026-07-12 -- #582-P2 SHIPPED"), with
@@ -239,6 +241,43 @@ __device__ __forceinline__ int kswz(int j)
 }
 
 // ---------------------------------------------------------------- dma k rows
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// One direct global -> LDS load: the 16 bytes at g (per lane) land at LDS
+// address lds + 16 * lane.  Written as asm so that the compiler neither
+// inserts its own (conservative or missing) waits for it nor reorders memory
+// accesses across it; callers wait with waitcnt_vm() before reading the data
+// and wait for their LDS reads (lgkmcnt) before overwriting a buffer.  M0 is
+// saved and restored around the load.
+__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(g), "s"(lds)
+                 : "memory");
+#else
+    (void)g;
+    (void)lds;
+#endif
+}
+
+// s_waitcnt vmcnt(n) (0 <= n <= 63), other counters untouched.
+template <int N>
+__device__ __forceinline__ void waitcnt_vm()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void waitcnt_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+
 
 // QC dims [d0, d0 + QC) of row j of a DMA-staged f32 / f16 K tile.
 template <int KT, int RB, int QC>
@@ -508,9 +547,8 @@ __device__ __forceinline__ float v_group_lds(const uint32_t *row, int dg, float 
 
 template <int KT, int VT, int D, int RT>
 __global__ void __launch_bounds__((64 * Shape<KT, VT, D>::NW))
-rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase, const uint8_t *__restrict__ vbase,
-                 float *__restrict__ part_acc, float2 *__restrict__ part_ml, float *__restrict__ o_out,
-                 float *__restrict__ lse_out, const SplitParams p)
+rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, float2 *__restrict__ part_ml,
+                 float *__restrict__ o_out, float *__restrict__ lse_out, const SplitParams p)
 {
     using Sh = Shape<KT, VT, D>;
     constexpr int NW = Sh::NW;
@@ -529,7 +567,7 @@ rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase,
     __shared__ float sP[NW][RT * kTile];
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform in the wave
     uint32_t *sK = smem + w * Sh::STAGE_DW;
     uint32_t *sV = sK + kTile * LSK;
 
@@ -539,11 +577,17 @@ rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase,
     if (cnt <= 0) return;
     const int nr = cnt < RT ? cnt : RT;
     const int z = blockIdx.z;
-    const int64_t kbeg = (int64_t)blockIdx.x * p.keys_per_split;
-    const int64_t kend = kbeg + p.keys_per_split < p.n_keys ? kbeg + p.keys_per_split : p.n_keys;
 
-    const uint8_t *kg = kbase + z * p.k_seq + g * p.k_head;
-    const uint8_t *vg = vbase + z * p.v_seq + g * p.v_head;
+    // the segment this workgroup's key split belongs to
+    SegParams sg = p.seg[0];
+#pragma unroll
+    for (int si = 1; si < kMaxSegs; ++si)
+        if (si < p.n_segs && (int)blockIdx.x >= p.seg[si].split_base) sg = p.seg[si];
+    const int64_t kbeg = (int64_t)((int)blockIdx.x - sg.split_base) * sg.keys_per_split;
+    const int64_t kend = kbeg + sg.keys_per_split < sg.n_keys ? kbeg + sg.keys_per_split : sg.n_keys;
+
+    const uint8_t *kg = sg.k + z * sg.k_seq + g * sg.k_head;
+    const uint8_t *vg = sg.v + z * sg.v_seq + g * sg.v_head;
 
     int rid[RT];
     const float *qp[RT];
@@ -587,18 +631,19 @@ rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase,
     KRegs kr;
     VRegs vr;
     uint32_t vreg[V_REG ? NSTEP : 1][VRW];
-    int vps = (int)p.v_pos;
+    uint32_t vnx[V_REG ? NSTEP : 1][VRW];
+    int vps = (int)sg.v_pos;
     asm volatile("" : "+s"(vps));
-    auto load_vreg = [&](int64_t t, int nkk) {
+    auto load_v_into = [&](uint32_t (&dst)[V_REG ? NSTEP : 1][VRW], int64_t t, int nkk) {
         if constexpr (!V_REG) return;
-        const uint8_t *vt = vg + t * p.v_pos;
+        const uint8_t *vt = vg + t * sg.v_pos;
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
             const int key = st * KPS + ks;
             const int keyc = key < nkk ? key : nkk - 1;  // weight 0 in P.V, finite data
             const uint8_t *pv = vt + (uint32_t)(keyc * vps + dg * (VRW * 4));
             const uint4 a = *(const uint4 *)pv;
-            uint32_t *vr8 = &vreg[st][0];
+            uint32_t *vr8 = &dst[st][0];
             vr8[0] = a.x; vr8[1] = a.y; vr8[2] = a.z; vr8[3] = a.w;
             if constexpr (VRW == 8) {
                 const uint4 b = *(const uint4 *)(pv + 16);
@@ -606,45 +651,66 @@ rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase,
             }
         }
     };
+    auto load_vreg = [&](int64_t t, int nkk) { load_v_into(vreg, t, nkk); };
     auto nk_at = [&](int64_t t) { return (int)(kend - t < kTile ? kend - t : kTile); };
 
     constexpr bool KDMA = Sh::KDMA;
+    // Option (off by default): with K by DMA and V in registers, double buffer
+    // V so tile i+1's V rows load a whole tile ahead (two tiles of V live in
+    // registers, one wave per SIMD).
+#ifdef RKV_VDB
+    constexpr bool VDB = KDMA && V_REG;
+#else
+    constexpr bool VDB = false;  // measured slower: it halves the waves per SIMD
+#endif
     // Issue the direct global -> LDS loads of a tile's K rows (rows past nkk
     // repeat row nkk-1).  Lane l of load i fills slot i*64 + l of the tile.
     auto dma_k = [&](int64_t t, int nkk) {
         if constexpr (KDMA) {
             constexpr int CPR = Sh::RBK / 16;
             constexpr int NI = kTile * Sh::RBK / 1024;
-            int kps = (int)p.k_pos;
+            int kps = (int)sg.k_pos;
             asm volatile("" : "+s"(kps));
-            const uint8_t *kt = kg + t * p.k_pos;
+            const uint8_t *kt = kg + t * sg.k_pos;
+            const uint32_t base = lds_addr(smem + w * Sh::STAGE_DW);
+            waitcnt_lgkm0();  // this wave's earlier LDS reads of the buffer are done
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int slot = i * 64 + lane;
                 const int j = slot / CPR, cs = slot % CPR;
                 const int c = cs ^ kswz<Sh::RBK>(j);
                 const int jc = j < nkk ? j : nkk - 1;
-#if defined(__HIP_DEVICE_COMPILE__)  // a device-only builtin: the host pass only needs the kernel's signature
-                __builtin_amdgcn_global_load_lds((const void *)(kt + (uint32_t)(jc * kps + 16 * c)),
-                                                 smem + w * Sh::STAGE_DW + i * 256, 16, 0, 0);
-#else
-                (void)jc; (void)c; (void)kt;
-#endif
+                lds_dma16(kt + (uint32_t)(jc * kps + 16 * c), base + 1024u * i);
             }
         }
     };
+    // VMEM instructions one load_v_into issues (outstanding loads a wait may leave)
+    constexpr int NV = V_REG ? NSTEP * (VRW / 4) : 0;
+    static_assert(2 * NV <= 63, "vmcnt range");
     const int sw = kswz<Sh::RBK>(lane);
 
     int64_t t0 = kbeg + (int64_t)w * kTile;
+    // VMEM loads issued after the K rows' DMA that may stay outstanding when
+    // the scores start: 0, NV or 2*NV
+    int v_after_dma = 0;
     if constexpr (KDMA) {
         if (t0 < kend) {
             dma_k(t0, nk_at(t0));
+            if constexpr (VDB) {
+                load_vreg(t0, nk_at(t0));
+                v_after_dma = NV;
+                const int64_t t1 = t0 + (int64_t)NW * kTile;
+                if (t1 < kend) {
+                    load_v_into(vnx, t1, nk_at(t1));
+                    v_after_dma = 2 * NV;
+                }
+            }
         }
     } else if constexpr (PIPE) {
         if (t0 < kend) {
-            load_rows(kr, kg + t0 * p.k_pos, (int)p.k_pos, nk_at(t0), lane);
+            load_rows(kr, kg + t0 * sg.k_pos, (int)sg.k_pos, nk_at(t0), lane);
             if constexpr (V_REG) load_vreg(t0, nk_at(t0));
-            else load_rows(vr, vg + t0 * p.v_pos, (int)p.v_pos, nk_at(t0), lane);
+            else load_rows(vr, vg + t0 * sg.v_pos, (int)sg.v_pos, nk_at(t0), lane);
         }
     }
     for (; t0 < kend; t0 += (int64_t)NW * kTile) {
@@ -654,15 +720,25 @@ rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase,
             // K rows arrive by DMA issued one tile ahead; V rows load now and
             // are in flight during the scores (holding two tiles of V in
             // registers would halve the occupancy).
-            if constexpr (V_REG) load_vreg(t0, nk);
-            if constexpr (!V_REG) stage_rows<Sh::RBV, VWV, LSV>(vg + t0 * p.v_pos, (int)p.v_pos, nk, sV, lane);
+            if constexpr (V_REG && !VDB) {
+                load_vreg(t0, nk);
+                v_after_dma = NV;
+            }
+            if constexpr (!V_REG) {
+                stage_rows<Sh::RBV, VWV, LSV>(vg + t0 * sg.v_pos, (int)sg.v_pos, nk, sV, lane);
+                v_after_dma = 0;
+            }
+            // this tile's K rows (DMA) have landed; later V loads may still fly
+            if (v_after_dma == 2 * NV) waitcnt_vm<2 * NV>();
+            else if (v_after_dma == NV) waitcnt_vm<NV>();
+            else waitcnt_vm<0>();
         } else if constexpr (PIPE) {
             store_rows<Sh::RBK, VWK, LSK>(kr, sK, lane);
             if constexpr (!V_REG) store_rows<Sh::RBV, VWV, LSV>(vr, sV, lane);
         } else {
             if constexpr (V_REG) load_vreg(t0, nk);
-            stage_rows<Sh::RBK, VWK, LSK>(kg + t0 * p.k_pos, (int)p.k_pos, nk, sK, lane);
-            if constexpr (!V_REG) stage_rows<Sh::RBV, VWV, LSV>(vg + t0 * p.v_pos, (int)p.v_pos, nk, sV, lane);
+            stage_rows<Sh::RBK, VWK, LSK>(kg + t0 * sg.k_pos, (int)sg.k_pos, nk, sK, lane);
+            if constexpr (!V_REG) stage_rows<Sh::RBV, VWV, LSV>(vg + t0 * sg.v_pos, (int)sg.v_pos, nk, sV, lane);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS stores are done
         __builtin_amdgcn_wave_barrier();
@@ -702,8 +778,8 @@ rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase,
             if (tn < kend) dma_k(tn, nk_at(tn));
         } else if constexpr (PIPE) {
             if (tn < kend) {
-                load_rows(kr, kg + tn * p.k_pos, (int)p.k_pos, nk_at(tn), lane);
-                if constexpr (!V_REG) load_rows(vr, vg + tn * p.v_pos, (int)p.v_pos, nk_at(tn), lane);
+                load_rows(kr, kg + tn * sg.k_pos, (int)sg.k_pos, nk_at(tn), lane);
+                if constexpr (!V_REG) load_rows(vr, vg + tn * sg.v_pos, (int)sg.v_pos, nk_at(tn), lane);
             }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -740,6 +816,18 @@ rkv_split_kernel(const float *__restrict__ q, const uint8_t *__restrict__ kbase,
         }
         if constexpr (PIPE && V_REG) {
             if (tn < kend) load_vreg(tn, nk_at(tn));
+        }
+        if constexpr (VDB) {
+#pragma unroll
+            for (int st = 0; st < NSTEP; ++st)
+#pragma unroll
+                for (int e = 0; e < VRW; ++e) vreg[st][e] = vnx[st][e];
+            const int64_t tnn = tn + (int64_t)NW * kTile;
+            v_after_dma = 0;
+            if (tnn < kend) {
+                load_v_into(vnx, tnn, nk_at(tnn));
+                v_after_dma = NV;
+            }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();

@@ -28,12 +28,23 @@ constexpr int kMaxRowTable = 1024;  // entries of the per-KV-head row table
 constexpr int kMaxKvHeads = 64;
 constexpr int kMaxParts = 64;
 
-// Launch parameters of the split (partial) attention kernel.  Byte strides.
-struct SplitParams {
+constexpr int kMaxSegs = 4;         // segments one launch can attend
+
+// One segment of a launch: its K/V base pointers and byte strides, its keys,
+// and the range of workgroups (key splits) that cover it.
+struct SegParams {
+    const uint8_t *k, *v;
     int64_t k_pos, v_pos, k_head, v_head, k_seq, v_seq;
     int64_t n_keys;
     int32_t keys_per_split;
-    int32_t n_splits;
+    int32_t split_base;  // first grid x index of this segment
+};
+
+// Launch parameters of the split attention kernel.
+struct SplitParams {
+    SegParams seg[kMaxSegs];
+    int32_t n_segs;
+    int32_t n_splits;      // total key splits over all segments (grid x)
     int32_t n_rg;          // row groups per KV head
     int32_t rows_per_g;    // stride of rowtab between KV heads
     int32_t n_rows_total;  // n_seq * n_q_heads
@@ -45,30 +56,34 @@ struct SplitParams {
     uint16_t rowtab[kMaxRowTable];
 };
 
-// How one segment is cut into work: shared by the workspace query and the launch.
+// How a launch is cut into work: shared by the workspace query and the launch.
 struct SplitPlan {
     int rt;          // rows per wave (template instance)
     int n_rg;        // row groups per KV head
     int rows_per_g;  // max rows of a KV head
     int z;           // grid z (sequences with own keys, or 1)
-    int n_splits;
-    int keys_per_split;
+    int n_splits;    // grid x
     int64_t n_rows_total;
+    size_t acc_bytes, ml_bytes;
     size_t ws_bytes;
 };
 
 // Kernel launchers (attend.hip / combine.hip / dequant.hip).  They enqueue on
 // `stream` and return the hipError_t of the launch.
-// One launch of the split kernel over `grid` work items.  With one split per
-// item (p.n_splits == 1) it writes o / lse directly, else the partials.
-hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q, const uint8_t *k,
-                        const uint8_t *v, float *part_acc, float2 *part_ml, float *o, float *lse,
-                        const SplitParams &p, hipStream_t stream);
+// One launch of the split kernel.  With one split in all (p.n_splits == 1) it
+// writes o / lse directly; otherwise every workgroup writes its partial and
+// launch_reduce merges them.
+hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q, float *part_acc,
+                        float2 *part_ml, float *o, float *lse, const SplitParams &p, hipStream_t stream);
+hipError_t launch_reduce(int d, int64_t n_rows, int n_splits, const float *part_acc, const float2 *part_ml,
+                         float *o, float *lse, hipStream_t stream);
 bool split_supported(int kt, int vt, int d, int rt);
 // Waves per workgroup of the split kernel for a (K type, V type, head_dim).
 int split_waves(int kt, int vt, int d);
-hipError_t launch_reduce(int d, int64_t n_rows, int n_splits, const float *part_acc, const float2 *part_ml,
-                         float *o, float *lse, hipStream_t stream);
+// Workgroups of a split-kernel instance resident per compute unit on the
+// current device, and the device's compute units (0 when no device answers).
+int split_occupancy(int kt, int vt, int d, int rt);
+int compute_units();
 hipError_t launch_fill_empty(int d, int64_t n_rows, float *o, float *lse, hipStream_t stream);
 
 struct CombineParts {

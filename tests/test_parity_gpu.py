@@ -218,3 +218,68 @@ def test_errors_on_device():
     P.rkv_attend_segment(desc, q, view, o, l, ws)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all()
+
+
+# ----------------------------------------------------------------------------- several segments in one launch
+
+SPLIT_CASES = [
+    # name, S, Hq, Hkv, D, K, V, n, cuts, softcap
+    ("f16_window_tail", 1, 40, 8, 128, synth.F16, synth.F16, 6000, [0, 4500, 6000], 0.0),
+    ("q8q4_window_tiles", 1, 40, 8, 128, synth.Q8_0, synth.Q4_0, 5000, [0, 2000, 3000, 4000, 5000], 0.0),
+    ("q8_d512_cap", 1, 16, 2, 512, synth.Q8_0, synth.Q8_0, 3000, [0, 2250, 3000], 30.0),
+    ("f16_empty_segment", 1, 8, 2, 128, synth.F16, synth.F16, 1000, [0, 0, 700, 1000], 0.0),
+    ("f16_batch_own_keys", 3, 8, 2, 128, synth.F16, synth.F16, 900, [0, 300, 900], 0.0),
+    ("f32_tiny", 1, 8, 2, 128, synth.F32, synth.F32, 4096, [0, 3072, 4096], 0.0),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_attend_split_parity(case):
+    name, S, Hq, Hkv, D, kt, vt, n, cuts, cap = case
+    note(f"attend_split {name}: segments {list(zip(cuts, cuts[1:]))}")
+    seed = zlib.crc32(name.encode()) % 100000
+    kc, vc = pair(S * n, Hkv, D, kt, vt, seed, DEV)
+    q = synth.make_query(S, Hq, D, synth.stream_seed(seed, 3), DEV)
+    desc = P.Desc(S, Hq, Hkv, D, default_scale(D), cap)
+    kss, vss = (n * kc.pos_stride, n * vc.pos_stride) if S > 1 else (0, 0)
+    segs = [P.view_of_cache(kc, vc, a, b, kss, vss) for a, b in zip(cuts, cuts[1:])]
+    o, l = P.attend_split(desc, q, segs)
+    torch.cuda.synchronize()
+    kh, vh = kc.to("cpu"), vc.to("cpu")
+    o_ref, l_ref = oracle.attend(q.cpu().numpy(), oracle_views(kh, vh, [0, n], (kss, vss)), Hkv, default_scale(D), cap)
+    compare(o, l, o_ref, l_ref, what="one launch")
+
+
+def test_workspace_reuse():
+    """A workspace is reused by consecutive calls without clearing; results
+    stay correct and deterministic."""
+    D, Hq, Hkv = 128, 40, 8
+    kc, vc = pair(30000, Hkv, D, synth.F16, synth.F16, 606, DEV)
+    q1 = synth.make_query(1, Hq, D, 607, DEV)
+    q2 = synth.make_query(1, Hq, D, 608, DEV)
+    desc = P.Desc(1, Hq, Hkv, D, 0.088)
+    segs = [P.view_of_cache(kc, vc, 0, 22000), P.view_of_cache(kc, vc, 22000, 30000)]
+    ws = P.workspace(P.rkv_attend_split_workspace_bytes(desc, segs))
+    note("workspace reuse")
+    outs = []
+    for qq in (q1, q2, q1, q2, q1):
+        o, l = P.attend_split(desc, qq, segs, ws=ws)
+        outs.append((o, l))
+    torch.cuda.synchronize()
+    for a, b in ((0, 2), (2, 4), (1, 3)):
+        assert torch.equal(outs[a][0], outs[b][0]) and torch.equal(outs[a][1], outs[b][1])
+    kh, vh = kc.to("cpu"), vc.to("cpu")
+    o_ref, l_ref = oracle.attend(q2.cpu().numpy(), [oracle.view_of(kh, vh)], Hkv, 0.088)
+    compare(outs[3][0], outs[3][1], o_ref, l_ref, what="reused workspace")
+
+
+def test_attend_split_mixed_types_rejected():
+    D, Hq, Hkv = 128, 8, 2
+    a, b = pair(200, Hkv, D, synth.Q8_0, synth.Q4_0, 1, DEV)
+    c, d = pair(200, Hkv, D, synth.F16, synth.F16, 2, DEV)
+    desc = P.Desc(1, Hq, Hkv, D, 0.1)
+    q = synth.make_query(1, Hq, D, 3, DEV)
+    note("mixed types in one launch")
+    with pytest.raises(P.RkvError) as e:
+        P.attend_split(desc, q, [P.view_of_cache(a, b), P.view_of_cache(c, d)], ws=P.workspace(1 << 20))
+    assert e.value.code == P.RKV_E_UNSUPPORTED
