@@ -3,15 +3,22 @@
 Workload (the headline configuration): a Qwen2.5-14B-shaped decode layer --
 1 query token, 40 query heads / 8 KV heads, head_dim 128, n_kv = 65536 keys
 of f16 K and V drawn N(0,1) with 1 % of the (KV head, dim) channels scaled by
-8 -- split into a device window of 49152 keys and a 16384-key tail (also
-device-resident); 48 independent layers run back to back.  One step = for
-every layer: rkv_attend_segment(window), rkv_attend_segment(tail),
-rkv_lse_combine.  The metric is effective KV bytes/s: the K+V bytes the step
-must read (48 x 268.4 MB) over the step time.
+8 -- split by key position into a device window [0, 49152) and a 16384-key
+tail [49152, 65536) (also device-resident); 48 independent layers run back to
+back.  One step = for every layer one rkv_attend_split call over the two
+segments: the split-K kernel attends window and tail tiles in one launch
+(Q staging, K/V tile reads, in-register conversion, scores, online softmax,
+PV accumulation, per-split partials) and the fixed-order merge kernel turns
+the partials of both segments into the combined O and LSE.  The metric is
+effective KV bytes/s: the K+V bytes the step must read (48 x 268.4 MB) over
+the step time.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-Prints one JSON line.  Only one GPU is used; --gpus above 1 exits.
+Prints one JSON line on stdout (progress on stderr).  Only one GPU is used;
+--gpus above 1 exits.  --copy-probe adds one plain 1 GiB device copy (torch)
+before the workload, whose hardware counters calibrate the FETCH_SIZE /
+WRITE_SIZE readings of the attention kernels.
 """
 from __future__ import annotations
 
@@ -19,6 +26,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -26,10 +34,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+# HBM bytes (read + write) per rkv_attend_split call on this workload (split
+# kernel + partial merge), from two rocprofv3 --pmc passes (FETCH_SIZE, then
+# WRITE_SIZE), each scaled by that counter's reading for a plain 1 GiB copy
+# (x2.0 and x1.0); None once the kernels have changed since the counters
+# were taken.
+MEASURED_TRAFFIC_BYTES = 280_986_829
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def pct(xs, p):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(p / 100.0 * (len(xs) - 1)))))]
 
 
 def main():
@@ -39,10 +58,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true", help="run one plain 1 GiB copy first (counter calibration)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the three-call comparison and the read-ceiling probe (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU design is described, "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); sharding across GPUs is described, "
               "not built", file=sys.stderr)
         sys.exit(2)
 
@@ -52,6 +74,16 @@ def main():
     import synth
 
     dev = "cuda"
+    torch.cuda.init()
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("bench: copy probe: 1073741824 bytes read, 1073741824 bytes written")
+        del a, b
+
     L, S, Hq, Hkv, D, n, wc = args.layers, 1, 40, 8, 128, 65536, 49152
     scale = 1.0 / math.sqrt(D)
     outliers = round(0.01 * Hkv * D)
@@ -66,21 +98,14 @@ def main():
         layers.append((kc, vc, q))
     torch.cuda.synchronize()
     desc = P.Desc(S, Hq, Hkv, D, scale)
-    views = [(P.view_of_cache(kc, vc, 0, wc), P.view_of_cache(kc, vc, wc, n)) for kc, vc, _ in layers]
-    ws_w = P.workspace(P.rkv_attend_workspace_bytes(desc, views[0][0]))
-    ws_t = P.workspace(P.rkv_attend_workspace_bytes(desc, views[0][1]))
-    ow = torch.empty(S, Hq, D, device=dev)
-    lw = torch.empty(S, Hq, device=dev)
-    ot = torch.empty_like(ow)
-    lt = torch.empty_like(lw)
-    outs = [(torch.empty_like(ow), torch.empty_like(lw)) for _ in range(L)]
+    segs = [[P.view_of_cache(kc, vc, 0, wc), P.view_of_cache(kc, vc, wc, n)] for kc, vc, _ in layers]
+    ws = P.workspace(P.rkv_attend_split_workspace_bytes(desc, segs[0]))
+    outs = [(torch.empty(S, Hq, D, device=dev), torch.empty(S, Hq, device=dev)) for _ in range(L)]
     stream = torch.cuda.current_stream()
 
     def step():
-        for li, (kc, vc, q) in enumerate(layers):
-            P.rkv_attend_segment(desc, q, views[li][0], ow, lw, ws_w, stream)
-            P.rkv_attend_segment(desc, q, views[li][1], ot, lt, ws_t, stream)
-            P.rkv_lse_combine([ow, ot], [lw, lt], outs[li][0], outs[li][1], D, stream)
+        for li in range(L):
+            P.rkv_attend_split(desc, layers[li][2], segs[li], outs[li][0], outs[li][1], ws, stream)
 
     for _ in range(args.warmup):
         step()
@@ -96,26 +121,31 @@ def main():
     step_bytes = L * kv_bytes_layer
     gbs = step_bytes / dt / 1e9
 
-    # dominant kernel: the window segment (49152 keys, 201.3 MB of K+V per launch),
-    # timed with events on the stream it is launched on, over the same layers
-    win_bytes = 2 * wc * Hkv * D * 2
+    # The dominant kernel: each rkv_attend_split call is the split kernel over
+    # all 65536 keys (268.4 MB of K+V) followed by the small partial-merge
+    # kernel; HIP events on the launch stream bracket the call.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
-    reps = max(1, args.steps // 4)
+    reps = max(2, args.steps // 2)
     times = []
     for _ in range(reps):
-        for li, (kc, vc, q) in enumerate(layers):
+        for li in range(L):
             ev[li][0].record(stream)
-            P.rkv_attend_segment(desc, q, views[li][0], ow, lw, ws_w, stream)
+            P.rkv_attend_split(desc, layers[li][2], segs[li], outs[li][0], outs[li][1], ws, stream)
             ev[li][1].record(stream)
         torch.cuda.synchronize()
         times += [a.elapsed_time(b) * 1e-3 for a, b in ev]
-    win_s = sum(times) / len(times)
-    win_gbs = win_bytes / win_s / 1e9
+    call_s = sum(times) / len(times)
+    call_gbs = kv_bytes_layer / call_s / 1e9
+
+    three_us = read_ceiling = None
+    if not args.no_extras:
+        three_us, read_ceiling = extras(P, desc, layers, segs, outs, stream, S, Hq, D, L)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(layers, desc, args.cpu_seconds)
 
+    traffic = MEASURED_TRAFFIC_BYTES
     out = {
         "metric": "decode attention effective KV GB/s & us/layer vs HBM peak; tail-hidden fraction",
         "value": round(gbs, 2),
@@ -134,49 +164,95 @@ def main():
                         "n_kv 65536 = window 49152 + tail 16384 (device), f16 K/V, 48 layers back to back",
             "layers": L, "n_kv": n, "wc": wc, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
             "us_per_layer": round(dt / L * 1e6, 3),
+            "us_per_layer_call_p10_p50_p90": [round(pct(times, p) * 1e6, 2) for p in (10, 50, 90)],
+            "us_per_layer_three_calls": three_us and round(three_us, 3),
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "read_ceiling_GBs_torch_sum_4GiB": read_ceiling and round(read_ceiling, 1),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "rkv_split_kernel<f16,f16,128,5> (window segment, incl. its partial-merge kernel)",
-            "achieved": round(win_gbs, 2),
+            "kernel": "rkv_split_kernel<f16,f16,128,5> + rkv_reduce_kernel<128> (one rkv_attend_split call)",
+            "achieved": round(call_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(win_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "algorithmic_bytes_per_launch": win_bytes,
-            "avg_launch_us": round(win_s * 1e6, 3),
+            "frac": round(call_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kv_bytes_layer,
+            "avg_launch_us": round(call_s * 1e6, 3),
+            "median_launch_us": round(statistics.median(times) * 1e6, 3),
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
 
+def extras(P, desc, layers, segs, outs, stream, S, Hq, D, L):
+    """The same layers through the three-call form (window, tail, combine),
+    and the read rate of a plain torch reduction over 4 GiB, for context."""
+    import torch
+
+    dev = "cuda"
+    ow, lw = torch.empty(S, Hq, D, device=dev), torch.empty(S, Hq, device=dev)
+    ot, lt = torch.empty_like(ow), torch.empty_like(lw)
+    ws_w = P.workspace(P.rkv_attend_workspace_bytes(desc, segs[0][0]))
+    ws_t = P.workspace(P.rkv_attend_workspace_bytes(desc, segs[0][1]))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for it in range(2):
+        if it == 1:
+            e0.record(stream)
+        for li in range(L):
+            P.rkv_attend_segment(desc, layers[li][2], segs[li][0], ow, lw, ws_w, stream)
+            P.rkv_attend_segment(desc, layers[li][2], segs[li][1], ot, lt, ws_t, stream)
+            P.rkv_lse_combine([ow, ot], [lw, lt], outs[li][0], outs[li][1], D, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    three_us = e0.elapsed_time(e1) * 1e3 / L
+
+    big = torch.ones(1 << 31, dtype=torch.float16, device=dev)
+    big.sum()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        big.sum()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    read_ceiling = 5 * big.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del big
+
+    return three_us, read_ceiling
+
+
 def cpu_baseline(layers, desc, seconds):
     """The binary64 oracle (as it stands) on the host cores, on a bounded
     sample of the same workload: whole layers (all 40 query heads over all
-    65536 keys) until about `seconds` of work; reported as effective K+V GB/s."""
+    65536 keys, unsplit) cycling over the first four layers until about
+    `seconds` of work; reported as effective K+V GB/s."""
     import oracle
 
     threads = oracle.max_threads()
-    kc, vc, q = layers[0]
-    kh, vh, qh = kc.to("cpu"), vc.to("cpu"), q.cpu().numpy()
+    host = []
+    for kc, vc, q in layers[:4]:
+        host.append((kc.to("cpu"), vc.to("cpu"), q.cpu().numpy()))
     Hkv = desc.c.n_kv_heads
     t0 = time.perf_counter()
     done = 0
     while True:
+        kh, vh, qh = host[done % len(host)]
         oracle.attend(qh, [oracle.view_of(kh, vh)], Hkv, desc.c.scale)
         done += 1
-        if time.perf_counter() - t0 >= seconds or done >= 8:
+        if time.perf_counter() - t0 >= seconds or done >= 400:
             break
     dt = time.perf_counter() - t0
+    kc, vc, _ = layers[0]
     layer_bytes = kc.data.numel() * kc.data.element_size() + vc.data.numel() * vc.data.element_size()
     return {
         "value": round(done * layer_bytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} full layer(s) (40 q heads x 65536 keys, f16 K/V, unsplit, binary64) in {dt:.1f} s",
+        "sample": f"{done} whole layers (40 q heads x 65536 keys, f16 K/V, unsplit, binary64, cycling over "
+                  f"4 layers) in {dt:.1f} s",
+        "us_per_layer": round(dt / done * 1e6, 1),
     }
 
 

@@ -147,18 +147,32 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
     // compute unit hold at once (measured on the current device; 2 per unit
     // on 256 units when no device answers, e.g. for a size query on a host
     // without a GPU).  Every segment is cut into splits of the same number of
-    // 64-key tiles, a multiple of the waves per workgroup.
+    // 64-key tiles, a multiple of the waves per KV head.  A workgroup takes
+    // as many KV heads (a power of two) as it has waves, so that it reads whole
+    // spans of each position's heads; the rest of its waves split the tiles.
     int64_t tiles_total = 0;
     for (int i = 0; i < n; ++i) tiles_total += (v[i]->n_keys + kTile - 1) / kTile;
-    const int64_t nw = std::max(1, split_waves(kt, vt, D));
-    const int64_t units = (int64_t)Hkv * pl->n_rg * pl->z;
+    const int nw = std::max(1, split_waves(kt, vt, D, rt));
+    int hpw = 1;
+#ifndef RKV_HPW_MAX
+#define RKV_HPW_MAX 64
+#endif
+    while (2 * hpw <= nw && 2 * hpw <= Hkv && 2 * hpw <= RKV_HPW_MAX) hpw *= 2;
+    pl->nw = nw;
+    pl->hpw = hpw;
+    pl->n_hg = (Hkv + hpw - 1) / hpw;
+    const int64_t wph = nw / hpw;
+    const int64_t units = (int64_t)pl->n_hg * pl->n_rg * pl->z;
     int occ = split_occupancy(kt, vt, D, rt);
     int cus = compute_units();
     if (occ <= 0) occ = 2;
     if (cus <= 0) cus = 256;
-    const int64_t want_groups = std::max<int64_t>(1, (int64_t)occ * cus / units);
+#ifndef RKV_ROUNDS
+#define RKV_ROUNDS 1
+#endif
+    const int64_t want_groups = std::max<int64_t>(1, (int64_t)RKV_ROUNDS * occ * cus / units);
     int64_t tps = std::max<int64_t>(1, (tiles_total + want_groups - 1) / want_groups);
-    tps = (tps + nw - 1) / nw * nw;
+    tps = (tps + wph - 1) / wph * wph;
     if (tps * kTile > (1 << 30)) tps = (1 << 30) / kTile;
     int64_t n_splits = 0;
     if (prm) memset(prm, 0, sizeof *prm);
@@ -198,6 +212,12 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
         prm->scale = d->scale;
         prm->scale_log2 = d->scale * 1.4426950408889634f;
         prm->softcap = d->softcap;
+        prm->n_kv_heads = Hkv;
+        int hl = 0, wl = 0;
+        while ((1 << hl) < hpw) ++hl;
+        while ((1 << wl) < wph) ++wl;
+        prm->hpw_log2 = hl;
+        prm->wph_log2 = wl;
         for (int g = 0; g < Hkv; ++g) {
             prm->rowcnt[g] = (uint16_t)rows[g].size();
             for (size_t i = 0; i < rows[g].size(); ++i) prm->rowtab[g * rmax + i] = (uint16_t)rows[g][i];
@@ -229,7 +249,7 @@ int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view
         return fail(RKV_E_UNSUPPORTED, "no kernel for this (type, head_dim, rows)");
     float *part_acc = (float *)ws;
     float2 *part_ml = (float2 *)((char *)ws + pl.acc_bytes);
-    const dim3 grid((unsigned)pl.n_splits, (unsigned)(d->n_kv_heads * pl.n_rg), (unsigned)pl.z);
+    const dim3 grid((unsigned)pl.n_splits, (unsigned)(pl.n_hg * pl.n_rg), (unsigned)pl.z);
     RKV_HIP(launch_split(kt, vt, d->head_dim, pl.rt, grid, q, part_acc, part_ml, o, lse, prm, stream));
     if (pl.n_splits > 1) RKV_HIP(launch_reduce(d->head_dim, n_rows, pl.n_splits, part_acc, part_ml, o, lse, stream));
     return RKV_OK;

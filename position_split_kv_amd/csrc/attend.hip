@@ -8,7 +8,7 @@ namespace rkv {
 #define RKV_DECL(kt, vt)                                                                                  \
     hipError_t launch_split_k##kt##_v##vt(int d, int rt, dim3 grid, const float *q, float *pa, float2 *pm, \
                                           float *o, float *lse, const SplitParams &p, hipStream_t s);       \
-    int split_waves_k##kt##_v##vt(int d);                                                                 \
+    int split_waves_k##kt##_v##vt(int d, int rt);                                                         \
     int split_occupancy_k##kt##_v##vt(int d, int rt);
 #define RKV_DECL_K(kt) RKV_DECL(kt, 0) RKV_DECL(kt, 1) RKV_DECL(kt, 2) RKV_DECL(kt, 3)
 RKV_DECL_K(0)
@@ -24,10 +24,10 @@ bool split_supported(int kt, int vt, int d, int rt)
     return t && dd && r;
 }
 
-int split_waves(int kt, int vt, int d)
+int split_waves(int kt, int vt, int d, int rt)
 {
 #define RKV_NW(kk, vv) \
-    if (kt == kk && vt == vv) return split_waves_k##kk##_v##vv(d);
+    if (kt == kk && vt == vv) return split_waves_k##kk##_v##vv(d, rt);
 #define RKV_NW_K(kk) RKV_NW(kk, 0) RKV_NW(kk, 1) RKV_NW(kk, 2) RKV_NW(kk, 3)
     RKV_NW_K(0)
     RKV_NW_K(1)
@@ -97,74 +97,80 @@ hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q
     return hipErrorInvalidValue;
 }
 
-// Merge of the per-range partials of one row (partials are in log2 units):
+// Merge of the per-split partials of one row (partials are in log2 units):
 // M = max_i m_i, L = sum_i l_i 2^(m_i - M), o = sum_i acc_i 2^(m_i - M) / L,
-// lse = (M + log2 L) ln 2.  One 256-thread block per row: each group of D/4
-// threads (a float4 each) takes every NG-th range, then the groups are summed
-// in a fixed order, so the result is deterministic.
-template <int D>
+// lse = (M + log2 L) ln 2.  Block (row, 32-dim slice) of 256 threads: 32
+// groups of 8 lanes, lane c holding 4 dims.  Group j folds splits j, j+32,
+// j+64, ... in that order with the running-max rule (so no separate pass for
+// the maximum), then group 0 folds the 32 group results in order: the result
+// does not depend on timing.
 __global__ void __launch_bounds__(256)
 rkv_reduce_kernel(const float *__restrict__ part_acc, const float2 *__restrict__ part_ml, int n_splits,
-                  int64_t n_rows, float *__restrict__ o, float *__restrict__ lse)
+                  int64_t n_rows, int D, float *__restrict__ o, float *__restrict__ lse)
 {
-    constexpr int TPC = D / 4;     // threads per copy of the row
-    constexpr int NG = 256 / TPC;  // groups
-    __shared__ float sM[256];
-    __shared__ float4 sA[NG][TPC];
-    __shared__ float sL[NG];
+    __shared__ float sM[32], sL[32];
+    __shared__ float4 sA[32][8];
     const int64_t row = blockIdx.x;
-    const int t = threadIdx.x, grp = t / TPC, c = t - grp * TPC;
-    float M = -INFINITY;
-    for (int sp = t; sp < n_splits; sp += 256) M = fmaxf(M, part_ml[sp * n_rows + row].x);
-    sM[t] = M;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-        if (t < off) sM[t] = fmaxf(sM[t], sM[t + off]);
-        __syncthreads();
-    }
-    M = sM[0];
+    const int t = threadIdx.x, grp = t >> 3, c = t & 7;
+    const int d0 = blockIdx.y * 32 + 4 * c;
+    float m = -INFINITY, l = 0.f;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    float L = 0.f;
-#pragma unroll 4
-    for (int sp = grp; sp < n_splits; sp += NG) {
-        const float2 ml = part_ml[sp * n_rows + row];
-        const float wgt = exp2f(ml.x - M);
-        const float4 x = *(const float4 *)(part_acc + (sp * n_rows + row) * D + 4 * c);
-        L = fmaf(ml.y, wgt, L);
-        a.x = fmaf(x.x, wgt, a.x);
-        a.y = fmaf(x.y, wgt, a.y);
-        a.z = fmaf(x.z, wgt, a.z);
-        a.w = fmaf(x.w, wgt, a.w);
+    // batches of 8 splits per group, all loads of a batch issued together
+    // (indices past the end repeat a valid split and are not folded in)
+    for (int base = grp; base < n_splits; base += 32 * 8) {
+        float2 ml[8];
+        float4 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sp = base + 32 * u < n_splits ? base + 32 * u : base;
+            const int64_t idx = (int64_t)sp * n_rows + row;
+            ml[u] = part_ml[idx];
+            x[u] = *(const float4 *)(part_acc + idx * D + d0);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (base + 32 * u >= n_splits) break;
+            const float mn = fmaxf(m, ml[u].x);
+            const float fa = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+            const float fb = ml[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - mn);
+            l = l * fa + ml[u].y * fb;
+            a.x = a.x * fa + x[u].x * fb;
+            a.y = a.y * fa + x[u].y * fb;
+            a.z = a.z * fa + x[u].z * fb;
+            a.w = a.w * fa + x[u].w * fb;
+            m = mn;
+        }
+    }
+    if (c == 0) {
+        sM[grp] = m;
+        sL[grp] = l;
     }
     sA[grp][c] = a;
-    if (c == 0) sL[grp] = L;
     __syncthreads();
     if (grp == 0) {
-        float4 s = sA[0][c];
-        float Lt = sL[0];
-        for (int gg = 1; gg < NG; ++gg) {
-            s.x += sA[gg][c].x;
-            s.y += sA[gg][c].y;
-            s.z += sA[gg][c].z;
-            s.w += sA[gg][c].w;
-            Lt += sL[gg];
+        float M = -INFINITY;
+        for (int j = 0; j < 32; ++j) M = fmaxf(M, sM[j]);
+        float L = 0.f;
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < 32; ++j) {
+            const float f = sM[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sM[j] - M);
+            L = fmaf(sL[j], f, L);
+            s.x = fmaf(sA[j][c].x, f, s.x);
+            s.y = fmaf(sA[j][c].y, f, s.y);
+            s.z = fmaf(sA[j][c].z, f, s.z);
+            s.w = fmaf(sA[j][c].w, f, s.w);
         }
-        *(float4 *)(o + row * D + 4 * c) = make_float4(s.x / Lt, s.y / Lt, s.z / Lt, s.w / Lt);
-        if (c == 0) lse[row] = (M + log2f(Lt)) * 0.69314718055994531f;
+        *(float4 *)(o + row * D + d0) = make_float4(s.x / L, s.y / L, s.z / L, s.w / L);
+        if (blockIdx.y == 0 && c == 0) lse[row] = (M + log2f(L)) * 0.69314718055994531f;
     }
 }
 
 hipError_t launch_reduce(int d, int64_t n_rows, int n_splits, const float *pa, const float2 *pm, float *o,
                          float *lse, hipStream_t s)
 {
-    const dim3 grid((unsigned)n_rows), block(256);
-    switch (d) {
-    case 64: hipLaunchKernelGGL(rkv_reduce_kernel<64>, grid, block, 0, s, pa, pm, n_splits, n_rows, o, lse); break;
-    case 128: hipLaunchKernelGGL(rkv_reduce_kernel<128>, grid, block, 0, s, pa, pm, n_splits, n_rows, o, lse); break;
-    case 256: hipLaunchKernelGGL(rkv_reduce_kernel<256>, grid, block, 0, s, pa, pm, n_splits, n_rows, o, lse); break;
-    case 512: hipLaunchKernelGGL(rkv_reduce_kernel<512>, grid, block, 0, s, pa, pm, n_splits, n_rows, o, lse); break;
-    default: return hipErrorInvalidValue;
-    }
+    if (d % 32 || n_rows <= 0) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)n_rows, (unsigned)(d / 32)), block(256);
+    hipLaunchKernelGGL(rkv_reduce_kernel, grid, block, 0, s, pa, pm, n_splits, n_rows, d, o, lse);
     return hipGetLastError();
 }
 

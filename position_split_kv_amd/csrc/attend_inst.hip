@@ -19,7 +19,7 @@ static hipError_t go(dim3 grid, const float *q, float *pa, float2 *pm, float *o,
     if constexpr (D == 512 && (RKV_KT == kF32 || RKV_VT == kF32)) {
         return hipErrorInvalidValue;  // an f32 row of 512 values does not fit the LDS tile
     } else {
-        hipLaunchKernelGGL((rkv_split_kernel<RKV_KT, RKV_VT, D, RT>), grid, dim3(64 * Shape<RKV_KT, RKV_VT, D>::NW), 0,
+        hipLaunchKernelGGL((rkv_split_kernel<RKV_KT, RKV_VT, D, RT>), grid, dim3(64 * Shape<RKV_KT, RKV_VT, D>::waves(RT)), 0,
                            stream, q, pa, pm, o, lse, p);
         return hipGetLastError();
     }
@@ -60,7 +60,7 @@ static int occ_of()
     } else {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rkv_split_kernel<RKV_KT, RKV_VT, D, RT>,
-                                                         64 * Shape<RKV_KT, RKV_VT, D>::NW, 0) != hipSuccess) {
+                                                         64 * Shape<RKV_KT, RKV_VT, D>::waves(RT), 0) != hipSuccess) {
             (void)hipGetLastError();
             return 0;
         }
@@ -95,14 +95,30 @@ int RKV_NAME_OCC(RKV_KT, RKV_VT)(int d, int rt)
     }
 }
 
+template <int D>
+static int nw_by_rt(int rt)
+{
+    using Sh = Shape<RKV_KT, RKV_VT, D>;
+    switch (rt) {
+    case 1: return Sh::waves(1);
+    case 2: return Sh::waves(2);
+    case 4: return Sh::waves(4);
+    case 5: return Sh::waves(5);
+    case 8: return Sh::waves(8);
+    case 16: return Sh::waves(16);
+    default: return 0;
+    }
+}
+
 #define RKV_NAME_NW(kt, vt) RKV_CAT4(split_waves_k, kt, _v, vt)
-int RKV_NAME_NW(RKV_KT, RKV_VT)(int d)
+// Waves per workgroup of an instance.
+int RKV_NAME_NW(RKV_KT, RKV_VT)(int d, int rt)
 {
     switch (d) {
-    case 64: return Shape<RKV_KT, RKV_VT, 64>::NW;
-    case 128: return Shape<RKV_KT, RKV_VT, 128>::NW;
-    case 256: return Shape<RKV_KT, RKV_VT, 256>::NW;
-    case 512: return Shape<RKV_KT, RKV_VT, 512>::NW;
+    case 64: return nw_by_rt<64>(rt);
+    case 128: return nw_by_rt<128>(rt);
+    case 256: return nw_by_rt<256>(rt);
+    case 512: return nw_by_rt<512>(rt);
     default: return 0;
     }
 }

@@ -1,10 +1,16 @@
 // attend_kernel.h -- split-K flash-decode kernel for one segment of the cache.
 //
-// A workgroup of NW waves owns one work item: a KV head g, a group of RT query
-// rows that attend g (all GQA rows of g, and for a segment shared by every
-// sequence, those rows of every sequence), and a contiguous range of the
-// segment's keys.  Wave w walks tiles w, w+NW, w+2NW, ... of the range, 64
-// keys per tile:
+// A workgroup of NW waves owns a key range of a segment and HPW KV heads
+// (HPW a power of two, chosen at launch; NW / HPW = WPH waves per head).  For
+// its head g each wave owns a group of RT query rows that attend g (all GQA
+// rows of g, and for a segment shared by every sequence, those rows of every
+// sequence).  The waves of a head walk tiles ws, ws+WPH, ws+2WPH, ... of the
+// range (ws = the wave's index among them), 64 keys per tile.  With HPW > 1
+// the waves of one workgroup read neighbouring heads' rows of the same
+// positions at the same time, so each position is read as one contiguous
+// span: that is what lets the position-major cache stream at the HBM rate
+// (reading one head's slice of every position from separate workgroups runs
+// about a third slower).  Per tile:
 //
 //   1. the K rows of the tile (and V rows when they are block-quantised or
 //      wide) are copied with coalesced vector loads into the wave's LDS area,
@@ -22,13 +28,14 @@
 //   4. P.V: lanes are (key-in-step, 8-dim group); each lane accumulates its 8
 //      dims for every row over the tile's keys.
 //
-// At the end the NW waves merge their (m, l, acc) in LDS.  A launch that is
-// one workgroup per work item writes its normalised output and LSE directly;
-// otherwise each workgroup writes a partial and a second, fixed-order kernel
-// merges them (the same LSE arithmetic as the segment combine), so the
-// results are deterministic.  (A merge by the last workgroup to finish was
-// measured slower: handing partials between workgroups inside a kernel needs
-// device-scope release fences, which write back the L2 of each XCD.)
+// At the end the waves of each head merge their (m, l, acc) in LDS.  A launch
+// that is one workgroup per work item writes its normalised output and LSE
+// directly; otherwise each workgroup writes a partial and a second,
+// fixed-order kernel merges them (the same LSE arithmetic as the segment
+// combine), so the results are deterministic.  (A merge by the last
+// workgroup to finish was measured slower: handing partials between
+// workgroups inside a kernel needs device-scope release fences, which write
+// back the L2 of each XCD.)
 //
 // This is the in-register reading of window and tail at their own types that
 // "F5 M7 -- Rolling KV" ships (section "2026-07-12 -- #582-P2 SHIPPED"), with
@@ -65,10 +72,17 @@ struct Shape {
     static constexpr bool V_REG = (VT == kF16 && D <= 128) || (VT == kF32 && D <= 64);
     static constexpr int LSV = V_REG ? 0 : lds_row_dwords(RBV);
     static constexpr int STAGE_DW = kTile * (LSK + LSV) + 8;  // per wave: K (+ V) rows plus read slack
-    // waves per workgroup: as many as fit 160 KiB of LDS with their staging
-    // and score rows (sized for 16 rows per wave)
-    static constexpr int WAVE_BYTES = STAGE_DW * 4 + 16 * kTile * 4;
-    static constexpr int NW = 4 * WAVE_BYTES <= 160 * 1024 ? 4 : 2 * WAVE_BYTES <= 160 * 1024 ? 2 : 1;
+    // LDS bytes of a workgroup of nw waves with rt rows each: the staging
+    // areas (reused for the final merge) and the score rows
+    static constexpr int lds_bytes(int nw, int rt)
+    {
+        return 4 * (nw * STAGE_DW > nw * rt * (D + 2) ? nw * STAGE_DW : nw * rt * (D + 2)) + 4 * nw * rt * kTile;
+    }
+    // waves per workgroup: as many (up to 8) as fit 160 KiB of LDS
+    static constexpr int waves(int rt)
+    {
+        return lds_bytes(8, rt) <= 160 * 1024 ? 8 : lds_bytes(4, rt) <= 160 * 1024 ? 4 : lds_bytes(2, rt) <= 160 * 1024 ? 2 : 1;
+    }
 };
 
 // ---------------------------------------------------------------- small helpers
@@ -546,12 +560,12 @@ __device__ __forceinline__ float v_group_lds(const uint32_t *row, int dg, float 
 // ---------------------------------------------------------------- the kernel
 
 template <int KT, int VT, int D, int RT>
-__global__ void __launch_bounds__((64 * Shape<KT, VT, D>::NW))
+__global__ void __launch_bounds__((64 * Shape<KT, VT, D>::waves(RT)))
 rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, float2 *__restrict__ part_ml,
                  float *__restrict__ o_out, float *__restrict__ lse_out, const SplitParams p)
 {
     using Sh = Shape<KT, VT, D>;
-    constexpr int NW = Sh::NW;
+    constexpr int NW = Sh::waves(RT);
     constexpr int LSK = Sh::LSK, LSV = Sh::LSV;
     constexpr bool V_REG = Sh::V_REG;
     constexpr int VWK = load_width_of(KT, D);
@@ -571,11 +585,15 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     uint32_t *sK = smem + w * Sh::STAGE_DW;
     uint32_t *sV = sK + kTile * LSK;
 
-    const int g = blockIdx.y / p.n_rg;
-    const int rg = blockIdx.y - g * p.n_rg;
-    const int cnt = (int)p.rowcnt[g] - rg * RT;
-    if (cnt <= 0) return;
-    const int nr = cnt < RT ? cnt : RT;
+    // this wave's head slot hs and its index ws among the head's waves
+    const int hg = blockIdx.y / p.n_rg;
+    const int rg = blockIdx.y - hg * p.n_rg;
+    const int wph = 1 << p.wph_log2;
+    const int hs = w >> p.wph_log2;
+    const int ws = w - hs * wph;
+    const int g = (hg << p.hpw_log2) + hs;
+    const int cnt = g < p.n_kv_heads ? (int)p.rowcnt[g] - rg * RT : 0;
+    const int nr = cnt <= 0 ? 0 : cnt < RT ? cnt : RT;  // 0: a wave with no rows (it still joins the barriers)
     const int z = blockIdx.z;
 
     // the segment this workgroup's key split belongs to
@@ -584,7 +602,8 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     for (int si = 1; si < kMaxSegs; ++si)
         if (si < p.n_segs && (int)blockIdx.x >= p.seg[si].split_base) sg = p.seg[si];
     const int64_t kbeg = (int64_t)((int)blockIdx.x - sg.split_base) * sg.keys_per_split;
-    const int64_t kend = kbeg + sg.keys_per_split < sg.n_keys ? kbeg + sg.keys_per_split : sg.n_keys;
+    const int64_t kend = nr == 0 ? kbeg : kbeg + sg.keys_per_split < sg.n_keys ? kbeg + sg.keys_per_split : sg.n_keys;
+    const int64_t tstep = (int64_t)wph * kTile;  // tile stride of this wave
 
     const uint8_t *kg = sg.k + z * sg.k_seq + g * sg.k_head;
     const uint8_t *vg = sg.v + z * sg.v_seq + g * sg.v_head;
@@ -594,7 +613,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
         const int rr = r < nr ? r : nr - 1;  // padding rows repeat the last row; never written
-        rid[r] = z * p.z_row_step + p.rowtab[g * p.rows_per_g + rg * RT + rr];
+        rid[r] = nr == 0 ? 0 : z * p.z_row_step + p.rowtab[g * p.rows_per_g + rg * RT + rr];
         qp[r] = q + rid[r] * D;
     }
 
@@ -689,7 +708,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     static_assert(2 * NV <= 63, "vmcnt range");
     const int sw = kswz<Sh::RBK>(lane);
 
-    int64_t t0 = kbeg + (int64_t)w * kTile;
+    int64_t t0 = kbeg + (int64_t)ws * kTile;
     // VMEM loads issued after the K rows' DMA that may stay outstanding when
     // the scores start: 0, NV or 2*NV
     int v_after_dma = 0;
@@ -699,7 +718,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             if constexpr (VDB) {
                 load_vreg(t0, nk_at(t0));
                 v_after_dma = NV;
-                const int64_t t1 = t0 + (int64_t)NW * kTile;
+                const int64_t t1 = t0 + tstep;
                 if (t1 < kend) {
                     load_v_into(vnx, t1, nk_at(t1));
                     v_after_dma = 2 * NV;
@@ -713,9 +732,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             else load_rows(vr, vg + t0 * sg.v_pos, (int)sg.v_pos, nk_at(t0), lane);
         }
     }
-    for (; t0 < kend; t0 += (int64_t)NW * kTile) {
+    for (; t0 < kend; t0 += tstep) {
         const int nk = nk_at(t0);
-        const int64_t tn = t0 + (int64_t)NW * kTile;
+        const int64_t tn = t0 + tstep;
         if constexpr (KDMA) {
             // K rows arrive by DMA issued one tile ahead; V rows load now and
             // are in flight during the scores (holding two tiles of V in
@@ -822,7 +841,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             for (int st = 0; st < NSTEP; ++st)
 #pragma unroll
                 for (int e = 0; e < VRW; ++e) vreg[st][e] = vnx[st][e];
-            const int64_t tnn = tn + (int64_t)NW * kTile;
+            const int64_t tnn = tn + tstep;
             v_after_dma = 0;
             if (tnn < kend) {
                 load_v_into(vnx, tnn, nk_at(tnn));
@@ -862,27 +881,27 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         }
         __syncthreads();
     }
-    // Thread t finalises (row r, dim d) pairs; a wave with no keys has m = -inf
-    // and weight 0.
+    // Thread t finalises (head slot, row, dim) triples, merging the waves of
+    // the head slot; a wave with no keys has m = -inf and weight 0.
     const bool single = p.n_splits == 1;
     const int64_t pbase = (int64_t)blockIdx.x * p.n_rows_total;
-    for (int i = threadIdx.x; i < nr * D; i += 64 * NW) {
-        const int r = i / D, d = i - r * D;
+    const int hpw = 1 << p.hpw_log2;
+    for (int i = threadIdx.x; i < hpw * RT * D; i += 64 * NW) {
+        const int h = i / (RT * D);
+        const int r = (i - h * RT * D) / D, d = i - (h * RT + r) * D;
+        const int gh = (hg << p.hpw_log2) + h;
+        if (gh >= p.n_kv_heads || r >= (int)p.rowcnt[gh] - rg * RT) continue;
+        const int w0 = h * wph;
         float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mML[(ww * RT + r) * 2]);
+        for (int ww = w0; ww < w0 + wph; ++ww) M = fmaxf(M, mML[(ww * RT + r) * 2]);
         float L = 0.f, A = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
+        for (int ww = w0; ww < w0 + wph; ++ww) {
             const float mw = mML[(ww * RT + r) * 2];
             const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
             L = fmaf(mML[(ww * RT + r) * 2 + 1], f, L);
             A = fmaf(mA[(ww * RT + r) * D + d], f, A);
         }
-        int rr = 0;
-#pragma unroll
-        for (int x = 0; x < RT; ++x)
-            if (x == r) rr = rid[x];
+        const int rr = z * p.z_row_step + p.rowtab[gh * p.rows_per_g + rg * RT + r];
         if (single) {
             o_out[(int64_t)rr * D + d] = A / L;
             if (d == 0) lse_out[rr] = (M + log2f(L)) * 0.69314718055994531f;

@@ -52,6 +52,9 @@ struct SplitParams {
     float scale;           // score scale
     float scale_log2;      // scale * log2(e)
     float softcap;         // natural units, 0 = off
+    int32_t n_kv_heads;
+    int32_t hpw_log2;      // log2 of the KV heads per workgroup
+    int32_t wph_log2;      // log2 of the waves per KV head (waves per workgroup / heads per workgroup)
     uint16_t rowcnt[kMaxKvHeads];
     uint16_t rowtab[kMaxRowTable];
 };
@@ -59,6 +62,9 @@ struct SplitParams {
 // How a launch is cut into work: shared by the workspace query and the launch.
 struct SplitPlan {
     int rt;          // rows per wave (template instance)
+    int nw;          // waves per workgroup of that instance
+    int hpw;         // KV heads per workgroup
+    int n_hg;        // head groups (grid y = n_hg * n_rg)
     int n_rg;        // row groups per KV head
     int rows_per_g;  // max rows of a KV head
     int z;           // grid z (sequences with own keys, or 1)
@@ -79,7 +85,7 @@ hipError_t launch_reduce(int d, int64_t n_rows, int n_splits, const float *part_
                          float *o, float *lse, hipStream_t stream);
 bool split_supported(int kt, int vt, int d, int rt);
 // Waves per workgroup of the split kernel for a (K type, V type, head_dim).
-int split_waves(int kt, int vt, int d);
+int split_waves(int kt, int vt, int d, int rt);
 // Workgroups of a split-kernel instance resident per compute unit on the
 // current device, and the device's compute units (0 when no device answers).
 int split_occupancy(int kt, int vt, int d, int rt);
