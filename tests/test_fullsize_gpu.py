@@ -1,0 +1,135 @@
+"""GPU parity at the full sizes of the five workloads, in the launch
+configuration the benchmark times, on sampled query rows that the binary64
+oracle computes one by one (every sampled row still attends every key).
+
+  - Qwen2.5-14B-shaped f16 layer: 40/8 heads, D 128, 65536 keys (1 % outlier
+    channels x8), window 49152 + tail 16384, one rkv_attend_split launch (the
+    bench step) and the three-call form;
+  - Gemma-style global layer: 16/2 heads, D 512, 262144 q8_0 keys, softcap 30,
+    window 196608 + tail 65536; plus the scale-1.0 softcap stress variant;
+  - streamed tail: q8_0 K / q4_0 V, 40/8 heads, 131072 keys, window 65536 on
+    the device, tail 65536 in pinned host memory in 8192-key tiles through a
+    3-slot ring (2 layers);
+  - shared prefix: 15 sequences x 32/8 heads; a 32768-key q8_0 / q4_0 prefix
+    stored once plus a private 2048-key f16 suffix per sequence.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import position_split_kv_amd as P
+import synth
+from gpu_util import attend_views, compare, note, pair
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _oracle_threads():
+    oracle.set_threads(min(16, oracle.max_threads()))
+
+
+def host_views(kc, vc, cuts=None):
+    kh, vh = kc.to("cpu"), vc.to("cpu")
+    return [oracle.view_of(kh, vh)], (kh, vh)
+
+
+def test_qwen14b_f16_layer_full():
+    S, Hq, Hkv, D, n, wc = 1, 40, 8, 128, 65536, 49152
+    note(f"full size f16: Hq={Hq} Hkv={Hkv} D={D} n={n} wc={wc}, 10 outlier channels")
+    kc, vc = pair(n, Hkv, D, synth.F16, synth.F16, 20001, DEV, outliers=round(0.01 * Hkv * D))
+    q = synth.make_query(S, Hq, D, synth.stream_seed(20001, 3), DEV)
+    desc = P.Desc(S, Hq, Hkv, D, 1.0 / math.sqrt(D))
+    segs = [P.view_of_cache(kc, vc, 0, wc), P.view_of_cache(kc, vc, wc, n)]
+    o1, l1 = P.attend_split(desc, q, segs)
+    o3, l3 = attend_views(desc, q, segs)
+    torch.cuda.synchronize()
+    rows = [0, 4, 5, 13, 22, 26, 31, 39]  # every KV head's first or last row among them
+    views, _ = host_views(kc, vc)
+    o_ref, l_ref = oracle.attend(q.cpu().numpy(), views, Hkv, 1.0 / math.sqrt(D), rows=rows)
+    compare(o1, l1, o_ref, l_ref, rows=rows, what="one launch (bench step)")
+    compare(o3, l3, o_ref, l_ref, rows=rows, what="segment, segment, combine")
+
+
+@pytest.mark.parametrize("scale", [None, 1.0], ids=["scale_1_over_sqrt_d", "stress_scale_1"])
+def test_gemma_q8_d512_softcap_full(scale):
+    S, Hq, Hkv, D, n, wc, cap = 1, 16, 2, 512, 262144, 196608, 30.0
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    note(f"full size q8_0 D512 softcap {cap}: n={n} wc={wc} scale={sc:.5f}")
+    kc, vc = pair(n, Hkv, D, synth.Q8_0, synth.Q8_0, 30001, DEV)
+    q = synth.make_query(S, Hq, D, synth.stream_seed(30001, 3), DEV)
+    desc = P.Desc(S, Hq, Hkv, D, sc, cap)
+    segs = [P.view_of_cache(kc, vc, 0, wc), P.view_of_cache(kc, vc, wc, n)]
+    o1, l1 = P.attend_split(desc, q, segs)
+    torch.cuda.synchronize()
+    rows = [0, 7, 8, 15]
+    views, _ = host_views(kc, vc)
+    o_ref, l_ref = oracle.attend(q.cpu().numpy(), views, Hkv, sc, softcap=cap, rows=rows)
+    compare(o1, l1, o_ref, l_ref, rows=rows, what="q8_0 D512 softcap")
+    if scale is not None:
+        # the cap must matter at this scale: the uncapped result is far away
+        o_nc, l_nc = oracle.attend(q.cpu().numpy(), views, Hkv, sc, softcap=0.0, rows=rows)
+        assert np.max(np.abs(l_nc - l_ref)) > 1e-2
+
+
+def test_streamed_tail_full():
+    L, S, Hq, Hkv, D, n, wc, tile, B = 2, 1, 40, 8, 128, 131072, 65536, 8192, 3
+    note(f"full size streamed tail: {L} layers, n={n} wc={wc} tile={tile} B={B}, q8_0 K / q4_0 V")
+    desc = P.Desc(S, Hq, Hkv, D, 1.0 / math.sqrt(D))
+    layers = []
+    for li in range(L):
+        kc, vc = pair(n, Hkv, D, synth.Q8_0, synth.Q4_0, 40001 + li, DEV)
+        q = synth.make_query(S, Hq, D, synth.stream_seed(40001, 3, li), DEV)
+        kh = torch.empty(kc.data[wc:].shape, dtype=kc.data.dtype, pin_memory=True)
+        vh = torch.empty(vc.data[wc:].shape, dtype=vc.data.dtype, pin_memory=True)
+        kh.copy_(kc.data[wc:])
+        vh.copy_(vc.data[wc:])
+        layers.append((kc, vc, q, synth.Cache(kh, kc.dtype, n - wc, Hkv, D), synth.Cache(vh, vc.dtype, n - wc, Hkv, D)))
+    torch.cuda.synchronize()
+    ring = P.Ring(B, tile * layers[0][0].pos_stride, tile * layers[0][1].pos_stride)
+    outs = []
+    try:
+        ring.rkv_ring_begin_step([P.view_of_cache(t[3], t[4]) for t in layers], tile)
+        for li, (kc, vc, q, _, _) in enumerate(layers):
+            o_w, l_w = P.attend(desc, q, P.view_of_cache(kc, vc, 0, wc))
+            ws = P.workspace(ring.rkv_stream_tail_workspace_bytes(li, desc))
+            o = torch.empty_like(q)
+            lse = torch.empty(S, Hq, device=DEV)
+            ring.rkv_stream_tail(li, desc, q, o_w, l_w, o, lse, ws)
+            outs.append((o, lse))
+        ring.rkv_ring_end_step()
+        torch.cuda.synchronize()
+    finally:
+        ring.close()
+    rows = [0, 9, 17, 24, 39]
+    for li, (kc, vc, q, _, _) in enumerate(layers):
+        views = [P.view_of_cache(kc, vc, 0, wc)] + [P.view_of_cache(kc, vc, a, a + tile) for a in range(wc, n, tile)]
+        o_r, l_r = attend_views(desc, q, views)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[li][0], o_r) and torch.equal(outs[li][1], l_r), f"layer {li}: streamed != resident"
+        hv, _ = host_views(kc, vc)
+        o_ref, l_ref = oracle.attend(q.cpu().numpy(), hv, Hkv, 1.0 / math.sqrt(D), rows=rows)
+        compare(outs[li][0], outs[li][1], o_ref, l_ref, rows=rows, what=f"streamed layer {li}")
+
+
+def test_shared_prefix_full():
+    S, Hq, Hkv, D, npre, nsuf = 15, 32, 8, 128, 32768, 2048
+    note(f"full size shared prefix: S={S} Hq={Hq} Hkv={Hkv} prefix={npre} q8_0/q4_0, suffix={nsuf} f16")
+    pk, pv = pair(npre, Hkv, D, synth.Q8_0, synth.Q4_0, 50001, DEV)
+    sk, sv = pair(S * nsuf, Hkv, D, synth.F16, synth.F16, 50002, DEV)
+    q = synth.make_query(S, Hq, D, synth.stream_seed(50001, 3), DEV)
+    desc = P.Desc(S, Hq, Hkv, D, 1.0 / math.sqrt(D))
+    prefix = P.view_of_cache(pk, pv)
+    suffix = P.view_of_cache(sk, sv, 0, nsuf, nsuf * sk.pos_stride, nsuf * sv.pos_stride)
+    o, l = attend_views(desc, q, [prefix, suffix])
+    torch.cuda.synchronize()
+    pkh, pvh, skh, svh = pk.to("cpu"), pv.to("cpu"), sk.to("cpu"), sv.to("cpu")
+    views = [oracle.view_of(pkh, pvh), oracle.view_of(skh, svh, 0, nsuf, nsuf * sk.pos_stride, nsuf * sv.pos_stride)]
+    rows = [0, 31, 32 * 7 + 5, 32 * 7 + 30, 32 * 14, 32 * 14 + 31]
+    o_ref, l_ref = oracle.attend(q.cpu().numpy(), views, Hkv, 1.0 / math.sqrt(D), rows=rows)
+    compare(o, l, o_ref, l_ref, rows=rows, what="prefix + suffix")

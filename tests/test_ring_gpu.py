@@ -1,0 +1,148 @@
+"""GPU: the pinned-host tail ring (rkv_ring_* / rkv_stream_tail).
+
+A tail held in pinned host memory, cut into tiles and streamed through a
+B-slot device ring, must give bit for bit what the same tiles give when they
+are resident in device memory (rkv_attend_segment per tile, then
+rkv_lse_combine in the order window, tile 0, tile 1, ...), whatever B is, and
+must match the binary64 oracle over the whole unsplit cache.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import position_split_kv_amd as P
+import synth
+from gpu_util import attend_views, compare, note, pair
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def pinned_copy(cache, start, stop):
+    """The positions [start, stop) of a device cache, in pinned host memory."""
+    host = torch.empty(cache.data[start:stop].shape, dtype=cache.data.dtype, pin_memory=True)
+    host.copy_(cache.data[start:stop])
+    return synth.Cache(host, cache.dtype, stop - start, cache.n_kv_heads, cache.head_dim)
+
+
+def make_layers(L, n, wcs, Hq, Hkv, D, kt, vt, seed):
+    layers = []
+    for li in range(L):
+        kc, vc = pair(n, Hkv, D, kt, vt, seed + 101 * li, DEV)
+        q = synth.make_query(1, Hq, D, synth.stream_seed(seed, 3, li), DEV)
+        wc = wcs[li]
+        layers.append(dict(kc=kc, vc=vc, q=q, wc=wc, kh=pinned_copy(kc, wc, n), vh=pinned_copy(vc, wc, n)))
+    torch.cuda.synchronize()
+    return layers
+
+
+def run_streamed(layers, desc, B, tile, n):
+    kc0, vc0 = layers[0]["kc"], layers[0]["vc"]
+    ring = P.Ring(B, tile * kc0.pos_stride, tile * vc0.pos_stride)
+    stream = torch.cuda.current_stream()
+    outs = []
+    try:
+        ring.rkv_ring_begin_step([P.view_of_cache(L_["kh"], L_["vh"]) for L_ in layers], tile)
+        for li, L_ in enumerate(layers):
+            if L_["wc"] > 0:
+                o_w, l_w = P.attend(desc, L_["q"], P.view_of_cache(L_["kc"], L_["vc"], 0, L_["wc"]), stream)
+            else:
+                o_w, l_w = None, None
+            ws = P.workspace(ring.rkv_stream_tail_workspace_bytes(li, desc))
+            o = torch.empty_like(L_["q"])
+            lse = torch.empty(L_["q"].shape[:2], dtype=torch.float32, device=DEV)
+            ring.rkv_stream_tail(li, desc, L_["q"], o_w, l_w, o, lse, ws, stream)
+            outs.append((o, lse))
+        ring.rkv_ring_end_step()
+        torch.cuda.synchronize()
+    finally:
+        ring.close()
+    return outs
+
+
+def resident(L_, desc, tile, n):
+    views = []
+    if L_["wc"] > 0:
+        views.append(P.view_of_cache(L_["kc"], L_["vc"], 0, L_["wc"]))
+    for a in range(L_["wc"], n, tile):
+        views.append(P.view_of_cache(L_["kc"], L_["vc"], a, min(n, a + tile)))
+    return attend_views(desc, L_["q"], views)
+
+
+@pytest.mark.parametrize("B", [2, 3, 4])
+def test_stream_tail_bit_identical_to_resident(B):
+    """q8_0 K / q4_0 V, 40/8 heads, D 128; 3 layers whose tails (2000 keys) are
+    cut into 512-key tiles (the last one partial)."""
+    L, n, Hq, Hkv, D, tile = 3, 4000, 40, 8, 128, 512
+    note(f"ring B={B}: {L} layers, n={n}, wc=2000, tile={tile}, q8_0 K / q4_0 V")
+    layers = make_layers(L, n, [2000] * L, Hq, Hkv, D, synth.Q8_0, synth.Q4_0, 7000 + B)
+    desc = P.Desc(1, Hq, Hkv, D, 1.0 / math.sqrt(D))
+    outs = run_streamed(layers, desc, B, tile, n)
+    for li, L_ in enumerate(layers):
+        o_r, l_r = resident(L_, desc, tile, n)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[li][0], o_r), f"layer {li}: streamed O differs from resident tiles"
+        assert torch.equal(outs[li][1], l_r), f"layer {li}: streamed LSE differs from resident tiles"
+    # and the oracle over the whole unsplit cache of layer 1
+    L_ = layers[1]
+    o_ref, l_ref = oracle.attend(L_["q"].cpu().numpy(), [oracle.view_of(L_["kc"].to("cpu"), L_["vc"].to("cpu"))],
+                                 Hkv, 1.0 / math.sqrt(D))
+    compare(outs[1][0], outs[1][1], o_ref, l_ref, what=f"ring B={B} vs oracle")
+
+
+def test_stream_tail_edge_layers():
+    """A layer with no window (wc = 0), a layer with an empty tail (the window
+    result comes back bit for bit), and a tail shorter than one tile."""
+    n, Hq, Hkv, D, tile = 1500, 8, 2, 128, 1024
+    wcs = [0, n, 1000]
+    note(f"ring edge layers: wc = {wcs}, n={n}, tile={tile}, f16")
+    layers = make_layers(3, n, wcs, Hq, Hkv, D, synth.F16, synth.F16, 8100)
+    desc = P.Desc(1, Hq, Hkv, D, 1.0 / math.sqrt(D))
+    outs = run_streamed(layers, desc, 2, tile, n)
+    for li, L_ in enumerate(layers):
+        o_r, l_r = resident(L_, desc, tile, n)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[li][0], o_r) and torch.equal(outs[li][1], l_r), f"layer {li}"
+        o_ref, l_ref = oracle.attend(L_["q"].cpu().numpy(),
+                                     [oracle.view_of(L_["kc"].to("cpu"), L_["vc"].to("cpu"))], Hkv,
+                                     1.0 / math.sqrt(D))
+        compare(outs[li][0], outs[li][1], o_ref, l_ref, what=f"edge layer {li} (wc={wcs[li]})")
+
+
+def test_ring_state_errors():
+    """Out-of-order layers, an early end of step, a second begin, and a tail in
+    device memory are refused with the documented status; every check happens
+    on the host before the offending work is enqueued."""
+    n, Hq, Hkv, D, tile = 1024, 8, 2, 128, 256
+    note("ring state errors")
+    layers = make_layers(2, n, [512, 512], Hq, Hkv, D, synth.F16, synth.F16, 8200)
+    desc = P.Desc(1, Hq, Hkv, D, 1.0 / math.sqrt(D))
+    kc0, vc0 = layers[0]["kc"], layers[0]["vc"]
+    ring = P.Ring(2, tile * kc0.pos_stride, tile * vc0.pos_stride)
+    try:
+        # a tail in device memory
+        with pytest.raises(P.RkvError) as e:
+            ring.rkv_ring_begin_step([P.view_of_cache(kc0, vc0, 512, n)], tile)
+        assert e.value.code == P.RKV_E_INVAL
+        ring.rkv_ring_begin_step([P.view_of_cache(L_["kh"], L_["vh"]) for L_ in layers], tile)
+        with pytest.raises(P.RkvError) as e:
+            ring.rkv_ring_begin_step([P.view_of_cache(L_["kh"], L_["vh"]) for L_ in layers], tile)
+        assert e.value.code == P.RKV_E_STATE
+        q = layers[1]["q"]
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+        ws = P.workspace(1 << 20)
+        with pytest.raises(P.RkvError) as e:  # layer 1 before layer 0
+            ring.rkv_stream_tail(1, desc, q, None, None, o, lse, ws)
+        assert e.value.code == P.RKV_E_STATE
+        ring.rkv_stream_tail(0, desc, layers[0]["q"], None, None, o, lse, ws)
+        with pytest.raises(P.RkvError) as e:  # one layer left
+            ring.rkv_ring_end_step()
+        assert e.value.code == P.RKV_E_STATE
+        torch.cuda.synchronize()
+    finally:
+        ring.close()
