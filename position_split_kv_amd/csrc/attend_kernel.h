@@ -500,6 +500,90 @@ __device__ __forceinline__ void key_dots(const uint32_t *row, const float *const
     }
 }
 
+// ---------------------------------------------------------------- MFMA scores
+
+typedef _Float16 rkv_half8 __attribute__((ext_vector_type(8)));
+typedef float rkv_float4v __attribute__((ext_vector_type(4)));
+
+// Maximum / sum over each group of 16 lanes (a DPP row), in every lane of it.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float x)
+{
+    x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
+    return fmaxf(x, dpp_mov<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    x += dpp_mov<0x141>(x);
+    return x + dpp_mov<0x140>(x);
+}
+
+// The query rows of a wave as the A operand of v_mfma_f32_16x16x32_f16: lane
+// l holds row l % 16, dims 32*kk + 8*(l / 16) .. +7 of chunk kk, each value
+// pre-multiplied by scale * log2(e) and split into binary16 high and low
+// parts (hi + lo keeps about 22 significant bits, so the products, exact in
+// the f32 accumulator, carry the f32 query).  Rows >= nr are zero.
+template <int D>
+__device__ __forceinline__ void mfma_q(const float *qrow, bool has, float sl2, int lane, rkv_half8 *qhi, rkv_half8 *qlo)
+{
+    const int kq = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        float x[8];
+        if (has) {
+            const float4 a = *(const float4 *)(qrow + 32 * kk + 8 * kq);
+            const float4 b = *(const float4 *)(qrow + 32 * kk + 8 * kq + 4);
+            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float y = x[e] * sl2;
+            const _Float16 h = (_Float16)y;
+            qhi[kk][e] = h;
+            qlo[kk][e] = (_Float16)(y - (float)h);
+        }
+    }
+}
+
+// Scores (log2 units) of the 64 keys of a DMA-staged f16 K tile against the
+// wave's query rows: sv[kb][i] = score of row 4*(lane/16) + i and key
+// 16*kb + lane % 16.  The B operand of chunk kk for key row j is the 16-byte
+// chunk 4*kk + lane/16 of that row (swizzled slot in LDS).
+template <int D, int RB>
+__device__ __forceinline__ void mfma_scores(const uint32_t *tile, const rkv_half8 *qhi, const rkv_half8 *qlo, int lane,
+                                            float (*sv)[4])
+{
+    rkv_float4v acc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) acc[kb] = rkv_float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int j = 16 * kb + (lane & 15);
+            const int c = 4 * kk + (lane >> 4);
+            const rkv_half8 b = *(const rkv_half8 *)(tile + j * (RB / 4) + 4 * (c ^ kswz<RB>(j)));
+            acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi[kk], b, acc[kb], 0, 0, 0);
+            acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo[kk], b, acc[kb], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[kb][i] = acc[kb][i];
+}
+
 // ---------------------------------------------------------------- values
 
 // 8 consecutive values (dims 8*dg .. 8*dg+7) of a V row held in LDS, as
@@ -625,12 +709,48 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
     }
+    rkv_float4v oc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) oc[c] = rkv_float4v{0.f, 0.f, 0.f, 0.f};
 
     const int ks = lane / LPR;
     const int dg = lane - ks * LPR;
     const float sl2 = p.scale_log2;
     const float cap = p.softcap;
     constexpr float kLog2e = 1.4426950408889634f;
+    const float scale_over_cap = cap > 0.f ? p.scale / cap : 0.f;
+
+    // Scores on the matrix cores: f16 K tiles staged by DMA, up to 16 query
+    // rows per wave as the 16-row A operand.  Running max and denominator are
+    // then kept per lane for the rows 4*(lane/16) .. +3 (mrow / lrow) and the
+    // wave-uniform m[] follows them.
+    constexpr bool MFMA_S = KT == kF16 && Sh::KDMA && D <= 128 && RT <= 16;
+    // P.V on the matrix cores as well, for f16 V rows of 128 values held in
+    // registers: lane (g = lane/16, n = lane%16) holds, for step st, the 8
+    // values of key 4*st + g at dims 8n .. 8n+7.  Taking as contraction index
+    // k = 8g + e the key 4*(8*kb + e) + g, and as output column n the dim
+    // 8n + c, every B-operand value a lane needs (element c of steps
+    // 8*kb .. 8*kb+7) is already in its own registers; P is stored in LDS as
+    // [row][key % 4][key / 4] so that the A operand (row lane%16, keys
+    // 4*(8*kb + e) + lane/16) is 8 consecutive floats.  O then lives in the
+    // MFMA output layout: oc[c][i] = O[4g + i][8n + c].
+    constexpr bool MFMA_PV = MFMA_S && VT == kF16 && Sh::V_REG && D == 128;
+    constexpr int NKQ = MFMA_S ? D / 32 : 1;
+    rkv_half8 qhi[NKQ], qlo[NKQ];
+    float mrow[4], lrow[4];
+    const float capl = cap * kLog2e;                  // cap in log2 units
+    const float inv_capl = cap > 0.f ? 1.f / capl : 0.f;
+    if constexpr (MFMA_S) {
+        const int qr = lane & 15;
+        const bool has = qr < nr;
+        const int rowi = has ? z * p.z_row_step + p.rowtab[g * p.rows_per_g + rg * RT + qr] : 0;
+        mfma_q<D>(q + (int64_t)rowi * D, has, sl2, lane, qhi, qlo);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            mrow[i] = -INFINITY;
+            lrow[i] = 0.f;
+        }
+    }
 
     // Software pipelining of the tile stream: when the raw rows of a tile fit
     // in registers, the loads of tile i+1's K (and block-type V) rows are
@@ -762,6 +882,64 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS stores are done
         __builtin_amdgcn_wave_barrier();
 
+        if constexpr (MFMA_S) {
+            // ---- scores on the matrix cores
+            float sv[4][4];
+            mfma_scores<D, Sh::RBK>(sK, qhi, qlo, lane, sv);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const bool valid = 16 * kb + (lane & 15) < nk;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = sv[kb][i];
+                    if (cap > 0.f) x = capl * tanhf(x * inv_capl);
+                    sv[kb][i] = valid ? x : -INFINITY;
+                }
+            }
+            // ---- online softmax: per-lane rows, then the wave-uniform rescale
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float mx = fmaxf(fmaxf(sv[0][i], sv[1][i]), fmaxf(sv[2][i], sv[3][i]));
+                mx = row16_max(mx);
+                const float mn = fmaxf(mrow[i], mx);
+                al[i] = __builtin_amdgcn_exp2f(mrow[i] - mn);
+                lrow[i] *= al[i];
+                mrow[i] = mn;
+            }
+            if constexpr (MFMA_PV) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) oc[c][i] *= al[i];
+            } else {
+#pragma unroll
+                for (int r = 0; r < RT; ++r) {
+                    const float mu = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mrow[r & 3]), 16 * (r >> 2)));
+                    if (mu > m[r]) {
+                        const float alpha = __builtin_amdgcn_exp2f(m[r] - mu);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+                        m[r] = mu;
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * (lane >> 4) + i;
+                float ps = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const float pv = __builtin_amdgcn_exp2f(sv[kb][i] - mrow[i]);
+                    ps += pv;
+                    const int key = 16 * kb + (lane & 15);
+                    const int at = MFMA_PV ? (key & 3) * 16 + (key >> 2) : key;
+                    if (row < RT) sP[w][row * kTile + at] = pv;
+                }
+                lrow[i] += ps;
+            }
+        } else {
         // ---- scores, one key per lane
         float s[RT];
         if constexpr (KDMA) key_dots<KT, D, RT, true>(sK, qp, s, lane, sw);
@@ -771,7 +949,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         for (int r = 0; r < RT; ++r) {
             float x;
             if (cap > 0.f)
-                x = cap * tanhf(s[r] * p.scale / cap) * kLog2e;
+                x = cap * tanhf(s[r] * scale_over_cap) * kLog2e;
             else
                 x = s[r] * sl2;
             s[r] = valid ? x : -INFINITY;
@@ -792,6 +970,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             l[r] += pr;
             sP[w][r * kTile + lane] = pr;
         }
+        }
         // the next tile's K (and block-type V) rows load during this tile's P.V
         if constexpr (KDMA) {
             if (tn < kend) dma_k(tn, nk_at(tn));
@@ -804,6 +983,43 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
 
+        if constexpr (MFMA_PV) {
+            // ---- P.V on the matrix cores (layout described where MFMA_PV is set)
+            const int qi = lane & 15, gq = lane >> 4;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                rkv_half8 ph, pl;
+                if (qi < RT) {
+                    const float4 a = *(const float4 *)&sP[w][qi * kTile + gq * 16 + 8 * kb];
+                    const float4 b = *(const float4 *)&sP[w][qi * kTile + gq * 16 + 8 * kb + 4];
+                    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const _Float16 h = (_Float16)x[e];
+                        ph[e] = h;
+                        pl[e] = (_Float16)(x[e] - (float)h);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        ph[e] = (_Float16)0.f;
+                        pl[e] = (_Float16)0.f;
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    uint32_t bw[4];
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        const uint32_t lo = vreg[8 * kb + 2 * e2][c >> 1], hi = vreg[8 * kb + 2 * e2 + 1][c >> 1];
+                        bw[e2] = __builtin_amdgcn_perm(hi, lo, (c & 1) ? 0x07060302u : 0x05040100u);
+                    }
+                    const rkv_half8 bv = __builtin_bit_cast(rkv_half8, bw);
+                    oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bv, oc[c], 0, 0, 0);
+                    oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bv, oc[c], 0, 0, 0);
+                }
+            }
+        } else {
         // ---- P.V (fully unrolled when V sits in registers: vreg is indexed by st).
         // Keys past nk have weight 0 and finite (repeated) data.
 #pragma unroll V_REG ? NSTEP : 4
@@ -833,6 +1049,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pw, x[e], acc[r][e]);
             }
         }
+        }
         if constexpr (PIPE && V_REG) {
             if (tn < kend) load_vreg(tn, nk_at(tn));
         }
@@ -855,10 +1072,40 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // ---- merge the waves of the workgroup in LDS.  Per wave and row: m, l,
     // and acc[D] summed over the wave's key-in-step lane groups.
 #pragma unroll
-    for (int r = 0; r < RT; ++r) l[r] = wave_sum(l[r]);
+    for (int r = 0; r < RT; ++r) {
+        if constexpr (MFMA_S) {
+            // per-lane partial sums of row r live in the 16 lanes of its group
+            const float t = row16_sum(lrow[r & 3]);
+            l[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), 16 * (r >> 2)));
+            if constexpr (MFMA_PV)
+                m[r] = __builtin_bit_cast(float,
+                                          __builtin_amdgcn_readlane(__builtin_bit_cast(int, mrow[r & 3]), 16 * (r >> 2)));
+        } else {
+            l[r] = wave_sum(l[r]);
+        }
+    }
     __syncthreads();  // every wave is done with its staging area
     float *mA = (float *)smem;                  // [NW][RT][D]
     float *mML = mA + NW * RT * D;              // [NW][RT][2]
+    if constexpr (MFMA_PV) {
+        // oc[c][i] = O[4g + i][8n + c]: every element once
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * (lane >> 4) + i;
+            if (row < RT) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) mA[(w * RT + row) * D + 8 * (lane & 15) + c] = oc[c][i];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (lane == 0) {
+                mML[(w * RT + r) * 2] = m[r];
+                mML[(w * RT + r) * 2 + 1] = l[r];
+            }
+        }
+        __syncthreads();
+    } else {
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
         if (ks == 0) {
@@ -880,6 +1127,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 for (int e = 0; e < 8; ++e) mA[(w * RT + r) * D + dg * 8 + e] += acc[r][e];
         }
         __syncthreads();
+    }
     }
     // Thread t finalises (head slot, row, dim) triples, merging the waves of
     // the head slot; a wave with no keys has m = -inf and weight 0.
