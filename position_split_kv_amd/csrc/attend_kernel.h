@@ -531,29 +531,33 @@ __device__ __forceinline__ float row16_sum(float x)
 // pre-multiplied by scale * log2(e) and split into binary16 high and low
 // parts (hi + lo keeps about 22 significant bits, so the products, exact in
 // the f32 accumulator, carry the f32 query).  Rows >= nr are zero.
+// Loads (mfma_q_load, issued early) and conversion (mfma_q_split).
+// (Unpredicated loads: a lane without a row reads a valid row and its values
+// are replaced by zero in mfma_q_split.)
 template <int D>
-__device__ __forceinline__ void mfma_q(const float *qrow, bool has, float sl2, int lane, rkv_half8 *qhi, rkv_half8 *qlo)
+__device__ __forceinline__ void mfma_q_load(const float *qrow, int lane, float (*x)[8])
 {
     const int kq = lane >> 4;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-        float x[8];
-        if (has) {
-            const float4 a = *(const float4 *)(qrow + 32 * kk + 8 * kq);
-            const float4 b = *(const float4 *)(qrow + 32 * kk + 8 * kq + 4);
-            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-        } else {
+        const float4 a = *(const float4 *)(qrow + 32 * kk + 8 * kq);
+        const float4 b = *(const float4 *)(qrow + 32 * kk + 8 * kq + 4);
+        x[kk][0] = a.x; x[kk][1] = a.y; x[kk][2] = a.z; x[kk][3] = a.w;
+        x[kk][4] = b.x; x[kk][5] = b.y; x[kk][6] = b.z; x[kk][7] = b.w;
+    }
+}
+template <int D>
+__device__ __forceinline__ void mfma_q_split(const float (*x)[8], bool has, float sl2, rkv_half8 *qhi, rkv_half8 *qlo)
+{
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = 0.f;
-        }
+    for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float y = x[e] * sl2;
+            const float y = has ? x[kk][e] * sl2 : 0.f;
             const _Float16 h = (_Float16)y;
             qhi[kk][e] = h;
             qlo[kk][e] = (_Float16)(y - (float)h);
         }
-    }
 }
 
 // Scores (log2 units) of the 64 keys of a DMA-staged f16 K tile against the
@@ -641,6 +645,16 @@ __device__ __forceinline__ float v_group_lds(const uint32_t *row, int dg, float 
     }
 }
 
+// Entry i of a 16-bit table in the kernel arguments, read as the aligned
+// 32-bit word that holds it: with a wave-uniform index that is a scalar load
+// (there are no 16-bit scalar loads), so its wait does not involve the vector
+// memory counter.
+__device__ __forceinline__ int u16_at(const uint16_t *tab, int i)
+{
+    const uint32_t v = ((const uint32_t *)tab)[i >> 1];
+    return (int)((i & 1) ? (v >> 16) : (v & 0xffffu));
+}
+
 // ---------------------------------------------------------------- the kernel
 
 template <int KT, int VT, int D, int RT>
@@ -663,6 +677,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
 
     __shared__ __attribute__((aligned(16))) uint32_t smem[SMEM_DW];
     __shared__ float sP[NW][RT * kTile];
+    __shared__ int sRow[NW][RT];  // output row of each wave's rows (-1: none), for the epilogue
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform in the wave
@@ -676,7 +691,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     const int hs = w >> p.wph_log2;
     const int ws = w - hs * wph;
     const int g = (hg << p.hpw_log2) + hs;
-    const int cnt = g < p.n_kv_heads ? (int)p.rowcnt[g] - rg * RT : 0;
+    const int cnt = g < p.n_kv_heads ? u16_at(p.rowcnt, g) - rg * RT : 0;
     const int nr = cnt <= 0 ? 0 : cnt < RT ? cnt : RT;  // 0: a wave with no rows (it still joins the barriers)
     const int z = blockIdx.z;
 
@@ -692,12 +707,26 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     const uint8_t *kg = sg.k + z * sg.k_seq + g * sg.k_head;
     const uint8_t *vg = sg.v + z * sg.v_seq + g * sg.v_head;
 
+    // Output rows of the wave's RT rows (-1 past nr).  The table is read at
+    // a clamped index whatever nr is, so these reads do not wait for the
+    // row count (one level of dependent loads fewer before the first tile).
+    int tabrow[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int ti = g * p.rows_per_g + rg * RT + r;
+        const int v = u16_at(p.rowtab, ti < kMaxRowTable ? ti : kMaxRowTable - 1);
+        tabrow[r] = r < nr ? z * p.z_row_step + v : -1;
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) sRow[w][r] = tabrow[r];
+    }
     int rid[RT];
     const float *qp[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
         const int rr = r < nr ? r : nr - 1;  // padding rows repeat the last row; never written
-        rid[r] = nr == 0 ? 0 : z * p.z_row_step + p.rowtab[g * p.rows_per_g + rg * RT + rr];
+        rid[r] = nr == 0 ? 0 : tabrow[rr];
         qp[r] = q + rid[r] * D;
     }
 
@@ -740,17 +769,6 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     float mrow[4], lrow[4];
     const float capl = cap * kLog2e;                  // cap in log2 units
     const float inv_capl = cap > 0.f ? 1.f / capl : 0.f;
-    if constexpr (MFMA_S) {
-        const int qr = lane & 15;
-        const bool has = qr < nr;
-        const int rowi = has ? z * p.z_row_step + p.rowtab[g * p.rows_per_g + rg * RT + qr] : 0;
-        mfma_q<D>(q + (int64_t)rowi * D, has, sl2, lane, qhi, qlo);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            mrow[i] = -INFINITY;
-            lrow[i] = 0.f;
-        }
-    }
 
     // Software pipelining of the tile stream: when the raw rows of a tile fit
     // in registers, the loads of tile i+1's K (and block-type V) rows are
@@ -770,7 +788,6 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     KRegs kr;
     VRegs vr;
     uint32_t vreg[V_REG ? NSTEP : 1][VRW];
-    uint32_t vnx[V_REG ? NSTEP : 1][VRW];
     int vps = (int)sg.v_pos;
     asm volatile("" : "+s"(vps));
     auto load_v_into = [&](uint32_t (&dst)[V_REG ? NSTEP : 1][VRW], int64_t t, int nkk) {
@@ -794,14 +811,6 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     auto nk_at = [&](int64_t t) { return (int)(kend - t < kTile ? kend - t : kTile); };
 
     constexpr bool KDMA = Sh::KDMA;
-    // Option (off by default): with K by DMA and V in registers, double buffer
-    // V so tile i+1's V rows load a whole tile ahead (two tiles of V live in
-    // registers, one wave per SIMD).
-#ifdef RKV_VDB
-    constexpr bool VDB = KDMA && V_REG;
-#else
-    constexpr bool VDB = false;  // measured slower: it halves the waves per SIMD
-#endif
     // Issue the direct global -> LDS loads of a tile's K rows (rows past nkk
     // repeat row nkk-1).  Lane l of load i fills slot i*64 + l of the tile.
     auto dma_k = [&](int64_t t, int nkk) {
@@ -828,21 +837,37 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     static_assert(2 * NV <= 63, "vmcnt range");
     const int sw = kswz<Sh::RBK>(lane);
 
+    // Query rows of the matrix-core path, loaded before the first tile's K / V
+    // loads are issued.  The row of lane l is row l % 16 of the wave's group:
+    // the row table is read with wave-uniform (scalar) loads and picked per
+    // lane, since a per-lane read of it would be a vector load whose wait
+    // would also wait for the tile loads.
+    float qraw[NKQ][8];
+    if constexpr (MFMA_S) {
+        const int qr = lane & 15;
+        int rowi = 0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) rowi = (qr == r && tabrow[r] >= 0) ? tabrow[r] : rowi;
+        mfma_q_load<D>(q + (int64_t)rowi * D, lane, qraw);
+    }
+
     int64_t t0 = kbeg + (int64_t)ws * kTile;
     // VMEM loads issued after the K rows' DMA that may stay outstanding when
-    // the scores start: 0, NV or 2*NV
+    // the scores start: 0 or NV.
+    //
+    // Order of a tile's loads with K by DMA and V in registers: both are
+    // issued together, right after the previous tile's P.V (and, for the
+    // first tile, before the query rows are loaded), so that a wave waits
+    // for one load latency per tile.  The DMA is invisible to the compiler's
+    // wait counting: a DMA issued before P.V would be waited for by the
+    // compiler's wait on the V registers, so none is in flight there.
     int v_after_dma = 0;
     if constexpr (KDMA) {
         if (t0 < kend) {
             dma_k(t0, nk_at(t0));
-            if constexpr (VDB) {
+            if constexpr (V_REG) {
                 load_vreg(t0, nk_at(t0));
                 v_after_dma = NV;
-                const int64_t t1 = t0 + tstep;
-                if (t1 < kend) {
-                    load_v_into(vnx, t1, nk_at(t1));
-                    v_after_dma = 2 * NV;
-                }
             }
         }
     } else if constexpr (PIPE) {
@@ -852,24 +877,29 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             else load_rows(vr, vg + t0 * sg.v_pos, (int)sg.v_pos, nk_at(t0), lane);
         }
     }
+    if constexpr (MFMA_S) {
+        // the pin keeps the conversion (and the waits for the query loads)
+        // after the first tile's loads have been issued
+        pin_v<8 * NKQ>(&qraw[0][0]);
+        mfma_q_split<D>(qraw, (lane & 15) < nr, sl2, qhi, qlo);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            mrow[i] = -INFINITY;
+            lrow[i] = 0.f;
+        }
+    }
     for (; t0 < kend; t0 += tstep) {
         const int nk = nk_at(t0);
         const int64_t tn = t0 + tstep;
         if constexpr (KDMA) {
-            // K rows arrive by DMA issued one tile ahead; V rows load now and
-            // are in flight during the scores (holding two tiles of V in
-            // registers would halve the occupancy).
-            if constexpr (V_REG && !VDB) {
-                load_vreg(t0, nk);
-                v_after_dma = NV;
-            }
+            // K rows arrive by DMA issued one tile ahead (V rows in registers
+            // were issued with them; block-type V rows are staged now).
             if constexpr (!V_REG) {
                 stage_rows<Sh::RBV, VWV, LSV>(vg + t0 * sg.v_pos, (int)sg.v_pos, nk, sV, lane);
                 v_after_dma = 0;
             }
-            // this tile's K rows (DMA) have landed; later V loads may still fly
-            if (v_after_dma == 2 * NV) waitcnt_vm<2 * NV>();
-            else if (v_after_dma == NV) waitcnt_vm<NV>();
+            // this tile's K rows (DMA) have landed; its V loads may still fly
+            if (v_after_dma == NV) waitcnt_vm<NV>();
             else waitcnt_vm<0>();
         } else if constexpr (PIPE) {
             store_rows<Sh::RBK, VWK, LSK>(kr, sK, lane);
@@ -972,8 +1002,11 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         }
         }
         // the next tile's K (and block-type V) rows load during this tile's P.V
+        // (with V in registers they load after it, see above)
         if constexpr (KDMA) {
-            if (tn < kend) dma_k(tn, nk_at(tn));
+            if constexpr (!V_REG) {
+                if (tn < kend) dma_k(tn, nk_at(tn));
+            }
         } else if constexpr (PIPE) {
             if (tn < kend) {
                 load_rows(kr, kg + tn * sg.k_pos, (int)sg.k_pos, nk_at(tn), lane);
@@ -1053,15 +1086,11 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         if constexpr (PIPE && V_REG) {
             if (tn < kend) load_vreg(tn, nk_at(tn));
         }
-        if constexpr (VDB) {
-#pragma unroll
-            for (int st = 0; st < NSTEP; ++st)
-#pragma unroll
-                for (int e = 0; e < VRW; ++e) vreg[st][e] = vnx[st][e];
-            const int64_t tnn = tn + tstep;
+        if constexpr (KDMA && V_REG) {
             v_after_dma = 0;
-            if (tnn < kend) {
-                load_v_into(vnx, tnn, nk_at(tnn));
+            if (tn < kend) {
+                dma_k(tn, nk_at(tn));
+                load_vreg(tn, nk_at(tn));
                 v_after_dma = NV;
             }
         }
@@ -1137,9 +1166,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     for (int i = threadIdx.x; i < hpw * RT * D; i += 64 * NW) {
         const int h = i / (RT * D);
         const int r = (i - h * RT * D) / D, d = i - (h * RT + r) * D;
-        const int gh = (hg << p.hpw_log2) + h;
-        if (gh >= p.n_kv_heads || r >= (int)p.rowcnt[gh] - rg * RT) continue;
         const int w0 = h * wph;
+        const int rr = sRow[w0][r];  // the head's waves share their rows
+        if (rr < 0) continue;
         float M = -INFINITY;
         for (int ww = w0; ww < w0 + wph; ++ww) M = fmaxf(M, mML[(ww * RT + r) * 2]);
         float L = 0.f, A = 0.f;
@@ -1149,7 +1178,6 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             L = fmaf(mML[(ww * RT + r) * 2 + 1], f, L);
             A = fmaf(mA[(ww * RT + r) * D + d], f, A);
         }
-        const int rr = z * p.z_row_step + p.rowtab[gh * p.rows_per_g + rg * RT + r];
         if (single) {
             o_out[(int64_t)rr * D + d] = A / L;
             if (d == 0) lse_out[rr] = (M + log2f(L)) * 0.69314718055994531f;

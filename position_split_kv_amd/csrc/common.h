@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "rkv.h"
@@ -58,6 +59,10 @@ struct SplitParams {
     uint16_t rowcnt[kMaxKvHeads];
     uint16_t rowtab[kMaxRowTable];
 };
+
+// The kernel reads the two 16-bit tables as aligned 32-bit words.
+static_assert(offsetof(SplitParams, rowcnt) % 4 == 0 && offsetof(SplitParams, rowtab) % 4 == 0, "table alignment");
+static_assert(kMaxKvHeads % 2 == 0 && kMaxRowTable % 2 == 0, "table sizes");
 
 // How a launch is cut into work: shared by the workspace query and the launch.
 struct SplitPlan {
