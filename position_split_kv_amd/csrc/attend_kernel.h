@@ -1113,6 +1113,49 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             l[r] = wave_sum(l[r]);
         }
     }
+    if constexpr (MFMA_PV) {
+        if (wph == 1) {
+            // One wave per KV head: nothing to merge inside the workgroup, so
+            // the wave writes its rows straight from the MFMA output layout
+            // (lane (g, n) holds dims 8n .. 8n+7 of rows 4g .. 4g+3).  The
+            // values are those the LDS merge would produce for one wave.
+            const bool single = p.n_splits == 1;
+            const int64_t pbase = (int64_t)blockIdx.x * p.n_rows_total;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * (lane >> 4) + i;
+                int rr = -1;
+                float lr = 1.f;
+#pragma unroll
+                for (int r = 0; r < RT; ++r) {
+                    rr = row == r ? tabrow[r] : rr;
+                    lr = row == r ? l[r] : lr;
+                }
+                if (rr < 0) continue;
+                float v[8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) v[c] = single ? oc[c][i] / lr : oc[c][i];
+                float *dst = single ? o_out + (int64_t)rr * D : part_acc + (pbase + rr) * D;
+                *(float4 *)(dst + 8 * (lane & 15)) = make_float4(v[0], v[1], v[2], v[3]);
+                *(float4 *)(dst + 8 * (lane & 15) + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            }
+            if (lane < RT) {
+                int rr = -1;
+                float mr = 0.f, lr = 1.f;
+#pragma unroll
+                for (int r = 0; r < RT; ++r) {
+                    rr = lane == r ? tabrow[r] : rr;
+                    mr = lane == r ? m[r] : mr;
+                    lr = lane == r ? l[r] : lr;
+                }
+                if (rr >= 0) {
+                    if (single) lse_out[rr] = (mr + log2f(lr)) * 0.69314718055994531f;
+                    else part_ml[pbase + rr] = make_float2(mr, lr);
+                }
+            }
+            return;
+        }
+    }
     __syncthreads();  // every wave is done with its staging area
     float *mA = (float *)smem;                  // [NW][RT][D]
     float *mML = mA + NW * RT * D;              // [NW][RT][2]
