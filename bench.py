@@ -62,6 +62,9 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="run one plain 1 GiB copy first (counter calibration)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the three-call comparison and the read-ceiling probe (profiling runs)")
+    ap.add_argument("--no-streamed", action="store_true", help="skip the streamed-tail measurement")
+    ap.add_argument("--streamed-sweep", action="store_true",
+                    help="also run the free-zone sweep of the streamed tail (tail 1024..6144 keys per layer)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); sharding across GPUs is described, "
@@ -145,6 +148,12 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(layers, desc, args.cpu_seconds)
 
+    streamed = None
+    if not args.no_streamed:
+        del layers, segs, outs, ws
+        torch.cuda.empty_cache()
+        streamed = streamed_tail(P, synth, args.streamed_sweep)
+
     traffic = MEASURED_TRAFFIC_BYTES
     out = {
         "metric": "decode attention effective KV GB/s & us/layer vs HBM peak; tail-hidden fraction",
@@ -182,7 +191,10 @@ def main():
             "median_launch_us": round(statistics.median(times) * 1e6, 3),
         },
         "cpu_baseline": cpu,
+        "streamed_tail": streamed,
     }
+    if streamed is not None:
+        out["config"]["tail_hidden_fraction"] = streamed["tail_hidden_fraction"]
     print(json.dumps(out), flush=True)
 
 
@@ -220,6 +232,155 @@ def extras(P, desc, layers, segs, outs, stream, S, Hq, D, L):
     del big
 
     return three_us, read_ceiling
+
+
+def streamed_tail(P, synth, sweep=False, L=48, steps=3):
+    """The streamed-tail workload: 40 q heads / 8 KV heads, head_dim 128, q8_0 K and
+    q4_0 V, 131072 keys per layer: window [0, 65536) in HBM, tail [65536, 131072) in
+    pinned host memory, streamed in 8192-key tiles through a 3-slot device ring on
+    a copy stream; between layers a dense-FFN stand-in (a 14336 x 4096 f16 GEMV,
+    48 distinct matrices, repeated r times to about 0.2 ms).
+
+    T_c: the step with the tails already in HBM (same kernels: window, one
+    segment call per tile, combine; no copies).  T_d: the tile copies alone on
+    the copy stream.  T_p: the pipelined step through the ring.  Tail-hidden
+    fraction h = (T_c + T_d - T_p) / T_d (clipped to [0, 1]); link fraction =
+    (tail bytes / T_p) / R_link, with R_link the measured pinned H2D rate."""
+    import torch
+
+    dev = "cuda"
+    Hq, Hkv, D, n, wc, tile, B = 40, 8, 128, 131072, 65536, 8192, 3
+    desc = P.Desc(1, Hq, Hkv, D, 1.0 / math.sqrt(D))
+    log(f"streamed: building {L} layers (q8_0 K / q4_0 V, {n} keys; tail {n - wc} keys in pinned host memory)")
+    lay = []
+    for li in range(L):
+        kc = synth.make_cache(n, Hkv, D, synth.Q8_0, synth.stream_seed(4, 1, li), dev)
+        vc = synth.make_cache(n, Hkv, D, synth.Q4_0, synth.stream_seed(4, 2, li), dev)
+        q = synth.make_query(1, Hq, D, synth.stream_seed(4, 3, li), dev)
+        kh = torch.empty(kc.data[wc:].shape, dtype=kc.data.dtype, pin_memory=True)
+        vh = torch.empty(vc.data[wc:].shape, dtype=vc.data.dtype, pin_memory=True)
+        kh.copy_(kc.data[wc:])
+        vh.copy_(vc.data[wc:])
+        lay.append(dict(kc=kc, vc=vc, q=q, kh=synth.Cache(kh, kc.dtype, n - wc, Hkv, D),
+                        vh=synth.Cache(vh, vc.dtype, n - wc, Hkv, D)))
+    W = [torch.randn(14336, 4096, device=dev, dtype=torch.float16, generator=torch.Generator(dev).manual_seed(900 + i))
+         for i in range(L)]
+    x = torch.randn(4096, device=dev, dtype=torch.float16)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    # FFN stand-in calibration
+    for _ in range(3):
+        torch.mv(W[0], x)
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for i in range(20):
+        torch.mv(W[i % L], x)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_gemv = e0.elapsed_time(e1) * 1e-3 / 20
+    reps = max(1, round(200e-6 / t_gemv))
+
+    def ffn(li):
+        for _ in range(reps):
+            torch.mv(W[li], x)
+
+    # pinned H2D rate (256 MiB, non-blocking stream)
+    cs = torch.cuda.Stream()
+    hbuf = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    dbuf = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(cs):
+        dbuf.copy_(hbuf, non_blocking=True)
+        a, b = ev(), ev()
+        a.record(cs)
+        for _ in range(4):
+            dbuf.copy_(hbuf, non_blocking=True)
+        b.record(cs)
+    torch.cuda.synchronize()
+    r_link = 4 * hbuf.numel() / (a.elapsed_time(b) * 1e-3) / 1e9
+    del hbuf, dbuf
+
+    outs = [(torch.empty(1, Hq, D, device=dev), torch.empty(1, Hq, device=dev)) for _ in range(L)]
+    o_w, l_w = torch.empty(1, Hq, D, device=dev), torch.empty(1, Hq, device=dev)
+    ws_w = P.workspace(P.rkv_attend_workspace_bytes(desc, P.view_of_cache(lay[0]["kc"], lay[0]["vc"], 0, wc)))
+
+    def run(tail_keys, tile_keys, mode):
+        """One step; mode 'resident' (T_c), 'copy' (T_d) or 'stream' (T_p).  Returns seconds."""
+        n_t = (tail_keys + tile_keys - 1) // tile_keys
+        kc0, vc0 = lay[0]["kc"], lay[0]["vc"]
+        if mode == "stream":
+            ring = P.Ring(B, tile_keys * kc0.pos_stride, tile_keys * vc0.pos_stride)
+            tails = [P.view_of_cache(l_["kh"], l_["vh"], 0, tail_keys) for l_ in lay]
+        elif mode == "copy":
+            slots = [(torch.empty(tile_keys * kc0.pos_stride, dtype=torch.uint8, device=dev),
+                      torch.empty(tile_keys * vc0.pos_stride, dtype=torch.uint8, device=dev)) for _ in range(B)]
+        parts_o = [torch.empty(1, Hq, D, device=dev) for _ in range(n_t + 1)]
+        parts_l = [torch.empty(1, Hq, device=dev) for _ in range(n_t + 1)]
+        ws_t = P.workspace(P.rkv_attend_workspace_bytes(desc, P.view_of_cache(kc0, vc0, wc, wc + min(tile_keys, tail_keys))))
+        times = []
+        try:
+            for it in range(steps + 1):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                if mode == "copy":
+                    with torch.cuda.stream(cs):
+                        j = 0
+                        for l_ in lay:
+                            kb, vb = l_["kh"].data.view(-1), l_["vh"].data.view(-1)
+                            for t in range(n_t):
+                                a0, a1 = t * tile_keys, min(tail_keys, (t + 1) * tile_keys)
+                                sk, sv = slots[j % B]
+                                sk[: (a1 - a0) * kc0.pos_stride].copy_(kb[a0 * kc0.pos_stride: a1 * kc0.pos_stride], non_blocking=True)
+                                sv[: (a1 - a0) * vc0.pos_stride].copy_(vb[a0 * vc0.pos_stride: a1 * vc0.pos_stride], non_blocking=True)
+                                j += 1
+                    cs.synchronize()
+                else:
+                    if mode == "stream":
+                        ring.rkv_ring_begin_step(tails, tile_keys)
+                        ws_s = P.workspace(ring.rkv_stream_tail_workspace_bytes(0, desc))
+                    for li, l_ in enumerate(lay):
+                        P.rkv_attend_segment(desc, l_["q"], P.view_of_cache(l_["kc"], l_["vc"], 0, wc), o_w, l_w, ws_w, stream)
+                        if mode == "stream":
+                            ring.rkv_stream_tail(li, desc, l_["q"], o_w, l_w, outs[li][0], outs[li][1], ws_s, stream)
+                        else:
+                            for t in range(n_t):
+                                a0, a1 = wc + t * tile_keys, wc + min(tail_keys, (t + 1) * tile_keys)
+                                P.rkv_attend_segment(desc, l_["q"], P.view_of_cache(l_["kc"], l_["vc"], a0, a1),
+                                                     parts_o[t + 1], parts_l[t + 1], ws_t, stream)
+                            P.rkv_lse_combine([o_w] + parts_o[1:], [l_w] + parts_l[1:], outs[li][0], outs[li][1], D, stream)
+                        ffn(li)
+                    if mode == "stream":
+                        ring.rkv_ring_end_step()
+                    torch.cuda.synchronize()
+                if it > 0:
+                    times.append(time.perf_counter() - t0)
+        finally:
+            if mode == "stream":
+                ring.close()
+        return statistics.median(times)
+
+    def measure(tail_keys, tile_keys):
+        t_c = run(tail_keys, tile_keys, "resident")
+        t_d = run(tail_keys, tile_keys, "copy")
+        t_p = run(tail_keys, tile_keys, "stream")
+        tail_bytes = L * tail_keys * (lay[0]["kc"].pos_stride + lay[0]["vc"].pos_stride)
+        h = min(1.0, max(0.0, (t_c + t_d - t_p) / t_d))
+        return {"tail_keys": tail_keys, "tile_keys": tile_keys, "T_c_ms": round(t_c * 1e3, 3),
+                "T_d_ms": round(t_d * 1e3, 3), "T_p_ms": round(t_p * 1e3, 3), "tail_hidden_fraction": round(h, 4),
+                "tail_GBs": round(tail_bytes / t_p / 1e9, 2), "link_fraction": round(tail_bytes / t_p / 1e9 / r_link, 4),
+                "free_zone_keys_per_layer": round(t_c * r_link * 1e9 / L / (lay[0]["kc"].pos_stride + lay[0]["vc"].pos_stride))}
+
+    log(f"streamed: FFN stand-in {reps} x GEMV ({t_gemv * 1e6:.1f} us each); pinned H2D {r_link:.1f} GB/s")
+    main = measure(n - wc, tile)
+    res = dict(main)
+    res.update({"workload": "q8_0 K / q4_0 V, 40/8 heads, D 128, 131072 keys = window 65536 (HBM) + tail 65536 "
+                            "(pinned host, 8192-key tiles, 3-slot ring), 48 layers, 0.2 ms FFN GEMV stand-in",
+                "R_link_GBs": round(r_link, 2), "ffn_gemv_reps": reps, "ffn_ms": round(reps * t_gemv * 1e3, 4)})
+    if sweep:
+        res["free_zone_sweep"] = [measure(t, min(tile, t)) for t in (1024, 2048, 4096, 6144)] + \
+                                 [measure(t, 1024) for t in (2048, 4096, 6144)]
+    return res
 
 
 def cpu_baseline(layers, desc, seconds):
