@@ -63,6 +63,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the three-call comparison and the read-ceiling probe (profiling runs)")
     ap.add_argument("--no-streamed", action="store_true", help="skip the streamed-tail measurement")
+    ap.add_argument("--no-others", action="store_true", help="skip the tiny, softcap-q8_0 and shared-prefix timings")
     ap.add_argument("--streamed-sweep", action="store_true",
                     help="also run the free-zone sweep of the streamed tail (tail 1024..6144 keys per layer)")
     args = ap.parse_args()
@@ -148,6 +149,10 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(layers, desc, args.cpu_seconds)
 
+    others = None
+    if not args.no_others:
+        others = other_workloads(P, synth)
+
     streamed = None
     if not args.no_streamed:
         del layers, segs, outs, ws
@@ -192,6 +197,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "streamed_tail": streamed,
+        "other_workloads": others,
     }
     if streamed is not None:
         out["config"]["tail_hidden_fraction"] = streamed["tail_hidden_fraction"]
@@ -232,6 +238,103 @@ def extras(P, desc, layers, segs, outs, stream, S, Hq, D, L):
     del big
 
     return three_us, read_ceiling
+
+
+def other_workloads(P, synth, reps=20):
+    """HIP-event timings (mean over reps calls after warm-up) of the other decode
+    workloads, each in the form a caller would run it:
+      tiny: f32, 8/2 heads, D 128, window 3072 + tail 1024 (cache-resident);
+      softcap_q8: q8_0 K and V, 16/2 heads, D 512, 262144 keys = 196608 + 65536,
+        softcap 30, one rkv_attend_split launch, two cache instances alternated
+        (1.14 GB, past the 256 MB last-level cache);
+      shared_prefix: 15 sequences x 32/8 heads, D 128, a 32768-key q8_0 / q4_0
+        prefix stored once + a private 2048-key f16 suffix per sequence:
+        segment call (prefix), segment call (suffixes), combine; two instances
+        alternated.  Bytes: the prefix is counted once."""
+    import torch
+
+    dev = "cuda"
+
+    def timed(f):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    res = {}
+    kc = synth.make_cache(4096, 2, 128, synth.F32, synth.stream_seed(1, 1), dev)
+    vc = synth.make_cache(4096, 2, 128, synth.F32, synth.stream_seed(1, 2), dev)
+    q = synth.make_query(1, 8, 128, synth.stream_seed(1, 3), dev)
+    d = P.Desc(1, 8, 2, 128, 1 / math.sqrt(128))
+    segs = [P.view_of_cache(kc, vc, 0, 3072), P.view_of_cache(kc, vc, 3072, 4096)]
+    ws = P.workspace(P.rkv_attend_split_workspace_bytes(d, segs))
+    o, l = torch.empty(1, 8, 128, device=dev), torch.empty(1, 8, device=dev)
+    t = timed(lambda: P.rkv_attend_split(d, q, segs, o, l, ws))
+    res["tiny_f32"] = {"us": round(t * 1e6, 2), "GBs": round(2 * 4096 * 2 * 512 / t / 1e9, 1),
+                       "note": "8.4 MB, cache-resident: launch-latency bound"}
+
+    inst = []
+    for i in range(2):
+        inst.append((synth.make_cache(262144, 2, 512, synth.Q8_0, synth.stream_seed(3, 1, i), dev),
+                     synth.make_cache(262144, 2, 512, synth.Q8_0, synth.stream_seed(3, 2, i), dev)))
+    q = synth.make_query(1, 16, 512, synth.stream_seed(3, 3), dev)
+    d = P.Desc(1, 16, 2, 512, 1 / math.sqrt(512), 30.0)
+    segs = [[P.view_of_cache(kc, vc, 0, 196608), P.view_of_cache(kc, vc, 196608, 262144)] for kc, vc in inst]
+    ws = P.workspace(P.rkv_attend_split_workspace_bytes(d, segs[0]))
+    o, l = torch.empty(1, 16, 512, device=dev), torch.empty(1, 16, device=dev)
+    k = [0]
+
+    def c3():
+        P.rkv_attend_split(d, q, segs[k[0] % 2], o, l, ws)
+        k[0] += 1
+    t = timed(c3)
+    b = 2 * 262144 * 2 * 544
+    res["softcap_q8_d512"] = {"us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1),
+                              "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4), "bytes": b}
+    del inst, segs
+    torch.cuda.empty_cache()
+
+    S, Hq, Hkv, D, npre, nsuf = 15, 32, 8, 128, 32768, 2048
+    inst = []
+    for i in range(2):
+        pk = synth.make_cache(npre, Hkv, D, synth.Q8_0, synth.stream_seed(5, 1, i), dev)
+        pv = synth.make_cache(npre, Hkv, D, synth.Q4_0, synth.stream_seed(5, 2, i), dev)
+        sk = synth.make_cache(S * nsuf, Hkv, D, synth.F16, synth.stream_seed(5, 4, i), dev)
+        sv = synth.make_cache(S * nsuf, Hkv, D, synth.F16, synth.stream_seed(5, 5, i), dev)
+        inst.append((P.view_of_cache(pk, pv),
+                     P.view_of_cache(sk, sv, 0, nsuf, nsuf * sk.pos_stride, nsuf * sv.pos_stride), pk, pv, sk, sv))
+    q = synth.make_query(S, Hq, D, synth.stream_seed(5, 3), dev)
+    d = P.Desc(S, Hq, Hkv, D, 1 / math.sqrt(D))
+    wsp = P.workspace(P.rkv_attend_workspace_bytes(d, inst[0][0]))
+    wss = P.workspace(P.rkv_attend_workspace_bytes(d, inst[0][1]))
+    op, lp = torch.empty(S, Hq, D, device=dev), torch.empty(S, Hq, device=dev)
+    os_, ls = torch.empty_like(op), torch.empty_like(lp)
+    oo, lo = torch.empty_like(op), torch.empty_like(lp)
+    k = [0]
+
+    def c5():
+        pv_, sv_ = inst[k[0] % 2][:2]
+        k[0] += 1
+        P.rkv_attend_segment(d, q, pv_, op, lp, wsp)
+        P.rkv_attend_segment(d, q, sv_, os_, ls, wss)
+        P.rkv_lse_combine([op, os_], [lp, ls], oo, lo, D)
+
+    def c5p():
+        P.rkv_attend_segment(d, q, inst[k[0] % 2][0], op, lp, wsp)
+        k[0] += 1
+    t = timed(c5)
+    tp = timed(c5p)
+    b = npre * Hkv * (136 + 72) + S * nsuf * Hkv * 2 * 256
+    res["shared_prefix"] = {"us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1),
+                            "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4), "bytes": b,
+                            "prefix_only_us": round(tp * 1e6, 2)}
+    return res
 
 
 def streamed_tail(P, synth, sweep=False, L=48, steps=3):
