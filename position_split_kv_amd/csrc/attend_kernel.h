@@ -282,6 +282,49 @@ __device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds)
 #endif
 }
 
+// The same for 4 bytes per lane (the dword lands at lds + 4 * lane).
+__device__ __forceinline__ void lds_dma4(const void *g, uint32_t lds)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(g), "s"(lds)
+                 : "memory");
+#else
+    (void)g;
+    (void)lds;
+#endif
+}
+
+// Direct global -> LDS copy of a tile's kTile rows of RBD dwords (rows past
+// nkk repeat row nkk-1) to rows of LS >= RBD dwords: slot s = i*64 + lane of
+// load i is dword s % LS of row s / LS (padding slots repeat the row's last
+// dword), so the tile takes exactly LS loads.
+// (The lane index passes through an empty asm so that the per-slot row and
+// column are recomputed here, by an add-and-carry recurrence, instead of being
+// hoisted out of the tile loop into registers.)
+template <int RBD, int LS>
+__device__ __forceinline__ void dma_rows4(const uint8_t *src, int pos_stride, int nkk, uint32_t lds_base, int lane)
+{
+    static_assert(LS <= 64, "one row per load at least");
+    asm volatile("" : "+v"(lane));
+    int j = lane / LS, c = lane - (lane / LS) * LS;  // slot lane of load 0
+    constexpr int DJ = 64 / LS, DC = 64 % LS;         // slot advance of 64 per load
+#pragma unroll
+    for (int i = 0; i < LS; ++i) {
+        const int cc = c < RBD ? c : RBD - 1;
+        const int jc = j < nkk ? j : nkk - 1;
+        lds_dma4(src + (uint32_t)(jc * pos_stride + 4 * cc), lds_base + 256u * i);
+        j += DJ;
+        c += DC;
+        if (c >= LS) {
+            c -= LS;
+            ++j;
+        }
+    }
+}
+
 // s_waitcnt vmcnt(n) (0 <= n <= 63), other counters untouched.
 template <int N>
 __device__ __forceinline__ void waitcnt_vm()
@@ -588,6 +631,82 @@ __device__ __forceinline__ void mfma_scores(const uint32_t *tile, const rkv_half
         for (int i = 0; i < 4; ++i) sv[kb][i] = acc[kb][i];
 }
 
+// Block-type K on the matrix cores.  The codes of one 32-value block are
+// exact in binary16 (q8_0: -127..127, q4_0: -8..7), and one block is one
+// k-step of v_mfma_f32_16x16x32_f16, so each step's product is multiplied by
+// the key's block scale afterwards: s = sum_kk d[key][kk] * (q_kk . code_kk).
+// Codes become f16 by placing each (biased) byte under the exponent byte 0x64
+// (value 1024 + byte) and subtracting the bias with one packed f16 add.
+typedef _Float16 rkv_half2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t f16pair_of_bytes(uint32_t x, uint32_t sel, _Float16 bias)
+{
+    const uint32_t w = __builtin_amdgcn_perm(0x64646464u, x, sel);
+    const rkv_half2 h = __builtin_bit_cast(rkv_half2, w) - rkv_half2{bias, bias};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// 8 codes of a q8_0 / q4_0 row in LDS (row = dword pointer) for dims
+// 32*kk + 8*g .. +7, as the f16 B operand; and the block scale of block kk.
+template <int KT>
+__device__ __forceinline__ rkv_half8 block_codes_f16(const uint32_t *row, int kk, int g, float &dsc)
+{
+    const int os = (KT == kQ8 ? 34 : 18) * kk;
+    const uint32_t s0 = row[os >> 2];
+    dsc = h2f((os & 2) ? (s0 >> 16) : s0);
+    const int o = KT == kQ8 ? os + 2 + 8 * g : os + 2 + 8 * (g & 1);
+    const uint32_t sh = o & 3;
+    const uint32_t A = row[o >> 2], B = row[(o >> 2) + 1], C = row[(o >> 2) + 2];
+    uint32_t w0 = funnel(A, B, sh), w1 = funnel(B, C, sh);
+    uint32_t out[4];
+    if constexpr (KT == kQ8) {
+        w0 ^= 0x80808080u;
+        w1 ^= 0x80808080u;
+        out[0] = f16pair_of_bytes(w0, 0x04010400u, (_Float16)1152.f);
+        out[1] = f16pair_of_bytes(w0, 0x04030402u, (_Float16)1152.f);
+        out[2] = f16pair_of_bytes(w1, 0x04010400u, (_Float16)1152.f);
+        out[3] = f16pair_of_bytes(w1, 0x04030402u, (_Float16)1152.f);
+    } else {
+        const int shn = (g >> 1) * 4;  // dims 0..15 of the block: low nibbles; 16..31: high
+        w0 = (w0 >> shn) & 0x0f0f0f0fu;
+        w1 = (w1 >> shn) & 0x0f0f0f0fu;
+        out[0] = f16pair_of_bytes(w0, 0x04010400u, (_Float16)1032.f);
+        out[1] = f16pair_of_bytes(w0, 0x04030402u, (_Float16)1032.f);
+        out[2] = f16pair_of_bytes(w1, 0x04010400u, (_Float16)1032.f);
+        out[3] = f16pair_of_bytes(w1, 0x04030402u, (_Float16)1032.f);
+    }
+    return __builtin_bit_cast(rkv_half8, out);
+}
+
+// Scores (log2 units) of the 64 keys of a staged q8_0 / q4_0 K tile (row
+// stride LS dwords) against the wave's query rows, in the layout of
+// mfma_scores.
+template <int KT, int D, int LS>
+__device__ __forceinline__ void mfma_scores_blk(const uint32_t *tile, const rkv_half8 *qhi, const rkv_half8 *qlo,
+                                                int lane, float (*sv)[4])
+{
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[kb][i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            float dsc;
+            const rkv_half8 b = block_codes_f16<KT>(tile + (16 * kb + (lane & 15)) * LS, kk, lane >> 4, dsc);
+            rkv_float4v acc = rkv_float4v{0.f, 0.f, 0.f, 0.f};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi[kk], b, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo[kk], b, acc, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[kb][i] = fmaf(dsc, acc[i], sv[kb][i]);
+        }
+        // one block of 32 dims at a time: keeps the code reads of later blocks
+        // from being hoisted (and held in registers) ahead of this one
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // ---------------------------------------------------------------- values
 
 // 8 consecutive values (dims 8*dg .. 8*dg+7) of a V row held in LDS, as
@@ -753,7 +872,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // rows per wave as the 16-row A operand.  Running max and denominator are
     // then kept per lane for the rows 4*(lane/16) .. +3 (mrow / lrow) and the
     // wave-uniform m[] follows them.
-    constexpr bool MFMA_S = KT == kF16 && Sh::KDMA && D <= 128 && RT <= 16;
+    constexpr bool MFMA_S = ((KT == kF16 && Sh::KDMA) || KT == kQ8 || KT == kQ4) && D <= 128 && RT <= 16;
     // P.V on the matrix cores as well, for f16 V rows of 128 values held in
     // registers: lane (g = lane/16, n = lane%16) holds, for step st, the 8
     // values of key 4*st + g at dims 8n .. 8n+7.  Taking as contraction index
@@ -783,7 +902,13 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
 #ifdef RKV_NO_PIPE
     constexpr bool PIPE = false;
 #else
-    constexpr bool PIPE = !Sh::KDMA && RAW_DW <= 64;
+    constexpr bool PIPE = !Sh::KDMA && RAW_DW <= 64 && !MFMA_S;  // MFMA operands need those registers
+    // Block-type K and V with the matrix-core scores: both tiles go global ->
+    // LDS by dword DMA (no staging registers), issued together after the
+    // previous tile's P.V; the wait for K leaves V's loads in flight.
+    constexpr bool BDMA = MFMA_S && (KT == kQ8 || KT == kQ4) && (VT == kQ8 || VT == kQ4) && Sh::RBK % 4 == 0 &&
+                          Sh::RBV % 4 == 0 && LSK <= 64 && LSV <= 64;
+    constexpr int NVD = LSV < 63 ? LSV : 63;  // V loads a wait for K may leave outstanding
 #endif
     KRegs kr;
     VRegs vr;
@@ -832,6 +957,16 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             }
         }
     };
+    auto dma_kv = [&](int64_t t, int nkk) {
+        if constexpr (BDMA) {
+            int kps = (int)sg.k_pos, vps2 = (int)sg.v_pos;
+            asm volatile("" : "+s"(kps), "+s"(vps2));
+            const uint32_t base = lds_addr(smem + w * Sh::STAGE_DW);
+            waitcnt_lgkm0();  // this wave's earlier LDS reads of both buffers are done
+            dma_rows4<Sh::RBK / 4, LSK>(kg + t * sg.k_pos, kps, nkk, base, lane);
+            dma_rows4<Sh::RBV / 4, LSV>(vg + t * sg.v_pos, vps2, nkk, base + 4u * kTile * LSK, lane);
+        }
+    };
     // VMEM instructions one load_v_into issues (outstanding loads a wait may leave)
     constexpr int NV = V_REG ? NSTEP * (VRW / 4) : 0;
     static_assert(2 * NV <= 63, "vmcnt range");
@@ -862,7 +997,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // wait counting: a DMA issued before P.V would be waited for by the
     // compiler's wait on the V registers, so none is in flight there.
     int v_after_dma = 0;
-    if constexpr (KDMA) {
+    if constexpr (BDMA) {
+        if (t0 < kend) dma_kv(t0, nk_at(t0));
+    } else if constexpr (KDMA) {
         if (t0 < kend) {
             dma_k(t0, nk_at(t0));
             if constexpr (V_REG) {
@@ -891,7 +1028,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     for (; t0 < kend; t0 += tstep) {
         const int nk = nk_at(t0);
         const int64_t tn = t0 + tstep;
-        if constexpr (KDMA) {
+        if constexpr (BDMA) {
+            waitcnt_vm<NVD>();  // this tile's K rows have landed; V may still fly
+        } else if constexpr (KDMA) {
             // K rows arrive by DMA issued one tile ahead (V rows in registers
             // were issued with them; block-type V rows are staged now).
             if constexpr (!V_REG) {
@@ -915,7 +1054,8 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         if constexpr (MFMA_S) {
             // ---- scores on the matrix cores
             float sv[4][4];
-            mfma_scores<D, Sh::RBK>(sK, qhi, qlo, lane, sv);
+            if constexpr (KT == kQ8 || KT == kQ4) mfma_scores_blk<KT, D, LSK>(sK, qhi, qlo, lane, sv);
+            else mfma_scores<D, Sh::RBK>(sK, qhi, qlo, lane, sv);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const bool valid = 16 * kb + (lane & 15) < nk;
@@ -1016,6 +1156,10 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
 
+        if constexpr (BDMA) {
+            waitcnt_vm<0>();  // this tile's V rows have landed
+            __builtin_amdgcn_wave_barrier();
+        }
         if constexpr (MFMA_PV) {
             // ---- P.V on the matrix cores (layout described where MFMA_PV is set)
             const int qi = lane & 15, gq = lane >> 4;
@@ -1055,7 +1199,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         } else {
         // ---- P.V (fully unrolled when V sits in registers: vreg is indexed by st).
         // Keys past nk have weight 0 and finite (repeated) data.
-#pragma unroll V_REG ? NSTEP : 4
+#pragma unroll V_REG ? NSTEP : MFMA_S ? 2 : 4
         for (int st = 0; st < NSTEP; ++st) {
             const int key = st * KPS + ks;
             float x[8];
@@ -1085,6 +1229,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         }
         if constexpr (PIPE && V_REG) {
             if (tn < kend) load_vreg(tn, nk_at(tn));
+        }
+        if constexpr (BDMA) {
+            if (tn < kend) dma_kv(tn, nk_at(tn));
         }
         if constexpr (KDMA && V_REG) {
             v_after_dma = 0;
