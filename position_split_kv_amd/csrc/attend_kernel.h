@@ -678,6 +678,37 @@ __device__ __forceinline__ rkv_half8 block_codes_f16(const uint32_t *row, int kk
     return __builtin_bit_cast(rkv_half8, out);
 }
 
+// The 8 codes of dims 8*dg .. 8*dg+7 of a q8_0 / q4_0 row in LDS as four
+// packed binary16 pairs (exact), and the block's binary16 scale bits.
+template <int VT>
+__device__ __forceinline__ void v_group_codes_f16(const uint32_t *row, int dg, uint32_t *c2, uint32_t &dbits)
+{
+    const int bb = dg >> 2, h = dg & 3;
+    const int os = (VT == kQ8 ? 34 : 18) * bb;
+    const uint32_t s0 = row[os >> 2];
+    dbits = (os & 2) ? (s0 >> 16) : (s0 & 0xffffu);
+    const int o = VT == kQ8 ? os + 2 + 8 * h : os + 2 + 8 * (h & 1);
+    const uint32_t sh = o & 3;
+    const uint32_t A = row[o >> 2], B = row[(o >> 2) + 1], C = row[(o >> 2) + 2];
+    uint32_t w0 = funnel(A, B, sh), w1 = funnel(B, C, sh);
+    if constexpr (VT == kQ8) {
+        w0 ^= 0x80808080u;
+        w1 ^= 0x80808080u;
+        c2[0] = f16pair_of_bytes(w0, 0x04010400u, (_Float16)1152.f);
+        c2[1] = f16pair_of_bytes(w0, 0x04030402u, (_Float16)1152.f);
+        c2[2] = f16pair_of_bytes(w1, 0x04010400u, (_Float16)1152.f);
+        c2[3] = f16pair_of_bytes(w1, 0x04030402u, (_Float16)1152.f);
+    } else {
+        const int shn = (h >> 1) * 4;
+        w0 = (w0 >> shn) & 0x0f0f0f0fu;
+        w1 = (w1 >> shn) & 0x0f0f0f0fu;
+        c2[0] = f16pair_of_bytes(w0, 0x04010400u, (_Float16)1032.f);
+        c2[1] = f16pair_of_bytes(w0, 0x04030402u, (_Float16)1032.f);
+        c2[2] = f16pair_of_bytes(w1, 0x04010400u, (_Float16)1032.f);
+        c2[3] = f16pair_of_bytes(w1, 0x04030402u, (_Float16)1032.f);
+    }
+}
+
 // Scores (log2 units) of the 64 keys of a staged q8_0 / q4_0 K tile (row
 // stride LS dwords) against the wave's query rows, in the layout of
 // mfma_scores.
@@ -883,6 +914,13 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // 4*(8*kb + e) + lane/16) is 8 consecutive floats.  O then lives in the
     // MFMA output layout: oc[c][i] = O[4g + i][8n + c].
     constexpr bool MFMA_PV = MFMA_S && VT == kF16 && Sh::V_REG && D == 128;
+    // Block-type V rows in LDS at head_dim 128 and 8 or more rows: P.V on the
+    // matrix cores with the same lane layout, lane (g, n) decoding dims
+    // 8n .. 8n+7 of key 4*st + g; the dequantised values d * code (exact in
+    // f32) are split into binary16 high and low parts and three MFMAs (Ph.Bh,
+    // Ph.Bl, Pl.Bh) keep about 22 bits.  Below 8 rows the VALU form is cheaper.
+    constexpr bool MFMA_PVB = MFMA_S && (VT == kQ8 || VT == kQ4) && !Sh::V_REG && D == 128 && RT >= 8;
+    constexpr bool MFMA_O = MFMA_PV || MFMA_PVB;  // O held in the MFMA output layout
     constexpr int NKQ = MFMA_S ? D / 32 : 1;
     rkv_half8 qhi[NKQ], qlo[NKQ];
     float mrow[4], lrow[4];
@@ -1077,7 +1115,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 lrow[i] *= al[i];
                 mrow[i] = mn;
             }
-            if constexpr (MFMA_PV) {
+            if constexpr (MFMA_O) {
 #pragma unroll
                 for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -1104,7 +1142,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                     const float pv = __builtin_amdgcn_exp2f(sv[kb][i] - mrow[i]);
                     ps += pv;
                     const int key = 16 * kb + (lane & 15);
-                    const int at = MFMA_PV ? (key & 3) * 16 + (key >> 2) : key;
+                    const int at = MFMA_O ? (key & 3) * 16 + (key >> 2) : key;
                     if (row < RT) sP[w][row * kTile + at] = pv;
                 }
                 lrow[i] += ps;
@@ -1160,7 +1198,65 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             waitcnt_vm<0>();  // this tile's V rows have landed
             __builtin_amdgcn_wave_barrier();
         }
-        if constexpr (MFMA_PV) {
+        if constexpr (MFMA_PVB) {
+            // ---- P.V on the matrix cores, block-type V (see where MFMA_PVB is set)
+            const int qi = lane & 15, gq = lane >> 4;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                rkv_half8 ph, pl;
+                if (qi < RT) {
+                    const float4 a = *(const float4 *)&sP[w][qi * kTile + gq * 16 + 8 * kb];
+                    const float4 b = *(const float4 *)&sP[w][qi * kTile + gq * 16 + 8 * kb + 4];
+                    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const _Float16 h = (_Float16)x[e];
+                        ph[e] = h;
+                        pl[e] = (_Float16)(x[e] - (float)h);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        ph[e] = (_Float16)0.f;
+                        pl[e] = (_Float16)0.f;
+                    }
+                }
+                // B operands built two keys at a time: element e of bh[c] / bl[c]
+                // is d * code of dim 8n + c of key 4*(8kb + e) + g.  The codes are
+                // exact in binary16; hi = d * code rounded once (packed f16
+                // multiply) and lo = d * code - hi (packed f16 fma, exact).
+                uint32_t hw[8][4], lw[8][4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    uint32_t ca[4], cb[4], da, db;
+                    v_group_codes_f16<VT>(sV + (4 * (8 * kb + 2 * e2) + gq) * LSV, qi, ca, da);
+                    v_group_codes_f16<VT>(sV + (4 * (8 * kb + 2 * e2 + 1) + gq) * LSV, qi, cb, db);
+                    const rkv_half2 d2 = __builtin_bit_cast(rkv_half2, da | (db << 16));
+#pragma unroll
+                    for (int p2 = 0; p2 < 4; ++p2) {
+                        // (key a, key b) of dims 2*p2 and 2*p2 + 1
+                        const rkv_half2 x0 = __builtin_bit_cast(rkv_half2, __builtin_amdgcn_perm(cb[p2], ca[p2], 0x05040100u));
+                        const rkv_half2 x1 = __builtin_bit_cast(rkv_half2, __builtin_amdgcn_perm(cb[p2], ca[p2], 0x07060302u));
+                        const rkv_half2 h0 = d2 * x0, h1 = d2 * x1;
+                        const rkv_half2 l0 = __builtin_elementwise_fma(d2, x0, -h0);
+                        const rkv_half2 l1 = __builtin_elementwise_fma(d2, x1, -h1);
+                        hw[2 * p2][e2] = __builtin_bit_cast(uint32_t, h0);
+                        hw[2 * p2 + 1][e2] = __builtin_bit_cast(uint32_t, h1);
+                        lw[2 * p2][e2] = __builtin_bit_cast(uint32_t, l0);
+                        lw[2 * p2 + 1][e2] = __builtin_bit_cast(uint32_t, l1);
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const rkv_half8 bh = __builtin_bit_cast(rkv_half8, hw[c]);
+                    const rkv_half8 bl = __builtin_bit_cast(rkv_half8, lw[c]);
+                    oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bh, oc[c], 0, 0, 0);
+                    oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bl, oc[c], 0, 0, 0);
+                    oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bh, oc[c], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if constexpr (MFMA_PV) {
             // ---- P.V on the matrix cores (layout described where MFMA_PV is set)
             const int qi = lane & 15, gq = lane >> 4;
 #pragma unroll
@@ -1253,14 +1349,14 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             // per-lane partial sums of row r live in the 16 lanes of its group
             const float t = row16_sum(lrow[r & 3]);
             l[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), 16 * (r >> 2)));
-            if constexpr (MFMA_PV)
+            if constexpr (MFMA_O)
                 m[r] = __builtin_bit_cast(float,
                                           __builtin_amdgcn_readlane(__builtin_bit_cast(int, mrow[r & 3]), 16 * (r >> 2)));
         } else {
             l[r] = wave_sum(l[r]);
         }
     }
-    if constexpr (MFMA_PV) {
+    if constexpr (MFMA_O) {
         if (wph == 1) {
             // One wave per KV head: nothing to merge inside the workgroup, so
             // the wave writes its rows straight from the MFMA output layout
@@ -1306,7 +1402,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     __syncthreads();  // every wave is done with its staging area
     float *mA = (float *)smem;                  // [NW][RT][D]
     float *mML = mA + NW * RT * D;              // [NW][RT][2]
-    if constexpr (MFMA_PV) {
+    if constexpr (MFMA_O) {
         // oc[c][i] = O[4g + i][8n + c]: every element once
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
