@@ -154,10 +154,7 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
     for (int i = 0; i < n; ++i) tiles_total += (v[i]->n_keys + kTile - 1) / kTile;
     const int nw = std::max(1, split_waves(kt, vt, D, rt));
     int hpw = 1;
-#ifndef RKV_HPW_MAX
-#define RKV_HPW_MAX 64
-#endif
-    while (2 * hpw <= nw && 2 * hpw <= Hkv && 2 * hpw <= RKV_HPW_MAX) hpw *= 2;
+    while (2 * hpw <= nw && 2 * hpw <= Hkv) hpw *= 2;
     pl->nw = nw;
     pl->hpw = hpw;
     pl->n_hg = (Hkv + hpw - 1) / hpw;
@@ -167,10 +164,7 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
     int cus = compute_units();
     if (occ <= 0) occ = 2;
     if (cus <= 0) cus = 256;
-#ifndef RKV_ROUNDS
-#define RKV_ROUNDS 1
-#endif
-    const int64_t want_groups = std::max<int64_t>(1, (int64_t)RKV_ROUNDS * occ * cus / units);
+    const int64_t want_groups = std::max<int64_t>(1, (int64_t)occ * cus / units);
     int64_t tps = std::max<int64_t>(1, (tiles_total + want_groups - 1) / want_groups);
     tps = (tps + wph - 1) / wph * wph;
     if (tps * kTile > (1 << 30)) tps = (1 << 30) / kTile;
