@@ -525,8 +525,14 @@ int rkv_ring_create(int n_slots, size_t slot_k_bytes, size_t slot_v_bytes, hipSt
             ring_free(r);
             return fail(RKV_E_NOMEM, "slot allocation failed");
         }
+        // compute_done only orders a slot's refill after the kernels that read
+        // it: those kernels write nothing the copy reads, so its record needs
+        // no system-scope cache writeback (which would also stall the compute
+        // queue and cool the caches of the kernels after it).  copy_done keeps
+        // the default fence: the compute side must see the copied bytes.
         if ((e = hipEventCreateWithFlags(&r->copy_done[i], hipEventDisableTiming)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&r->compute_done[i], hipEventDisableTiming)) != hipSuccess) {
+            (e = hipEventCreateWithFlags(&r->compute_done[i], hipEventDisableTiming | hipEventDisableSystemFence)) !=
+                hipSuccess) {
             ring_free(r);
             return hip_fail(e, "hipEventCreateWithFlags");
         }
