@@ -914,12 +914,14 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // 4*(8*kb + e) + lane/16) is 8 consecutive floats.  O then lives in the
     // MFMA output layout: oc[c][i] = O[4g + i][8n + c].
     constexpr bool MFMA_PV = MFMA_S && VT == kF16 && Sh::V_REG && D == 128;
-    // Block-type V rows in LDS at head_dim 128 and 8 or more rows: P.V on the
-    // matrix cores with the same lane layout, lane (g, n) decoding dims
-    // 8n .. 8n+7 of key 4*st + g; the dequantised values d * code (exact in
-    // f32) are split into binary16 high and low parts and three MFMAs (Ph.Bh,
-    // Ph.Bl, Pl.Bh) keep about 22 bits.  Below 8 rows the VALU form is cheaper.
-    constexpr bool MFMA_PVB = MFMA_S && (VT == kQ8 || VT == kQ4) && !Sh::V_REG && D == 128 && RT >= 8;
+    // Block-type V rows in LDS at head_dim 128: P.V on the matrix cores with
+    // the same lane layout, lane (g, n) decoding dims 8n .. 8n+7 of key
+    // 4*st + g; the dequantised values d * code (exact in f32) are split into
+    // binary16 high and low parts and three MFMAs (Ph.Bh, Ph.Bl, Pl.Bh) keep
+    // about 22 bits.  The MFMA cost does not depend on the row count (rows are
+    // padded to 16), while the VALU form decodes and multiplies every value
+    // once per row: even at 1 row the matrix cores leave the VALU far less.
+    constexpr bool MFMA_PVB = MFMA_S && (VT == kQ8 || VT == kQ4) && !Sh::V_REG && D == 128;
     constexpr bool MFMA_O = MFMA_PV || MFMA_PVB;  // O held in the MFMA output layout
     constexpr int NKQ = MFMA_S ? D / 32 : 1;
     rkv_half8 qhi[NKQ], qlo[NKQ];
@@ -995,14 +997,24 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             }
         }
     };
-    auto dma_kv = [&](int64_t t, int nkk) {
+    // Block-type K and V tiles by dword DMA, issued separately: a tile's K
+    // rows once the previous tile's scores have read theirs, its V rows once
+    // the previous tile's P.V has read theirs.
+    auto dma_kb = [&](int64_t t, int nkk) {
         if constexpr (BDMA) {
-            int kps = (int)sg.k_pos, vps2 = (int)sg.v_pos;
-            asm volatile("" : "+s"(kps), "+s"(vps2));
-            const uint32_t base = lds_addr(smem + w * Sh::STAGE_DW);
-            waitcnt_lgkm0();  // this wave's earlier LDS reads of both buffers are done
-            dma_rows4<Sh::RBK / 4, LSK>(kg + t * sg.k_pos, kps, nkk, base, lane);
-            dma_rows4<Sh::RBV / 4, LSV>(vg + t * sg.v_pos, vps2, nkk, base + 4u * kTile * LSK, lane);
+            int kps = (int)sg.k_pos;
+            asm volatile("" : "+s"(kps));
+            waitcnt_lgkm0();  // this wave's earlier LDS reads of the K buffer are done
+            dma_rows4<Sh::RBK / 4, LSK>(kg + t * sg.k_pos, kps, nkk, lds_addr(smem + w * Sh::STAGE_DW), lane);
+        }
+    };
+    auto dma_vb = [&](int64_t t, int nkk) {
+        if constexpr (BDMA) {
+            int vps2 = (int)sg.v_pos;
+            asm volatile("" : "+s"(vps2));
+            waitcnt_lgkm0();  // this wave's earlier LDS reads of the V buffer are done
+            dma_rows4<Sh::RBV / 4, LSV>(vg + t * sg.v_pos, vps2, nkk,
+                                        lds_addr(smem + w * Sh::STAGE_DW) + 4u * kTile * LSK, lane);
         }
     };
     // VMEM instructions one load_v_into issues (outstanding loads a wait may leave)
@@ -1036,7 +1048,10 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // compiler's wait on the V registers, so none is in flight there.
     int v_after_dma = 0;
     if constexpr (BDMA) {
-        if (t0 < kend) dma_kv(t0, nk_at(t0));
+        if (t0 < kend) {
+            dma_kb(t0, nk_at(t0));
+            dma_vb(t0, nk_at(t0));
+        }
     } else if constexpr (KDMA) {
         if (t0 < kend) {
             dma_k(t0, nk_at(t0));
@@ -1067,7 +1082,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         const int nk = nk_at(t0);
         const int64_t tn = t0 + tstep;
         if constexpr (BDMA) {
-            waitcnt_vm<NVD>();  // this tile's K rows have landed; V may still fly
+            // K went out before the previous tile's P.V and V after it: once
+            // at most V's loads are outstanding this tile's K rows have landed
+            waitcnt_vm<NVD>();
         } else if constexpr (KDMA) {
             // K rows arrive by DMA issued one tile ahead (V rows in registers
             // were issued with them; block-type V rows are staged now).
@@ -1094,6 +1111,13 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             float sv[4][4];
             if constexpr (KT == kQ8 || KT == kQ4) mfma_scores_blk<KT, D, LSK>(sK, qhi, qlo, lane, sv);
             else mfma_scores<D, Sh::RBK>(sK, qhi, qlo, lane, sv);
+            if constexpr (BDMA) {
+                // this tile's V rows have landed (nothing else is in flight), so
+                // the next tile's K rows can load through the rest of the tile
+                waitcnt_vm<0>();
+                __builtin_amdgcn_wave_barrier();
+                if (tn < kend) dma_kb(tn, nk_at(tn));
+            }
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const bool valid = 16 * kb + (lane & 15) < nk;
@@ -1194,10 +1218,6 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
 
-        if constexpr (BDMA) {
-            waitcnt_vm<0>();  // this tile's V rows have landed
-            __builtin_amdgcn_wave_barrier();
-        }
         if constexpr (MFMA_PVB) {
             // ---- P.V on the matrix cores, block-type V (see where MFMA_PVB is set)
             const int qi = lane & 15, gq = lane >> 4;
@@ -1327,7 +1347,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             if (tn < kend) load_vreg(tn, nk_at(tn));
         }
         if constexpr (BDMA) {
-            if (tn < kend) dma_kv(tn, nk_at(tn));
+            if (tn < kend) dma_vb(tn, nk_at(tn));
         }
         if constexpr (KDMA && V_REG) {
             v_after_dma = 0;
