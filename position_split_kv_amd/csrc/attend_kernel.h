@@ -325,6 +325,69 @@ __device__ __forceinline__ void dma_rows4(const uint8_t *src, int pos_stride, in
     }
 }
 
+// The same copy with a uniform base and a per-lane 32-bit offset
+// (global address = sbase + voff).
+__device__ __forceinline__ void lds_dma4_s(const void *sbase, uint32_t voff, uint32_t lds)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory");
+#else
+    (void)sbase;
+    (void)voff;
+    (void)lds;
+#endif
+}
+
+// Lane plan of dma_rows4_full for rows of LS dwords: slot s = i*64 + lane of
+// load i sits at byte (s / LS) * P + 4 * (s % LS) of the tile.  From load i to
+// i+1 that offset grows by DJ*P + 4*DC (uniform) plus P - 4*LS when the slot
+// wraps past a row end; bit i of wrap holds that wrap for the lane, so that
+// offset_i = i*(DJ*P + 4*DC) + 4*lane + (lane/LS + wraps before i)*(P - 4*LS).
+template <int LS>
+__device__ __forceinline__ uint64_t dma_wraps(int lane)
+{
+    constexpr int DC = 64 % LS;
+    int c = lane % LS;
+    uint64_t wrap = 0;
+#pragma unroll
+    for (int i = 0; i + 1 < LS; ++i) {
+        if (c >= LS - DC) wrap |= 1ull << i;
+        c += DC;
+        if (c >= LS) c -= LS;
+    }
+    return wrap;
+}
+
+// dma_rows4 for a whole tile (kTile rows) that is followed by at least one
+// more position of the segment, with P >= 4*LS: no clamps; a row's padding
+// slots read the dwords after the row (inside the next row or position,
+// never used).  Per load: one bit test and one 24-bit multiply-add.
+template <int LS>
+__device__ __forceinline__ void dma_rows4_full(const uint8_t *src, int P, uint64_t wrap, uint32_t lds_base, int lane)
+{
+    static_assert(LS <= 64, "one row per load at least");
+    constexpr int DJ = 64 / LS, DC = 64 % LS;
+    const int db = DJ * P + 4 * DC;
+    const int xd = P - 4 * LS;  // >= 0, < 2^23
+    uint32_t wlo = (uint32_t)wrap, whi = (uint32_t)(wrap >> 32);
+    // (opaque to the compiler, so that the per-load offsets are recomputed
+    // here rather than hoisted out of the tile loop into registers)
+    asm volatile("" : "+v"(wlo), "+v"(whi), "+v"(lane));
+    uint32_t voff = __umul24((uint32_t)(lane / LS), (uint32_t)xd) + 4u * (uint32_t)lane;
+#pragma unroll
+    for (int i = 0; i < LS; ++i) {
+        lds_dma4_s(src + (int64_t)i * db, voff, lds_base + 256u * i);
+        if (i + 1 < LS) {
+            const uint32_t bit = ((i < 32 ? wlo >> i : whi >> (i - 32)) & 1u);
+            voff += __umul24(bit, (uint32_t)xd);
+        }
+    }
+}
+
 // s_waitcnt vmcnt(n) (0 <= n <= 63), other counters untouched.
 template <int N>
 __device__ __forceinline__ void waitcnt_vm()
@@ -1000,12 +1063,23 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // Block-type K and V tiles by dword DMA, issued separately: a tile's K
     // rows once the previous tile's scores have read theirs, its V rows once
     // the previous tile's P.V has read theirs.
+    // A whole tile followed by another position of the segment, with
+    // position strides of at least a padded row and below 2^23 bytes, takes
+    // the clamp-free form; the segment's last tile the clamped one.
+    constexpr int LSK1 = LSK > 0 ? LSK : 1, LSV1 = LSV > 0 ? LSV : 1;
+    const uint64_t kwrap = BDMA ? dma_wraps<LSK1>(lane) : 0, vwrap = BDMA ? dma_wraps<LSV1>(lane) : 0;
+    const bool kfull_ok = sg.k_pos >= 4 * LSK && sg.k_pos < (1 << 23);
+    const bool vfull_ok = sg.v_pos >= 4 * LSV && sg.v_pos < (1 << 23);
     auto dma_kb = [&](int64_t t, int nkk) {
         if constexpr (BDMA) {
             int kps = (int)sg.k_pos;
             asm volatile("" : "+s"(kps));
             waitcnt_lgkm0();  // this wave's earlier LDS reads of the K buffer are done
-            dma_rows4<Sh::RBK / 4, LSK>(kg + t * sg.k_pos, kps, nkk, lds_addr(smem + w * Sh::STAGE_DW), lane);
+            const uint32_t base = lds_addr(smem + w * Sh::STAGE_DW);
+            if (kfull_ok && nkk == kTile && t + kTile < sg.n_keys)
+                dma_rows4_full<LSK1>(kg + t * sg.k_pos, kps, kwrap, base, lane);
+            else
+                dma_rows4<Sh::RBK / 4, LSK>(kg + t * sg.k_pos, kps, nkk, base, lane);
         }
     };
     auto dma_vb = [&](int64_t t, int nkk) {
@@ -1013,8 +1087,11 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             int vps2 = (int)sg.v_pos;
             asm volatile("" : "+s"(vps2));
             waitcnt_lgkm0();  // this wave's earlier LDS reads of the V buffer are done
-            dma_rows4<Sh::RBV / 4, LSV>(vg + t * sg.v_pos, vps2, nkk,
-                                        lds_addr(smem + w * Sh::STAGE_DW) + 4u * kTile * LSK, lane);
+            const uint32_t base = lds_addr(smem + w * Sh::STAGE_DW) + 4u * kTile * LSK;
+            if (vfull_ok && nkk == kTile && t + kTile < sg.n_keys)
+                dma_rows4_full<LSV1>(vg + t * sg.v_pos, vps2, vwrap, base, lane);
+            else
+                dma_rows4<Sh::RBV / 4, LSV>(vg + t * sg.v_pos, vps2, nkk, base, lane);
         }
     };
     // VMEM instructions one load_v_into issues (outstanding loads a wait may leave)
