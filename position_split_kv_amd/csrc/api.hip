@@ -153,11 +153,19 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
     int64_t tiles_total = 0;
     for (int i = 0; i < n; ++i) tiles_total += (v[i]->n_keys + kTile - 1) / kTile;
     const int nw = std::max(1, split_waves(kt, vt, D, rt));
+    // With dim slices a head slot is one (KV head, slice) and every wave of a
+    // workgroup takes a slot (the slices of a head meet at barriers).
+    const int ds = split_dim_slices(kt, vt, D);
+    const int slots = Hkv * ds;
     int hpw = 1;
-    while (2 * hpw <= nw && 2 * hpw <= Hkv) hpw *= 2;
+    if (ds > 1 && nw < ds) return fail(RKV_E_UNSUPPORTED, "too few waves per workgroup for %d dim slices", ds);
+    if (ds > 1)
+        hpw = nw;
+    else
+        while (2 * hpw <= nw && 2 * hpw <= slots) hpw *= 2;
     pl->nw = nw;
     pl->hpw = hpw;
-    pl->n_hg = (Hkv + hpw - 1) / hpw;
+    pl->n_hg = (slots + hpw - 1) / hpw;
     const int64_t wph = nw / hpw;
     const int64_t units = (int64_t)pl->n_hg * pl->n_rg * pl->z;
     int occ = split_occupancy(kt, vt, D, rt);

@@ -24,6 +24,12 @@ bool split_supported(int kt, int vt, int d, int rt)
     return t && dd && r;
 }
 
+int split_dim_slices(int kt, int vt, int d)
+{
+    const bool blk = (kt == kQ8 || kt == kQ4) && (vt == kQ8 || vt == kQ4);
+    return blk && d > 128 ? d / 128 : 1;
+}
+
 int split_waves(int kt, int vt, int d, int rt)
 {
 #define RKV_NW(kk, vv) \

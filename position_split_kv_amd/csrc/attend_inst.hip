@@ -12,12 +12,23 @@
 
 namespace rkv {
 
+// Block-type K and V at head_dim 256 / 512 run as 2 / 4 dim slices of 128
+// (see rkv_split_kernel): the instance used for a requested head_dim.
+constexpr bool kBlockKV = (RKV_KT == kQ8 || RKV_KT == kQ4) && (RKV_VT == kQ8 || RKV_VT == kQ4);
+template <int D>
+constexpr int slices_of() { return kBlockKV && D > 128 ? D / 128 : 1; }
+
 template <int D, int RT>
 static hipError_t go(dim3 grid, const float *q, float *pa, float2 *pm, float *o, float *lse, const SplitParams &p,
                      hipStream_t stream)
 {
     if constexpr (D == 512 && (RKV_KT == kF32 || RKV_VT == kF32)) {
         return hipErrorInvalidValue;  // an f32 row of 512 values does not fit the LDS tile
+    } else if constexpr (slices_of<D>() > 1) {
+        constexpr int DS = slices_of<D>();
+        hipLaunchKernelGGL((rkv_split_kernel<RKV_KT, RKV_VT, 128, RT, DS>), grid,
+                           dim3(64 * Shape<RKV_KT, RKV_VT, 128>::waves(sp_rows(RT, DS))), 0, stream, q, pa, pm, o, lse, p);
+        return hipGetLastError();
     } else {
         hipLaunchKernelGGL((rkv_split_kernel<RKV_KT, RKV_VT, D, RT>), grid, dim3(64 * Shape<RKV_KT, RKV_VT, D>::waves(RT)), 0,
                            stream, q, pa, pm, o, lse, p);
@@ -57,6 +68,16 @@ static int occ_of()
 {
     if constexpr (D == 512 && (RKV_KT == kF32 || RKV_VT == kF32)) {
         return 0;
+    } else if constexpr (slices_of<D>() > 1) {
+        constexpr int DS = slices_of<D>();
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rkv_split_kernel<RKV_KT, RKV_VT, 128, RT, DS>,
+                                                         64 * Shape<RKV_KT, RKV_VT, 128>::waves(sp_rows(RT, DS)), 0) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        return n;
     } else {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rkv_split_kernel<RKV_KT, RKV_VT, D, RT>,
@@ -98,14 +119,15 @@ int RKV_NAME_OCC(RKV_KT, RKV_VT)(int d, int rt)
 template <int D>
 static int nw_by_rt(int rt)
 {
-    using Sh = Shape<RKV_KT, RKV_VT, D>;
+    constexpr int DS = slices_of<D>();
+    using Sh = Shape<RKV_KT, RKV_VT, (DS > 1 ? 128 : D)>;
     switch (rt) {
-    case 1: return Sh::waves(1);
-    case 2: return Sh::waves(2);
-    case 4: return Sh::waves(4);
-    case 5: return Sh::waves(5);
-    case 8: return Sh::waves(8);
-    case 16: return Sh::waves(16);
+    case 1: return Sh::waves(sp_rows(1, DS));
+    case 2: return Sh::waves(sp_rows(2, DS));
+    case 4: return Sh::waves(sp_rows(4, DS));
+    case 5: return Sh::waves(sp_rows(5, DS));
+    case 8: return Sh::waves(sp_rows(8, DS));
+    case 16: return Sh::waves(sp_rows(16, DS));
     default: return 0;
     }
 }

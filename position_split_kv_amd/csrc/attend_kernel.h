@@ -870,13 +870,26 @@ __device__ __forceinline__ int u16_at(const uint16_t *tab, int i)
 
 // ---------------------------------------------------------------- the kernel
 
-template <int KT, int VT, int D, int RT>
-__global__ void __launch_bounds__((64 * Shape<KT, VT, D>::waves(RT)))
+// Rows of a wave's score buffer: RT, or with dim slices (DS > 1) the rows of
+// the lanes that hold real rows in the MFMA layout (a multiple of 4), since
+// the buffer also carries the partial scores between the slices of a head.
+__host__ __device__ constexpr int sp_rows(int rt, int ds) { return ds > 1 ? (rt + 3) / 4 * 4 : rt; }
+
+// D is the head_dim a wave works on.  DS > 1 (block-type K and V at head_dim
+// DS*D): every KV head is cut into DS slices of D dims, one wave each, in the
+// same workgroup; a slice's partial scores (q . k over its D dims) are summed
+// with those of the head's other slices through LDS, in slice order, so that
+// all DS waves hold the same scores and softmax, and each then accumulates
+// P.V for its own D dims of V.
+template <int KT, int VT, int D, int RT, int DS = 1>
+__global__ void __launch_bounds__((64 * Shape<KT, VT, D>::waves(sp_rows(RT, DS))))
 rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, float2 *__restrict__ part_ml,
                  float *__restrict__ o_out, float *__restrict__ lse_out, const SplitParams p)
 {
     using Sh = Shape<KT, VT, D>;
-    constexpr int NW = Sh::waves(RT);
+    constexpr int RTX = sp_rows(RT, DS);
+    constexpr int NW = Sh::waves(RTX);
+    constexpr int DF = D * DS;  // head_dim of q, o and the partials
     constexpr int LSK = Sh::LSK, LSV = Sh::LSV;
     constexpr bool V_REG = Sh::V_REG;
     constexpr int VWK = load_width_of(KT, D);
@@ -889,7 +902,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     constexpr int SMEM_DW = NW * Sh::STAGE_DW > MERGE_DW ? NW * Sh::STAGE_DW : MERGE_DW;
 
     __shared__ __attribute__((aligned(16))) uint32_t smem[SMEM_DW];
-    __shared__ float sP[NW][RT * kTile];
+    __shared__ __attribute__((aligned(16))) float sP[NW][RTX * kTile];
     __shared__ int sRow[NW][RT];  // output row of each wave's rows (-1: none), for the epilogue
 
     const int lane = threadIdx.x & 63;
@@ -903,7 +916,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     const int wph = 1 << p.wph_log2;
     const int hs = w >> p.wph_log2;
     const int ws = w - hs * wph;
-    const int g = (hg << p.hpw_log2) + hs;
+    // head slot -> KV head g and dim slice js (js = 0 and g the slot when DS = 1)
+    const int vh = (hg << p.hpw_log2) + hs;
+    const int g = vh / DS, js = vh - (vh / DS) * DS;
     const int cnt = g < p.n_kv_heads ? u16_at(p.rowcnt, g) - rg * RT : 0;
     const int nr = cnt <= 0 ? 0 : cnt < RT ? cnt : RT;  // 0: a wave with no rows (it still joins the barriers)
     const int z = blockIdx.z;
@@ -914,11 +929,15 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     for (int si = 1; si < kMaxSegs; ++si)
         if (si < p.n_segs && (int)blockIdx.x >= p.seg[si].split_base) sg = p.seg[si];
     const int64_t kbeg = (int64_t)((int)blockIdx.x - sg.split_base) * sg.keys_per_split;
-    const int64_t kend = nr == 0 ? kbeg : kbeg + sg.keys_per_split < sg.n_keys ? kbeg + sg.keys_per_split : sg.n_keys;
+    // (with dim slices every wave walks the same tiles, rows or not: the slices
+    // meet at a barrier per tile)
+    const int64_t kend = (nr == 0 && DS == 1) ? kbeg
+                         : kbeg + sg.keys_per_split < sg.n_keys ? kbeg + sg.keys_per_split : sg.n_keys;
     const int64_t tstep = (int64_t)wph * kTile;  // tile stride of this wave
 
-    const uint8_t *kg = sg.k + z * sg.k_seq + g * sg.k_head;
-    const uint8_t *vg = sg.v + z * sg.v_seq + g * sg.v_head;
+    const int gr = g < p.n_kv_heads ? g : p.n_kv_heads - 1;  // a slot past the heads reads a real one
+    const uint8_t *kg = sg.k + z * sg.k_seq + gr * sg.k_head + js * Sh::RBK;
+    const uint8_t *vg = sg.v + z * sg.v_seq + gr * sg.v_head + js * Sh::RBV;
 
     // Output rows of the wave's RT rows (-1 past nr).  The table is read at
     // a clamped index whatever nr is, so these reads do not wait for the
@@ -940,7 +959,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     for (int r = 0; r < RT; ++r) {
         const int rr = r < nr ? r : nr - 1;  // padding rows repeat the last row; never written
         rid[r] = nr == 0 ? 0 : tabrow[rr];
-        qp[r] = q + rid[r] * D;
+        qp[r] = q + rid[r] * DF + js * D;
     }
 
     float m[RT], l[RT], acc[RT][8];
@@ -986,6 +1005,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // once per row: even at 1 row the matrix cores leave the VALU far less.
     constexpr bool MFMA_PVB = MFMA_S && (VT == kQ8 || VT == kQ4) && !Sh::V_REG && D == 128;
     constexpr bool MFMA_O = MFMA_PV || MFMA_PVB;  // O held in the MFMA output layout
+    static_assert(DS == 1 || MFMA_PVB, "dim slices need block-type K and V on the matrix cores");
     constexpr int NKQ = MFMA_S ? D / 32 : 1;
     rkv_half8 qhi[NKQ], qlo[NKQ];
     float mrow[4], lrow[4];
@@ -1110,7 +1130,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         int rowi = 0;
 #pragma unroll
         for (int r = 0; r < RT; ++r) rowi = (qr == r && tabrow[r] >= 0) ? tabrow[r] : rowi;
-        mfma_q_load<D>(q + (int64_t)rowi * D, lane, qraw);
+        mfma_q_load<D>(q + (int64_t)rowi * DF + js * D, lane, qraw);
     }
 
     int64_t t0 = kbeg + (int64_t)ws * kTile;
@@ -1194,6 +1214,44 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 waitcnt_vm<0>();
                 __builtin_amdgcn_wave_barrier();
                 if (tn < kend) dma_kb(tn, nk_at(tn));
+            }
+            if constexpr (DS > 1) {
+                // The head's slices exchange their partial scores: lane l holds
+                // rows 4*(l/16) .. +3 of keys 16*kb + l%16, so lanes below 4*RTX
+                // carry every real row; each slice sums the DS partials in slice
+                // order (the same sums, bit for bit, in all DS waves).
+                constexpr int XL = 4 * RTX;
+                float4 *xs = (float4 *)&sP[w][0];
+                if (lane < XL) {
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) xs[4 * lane + kb] = make_float4(sv[kb][0], sv[kb][1], sv[kb][2], sv[kb][3]);
+                }
+                __syncthreads();
+                if (lane < XL) {
+                    float4 a4[4];
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) a4[kb] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                    for (int j = 0; j < DS; ++j) {
+                        const float4 *xo = (const float4 *)&sP[w - js + j][0];
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb) {
+                            const float4 x = xo[4 * lane + kb];
+                            a4[kb].x += x.x;
+                            a4[kb].y += x.y;
+                            a4[kb].z += x.z;
+                            a4[kb].w += x.w;
+                        }
+                    }
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) {
+                        sv[kb][0] = a4[kb].x;
+                        sv[kb][1] = a4[kb].y;
+                        sv[kb][2] = a4[kb].z;
+                        sv[kb][3] = a4[kb].w;
+                    }
+                }
+                __syncthreads();  // every slice has read the partials before P overwrites them
             }
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
@@ -1454,8 +1512,8 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         }
     }
     if constexpr (MFMA_O) {
-        if (wph == 1) {
-            // One wave per KV head: nothing to merge inside the workgroup, so
+        if (DS > 1 || wph == 1) {
+            // One wave per KV head (or dim slice): nothing to merge inside the workgroup, so
             // the wave writes its rows straight from the MFMA output layout
             // (lane (g, n) holds dims 8n .. 8n+7 of rows 4g .. 4g+3).  The
             // values are those the LDS merge would produce for one wave.
@@ -1475,11 +1533,11 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 float v[8];
 #pragma unroll
                 for (int c = 0; c < 8; ++c) v[c] = single ? oc[c][i] / lr : oc[c][i];
-                float *dst = single ? o_out + (int64_t)rr * D : part_acc + (pbase + rr) * D;
+                float *dst = (single ? o_out + (int64_t)rr * DF : part_acc + (pbase + rr) * DF) + js * D;
                 *(float4 *)(dst + 8 * (lane & 15)) = make_float4(v[0], v[1], v[2], v[3]);
                 *(float4 *)(dst + 8 * (lane & 15) + 4) = make_float4(v[4], v[5], v[6], v[7]);
             }
-            if (lane < RT) {
+            if (js == 0 && lane < RT) {
                 int rr = -1;
                 float mr = 0.f, lr = 1.f;
 #pragma unroll

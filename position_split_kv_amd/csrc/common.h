@@ -89,6 +89,10 @@ hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q
 hipError_t launch_reduce(int d, int64_t n_rows, int n_splits, const float *part_acc, const float2 *part_ml,
                          float *o, float *lse, hipStream_t stream);
 bool split_supported(int kt, int vt, int d, int rt);
+// Dim slices per KV head the split kernel uses for a (K type, V type,
+// head_dim): block-type K and V at head_dim 256 / 512 run as 2 / 4 slices of
+// 128 dims, one wave each, all of a head's slices in one workgroup; else 1.
+int split_dim_slices(int kt, int vt, int d);
 // Waves per workgroup of the split kernel for a (K type, V type, head_dim).
 int split_waves(int kt, int vt, int d, int rt);
 // Workgroups of a split-kernel instance resident per compute unit on the
