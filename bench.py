@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # WRITE_SIZE), each scaled by that counter's reading for a plain 1 GiB copy
 # (x2.0 and x1.0); None once the kernels have changed since the counters
 # were taken.
-MEASURED_TRAFFIC_BYTES = 280_247_416
+MEASURED_TRAFFIC_BYTES = 280_234_194
 
 
 def log(msg):
@@ -483,7 +483,7 @@ def streamed_tail(P, synth, sweep=False, L=48, steps=3):
     # The same layers with shorter tails (same window, same 8192-key tiles):
     # the tail-hidden fraction is judged where the tail fits the free zone,
     # and the figure reported is the worst of those points.
-    fz = [measure(t, tile) for t in (4096, 8192, 12288)]
+    fz = [measure(t, tile) for t in (4096, 6144, 8192, 12288)]
     res["free_zone_points"] = fz
     inside = [x["tail_hidden_fraction"] for x in fz if x["tail_keys"] <= x["free_zone_keys_per_layer"]]
     res["tail_hidden_fraction_in_free_zone"] = min(inside) if inside else None
