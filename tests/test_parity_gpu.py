@@ -71,6 +71,15 @@ CASES = [
     ("f16_batch3_own_keys", 3, 8, 2, 128, synth.F16, synth.F16, 300, 100, None, 0.0, None),
     ("q8q8_d256_g8", 1, 16, 2, 256, synth.Q8_0, synth.Q8_0, 200, 64, None, 0.0, None),
     ("f16_d512", 1, 4, 1, 512, synth.F16, synth.F16, 150, 70, None, 0.0, None),
+    # block-type K and V at head_dim 256 / 512 run as dim slices of 128 (one wave each, partial scores summed
+    # across the slices of a head): MHA with a second workgroup of head slots half empty; 16 rows per slice
+    # (4-wave workgroups) with a cap; sequences with their own keys; and a head map whose second row group is
+    # empty for one head (its slice waves hold no rows and still walk every tile)
+    ("q4q4_d512_mha3", 1, 3, 3, 512, synth.Q4_0, synth.Q4_0, 600, 300, None, 0.0, None),
+    ("q8q8_d512_g16_cap", 1, 32, 2, 512, synth.Q8_0, synth.Q8_0, 300, 100, None, 10.0, None),
+    ("q4q8_d256_batch2", 2, 8, 2, 256, synth.Q4_0, synth.Q8_0, 260, 130, None, 0.0, None),
+    ("q8q4_d256_g2", 1, 4, 2, 256, synth.Q8_0, synth.Q4_0, 333, 200, None, 0.0, None),
+    ("q8q8_d512_map_rowgroups", 1, 20, 2, 512, synth.Q8_0, synth.Q8_0, 257, 128, None, 0.0, [0] * 18 + [1] * 2),
 ]
 
 
