@@ -408,71 +408,76 @@ def streamed_tail(P, synth, sweep=False, L=48, steps=3):
     o_w, l_w = torch.empty(1, Hq, D, device=dev), torch.empty(1, Hq, device=dev)
     ws_w = P.workspace(P.rkv_attend_workspace_bytes(desc, P.view_of_cache(lay[0]["kc"], lay[0]["vc"], 0, wc)))
 
-    def run(tail_keys, tile_keys, mode):
-        """One step; mode 'resident' (T_c), 'copy' (T_d) or 'stream' (T_p).  Returns seconds."""
+    def measure(tail_keys, tile_keys, reps=steps):
+        """T_c, T_d, T_p of one (tail, tile) setting.  The three kinds of step
+        ('resident': the tiles attended from HBM, no copies; 'copy': the tile
+        copies alone on the copy stream; 'stream': the pipelined step through
+        the ring) are set up once and run interleaved, rep after rep, so that
+        slow drifts of the part's clocks hit all three alike; each figure is
+        the median over the reps (after one untimed rep)."""
         n_t = (tail_keys + tile_keys - 1) // tile_keys
         kc0, vc0 = lay[0]["kc"], lay[0]["vc"]
-        if mode == "stream":
-            ring = P.Ring(B, tile_keys * kc0.pos_stride, tile_keys * vc0.pos_stride)
-            tails = [P.view_of_cache(l_["kh"], l_["vh"], 0, tail_keys) for l_ in lay]
-        elif mode == "copy":
-            slots = [(torch.empty(tile_keys * kc0.pos_stride, dtype=torch.uint8, device=dev),
-                      torch.empty(tile_keys * vc0.pos_stride, dtype=torch.uint8, device=dev)) for _ in range(B)]
+        ring = P.Ring(B, tile_keys * kc0.pos_stride, tile_keys * vc0.pos_stride)
+        tails = [P.view_of_cache(l_["kh"], l_["vh"], 0, tail_keys) for l_ in lay]
+        slots = [(torch.empty(tile_keys * kc0.pos_stride, dtype=torch.uint8, device=dev),
+                  torch.empty(tile_keys * vc0.pos_stride, dtype=torch.uint8, device=dev)) for _ in range(B)]
         parts_o = [torch.empty(1, Hq, D, device=dev) for _ in range(n_t + 1)]
         parts_l = [torch.empty(1, Hq, device=dev) for _ in range(n_t + 1)]
         ws_t = P.workspace(P.rkv_attend_workspace_bytes(desc, P.view_of_cache(kc0, vc0, wc, wc + min(tile_keys, tail_keys))))
-        times = []
-        try:
-            for it in range(steps + 1):
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                if mode == "copy":
-                    with torch.cuda.stream(cs):
-                        j = 0
-                        for l_ in lay:
-                            kb, vb = l_["kh"].data.view(-1), l_["vh"].data.view(-1)
-                            for t in range(n_t):
-                                a0, a1 = t * tile_keys, min(tail_keys, (t + 1) * tile_keys)
-                                sk, sv = slots[j % B]
-                                sk[: (a1 - a0) * kc0.pos_stride].copy_(kb[a0 * kc0.pos_stride: a1 * kc0.pos_stride], non_blocking=True)
-                                sv[: (a1 - a0) * vc0.pos_stride].copy_(vb[a0 * vc0.pos_stride: a1 * vc0.pos_stride], non_blocking=True)
-                                j += 1
-                    cs.synchronize()
-                else:
-                    if mode == "stream":
-                        ring.rkv_ring_begin_step(tails, tile_keys)
-                        ws_s = P.workspace(ring.rkv_stream_tail_workspace_bytes(0, desc))
-                    for li, l_ in enumerate(lay):
-                        P.rkv_attend_segment(desc, l_["q"], P.view_of_cache(l_["kc"], l_["vc"], 0, wc), o_w, l_w, ws_w, stream)
-                        if mode == "stream":
-                            ring.rkv_stream_tail(li, desc, l_["q"], o_w, l_w, outs[li][0], outs[li][1], ws_s, stream)
-                        else:
-                            for t in range(n_t):
-                                a0, a1 = wc + t * tile_keys, wc + min(tail_keys, (t + 1) * tile_keys)
-                                P.rkv_attend_segment(desc, l_["q"], P.view_of_cache(l_["kc"], l_["vc"], a0, a1),
-                                                     parts_o[t + 1], parts_l[t + 1], ws_t, stream)
-                            P.rkv_lse_combine([o_w] + parts_o[1:], [l_w] + parts_l[1:], outs[li][0], outs[li][1], D, stream)
-                        ffn(li)
-                    if mode == "stream":
-                        ring.rkv_ring_end_step()
-                    torch.cuda.synchronize()
-                if it > 0:
-                    times.append(time.perf_counter() - t0)
-        finally:
-            if mode == "stream":
-                ring.close()
-        return statistics.median(times)
+        ws_s = [None]
 
-    def measure(tail_keys, tile_keys):
-        t_c = run(tail_keys, tile_keys, "resident")
-        t_d = run(tail_keys, tile_keys, "copy")
-        t_p = run(tail_keys, tile_keys, "stream")
-        tail_bytes = L * tail_keys * (lay[0]["kc"].pos_stride + lay[0]["vc"].pos_stride)
+        def step(mode):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            if mode == "copy":
+                with torch.cuda.stream(cs):
+                    j = 0
+                    for l_ in lay:
+                        kb, vb = l_["kh"].data.view(-1), l_["vh"].data.view(-1)
+                        for t in range(n_t):
+                            a0, a1 = t * tile_keys, min(tail_keys, (t + 1) * tile_keys)
+                            sk, sv = slots[j % B]
+                            sk[: (a1 - a0) * kc0.pos_stride].copy_(kb[a0 * kc0.pos_stride: a1 * kc0.pos_stride], non_blocking=True)
+                            sv[: (a1 - a0) * vc0.pos_stride].copy_(vb[a0 * vc0.pos_stride: a1 * vc0.pos_stride], non_blocking=True)
+                            j += 1
+                cs.synchronize()
+            else:
+                if mode == "stream":
+                    ring.rkv_ring_begin_step(tails, tile_keys)
+                    if ws_s[0] is None:
+                        ws_s[0] = P.workspace(ring.rkv_stream_tail_workspace_bytes(0, desc))
+                for li, l_ in enumerate(lay):
+                    P.rkv_attend_segment(desc, l_["q"], P.view_of_cache(l_["kc"], l_["vc"], 0, wc), o_w, l_w, ws_w, stream)
+                    if mode == "stream":
+                        ring.rkv_stream_tail(li, desc, l_["q"], o_w, l_w, outs[li][0], outs[li][1], ws_s[0], stream)
+                    else:
+                        for t in range(n_t):
+                            a0, a1 = wc + t * tile_keys, wc + min(tail_keys, (t + 1) * tile_keys)
+                            P.rkv_attend_segment(desc, l_["q"], P.view_of_cache(l_["kc"], l_["vc"], a0, a1),
+                                                 parts_o[t + 1], parts_l[t + 1], ws_t, stream)
+                        P.rkv_lse_combine([o_w] + parts_o[1:], [l_w] + parts_l[1:], outs[li][0], outs[li][1], D, stream)
+                    ffn(li)
+                if mode == "stream":
+                    ring.rkv_ring_end_step()
+                torch.cuda.synchronize()
+            return time.perf_counter() - t0
+
+        times = {"resident": [], "copy": [], "stream": []}
+        try:
+            for rep in range(reps + 1):
+                for mode in ("resident", "copy", "stream"):
+                    dt = step(mode)
+                    if rep > 0:
+                        times[mode].append(dt)
+        finally:
+            ring.close()
+        t_c, t_d, t_p = (statistics.median(times[m]) for m in ("resident", "copy", "stream"))
+        tail_bytes = L * tail_keys * (kc0.pos_stride + vc0.pos_stride)
         h = min(1.0, max(0.0, (t_c + t_d - t_p) / t_d))
-        return {"tail_keys": tail_keys, "tile_keys": tile_keys, "T_c_ms": round(t_c * 1e3, 3),
+        return {"tail_keys": tail_keys, "tile_keys": tile_keys, "reps": reps, "T_c_ms": round(t_c * 1e3, 3),
                 "T_d_ms": round(t_d * 1e3, 3), "T_p_ms": round(t_p * 1e3, 3), "tail_hidden_fraction": round(h, 4),
                 "tail_GBs": round(tail_bytes / t_p / 1e9, 2), "link_fraction": round(tail_bytes / t_p / 1e9 / r_link, 4),
-                "free_zone_keys_per_layer": round(t_c * r_link * 1e9 / L / (lay[0]["kc"].pos_stride + lay[0]["vc"].pos_stride))}
+                "free_zone_keys_per_layer": round(t_c * r_link * 1e9 / L / (kc0.pos_stride + vc0.pos_stride))}
 
     log(f"streamed: FFN stand-in {reps} x GEMV ({t_gemv * 1e6:.1f} us each); pinned H2D {r_link:.1f} GB/s")
     main = measure(n - wc, tile)
@@ -483,7 +488,7 @@ def streamed_tail(P, synth, sweep=False, L=48, steps=3):
     # The same layers with shorter tails (same window, same 8192-key tiles):
     # the tail-hidden fraction is judged where the tail fits the free zone,
     # and the figure reported is the worst of those points.
-    fz = [measure(t, tile) for t in (4096, 6144, 8192, 12288)]
+    fz = [measure(t, tile, reps=9) for t in (4096, 6144, 8192, 12288)]
     res["free_zone_points"] = fz
     inside = [x["tail_hidden_fraction"] for x in fz if x["tail_keys"] <= x["free_zone_keys_per_layer"]]
     res["tail_hidden_fraction_in_free_zone"] = min(inside) if inside else None
