@@ -193,7 +193,12 @@ int rkv_dequant_q4_0(const void *blocks, int64_t n_values, float *out, hipStream
  * of V, filled from pinned host memory by asynchronous copies on a copy
  * stream.  The copy into a slot waits for the slot's compute_done event; the
  * attention of a tile waits for its slot's copy_done event ("F5 M7 -- Rolling
- * KV", "CUDA stream graph").  The order of copies is one flat sequence over
+ * KV", "CUDA stream graph").  The first of these waits is taken on the host:
+ * a copier thread owned by the ring waits for a slot's compute_done and then
+ * enqueues the slot's copies (DMA-engine hipMemcpyAsync) and copy_done record,
+ * so the copy stream carries no wait on a compute-queue event (such a wait
+ * costs a DMA-engine copy tens of microseconds even when the event has long
+ * completed).  The order of copies is one flat sequence over
  * (layer, tile) for a whole decode step, kept n_slots ahead of compute
  * across layer boundaries ("Rolling-KV: step/graph-level tail prefetch
  * (design)", "The fix: a persistent, step-spanning tail-prefetch ring"), so a
@@ -204,17 +209,20 @@ typedef struct rkv_ring rkv_ring;
 /* Create a ring.  n_slots >= 2 (<= 16).  slot_k_bytes / slot_v_bytes: bytes
  * of one tile of K / V (tile_keys * pos_stride of the tail views).
  * copy_stream: NULL makes the ring create and own a non-blocking stream.
- * The ring owns its slots, its events (created here, timing disabled) and a
- * stream it created.  Errors: RKV_E_INVAL, RKV_E_NOMEM, RKV_E_HIP. */
+ * The ring owns its slots, its events (created here, timing disabled), a
+ * stream it created and its copier thread (started here, on the current
+ * device).  Errors: RKV_E_INVAL, RKV_E_NOMEM, RKV_E_HIP. */
 int rkv_ring_create(int n_slots, size_t slot_k_bytes, size_t slot_v_bytes, hipStream_t copy_stream,
                     rkv_ring **out);
-/* Wait for the ring's work to finish, then free it.  NULL is a no-op. */
+/* Stop the copier (copies it has not enqueued yet are dropped), wait for the
+ * ring's enqueued work to finish, then free it.  NULL is a no-op. */
 int rkv_ring_destroy(rkv_ring *ring);
 
 /* Plan one step: the tails of n_layers layers (host_tails[l], each in pinned
  * host memory, one sequence or shared by all sequences), cut into tiles of
  * tile_keys keys (the last tile of a layer may be partial; an empty tail has
- * no tiles).  Enqueues the first n_slots copies.  The host buffers must stay
+ * no tiles).  Hands the first n_slots copies to the copier (each waits for
+ * the previous step's last use of its slot).  The host buffers must stay
  * alive and unchanged until the step's attention has completed.
  * Errors: RKV_E_INVAL (device pointer, tile larger than a slot, misaligned),
  * RKV_E_STATE (previous step not ended). */
@@ -227,15 +235,19 @@ int rkv_stream_tail_workspace_bytes(const rkv_ring *ring, int layer, const rkv_a
  * rkv_stream_tail -- attention over layer `layer`'s tail, tile by tile from
  * the ring, merged with the window's result.
  *
- * For each tile: the compute stream waits copy_done of its slot, attends the
+ * For each tile: the call waits on the host until the copier has enqueued
+ * the tile's copy (at most until the GPU has finished the compute n_slots
+ * items earlier); the compute stream waits copy_done of its slot, attends the
  * slot, records compute_done; then the refill of that slot with the item
- * n_slots further on in the flat order is enqueued on the copy stream.
+ * n_slots further on in the flat order is handed to the copier.
  * Finally (o_window, lse_window) and the tiles' results are merged with
  * rkv_lse_combine in the order window, tile 0, tile 1, ...  lse_window may be
  * NULL (no window; o_window is then ignored).  The result equals, bit for
  * bit, rkv_attend_segment on each tile resident in device memory followed by
  * that combine, whatever n_slots is.  Layers must be consumed in plan order.
- * Errors: RKV_E_STATE (layer out of order / no step), RKV_E_INVAL.
+ * Errors: RKV_E_STATE (layer out of order / no step), RKV_E_INVAL, RKV_E_HIP
+ * (also a failure of the copier).  A failure once the tiles have started
+ * aborts the step: later calls return RKV_E_STATE until the next begin_step.
  */
 int rkv_stream_tail(rkv_ring *ring, int layer, const rkv_attn_desc *desc, const float *q,
                     const float *o_window, const float *lse_window, float *o, float *lse,

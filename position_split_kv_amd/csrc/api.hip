@@ -7,7 +7,11 @@
 #include <string.h>
 
 #include <algorithm>
+#include <condition_variable>
+#include <deque>
+#include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "common.h"
@@ -472,25 +476,108 @@ struct rkv_ring {
     std::vector<Item> items;
     std::vector<int64_t> first_item;  // per layer, plus end
     int next_layer = 0;
+    int64_t base = 0;  // sequence number of the step's item 0 (items of all steps are numbered in order)
+    // The copier thread: for each requested item it waits on the host for the
+    // compute that last read the item's slot, then enqueues the slot's copy
+    // and its copy_done record (see enqueue_copy).
+    std::thread copier;
+    std::mutex mu;
+    std::condition_variable cv_req, cv_done;
+    std::deque<int64_t> req;       // items (indices in the step) whose copy is to be enqueued
+    int64_t enq[16];               // sequence number of the item whose copy slot s holds or receives
+    bool busy = false, stop = false;
+    hipError_t err = hipSuccess;   // first failure of the copier
+    const char *err_what = "";
 };
 
 namespace {
 
-int enqueue_copy(rkv_ring *r, int64_t j)
+// Enqueue the copy of item j (index in the step) into its slot, on the copy
+// stream, after the compute that last read the slot has finished: the copier
+// waits for that on the host (the slot's compute_done holds its latest record,
+// since the compute stream records the slot again only once this copy is
+// enqueued).  A DMA-engine copy made to wait on a compute-queue event on the
+// GPU costs tens of microseconds per copy even when the event has long
+// completed; waited for here, the copy goes out with no GPU-side dependency.
+hipError_t enqueue_copy(rkv_ring *r, int64_t j, const char **what)
 {
     const rkv_ring::Item &it = r->items[j];
     const rkv_kv_view &t = r->tails[it.layer];
     const int s = (int)(j % r->B);
-    RKV_HIP(hipStreamWaitEvent(r->copy, r->compute_done[s], 0));
     const size_t kb = (size_t)(it.nk * t.k_pos_stride), vb = (size_t)(it.nk * t.v_pos_stride);
-    RKV_HIP(hipMemcpyAsync(r->sk[s], (const char *)t.k + it.k0 * t.k_pos_stride, kb, hipMemcpyHostToDevice, r->copy));
-    RKV_HIP(hipMemcpyAsync(r->sv[s], (const char *)t.v + it.k0 * t.v_pos_stride, vb, hipMemcpyHostToDevice, r->copy));
-    RKV_HIP(hipEventRecord(r->copy_done[s], r->copy));
+    hipError_t e;
+    *what = "hipEventSynchronize (slot release)";
+    if ((e = hipEventSynchronize(r->compute_done[s])) != hipSuccess) return e;
+    *what = "hipMemcpyAsync (tile K)";
+    if ((e = hipMemcpyAsync(r->sk[s], (const char *)t.k + it.k0 * t.k_pos_stride, kb, hipMemcpyHostToDevice,
+                            r->copy)) != hipSuccess)
+        return e;
+    *what = "hipMemcpyAsync (tile V)";
+    if ((e = hipMemcpyAsync(r->sv[s], (const char *)t.v + it.k0 * t.v_pos_stride, vb, hipMemcpyHostToDevice,
+                            r->copy)) != hipSuccess)
+        return e;
+    *what = "hipEventRecord (copy_done)";
+    return hipEventRecord(r->copy_done[s], r->copy);
+}
+
+void copier_main(rkv_ring *r)
+{
+    (void)hipSetDevice(r->device);
+    std::unique_lock<std::mutex> lk(r->mu);
+    for (;;) {
+        r->cv_req.wait(lk, [r] { return r->stop || !r->req.empty(); });
+        if (r->stop) return;
+        const int64_t j = r->req.front();
+        r->req.pop_front();
+        r->busy = true;
+        lk.unlock();
+        const char *what = "";
+        hipError_t e = r->err == hipSuccess ? enqueue_copy(r, j, &what) : hipSuccess;
+        lk.lock();
+        if (e != hipSuccess && r->err == hipSuccess) {
+            r->err = e;
+            r->err_what = what;
+        }
+        r->enq[j % r->B] = r->base + j;  // also on failure: the waiter then sees the error
+        r->busy = false;
+        r->cv_done.notify_all();
+    }
+}
+
+// Hand item j (index in the step) to the copier.
+void request_copy(rkv_ring *r, int64_t j)
+{
+    {
+        std::lock_guard<std::mutex> lk(r->mu);
+        r->req.push_back(j);
+    }
+    r->cv_req.notify_one();
+}
+
+// Wait (on the host) until the copy of item j and its copy_done record are
+// enqueued.  Returns the copier's failure, if any.
+int wait_enqueued(rkv_ring *r, int64_t j)
+{
+    std::unique_lock<std::mutex> lk(r->mu);
+    r->cv_done.wait(lk, [r, j] { return r->err != hipSuccess || r->enq[j % r->B] == r->base + j; });
+    if (r->err != hipSuccess) return hip_fail(r->err, r->err_what);
     return RKV_OK;
+}
+
+void copier_stop(rkv_ring *r)
+{
+    if (!r->copier.joinable()) return;
+    {
+        std::lock_guard<std::mutex> lk(r->mu);
+        r->stop = true;
+    }
+    r->cv_req.notify_all();
+    r->copier.join();
 }
 
 void ring_free(rkv_ring *r)
 {
+    copier_stop(r);
     for (int i = 0; i < 16; ++i) {
         if (r->sk[i]) (void)hipFree(r->sk[i]);
         if (r->sv[i]) (void)hipFree(r->sv[i]);
@@ -555,6 +642,13 @@ int rkv_ring_create(int n_slots, size_t slot_k_bytes, size_t slot_v_bytes, hipSt
         }
         r->own_copy = true;
     }
+    for (int i = 0; i < 16; ++i) r->enq[i] = -1;
+    try {
+        r->copier = std::thread(copier_main, r);
+    } catch (...) {
+        ring_free(r);
+        return fail(RKV_E_NOMEM, "could not start the copier thread");
+    }
     *out = r;
     return RKV_OK;
 }
@@ -562,6 +656,7 @@ int rkv_ring_create(int n_slots, size_t slot_k_bytes, size_t slot_v_bytes, hipSt
 int rkv_ring_destroy(rkv_ring *r)
 {
     if (!r) return RKV_OK;
+    copier_stop(r);
     hipError_t e = hipStreamSynchronize(r->copy);
     for (int i = 0; i < r->B && e == hipSuccess; ++i) e = hipEventSynchronize(r->compute_done[i]);
     ring_free(r);
@@ -595,20 +690,23 @@ int rkv_ring_begin_step(rkv_ring *r, int n_layers, const rkv_kv_view *tails, int
             return fail(RKV_E_UNSUPPORTED, "tail %d: more than %d tiles", l, kMaxParts - 1);
     }
     first[n_layers] = (int64_t)items.size();
-    r->tails.assign(tails, tails + n_layers);
-    r->items.swap(items);
-    r->first_item.swap(first);
+    {
+        // the copier is idle between steps (every item of a finished step had
+        // its copy enqueued before it was consumed; an aborted step's requests
+        // drain here)
+        std::unique_lock<std::mutex> lk(r->mu);
+        r->cv_done.wait(lk, [r] { return r->req.empty() && !r->busy; });
+        if (r->err != hipSuccess) return hip_fail(r->err, r->err_what);
+        r->base += (int64_t)r->items.size();
+        r->tails.assign(tails, tails + n_layers);
+        r->items.swap(items);
+        r->first_item.swap(first);
+    }
     r->tile_keys = tile_keys;
     r->next_layer = 0;
     r->in_step = true;
     const int64_t n = std::min<int64_t>(r->B, (int64_t)r->items.size());
-    for (int64_t j = 0; j < n; ++j) {
-        int rc = enqueue_copy(r, j);
-        if (rc) {
-            r->in_step = false;
-            return rc;
-        }
-    }
+    for (int64_t j = 0; j < n; ++j) request_copy(r, j);
     return RKV_OK;
 }
 
@@ -677,15 +775,28 @@ int rkv_stream_tail(rkv_ring *r, int layer, const rkv_attn_desc *desc, const flo
         v.n_keys = r->items[j].nk;
         v.k_seq_stride = 0;
         v.v_seq_stride = 0;
-        if ((rc = check_view_fields(desc, &v))) return rc;
-        RKV_HIP(hipStreamWaitEvent(cs, r->copy_done[s], 0));
+        // A failure from here on aborts the step (later calls: RKV_E_STATE),
+        // so that nothing waits for a copy that will not be requested.
+        if ((rc = check_view_fields(desc, &v)) || (rc = wait_enqueued(r, j))) {
+            r->in_step = false;
+            return rc;
+        }
+        hipError_t e = hipStreamWaitEvent(cs, r->copy_done[s], 0);
+        if (e != hipSuccess) {
+            r->in_step = false;
+            return hip_fail(e, "hipStreamWaitEvent (copy_done)");
+        }
         const rkv_kv_view *vp = &v;
         if ((rc = attend_impl(desc, q, 1, &vp, tile_o + (j - j0) * n_rows * D, tile_lse + (j - j0) * n_rows, attend_ws,
-                              attend_bytes, cs)))
+                              attend_bytes, cs))) {
+            r->in_step = false;
             return rc;
-        RKV_HIP(hipEventRecord(r->compute_done[s], cs));
-        if (j + r->B < (int64_t)r->items.size())
-            if ((rc = enqueue_copy(r, j + r->B))) return rc;
+        }
+        if ((e = hipEventRecord(r->compute_done[s], cs)) != hipSuccess) {
+            r->in_step = false;
+            return hip_fail(e, "hipEventRecord (compute_done)");
+        }
+        if (j + r->B < (int64_t)r->items.size()) request_copy(r, j + r->B);
     }
     CombineParts parts;
     memset(&parts, 0, sizeof parts);
