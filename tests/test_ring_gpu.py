@@ -146,3 +146,36 @@ def test_ring_state_errors():
         torch.cuda.synchronize()
     finally:
         ring.close()
+
+
+def test_ring_consecutive_steps():
+    """One ring over three steps with different tails (a decode loop): the
+    slots a step starts with are released by the previous step's last tiles,
+    and every step still equals its tiles attended resident, bit for bit."""
+    n, Hq, Hkv, D, tile, B = 3000, 16, 4, 128, 512, 3
+    note(f"ring consecutive steps: n={n}, tile={tile}, B={B}, q8_0 K / q4_0 V")
+    layers = make_layers(2, n, [1000, 1000], Hq, Hkv, D, synth.Q8_0, synth.Q4_0, 8300)
+    desc = P.Desc(1, Hq, Hkv, D, 1.0 / math.sqrt(D))
+    kc0, vc0 = layers[0]["kc"], layers[0]["vc"]
+    ring = P.Ring(B, tile * kc0.pos_stride, tile * vc0.pos_stride)
+    stream = torch.cuda.current_stream()
+    try:
+        for step, tail_keys in enumerate([2000, 700, 1300]):
+            note(f"  step {step}: tail {tail_keys} keys per layer")
+            tails = [P.view_of_cache(L_["kh"], L_["vh"], 0, tail_keys) for L_ in layers]
+            ring.rkv_ring_begin_step(tails, tile)
+            outs = []
+            for li, L_ in enumerate(layers):
+                o_w, l_w = P.attend(desc, L_["q"], P.view_of_cache(L_["kc"], L_["vc"], 0, L_["wc"]), stream)
+                ws = P.workspace(ring.rkv_stream_tail_workspace_bytes(li, desc))
+                o = torch.empty_like(L_["q"])
+                lse = torch.empty(L_["q"].shape[:2], dtype=torch.float32, device=DEV)
+                ring.rkv_stream_tail(li, desc, L_["q"], o_w, l_w, o, lse, ws, stream)
+                outs.append((o, lse))
+            ring.rkv_ring_end_step()
+            for li, L_ in enumerate(layers):
+                o_r, l_r = resident(L_, desc, tile, L_["wc"] + tail_keys)
+                torch.cuda.synchronize()
+                assert torch.equal(outs[li][0], o_r) and torch.equal(outs[li][1], l_r), f"step {step} layer {li}"
+    finally:
+        ring.close()
