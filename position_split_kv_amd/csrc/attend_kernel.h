@@ -267,12 +267,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 // inserts its own (conservative or missing) waits for it nor reorders memory
 // accesses across it; callers wait with waitcnt_vm() before reading the data
 // and wait for their LDS reads (lgkmcnt) before overwriting a buffer.  M0 is
-// saved and restored around the load.
+// saved and restored around the load.  Each 16-byte chunk is read exactly once
+// and every load takes whole cache lines, so it carries the non-temporal cache
+// policy (nt): on the 48-layer f16 step 2.5 % less time than the default
+// policy.  (The 4-byte loads below touch each line from several loads and
+// keep the default: with nt they were up to 15 % slower.)
 __device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved)
                  : "v"(g), "s"(lds)
                  : "memory");
