@@ -63,11 +63,7 @@ struct Shape {
     static constexpr int RBV = row_bytes_of(VT, D);
     // f32 / f16 K rows of 128..512 bytes go global -> LDS directly (no staging
     // registers), packed at RBK bytes with their 16-byte chunks swizzled.
-#ifdef RKV_NO_KDMA
-    static constexpr bool KDMA = false;
-#else
     static constexpr bool KDMA = (KT == kF32 || KT == kF16) && RBK >= 128 && RBK <= 512 && is_pow2(RBK / 16);
-#endif
     static constexpr int LSK = KDMA ? RBK / 4 : lds_row_dwords(RBK);
     static constexpr bool V_REG = (VT == kF16 && D <= 128) || (VT == kF32 && D <= 64);
     static constexpr int LSV = V_REG ? 0 : lds_row_dwords(RBV);
@@ -1026,17 +1022,14 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     using KRegs = RowRegs<Sh::RBK, VWK>;
     using VRegs = RowRegs<Sh::RBV, VWV>;
     constexpr int RAW_DW = KRegs::IT * KRegs::NWD + (V_REG ? NSTEP * VRW : VRegs::IT * VRegs::NWD);
-#ifdef RKV_NO_PIPE
-    constexpr bool PIPE = false;
-#else
     constexpr bool PIPE = !Sh::KDMA && RAW_DW <= 64 && !MFMA_S;  // MFMA operands need those registers
     // Block-type K and V with the matrix-core scores: both tiles go global ->
-    // LDS by dword DMA (no staging registers), issued together after the
-    // previous tile's P.V; the wait for K leaves V's loads in flight.
+    // LDS by dword DMA (no staging registers); a tile's K rows go out once
+    // the previous tile's scores are done, its V rows after the previous P.V,
+    // and the wait for K leaves V's loads in flight.
     constexpr bool BDMA = MFMA_S && (KT == kQ8 || KT == kQ4) && (VT == kQ8 || VT == kQ4) && Sh::RBK % 4 == 0 &&
                           Sh::RBV % 4 == 0 && LSK <= 64 && LSV <= 64;
     constexpr int NVD = LSV < 63 ? LSV : 63;  // V loads a wait for K may leave outstanding
-#endif
     KRegs kr;
     VRegs vr;
     uint32_t vreg[V_REG ? NSTEP : 1][VRW];
