@@ -202,6 +202,27 @@ def test_shared_prefix_batch():
     compare(o, l, o_ref, l_ref, what="prefix+suffix")
 
 
+@pytest.mark.parametrize("D", [256, 512])
+def test_shared_prefix_dim_slices(D):
+    """A shared q8_0 / q4_0 prefix at head_dim 256 / 512 (dim slices, several
+    sequences reading one copy of the keys) plus per-sequence f16 suffixes,
+    merged by the LSE combine."""
+    S, Hq, Hkv, npre, nsuf = 3, 8, 2, 300, 100
+    note(f"shared prefix with dim slices: D={D} S={S} prefix={npre} suffix={nsuf}")
+    pk, pv = pair(npre, Hkv, D, synth.Q8_0, synth.Q4_0, 121 + D, DEV)
+    sk, sv = pair(S * nsuf, Hkv, D, synth.F16, synth.F16, 122 + D, DEV)
+    q = synth.make_query(S, Hq, D, 123 + D, DEV)
+    desc = P.Desc(S, Hq, Hkv, D, default_scale(D))
+    prefix = P.view_of_cache(pk, pv)
+    suffix = P.view_of_cache(sk, sv, 0, nsuf, nsuf * sk.pos_stride, nsuf * sv.pos_stride)
+    o, l = attend_views(desc, q, [prefix, suffix])
+    torch.cuda.synchronize()
+    pkh, pvh, skh, svh = pk.to("cpu"), pv.to("cpu"), sk.to("cpu"), sv.to("cpu")
+    views = [oracle.view_of(pkh, pvh), oracle.view_of(skh, svh, 0, nsuf, nsuf * sk.pos_stride, nsuf * sv.pos_stride)]
+    o_ref, l_ref = oracle.attend(q.cpu().numpy(), views, Hkv, default_scale(D))
+    compare(o, l, o_ref, l_ref, what=f"prefix+suffix D={D}")
+
+
 def test_errors_on_device():
     D, Hq, Hkv, n = 128, 8, 2, 20000  # long enough to need a workspace
     kc, vc = pair(n, Hkv, D, synth.F16, synth.F16, 5, DEV)

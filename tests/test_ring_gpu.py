@@ -94,6 +94,24 @@ def test_stream_tail_bit_identical_to_resident(B):
     compare(outs[1][0], outs[1][1], o_ref, l_ref, what=f"ring B={B} vs oracle")
 
 
+def test_stream_tail_dim_slices():
+    """Tails of q8_0 K and V at head_dim 256 (each tile attended by the dim-sliced
+    kernel) through a 2-slot ring: bit for bit the resident tiles, and the oracle."""
+    L, n, Hq, Hkv, D, tile = 2, 900, 8, 2, 256, 256
+    note(f"ring dim slices: {L} layers, n={n}, wc=400, tile={tile}, D={D}, q8_0 K / q8_0 V")
+    layers = make_layers(L, n, [400] * L, Hq, Hkv, D, synth.Q8_0, synth.Q8_0, 8400)
+    desc = P.Desc(1, Hq, Hkv, D, 1.0 / math.sqrt(D))
+    outs = run_streamed(layers, desc, 2, tile, n)
+    for li, L_ in enumerate(layers):
+        o_r, l_r = resident(L_, desc, tile, n)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[li][0], o_r) and torch.equal(outs[li][1], l_r), f"layer {li}"
+    L_ = layers[0]
+    o_ref, l_ref = oracle.attend(L_["q"].cpu().numpy(), [oracle.view_of(L_["kc"].to("cpu"), L_["vc"].to("cpu"))],
+                                 Hkv, 1.0 / math.sqrt(D))
+    compare(outs[0][0], outs[0][1], o_ref, l_ref, what="ring D256 vs oracle")
+
+
 def test_stream_tail_edge_layers():
     """A layer with no window (wc = 0), a layer with an empty tail (the window
     result comes back bit for bit), and a tail shorter than one tile."""
