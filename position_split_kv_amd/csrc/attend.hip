@@ -106,65 +106,77 @@ hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q
 // Merge of the per-split partials of one row (partials are in log2 units):
 // M = max_i m_i, L = sum_i l_i 2^(m_i - M), o = sum_i acc_i 2^(m_i - M) / L,
 // lse = (M + log2 L) ln 2.  Block (row, 32-dim slice) of 256 threads: 32
-// groups of 8 lanes, lane c holding 4 dims.  Group j folds splits j, j+32,
-// j+64, ... in that order with the running-max rule (so no separate pass for
-// the maximum), then group 0 folds the 32 group results in order: the result
-// does not depend on timing.
+// groups of 8 lanes, lane c holding 4 dims; group j takes splits j, j+32,
+// j+64, ...  The row's maximum M is found first (thread t reads the (m, l) of
+// splits t, t+256, ..., a block reduction), so every weight 2^(m_i - M) is
+// independent of the others (no running rescale); the weighted sums are added
+// per group in split order and then over the groups in group order: the
+// result does not depend on timing.  The loads of the weighted pass are
+// issued before the maximum is known.
+__device__ __forceinline__ float block_max256(float v, float *sw)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    const int t = threadIdx.x;
+    if ((t & 63) == 0) sw[t >> 6] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(sw[0], sw[1]), fmaxf(sw[2], sw[3]));
+}
+
 __global__ void __launch_bounds__(256)
 rkv_reduce_kernel(const float *__restrict__ part_acc, const float2 *__restrict__ part_ml, int n_splits,
                   int64_t n_rows, int D, float *__restrict__ o, float *__restrict__ lse)
 {
-    __shared__ float sM[32], sL[32];
+    __shared__ float sW[4], sL[32];
     __shared__ float4 sA[32][8];
     const int64_t row = blockIdx.x;
     const int t = threadIdx.x, grp = t >> 3, c = t & 7;
     const int d0 = blockIdx.y * 32 + 4 * c;
-    float m = -INFINITY, l = 0.f;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    // batches of 8 splits per group, all loads of a batch issued together
-    // (indices past the end repeat a valid split and are not folded in)
-    for (int base = grp; base < n_splits; base += 32 * 8) {
-        float2 ml[8];
-        float4 x[8];
+    const float2 *ml_row = part_ml + row * n_splits;  // (m, l) are row-major: a row's splits are contiguous
+    auto load = [&](int base, float2 (&ml)[8], float4 (&x)[8]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
+            // (indices past the end repeat a valid split and are not added)
             const int sp = base + 32 * u < n_splits ? base + 32 * u : base;
-            const int64_t idx = (int64_t)sp * n_rows + row;
-            ml[u] = part_ml[idx];
-            x[u] = *(const float4 *)(part_acc + idx * D + d0);
+            ml[u] = ml_row[sp];
+            x[u] = *(const float4 *)(part_acc + ((int64_t)sp * n_rows + row) * D + d0);
         }
+    };
+    float2 ml[8];
+    float4 x[8];
+    if (grp < n_splits) load(grp, ml, x);
+    float mloc = -INFINITY;
+    for (int sp = t; sp < n_splits; sp += 256) mloc = fmaxf(mloc, ml_row[sp].x);
+    const float M = block_max256(mloc, sW);
+    float l = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int base = grp; base < n_splits; base += 32 * 8) {
+        if (base != grp) load(base, ml, x);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            if (base + 32 * u >= n_splits) break;
-            const float mn = fmaxf(m, ml[u].x);
-            const float fa = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-            const float fb = ml[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - mn);
-            l = l * fa + ml[u].y * fb;
-            a.x = a.x * fa + x[u].x * fb;
-            a.y = a.y * fa + x[u].y * fb;
-            a.z = a.z * fa + x[u].z * fb;
-            a.w = a.w * fa + x[u].w * fb;
-            m = mn;
+            if (base + 32 * u < n_splits) {
+                const float w = ml[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - M);
+                l = fmaf(ml[u].y, w, l);
+                a.x = fmaf(x[u].x, w, a.x);
+                a.y = fmaf(x[u].y, w, a.y);
+                a.z = fmaf(x[u].z, w, a.z);
+                a.w = fmaf(x[u].w, w, a.w);
+            }
         }
     }
-    if (c == 0) {
-        sM[grp] = m;
-        sL[grp] = l;
-    }
+    if (c == 0) sL[grp] = l;
     sA[grp][c] = a;
     __syncthreads();
     if (grp == 0) {
-        float M = -INFINITY;
-        for (int j = 0; j < 32; ++j) M = fmaxf(M, sM[j]);
         float L = 0.f;
         float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
         for (int j = 0; j < 32; ++j) {
-            const float f = sM[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sM[j] - M);
-            L = fmaf(sL[j], f, L);
-            s.x = fmaf(sA[j][c].x, f, s.x);
-            s.y = fmaf(sA[j][c].y, f, s.y);
-            s.z = fmaf(sA[j][c].z, f, s.z);
-            s.w = fmaf(sA[j][c].w, f, s.w);
+            L += sL[j];
+            s.x += sA[j][c].x;
+            s.y += sA[j][c].y;
+            s.z += sA[j][c].z;
+            s.w += sA[j][c].w;
         }
         *(float4 *)(o + row * D + d0) = make_float4(s.x / L, s.y / L, s.z / L, s.w / L);
         if (blockIdx.y == 0 && c == 0) lse[row] = (M + log2f(L)) * 0.69314718055994531f;

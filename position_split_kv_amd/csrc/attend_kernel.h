@@ -1545,7 +1545,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 }
                 if (rr >= 0) {
                     if (single) lse_out[rr] = (mr + log2f(lr)) * 0.69314718055994531f;
-                    else part_ml[pbase + rr] = make_float2(mr, lr);
+                    else part_ml[(int64_t)rr * p.n_splits + blockIdx.x] = make_float2(mr, lr);
                 }
             }
             return;
@@ -1621,7 +1621,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             if (d == 0) lse_out[rr] = (M + log2f(L)) * 0.69314718055994531f;
         } else {
             part_acc[(pbase + rr) * D + d] = A;
-            if (d == 0) part_ml[pbase + rr] = make_float2(M, L);
+            if (d == 0) part_ml[(int64_t)rr * p.n_splits + blockIdx.x] = make_float2(M, L);
         }
     }
 }
