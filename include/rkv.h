@@ -13,7 +13,8 @@
  * SHIPPED: position-axis mixed KV": window and tail each read in-register at
  * its own type, no whole-cache f16 materialise).  A tail held in
  * pinned host memory is streamed through a B-slot device ring on a copy
- * stream with per-slot copy_done / compute_done events ("Architecture",
+ * stream; a slot's refill waits for the compute that read it, a tile's
+ * compute waits for its slot's copy ("Architecture",
  * "CUDA stream graph"; and the page "Rolling-KV: step/graph-level tail
  * prefetch (design)", section "The fix: a persistent, step-spanning
  * tail-prefetch ring").
@@ -191,14 +192,17 @@ int rkv_dequant_q4_0(const void *blocks, int64_t n_values, float *out, hipStream
 /* ---- streamed tail --------------------------------------------------------
  * A ring of n_slots device staging slots, each holding one tile of K and one
  * of V, filled from pinned host memory by asynchronous copies on a copy
- * stream.  The copy into a slot waits for the slot's compute_done event; the
- * attention of a tile waits for its slot's copy_done event ("F5 M7 -- Rolling
- * KV", "CUDA stream graph").  The first of these waits is taken on the host:
- * a copier thread owned by the ring waits for a slot's compute_done and then
- * enqueues the slot's copies (DMA-engine hipMemcpyAsync) and copy_done record,
- * so the copy stream carries no wait on a compute-queue event (such a wait
- * costs a DMA-engine copy tens of microseconds even when the event has long
- * completed).  The order of copies is one flat sequence over
+ * stream.  The copy into a slot waits until the attention of the slot's
+ * previous tile has read it; the attention of a tile waits for its slot's
+ * copy_done event ("F5 M7 -- Rolling KV", "CUDA stream graph").  The first of
+ * these waits is taken on the host: the kernel after a tile's split kernel
+ * (the partial merge, or a one-thread signal kernel) writes the tile's
+ * sequence number to a per-slot word in pinned host memory, and a copier
+ * thread owned by the ring watches that word and then enqueues the slot's
+ * copies (DMA-engine hipMemcpyAsync) and copy_done record.  So the copy
+ * stream carries no wait on a compute-queue event (such a wait costs a
+ * DMA-engine copy tens of microseconds even when the event has long
+ * completed) and the compute stream records no event per tile.  The order of copies is one flat sequence over
  * (layer, tile) for a whole decode step, kept n_slots ahead of compute
  * across layer boundaries ("Rolling-KV: step/graph-level tail prefetch
  * (design)", "The fix: a persistent, step-spanning tail-prefetch ring"), so a
@@ -209,13 +213,17 @@ typedef struct rkv_ring rkv_ring;
 /* Create a ring.  n_slots >= 2 (<= 16).  slot_k_bytes / slot_v_bytes: bytes
  * of one tile of K / V (tile_keys * pos_stride of the tail views).
  * copy_stream: NULL makes the ring create and own a non-blocking stream.
- * The ring owns its slots, its events (created here, timing disabled), a
- * stream it created and its copier thread (started here, on the current
- * device).  Errors: RKV_E_INVAL, RKV_E_NOMEM, RKV_E_HIP. */
+ * The ring owns its slots, its copy_done events (created here, timing
+ * disabled), its progress words (128 bytes of pinned host memory), a stream
+ * it created and its copier thread (started here, on the current device).
+ * Errors: RKV_E_INVAL, RKV_E_NOMEM, RKV_E_HIP. */
 int rkv_ring_create(int n_slots, size_t slot_k_bytes, size_t slot_v_bytes, hipStream_t copy_stream,
                     rkv_ring **out);
 /* Stop the copier (copies it has not enqueued yet are dropped), wait for the
- * ring's enqueued work to finish, then free it.  NULL is a no-op. */
+ * ring's enqueued copies and for the attention of every tile already handed
+ * to rkv_stream_tail to finish reading its slot, then free it.  A GPU that
+ * does not finish within 60 s gives RKV_E_HIP (the ring is freed anyway).
+ * NULL is a no-op. */
 int rkv_ring_destroy(rkv_ring *ring);
 
 /* Plan one step: the tails of n_layers layers (host_tails[l], each in pinned
@@ -237,9 +245,13 @@ int rkv_stream_tail_workspace_bytes(const rkv_ring *ring, int layer, const rkv_a
  *
  * For each tile: the call waits on the host until the copier has enqueued
  * the tile's copy (at most until the GPU has finished the compute n_slots
- * items earlier); the compute stream waits copy_done of its slot, attends the
- * slot, records compute_done; then the refill of that slot with the item
- * n_slots further on in the flat order is handed to the copier.
+ * items earlier); the compute stream waits copy_done of its slot and attends
+ * the slot, and the kernel after the split kernel signals the slot free;
+ * then the refill of that slot with the item n_slots further on in the flat
+ * order is handed to the copier.  Tiles may run on different compute
+ * streams.  A slot whose previous reader has not finished within 60 s of the
+ * copier starting to wait fails the ring's copier (RKV_E_HIP at the next
+ * call).
  * Finally (o_window, lse_window) and the tiles' results are merged with
  * rkv_lse_combine in the order window, tile 0, tile 1, ...  lse_window may be
  * NULL (no window; o_window is then ignored).  The result equals, bit for

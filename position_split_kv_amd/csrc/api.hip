@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <condition_variable>
 #include <deque>
 #include <mutex>
@@ -234,14 +235,17 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
 
 // Enqueue one launch over segments of one (K, V) type pair (arguments already
 // validated).  All segments empty: o = 0, lse = -inf.
+// done (optional): host-visible memory that receives done_value once the
+// launch has finished reading its keys.
 int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view *const *v, float *o, float *lse,
-                void *ws, size_t ws_bytes, hipStream_t stream)
+                void *ws, size_t ws_bytes, hipStream_t stream, uint64_t *done = nullptr, uint64_t done_value = 0)
 {
     const int64_t n_rows = (int64_t)d->n_seq * d->n_q_heads;
     int64_t keys = 0;
     for (int i = 0; i < n; ++i) keys += v[i]->n_keys;
     if (keys == 0) {
         RKV_HIP(launch_fill_empty(d->head_dim, n_rows, o, lse, stream));
+        if (done) RKV_HIP(launch_signal(done, done_value, stream));
         return RKV_OK;
     }
     SplitPlan pl;
@@ -257,7 +261,10 @@ int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view
     float2 *part_ml = (float2 *)((char *)ws + pl.acc_bytes);
     const dim3 grid((unsigned)pl.n_splits, (unsigned)(pl.n_hg * pl.n_rg), (unsigned)pl.z);
     RKV_HIP(launch_split(kt, vt, d->head_dim, pl.rt, grid, q, part_acc, part_ml, o, lse, prm, stream));
-    if (pl.n_splits > 1) RKV_HIP(launch_reduce(d->head_dim, n_rows, pl.n_splits, part_acc, part_ml, o, lse, stream));
+    if (pl.n_splits > 1)
+        RKV_HIP(launch_reduce(d->head_dim, n_rows, pl.n_splits, part_acc, part_ml, o, lse, stream, done, done_value));
+    else if (done)
+        RKV_HIP(launch_signal(done, done_value, stream));
     return RKV_OK;
 }
 
@@ -464,7 +471,16 @@ struct rkv_ring {
     void *sk[16] = {}, *sv[16] = {};
     hipStream_t copy = nullptr;
     bool own_copy = false;
-    hipEvent_t copy_done[16] = {}, compute_done[16] = {};
+    hipEvent_t copy_done[16] = {};
+    // Slot release: the merge kernel after a tile's attention (it starts only
+    // once the split kernel has read the slot) writes the tile's sequence
+    // number + 1 to progress[slot], pinned and coherent host memory.  A slot's
+    // tiles run one after another (each waits for its copy, which waits for
+    // the previous tile of the slot), so each word only grows, whatever
+    // streams the tiles run on.  last_user[s]: sequence number of the tile that
+    // last read slot s (-1: none); written by the caller's thread under mu.
+    uint64_t *progress = nullptr;
+    int64_t last_user[16];
     // plan of the current step
     bool in_step = false;
     std::vector<rkv_kv_view> tails;
@@ -483,7 +499,7 @@ struct rkv_ring {
     std::thread copier;
     std::mutex mu;
     std::condition_variable cv_req, cv_done;
-    std::deque<int64_t> req;       // items (indices in the step) whose copy is to be enqueued
+    std::deque<std::pair<int64_t, int64_t>> req;  // (item index in the step, sequence number the slot must reach)
     int64_t enq[16];               // sequence number of the item whose copy slot s holds or receives
     bool busy = false, stop = false;
     hipError_t err = hipSuccess;   // first failure of the copier
@@ -493,21 +509,36 @@ struct rkv_ring {
 namespace {
 
 // Enqueue the copy of item j (index in the step) into its slot, on the copy
-// stream, after the compute that last read the slot has finished: the copier
-// waits for that on the host (the slot's compute_done holds its latest record,
-// since the compute stream records the slot again only once this copy is
-// enqueued).  A DMA-engine copy made to wait on a compute-queue event on the
-// GPU costs tens of microseconds per copy even when the event has long
-// completed; waited for here, the copy goes out with no GPU-side dependency.
-hipError_t enqueue_copy(rkv_ring *r, int64_t j, const char **what)
+// stream, once the compute that last read the slot has finished: the copier
+// waits for that on the host, watching the ring's progress word (the merge
+// kernel after that tile's attention writes it).  A DMA-engine copy made to
+// wait on a compute-queue event on the GPU costs tens of microseconds per copy
+// even when the event has long completed, and an event record on the compute
+// queue costs it a few microseconds per tile; this way the copy goes out with
+// no GPU-side dependency and the compute queue records nothing.
+hipError_t enqueue_copy(rkv_ring *r, int64_t j, int64_t need, const char **what)
 {
     const rkv_ring::Item &it = r->items[j];
     const rkv_kv_view &t = r->tails[it.layer];
     const int s = (int)(j % r->B);
     const size_t kb = (size_t)(it.nk * t.k_pos_stride), vb = (size_t)(it.nk * t.v_pos_stride);
     hipError_t e;
-    *what = "hipEventSynchronize (slot release)";
-    if ((e = hipEventSynchronize(r->compute_done[s])) != hipSuccess) return e;
+    const uint64_t *done = r->progress + s;
+    if (need > 0 && __atomic_load_n(done, __ATOMIC_ACQUIRE) < (uint64_t)need) {
+        const auto t0 = std::chrono::steady_clock::now();
+        unsigned spins = 0;
+        while (__atomic_load_n(done, __ATOMIC_ACQUIRE) < (uint64_t)need) {
+            // spin briefly (a tile takes tens of microseconds), then yield
+            if (++spins < 4096)
+                __builtin_ia32_pause();
+            else
+                std::this_thread::yield();
+            if (spins % 1024 == 0 && std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60)) {
+                *what = "slot release: the compute that last read the slot did not finish within 60 s";
+                return hipErrorLaunchTimeOut;
+            }
+        }
+    }
     *what = "hipMemcpyAsync (tile K)";
     if ((e = hipMemcpyAsync(r->sk[s], (const char *)t.k + it.k0 * t.k_pos_stride, kb, hipMemcpyHostToDevice,
                             r->copy)) != hipSuccess)
@@ -527,12 +558,12 @@ void copier_main(rkv_ring *r)
     for (;;) {
         r->cv_req.wait(lk, [r] { return r->stop || !r->req.empty(); });
         if (r->stop) return;
-        const int64_t j = r->req.front();
+        const int64_t j = r->req.front().first, need = r->req.front().second;
         r->req.pop_front();
         r->busy = true;
         lk.unlock();
         const char *what = "";
-        hipError_t e = r->err == hipSuccess ? enqueue_copy(r, j, &what) : hipSuccess;
+        hipError_t e = r->err == hipSuccess ? enqueue_copy(r, j, need, &what) : hipSuccess;
         lk.lock();
         if (e != hipSuccess && r->err == hipSuccess) {
             r->err = e;
@@ -544,12 +575,13 @@ void copier_main(rkv_ring *r)
     }
 }
 
-// Hand item j (index in the step) to the copier.
+// Hand item j (index in the step) to the copier; its copy waits until the
+// tile that last read its slot has finished (progress > that tile's number).
 void request_copy(rkv_ring *r, int64_t j)
 {
     {
         std::lock_guard<std::mutex> lk(r->mu);
-        r->req.push_back(j);
+        r->req.emplace_back(j, r->last_user[j % r->B] + 1);
     }
     r->cv_req.notify_one();
 }
@@ -582,8 +614,8 @@ void ring_free(rkv_ring *r)
         if (r->sk[i]) (void)hipFree(r->sk[i]);
         if (r->sv[i]) (void)hipFree(r->sv[i]);
         if (r->copy_done[i]) (void)hipEventDestroy(r->copy_done[i]);
-        if (r->compute_done[i]) (void)hipEventDestroy(r->compute_done[i]);
     }
+    if (r->progress) (void)hipHostFree(r->progress);
     if (r->own_copy && r->copy) (void)hipStreamDestroy(r->copy);
     delete r;
 }
@@ -620,17 +652,19 @@ int rkv_ring_create(int n_slots, size_t slot_k_bytes, size_t slot_v_bytes, hipSt
             ring_free(r);
             return fail(RKV_E_NOMEM, "slot allocation failed");
         }
-        // compute_done only orders a slot's refill after the kernels that read
-        // it: those kernels write nothing the copy reads, so its record needs
-        // no system-scope cache writeback (which would also stall the compute
-        // queue and cool the caches of the kernels after it).  copy_done keeps
-        // the default fence: the compute side must see the copied bytes.
-        if ((e = hipEventCreateWithFlags(&r->copy_done[i], hipEventDisableTiming)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&r->compute_done[i], hipEventDisableTiming | hipEventDisableSystemFence)) !=
-                hipSuccess) {
+        if ((e = hipEventCreateWithFlags(&r->copy_done[i], hipEventDisableTiming)) != hipSuccess) {
             ring_free(r);
             return hip_fail(e, "hipEventCreateWithFlags");
         }
+    }
+    if ((e = hipHostMalloc((void **)&r->progress, 16 * sizeof(uint64_t), hipHostMallocCoherent)) != hipSuccess) {
+        r->progress = nullptr;
+        ring_free(r);
+        return hip_fail(e, "hipHostMalloc (progress)");
+    }
+    for (int i = 0; i < 16; ++i) {
+        __atomic_store_n(r->progress + i, (uint64_t)0, __ATOMIC_RELEASE);
+        r->last_user[i] = -1;
     }
     if (copy_stream) {
         r->copy = copy_stream;
@@ -658,7 +692,16 @@ int rkv_ring_destroy(rkv_ring *r)
     if (!r) return RKV_OK;
     copier_stop(r);
     hipError_t e = hipStreamSynchronize(r->copy);
-    for (int i = 0; i < r->B && e == hipSuccess; ++i) e = hipEventSynchronize(r->compute_done[i]);
+    // the slots are freed only after the last tile of each has been read
+    const auto t0 = std::chrono::steady_clock::now();
+    for (int i = 0; i < r->B && e == hipSuccess; ++i)
+        while (__atomic_load_n(r->progress + i, __ATOMIC_ACQUIRE) < (uint64_t)(r->last_user[i] + 1)) {
+            std::this_thread::sleep_for(std::chrono::microseconds(50));
+            if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60)) {
+                e = hipErrorLaunchTimeOut;
+                break;
+            }
+        }
     ring_free(r);
     if (e != hipSuccess) return hip_fail(e, "ring destroy synchronisation");
     return RKV_OK;
@@ -787,14 +830,18 @@ int rkv_stream_tail(rkv_ring *r, int layer, const rkv_attn_desc *desc, const flo
             return hip_fail(e, "hipStreamWaitEvent (copy_done)");
         }
         const rkv_kv_view *vp = &v;
+        const int64_t g = r->base + j;
         if ((rc = attend_impl(desc, q, 1, &vp, tile_o + (j - j0) * n_rows * D, tile_lse + (j - j0) * n_rows, attend_ws,
-                              attend_bytes, cs))) {
+                              attend_bytes, cs, r->progress + s, (uint64_t)(g + 1)))) {
+            // a kernel of the tile may have been launched: let it finish
+            // before the slot can be refilled (its progress may never come)
+            (void)hipStreamSynchronize(cs);
             r->in_step = false;
             return rc;
         }
-        if ((e = hipEventRecord(r->compute_done[s], cs)) != hipSuccess) {
-            r->in_step = false;
-            return hip_fail(e, "hipEventRecord (compute_done)");
+        {
+            std::lock_guard<std::mutex> lk(r->mu);
+            r->last_user[s] = g;
         }
         if (j + r->B < (int64_t)r->items.size()) request_copy(r, j + r->B);
     }

@@ -112,7 +112,9 @@ hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q
 // independent of the others (no running rescale); the weighted sums are added
 // per group in split order and then over the groups in group order: the
 // result does not depend on timing.  The loads of the weighted pass are
-// issued before the maximum is known.
+// issued before the maximum is known.  If `done` is given, one thread writes
+// done_value there (host-visible memory, system scope) as the kernel starts:
+// the split kernel before it has then finished reading its key tiles.
 __device__ __forceinline__ float block_max256(float v, float *sw)
 {
 #pragma unroll
@@ -125,8 +127,11 @@ __device__ __forceinline__ float block_max256(float v, float *sw)
 
 __global__ void __launch_bounds__(256)
 rkv_reduce_kernel(const float *__restrict__ part_acc, const float2 *__restrict__ part_ml, int n_splits,
-                  int64_t n_rows, int D, float *__restrict__ o, float *__restrict__ lse)
+                  int64_t n_rows, int D, float *__restrict__ o, float *__restrict__ lse, uint64_t *done,
+                  uint64_t done_value)
 {
+    if (done && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+        __hip_atomic_store(done, done_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __shared__ float sW[4], sL[32];
     __shared__ float4 sA[32][8];
     const int64_t row = blockIdx.x;
@@ -184,11 +189,23 @@ rkv_reduce_kernel(const float *__restrict__ part_acc, const float2 *__restrict__
 }
 
 hipError_t launch_reduce(int d, int64_t n_rows, int n_splits, const float *pa, const float2 *pm, float *o,
-                         float *lse, hipStream_t s)
+                         float *lse, hipStream_t s, uint64_t *done, uint64_t done_value)
 {
     if (d % 32 || n_rows <= 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)n_rows, (unsigned)(d / 32)), block(256);
-    hipLaunchKernelGGL(rkv_reduce_kernel, grid, block, 0, s, pa, pm, n_splits, n_rows, d, o, lse);
+    hipLaunchKernelGGL(rkv_reduce_kernel, grid, block, 0, s, pa, pm, n_splits, n_rows, d, o, lse, done, done_value);
+    return hipGetLastError();
+}
+
+// The same signal on its own (when no merge follows the split kernel).
+__global__ void __launch_bounds__(64) rkv_signal_kernel(uint64_t *done, uint64_t done_value)
+{
+    if (threadIdx.x == 0) __hip_atomic_store(done, done_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+hipError_t launch_signal(uint64_t *done, uint64_t done_value, hipStream_t s)
+{
+    hipLaunchKernelGGL(rkv_signal_kernel, dim3(1), dim3(64), 0, s, done, done_value);
     return hipGetLastError();
 }
 

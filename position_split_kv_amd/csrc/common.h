@@ -86,8 +86,12 @@ struct SplitPlan {
 // launch_reduce merges them.
 hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q, float *part_acc,
                         float2 *part_ml, float *o, float *lse, const SplitParams &p, hipStream_t stream);
+// done (optional): host-visible memory that receives done_value once the split
+// kernel before the merge has finished (a progress signal for the tail ring).
 hipError_t launch_reduce(int d, int64_t n_rows, int n_splits, const float *part_acc, const float2 *part_ml,
-                         float *o, float *lse, hipStream_t stream);
+                         float *o, float *lse, hipStream_t stream, uint64_t *done = nullptr, uint64_t done_value = 0);
+// Write done_value to done (system scope) once the work before it on the stream has finished.
+hipError_t launch_signal(uint64_t *done, uint64_t done_value, hipStream_t stream);
 bool split_supported(int kt, int vt, int d, int rt);
 // Dim slices per KV head the split kernel uses for a (K type, V type,
 // head_dim): block-type K and V at head_dim 256 / 512 run as 2 / 4 slices of
