@@ -5,8 +5,9 @@ the CPU-baseline leg of ``bench.py`` may use this module; the product path
 (``position_split_kv_amd``) never imports it.
 
 The oracle is plain unsplit softmax attention over the whole key set in
-binary64 plus scalar block dequantisation; see the header of oracle.c for the
-passages it follows.
+binary64, scalar block dequantisation, and the write path (storing binary32
+rows in a cache type, routing a position to the window or the tail); see the
+header of oracle.c for the passages it follows.
 """
 from __future__ import annotations
 
@@ -66,6 +67,12 @@ class Oracle:
         L.orc_lse_combine.restype = ctypes.c_int
         L.orc_lse_combine.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                       ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        L.orc_f32_to_f16.restype = ctypes.c_uint16
+        L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        L.orc_encode_row.restype = ctypes.c_int
+        L.orc_encode_row.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        L.orc_route.restype = ctypes.c_int
+        L.orc_route.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
         L.orc_max_threads.restype = ctypes.c_int
         L.orc_set_threads.argtypes = [ctypes.c_int]
         self.L = L
@@ -126,6 +133,33 @@ class Oracle:
             raise ValueError("orc_lse_combine failed")
         return o, lse
 
+    def f32_to_f16(self, x: float) -> int:
+        """binary16 bits nearest (ties to even) to the binary32 value x."""
+        return self.L.orc_f32_to_f16(float(np.float32(x)))
+
+    def encode_rows(self, x, dtype: int) -> np.ndarray:
+        """Store binary32 rows x [..., D] in ``dtype``: uint8 [..., row_bytes]."""
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+        d = x.shape[-1]
+        rb = self.row_bytes(dtype, d)
+        if rb == 0:
+            raise ValueError("bad type or head_dim")
+        flat = x.reshape(-1, d)
+        out = np.zeros((flat.shape[0], rb), dtype=np.uint8)
+        for i in range(flat.shape[0]):
+            if self.L.orc_encode_row(dtype, flat[i].ctypes.data, d, out[i].ctypes.data) != 0:
+                raise ValueError("orc_encode_row failed")
+        return out.reshape(*x.shape[:-1], rb)
+
+    def route(self, pos: int, window_cap: int, tail_cap: int):
+        """("window" | "tail", row) for a new row at position pos; ValueError
+        when the position fits neither region."""
+        row = ctypes.c_int64(0)
+        r = self.L.orc_route(pos, window_cap, tail_cap, ctypes.byref(row))
+        if r < 0:
+            raise ValueError(f"position {pos} outside window {window_cap} + tail {tail_cap}")
+        return ("window", "tail")[r], row.value
+
     def max_threads(self) -> int:
         return self.L.orc_max_threads()
 
@@ -165,6 +199,18 @@ def attend(q, views, n_kv_heads, scale, softcap=0.0, q_to_kv=None, rows=None):
 
 def lse_combine(o_parts, lse_parts):
     return default().lse_combine(o_parts, lse_parts)
+
+
+def f32_to_f16(x):
+    return default().f32_to_f16(x)
+
+
+def encode_rows(x, dtype):
+    return default().encode_rows(x, dtype)
+
+
+def route(pos, window_cap, tail_cap):
+    return default().route(pos, window_cap, tail_cap)
 
 
 def max_threads() -> int:

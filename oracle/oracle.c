@@ -28,6 +28,23 @@
  *  - Logit softcap c*tanh(s/c) applied after the scale (reading: the pages
  *    list softcap among the score modifiers of the streaming path but do not
  *    order it; the softmax and the LSE are taken over the capped scores).
+ *  - The write path (orc_route, orc_encode_row).  Routing: "Rolling-KV:
+ *    step/graph-level tail prefetch (design)", section "Staged plan" (S0,
+ *    bug-1341: a layer's writes follow that layer's own window size; a layer
+ *    without a tail writes everything to its window) and "F5 M7 -- Rolling
+ *    KV", section "2026-07-14 -- bug-2172 SHIPPED" (each new row goes to the
+ *    window or to the tail by its destination position).  A row at position
+ *    p goes to window row p when p < wc, else to tail row p - wc.
+ *    Storing a binary32 row in the cache's type (quantise on append) is not
+ *    spelled out by the pages, which only name the block types; the reading
+ *    taken is the common rule for these formats, in binary32 arithmetic:
+ *    q8_0 d = amax / 127, q = round-half-away-from-zero(x * (1 / d)); q4_0
+ *    m = the first value of largest magnitude (+0 for a block of zeros),
+ *    d = m / -8, n = min(15, trunc(x * (1 / d) + 8.5)); 1/d is taken as 0
+ *    when d = 0; the scale is stored as the binary16 nearest to the binary32
+ *    d (ties to even), the codes come from the binary32 d.  The codes are
+ *    integers decided by binary32 arithmetic, so they are computed here in
+ *    binary32, as the kernel computes them, and compared bit for bit.
  */
 #include <math.h>
 #include <stdint.h>
@@ -130,6 +147,119 @@ int orc_dequant_q4_0(const void *blocks, int64_t n_values, float *out)
     for (i = 0; i < n_values; ++i)
         out[i] = (float)q4_0_value((const uint8_t *)blocks + 18 * (i / 32), (int)(i % 32));
     return 0;
+}
+
+/* binary32 -> IEEE 754 binary16, round to nearest, ties to even.  Written
+ * from the format's definition in binary64 (every binary32 value and every
+ * scaling by a power of two below is exact there): subnormal results are
+ * multiples of 2^-24; a normal result 2^e (1 + m / 1024) has 1024 + m the
+ * nearest integer to |x| 2^(10 - e); |x| >= 65520 (the midpoint between the
+ * largest finite value 65504 and 2^16) rounds to infinity. */
+uint16_t orc_f32_to_f16(float f)
+{
+    const double v = fabs((double)f);
+    const uint16_t sign = signbit(f) ? 0x8000 : 0;
+    double m;
+    int ex, e;
+    if (isnan(f)) return sign | 0x7e00;
+    if (v >= 65520.0) return sign | 0x7c00;
+    if (v < ldexp(1.0, -14)) /* rint gives 1024 for values that round up to 2^-14: the encoding 0x0400 */
+        return sign | (uint16_t)rint(ldexp(v, 24));
+    (void)frexp(v, &ex);
+    e = ex - 1; /* 2^e <= v < 2^(e+1) */
+    m = rint(ldexp(v, 10 - e));
+    if (m == 2048.0) {
+        m = 1024.0;
+        ++e;
+    }
+    return sign | (uint16_t)(((e + 15) << 10) | ((int)m - 1024));
+}
+
+static void wr_u16(uint8_t *p, uint16_t h)
+{
+    p[0] = (uint8_t)(h & 0xff);
+    p[1] = (uint8_t)(h >> 8);
+}
+
+/* One q8_0 block from 32 binary32 values (rule in the header). */
+static void quant_q8_0_block(const float *x, uint8_t *blk)
+{
+    float amax = 0.0f, d, id;
+    int i;
+    for (i = 0; i < 32; ++i)
+        if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+    d = amax / 127.0f;
+    id = d != 0.0f ? 1.0f / d : 0.0f;
+    wr_u16(blk, orc_f32_to_f16(d));
+    for (i = 0; i < 32; ++i) {
+        const float v = x[i] * id;
+        blk[2 + i] = (uint8_t)(int8_t)roundf(v);
+    }
+}
+
+/* One q4_0 block from 32 binary32 values (rule in the header). */
+static void quant_q4_0_block(const float *x, uint8_t *blk)
+{
+    float amax = 0.0f, m = 0.0f, d, id;
+    int i, n[32];
+    for (i = 0; i < 32; ++i)
+        if (fabsf(x[i]) > amax) {
+            amax = fabsf(x[i]);
+            m = x[i];
+        }
+    d = m / -8.0f;
+    id = d != 0.0f ? 1.0f / d : 0.0f;
+    wr_u16(blk, orc_f32_to_f16(d));
+    for (i = 0; i < 32; ++i) {
+        const float v = x[i] * id;
+        const float w = v + 8.5f;
+        int c = (int)w;
+        if (c > 15) c = 15;
+        n[i] = c;
+    }
+    for (i = 0; i < 16; ++i) blk[2 + i] = (uint8_t)(n[i] | (n[i + 16] << 4));
+}
+
+/* Store one row of D binary32 values in a cache type: binary32 bytes as
+ * they are, binary16 rounded to nearest even, or D/32 blocks.  Returns 0, or
+ * -1 for a bad type or a block type with D % 32 != 0. */
+int orc_encode_row(int type, const float *x, int64_t d, uint8_t *out)
+{
+    int64_t i;
+    if (!orc_row_bytes(type, d)) return -1;
+    switch (type) {
+    case ORC_F32:
+        memcpy(out, x, 4 * d);
+        break;
+    case ORC_F16:
+        for (i = 0; i < d; ++i) wr_u16(out + 2 * i, orc_f32_to_f16(x[i]));
+        break;
+    case ORC_Q8_0:
+        for (i = 0; i < d / 32; ++i) quant_q8_0_block(x + 32 * i, out + 34 * i);
+        break;
+    case ORC_Q4_0:
+        for (i = 0; i < d / 32; ++i) quant_q4_0_block(x + 32 * i, out + 18 * i);
+        break;
+    }
+    return 0;
+}
+
+/* Where a new row at absolute position pos goes, for a layer whose window
+ * holds positions [0, window_cap) and whose tail holds [window_cap,
+ * window_cap + tail_cap): returns 0 (window) or 1 (tail) and the row index
+ * inside that region in *row, or -1 when the position fits neither. */
+int orc_route(int64_t pos, int64_t window_cap, int64_t tail_cap, int64_t *row)
+{
+    if (pos < 0) return -1;
+    if (pos < window_cap) {
+        *row = pos;
+        return 0;
+    }
+    if (pos - window_cap < tail_cap) {
+        *row = pos - window_cap;
+        return 1;
+    }
+    return -1;
 }
 
 /* A segment of the KV cache: positions [0, n_keys) of a view.  Byte strides:

@@ -16,6 +16,13 @@ What pins what:
     window and tail is exact online softmax ("F5 M7 -- Rolling KV",
     "Implementation decomposition, refined", S2), and that a single tile /
     an all-resident cache degenerates to plain attention.
+  - the write path: binary16 encoding against hand-worked patterns, every
+    binary16 value and every midpoint between neighbours (ties to even), and
+    numpy's float16 cast; block quantisation against hand-worked blocks
+    (tests/golden/quant_blocks.json), against optimality of each code given
+    the scale (brute force over all codes), and against the round-trip error
+    bound through the separately pinned dequantiser; routing against a
+    hand-worked table.
 """
 from __future__ import annotations
 
@@ -169,6 +176,178 @@ def pin_block_sizes_match_pages(orc):
         assert orc.row_bytes(synth.Q8_0, d) == 34 * d // 32
         assert orc.row_bytes(synth.Q4_0, d) == 18 * d // 32
     assert orc.row_bytes(synth.Q8_0, 48) == 0  # D % 32 != 0 is not a block row
+
+
+# ----------------------------------------------------------------------------- write path
+
+def _quant_golden():
+    return json.load(open(os.path.join(GOLDEN, "quant_blocks.json")))
+
+
+def pin_f16_encode_hand(orc):
+    for x, bits, _why in _quant_golden()["f16"]["cases"]:
+        v = float(x) if x in ("inf", "-inf") else float.fromhex(x)
+        assert orc.f32_to_f16(v) == int(bits, 16), (x, bits, hex(orc.f32_to_f16(v)))
+
+
+def pin_f16_encode_exhaustive(orc):
+    # every finite binary16 value encodes to itself; every midpoint between
+    # two neighbours (exact in binary32) goes to the one with the even
+    # fraction, and the binary32 values just beside the midpoint go to the
+    # nearer neighbour
+    enc = np.frompyfunc(lambda v: orc.f32_to_f16(float(v)), 1, 1)
+    pos = np.arange(0, 0x7C00, dtype=np.uint16)
+    vals = pos.view(np.float16).astype(np.float32)
+    got = enc(vals).astype(np.int64)
+    assert np.array_equal(got, pos.astype(np.int64))
+    got = enc(-vals).astype(np.int64)
+    assert np.array_equal(got, pos.astype(np.int64) | 0x8000)
+    lo = pos[:-1].view(np.float16).astype(np.float64)
+    hi = pos[1:].view(np.float16).astype(np.float64)
+    mid = ((lo + hi) / 2).astype(np.float32)
+    assert np.array_equal(mid.astype(np.float64), (lo + hi) / 2)
+    even = np.where(pos[:-1] % 2 == 0, pos[:-1], pos[1:]).astype(np.int64)
+    assert np.array_equal(enc(mid).astype(np.int64), even)
+    below = np.nextafter(mid, np.float32(0))
+    above = np.nextafter(mid, np.float32(np.inf))
+    assert np.array_equal(enc(below).astype(np.int64), pos[:-1].astype(np.int64))
+    assert np.array_equal(enc(above).astype(np.int64), pos[1:].astype(np.int64))
+
+
+def pin_f16_encode_library(orc):
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(4000), rng.standard_normal(2000) * 1e-5,
+                        rng.standard_normal(2000) * 3e4, rng.standard_normal(500) * 1e-7]).astype(np.float32)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16).astype(np.int64)
+    got = np.array([orc.f32_to_f16(float(v)) for v in x], dtype=np.int64)
+    assert np.array_equal(got, ref)
+
+
+def pin_quant_hand_blocks(orc):
+    for b in _quant_golden()["blocks"]:
+        x = np.array([float.fromhex(v) for v in b["x"]], dtype=np.float32)
+        got = orc.encode_rows(x, b["type"]).tobytes().hex()
+        assert got == b["expected"], (b["name"], got)
+
+
+def _random_blocks(seed, n):
+    """N(0,1) blocks at several magnitudes, some with planted ties of the
+    largest magnitude (same and opposite sign) and exact half-way values."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 32)).astype(np.float32)
+    x *= np.float32(10.0) ** rng.integers(-6, 4, size=(n, 1)).astype(np.float32)
+    for i in range(0, n, 3):
+        j, k = rng.choice(32, 2, replace=False)
+        x[i, k] = -x[i, j] if i % 2 else x[i, j]
+        x[i, j] = x[i, k] if abs(x[i, k]) >= np.abs(x[i]).max() else x[i, j]
+    x[::7] = np.round(x[::7] * 4) / 4  # quarter grid: many exact halves after scaling
+    return x
+
+
+def _decode_scale(orc, blk):
+    return orc.f16_to_f64(int(blk[0]) | (int(blk[1]) << 8))
+
+
+def _nearest_f16(orc, d32, bits):
+    """bits is a binary16 value nearest to d32 (checked against both neighbours)."""
+    h = orc.f16_to_f64(bits)
+    for nb in (bits - 1, bits + 1):
+        if (nb & 0x7FFF) <= 0x7BFF and (nb & 0x7FFF) != 0x7FFF:
+            assert abs(h - d32) <= abs(orc.f16_to_f64(nb & 0xFFFF) - d32), (d32, bits)
+
+
+def pin_quant_brute_force(orc):
+    # Each code is the best one for the binary32 scale, over all codes the
+    # format can hold; the stored scale is a nearest binary16 of it.
+    x = _random_blocks(11, 96)
+    q8 = orc.encode_rows(x, synth.Q8_0)
+    q4 = orc.encode_rows(x, synth.Q4_0)
+    cand8 = np.arange(-128, 128, dtype=np.float64)
+    cand4 = np.arange(0, 16, dtype=np.float64)
+    for b in range(x.shape[0]):
+        xb = x[b]
+        amax = float(np.abs(xb).max())
+        # --- q8_0
+        d = float(np.float32(amax / 127.0))  # binary64 quotient rounded once: the binary32 quotient
+        inv = np.float32(1.0 / d) if d else np.float32(0.0)
+        bits = int(q8[b, 0]) | (int(q8[b, 1]) << 8)
+        _nearest_f16(orc, d, bits)
+        codes = q8[b, 2:].view(np.int8).astype(np.float64)
+        v = (xb * inv).astype(np.float64)  # the binary32 scaled values
+        for i in range(32):
+            err = np.abs(v[i] - cand8)
+            best = cand8[err == err.min()]
+            want = best[np.argmax(np.abs(best))]  # a tie goes away from zero
+            assert codes[i] == want, ("q8_0", b, i, v[i], codes[i])
+        # --- q4_0
+        m = 0.0
+        for t in range(32):  # first value of largest magnitude
+            if abs(float(xb[t])) > abs(m):
+                m = float(xb[t])
+        d4 = m / -8.0
+        assert d4 == float(np.float32(d4))
+        bits = int(q4[b, 0]) | (int(q4[b, 1]) << 8)
+        _nearest_f16(orc, d4, bits)
+        if m == 0.0:
+            assert bits == 0x8000 and np.all(q4[b, 2:] == 0x88)
+            continue
+        inv4 = np.float32(1.0 / d4)
+        nib = q4[b, 2:]
+        n = np.concatenate([nib & 15, nib >> 4]).astype(np.float64)
+        v4 = (xb * inv4).astype(np.float64)
+        for i in range(32):
+            # n - 8 is the nearest code to v (within the rounding of one
+            # binary32 add), clamped to the 16 codes; the value -m alone
+            # (v = +8) needs the clamp
+            err = np.abs(v4[i] - (cand4 - 8))
+            assert err[int(n[i])] <= err.min() + 2.0 ** -19 * 16, ("q4_0", b, i, v4[i], n[i])
+            if abs(v4[i] - round(v4[i])) > 2.0 ** -18 and abs(abs(v4[i] - np.floor(v4[i])) - 0.5) > 2.0 ** -18:
+                assert n[i] - 8 == min(7, int(np.floor(v4[i] + 0.5))), ("q4_0", b, i, v4[i], n[i])
+        # exact halves go up: v = k + 1/2 -> code k + 1
+        for i in range(32):
+            if v4[i] - np.floor(v4[i]) == 0.5 and v4[i] < 7:
+                assert n[i] - 8 == np.floor(v4[i]) + 1
+
+
+def pin_quant_round_trip(orc):
+    # Through the separately pinned dequantiser: each value is within half a
+    # step of the binary32 scale, plus what storing the scale as binary16
+    # moves the grid.  q4_0's 16 codes cover -8..7 steps on the side of -m
+    # ... +m: a value beyond 7.5 steps (on the side opposite m) is clamped to
+    # 7 steps and may be up to a whole step away.
+    x = _random_blocks(12, 200)
+    for t in (synth.Q8_0, synth.Q4_0):
+        blocks = orc.encode_rows(x, t)
+        deq = (orc.dequant_q8_0 if t == synth.Q8_0 else orc.dequant_q4_0)(blocks.reshape(-1), x.size).reshape(x.shape)
+        bb = blocks.reshape(x.shape[0], -1)
+        for b in range(x.shape[0]):
+            xb = x[b].astype(np.float64)
+            d16 = _decode_scale(orc, bb[b])
+            if t == synth.Q8_0:
+                d32 = float(np.abs(xb).max()) / 127.0
+                allowed = 0.5 * d32 * (1 + 2.0 ** -18) + 127 * abs(abs(d16) - d32)
+            else:
+                m = xb[np.argmax(np.abs(xb))]
+                d32 = m / -8.0
+                steps = xb / d32 if d32 else np.zeros(32)
+                allowed = np.maximum(0.5, steps - 7) * abs(d32) * (1 + 2.0 ** -18) + 8 * abs(d16 - d32)
+            err = np.abs(xb - deq[b].astype(np.float64))
+            assert np.all(err <= allowed + 1e-30), (t, b, float(err.max()))
+    # float storage types: binary32 unchanged, binary16 as numpy rounds it
+    assert np.array_equal(orc.encode_rows(x, synth.F32).view(np.float32).reshape(x.shape), x)
+    assert np.array_equal(orc.encode_rows(x, synth.F16).view(np.float16).reshape(x.shape), x.astype(np.float16))
+
+
+def pin_route(orc):
+    for pos, wc, tc, region, row in _quant_golden()["route"]["cases"]:
+        if region is None:
+            try:
+                orc.route(pos, wc, tc)
+            except ValueError:
+                continue
+            raise AssertionError(f"position {pos} routed with window {wc}, tail {tc}")
+        assert orc.route(pos, wc, tc) == (region, row), (pos, wc, tc)
 
 
 # ----------------------------------------------------------------------------- attention against library routines

@@ -31,6 +31,25 @@ MUTANTS = {
     "seq_stride_ignored": ("(int64_t)b * w->k_seq_stride", "(int64_t)0 * w->k_seq_stride"),
     "dot_index_shift": ("qd[d] * kv[d]", "qd[d] * kv[(d + 1) % head_dim]"),
     "combine_lse_drops_max": ("lse_out[r] = mx + log(z);", "lse_out[r] = log(z);"),
+    # write path
+    "f16enc_truncate": ("m = rint(ldexp(v, 10 - e));", "m = floor(ldexp(v, 10 - e));"),
+    "f16enc_subnormal_shift": ("rint(ldexp(v, 24))", "rint(ldexp(v, 23))"),
+    "f16enc_overflow_guard": ("if (v >= 65520.0)", "if (v >= 131072.0)"),
+    "f16enc_no_carry": ("if (m == 2048.0) {", "if (m > 2048.0) {"),
+    "f16enc_bias": ("((e + 15) << 10)", "((e + 14) << 10)"),
+    "q8enc_divisor": ("d = amax / 127.0f;", "d = amax / 128.0f;"),
+    "q8enc_round_even": ("roundf(v)", "rintf(v)"),
+    "q8enc_codes_from_f16_scale": ("blk[2 + i] = (uint8_t)(int8_t)roundf(v);",
+                                   "blk[2 + i] = (uint8_t)(int8_t)roundf((float)(x[i] / orc_f16_to_f64(orc_f32_to_f16(d))));"),
+    "q4enc_offset": ("const float w = v + 8.5f;", "const float w = v + 8.0f;"),
+    "q4enc_scale_sign": ("d = m / -8.0f;", "d = m / 8.0f;"),
+    "q4enc_last_largest": ("if (fabsf(x[i]) > amax) {", "if (fabsf(x[i]) >= amax) {"),
+    "q4enc_no_clamp": ("if (c > 15) c = 15;", ""),
+    "q4enc_nibble_order": ("(uint8_t)(n[i] | (n[i + 16] << 4))", "(uint8_t)(n[2 * i] | (n[2 * i + 1] << 4))"),
+    "q4enc_zero_block_sign": ("float amax = 0.0f, m = 0.0f, d, id;", "float amax = 0.0f, m = -0.0f, d, id;"),
+    "route_window_edge": ("if (pos < window_cap) {", "if (pos <= window_cap) {"),
+    "route_tail_row": ("*row = pos - window_cap;", "*row = pos;"),
+    "route_tail_edge": ("if (pos - window_cap < tail_cap) {", "if (pos - window_cap <= tail_cap) {"),
 }
 
 
