@@ -343,6 +343,37 @@ def other_workloads(P, synth, reps=20):
     res["shared_prefix"] = {"us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1),
                             "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4), "bytes": b,
                             "prefix_only_us": round(tp * 1e6, 2)}
+    del inst
+    torch.cuda.empty_cache()
+
+    # The write path: new binary32 rows quantised on append (q8_0 K, q4_0 V),
+    # 8 KV heads x head_dim 128.  decode: one token into each of 48 layers'
+    # windows (latency per call); prefill: a 4096-token chunk that crosses from
+    # the window into the tail of one layer (bytes = f32 rows read + stored rows
+    # written).
+    Hkv, D, wc, tc = 8, 128, 49152, 16384
+    win = [(synth.make_cache(wc, Hkv, D, synth.Q8_0, synth.stream_seed(6, 1, i), dev),
+            synth.make_cache(wc, Hkv, D, synth.Q4_0, synth.stream_seed(6, 2, i), dev)) for i in range(48)]
+    tail = (synth.make_cache(tc, Hkv, D, synth.Q8_0, synth.stream_seed(6, 3), dev),
+            synth.make_cache(tc, Hkv, D, synth.Q4_0, synth.stream_seed(6, 4), dev))
+    wv = [P.view_of_cache(kc, vc) for kc, vc in win]
+    tv = P.view_of_cache(*tail)
+    x1 = synth.append_rows(1, Hkv, D, synth.stream_seed(6, 5), dev, large=False)
+    k = [0]
+
+    def dec():
+        P.rkv_append_kv(Hkv, D, 1, 1000 + k[0] % 4096, 0, x1, x1, wv[k[0] % 48], tv)
+        k[0] += 1
+    t = timed(dec)
+    res["append_decode"] = {"us_per_call": round(t * 1e6, 2),
+                            "note": "one token, 8 KV heads x 128, q8_0 K / q4_0 V, 48 layers' windows in turn"}
+    nch = 4096
+    xk = synth.append_rows(nch, Hkv, D, synth.stream_seed(6, 6), dev, large=False)
+    xv = synth.append_rows(nch, Hkv, D, synth.stream_seed(6, 7), dev, large=False)
+    t = timed(lambda: P.rkv_append_kv(Hkv, D, nch, wc - nch // 2, 0, xk, xv, wv[0], tv))
+    b = 2 * nch * Hkv * D * 4 + nch * Hkv * (136 + 72)
+    res["append_prefill_4096"] = {"us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1),
+                                  "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4), "bytes": b}
     return res
 
 

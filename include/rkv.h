@@ -278,6 +278,58 @@ int rkv_ring_end_step(rkv_ring *ring);
 int64_t rkv_ring_schedule(int n_layers, const int64_t *tiles_per_layer, int n_slots, int64_t max_items,
                           int32_t *layer_of, int64_t *tile_of, int32_t *slot_of, int64_t *waits_on);
 
+/* ---- write path ------------------------------------------------------------
+ * rkv_append_kv -- store the K and V rows of n_tokens new tokens of one layer
+ * and one sequence at the consecutive positions pos0, pos0 + 1, ..., each in
+ * the storage type of the region it lands in.
+ *
+ * Routing ("Rolling-KV: step/graph-level tail prefetch (design)", section
+ * "Staged plan", S0 / bug-1341: a layer's writes follow that layer's own
+ * window size, so a layer without a tail writes everything to its window;
+ * "F5 M7 -- Rolling KV", section "2026-07-14 -- bug-2172 SHIPPED": each new
+ * row goes to the window or the tail by its position): position p goes to
+ * window row p when p < window->n_keys, else to tail row p - window->n_keys.
+ * Here n_keys of window and tail is read as the region's capacity in
+ * positions; NULL is a region of capacity 0.  pos0 + n_tokens must not exceed
+ * the two capacities together (RKV_E_INVAL, nothing written).
+ *
+ * Storage (block formats of "F5 M6 -- PolyKV", section "S0 -- Bootstrap"; the
+ * pages print no rule for making codes, the one used is the common rule for
+ * these formats, in binary32 arithmetic without fused multiply-add):
+ *   RKV_F32  the value; RKV_F16 the nearest binary16 (ties to even);
+ *   RKV_Q8_0 d = amax / 127, q = round-half-away-from-zero(x * (1/d));
+ *   RKV_Q4_0 m = the first value of largest magnitude in the block (+0 if
+ *            all are zero), d = m / -8, n = min(15, trunc(x * (1/d) + 8.5));
+ *   1/d is 0 when d = 0; the block scale is stored as the binary16 nearest
+ *   the binary32 d (ties to even) and the codes are made from the binary32 d.
+ * Values must be finite.
+ *
+ * k_new, v_new: device binary32 [n_tokens][n_kv_heads][head_dim], contiguous,
+ *   4-byte aligned.  head_dim 64, 128, 256 or 512.
+ * window: device memory.  tail: device memory or pinned host memory (then
+ *   the kernel makes its stores visible system-wide before it ends).  Both are
+ *   position-major with the byte strides of the view; seq selects the
+ *   sequence (seq * seq_stride); pointers and strides must be even, the rows
+ *   of one position must fit in its position stride.  Window and tail may
+ *   have different types.
+ * fresh (optional, device memory): receives the tail-routed rows as well, row
+ *   j = the j-th of them (n_keys >= their count), in fresh's own types, so the
+ *   step that writes them can attend them from device memory (the ring's
+ *   copies of a step may have started before the step's own appends).
+ * ring (optional) with layer in [0, 1024): when tail rows are written, a
+ *   one-thread kernel after the append marks the layer written (a host-visible
+ *   word of the ring); copies of that layer's tail in steps begun with
+ *   rkv_ring_begin_step after this call wait on the host until the append has
+ *   finished.  Appends to one layer that name a ring must be ordered (one
+ *   stream, or the caller's own ordering), and must be issued from the thread
+ *   that calls rkv_ring_begin_step, or ordered with it.
+ * Enqueued on stream; allocates nothing.  Errors: RKV_E_INVAL,
+ * RKV_E_UNSUPPORTED, RKV_E_HIP.
+ */
+int rkv_append_kv(int n_kv_heads, int head_dim, int n_tokens, int64_t pos0, int seq, const float *k_new,
+                  const float *v_new, const rkv_kv_view *window, const rkv_kv_view *tail, const rkv_kv_view *fresh,
+                  rkv_ring *ring, int layer, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ EXPORTS = (
     "rkv_status_string", "rkv_last_error", "rkv_row_bytes", "rkv_attend_workspace_bytes", "rkv_attend_segment",
     "rkv_lse_combine", "rkv_dequant_q8_0", "rkv_dequant_q4_0", "rkv_ring_create", "rkv_ring_destroy",
     "rkv_ring_begin_step", "rkv_stream_tail_workspace_bytes", "rkv_stream_tail", "rkv_ring_end_step",
-    "rkv_ring_schedule", "rkv_attend_split", "rkv_attend_split_workspace_bytes",
+    "rkv_ring_schedule", "rkv_attend_split", "rkv_attend_split_workspace_bytes", "rkv_append_kv",
 )
 
 
@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
                                                       ctypes.POINTER(sz)]
         L.rkv_stream_tail.argtypes = [vp, ctypes.c_int, ctypes.POINTER(rkv_attn_desc), vp, vp, vp, vp, vp, vp, sz, vp]
         L.rkv_ring_end_step.argtypes = [vp]
+        L.rkv_append_kv.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, ctypes.c_int, vp, vp,
+                                    ctypes.POINTER(rkv_kv_view), ctypes.POINTER(rkv_kv_view),
+                                    ctypes.POINTER(rkv_kv_view), vp, ctypes.c_int, vp]
         L.rkv_ring_schedule.restype = i64
         L.rkv_ring_schedule.argtypes = [ctypes.c_int, ctypes.POINTER(i64), ctypes.c_int, i64, vp, vp, vp, vp]
         for name in EXPORTS:
@@ -258,6 +261,16 @@ class Ring:
 
     def rkv_ring_end_step(self) -> None:
         _check(lib().rkv_ring_end_step(self.h))
+
+
+def rkv_append_kv(n_kv_heads: int, head_dim: int, n_tokens: int, pos0: int, seq: int, k_new: torch.Tensor,
+                  v_new: torch.Tensor, window: rkv_kv_view | None, tail: rkv_kv_view | None,
+                  fresh: rkv_kv_view | None = None, ring: "Ring | None" = None, layer: int = 0, stream=None) -> None:
+    """Store n_tokens new K / V rows (binary32 [n_tokens][n_kv_heads][head_dim]
+    on the device) at positions pos0.. of a layer's window / tail."""
+    ref = lambda v: None if v is None else ctypes.byref(v)
+    _check(lib().rkv_append_kv(n_kv_heads, head_dim, n_tokens, pos0, seq, _addr(k_new), _addr(v_new), ref(window),
+                               ref(tail), ref(fresh), None if ring is None else ring.h, layer, _stream(stream)))
 
 
 def view_of_cache(kc, vc, start: int = 0, stop: int | None = None, k_seq_stride: int = 0,

@@ -481,6 +481,13 @@ struct rkv_ring {
     // last read slot s (-1: none); written by the caller's thread under mu.
     uint64_t *progress = nullptr;
     int64_t last_user[16];
+    // Rows appended to a layer's tail by rkv_append_kv naming this ring: a
+    // kernel after the append writes the layer's append count to
+    // written[layer] (pinned, coherent host memory) once the rows are stored,
+    // and the copies of that layer in steps begun later wait for it.
+    // appends[layer]: appends issued so far (the caller's thread).
+    uint64_t *written = nullptr;
+    int64_t appends[kRingMaxLayers] = {};
     // plan of the current step
     bool in_step = false;
     std::vector<rkv_kv_view> tails;
@@ -488,6 +495,7 @@ struct rkv_ring {
     struct Item {
         int layer;
         int64_t k0, nk;
+        int64_t need_w;  // written[layer] must reach this before the copy (appends issued before the step)
     };
     std::vector<Item> items;
     std::vector<int64_t> first_item;  // per layer, plus end
@@ -508,6 +516,24 @@ struct rkv_ring {
 
 namespace {
 
+// Wait on the host until a host-visible word written by a kernel reaches
+// need (spin briefly, since a tile takes tens of microseconds, then yield).
+// false after 60 s.
+bool wait_word(const uint64_t *w, int64_t need)
+{
+    if (need <= 0 || __atomic_load_n(w, __ATOMIC_ACQUIRE) >= (uint64_t)need) return true;
+    const auto t0 = std::chrono::steady_clock::now();
+    unsigned spins = 0;
+    while (__atomic_load_n(w, __ATOMIC_ACQUIRE) < (uint64_t)need) {
+        if (++spins < 4096)
+            __builtin_ia32_pause();
+        else
+            std::this_thread::yield();
+        if (spins % 1024 == 0 && std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60)) return false;
+    }
+    return true;
+}
+
 // Enqueue the copy of item j (index in the step) into its slot, on the copy
 // stream, once the compute that last read the slot has finished: the copier
 // waits for that on the host, watching the ring's progress word (the merge
@@ -523,21 +549,13 @@ hipError_t enqueue_copy(rkv_ring *r, int64_t j, int64_t need, const char **what)
     const int s = (int)(j % r->B);
     const size_t kb = (size_t)(it.nk * t.k_pos_stride), vb = (size_t)(it.nk * t.v_pos_stride);
     hipError_t e;
-    const uint64_t *done = r->progress + s;
-    if (need > 0 && __atomic_load_n(done, __ATOMIC_ACQUIRE) < (uint64_t)need) {
-        const auto t0 = std::chrono::steady_clock::now();
-        unsigned spins = 0;
-        while (__atomic_load_n(done, __ATOMIC_ACQUIRE) < (uint64_t)need) {
-            // spin briefly (a tile takes tens of microseconds), then yield
-            if (++spins < 4096)
-                __builtin_ia32_pause();
-            else
-                std::this_thread::yield();
-            if (spins % 1024 == 0 && std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60)) {
-                *what = "slot release: the compute that last read the slot did not finish within 60 s";
-                return hipErrorLaunchTimeOut;
-            }
-        }
+    if (!wait_word(r->progress + s, need)) {
+        *what = "slot release: the compute that last read the slot did not finish within 60 s";
+        return hipErrorLaunchTimeOut;
+    }
+    if (!wait_word(r->written + it.layer, it.need_w)) {
+        *what = "tail rows: an append to the layer's tail did not finish within 60 s";
+        return hipErrorLaunchTimeOut;
     }
     *what = "hipMemcpyAsync (tile K)";
     if ((e = hipMemcpyAsync(r->sk[s], (const char *)t.k + it.k0 * t.k_pos_stride, kb, hipMemcpyHostToDevice,
@@ -616,6 +634,7 @@ void ring_free(rkv_ring *r)
         if (r->copy_done[i]) (void)hipEventDestroy(r->copy_done[i]);
     }
     if (r->progress) (void)hipHostFree(r->progress);
+    if (r->written) (void)hipHostFree(r->written);
     if (r->own_copy && r->copy) (void)hipStreamDestroy(r->copy);
     delete r;
 }
@@ -662,6 +681,13 @@ int rkv_ring_create(int n_slots, size_t slot_k_bytes, size_t slot_v_bytes, hipSt
         ring_free(r);
         return hip_fail(e, "hipHostMalloc (progress)");
     }
+    if ((e = hipHostMalloc((void **)&r->written, kRingMaxLayers * sizeof(uint64_t), hipHostMallocCoherent)) !=
+        hipSuccess) {
+        r->written = nullptr;
+        ring_free(r);
+        return hip_fail(e, "hipHostMalloc (written)");
+    }
+    for (int i = 0; i < kRingMaxLayers; ++i) __atomic_store_n(r->written + i, (uint64_t)0, __ATOMIC_RELEASE);
     for (int i = 0; i < 16; ++i) {
         __atomic_store_n(r->progress + i, (uint64_t)0, __ATOMIC_RELEASE);
         r->last_user[i] = -1;
@@ -694,14 +720,19 @@ int rkv_ring_destroy(rkv_ring *r)
     hipError_t e = hipStreamSynchronize(r->copy);
     // the slots are freed only after the last tile of each has been read
     const auto t0 = std::chrono::steady_clock::now();
-    for (int i = 0; i < r->B && e == hipSuccess; ++i)
-        while (__atomic_load_n(r->progress + i, __ATOMIC_ACQUIRE) < (uint64_t)(r->last_user[i] + 1)) {
+    // (and the signals of appends that name the ring have been written: they
+    // write into the ring's memory)
+    auto reached = [&](const uint64_t *w, int64_t need) {
+        while (__atomic_load_n(w, __ATOMIC_ACQUIRE) < (uint64_t)need) {
             std::this_thread::sleep_for(std::chrono::microseconds(50));
-            if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60)) {
-                e = hipErrorLaunchTimeOut;
-                break;
-            }
+            if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60)) return false;
         }
+        return true;
+    };
+    for (int i = 0; i < r->B && e == hipSuccess; ++i)
+        if (!reached(r->progress + i, r->last_user[i] + 1)) e = hipErrorLaunchTimeOut;
+    for (int l = 0; l < kRingMaxLayers && e == hipSuccess; ++l)
+        if (!reached(r->written + l, r->appends[l])) e = hipErrorLaunchTimeOut;
     ring_free(r);
     if (e != hipSuccess) return hip_fail(e, "ring destroy synchronisation");
     return RKV_OK;
@@ -712,6 +743,7 @@ int rkv_ring_begin_step(rkv_ring *r, int n_layers, const rkv_kv_view *tails, int
     if (!r) return fail(RKV_E_INVAL, "ring is NULL");
     if (r->in_step) return fail(RKV_E_STATE, "previous step not ended");
     if (n_layers < 0 || (n_layers > 0 && !tails)) return fail(RKV_E_INVAL, "bad layers");
+    if (n_layers > kRingMaxLayers) return fail(RKV_E_UNSUPPORTED, "more than %d layers", kRingMaxLayers);
     if (tile_keys < 1) return fail(RKV_E_INVAL, "tile_keys must be >= 1");
     std::vector<rkv_ring::Item> items;
     std::vector<int64_t> first(n_layers + 1, 0);
@@ -728,7 +760,7 @@ int rkv_ring_begin_step(rkv_ring *r, int n_layers, const rkv_kv_view *tails, int
         if (mem_kind(t.k) != 1 || mem_kind(t.v) != 1)
             return fail(RKV_E_INVAL, "tail %d must be pinned host memory", l);
         for (int64_t k0 = 0; k0 < t.n_keys; k0 += tile_keys)
-            items.push_back({l, k0, std::min(tile_keys, t.n_keys - k0)});
+            items.push_back({l, k0, std::min(tile_keys, t.n_keys - k0), r->appends[l]});
         if ((int64_t)items.size() - first[l] > kMaxParts - 1)
             return fail(RKV_E_UNSUPPORTED, "tail %d: more than %d tiles", l, kMaxParts - 1);
     }
@@ -862,6 +894,85 @@ int rkv_stream_tail(rkv_ring *r, int layer, const rkv_attn_desc *desc, const flo
         RKV_HIP(launch_combine(np, parts, n_rows, D, o, lse, cs));
     }
     r->next_layer++;
+    return RKV_OK;
+}
+
+int rkv_append_kv(int n_kv_heads, int head_dim, int n_tokens, int64_t pos0, int seq, const float *k_new,
+                  const float *v_new, const rkv_kv_view *window, const rkv_kv_view *tail, const rkv_kv_view *fresh,
+                  rkv_ring *ring, int layer, hipStream_t stream)
+{
+    if (n_kv_heads < 1 || n_kv_heads > 65535) return fail(RKV_E_INVAL, "n_kv_heads must be in [1, 65535]");
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+        return fail(RKV_E_UNSUPPORTED, "head_dim must be 64, 128, 256 or 512");
+    if (n_tokens < 0) return fail(RKV_E_INVAL, "n_tokens < 0");
+    if (pos0 < 0 || seq < 0) return fail(RKV_E_INVAL, "pos0 and seq must be >= 0");
+    if (ring && (layer < 0 || layer >= kRingMaxLayers))
+        return fail(RKV_E_INVAL, "layer must be in [0, %d)", kRingMaxLayers);
+    const int64_t wc = window ? window->n_keys : 0, tc = tail ? tail->n_keys : 0;
+    if (wc < 0 || tc < 0) return fail(RKV_E_INVAL, "capacities (n_keys) must be >= 0");
+    if (pos0 + n_tokens > wc + tc)
+        return fail(RKV_E_INVAL, "positions [%lld, %lld) exceed window %lld + tail %lld", (long long)pos0,
+                    (long long)(pos0 + n_tokens), (long long)wc, (long long)tc);
+    if (n_tokens == 0) return RKV_OK;
+    if (n_tokens > (1 << 30)) return fail(RKV_E_UNSUPPORTED, "n_tokens too large");
+    int rc;
+    if ((rc = check_device(k_new, "k_new")) || (rc = check_device(v_new, "v_new"))) return rc;
+    if ((uintptr_t)k_new % 4 || (uintptr_t)v_new % 4) return fail(RKV_E_INVAL, "k_new / v_new must be 4-byte aligned");
+    // tokens [0, nw) go to the window, [nw, n_tokens) to the tail
+    const int nw = (int)std::max<int64_t>(0, std::min<int64_t>(n_tokens, wc - pos0));
+    const int nt = n_tokens - nw;
+    AppendParams p;
+    memset(&p, 0, sizeof p);
+    p.n_kv_heads = n_kv_heads;
+    // One destination: validate the region and fill p.dst[p.n_dst].  kinds:
+    // bit 1 device memory allowed, bit 0 pinned host memory allowed.
+    auto add = [&](const rkv_kv_view *v, const char *name, int first, int count, int64_t row0, int kinds) -> int {
+        if (count == 0) return RKV_OK;
+        if (!valid_type(v->k_type) || !valid_type(v->v_type)) return fail(RKV_E_INVAL, "%s: bad K/V type", name);
+        if (!v->k || !v->v) return fail(RKV_E_INVAL, "%s: K or V pointer is NULL", name);
+        const int64_t rbk = row_bytes_of(v->k_type, head_dim), rbv = row_bytes_of(v->v_type, head_dim);
+        if (v->k_pos_stride <= 0 || v->v_pos_stride <= 0 || v->k_head_stride < 0 || v->v_head_stride < 0 ||
+            v->k_seq_stride < 0 || v->v_seq_stride < 0)
+            return fail(RKV_E_INVAL, "%s: strides must be non-negative (position strides positive)", name);
+        if ((uintptr_t)v->k % 2 || (uintptr_t)v->v % 2 || v->k_pos_stride % 2 || v->v_pos_stride % 2 ||
+            v->k_head_stride % 2 || v->v_head_stride % 2 || v->k_seq_stride % 2 || v->v_seq_stride % 2)
+            return fail(RKV_E_INVAL, "%s: pointers and strides must be even", name);
+        if (n_kv_heads > 1 && (v->k_head_stride < rbk || v->v_head_stride < rbv))
+            return fail(RKV_E_INVAL, "%s: head stride smaller than a row", name);
+        if ((n_kv_heads - 1) * v->k_head_stride + rbk > v->k_pos_stride ||
+            (n_kv_heads - 1) * v->v_head_stride + rbv > v->v_pos_stride)
+            return fail(RKV_E_INVAL, "%s: the rows of one position must fit in its position stride", name);
+        auto allowed = [kinds](int m) { return (m == 2 && (kinds & 2)) || (m == 1 && (kinds & 1)); };
+        const int mk = mem_kind(v->k), mv = mem_kind(v->v);
+        if (!allowed(mk) || !allowed(mv))
+            return fail(RKV_E_INVAL, "%s: must be %s", name,
+                        kinds == 2 ? "device memory" : "device memory or pinned host memory");
+        if (mk == 1 || mv == 1) p.sys_fence = 1;
+        AppendDst &d = p.dst[p.n_dst++];
+        d.k = (uint8_t *)v->k + (int64_t)seq * v->k_seq_stride;
+        d.v = (uint8_t *)v->v + (int64_t)seq * v->v_seq_stride;
+        d.k_pos = v->k_pos_stride;
+        d.v_pos = v->v_pos_stride;
+        d.k_head = v->k_head_stride;
+        d.v_head = v->v_head_stride;
+        d.k_type = v->k_type;
+        d.v_type = v->v_type;
+        d.first_tok = first;
+        d.n_tok = count;
+        d.row0 = row0;
+        return RKV_OK;
+    };
+    if ((rc = add(window, "window", 0, nw, pos0, 2))) return rc;
+    if ((rc = add(tail, "tail", nw, nt, pos0 + nw - wc, 3))) return rc;
+    if (fresh && nt > 0) {
+        if (fresh->n_keys < nt) return fail(RKV_E_INVAL, "fresh holds %lld rows, %d needed", (long long)fresh->n_keys, nt);
+        if ((rc = add(fresh, "fresh", nw, nt, 0, 2))) return rc;
+    }
+    RKV_HIP(launch_append(head_dim, n_tokens, n_kv_heads, k_new, v_new, p, stream));
+    if (ring && nt > 0) {
+        RKV_HIP(launch_signal(ring->written + layer, (uint64_t)(ring->appends[layer] + 1), stream));
+        ring->appends[layer]++;
+    }
     return RKV_OK;
 }
 

@@ -30,6 +30,7 @@ constexpr int kMaxKvHeads = 64;
 constexpr int kMaxParts = 64;
 
 constexpr int kMaxSegs = 4;         // segments one launch can attend
+constexpr int kRingMaxLayers = 1024;  // layers a tail ring can plan
 
 // One segment of a launch: its K/V base pointers and byte strides, its keys,
 // and the range of workgroups (key splits) that cover it.
@@ -111,6 +112,29 @@ struct CombineParts {
 };
 hipError_t launch_combine(int n_parts, const CombineParts &parts, int64_t n_rows, int d, float *o_out,
                           float *lse_out, hipStream_t stream);
+
+// One destination range of an append: tokens [first_tok, first_tok + n_tok)
+// of the call go to rows row0, row0 + 1, ... of a region (k / v already
+// offset to the call's sequence).
+struct AppendDst {
+    uint8_t *k, *v;
+    int64_t k_pos, v_pos, k_head, v_head;
+    int64_t row0;
+    int32_t k_type, v_type;
+    int32_t first_tok, n_tok;
+};
+
+struct AppendParams {
+    AppendDst dst[3];  // window, tail, device copy of the tail rows (unused entries have n_tok = 0)
+    int32_t n_dst;
+    int32_t n_kv_heads;
+    int32_t sys_fence;  // a destination is host memory: make the rows visible system-wide before the end
+};
+
+// One launch of the append kernel (append.hip): n_tokens x n_kv_heads
+// workgroups; k_new / v_new binary32 [n_tokens][n_kv_heads][d].
+hipError_t launch_append(int d, int n_tokens, int n_kv_heads, const float *k_new, const float *v_new,
+                         const AppendParams &p, hipStream_t stream);
 
 hipError_t launch_dequant_q8_0(const void *blocks, int64_t n_values, float *out, hipStream_t stream);
 hipError_t launch_dequant_q4_0(const void *blocks, int64_t n_values, float *out, hipStream_t stream);

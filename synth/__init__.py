@@ -176,3 +176,33 @@ def make_cache(n_keys: int, n_kv_heads: int, head_dim: int, dtype: int, seed: in
 def make_query(n_seq: int, n_q_heads: int, head_dim: int, seed: int, device="cpu") -> torch.Tensor:
     """Query [n_seq][n_q_heads][head_dim] float32 N(0,1)."""
     return normal((n_seq, n_q_heads, head_dim), seed, device)
+
+
+def append_rows(n_tokens: int, n_kv_heads: int, head_dim: int, seed: int, device="cpu",
+                large: bool = True) -> torch.Tensor:
+    """New K or V rows to append: binary32 [n_tokens][n_kv_heads][head_dim].
+
+    N(0,1) draws, with planted 32-value blocks that exercise the storage
+    rules: zero blocks, blocks scaled by 2^-20 (block scales in binary16's
+    subnormal range) or 2^10, blocks on a quarter grid (many values exactly
+    half-way between codes), and blocks whose largest magnitude occurs twice
+    (same and opposite sign).  Which blocks are planted is drawn from the
+    seed; the values are exact binary32 numbers.  large=False leaves the
+    2^10-scaled blocks at N(0,1) scale (rows for attention checks: an absolute
+    tolerance on O presumes values of order one).
+    """
+    g = generator(seed, "cpu")
+    x = torch.randn(n_tokens, n_kv_heads, head_dim, generator=g, dtype=torch.float32)
+    blocks = x.view(-1, 32)
+    kind = torch.randint(0, 8, (blocks.shape[0],), generator=g)
+    blocks[kind == 1] = 0.0
+    blocks[kind == 2] *= 2.0 ** -20
+    if large:
+        blocks[kind == 3] *= 2.0 ** 10
+    blocks[kind == 4] = torch.round(blocks[kind == 4] * 4) / 4
+    for b in torch.nonzero(kind >= 6).flatten().tolist():
+        i, j = torch.randperm(32, generator=g)[:2].tolist()
+        top = blocks[b].abs().max()
+        blocks[b, i] = top
+        blocks[b, j] = top if kind[b] == 6 else -top
+    return x.to(device)
