@@ -61,7 +61,7 @@ class Oracle:
             f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         L.orc_attend.restype = ctypes.c_int
         L.orc_attend.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                 ctypes.c_double, ctypes.c_double, ctypes.c_void_p,
+                                 ctypes.c_double, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(_View),
                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         L.orc_lse_combine.restype = ctypes.c_int
@@ -95,12 +95,15 @@ class Oracle:
             raise ValueError("n_values must be a multiple of 32")
         return out
 
-    def attend(self, q, views, n_kv_heads: int, scale: float, softcap: float = 0.0, q_to_kv=None, rows=None):
+    def attend(self, q, views, n_kv_heads: int, scale: float, softcap: float = 0.0, q_to_kv=None, rows=None,
+               q_pos=None):
         """Unsplit binary64 attention.
 
         q: float32 [n_seq][n_q_heads][head_dim] (host).  views: list of View
         whose keys are attended together.  rows: optional flattened row
-        indices.  Returns (o float64 [n_rows][head_dim], lse float64 [n_rows]).
+        indices.  q_pos: optional absolute position of each sequence's query
+        (it sees keys 0 .. q_pos[b] of the concatenated views).  Returns
+        (o float64 [n_rows][head_dim], lse float64 [n_rows]).
         """
         q = np.ascontiguousarray(np.asarray(q, dtype=np.float32))
         n_seq, n_q_heads, head_dim = q.shape
@@ -112,8 +115,13 @@ class Oracle:
         m = None
         if q_to_kv is not None:
             m = np.ascontiguousarray(np.asarray(q_to_kv, dtype=np.int32))
+        qp = None
+        if q_pos is not None:
+            qp = np.ascontiguousarray(np.asarray(q_pos, dtype=np.int64))
+            assert qp.shape == (n_seq,)
         rc = self.L.orc_attend(n_seq, n_q_heads, n_kv_heads, head_dim, float(scale), float(softcap),
-                               None if m is None else m.ctypes.data, q.ctypes.data, len(views), arr,
+                               None if m is None else m.ctypes.data, None if qp is None else qp.ctypes.data,
+                               q.ctypes.data, len(views), arr,
                                None if rows_arr is None else rows_arr.ctypes.data, n_rows,
                                o.ctypes.data, lse.ctypes.data)
         if rc != 0:
@@ -193,8 +201,8 @@ def dequant_q4_0(blocks, n_values):
     return default().dequant_q4_0(blocks, n_values)
 
 
-def attend(q, views, n_kv_heads, scale, softcap=0.0, q_to_kv=None, rows=None):
-    return default().attend(q, views, n_kv_heads, scale, softcap, q_to_kv, rows)
+def attend(q, views, n_kv_heads, scale, softcap=0.0, q_to_kv=None, rows=None, q_pos=None):
+    return default().attend(q, views, n_kv_heads, scale, softcap, q_to_kv, rows, q_pos)
 
 
 def lse_combine(o_parts, lse_parts):

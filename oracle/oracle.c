@@ -274,6 +274,13 @@ typedef struct {
     int64_t k_seq_stride, v_seq_stride;
 } orc_view;
 
+/* The causal mask: sequence b's query sees key position t iff t <= q_pos[b]
+ * (every key when there is no mask). */
+static int key_seen(const int64_t *q_pos, int b, int64_t t)
+{
+    return !q_pos || t <= q_pos[b];
+}
+
 /*
  * Unsplit softmax attention of one query token per sequence over the keys of
  * all n_views views taken together (view 0's keys, then view 1's, ...).
@@ -284,10 +291,18 @@ typedef struct {
  *        written for the r-th listed row (or row r when rows is NULL).
  * q_to_kv: optional map query head -> KV head; NULL means contiguous groups
  *        h / (n_q_heads / n_kv_heads).
- * An empty key set gives o = 0 and lse = -inf.
+ * q_pos: optional causal mask by absolute key position ("Rolling-KV:
+ *        step/graph-level tail prefetch (design)", the multi-row batch of a
+ *        prefill chunk or a verify step, whose mask is indexed by absolute
+ *        position with -inf for hidden keys).  Key t of the concatenation
+ *        (t = 0, 1, ... over view 0's keys, then view 1's, ...) sits at
+ *        absolute position t; sequence b's query sits at q_pos[b] and sees
+ *        the keys with t <= q_pos[b].  NULL: every key is seen.
+ * A row that sees no key (an empty key set, or q_pos[b] < 0) gives o = 0 and
+ * lse = -inf.
  */
 int orc_attend(int n_seq, int n_q_heads, int n_kv_heads, int head_dim,
-               double scale, double softcap, const int32_t *q_to_kv,
+               double scale, double softcap, const int32_t *q_to_kv, const int64_t *q_pos,
                const float *q, int n_views, const orc_view *views,
                const int64_t *rows, int64_t n_rows, double *o, double *lse)
 {
@@ -329,6 +344,7 @@ int orc_attend(int n_seq, int n_q_heads, int n_kv_heads, int head_dim,
             const uint8_t *kb = (const uint8_t *)w->k + (int64_t)b * w->k_seq_stride + (int64_t)g * w->k_head_stride;
             for (j = 0; j < w->n_keys; ++j, ++t) {
                 double dot = 0.0;
+                if (!key_seen(q_pos, b, t)) continue; /* hidden key: no score */
                 dequant_row(w->k_type, kb + j * w->k_pos_stride, head_dim, kv);
                 for (d = 0; d < head_dim; ++d) dot += qd[d] * kv[d];
                 s[t] = scale * dot;
@@ -339,23 +355,26 @@ int orc_attend(int n_seq, int n_q_heads, int n_kv_heads, int head_dim,
 
         /* softmax-weighted sum of the value rows */
         for (d = 0; d < head_dim; ++d) acc[d] = 0.0;
+        if (mx == -INFINITY) { /* no key seen */
+            lse[r] = -INFINITY;
+            free(s); free(kv); free(qd);
+            continue;
+        }
         t = 0;
         for (w_i = 0; w_i < n_views; ++w_i) {
             const orc_view *w = &views[w_i];
             const uint8_t *vb = (const uint8_t *)w->v + (int64_t)b * w->v_seq_stride + (int64_t)g * w->v_head_stride;
             for (j = 0; j < w->n_keys; ++j, ++t) {
-                double p = exp(s[t] - mx);
+                double p;
+                if (!key_seen(q_pos, b, t)) continue;
+                p = exp(s[t] - mx);
                 z += p;
                 dequant_row(w->v_type, vb + j * w->v_pos_stride, head_dim, kv);
                 for (d = 0; d < head_dim; ++d) acc[d] += p * kv[d];
             }
         }
-        if (n_total == 0) {
-            lse[r] = -INFINITY;
-        } else {
-            for (d = 0; d < head_dim; ++d) acc[d] /= z;
-            lse[r] = mx + log(z);
-        }
+        for (d = 0; d < head_dim; ++d) acc[d] /= z;
+        lse[r] = mx + log(z);
         free(s); free(kv); free(qd);
     }
     return err;

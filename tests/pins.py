@@ -23,6 +23,9 @@ What pins what:
     the scale (brute force over all codes), and against the round-trip error
     bound through the separately pinned dequantiser; routing against a
     hand-worked table.
+  - the causal mask of several query rows: bit-equality with the unmasked
+    attention over the truncated key set, torch SDPA with a boolean mask,
+    closed forms and pure-Python brute force, and the masked split merge.
 """
 from __future__ import annotations
 
@@ -619,6 +622,109 @@ def pin_split_degenerate(orc):
     e = orc.attend(q, [oracle.view_of(kc, vc, 3, 3)], hkv, 0.2)
     o, l = orc.lse_combine([e[0], e[0]], [e[1], e[1]])
     assert not np.any(o) and np.all(np.isneginf(l))
+
+
+# ----------------------------------------------------------------------------- causal mask (several query rows)
+#
+# Rows of a prefill chunk or a verify step sit at absolute positions; a row at
+# position p sees the keys at positions 0 .. p and no later one ("Rolling-KV:
+# step/graph-level tail prefetch (design)": the multi-row batch is masked by
+# absolute key position, hidden keys at -inf).  Key t of the concatenated
+# views sits at position t.
+
+def _mask_case(seed, n=70, wc=40, hq=8, hkv=2, d=32, kt=synth.Q8_0, vt=synth.F16):
+    kc, vc = host_pair(n, hkv, d, kt, vt, seed)
+    pos = [-1, 0, 5, wc - 1, wc, wc + 1, n - 2, n - 1, n + 30]
+    q = synth.make_query(len(pos), hq, d, synth.stream_seed(seed, 3)).numpy()
+    return kc, vc, q, pos
+
+
+def pin_mask_is_truncation(orc):
+    """A row at position p equals, bit for bit, the unmasked row over keys
+    [0, p] (the seen keys are the same and summed in the same order); p < 0
+    sees nothing (O = 0, LSE = -inf); p >= n sees everything."""
+    n, wc, hq, hkv = 70, 40, 8, 2
+    kc, vc, q, pos = _mask_case(101)
+    views = [oracle.view_of(kc, vc, 0, wc), oracle.view_of(kc, vc, wc, n)]
+    o, lse = orc.attend(q, views, hkv, 0.2, q_pos=pos)
+    for b, p in enumerate(pos):
+        rows = slice(b * hq, (b + 1) * hq)
+        if p < 0:
+            assert not np.any(o[rows]) and np.all(np.isneginf(lse[rows]))
+            continue
+        top = min(p + 1, n)
+        ro, rl = orc.attend(q[b:b + 1], [oracle.view_of(kc, vc, 0, top)], hkv, 0.2)
+        assert np.array_equal(o[rows], ro) and np.array_equal(lse[rows], rl), p
+
+
+def pin_mask_sdpa(orc):
+    """torch SDPA (float64) with a boolean mask of keys t <= p per row."""
+    n, wc, hq, hkv, d = 70, 40, 8, 2, 32
+    kc, vc, q, pos = _mask_case(102, kt=synth.F16, vt=synth.Q4_0)
+    o, lse = orc.attend(q, [oracle.view_of(kc, vc, 0, wc), oracle.view_of(kc, vc, wc, n)], hkv, 0.3, q_pos=pos)
+    kk = torch.from_numpy(values_f64(orc, kc))
+    vv = torch.from_numpy(values_f64(orc, vc))
+    idx = torch.tensor(default_map(hq, hkv))
+    ke = kk[:, idx, :].permute(1, 0, 2).contiguous()
+    ve = vv[:, idx, :].permute(1, 0, 2).contiguous()
+    for b, p in enumerate(pos):
+        if p < 0:
+            continue
+        qb = torch.from_numpy(q[b].astype(np.float64))[:, None, :]
+        mask = (torch.arange(n) <= p)[None, None, :].expand(hq, 1, n)
+        ro = torch.nn.functional.scaled_dot_product_attention(qb, ke, ve, attn_mask=mask, scale=0.3)[:, 0, :]
+        sc = (torch.matmul(qb, ke.transpose(1, 2)) * 0.3)[:, 0, :].masked_fill(~mask[:, 0, :], -math.inf)
+        rl = torch.logsumexp(sc, dim=-1)
+        rows = slice(b * hq, (b + 1) * hq)
+        assert close(o[rows], ro.numpy(), 1e-10, 1e-12) and close(lse[rows], rl.numpy()), p
+
+
+def pin_mask_closed_form_and_brute_force(orc):
+    """p = 0: O = v_0 and LSE = s_0 exactly; tiny random cases against a
+    pure-Python sum (no max shift, math.fsum) over the keys t <= p."""
+    rng = np.random.default_rng(12)
+    for trial in range(6):
+        n = int(rng.integers(2, 12))
+        hkv, g, d = int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 7))
+        k = rng.standard_normal((n, hkv, d)).astype(np.float32)
+        v = rng.standard_normal((n, hkv, d)).astype(np.float32)
+        pos = [0] + [int(rng.integers(0, n)) for _ in range(3)]
+        q = rng.standard_normal((len(pos), hkv * g, d)).astype(np.float32)
+        scale = float(rng.uniform(0.1, 1.5))
+        kc = synth.Cache(torch.from_numpy(k), synth.F32, n, hkv, d)
+        vc = synth.Cache(torch.from_numpy(v), synth.F32, n, hkv, d)
+        o, lse = orc.attend(q, [oracle.view_of(kc, vc)], hkv, scale, q_pos=pos)
+        for b, p in enumerate(pos):
+            for h in range(hkv * g):
+                r, kv = b * hkv * g + h, h // g
+                s = [scale * math.fsum(float(q[b, h, i]) * float(k[j, kv, i]) for i in range(d)) for j in range(p + 1)]
+                if p == 0:
+                    assert np.array_equal(o[r], v[0, kv].astype(np.float64))
+                    assert abs(lse[r] - s[0]) <= 1e-15 * max(1.0, abs(s[0]))
+                e = [math.exp(x) for x in s]
+                z = math.fsum(e)
+                assert abs(lse[r] - math.log(z)) <= 1e-12 * max(1.0, abs(math.log(z)))
+                for i in range(d):
+                    ref = math.fsum(e[j] * float(v[j, kv, i]) for j in range(p + 1)) / z
+                    assert abs(o[r, i] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def pin_mask_split_merge(orc):
+    """Masked window and tail attended apart (the tail's keys start at
+    position wc, so its rows see t <= p - wc) and merged equal the masked
+    unsplit attention; a row before the tail gets a hidden tail (weight 0)
+    and the window's result exactly."""
+    n, wc, hq, hkv = 70, 40, 8, 2
+    kc, vc, q, pos = _mask_case(103)
+    full = orc.attend(q, [oracle.view_of(kc, vc)], hkv, 0.2, q_pos=pos)
+    w = orc.attend(q, [oracle.view_of(kc, vc, 0, wc)], hkv, 0.2, q_pos=pos)
+    t = orc.attend(q, [oracle.view_of(kc, vc, wc, n)], hkv, 0.2, q_pos=[p - wc for p in pos])
+    o, l = orc.lse_combine([w[0], t[0]], [w[1], t[1]])
+    assert close(o, full[0]) and close(l, full[1])
+    for b, p in enumerate(pos):
+        rows = slice(b * hq, (b + 1) * hq)
+        if p < wc:
+            assert np.all(np.isneginf(t[1][rows])) and np.array_equal(o[rows], w[0][rows])
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

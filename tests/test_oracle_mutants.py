@@ -50,6 +50,11 @@ MUTANTS = {
     "route_window_edge": ("if (pos < window_cap) {", "if (pos <= window_cap) {"),
     "route_tail_row": ("*row = pos - window_cap;", "*row = pos;"),
     "route_tail_edge": ("if (pos - window_cap < tail_cap) {", "if (pos - window_cap <= tail_cap) {"),
+    # causal mask
+    "mask_strict": ("return !q_pos || t <= q_pos[b];", "return !q_pos || t < q_pos[b];"),
+    "mask_first_seq": ("return !q_pos || t <= q_pos[b];", "return !q_pos || t <= q_pos[0];"),
+    "mask_ignored_in_values": ("if (!key_seen(q_pos, b, t)) continue;\n                p = exp",
+                               "p = exp"),
 }
 
 
