@@ -346,6 +346,31 @@ def other_workloads(P, synth, reps=20):
     del inst
     torch.cuda.empty_cache()
 
+    # Several query rows under the causal mask: a verify step of 8 draft tokens
+    # (positions 65528 .. 65535) over the 40/8-head, head_dim 128 f16 cache of
+    # 65536 keys (window 49152 + tail 16384, one launch); two instances
+    # alternated.  Bytes: the K/V read once.
+    Hq, Hkv, D, n, wc, nq = 40, 8, 128, 65536, 49152, 8
+    inst = [(synth.make_cache(n, Hkv, D, synth.F16, synth.stream_seed(2, 1, i), dev),
+             synth.make_cache(n, Hkv, D, synth.F16, synth.stream_seed(2, 2, i), dev)) for i in range(2)]
+    q = synth.make_query(nq, Hq, D, synth.stream_seed(2, 9), dev)
+    d = P.Desc(nq, Hq, Hkv, D, 1 / math.sqrt(D), q_pos=list(range(n - nq, n)))
+    segs = [[P.view_of_cache(kc, vc, 0, wc), P.view_of_cache(kc, vc, wc, n)] for kc, vc in inst]
+    ws = P.workspace(P.rkv_attend_split_workspace_bytes(d, segs[0]))
+    o, l = torch.empty(nq, Hq, D, device=dev), torch.empty(nq, Hq, device=dev)
+    k = [0]
+
+    def ver():
+        P.rkv_attend_split(d, q, segs[k[0] % 2], o, l, ws)
+        k[0] += 1
+    t = timed(ver)
+    b = 2 * n * Hkv * D * 2
+    res["verify_8_rows_f16"] = {"us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1),
+                                "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4), "bytes": b,
+                                "rows_per_kv_head": nq * Hq // Hkv}
+    del inst, segs
+    torch.cuda.empty_cache()
+
     # The write path: new binary32 rows quantised on append (q8_0 K, q4_0 V),
     # 8 KV heads x head_dim 128.  decode: one token into each of 48 layers'
     # windows (latency per call); prefill: a 4096-token chunk that crosses from

@@ -95,6 +95,11 @@ typedef struct rkv_kv_view {
     int64_t k_pos_stride, v_pos_stride;
     int64_t k_head_stride, v_head_stride;
     int64_t k_seq_stride, v_seq_stride;
+    /* Absolute position of the view's first key: key j of the view sits at
+     * position pos0 + j.  Read only by a call whose descriptor carries query
+     * positions (q_pos); a window view of positions [0, wc) has pos0 = 0,
+     * its tail pos0 = wc. */
+    int64_t pos0;
 } rkv_kv_view;
 
 /* ---- the attention problem ------------------------------------------------
@@ -104,7 +109,17 @@ typedef struct rkv_kv_view {
  *     s_j = scale * (q . k_j),  then  s_j = softcap * tanh(s_j / softcap)  if softcap > 0,
  * and the softmax and LSE are taken over the final s_j.  Limits:
  * head_dim in {64, 128, 256, 512}; n_q_heads <= 256; n_kv_heads <= 64;
- * n_seq * n_q_heads <= 65535. */
+ * n_seq * n_q_heads <= 65535.
+ *
+ * Several query rows of one sequence -- a prefill chunk or the draft tokens
+ * of a verify step ("Rolling-KV: step/graph-level tail prefetch (design)": a
+ * multi-row batch over the split cache, masked by absolute key position with
+ * -inf for hidden keys) -- are passed as n_seq "sequences" over views with
+ * sequence stride 0, each with its position in q_pos: the row at position p
+ * sees the keys at absolute positions <= p (a key's absolute position is the
+ * view's pos0 plus its index).  A row that sees no key of a call gets o = 0
+ * and lse = -inf, the empty-segment result, so that the segment merge gives it
+ * weight 0.  With q_pos, n_seq <= 64. */
 typedef struct rkv_attn_desc {
     int32_t n_seq;
     int32_t n_q_heads;
@@ -113,6 +128,7 @@ typedef struct rkv_attn_desc {
     float scale;
     float softcap;          /* 0 = off */
     const int32_t *q_to_kv; /* host array of n_q_heads, or NULL */
+    const int64_t *q_pos;   /* host array of n_seq (absolute query positions), or NULL: no mask */
 } rkv_attn_desc;
 
 /* Workspace bytes rkv_attend_segment needs for this problem and segment

@@ -42,6 +42,7 @@ class rkv_kv_view(ctypes.Structure):
         ("k_pos_stride", ctypes.c_int64), ("v_pos_stride", ctypes.c_int64),
         ("k_head_stride", ctypes.c_int64), ("v_head_stride", ctypes.c_int64),
         ("k_seq_stride", ctypes.c_int64), ("v_seq_stride", ctypes.c_int64),
+        ("pos0", ctypes.c_int64),
     ]
 
 
@@ -50,6 +51,7 @@ class rkv_attn_desc(ctypes.Structure):
         ("n_seq", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
         ("q_to_kv", ctypes.POINTER(ctypes.c_int32)),
+        ("q_pos", ctypes.POINTER(ctypes.c_int64)),
     ]
 
 
@@ -133,23 +135,28 @@ def row_bytes(dtype: int, head_dim: int) -> int:
 
 
 def make_view(k, v, k_type: int, v_type: int, n_keys: int, k_pos_stride: int, v_pos_stride: int,
-              k_head_stride: int, v_head_stride: int, k_seq_stride: int = 0, v_seq_stride: int = 0) -> rkv_kv_view:
-    """A segment view; k / v are tensors or raw addresses (bytes)."""
+              k_head_stride: int, v_head_stride: int, k_seq_stride: int = 0, v_seq_stride: int = 0,
+              pos0: int = 0) -> rkv_kv_view:
+    """A segment view; k / v are tensors or raw addresses (bytes); pos0 is the
+    absolute position of its first key (used by masked calls)."""
     return rkv_kv_view(_addr(k), _addr(v), k_type, v_type, n_keys, k_pos_stride, v_pos_stride,
-                       k_head_stride, v_head_stride, k_seq_stride, v_seq_stride)
+                       k_head_stride, v_head_stride, k_seq_stride, v_seq_stride, pos0)
 
 
 class Desc:
     """rkv_attn_desc plus the storage of its head map."""
 
     def __init__(self, n_seq: int, n_q_heads: int, n_kv_heads: int, head_dim: int, scale: float,
-                 softcap: float = 0.0, q_to_kv=None):
-        self._map = None
-        mp = None
+                 softcap: float = 0.0, q_to_kv=None, q_pos=None):
+        self._map = self._pos = None
+        mp = pp = None
         if q_to_kv is not None:
             self._map = (ctypes.c_int32 * n_q_heads)(*[int(x) for x in q_to_kv])
             mp = ctypes.cast(self._map, ctypes.POINTER(ctypes.c_int32))
-        self.c = rkv_attn_desc(n_seq, n_q_heads, n_kv_heads, head_dim, scale, softcap, mp)
+        if q_pos is not None:
+            self._pos = (ctypes.c_int64 * n_seq)(*[int(x) for x in q_pos])
+            pp = ctypes.cast(self._pos, ctypes.POINTER(ctypes.c_int64))
+        self.c = rkv_attn_desc(n_seq, n_q_heads, n_kv_heads, head_dim, scale, softcap, mp, pp)
 
     @property
     def n_rows(self) -> int:
@@ -274,13 +281,14 @@ def rkv_append_kv(n_kv_heads: int, head_dim: int, n_tokens: int, pos0: int, seq:
 
 
 def view_of_cache(kc, vc, start: int = 0, stop: int | None = None, k_seq_stride: int = 0,
-                  v_seq_stride: int = 0) -> rkv_kv_view:
+                  v_seq_stride: int = 0, pos0: int | None = None) -> rkv_kv_view:
     """View of positions [start, stop) of a pair of position-major caches
-    (objects with .data, .dtype, .pos_stride, .head_stride, .n_keys)."""
+    (objects with .data, .dtype, .pos_stride, .head_stride, .n_keys); its
+    first key sits at absolute position pos0 (default: start)."""
     stop = kc.n_keys if stop is None else stop
     return make_view(kc.data.data_ptr() + start * kc.pos_stride, vc.data.data_ptr() + start * vc.pos_stride,
                      kc.dtype, vc.dtype, stop - start, kc.pos_stride, vc.pos_stride, kc.head_stride,
-                     vc.head_stride, k_seq_stride, v_seq_stride)
+                     vc.head_stride, k_seq_stride, v_seq_stride, start if pos0 is None else pos0)
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

@@ -74,6 +74,8 @@ int check_desc(const rkv_attn_desc *d)
     if ((int64_t)d->n_seq * d->n_q_heads > 65535) return fail(RKV_E_UNSUPPORTED, "n_seq * n_q_heads > 65535");
     if (!(d->scale == d->scale) || !(d->softcap >= 0.f) || d->softcap == INFINITY)
         return fail(RKV_E_INVAL, "scale must be a number and softcap finite >= 0");
+    if (d->q_pos && d->n_seq > kMaxMaskSeqs)
+        return fail(RKV_E_UNSUPPORTED, "query positions for at most %d sequences", kMaxMaskSeqs);
     if (d->q_to_kv) {
         for (int h = 0; h < d->n_q_heads; ++h)
             if (d->q_to_kv[h] < 0 || d->q_to_kv[h] >= d->n_kv_heads)
@@ -96,6 +98,7 @@ int check_view_fields(const rkv_attn_desc *d, const rkv_kv_view *v)
     if (!valid_type(v->k_type) || !valid_type(v->v_type)) return fail(RKV_E_INVAL, "bad K/V type");
     if (v->n_keys < 0) return fail(RKV_E_INVAL, "n_keys < 0");
     if (v->n_keys > ((int64_t)1 << 40)) return fail(RKV_E_UNSUPPORTED, "n_keys too large");
+    if (v->pos0 < 0 || v->pos0 > ((int64_t)1 << 40)) return fail(RKV_E_INVAL, "pos0 must be in [0, 2^40]");
     if (v->n_keys == 0) return RKV_OK;
     if (!v->k || !v->v) return fail(RKV_E_INVAL, "K or V pointer is NULL");
     const int D = d->head_dim;
@@ -155,6 +158,10 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
     // 64-key tiles, a multiple of the waves per KV head.  A workgroup takes
     // as many KV heads (a power of two) as it has waves, so that it reads whole
     // spans of each position's heads; the rest of its waves split the tiles.
+    if (d->q_pos)
+        for (int i = 0; i < n; ++i)
+            if (v[i]->n_keys >= ((int64_t)1 << 30))
+                return fail(RKV_E_UNSUPPORTED, "a masked call takes segments of fewer than 2^30 keys");
     int64_t tiles_total = 0;
     for (int i = 0; i < n; ++i) tiles_total += (v[i]->n_keys + kTile - 1) / kTile;
     const int nw = std::max(1, split_waves(kt, vt, D, rt));
@@ -198,6 +205,7 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
             sp.k_seq = shared ? 0 : v[i]->k_seq_stride;
             sp.v_seq = shared ? 0 : v[i]->v_seq_stride;
             sp.n_keys = v[i]->n_keys;
+            sp.pos0 = v[i]->pos0;
             sp.keys_per_split = (int32_t)(tps * kTile);
             sp.split_base = (int32_t)n_splits;
         }
@@ -225,6 +233,11 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
         while ((1 << wl) < wph) ++wl;
         prm->hpw_log2 = hl;
         prm->wph_log2 = wl;
+        prm->n_q_heads = Hq;
+        prm->masked = d->q_pos != nullptr;
+        if (d->q_pos)
+            for (int b = 0; b < S; ++b)  // (clamped so that position differences stay far from overflow)
+                prm->qpos[b] = std::min<int64_t>(std::max<int64_t>(d->q_pos[b], -1), (int64_t)1 << 42);
         for (int g = 0; g < Hkv; ++g) {
             prm->rowcnt[g] = (uint16_t)rows[g].size();
             for (size_t i = 0; i < rows[g].size(); ++i) prm->rowtab[g * rmax + i] = (uint16_t)rows[g][i];
@@ -848,6 +861,7 @@ int rkv_stream_tail(rkv_ring *r, int layer, const rkv_attn_desc *desc, const flo
         v.k = r->sk[s];
         v.v = r->sv[s];
         v.n_keys = r->items[j].nk;
+        v.pos0 = tail.pos0 + r->items[j].k0;
         v.k_seq_stride = 0;
         v.v_seq_stride = 0;
         // A failure from here on aborts the step (later calls: RKV_E_STATE),

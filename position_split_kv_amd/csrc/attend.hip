@@ -183,7 +183,9 @@ rkv_reduce_kernel(const float *__restrict__ part_acc, const float2 *__restrict__
             s.z += sA[j][c].z;
             s.w += sA[j][c].w;
         }
-        *(float4 *)(o + row * D + d0) = make_float4(s.x / L, s.y / L, s.z / L, s.w / L);
+        // a row that saw no key in any split: o = 0, lse = -inf
+        *(float4 *)(o + row * D + d0) = L > 0.f ? make_float4(s.x / L, s.y / L, s.z / L, s.w / L)
+                                                : make_float4(0.f, 0.f, 0.f, 0.f);
         if (blockIdx.y == 0 && c == 0) lse[row] = (M + log2f(L)) * 0.69314718055994531f;
     }
 }

@@ -931,8 +931,8 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     const int64_t kbeg = (int64_t)((int)blockIdx.x - sg.split_base) * sg.keys_per_split;
     // (with dim slices every wave walks the same tiles, rows or not: the slices
     // meet at a barrier per tile)
-    const int64_t kend = (nr == 0 && DS == 1) ? kbeg
-                         : kbeg + sg.keys_per_split < sg.n_keys ? kbeg + sg.keys_per_split : sg.n_keys;
+    int64_t kend = (nr == 0 && DS == 1) ? kbeg
+                   : kbeg + sg.keys_per_split < sg.n_keys ? kbeg + sg.keys_per_split : sg.n_keys;
     const int64_t tstep = (int64_t)wph * kTile;  // tile stride of this wave
 
     const int gr = g < p.n_kv_heads ? g : p.n_kv_heads - 1;  // a slot past the heads reads a real one
@@ -961,6 +961,26 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         rid[r] = nr == 0 ? 0 : tabrow[rr];
         qp[r] = q + rid[r] * DF + js * D;
     }
+    // Causal mask (masked launches): row r sees the keys of the segment with
+    // index <= lim[r] (its sequence's query position minus the segment's
+    // first position); without a mask every key.  A wave (without dim slices)
+    // walks no tile that none of its rows sees.
+    // (32-bit: a masked launch has segments of fewer than 2^30 keys, and the
+    // limits are clamped to [-1, 2^30])
+    constexpr int kSeeAll = 1 << 30;
+    int lim[RT];
+    int lim_max = -1;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        int x = kSeeAll;
+        if (p.masked) {
+            const int64_t rel = p.qpos[rid[r] / p.n_q_heads] - sg.pos0;
+            x = rel < -1 ? -1 : rel > kSeeAll ? kSeeAll : (int)rel;
+        }
+        lim[r] = x;
+        if (r < nr) lim_max = x > lim_max ? x : lim_max;
+    }
+    if (DS == 1 && p.masked && kend > kbeg + lim_max + 1) kend = kbeg + lim_max + 1 > kbeg ? kbeg + lim_max + 1 : kbeg;
 
     float m[RT], l[RT], acc[RT][8];
 #pragma unroll
@@ -1172,6 +1192,16 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             lrow[i] = 0.f;
         }
     }
+    // limit of the row of each of the lane's MFMA outputs (rows 4*(lane/16) + i)
+    int limv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * (lane >> 4) + i;
+        int x = kSeeAll;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) x = row == r ? lim[r] : x;
+        limv[i] = x;
+    }
     for (; t0 < kend; t0 += tstep) {
         const int nk = nk_at(t0);
         const int64_t tn = t0 + tstep;
@@ -1250,24 +1280,38 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 }
                 __syncthreads();  // every slice has read the partials before P overwrites them
             }
+            // last key of the tile each output row sees
+            int kmx[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kmx[i] = nk - 1;
+            if (p.masked) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tl = limv[i] - (int)t0;
+                    kmx[i] = tl < nk - 1 ? (tl < -1 ? -1 : tl) : nk - 1;
+                }
+            }
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const bool valid = 16 * kb + (lane & 15) < nk;
+                const int key = 16 * kb + (lane & 15);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float x = sv[kb][i];
                     if (cap > 0.f) x = capl * tanhf(x * inv_capl);
-                    sv[kb][i] = valid ? x : -INFINITY;
+                    sv[kb][i] = key <= kmx[i] ? x : -INFINITY;
                 }
             }
             // ---- online softmax: per-lane rows, then the wave-uniform rescale
-            float al[4];
+            // (a row that has seen no key yet keeps m = -inf, l = 0: its
+            // exponents are taken against 0 so that they give 0, not NaN)
+            float al[4], mex[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float mx = fmaxf(fmaxf(sv[0][i], sv[1][i]), fmaxf(sv[2][i], sv[3][i]));
                 mx = row16_max(mx);
                 const float mn = fmaxf(mrow[i], mx);
-                al[i] = __builtin_amdgcn_exp2f(mrow[i] - mn);
+                mex[i] = mn == -INFINITY ? 0.f : mn;
+                al[i] = __builtin_amdgcn_exp2f(mrow[i] - mex[i]);
                 lrow[i] *= al[i];
                 mrow[i] = mn;
             }
@@ -1295,7 +1339,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 float ps = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    const float pv = __builtin_amdgcn_exp2f(sv[kb][i] - mrow[i]);
+                    const float pv = __builtin_amdgcn_exp2f(sv[kb][i] - mex[i]);
                     ps += pv;
                     const int key = 16 * kb + (lane & 15);
                     const int at = MFMA_O ? (key & 3) * 16 + (key >> 2) : key;
@@ -1308,7 +1352,6 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         float s[RT];
         if constexpr (KDMA) key_dots<KT, D, RT, true>(sK, qp, s, lane, sw);
         else key_dots<KT, D, RT>(sK + lane * LSK, qp, s);
-        const bool valid = lane < nk;
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             float x;
@@ -1316,7 +1359,10 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 x = cap * tanhf(s[r] * scale_over_cap) * kLog2e;
             else
                 x = s[r] * sl2;
-            s[r] = valid ? x : -INFINITY;
+            // last key of the tile row r sees (wave-uniform)
+            const int tl = lim[r] - (int)t0;
+            const int kmr = tl < nk - 1 ? (tl < -1 ? -1 : tl) : nk - 1;
+            s[r] = lane <= kmr ? x : -INFINITY;
         }
 
         // ---- online softmax update (rescale only when a row's max moved)
@@ -1330,7 +1376,8 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
                 m[r] = mn;
             }
-            const float pr = __builtin_amdgcn_exp2f(s[r] - m[r]);
+            // (a row that has seen no key yet has m = -inf and gets 0)
+            const float pr = m[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[r] - m[r]);
             l[r] += pr;
             sP[w][r * kTile + lane] = pr;
         }
@@ -1529,7 +1576,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 if (rr < 0) continue;
                 float v[8];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) v[c] = single ? oc[c][i] / lr : oc[c][i];
+                for (int c = 0; c < 8; ++c) v[c] = single ? (lr > 0.f ? oc[c][i] / lr : 0.f) : oc[c][i];
                 float *dst = (single ? o_out + (int64_t)rr * DF : part_acc + (pbase + rr) * DF) + js * D;
                 *(float4 *)(dst + 8 * (lane & 15)) = make_float4(v[0], v[1], v[2], v[3]);
                 *(float4 *)(dst + 8 * (lane & 15) + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -1617,7 +1664,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             A = fmaf(mA[(ww * RT + r) * D + d], f, A);
         }
         if (single) {
-            o_out[(int64_t)rr * D + d] = A / L;
+            o_out[(int64_t)rr * D + d] = L > 0.f ? A / L : 0.f;  // a row that saw no key: o = 0, lse = -inf
             if (d == 0) lse_out[rr] = (M + log2f(L)) * 0.69314718055994531f;
         } else {
             part_acc[(pbase + rr) * D + d] = A;

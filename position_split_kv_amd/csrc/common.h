@@ -30,6 +30,7 @@ constexpr int kMaxKvHeads = 64;
 constexpr int kMaxParts = 64;
 
 constexpr int kMaxSegs = 4;         // segments one launch can attend
+constexpr int kMaxMaskSeqs = 64;    // sequences (query rows) of a call with query positions
 constexpr int kRingMaxLayers = 1024;  // layers a tail ring can plan
 
 // One segment of a launch: its K/V base pointers and byte strides, its keys,
@@ -38,6 +39,7 @@ struct SegParams {
     const uint8_t *k, *v;
     int64_t k_pos, v_pos, k_head, v_head, k_seq, v_seq;
     int64_t n_keys;
+    int64_t pos0;        // absolute position of the segment's first key (masked launches)
     int32_t keys_per_split;
     int32_t split_base;  // first grid x index of this segment
 };
@@ -57,6 +59,9 @@ struct SplitParams {
     int32_t n_kv_heads;
     int32_t hpw_log2;      // log2 of the KV heads per workgroup
     int32_t wph_log2;      // log2 of the waves per KV head (waves per workgroup / heads per workgroup)
+    int32_t n_q_heads;     // sequence of output row r: r / n_q_heads
+    int32_t masked;        // qpos holds the absolute query position of each sequence
+    int64_t qpos[kMaxMaskSeqs];
     uint16_t rowcnt[kMaxKvHeads];
     uint16_t rowtab[kMaxRowTable];
 };
