@@ -539,10 +539,23 @@ def streamed_tail(P, synth, sweep=False, L=48, steps=3):
         t_c, t_d, t_p = (statistics.median(times[m]) for m in ("resident", "copy", "stream"))
         tail_bytes = L * tail_keys * (kc0.pos_stride + vc0.pos_stride)
         h = min(1.0, max(0.0, (t_c + t_d - t_p) / t_d))
+        # The residency planner on the measured terms: the device memory this
+        # layout uses (L windows + a 3-slot ring), the measured link rate and
+        # per-layer compute, the FFN weights the step reads; its window, tile,
+        # slots and bounded-win prediction beside the measurement.
+        bpk = kc0.pos_stride + vc0.pos_stride
+        plan = P.rkv_plan_residency(L, wc + tail_keys, bpk, L * wc * bpk + 3 * tile_keys * bpk,
+                                    L * 14336 * 4096 * 2, HBM_PEAK_GBS * 1e9, r_link * 1e9, 0.0, 0.0, t_c / L)
         return {"tail_keys": tail_keys, "tile_keys": tile_keys, "reps": reps, "T_c_ms": round(t_c * 1e3, 3),
                 "T_d_ms": round(t_d * 1e3, 3), "T_p_ms": round(t_p * 1e3, 3), "tail_hidden_fraction": round(h, 4),
                 "tail_GBs": round(tail_bytes / t_p / 1e9, 2), "link_fraction": round(tail_bytes / t_p / 1e9 / r_link, 4),
-                "free_zone_keys_per_layer": round(t_c * r_link * 1e9 / L / (kc0.pos_stride + vc0.pos_stride))}
+                "free_zone_keys_per_layer": round(t_c * r_link * 1e9 / L / bpk),
+                "planner": {"window_keys": plan["window_keys"], "tail_keys": plan["tail_keys"],
+                            "tile_keys": plan["tile_keys"], "n_slots": plan["n_slots"],
+                            "tactic": ["resident", "stream", "quantize"][plan["tactic"]],
+                            "predicted_step_ms": round(plan["predicted_step_s"] * 1e3, 3),
+                            "predicted_hidden": round(plan["predicted_hidden"], 4),
+                            "t_star_MB": round(plan["t_star_bytes"] / 1e6, 1)}}
 
     log(f"streamed: FFN stand-in {reps} x GEMV ({t_gemv * 1e6:.1f} us each); pinned H2D {r_link:.1f} GB/s")
     main = measure(n - wc, tile)

@@ -346,6 +346,75 @@ int rkv_append_kv(int n_kv_heads, int head_dim, int n_tokens, int64_t pos0, int 
                   const float *v_new, const rkv_kv_view *window, const rkv_kv_view *tail, const rkv_kv_view *fresh,
                   rkv_ring *ring, int layer, hipStream_t stream);
 
+/* ---- residency planner (host only) ----------------------------------------
+ * rkv_plan_residency -- choose, for a decode step over n_layers layers of
+ * n_kv positions, the window (positions per layer kept in device memory),
+ * the tail tile and the ring's slot count, and estimate what streaming the
+ * tail costs.  Pure host arithmetic in binary64 on measured inputs; no GPU
+ * call.  The steps:
+ *  - bw_eff = min(link_bw, host_ram_bw), host_ram_bw <= 0 meaning unknown
+ *    ("T*-aware auto rolling-KV spill", T* section: the host-to-device rate
+ *    is bound by the slower of the link and the host memory read).
+ *  - The whole cache within kv_budget_bytes: RKV_RESIDENT, window = n_kv
+ *    ("F5 M7 -- Rolling KV", runtime tactic table: a layer that fits stays
+ *    hot).
+ *  - Otherwise tile_keys = floor(compute_s_per_layer * bw_eff * safety /
+ *    bytes_per_key) (>= 1, "F5 M7 -- Rolling KV", section "Slot pool"); the
+ *    window is what the budget holds after two slots; a tail of more than 63
+ *    tiles per layer grows the tile (one combine merges the window and at most
+ *    63 tiles) and the window is sized again; n_slots = clamp(budget left /
+ *    slot bytes, 2, 4).
+ *  - t_resident = (weights_bytes + whole KV) / vram_bw; drop = (c_engage_s +
+ *    tail bytes / bw_eff) / t_resident; T* = (target_drop * t_resident -
+ *    c_engage_s) * bw_eff ("T*-aware auto rolling-KV spill", T* section).  A
+ *    tail of at most T* bytes (all layers): RKV_STREAM; more: RKV_QUANTIZE (the
+ *    spill costs more than the target drop; a smaller cache type should be
+ *    chosen).
+ *  - predicted_step_s = max(step compute, tail DMA) + c_engage_s, free zone =
+ *    step compute * bw_eff, predicted_hidden = min(compute, DMA) / DMA ("F5
+ *    M7 -- Rolling KV", section "Bounded win").
+ * Units: bytes, bytes per second, seconds.  Errors: RKV_E_INVAL (NULL,
+ * non-positive or non-finite rates, a budget below two slots of one
+ * position); the message is rkv_plan_last_error().
+ */
+enum { RKV_RESIDENT = 0, RKV_STREAM = 1, RKV_QUANTIZE = 2 };
+enum { RKV_LINK_BOUND = 0, RKV_HOST_RAM_BOUND = 1 };
+
+typedef struct rkv_residency_in {
+    int32_t n_layers;
+    int64_t n_kv;               /* positions per layer */
+    int64_t bytes_per_key;      /* K + V bytes of one position of one layer, all KV heads, stored types */
+    int64_t kv_budget_bytes;    /* device memory for the windows and the ring slots */
+    int64_t weights_bytes;      /* other bytes a step reads from device memory (active weights) */
+    double vram_bw;             /* device memory read rate, bytes/s */
+    double link_bw;             /* pinned host-to-device copy rate, bytes/s (measured) */
+    double host_ram_bw;         /* host memory read rate, bytes/s; <= 0 unknown */
+    double c_engage_s;          /* fixed cost per step of engaging the split path, s (measured) */
+    double compute_s_per_layer; /* one layer's step time with its window resident, s (measured) */
+    double target_drop;         /* tolerated throughput drop of a spill, e.g. 0.20 */
+    double safety;              /* tile sizing safety factor in (0, 1], e.g. 0.8 */
+} rkv_residency_in;
+
+typedef struct rkv_residency_plan {
+    int32_t tactic;       /* RKV_RESIDENT, RKV_STREAM or RKV_QUANTIZE */
+    int32_t binding;      /* RKV_LINK_BOUND or RKV_HOST_RAM_BOUND */
+    int64_t window_keys;  /* positions per layer in device memory */
+    int64_t tail_keys;    /* positions per layer in the tail */
+    int64_t tile_keys;    /* positions per ring tile (0 without a tail) */
+    int32_t n_slots;      /* ring slots (0 without a tail) */
+    double bw_eff;        /* binding host-to-device rate, bytes/s */
+    double t_resident_s;  /* step time with the whole cache resident (model) */
+    double t_star_bytes;  /* tolerable tail bytes at target_drop (<= 0: never spill) */
+    double drop;          /* modelled throughput drop of this plan's tail */
+    double free_zone_bytes;
+    double predicted_step_s;
+    double predicted_hidden; /* fraction of the tail DMA hidden under compute */
+} rkv_residency_plan;
+
+int rkv_plan_residency(const rkv_residency_in *in, rkv_residency_plan *out);
+/* Message of the last failing rkv_plan_residency call on this thread. */
+const char *rkv_plan_last_error(void);
+
 #ifdef __cplusplus
 }
 #endif

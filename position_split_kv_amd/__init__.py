@@ -25,7 +25,10 @@ EXPORTS = (
     "rkv_lse_combine", "rkv_dequant_q8_0", "rkv_dequant_q4_0", "rkv_ring_create", "rkv_ring_destroy",
     "rkv_ring_begin_step", "rkv_stream_tail_workspace_bytes", "rkv_stream_tail", "rkv_ring_end_step",
     "rkv_ring_schedule", "rkv_attend_split", "rkv_attend_split_workspace_bytes", "rkv_append_kv",
+    "rkv_plan_residency", "rkv_plan_last_error",
 )
+RKV_RESIDENT, RKV_STREAM, RKV_QUANTIZE = 0, 1, 2
+RKV_LINK_BOUND, RKV_HOST_RAM_BOUND = 0, 1
 
 
 class RkvError(RuntimeError):
@@ -52,6 +55,27 @@ class rkv_attn_desc(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
         ("q_to_kv", ctypes.POINTER(ctypes.c_int32)),
         ("q_pos", ctypes.POINTER(ctypes.c_int64)),
+    ]
+
+
+class rkv_residency_in(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("n_kv", ctypes.c_int64), ("bytes_per_key", ctypes.c_int64),
+        ("kv_budget_bytes", ctypes.c_int64), ("weights_bytes", ctypes.c_int64),
+        ("vram_bw", ctypes.c_double), ("link_bw", ctypes.c_double), ("host_ram_bw", ctypes.c_double),
+        ("c_engage_s", ctypes.c_double), ("compute_s_per_layer", ctypes.c_double),
+        ("target_drop", ctypes.c_double), ("safety", ctypes.c_double),
+    ]
+
+
+class rkv_residency_plan(ctypes.Structure):
+    _fields_ = [
+        ("tactic", ctypes.c_int32), ("binding", ctypes.c_int32),
+        ("window_keys", ctypes.c_int64), ("tail_keys", ctypes.c_int64), ("tile_keys", ctypes.c_int64),
+        ("n_slots", ctypes.c_int32),
+        ("bw_eff", ctypes.c_double), ("t_resident_s", ctypes.c_double), ("t_star_bytes", ctypes.c_double),
+        ("drop", ctypes.c_double), ("free_zone_bytes", ctypes.c_double), ("predicted_step_s", ctypes.c_double),
+        ("predicted_hidden", ctypes.c_double),
     ]
 
 
@@ -93,10 +117,14 @@ def lib() -> ctypes.CDLL:
         L.rkv_append_kv.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, ctypes.c_int, vp, vp,
                                     ctypes.POINTER(rkv_kv_view), ctypes.POINTER(rkv_kv_view),
                                     ctypes.POINTER(rkv_kv_view), vp, ctypes.c_int, vp]
+        L.rkv_plan_residency.argtypes = [ctypes.POINTER(rkv_residency_in), ctypes.POINTER(rkv_residency_plan)]
+        L.rkv_plan_last_error.restype = ctypes.c_char_p
+        L.rkv_plan_last_error.argtypes = []
         L.rkv_ring_schedule.restype = i64
         L.rkv_ring_schedule.argtypes = [ctypes.c_int, ctypes.POINTER(i64), ctypes.c_int, i64, vp, vp, vp, vp]
         for name in EXPORTS:
-            if name not in ("rkv_status_string", "rkv_last_error", "rkv_row_bytes", "rkv_ring_schedule"):
+            if name not in ("rkv_status_string", "rkv_last_error", "rkv_row_bytes", "rkv_ring_schedule",
+                            "rkv_plan_last_error"):
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -316,3 +344,17 @@ def attend(desc: Desc, q: torch.Tensor, seg: rkv_kv_view, stream=None, ws: torch
         ws = workspace(rkv_attend_workspace_bytes(desc, seg), q.device)
     rkv_attend_segment(desc, q, seg, o, lse, ws, stream)
     return o, lse
+
+
+def rkv_plan_residency(n_layers: int, n_kv: int, bytes_per_key: int, kv_budget_bytes: int, weights_bytes: int,
+                       vram_bw: float, link_bw: float, host_ram_bw: float, c_engage_s: float,
+                       compute_s_per_layer: float, target_drop: float = 0.20, safety: float = 0.8) -> dict:
+    """The residency plan (host arithmetic, no GPU) as a dict of the
+    rkv_residency_plan fields."""
+    i = rkv_residency_in(n_layers, n_kv, bytes_per_key, kv_budget_bytes, weights_bytes, vram_bw, link_bw,
+                         host_ram_bw, c_engage_s, compute_s_per_layer, target_drop, safety)
+    o = rkv_residency_plan()
+    code = lib().rkv_plan_residency(ctypes.byref(i), ctypes.byref(o))
+    if code != RKV_OK:
+        raise RkvError(code, lib().rkv_plan_last_error().decode())
+    return {name: getattr(o, name) for name, _ in rkv_residency_plan._fields_}

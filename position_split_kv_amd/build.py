@@ -42,7 +42,7 @@ def _units():
         for vt in range(4):
             units.append((os.path.join(CSRC, "attend_inst.hip"), os.path.join(BUILD, f"attend_k{kt}_v{vt}.o"),
                           [f"-DRKV_KT={kt}", f"-DRKV_VT={vt}"]))
-    for name in ("attend", "combine", "dequant", "append", "api"):
+    for name in ("attend", "combine", "dequant", "append", "plan", "api"):
         units.append((os.path.join(CSRC, f"{name}.hip"), os.path.join(BUILD, f"{name}.o"), []))
     return units
 
