@@ -449,10 +449,14 @@ def streamed_tail(P, synth, sweep=False, L=48, steps=3):
     torch.cuda.synchronize()
     t_gemv = e0.elapsed_time(e1) * 1e-3 / 20
     reps = max(1, round(200e-6 / t_gemv))
+    reps_ffn = reps
 
+    # every GEMV of the stand-in reads a different matrix, as the calibration
+    # did (a matrix read again right after would come from the last-level
+    # cache and the FFN would be shorter than the 0.2 ms it stands for)
     def ffn(li):
-        for _ in range(reps):
-            torch.mv(W[li], x)
+        for r in range(reps):
+            torch.mv(W[(li * reps + r) % L], x)
 
     # pinned H2D rate (256 MiB, non-blocking stream)
     cs = torch.cuda.Stream()
@@ -545,7 +549,8 @@ def streamed_tail(P, synth, sweep=False, L=48, steps=3):
         # slots and bounded-win prediction beside the measurement.
         bpk = kc0.pos_stride + vc0.pos_stride
         plan = P.rkv_plan_residency(L, wc + tail_keys, bpk, L * wc * bpk + 3 * tile_keys * bpk,
-                                    L * 14336 * 4096 * 2, HBM_PEAK_GBS * 1e9, r_link * 1e9, 0.0, 0.0, t_c / L)
+                                    L * reps_ffn * 14336 * 4096 * 2, HBM_PEAK_GBS * 1e9, r_link * 1e9, 0.0, 0.0,
+                                    t_c / L)
         return {"tail_keys": tail_keys, "tile_keys": tile_keys, "reps": reps, "T_c_ms": round(t_c * 1e3, 3),
                 "T_d_ms": round(t_d * 1e3, 3), "T_p_ms": round(t_p * 1e3, 3), "tail_hidden_fraction": round(h, 4),
                 "tail_GBs": round(tail_bytes / t_p / 1e9, 2), "link_fraction": round(tail_bytes / t_p / 1e9 / r_link, 4),
