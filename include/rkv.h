@@ -180,6 +180,25 @@ int rkv_attend_split(const rkv_attn_desc *desc, const float *q, int n_segments, 
                      float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The two phases of rkv_attend_split as separate calls, for callers that
+ * time them or put other work between them:
+ *   rkv_attend_split_partials  the attention kernel: every key split writes
+ *       its partial (running max, denominator, weighted sum) into ws, in a
+ *       layout of the library's own; when the launch has a single split, or
+ *       no keys at all, the final o / lse are written here instead.
+ *   rkv_attend_split_merge  the fixed-order merge of those partials into o /
+ *       lse (nothing to do in the single-split and no-key cases).
+ * Called in this order on one stream with the same desc, segments (the same
+ * sizes and types) and workspace, they enqueue exactly what rkv_attend_split
+ * enqueues and give the same bits.  ws must not be reused in between.
+ * Arguments and errors as for rkv_attend_split (the merge takes no query).
+ */
+int rkv_attend_split_partials(const rkv_attn_desc *desc, const float *q, int n_segments, const rkv_kv_view *segs,
+                              float *o, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+int rkv_attend_split_merge(const rkv_attn_desc *desc, int n_segments, const rkv_kv_view *segs, float *o, float *lse,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * rkv_lse_combine -- merge per-segment results ("F5 M7 -- Rolling KV",
  * "Implementation decomposition, refined", S2):
  *     M = max_t lse_t;  w_t = e^{lse_t - M};

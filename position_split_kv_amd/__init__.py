@@ -25,7 +25,7 @@ EXPORTS = (
     "rkv_lse_combine", "rkv_dequant_q8_0", "rkv_dequant_q4_0", "rkv_ring_create", "rkv_ring_destroy",
     "rkv_ring_begin_step", "rkv_stream_tail_workspace_bytes", "rkv_stream_tail", "rkv_ring_end_step",
     "rkv_ring_schedule", "rkv_attend_split", "rkv_attend_split_workspace_bytes", "rkv_append_kv",
-    "rkv_plan_residency", "rkv_plan_last_error",
+    "rkv_plan_residency", "rkv_plan_last_error", "rkv_attend_split_partials", "rkv_attend_split_merge",
 )
 RKV_RESIDENT, RKV_STREAM, RKV_QUANTIZE = 0, 1, 2
 RKV_LINK_BOUND, RKV_HOST_RAM_BOUND = 0, 1
@@ -104,6 +104,10 @@ def lib() -> ctypes.CDLL:
                                                        ctypes.POINTER(rkv_kv_view), ctypes.POINTER(sz)]
         L.rkv_attend_split.argtypes = [ctypes.POINTER(rkv_attn_desc), vp, ctypes.c_int, ctypes.POINTER(rkv_kv_view),
                                        vp, vp, vp, sz, vp]
+        L.rkv_attend_split_partials.argtypes = [ctypes.POINTER(rkv_attn_desc), vp, ctypes.c_int,
+                                                ctypes.POINTER(rkv_kv_view), vp, vp, vp, sz, vp]
+        L.rkv_attend_split_merge.argtypes = [ctypes.POINTER(rkv_attn_desc), ctypes.c_int, ctypes.POINTER(rkv_kv_view),
+                                             vp, vp, vp, sz, vp]
         L.rkv_lse_combine.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i32, vp, vp, vp]
         L.rkv_dequant_q8_0.argtypes = [vp, i64, vp, vp]
         L.rkv_dequant_q4_0.argtypes = [vp, i64, vp, vp]
@@ -222,6 +226,20 @@ def rkv_attend_split(desc: Desc, q: torch.Tensor, segs, o: torch.Tensor, lse: to
     arr = _segs(segs)
     _check(lib().rkv_attend_split(ctypes.byref(desc.c), _addr(q), len(segs), arr, _addr(o), _addr(lse), _addr(ws),
                                   ws_bytes, _stream(stream)))
+
+
+def rkv_attend_split_partials(desc: Desc, q: torch.Tensor, segs, o: torch.Tensor, lse: torch.Tensor,
+                              ws: torch.Tensor | None, stream=None) -> None:
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().rkv_attend_split_partials(ctypes.byref(desc.c), _addr(q), len(segs), _segs(segs), _addr(o),
+                                           _addr(lse), _addr(ws), ws_bytes, _stream(stream)))
+
+
+def rkv_attend_split_merge(desc: Desc, segs, o: torch.Tensor, lse: torch.Tensor, ws: torch.Tensor | None,
+                           stream=None) -> None:
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().rkv_attend_split_merge(ctypes.byref(desc.c), len(segs), _segs(segs), _addr(o), _addr(lse),
+                                        _addr(ws), ws_bytes, _stream(stream)))
 
 
 def rkv_lse_combine(o_parts, lse_parts, o_out: torch.Tensor, lse_out: torch.Tensor, head_dim: int,

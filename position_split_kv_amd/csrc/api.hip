@@ -250,14 +250,17 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
 // validated).  All segments empty: o = 0, lse = -inf.
 // done (optional): host-visible memory that receives done_value once the
 // launch has finished reading its keys.
+// phase: 0 the whole launch; 1 the split kernel alone (partials in ws, or o /
+// lse directly when the plan has one split or no keys); 2 the merge alone.
 int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view *const *v, float *o, float *lse,
-                void *ws, size_t ws_bytes, hipStream_t stream, uint64_t *done = nullptr, uint64_t done_value = 0)
+                void *ws, size_t ws_bytes, hipStream_t stream, uint64_t *done = nullptr, uint64_t done_value = 0,
+                int phase = 0)
 {
     const int64_t n_rows = (int64_t)d->n_seq * d->n_q_heads;
     int64_t keys = 0;
     for (int i = 0; i < n; ++i) keys += v[i]->n_keys;
     if (keys == 0) {
-        RKV_HIP(launch_fill_empty(d->head_dim, n_rows, o, lse, stream));
+        if (phase != 2) RKV_HIP(launch_fill_empty(d->head_dim, n_rows, o, lse, stream));
         if (done) RKV_HIP(launch_signal(done, done_value, stream));
         return RKV_OK;
     }
@@ -273,7 +276,8 @@ int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view
     float *part_acc = (float *)ws;
     float2 *part_ml = (float2 *)((char *)ws + pl.acc_bytes);
     const dim3 grid((unsigned)pl.n_splits, (unsigned)(pl.n_hg * pl.n_rg), (unsigned)pl.z);
-    RKV_HIP(launch_split(kt, vt, d->head_dim, pl.rt, grid, q, part_acc, part_ml, o, lse, prm, stream));
+    if (phase != 2) RKV_HIP(launch_split(kt, vt, d->head_dim, pl.rt, grid, q, part_acc, part_ml, o, lse, prm, stream));
+    if (phase == 1) return RKV_OK;
     if (pl.n_splits > 1)
         RKV_HIP(launch_reduce(d->head_dim, n_rows, pl.n_splits, part_acc, part_ml, o, lse, stream, done, done_value));
     else if (done)
@@ -373,14 +377,18 @@ int rkv_attend_split_workspace_bytes(const rkv_attn_desc *desc, int n_segments, 
     return RKV_OK;
 }
 
-int rkv_attend_split(const rkv_attn_desc *desc, const float *q, int n_segments, const rkv_kv_view *segs, float *o,
-                     float *lse, void *ws, size_t ws_bytes, hipStream_t stream)
+// rkv_attend_split and its two phases: validation, then the launch (phase as
+// for attend_impl; the merge phase reads no query).
+static int attend_split_phase(const rkv_attn_desc *desc, const float *q, int n_segments, const rkv_kv_view *segs,
+                              float *o, float *lse, void *ws, size_t ws_bytes, hipStream_t stream, int phase)
 {
     int rc = check_desc(desc);
     if (rc) return rc;
     if ((rc = check_segs(desc, n_segments, segs))) return rc;
-    if ((rc = check_out_args(q, o, lse))) return rc;
-    if ((rc = check_device(q, "q")) || (rc = check_device(o, "o")) || (rc = check_device(lse, "lse"))) return rc;
+    static const float kDummy[4] __attribute__((aligned(16))) = {};
+    if ((rc = check_out_args(phase == 2 ? kDummy : q, o, lse))) return rc;
+    if ((phase != 2 && (rc = check_device(q, "q"))) || (rc = check_device(o, "o")) || (rc = check_device(lse, "lse")))
+        return rc;
     for (int i = 0; i < n_segments; ++i)
         if (segs[i].n_keys > 0 && ((rc = check_device(segs[i].k, "K")) || (rc = check_device(segs[i].v, "V"))))
             return rc;
@@ -390,7 +398,25 @@ int rkv_attend_split(const rkv_attn_desc *desc, const float *q, int n_segments, 
     int nz = 0;
     while (nz < n_segments - 1 && segs[nz].n_keys == 0) ++nz;
     std::swap(vp[0], vp[nz]);
-    return attend_impl(desc, q, n_segments, vp, o, lse, ws, ws_bytes, stream);
+    return attend_impl(desc, q, n_segments, vp, o, lse, ws, ws_bytes, stream, nullptr, 0, phase);
+}
+
+int rkv_attend_split(const rkv_attn_desc *desc, const float *q, int n_segments, const rkv_kv_view *segs, float *o,
+                     float *lse, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return attend_split_phase(desc, q, n_segments, segs, o, lse, ws, ws_bytes, stream, 0);
+}
+
+int rkv_attend_split_partials(const rkv_attn_desc *desc, const float *q, int n_segments, const rkv_kv_view *segs,
+                              float *o, float *lse, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return attend_split_phase(desc, q, n_segments, segs, o, lse, ws, ws_bytes, stream, 1);
+}
+
+int rkv_attend_split_merge(const rkv_attn_desc *desc, int n_segments, const rkv_kv_view *segs, float *o, float *lse,
+                           void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return attend_split_phase(desc, nullptr, n_segments, segs, o, lse, ws, ws_bytes, stream, 2);
 }
 
 int rkv_attend_workspace_bytes(const rkv_attn_desc *desc, const rkv_kv_view *seg, size_t *bytes)

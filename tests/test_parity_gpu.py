@@ -313,3 +313,26 @@ def test_attend_split_mixed_types_rejected():
     with pytest.raises(P.RkvError) as e:
         P.attend_split(desc, q, [P.view_of_cache(a, b), P.view_of_cache(c, d)], ws=P.workspace(1 << 20))
     assert e.value.code == P.RKV_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kt,vt,n,wc,D,Hq,Hkv", [
+    (synth.F16, synth.F16, 20000, 15000, 128, 40, 8),   # many splits: partials then the merge
+    (synth.Q8_0, synth.Q4_0, 3000, 0, 128, 40, 8),      # an empty window
+    (synth.Q8_0, synth.Q8_0, 5000, 3000, 512, 16, 2),   # dim slices
+    (synth.F16, synth.F16, 40, 20, 128, 8, 2),          # one split: o / lse written by the first phase
+])
+def test_split_phases_equal_one_call(kt, vt, n, wc, D, Hq, Hkv):
+    """rkv_attend_split_partials then rkv_attend_split_merge give the bits of
+    rkv_attend_split."""
+    note(f"split phases: K={kt} V={vt} n={n} wc={wc} D={D} Hq={Hq} Hkv={Hkv}")
+    kc, vc = pair(n, Hkv, D, kt, vt, 61, DEV)
+    q = synth.make_query(1, Hq, D, 62, DEV)
+    desc = P.Desc(1, Hq, Hkv, D, default_scale(D))
+    segs = [P.view_of_cache(kc, vc, 0, wc), P.view_of_cache(kc, vc, wc, n)]
+    o1, l1 = P.attend_split(desc, q, segs)
+    ws = P.workspace(P.rkv_attend_split_workspace_bytes(desc, segs))
+    o2, l2 = torch.full_like(o1, float("nan")), torch.full_like(l1, float("nan"))
+    P.rkv_attend_split_partials(desc, q, segs, o2, l2, ws)
+    P.rkv_attend_split_merge(desc, segs, o2, l2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
