@@ -94,6 +94,16 @@ __device__ __forceinline__ float h2f(uint32_t bits)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xffffu));
 }
 
+// tanh(y) from the identity tanh(y) = 1 - 2 / (e^(2y) + 1), given
+// two_y_log2 = 2y log2(e): one hardware exp2, one reciprocal, no branches.
+// e^(2y) overflowing to +inf gives 1, underflowing to 0 gives -1.  The
+// absolute error is a few units of 2^-24 (the softcap scales it by the cap).
+__device__ __forceinline__ float tanh_from_exp2(float two_y_log2)
+{
+    const float t = __builtin_amdgcn_exp2f(two_y_log2);
+    return fmaf(-2.f, __builtin_amdgcn_rcpf(t + 1.f), 1.f);
+}
+
 __device__ __forceinline__ float sbyte(uint32_t w, int k) { return (float)(int)(int8_t)(uint8_t)(w >> (8 * k)); }
 
 __device__ __forceinline__ float nib(uint32_t w, int shift) { return (float)((int)((w >> shift) & 0xfu) - 8); }
@@ -1030,7 +1040,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     rkv_half8 qhi[NKQ], qlo[NKQ];
     float mrow[4], lrow[4];
     const float capl = cap * kLog2e;                  // cap in log2 units
-    const float inv_capl = cap > 0.f ? 1.f / capl : 0.f;
+    const float two_over_cap = cap > 0.f ? 2.f / cap : 0.f;
 
     // Software pipelining of the tile stream: when the raw rows of a tile fit
     // in registers, the loads of tile i+1's K (and block-type V) rows are
@@ -1297,7 +1307,8 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float x = sv[kb][i];
-                    if (cap > 0.f) x = capl * tanhf(x * inv_capl);
+                    // (x in log2 units: s/c = x/capl, and 2 (s/c) log2 e = x * 2/c)
+                    if (cap > 0.f) x = capl * tanh_from_exp2(x * two_over_cap);
                     sv[kb][i] = key <= kmx[i] ? x : -INFINITY;
                 }
             }
@@ -1356,7 +1367,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         for (int r = 0; r < RT; ++r) {
             float x;
             if (cap > 0.f)
-                x = cap * tanhf(s[r] * scale_over_cap) * kLog2e;
+                x = cap * tanh_from_exp2(s[r] * scale_over_cap * (2.f * kLog2e)) * kLog2e;
             else
                 x = s[r] * sl2;
             // last key of the tile row r sees (wave-uniform)
