@@ -68,11 +68,17 @@ struct Shape {
     static constexpr bool V_REG = (VT == kF16 && D <= 128) || (VT == kF32 && D <= 64);
     static constexpr int LSV = V_REG ? 0 : lds_row_dwords(RBV);
     static constexpr int STAGE_DW = kTile * (LSK + LSV) + 8;  // per wave: K (+ V) rows plus read slack
+    // With K rows by DMA and V rows in registers, a wave's K tile is not
+    // needed between its scores and the next tile's DMA (issued after P.V),
+    // so the score rows P of the tile live there (up to 16 rows of 64 keys).
+    static constexpr bool P_IN_K = KDMA && V_REG;
+    static_assert(!P_IN_K || LSK >= 16, "the K tile holds 16 score rows");
     // LDS bytes of a workgroup of nw waves with rt rows each: the staging
     // areas (reused for the final merge) and the score rows
     static constexpr int lds_bytes(int nw, int rt)
     {
-        return 4 * (nw * STAGE_DW > nw * rt * (D + 2) ? nw * STAGE_DW : nw * rt * (D + 2)) + 4 * nw * rt * kTile;
+        return 4 * (nw * STAGE_DW > nw * rt * (D + 2) ? nw * STAGE_DW : nw * rt * (D + 2)) +
+               (P_IN_K ? 0 : 4 * nw * rt * kTile);
     }
     // waves per workgroup: as many (up to 8) as fit 160 KiB of LDS
     static constexpr int waves(int rt)
@@ -912,13 +918,15 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     constexpr int SMEM_DW = NW * Sh::STAGE_DW > MERGE_DW ? NW * Sh::STAGE_DW : MERGE_DW;
 
     __shared__ __attribute__((aligned(16))) uint32_t smem[SMEM_DW];
-    __shared__ __attribute__((aligned(16))) float sP[NW][RTX * kTile];
+    __shared__ __attribute__((aligned(16))) float sP[NW][Sh::P_IN_K ? 4 : RTX * kTile];
     __shared__ int sRow[NW][RT];  // output row of each wave's rows (-1: none), for the epilogue
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform in the wave
     uint32_t *sK = smem + w * Sh::STAGE_DW;
     uint32_t *sV = sK + kTile * LSK;
+    // this wave's score rows P [row][key] (in its K tile when that is free)
+    float *const sPw = Sh::P_IN_K ? (float *)sK : &sP[w][0];
 
     // this wave's head slot hs and its index ws among the head's waves
     const int hg = blockIdx.y / p.n_rg;
@@ -1354,7 +1362,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                     ps += pv;
                     const int key = 16 * kb + (lane & 15);
                     const int at = MFMA_O ? (key & 3) * 16 + (key >> 2) : key;
-                    if (row < RT) sP[w][row * kTile + at] = pv;
+                    if (row < RT) sPw[row * kTile + at] = pv;
                 }
                 lrow[i] += ps;
             }
@@ -1390,7 +1398,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             // (a row that has seen no key yet has m = -inf and gets 0)
             const float pr = m[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[r] - m[r]);
             l[r] += pr;
-            sP[w][r * kTile + lane] = pr;
+            sPw[r * kTile + lane] = pr;
         }
         }
         // the next tile's K (and block-type V) rows load during this tile's P.V
@@ -1415,8 +1423,8 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             for (int kb = 0; kb < 2; ++kb) {
                 rkv_half8 ph, pl;
                 if (qi < RT) {
-                    const float4 a = *(const float4 *)&sP[w][qi * kTile + gq * 16 + 8 * kb];
-                    const float4 b = *(const float4 *)&sP[w][qi * kTile + gq * 16 + 8 * kb + 4];
+                    const float4 a = *(const float4 *)&sPw[qi * kTile + gq * 16 + 8 * kb];
+                    const float4 b = *(const float4 *)&sPw[qi * kTile + gq * 16 + 8 * kb + 4];
                     const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -1473,8 +1481,8 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             for (int kb = 0; kb < 2; ++kb) {
                 rkv_half8 ph, pl;
                 if (qi < RT) {
-                    const float4 a = *(const float4 *)&sP[w][qi * kTile + gq * 16 + 8 * kb];
-                    const float4 b = *(const float4 *)&sP[w][qi * kTile + gq * 16 + 8 * kb + 4];
+                    const float4 a = *(const float4 *)&sPw[qi * kTile + gq * 16 + 8 * kb];
+                    const float4 b = *(const float4 *)&sPw[qi * kTile + gq * 16 + 8 * kb + 4];
                     const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -1527,7 +1535,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             }
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
-                const float pw = (VT == kQ8 || VT == kQ4) ? sP[w][r * kTile + key] * dsc : sP[w][r * kTile + key];
+                const float pw = (VT == kQ8 || VT == kQ4) ? sPw[r * kTile + key] * dsc : sPw[r * kTile + key];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pw, x[e], acc[r][e]);
             }
