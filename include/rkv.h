@@ -162,11 +162,15 @@ int rkv_attend_segment(const rkv_attn_desc *desc, const float *q, const rkv_kv_v
  * KV", header note: window [0, wc) and tail [wc, n_kv) attended separately
  * and merged; the result equals softmax attention over all their keys).
  * This is the window + tail (+ tail tiles) step of one layer as a single
- * kernel; rkv_attend_segment is the case n_segments == 1.
+ * call; rkv_attend_segment is the case n_segments == 1.
  *
- *   segs  1..4 views sharing one K type and one V type (else
- *         RKV_E_UNSUPPORTED: attend them separately and use rkv_lse_combine),
- *         all shared by every sequence or all per sequence.  Empty segments
+ *   segs  1..4 views.  Segments of one K type, one V type and one sequence
+ *         sharing (all shared by every sequence, or all per sequence) go to
+ *         one launch of the attention kernel; segments that differ in these
+ *         -- a window and a tail stored at different types ("F5 M7 -- Rolling
+ *         KV", "2026-07-12 -- #582-P2 SHIPPED": each segment read at its own
+ *         type), a shared prefix and private suffixes -- get one launch per
+ *         group, all writing one set of partials, merged once.  Empty segments
  *         are allowed; if every segment is empty o = 0 and lse = -inf.
  *   q, o, lse, ws, stream: as for rkv_attend_segment.
  *

@@ -220,6 +220,8 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
     if (prm) {
         prm->n_segs = ns;
         prm->n_splits = pl->n_splits;
+        prm->split_off = 0;
+        prm->n_splits_all = pl->n_splits;
         prm->n_rg = pl->n_rg;
         prm->rows_per_g = rmax;
         prm->n_rows_total = (int32_t)pl->n_rows_total;
@@ -246,12 +248,69 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
     return RKV_OK;
 }
 
-// Enqueue one launch over segments of one (K, V) type pair (arguments already
-// validated).  All segments empty: o = 0, lse = -inf.
+// The non-empty segments of a call, grouped by what one launch of the split
+// kernel takes: the same K and V types and the same sequence sharing (kept
+// in the caller's order, groups in order of first appearance).
+struct SegGroups {
+    int n = 0;
+    int size[kMaxSegs] = {};
+    const rkv_kv_view *v[kMaxSegs][kMaxSegs] = {};
+};
+
+void group_segs(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SegGroups *g)
+{
+    bool shared[kMaxSegs];
+    for (int i = 0; i < n; ++i) {
+        if (v[i]->n_keys == 0) continue;
+        const bool sh = d->n_seq == 1 || v[i]->k_seq_stride == 0;
+        int j = 0;
+        while (j < g->n && !(g->v[j][0]->k_type == v[i]->k_type && g->v[j][0]->v_type == v[i]->v_type &&
+                             shared[j] == sh))
+            ++j;
+        if (j == g->n) shared[g->n++] = sh;
+        g->v[j][g->size[j]++] = v[i];
+    }
+}
+
+// Plans of every launch of a call and the partial workspace they share:
+// launch j writes its splits at split_off[j] among n_splits_all partials,
+// which one merge reduces.
+struct CallPlan {
+    SegGroups g;
+    SplitPlan pl[kMaxSegs];
+    int n_splits_all = 0;
+    size_t acc_bytes = 0, ml_bytes = 0, ws_bytes = 0;
+};
+
+int make_call_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, CallPlan *cp, SplitParams *prm)
+{
+    group_segs(d, n, v, &cp->g);
+    int off = 0;
+    for (int j = 0; j < cp->g.n; ++j) {
+        int rc = make_plan(d, cp->g.size[j], cp->g.v[j], &cp->pl[j], prm ? &prm[j] : nullptr);
+        if (rc) return rc;
+        if (prm) prm[j].split_off = off;
+        off += cp->pl[j].n_splits;
+    }
+    if (off > 65535) return fail(RKV_E_UNSUPPORTED, "segments too long for one call");
+    cp->n_splits_all = off;
+    if (prm)
+        for (int j = 0; j < cp->g.n; ++j) prm[j].n_splits_all = off;
+    const int64_t rows = (int64_t)d->n_seq * d->n_q_heads;
+    cp->acc_bytes = off > 1 ? ((size_t)off * rows * d->head_dim * sizeof(float) + 255) & ~(size_t)255 : 0;
+    cp->ml_bytes = off > 1 ? (size_t)off * rows * sizeof(float2) : 0;
+    cp->ws_bytes = cp->acc_bytes + cp->ml_bytes;
+    return RKV_OK;
+}
+
+// Enqueue the work of one call over up to kMaxSegs segments (arguments already
+// validated): one split-kernel launch per group of segments (same K / V types
+// and sequence sharing), all writing into one set of per-split partials, then
+// one fixed-order merge.  All segments empty: o = 0, lse = -inf.
 // done (optional): host-visible memory that receives done_value once the
-// launch has finished reading its keys.
-// phase: 0 the whole launch; 1 the split kernel alone (partials in ws, or o /
-// lse directly when the plan has one split or no keys); 2 the merge alone.
+// launches have finished reading their keys.
+// phase: 0 the whole call; 1 the split kernels alone (partials in ws, or o /
+// lse directly when the call has one split or no keys); 2 the merge alone.
 int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view *const *v, float *o, float *lse,
                 void *ws, size_t ws_bytes, hipStream_t stream, uint64_t *done = nullptr, uint64_t done_value = 0,
                 int phase = 0)
@@ -264,22 +323,28 @@ int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view
         if (done) RKV_HIP(launch_signal(done, done_value, stream));
         return RKV_OK;
     }
-    SplitPlan pl;
-    SplitParams prm;
-    int rc = make_plan(d, n, v, &pl, &prm);
+    CallPlan cp;
+    SplitParams prm[kMaxSegs];
+    int rc = make_call_plan(d, n, v, &cp, prm);
     if (rc) return rc;
-    if (pl.ws_bytes && (ws_bytes < pl.ws_bytes || !ws))
-        return fail(RKV_E_INVAL, "workspace too small: %zu < %zu", ws_bytes, pl.ws_bytes);
-    const int kt = v[0]->k_type, vt = v[0]->v_type;
-    if (!split_supported(kt, vt, d->head_dim, pl.rt))
-        return fail(RKV_E_UNSUPPORTED, "no kernel for this (type, head_dim, rows)");
+    if (cp.ws_bytes && (ws_bytes < cp.ws_bytes || !ws))
+        return fail(RKV_E_INVAL, "workspace too small: %zu < %zu", ws_bytes, cp.ws_bytes);
+    for (int j = 0; j < cp.g.n; ++j)
+        if (!split_supported(cp.g.v[j][0]->k_type, cp.g.v[j][0]->v_type, d->head_dim, cp.pl[j].rt))
+            return fail(RKV_E_UNSUPPORTED, "no kernel for this (type, head_dim, rows)");
     float *part_acc = (float *)ws;
-    float2 *part_ml = (float2 *)((char *)ws + pl.acc_bytes);
-    const dim3 grid((unsigned)pl.n_splits, (unsigned)(pl.n_hg * pl.n_rg), (unsigned)pl.z);
-    if (phase != 2) RKV_HIP(launch_split(kt, vt, d->head_dim, pl.rt, grid, q, part_acc, part_ml, o, lse, prm, stream));
+    float2 *part_ml = (float2 *)((char *)ws + cp.acc_bytes);
+    if (phase != 2)
+        for (int j = 0; j < cp.g.n; ++j) {
+            const SplitPlan &pl = cp.pl[j];
+            const dim3 grid((unsigned)pl.n_splits, (unsigned)(pl.n_hg * pl.n_rg), (unsigned)pl.z);
+            RKV_HIP(launch_split(cp.g.v[j][0]->k_type, cp.g.v[j][0]->v_type, d->head_dim, pl.rt, grid, q, part_acc,
+                                 part_ml, o, lse, prm[j], stream));
+        }
     if (phase == 1) return RKV_OK;
-    if (pl.n_splits > 1)
-        RKV_HIP(launch_reduce(d->head_dim, n_rows, pl.n_splits, part_acc, part_ml, o, lse, stream, done, done_value));
+    if (cp.n_splits_all > 1)
+        RKV_HIP(launch_reduce(d->head_dim, n_rows, cp.n_splits_all, part_acc, part_ml, o, lse, stream, done,
+                              done_value));
     else if (done)
         RKV_HIP(launch_signal(done, done_value, stream));
     return RKV_OK;
@@ -299,7 +364,8 @@ int check_device(const void *p, const char *name)
     return RKV_OK;
 }
 
-// Segments of one launch must share K and V types and sequence sharing.
+// The segments of one call: each view valid (segments of different types or
+// sharing are grouped into separate launches).
 int check_segs(const rkv_attn_desc *d, int n, const rkv_kv_view *segs)
 {
     if (n < 1 || n > kMaxSegs) return fail(RKV_E_INVAL, "n_segments must be in [1, %d]", kMaxSegs);
@@ -307,19 +373,6 @@ int check_segs(const rkv_attn_desc *d, int n, const rkv_kv_view *segs)
     int rc;
     for (int i = 0; i < n; ++i)
         if ((rc = check_view_fields(d, &segs[i]))) return rc;
-    int first = -1;
-    for (int i = 0; i < n; ++i) {
-        if (segs[i].n_keys == 0) continue;
-        if (first < 0) {
-            first = i;
-            continue;
-        }
-        const rkv_kv_view &a = segs[first], &b = segs[i];
-        if (a.k_type != b.k_type || a.v_type != b.v_type)
-            return fail(RKV_E_UNSUPPORTED, "segments of one launch must share K and V types");
-        if (d->n_seq > 1 && ((a.k_seq_stride == 0) != (b.k_seq_stride == 0)))
-            return fail(RKV_E_INVAL, "segments of one launch must all be shared or all per sequence");
-    }
     return RKV_OK;
 }
 
@@ -366,14 +419,10 @@ int rkv_attend_split_workspace_bytes(const rkv_attn_desc *desc, int n_segments, 
         *bytes = 0;
         return RKV_OK;
     }
-    // take the types from a non-empty segment
-    int nz = 0;
-    while (segs[nz].n_keys == 0) ++nz;
-    std::swap(vp[0], vp[nz]);
-    SplitPlan pl;
-    rc = make_plan(desc, n_segments, vp, &pl, nullptr);
+    CallPlan cp;
+    rc = make_call_plan(desc, n_segments, vp, &cp, nullptr);
     if (rc) return rc;
-    *bytes = pl.ws_bytes;
+    *bytes = cp.ws_bytes;
     return RKV_OK;
 }
 
@@ -395,9 +444,6 @@ static int attend_split_phase(const rkv_attn_desc *desc, const float *q, int n_s
     if (ws && (rc = check_device(ws, "workspace"))) return rc;
     const rkv_kv_view *vp[kMaxSegs];
     for (int i = 0; i < n_segments; ++i) vp[i] = &segs[i];
-    int nz = 0;
-    while (nz < n_segments - 1 && segs[nz].n_keys == 0) ++nz;
-    std::swap(vp[0], vp[nz]);
     return attend_impl(desc, q, n_segments, vp, o, lse, ws, ws_bytes, stream, nullptr, 0, phase);
 }
 

@@ -1580,8 +1580,8 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             // the wave writes its rows straight from the MFMA output layout
             // (lane (g, n) holds dims 8n .. 8n+7 of rows 4g .. 4g+3).  The
             // values are those the LDS merge would produce for one wave.
-            const bool single = p.n_splits == 1;
-            const int64_t pbase = (int64_t)blockIdx.x * p.n_rows_total;
+            const bool single = p.n_splits_all == 1;
+            const int64_t pbase = (int64_t)(p.split_off + (int)blockIdx.x) * p.n_rows_total;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * (lane >> 4) + i;
@@ -1611,7 +1611,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 }
                 if (rr >= 0) {
                     if (single) lse_out[rr] = (mr + log2f(lr)) * 0.69314718055994531f;
-                    else part_ml[(int64_t)rr * p.n_splits + blockIdx.x] = make_float2(mr, lr);
+                    else part_ml[(int64_t)rr * p.n_splits_all + p.split_off + blockIdx.x] = make_float2(mr, lr);
                 }
             }
             return;
@@ -1664,8 +1664,8 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     }
     // Thread t finalises (head slot, row, dim) triples, merging the waves of
     // the head slot; a wave with no keys has m = -inf and weight 0.
-    const bool single = p.n_splits == 1;
-    const int64_t pbase = (int64_t)blockIdx.x * p.n_rows_total;
+    const bool single = p.n_splits_all == 1;
+    const int64_t pbase = (int64_t)(p.split_off + (int)blockIdx.x) * p.n_rows_total;
     const int hpw = 1 << p.hpw_log2;
     for (int i = threadIdx.x; i < hpw * RT * D; i += 64 * NW) {
         const int h = i / (RT * D);
@@ -1687,7 +1687,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             if (d == 0) lse_out[rr] = (M + log2f(L)) * 0.69314718055994531f;
         } else {
             part_acc[(pbase + rr) * D + d] = A;
-            if (d == 0) part_ml[(int64_t)rr * p.n_splits + blockIdx.x] = make_float2(M, L);
+            if (d == 0) part_ml[(int64_t)rr * p.n_splits_all + p.split_off + blockIdx.x] = make_float2(M, L);
         }
     }
 }

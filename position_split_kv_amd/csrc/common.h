@@ -49,6 +49,8 @@ struct SplitParams {
     SegParams seg[kMaxSegs];
     int32_t n_segs;
     int32_t n_splits;      // total key splits over all segments (grid x)
+    int32_t split_off;     // index of this launch's first split among all partials of the call
+    int32_t n_splits_all;  // partials of the call (all its launches); 1: the result is written directly
     int32_t n_rg;          // row groups per KV head
     int32_t rows_per_g;    // stride of rowtab between KV heads
     int32_t n_rows_total;  // n_seq * n_q_heads

@@ -195,11 +195,13 @@ def test_shared_prefix_batch():
     prefix = P.view_of_cache(pk, pv)
     suffix = P.view_of_cache(sk, sv, 0, nsuf, nsuf * sk.pos_stride, nsuf * sv.pos_stride)
     o, l = attend_views(desc, q, [prefix, suffix])
+    o1, l1 = P.attend_split(desc, q, [prefix, suffix])  # one call: two launches, one merge
     torch.cuda.synchronize()
     pkh, pvh, skh, svh = pk.to("cpu"), pv.to("cpu"), sk.to("cpu"), sv.to("cpu")
     views = [oracle.view_of(pkh, pvh), oracle.view_of(skh, svh, 0, nsuf, nsuf * sk.pos_stride, nsuf * sv.pos_stride)]
     o_ref, l_ref = oracle.attend(q.cpu().numpy(), views, Hkv, default_scale(D))
     compare(o, l, o_ref, l_ref, what="prefix+suffix")
+    compare(o1, l1, o_ref, l_ref, what="prefix+suffix, one call")
 
 
 @pytest.mark.parametrize("D", [256, 512])
@@ -216,11 +218,13 @@ def test_shared_prefix_dim_slices(D):
     prefix = P.view_of_cache(pk, pv)
     suffix = P.view_of_cache(sk, sv, 0, nsuf, nsuf * sk.pos_stride, nsuf * sv.pos_stride)
     o, l = attend_views(desc, q, [prefix, suffix])
+    o1, l1 = P.attend_split(desc, q, [prefix, suffix])
     torch.cuda.synchronize()
     pkh, pvh, skh, svh = pk.to("cpu"), pv.to("cpu"), sk.to("cpu"), sv.to("cpu")
     views = [oracle.view_of(pkh, pvh), oracle.view_of(skh, svh, 0, nsuf, nsuf * sk.pos_stride, nsuf * sv.pos_stride)]
     o_ref, l_ref = oracle.attend(q.cpu().numpy(), views, Hkv, default_scale(D))
     compare(o, l, o_ref, l_ref, what=f"prefix+suffix D={D}")
+    compare(o1, l1, o_ref, l_ref, what=f"prefix+suffix D={D}, one call")
 
 
 def test_errors_on_device():
@@ -303,15 +307,18 @@ def test_workspace_reuse():
     compare(outs[3][0], outs[3][1], o_ref, l_ref, what="reused workspace")
 
 
-def test_attend_split_mixed_types_rejected():
-    D, Hq, Hkv = 128, 8, 2
-    a, b = pair(200, Hkv, D, synth.Q8_0, synth.Q4_0, 1, DEV)
-    c, d = pair(200, Hkv, D, synth.F16, synth.F16, 2, DEV)
+def test_attend_split_unsupported_group_rejected():
+    """Segments of different types are accepted (one launch each), but a group
+    with no kernel -- f32 rows of 512 values -- is refused before anything is
+    enqueued."""
+    D, Hq, Hkv = 512, 8, 2
+    a, b = pair(200, Hkv, D, synth.Q8_0, synth.Q8_0, 1, DEV)
+    c, d = pair(200, Hkv, D, synth.F32, synth.F32, 2, DEV)
     desc = P.Desc(1, Hq, Hkv, D, 0.1)
     q = synth.make_query(1, Hq, D, 3, DEV)
-    note("mixed types in one launch")
+    note("a group without a kernel in a mixed call")
     with pytest.raises(P.RkvError) as e:
-        P.attend_split(desc, q, [P.view_of_cache(a, b), P.view_of_cache(c, d)], ws=P.workspace(1 << 20))
+        P.attend_split(desc, q, [P.view_of_cache(a, b), P.view_of_cache(c, d)], ws=P.workspace(1 << 22))
     assert e.value.code == P.RKV_E_UNSUPPORTED
 
 
@@ -336,3 +343,49 @@ def test_split_phases_equal_one_call(kt, vt, n, wc, D, Hq, Hkv):
     P.rkv_attend_split_merge(desc, segs, o2, l2, ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+MIXED = [
+    # name, Hq, Hkv, D, [(K, V, keys), ...] segments in position order, softcap, masked rows
+    ("f16_window_q8q4_tail", 40, 8, 128, [(synth.F16, synth.F16, 1500), (synth.Q8_0, synth.Q4_0, 700)], 0.0, 0),
+    ("q8q8_window_q4q4_tail_d512_cap", 16, 2, 512, [(synth.Q8_0, synth.Q8_0, 600), (synth.Q4_0, synth.Q4_0, 330)],
+     30.0, 0),
+    ("three_groups", 8, 2, 128, [(synth.F16, synth.F16, 257), (synth.Q8_0, synth.Q8_0, 300),
+                                 (synth.Q4_0, synth.Q4_0, 99)], 0.0, 0),
+    ("f16_window_q8q4_tail_masked", 40, 8, 128, [(synth.F16, synth.F16, 1500), (synth.Q8_0, synth.Q4_0, 700)], 0.0, 6),
+    ("same_types_split_apart", 8, 2, 64, [(synth.F32, synth.F16, 200), (synth.Q8_0, synth.Q4_0, 64),
+                                         (synth.F32, synth.F16, 130)], 5.0, 0),
+]
+
+
+@pytest.mark.parametrize("case", MIXED, ids=[c[0] for c in MIXED])
+def test_mixed_segments_one_call(case):
+    """Segments stored at different types in one rkv_attend_split call (the
+    pages' window and tail each at its own type): one launch per type group,
+    one merge; against the oracle over the concatenated keys, and the two
+    phases give the bits of the one call."""
+    name, Hq, Hkv, D, parts, cap, nq = case
+    note(f"mixed segments {name}: Hq={Hq} Hkv={Hkv} D={D} parts={[(k, v, n) for k, v, n in parts]} rows={nq}")
+    seed = zlib.crc32(name.encode()) % 100000
+    caches = [pair(n, Hkv, D, kt, vt, seed + 7 * i, DEV) for i, (kt, vt, n) in enumerate(parts)]
+    n_all = sum(n for _, _, n in parts)
+    pos = None
+    if nq:
+        pos = [-1, 3, 1499, 1500, 1800, n_all + 5][:nq]
+    S = nq or 1
+    q = synth.make_query(S, Hq, D, synth.stream_seed(seed, 3), DEV)
+    desc = P.Desc(S, Hq, Hkv, D, default_scale(D), cap, q_pos=pos)
+    segs, p0 = [], 0
+    for (kc, vc), (_, _, n) in zip(caches, parts):
+        segs.append(P.view_of_cache(kc, vc, pos0=p0))
+        p0 += n
+    o, l = P.attend_split(desc, q, segs)
+    ws = P.workspace(P.rkv_attend_split_workspace_bytes(desc, segs))
+    o2, l2 = torch.full_like(o, float("nan")), torch.full_like(l, float("nan"))
+    P.rkv_attend_split_partials(desc, q, segs, o2, l2, ws)
+    P.rkv_attend_split_merge(desc, segs, o2, l2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(l, l2)
+    views = [oracle.view_of(kc.to("cpu"), vc.to("cpu")) for kc, vc in caches]
+    o_ref, l_ref = oracle.attend(q.cpu().numpy(), views, Hkv, default_scale(D), cap, q_pos=pos)
+    compare(o, l, o_ref, l_ref, what=name)
