@@ -1000,7 +1000,8 @@ int rkv_append_kv(int n_kv_heads, int head_dim, int n_tokens, int64_t pos0, int 
         return fail(RKV_E_INVAL, "positions [%lld, %lld) exceed window %lld + tail %lld", (long long)pos0,
                     (long long)(pos0 + n_tokens), (long long)wc, (long long)tc);
     if (n_tokens == 0) return RKV_OK;
-    if (n_tokens > (1 << 30)) return fail(RKV_E_UNSUPPORTED, "n_tokens too large");
+    if (n_tokens > (1 << 30) || (int64_t)n_tokens * n_kv_heads > 0x7fff0000)
+        return fail(RKV_E_UNSUPPORTED, "n_tokens x n_kv_heads too large");
     int rc;
     if ((rc = check_device(k_new, "k_new")) || (rc = check_device(v_new, "v_new"))) return rc;
     if ((uintptr_t)k_new % 4 || (uintptr_t)v_new % 4) return fail(RKV_E_INVAL, "k_new / v_new must be 4-byte aligned");

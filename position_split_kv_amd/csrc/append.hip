@@ -18,10 +18,11 @@
 //   1/d = 0 when d = 0; the scale is stored as the nearest binary16 of the
 //   binary32 d, the codes come from the binary32 d.
 //
-// One 64-lane workgroup per (token, KV head): the wave reads the K row and
-// the V row (D binary32 values, coalesced), encodes each into LDS for every
-// destination the token has, and copies the LDS row out with dword stores
-// (16-bit stores when the row is only 2-byte aligned).  Lane l holds values
+// Workgroups of 4 waves; each wave stores whole (token, KV head) rows in
+// turn: it reads the K row and the V row (D binary32 values, coalesced) and,
+// for every destination the token has, encodes each row in registers and
+// stores it from there (bytes for codes, 16 bits for scales and binary16
+// values, 32 bits for binary32 values on 4-byte aligned rows).  Lane l holds values
 // l + 64 i, so a 32-value block is one half-wave and its reductions are
 // xor-shuffles within the half.  HBM-bound for long appends (4 B read per
 // value, row bytes written per destination), latency-bound for one token.
@@ -30,8 +31,6 @@
 namespace rkv {
 
 namespace {
-
-constexpr int kMaxD = 512;
 
 // amax over the 32 lanes of a half-wave.
 __device__ __forceinline__ float half_max(float a)
@@ -47,17 +46,29 @@ __device__ __forceinline__ uint16_t f16_bits(float x)
     return __builtin_bit_cast(uint16_t, h);
 }
 
-// Encode one row (values xr[i] = x[lane + 64 i]) of type t into row (LDS).
+// Encode one row (values xr[i] = x[lane + 64 i]) of type t and store it at
+// row (global memory, 2-byte aligned): each lane stores its own values, codes
+// and (lane 0 of a block) scale with 1-, 2- or 4-byte stores; the stores of a
+// wave cover the row's bytes contiguously.
 template <int D>
 __device__ __forceinline__ void encode_row(int t, const float (&xr)[D / 64], uint8_t *row)
 {
     // the code decisions are defined on separately rounded binary32 products
     // and sums: no multiply-add contraction here
 #pragma clang fp contract(off)
-    const int lane = threadIdx.x, e = lane & 31;
+    const int lane = threadIdx.x & 63, e = lane & 31;
     if (t == kF32) {
+        if (((uintptr_t)row & 3) == 0) {
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i) ((float *)row)[lane + 64 * i] = xr[i];
+            for (int i = 0; i < D / 64; ++i) ((float *)row)[lane + 64 * i] = xr[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < D / 64; ++i) {
+                const uint32_t b = __float_as_uint(xr[i]);
+                ((uint16_t *)row)[2 * (lane + 64 * i)] = (uint16_t)b;
+                ((uint16_t *)row)[2 * (lane + 64 * i) + 1] = (uint16_t)(b >> 16);
+            }
+        }
     } else if (t == kF16) {
 #pragma unroll
         for (int i = 0; i < D / 64; ++i) ((uint16_t *)row)[lane + 64 * i] = f16_bits(xr[i]);
@@ -105,41 +116,33 @@ __device__ __forceinline__ void encode_row(int t, const float (&xr)[D / 64], uin
     }
 }
 
-__device__ __forceinline__ void copy_row(const uint8_t *row, uint8_t *dst, int nbytes)
-{
-    const int lane = threadIdx.x;
-    if (((uintptr_t)dst & 3) == 0) {
-        for (int w = lane; w < nbytes / 4; w += 64) ((uint32_t *)dst)[w] = ((const uint32_t *)row)[w];
-    } else {
-        for (int w = lane; w < nbytes / 2; w += 64) ((uint16_t *)dst)[w] = ((const uint16_t *)row)[w];
-    }
-}
+constexpr int kAppendWaves = 4;  // waves per workgroup; each wave stores whole rows
 
 template <int D>
-__global__ void __launch_bounds__(64) rkv_append_kernel(const float *__restrict__ k_new,
-                                                        const float *__restrict__ v_new, AppendParams p)
+__global__ void __launch_bounds__(64 * kAppendWaves) rkv_append_kernel(const float *__restrict__ k_new,
+                                                                       const float *__restrict__ v_new,
+                                                                       AppendParams p, int n_rows)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t row[4 * kMaxD];
-    const int tok = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-    const int64_t src = ((int64_t)tok * p.n_kv_heads + h) * D;
-    float xk[D / 64], xv[D / 64];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    // row r = (token, KV head) = (r / n_kv_heads, r % n_kv_heads); the waves of
+    // the grid take rows in turn (a wave-uniform loop: no workgroup barriers)
+    for (int r = blockIdx.x * kAppendWaves + wv; r < n_rows; r += gridDim.x * kAppendWaves) {
+        const int tok = r / p.n_kv_heads, h = r - tok * p.n_kv_heads;
+        const int64_t src = (int64_t)r * D;
+        float xk[D / 64], xv[D / 64];
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) {
-        xk[i] = k_new[src + lane + 64 * i];
-        xv[i] = v_new[src + lane + 64 * i];
-    }
-    for (int di = 0; di < p.n_dst; ++di) {
-        const AppendDst &dd = p.dst[di];
-        if (tok < dd.first_tok || tok >= dd.first_tok + dd.n_tok) continue;  // uniform over the workgroup
-        const int64_t r = dd.row0 + (tok - dd.first_tok);
-        encode_row<D>(dd.k_type, xk, row);
-        __syncthreads();
-        copy_row(row, dd.k + r * dd.k_pos + h * dd.k_head, row_bytes_of(dd.k_type, D));
-        __syncthreads();
-        encode_row<D>(dd.v_type, xv, row);
-        __syncthreads();
-        copy_row(row, dd.v + r * dd.v_pos + h * dd.v_head, row_bytes_of(dd.v_type, D));
-        __syncthreads();
+        for (int i = 0; i < D / 64; ++i) {
+            xk[i] = k_new[src + lane + 64 * i];
+            xv[i] = v_new[src + lane + 64 * i];
+        }
+        for (int di = 0; di < p.n_dst; ++di) {
+            const AppendDst &dd = p.dst[di];
+            if (tok < dd.first_tok || tok >= dd.first_tok + dd.n_tok) continue;  // uniform over the wave
+            const int64_t rr = dd.row0 + (tok - dd.first_tok);
+            encode_row<D>(dd.k_type, xk, dd.k + rr * dd.k_pos + h * dd.k_head);
+            encode_row<D>(dd.v_type, xv, dd.v + rr * dd.v_pos + h * dd.v_head);
+        }
     }
     // rows written to host memory reach it before the kernel ends (a copy
     // engine reads them next, ordered only through a host-visible signal)
@@ -152,12 +155,18 @@ hipError_t launch_append(int d, int n_tokens, int n_kv_heads, const float *k_new
                          const AppendParams &p, hipStream_t stream)
 {
     if (n_tokens <= 0) return hipSuccess;
-    const dim3 grid((unsigned)n_tokens, (unsigned)n_kv_heads), block(64);
+    const int64_t n_rows = (int64_t)n_tokens * n_kv_heads;
+    if (n_rows > 0x7fffffff - 64 * kAppendWaves) return hipErrorInvalidValue;
+    // one row per wave up to 8192 workgroups (rows in flight hide the load
+    // latency of each row), then waves take several rows
+    const int64_t need = (n_rows + kAppendWaves - 1) / kAppendWaves;
+    const dim3 grid((unsigned)(need < 8192 ? need : 8192)), block(64 * kAppendWaves);
+    const int nr = (int)n_rows;
     switch (d) {
-    case 64: hipLaunchKernelGGL(rkv_append_kernel<64>, grid, block, 0, stream, k_new, v_new, p); break;
-    case 128: hipLaunchKernelGGL(rkv_append_kernel<128>, grid, block, 0, stream, k_new, v_new, p); break;
-    case 256: hipLaunchKernelGGL(rkv_append_kernel<256>, grid, block, 0, stream, k_new, v_new, p); break;
-    case 512: hipLaunchKernelGGL(rkv_append_kernel<512>, grid, block, 0, stream, k_new, v_new, p); break;
+    case 64: hipLaunchKernelGGL(rkv_append_kernel<64>, grid, block, 0, stream, k_new, v_new, p, nr); break;
+    case 128: hipLaunchKernelGGL(rkv_append_kernel<128>, grid, block, 0, stream, k_new, v_new, p, nr); break;
+    case 256: hipLaunchKernelGGL(rkv_append_kernel<256>, grid, block, 0, stream, k_new, v_new, p, nr); break;
+    case 512: hipLaunchKernelGGL(rkv_append_kernel<512>, grid, block, 0, stream, k_new, v_new, p, nr); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
