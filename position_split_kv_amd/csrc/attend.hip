@@ -1,6 +1,8 @@
 // attend.hip -- dispatch of the split kernel, occupancy queries, the
 // fixed-order merge of the per-split partials, and the fill of an empty
 // segment's result.
+#include <atomic>
+
 #include "common.h"
 
 namespace rkv {
@@ -44,8 +46,9 @@ int split_waves(int kt, int vt, int d, int rt)
 
 int split_occupancy(int kt, int vt, int d, int rt)
 {
-    // cached per instance and device (the first query on a device may be slow)
-    static int cache[4][4][4][6][16];
+    // cached per instance and device (the first query on a device may be
+    // slow); atomics, since calls may plan from several host threads
+    static std::atomic<int> cache[4][4][4][6][16];
     static const int rts[6] = {1, 2, 4, 5, 8, 16};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
@@ -57,7 +60,8 @@ int split_occupancy(int kt, int vt, int d, int rt)
         if (rts[i] == rt) ri = i;
     const int di = d == 64 ? 0 : d == 128 ? 1 : d == 256 ? 2 : d == 512 ? 3 : -1;
     if (ri < 0 || di < 0 || kt < 0 || kt > 3 || vt < 0 || vt > 3 || dev < 0 || dev >= 16) return 0;
-    int &c = cache[kt][vt][di][ri][dev];
+    std::atomic<int> &slot = cache[kt][vt][di][ri][dev];
+    int c = slot.load(std::memory_order_relaxed);
     if (c == 0) {
 #define RKV_OCC(kk, vv) \
     if (kt == kk && vt == vv) c = split_occupancy_k##kk##_v##vv(d, rt);
@@ -67,27 +71,28 @@ int split_occupancy(int kt, int vt, int d, int rt)
         RKV_OCC_K(2)
         RKV_OCC_K(3)
         if (c <= 0) c = -1;
+        slot.store(c, std::memory_order_relaxed);  // every thread computes the same value
     }
     return c > 0 ? c : 0;
 }
 
 int compute_units()
 {
-    static int cu[16];
+    static std::atomic<int> cu[16];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) {
         (void)hipGetLastError();
         return 0;
     }
-    if (cu[dev] == 0) {
-        int n = 0;
+    int n = cu[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
             (void)hipGetLastError();
             n = -1;
         }
-        cu[dev] = n;
+        cu[dev].store(n, std::memory_order_relaxed);
     }
-    return cu[dev] > 0 ? cu[dev] : 0;
+    return n > 0 ? n : 0;
 }
 
 hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q, float *pa, float2 *pm, float *o,
