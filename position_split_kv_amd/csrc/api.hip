@@ -164,23 +164,31 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
                 return fail(RKV_E_UNSUPPORTED, "a masked call takes segments of fewer than 2^30 keys");
     int64_t tiles_total = 0;
     for (int i = 0; i < n; ++i) tiles_total += (v[i]->n_keys + kTile - 1) / kTile;
-    const int nw = std::max(1, split_waves(kt, vt, D, rt));
     // With dim slices a head slot is one (KV head, slice) and every wave of a
     // workgroup takes a slot (the slices of a head meet at barriers).
     const int ds = split_dim_slices(kt, vt, D);
+    // Several 16-row groups per KV head over block-type K and q4_0 V at
+    // head_dim 128: the shared-decode kernel, whose workgroups hold 2 KV heads
+    // x 4 row groups that decode each tile once (n_rg then counts blocks of 4
+    // row groups).
+    pl->shd = ds == 1 && D == 128 && rt == 16 && pl->n_rg >= 2 && split_shd_supported(kt, vt);
+    const int nw = pl->shd ? 4 : std::max(1, split_waves(kt, vt, D, rt));
     const int slots = Hkv * ds;
     int hpw = 1;
     if (ds > 1 && nw < ds) return fail(RKV_E_UNSUPPORTED, "too few waves per workgroup for %d dim slices", ds);
-    if (ds > 1)
+    if (pl->shd)
+        hpw = 1;
+    else if (ds > 1)
         hpw = nw;
     else
         while (2 * hpw <= nw && 2 * hpw <= slots) hpw *= 2;
+    if (pl->shd) pl->n_rg = (pl->n_rg + 3) / 4;
     pl->nw = nw;
     pl->hpw = hpw;
     pl->n_hg = (slots + hpw - 1) / hpw;
-    const int64_t wph = nw / hpw;
+    const int64_t wph = pl->shd ? 1 : nw / hpw;
     const int64_t units = (int64_t)pl->n_hg * pl->n_rg * pl->z;
-    int occ = split_occupancy(kt, vt, D, rt);
+    int occ = pl->shd ? split_shd_occupancy(kt, vt) : split_occupancy(kt, vt, D, rt);
     int cus = compute_units();
     if (occ <= 0) occ = 2;
     if (cus <= 0) cus = 256;
@@ -338,8 +346,12 @@ int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view
         for (int j = 0; j < cp.g.n; ++j) {
             const SplitPlan &pl = cp.pl[j];
             const dim3 grid((unsigned)pl.n_splits, (unsigned)(pl.n_hg * pl.n_rg), (unsigned)pl.z);
-            RKV_HIP(launch_split(cp.g.v[j][0]->k_type, cp.g.v[j][0]->v_type, d->head_dim, pl.rt, grid, q, part_acc,
-                                 part_ml, o, lse, prm[j], stream));
+            if (pl.shd)
+                RKV_HIP(launch_split_shd(cp.g.v[j][0]->k_type, cp.g.v[j][0]->v_type, grid, q, part_acc, part_ml, o, lse,
+                                         prm[j], stream));
+            else
+                RKV_HIP(launch_split(cp.g.v[j][0]->k_type, cp.g.v[j][0]->v_type, d->head_dim, pl.rt, grid, q,
+                                     part_acc, part_ml, o, lse, prm[j], stream));
         }
     if (phase == 1) return RKV_OK;
     if (cp.n_splits_all > 1)

@@ -11,7 +11,11 @@ namespace rkv {
     hipError_t launch_split_k##kt##_v##vt(int d, int rt, dim3 grid, const float *q, float *pa, float2 *pm, \
                                           float *o, float *lse, const SplitParams &p, hipStream_t s);       \
     int split_waves_k##kt##_v##vt(int d, int rt);                                                         \
-    int split_occupancy_k##kt##_v##vt(int d, int rt);
+    int split_occupancy_k##kt##_v##vt(int d, int rt);                                                     \
+    hipError_t launch_split_shd_k##kt##_v##vt(dim3 grid, const float *q, float *pa, float2 *pm, float *o, \
+                                              float *lse, const SplitParams &p, hipStream_t s);           \
+    int split_shd_occupancy_k##kt##_v##vt();                                                              \
+    bool split_shd_supported_k##kt##_v##vt();
 #define RKV_DECL_K(kt) RKV_DECL(kt, 0) RKV_DECL(kt, 1) RKV_DECL(kt, 2) RKV_DECL(kt, 3)
 RKV_DECL_K(0)
 RKV_DECL_K(1)
@@ -93,6 +97,56 @@ int compute_units()
         cu[dev].store(n, std::memory_order_relaxed);
     }
     return n > 0 ? n : 0;
+}
+
+bool split_shd_supported(int kt, int vt)
+{
+#define RKV_SOK(kk, vv) \
+    if (kt == kk && vt == vv) return split_shd_supported_k##kk##_v##vv();
+#define RKV_SOK_K(kk) RKV_SOK(kk, 0) RKV_SOK(kk, 1) RKV_SOK(kk, 2) RKV_SOK(kk, 3)
+    RKV_SOK_K(0)
+    RKV_SOK_K(1)
+    RKV_SOK_K(2)
+    RKV_SOK_K(3)
+    return false;
+}
+
+int split_shd_occupancy(int kt, int vt)
+{
+    static std::atomic<int> cache[4][4][16];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (kt < 0 || kt > 3 || vt < 0 || vt > 3 || dev < 0 || dev >= 16) return 0;
+    std::atomic<int> &slot = cache[kt][vt][dev];
+    int c = slot.load(std::memory_order_relaxed);
+    if (c == 0) {
+#define RKV_SOCC(kk, vv) \
+    if (kt == kk && vt == vv) c = split_shd_occupancy_k##kk##_v##vv();
+#define RKV_SOCC_K(kk) RKV_SOCC(kk, 0) RKV_SOCC(kk, 1) RKV_SOCC(kk, 2) RKV_SOCC(kk, 3)
+        RKV_SOCC_K(0)
+        RKV_SOCC_K(1)
+        RKV_SOCC_K(2)
+        RKV_SOCC_K(3)
+        if (c <= 0) c = -1;
+        slot.store(c, std::memory_order_relaxed);
+    }
+    return c > 0 ? c : 0;
+}
+
+hipError_t launch_split_shd(int kt, int vt, dim3 grid, const float *q, float *pa, float2 *pm, float *o, float *lse,
+                            const SplitParams &p, hipStream_t s)
+{
+#define RKV_SCASE(kk, vv) \
+    if (kt == kk && vt == vv) return launch_split_shd_k##kk##_v##vv(grid, q, pa, pm, o, lse, p, s);
+#define RKV_SCASE_K(kk) RKV_SCASE(kk, 0) RKV_SCASE(kk, 1) RKV_SCASE(kk, 2) RKV_SCASE(kk, 3)
+    RKV_SCASE_K(0)
+    RKV_SCASE_K(1)
+    RKV_SCASE_K(2)
+    RKV_SCASE_K(3)
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q, float *pa, float2 *pm, float *o,

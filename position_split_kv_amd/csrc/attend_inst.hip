@@ -2,6 +2,7 @@
 // pair.  Built once per pair with -DRKV_KT=<t> -DRKV_VT=<t> (0 f32, 1 f16,
 // 2 q8_0, 3 q4_0) so that the instances compile in parallel.
 #include "attend_kernel.h"
+#include "attend_shd.h"
 
 #if !defined(RKV_KT) || !defined(RKV_VT)
 #error "RKV_KT and RKV_VT must be defined"
@@ -144,5 +145,40 @@ int RKV_NAME_NW(RKV_KT, RKV_VT)(int d, int rt)
     default: return 0;
     }
 }
+
+// The shared-decode kernel (attend_shd.h): block-type K, q4_0 V, head_dim
+// 128, 16 rows per wave, 4 row groups and 2 KV heads per workgroup; absent
+// (invalid value / occupancy 0) for the other type pairs.
+#define RKV_NAME_SHD(kt, vt) RKV_CAT4(launch_split_shd_k, kt, _v, vt)
+hipError_t RKV_NAME_SHD(RKV_KT, RKV_VT)(dim3 grid, const float *q, float *pa, float2 *pm, float *o, float *lse,
+                                        const SplitParams &p, hipStream_t s)
+{
+    if constexpr (ShdShape<RKV_KT, RKV_VT>::OK) {
+        hipLaunchKernelGGL((rkv_split_shd_kernel<RKV_KT, RKV_VT>), grid, dim3(64 * kShdWaves), 0, s, q, pa, pm, o, lse,
+                           p);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
+#define RKV_NAME_SHD_OCC(kt, vt) RKV_CAT4(split_shd_occupancy_k, kt, _v, vt)
+int RKV_NAME_SHD_OCC(RKV_KT, RKV_VT)()
+{
+    if constexpr (ShdShape<RKV_KT, RKV_VT>::OK) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rkv_split_shd_kernel<RKV_KT, RKV_VT>, 64 * kShdWaves, 0) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        return n;
+    } else {
+        return 0;
+    }
+}
+
+#define RKV_NAME_SHD_OK(kt, vt) RKV_CAT4(split_shd_supported_k, kt, _v, vt)
+bool RKV_NAME_SHD_OK(RKV_KT, RKV_VT)() { return ShdShape<RKV_KT, RKV_VT>::OK; }
 
 }  // namespace rkv

@@ -1,0 +1,339 @@
+// attend_shd.h -- the split kernel for many query rows per KV head over
+// block-type K (q8_0 / q4_0) and q4_0 V at head_dim 128, with the block
+// decode shared by the row groups of a head.
+//
+// With more than 16 query rows per KV head (sequences sharing one prefix, the
+// rows of a verify step or a prefill chunk), the general split kernel runs
+// each 16-row group of a head in its own workgroup, and every group decodes
+// the same key tiles.  Here a workgroup holds 2 KV heads x 4 row groups
+// (8 waves, one 16-row group each).  Per 64-key tile, a head's K and V rows
+// go global -> LDS once (one DMA each, issued by two of its waves); each of
+// the head's four waves decodes a quarter of them into the exact binary16
+// matrix-core operands -- K codes of one 32-dim block (with its scales), and
+// d * code of one key pair per 8-key group split into high and low binary16
+// parts -- in LDS; after a workgroup barrier every wave runs its scores,
+// softmax and P.V from those operands.  A second barrier per tile (at the
+// next tile's top) keeps the operands until every wave has used them.  The
+// arithmetic per row is that of the general kernel (the same MFMA shapes,
+// binary16 operands and accumulation orders); only where the operands are
+// made differs.
+#pragma once
+
+#include "attend_kernel.h"
+
+namespace rkv {
+
+constexpr int kShdRG = 4;                     // row groups of 16 rows per KV head in a workgroup
+constexpr int kShdHeads = 1;                  // KV heads per workgroup (two workgroups share a compute unit)
+constexpr int kShdWaves = kShdRG * kShdHeads;  // waves per workgroup
+
+template <int KT, int VT>
+struct ShdShape {
+    using Sh = Shape<KT, VT, 128>;
+    static constexpr int LSK = Sh::LSK, LSV = Sh::LSV;
+    static constexpr int RAW_DW = kTile * (LSK + LSV) + 8;  // a head's raw K and V tiles (+ read slack)
+    static constexpr int BK_DW = 4 * 4 * 64 * 4;             // K operands [kb 4][kk 4][lane 64] x 16 bytes
+    static constexpr int DK_DW = 4 * 4 * 16;                 // K block scales [kb][kk][key 16]
+    static constexpr int BV_DW = 2 * 8 * 64 * 4;             // V operands [kb 2][c 8][lane 64] x 16 bytes
+    static constexpr int HEAD_DW = RAW_DW + BK_DW + DK_DW + 2 * BV_DW;  // (V: high and low parts)
+    static constexpr int SP_DW = 16 * kTile;                 // one wave's score rows
+    static constexpr int LDS_DW = kShdHeads * HEAD_DW + kShdWaves * SP_DW;
+    static constexpr bool OK = (KT == kQ8 || KT == kQ4) && VT == kQ4 && 4 * LDS_DW <= 160 * 1024;
+};
+
+template <int KT, int VT>
+__global__ void __launch_bounds__(64 * kShdWaves, 2)
+rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, float2 *__restrict__ part_ml,
+                     float *__restrict__ o_out, float *__restrict__ lse_out, const SplitParams p)
+{
+    using SS = ShdShape<KT, VT>;
+    using Sh = typename SS::Sh;
+    static_assert(SS::OK, "instance outside the shared-decode kernel's LDS budget");
+    constexpr int D = 128, RT = 16;
+    constexpr int LSK = SS::LSK, LSV = SS::LSV;
+    __shared__ __attribute__((aligned(16))) uint32_t lds[SS::LDS_DW];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hs = w / kShdRG, rgl = w - hs * kShdRG;  // head slot, row group within the head
+    const int hg = blockIdx.y / p.n_rg, rgb = blockIdx.y - hg * p.n_rg;
+    const int g = hg * kShdHeads + hs;
+    const int rg = rgb * kShdRG + rgl;
+    const int cnt = g < p.n_kv_heads ? u16_at(p.rowcnt, g) - rg * RT : 0;
+    const int nr = cnt <= 0 ? 0 : cnt < RT ? cnt : RT;  // a wave with no rows still decodes and joins the barriers
+    const int z = blockIdx.z;
+
+    uint32_t *const rawK = lds + hs * SS::HEAD_DW;
+    uint32_t *const rawV = rawK + kTile * LSK;
+    uint32_t *const bK = rawK + SS::RAW_DW;
+    float *const dK = (float *)(bK + SS::BK_DW);
+    uint32_t *const bVh = (uint32_t *)(dK + SS::DK_DW);
+    uint32_t *const bVl = bVh + SS::BV_DW;
+    float *const sPw = (float *)(lds + kShdHeads * SS::HEAD_DW + w * SS::SP_DW);
+
+    SegParams sg = p.seg[0];
+#pragma unroll
+    for (int si = 1; si < kMaxSegs; ++si)
+        if (si < p.n_segs && (int)blockIdx.x >= p.seg[si].split_base) sg = p.seg[si];
+    const int64_t kbeg = (int64_t)((int)blockIdx.x - sg.split_base) * sg.keys_per_split;
+    // every wave of the workgroup walks every tile of the split (barriers)
+    const int64_t kend = kbeg + sg.keys_per_split < sg.n_keys ? kbeg + sg.keys_per_split : sg.n_keys;
+    const int gr = g < p.n_kv_heads ? g : p.n_kv_heads - 1;
+    const uint8_t *kg = sg.k + z * sg.k_seq + gr * sg.k_head;
+    const uint8_t *vg = sg.v + z * sg.v_seq + gr * sg.v_head;
+
+    int tabrow[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int ti = g * p.rows_per_g + rg * RT + r;
+        const int v = u16_at(p.rowtab, ti < kMaxRowTable ? ti : kMaxRowTable - 1);
+        tabrow[r] = r < nr ? z * p.z_row_step + v : -1;
+    }
+    // causal mask: row r sees the segment's keys with index <= lim[r]
+    constexpr int kSeeAll = 1 << 30;
+    int limv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * (lane >> 4) + i;
+        int x = kSeeAll;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (p.masked && row == r && tabrow[r] >= 0) {
+                const int64_t rel = p.qpos[tabrow[r] / p.n_q_heads] - sg.pos0;
+                x = rel < -1 ? -1 : rel > kSeeAll ? kSeeAll : (int)rel;
+            }
+        }
+        limv[i] = x;
+    }
+
+    // raw tile DMA: K by row group 0 of the head, V by row group 1
+    constexpr int LSK1 = LSK > 0 ? LSK : 1, LSV1 = LSV > 0 ? LSV : 1;
+    const uint64_t kwrap = dma_wraps<LSK1>(lane), vwrap = dma_wraps<LSV1>(lane);
+    const bool kfull_ok = sg.k_pos >= 4 * LSK && sg.k_pos < (1 << 23);
+    const bool vfull_ok = sg.v_pos >= 4 * LSV && sg.v_pos < (1 << 23);
+    auto nk_at = [&](int64_t t) { return (int)(kend - t < kTile ? kend - t : kTile); };
+    auto dma_raw = [&](int64_t t) {
+        const int nkk = nk_at(t);
+        if (rgl == 0) {
+            int kps = (int)sg.k_pos;
+            asm volatile("" : "+s"(kps));
+            waitcnt_lgkm0();
+            const uint32_t base = lds_addr(rawK);
+            if (kfull_ok && nkk == kTile && t + kTile < sg.n_keys)
+                dma_rows4_full<LSK1>(kg + t * sg.k_pos, kps, kwrap, base, lane);
+            else
+                dma_rows4<Sh::RBK / 4, LSK>(kg + t * sg.k_pos, kps, nkk, base, lane);
+        } else if (rgl == 1) {
+            int vps = (int)sg.v_pos;
+            asm volatile("" : "+s"(vps));
+            waitcnt_lgkm0();
+            const uint32_t base = lds_addr(rawV);
+            if (vfull_ok && nkk == kTile && t + kTile < sg.n_keys)
+                dma_rows4_full<LSV1>(vg + t * sg.v_pos, vps, vwrap, base, lane);
+            else
+                dma_rows4<Sh::RBV / 4, LSV>(vg + t * sg.v_pos, vps, nkk, base, lane);
+        }
+    };
+
+    float qraw[D / 32][8];
+    {
+        const int qr = lane & 15;
+        int rowi = 0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) rowi = (qr == r && tabrow[r] >= 0) ? tabrow[r] : rowi;
+        mfma_q_load<D>(q + (int64_t)rowi * D, lane, qraw);
+    }
+    int64_t t0 = kbeg;
+    if (t0 < kend) dma_raw(t0);
+    rkv_half8 qhi[D / 32], qlo[D / 32];
+    pin_v<8 * (D / 32)>(&qraw[0][0]);
+    mfma_q_split<D>(qraw, (lane & 15) < nr, p.scale_log2, qhi, qlo);
+    float mrow[4], lrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        mrow[i] = -INFINITY;
+        lrow[i] = 0.f;
+    }
+    rkv_float4v oc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) oc[c] = rkv_float4v{0.f, 0.f, 0.f, 0.f};
+    const float cap = p.softcap;
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float capl = cap * kLog2e;
+    const float two_over_cap = cap > 0.f ? 2.f / cap : 0.f;
+    const int qi = lane & 15, gq = lane >> 4;
+
+    for (; t0 < kend; t0 += kTile) {
+        const int nk = nk_at(t0);
+        waitcnt_vm<0>();  // this wave's raw tile DMA (if any) has landed
+        __syncthreads();  // the head's raw tiles are in LDS; every wave is done with the last tile's operands
+
+        // ---- decode this wave's quarter of the head's operands
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            float dsc;
+            const rkv_half8 b = block_codes_f16<KT>(rawK + (16 * kb + qi) * LSK, rgl, gq, dsc);
+            *(rkv_half8 *)(bK + ((kb * 4 + rgl) * 64 + lane) * 4) = b;
+            if (lane < 16) dK[(kb * 4 + rgl) * 16 + lane] = dsc;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            uint32_t ca[4], cb[4], da, db;
+            v_group_codes_f16<VT>(rawV + (4 * (8 * kb + 2 * rgl) + gq) * LSV, qi, ca, da);
+            v_group_codes_f16<VT>(rawV + (4 * (8 * kb + 2 * rgl + 1) + gq) * LSV, qi, cb, db);
+            const rkv_half2 d2 = __builtin_bit_cast(rkv_half2, da | (db << 16));
+#pragma unroll
+            for (int p2 = 0; p2 < 4; ++p2) {
+                const rkv_half2 x0 = __builtin_bit_cast(rkv_half2, __builtin_amdgcn_perm(cb[p2], ca[p2], 0x05040100u));
+                const rkv_half2 x1 = __builtin_bit_cast(rkv_half2, __builtin_amdgcn_perm(cb[p2], ca[p2], 0x07060302u));
+                const rkv_half2 h0 = d2 * x0, h1 = d2 * x1;
+                const rkv_half2 l0 = __builtin_elementwise_fma(d2, x0, -h0);
+                const rkv_half2 l1 = __builtin_elementwise_fma(d2, x1, -h1);
+                const int i0 = ((kb * 8 + 2 * p2) * 64 + lane) * 4 + rgl, i1 = i0 + 64 * 4;
+                bVh[i0] = __builtin_bit_cast(uint32_t, h0);
+                bVh[i1] = __builtin_bit_cast(uint32_t, h1);
+                bVl[i0] = __builtin_bit_cast(uint32_t, l0);
+                bVl[i1] = __builtin_bit_cast(uint32_t, l1);
+            }
+        }
+        __syncthreads();  // the operands are in LDS; the raw tiles are free
+        if (t0 + kTile < kend) dma_raw(t0 + kTile);
+
+        // ---- scores on the matrix cores from the shared K operands
+        float sv[4][4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[kb][i] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const rkv_half8 b = *(const rkv_half8 *)(bK + ((kb * 4 + kk) * 64 + lane) * 4);
+                const float dsc = dK[(kb * 4 + kk) * 16 + qi];
+                rkv_float4v acc = rkv_float4v{0.f, 0.f, 0.f, 0.f};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi[kk], b, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo[kk], b, acc, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[kb][i] = fmaf(dsc, acc[i], sv[kb][i]);
+            }
+        }
+        // ---- mask, cap, online softmax (as the general kernel)
+        int kmx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tl = limv[i] - (int)t0;
+            kmx[i] = p.masked ? (tl < nk - 1 ? (tl < -1 ? -1 : tl) : nk - 1) : nk - 1;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int key = 16 * kb + qi;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float x = sv[kb][i];
+                if (cap > 0.f) x = capl * tanh_from_exp2(x * two_over_cap);
+                sv[kb][i] = key <= kmx[i] ? x : -INFINITY;
+            }
+        }
+        float al[4], mex[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float mx = fmaxf(fmaxf(sv[0][i], sv[1][i]), fmaxf(sv[2][i], sv[3][i]));
+            mx = row16_max(mx);
+            const float mn = fmaxf(mrow[i], mx);
+            mex[i] = mn == -INFINITY ? 0.f : mn;
+            al[i] = __builtin_amdgcn_exp2f(mrow[i] - mex[i]);
+            lrow[i] *= al[i];
+            mrow[i] = mn;
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oc[c][i] *= al[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * (lane >> 4) + i;
+            float ps = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const float pv = __builtin_amdgcn_exp2f(sv[kb][i] - mex[i]);
+                ps += pv;
+                const int key = 16 * kb + qi;
+                sPw[row * kTile + (key & 3) * 16 + (key >> 2)] = pv;
+            }
+            lrow[i] += ps;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+
+        // ---- P.V on the matrix cores from the shared V operands
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            rkv_half8 ph, pl;
+            {
+                const float4 a = *(const float4 *)&sPw[qi * kTile + gq * 16 + 8 * kb];
+                const float4 b = *(const float4 *)&sPw[qi * kTile + gq * 16 + 8 * kb + 4];
+                const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const _Float16 h = (_Float16)x[e];
+                    ph[e] = h;
+                    pl[e] = (_Float16)(x[e] - (float)h);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const rkv_half8 bh = *(const rkv_half8 *)(bVh + ((kb * 8 + c) * 64 + lane) * 4);
+                const rkv_half8 bl = *(const rkv_half8 *)(bVl + ((kb * 8 + c) * 64 + lane) * 4);
+                oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bh, oc[c], 0, 0, 0);
+                oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bl, oc[c], 0, 0, 0);
+                oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bh, oc[c], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- each wave owns its rows: write them from the MFMA output layout
+    float m[RT], l[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const float t = row16_sum(lrow[r & 3]);
+        l[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), 16 * (r >> 2)));
+        m[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mrow[r & 3]), 16 * (r >> 2)));
+    }
+    const bool single = p.n_splits_all == 1;
+    const int64_t pbase = (int64_t)(p.split_off + (int)blockIdx.x) * p.n_rows_total;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * (lane >> 4) + i;
+        int rr = -1;
+        float lr = 1.f;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            rr = row == r ? tabrow[r] : rr;
+            lr = row == r ? l[r] : lr;
+        }
+        if (rr < 0) continue;
+        float v[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = single ? (lr > 0.f ? oc[c][i] / lr : 0.f) : oc[c][i];
+        float *dst = single ? o_out + (int64_t)rr * D : part_acc + (pbase + rr) * D;
+        *(float4 *)(dst + 8 * qi) = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4 *)(dst + 8 * qi + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    if (lane < RT) {
+        int rr = -1;
+        float mr = 0.f, lr = 1.f;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            rr = lane == r ? tabrow[r] : rr;
+            mr = lane == r ? m[r] : mr;
+            lr = lane == r ? l[r] : lr;
+        }
+        if (rr >= 0) {
+            if (single) lse_out[rr] = (mr + log2f(lr)) * 0.69314718055994531f;
+            else part_ml[(int64_t)rr * p.n_splits_all + p.split_off + blockIdx.x] = make_float2(mr, lr);
+        }
+    }
+}
+
+}  // namespace rkv

@@ -82,6 +82,7 @@ struct SplitPlan {
     int rows_per_g;  // max rows of a KV head
     int z;           // grid z (sequences with own keys, or 1)
     int n_splits;    // grid x
+    bool shd;        // the shared-decode kernel (n_rg then counts blocks of its row groups)
     int64_t n_rows_total;
     size_t acc_bytes, ml_bytes;
     size_t ws_bytes;
@@ -111,6 +112,13 @@ int split_waves(int kt, int vt, int d, int rt);
 // current device, and the device's compute units (0 when no device answers).
 int split_occupancy(int kt, int vt, int d, int rt);
 int compute_units();
+// The shared-decode split kernel (attend_shd.h): many rows per KV head over
+// block-type K and q4_0 V at head_dim 128 (16 rows per wave, 4 row groups x
+// 2 KV heads per workgroup, grid y = head pairs x row-group blocks).
+bool split_shd_supported(int kt, int vt);
+int split_shd_occupancy(int kt, int vt);
+hipError_t launch_split_shd(int kt, int vt, dim3 grid, const float *q, float *part_acc, float2 *part_ml, float *o,
+                            float *lse, const SplitParams &p, hipStream_t stream);
 hipError_t launch_fill_empty(int d, int64_t n_rows, float *o, float *lse, hipStream_t stream);
 
 struct CombineParts {

@@ -80,6 +80,12 @@ CASES = [
     ("q4q8_d256_batch2", 2, 8, 2, 256, synth.Q4_0, synth.Q8_0, 260, 130, None, 0.0, None),
     ("q8q4_d256_g2", 1, 4, 2, 256, synth.Q8_0, synth.Q4_0, 333, 200, None, 0.0, None),
     ("q8q8_d512_map_rowgroups", 1, 20, 2, 512, synth.Q8_0, synth.Q8_0, 257, 128, None, 0.0, [0] * 18 + [1] * 2),
+    # more than 16 rows per KV head over block K and q4_0 V at head_dim 128: the shared-decode kernel (two KV heads
+    # x four 16-row groups per workgroup): an odd KV-head count (an empty head slot) with 20 rows per head (two
+    # empty row groups), one KV head of 40 rows with a cap, and 120 rows per head (two blocks of row groups)
+    ("q4q4_shd_odd_heads", 1, 60, 3, 128, synth.Q4_0, synth.Q4_0, 777, 333, None, 0.0, None),
+    ("q8q4_shd_rows40_cap", 1, 40, 1, 128, synth.Q8_0, synth.Q4_0, 500, 200, None, 20.0, None),
+    ("q8q4_shd_rows120", 1, 240, 2, 128, synth.Q8_0, synth.Q4_0, 420, 70, None, 0.0, None),
 ]
 
 
