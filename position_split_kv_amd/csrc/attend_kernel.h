@@ -110,6 +110,28 @@ __device__ __forceinline__ float tanh_from_exp2(float two_y_log2)
     return fmaf(-2.f, __builtin_amdgcn_rcpf(t + 1.f), 1.f);
 }
 
+// Softcap (CAP) and causal mask of one 64-key score tile in the matrix-core
+// output layout: sv[kb][i] holds key 16 kb + qi of the lane's output row i
+// (scores in log2 units); keys past kmx[i] become -inf.  The cap is a template
+// argument: the caller branches once per tile on the uniform cap, so that a
+// tile without one carries no exp2 or reciprocal.
+template <bool CAP>
+__device__ __forceinline__ void cap_mask_tile(float (&sv)[4][4], const int (&kmx)[4], int qi, float capl,
+                                              float two_over_cap)
+{
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int key = 16 * kb + qi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x = sv[kb][i];
+            // (s/c = x/capl, and 2 (s/c) log2 e = x * 2/c)
+            if constexpr (CAP) x = capl * tanh_from_exp2(x * two_over_cap);
+            sv[kb][i] = key <= kmx[i] ? x : -INFINITY;
+        }
+    }
+}
+
 __device__ __forceinline__ float sbyte(uint32_t w, int k) { return (float)(int)(int8_t)(uint8_t)(w >> (8 * k)); }
 
 __device__ __forceinline__ float nib(uint32_t w, int shift) { return (float)((int)((w >> shift) & 0xfu) - 8); }
@@ -316,19 +338,22 @@ __device__ __forceinline__ void lds_dma4(const void *g, uint32_t lds)
 // Direct global -> LDS copy of a tile's kTile rows of RBD dwords (rows past
 // nkk repeat row nkk-1) to rows of LS >= RBD dwords: slot s = i*64 + lane of
 // load i is dword s % LS of row s / LS (padding slots repeat the row's last
-// dword), so the tile takes exactly LS loads.
+// dword), so the tile takes exactly LS loads.  [I0, I1) selects a range of
+// those loads, so that several waves can share one tile's copy.
 // (The lane index passes through an empty asm so that the per-slot row and
 // column are recomputed here, by an add-and-carry recurrence, instead of being
 // hoisted out of the tile loop into registers.)
-template <int RBD, int LS>
+template <int RBD, int LS, int I0 = 0, int I1 = LS>
 __device__ __forceinline__ void dma_rows4(const uint8_t *src, int pos_stride, int nkk, uint32_t lds_base, int lane)
 {
     static_assert(LS <= 64, "one row per load at least");
+    static_assert(0 <= I0 && I0 <= I1 && I1 <= LS, "load range");
     asm volatile("" : "+v"(lane));
-    int j = lane / LS, c = lane - (lane / LS) * LS;  // slot lane of load 0
-    constexpr int DJ = 64 / LS, DC = 64 % LS;         // slot advance of 64 per load
+    const int s0 = I0 * 64 + lane;
+    int j = s0 / LS, c = s0 - (s0 / LS) * LS;  // slot of load I0
+    constexpr int DJ = 64 / LS, DC = 64 % LS;  // slot advance of 64 per load
 #pragma unroll
-    for (int i = 0; i < LS; ++i) {
+    for (int i = I0; i < I1; ++i) {
         const int cc = c < RBD ? c : RBD - 1;
         const int jc = j < nkk ? j : nkk - 1;
         lds_dma4(src + (uint32_t)(jc * pos_stride + 4 * cc), lds_base + 256u * i);
@@ -381,11 +406,13 @@ __device__ __forceinline__ uint64_t dma_wraps(int lane)
 // dma_rows4 for a whole tile (kTile rows) that is followed by at least one
 // more position of the segment, with P >= 4*LS: no clamps; a row's padding
 // slots read the dwords after the row (inside the next row or position,
-// never used).  Per load: one bit test and one 24-bit multiply-add.
-template <int LS>
+// never used).  Per load: one bit test and one 24-bit multiply-add.  [I0, I1)
+// selects a range of the LS loads, as for dma_rows4.
+template <int LS, int I0 = 0, int I1 = LS>
 __device__ __forceinline__ void dma_rows4_full(const uint8_t *src, int P, uint64_t wrap, uint32_t lds_base, int lane)
 {
     static_assert(LS <= 64, "one row per load at least");
+    static_assert(0 <= I0 && I0 <= I1 && I1 <= LS, "load range");
     constexpr int DJ = 64 / LS, DC = 64 % LS;
     const int db = DJ * P + 4 * DC;
     const int xd = P - 4 * LS;  // >= 0, < 2^23
@@ -393,9 +420,15 @@ __device__ __forceinline__ void dma_rows4_full(const uint8_t *src, int P, uint64
     // (opaque to the compiler, so that the per-load offsets are recomputed
     // here rather than hoisted out of the tile loop into registers)
     asm volatile("" : "+v"(wlo), "+v"(whi), "+v"(lane));
-    uint32_t voff = __umul24((uint32_t)(lane / LS), (uint32_t)xd) + 4u * (uint32_t)lane;
+    // wraps before load I0: the low I0 bits of the plan
+    uint32_t wr0 = 0;
+    if constexpr (I0 > 0) {
+        constexpr uint64_t mask = (1ull << I0) - 1ull;
+        wr0 = (uint32_t)__builtin_popcountll(((uint64_t)whi << 32 | wlo) & mask);
+    }
+    uint32_t voff = __umul24((uint32_t)(lane / LS) + wr0, (uint32_t)xd) + 4u * (uint32_t)lane;
 #pragma unroll
-    for (int i = 0; i < LS; ++i) {
+    for (int i = I0; i < I1; ++i) {
         lds_dma4_s(src + (int64_t)i * db, voff, lds_base + 256u * i);
         if (i + 1 < LS) {
             const uint32_t bit = ((i < 32 ? wlo >> i : whi >> (i - 32)) & 1u);
@@ -1309,17 +1342,10 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                     kmx[i] = tl < nk - 1 ? (tl < -1 ? -1 : tl) : nk - 1;
                 }
             }
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int key = 16 * kb + (lane & 15);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = sv[kb][i];
-                    // (x in log2 units: s/c = x/capl, and 2 (s/c) log2 e = x * 2/c)
-                    if (cap > 0.f) x = capl * tanh_from_exp2(x * two_over_cap);
-                    sv[kb][i] = key <= kmx[i] ? x : -INFINITY;
-                }
-            }
+            if (cap > 0.f)
+                cap_mask_tile<true>(sv, kmx, lane & 15, capl, two_over_cap);
+            else
+                cap_mask_tile<false>(sv, kmx, lane & 15, capl, two_over_cap);
             // ---- online softmax: per-lane rows, then the wave-uniform rescale
             // (a row that has seen no key yet keeps m = -inf, l = 0: its
             // exponents are taken against 0 so that they give 0, not NaN)

@@ -5,10 +5,11 @@
 // With more than 16 query rows per KV head (sequences sharing one prefix, the
 // rows of a verify step or a prefill chunk), the general split kernel runs
 // each 16-row group of a head in its own workgroup, and every group decodes
-// the same key tiles.  Here a workgroup holds 2 KV heads x 4 row groups
-// (8 waves, one 16-row group each).  Per 64-key tile, a head's K and V rows
-// go global -> LDS once (one DMA each, issued by two of its waves); each of
-// the head's four waves decodes a quarter of them into the exact binary16
+// the same key tiles.  Here a workgroup holds one KV head x 4 row groups
+// (4 waves, one 16-row group each; two workgroups share a compute unit).
+// Per 64-key tile, the head's K and V rows go global -> LDS once (the tile's
+// direct-to-LDS loads shared out evenly over the four waves); each of the
+// head's four waves decodes a quarter of them into the exact binary16
 // matrix-core operands -- K codes of one 32-dim block (with its scales), and
 // d * code of one key pair per 8-key group split into high and low binary16
 // parts -- in LDS; after a workgroup barrier every wave runs its scores,
@@ -106,32 +107,49 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
         limv[i] = x;
     }
 
-    // raw tile DMA: K by row group 0 of the head, V by row group 1
-    constexpr int LSK1 = LSK > 0 ? LSK : 1, LSV1 = LSV > 0 ? LSV : 1;
-    const uint64_t kwrap = dma_wraps<LSK1>(lane), vwrap = dma_wraps<LSV1>(lane);
+    // raw tile DMA: the LSK K loads and LSV V loads of a tile, a quarter per
+    // wave (wave 0: K loads [0, KA), 1: [KA, KB), 2: K [KB, LSK) and V [0, VA),
+    // 3: V [VA, LSV))
+    static_assert(LSK > 0 && LSV > 0, "block K and V rows are staged in LDS");
+    constexpr int NQ = (LSK + LSV + 3) / 4;
+    constexpr int KA = NQ < LSK ? NQ : LSK, KB = 2 * NQ < LSK ? 2 * NQ : LSK;
+    constexpr int VA = 3 * NQ - LSK < 0 ? 0 : 3 * NQ - LSK < LSV ? 3 * NQ - LSK : LSV;
+    const uint64_t kwrap = dma_wraps<LSK>(lane), vwrap = dma_wraps<LSV>(lane);
     const bool kfull_ok = sg.k_pos >= 4 * LSK && sg.k_pos < (1 << 23);
     const bool vfull_ok = sg.v_pos >= 4 * LSV && sg.v_pos < (1 << 23);
     auto nk_at = [&](int64_t t) { return (int)(kend - t < kTile ? kend - t : kTile); };
     auto dma_raw = [&](int64_t t) {
         const int nkk = nk_at(t);
+        const bool whole = nkk == kTile && t + kTile < sg.n_keys;
+        int kps = (int)sg.k_pos, vps = (int)sg.v_pos;
+        asm volatile("" : "+s"(kps), "+s"(vps));
+        waitcnt_lgkm0();
+        const uint8_t *ks = kg + t * sg.k_pos, *vs = vg + t * sg.v_pos;
+        const uint32_t kbase = lds_addr(rawK), vbase = lds_addr(rawV);
         if (rgl == 0) {
-            int kps = (int)sg.k_pos;
-            asm volatile("" : "+s"(kps));
-            waitcnt_lgkm0();
-            const uint32_t base = lds_addr(rawK);
-            if (kfull_ok && nkk == kTile && t + kTile < sg.n_keys)
-                dma_rows4_full<LSK1>(kg + t * sg.k_pos, kps, kwrap, base, lane);
+            if (kfull_ok && whole)
+                dma_rows4_full<LSK, 0, KA>(ks, kps, kwrap, kbase, lane);
             else
-                dma_rows4<Sh::RBK / 4, LSK>(kg + t * sg.k_pos, kps, nkk, base, lane);
+                dma_rows4<Sh::RBK / 4, LSK, 0, KA>(ks, kps, nkk, kbase, lane);
         } else if (rgl == 1) {
-            int vps = (int)sg.v_pos;
-            asm volatile("" : "+s"(vps));
-            waitcnt_lgkm0();
-            const uint32_t base = lds_addr(rawV);
-            if (vfull_ok && nkk == kTile && t + kTile < sg.n_keys)
-                dma_rows4_full<LSV1>(vg + t * sg.v_pos, vps, vwrap, base, lane);
+            if (kfull_ok && whole)
+                dma_rows4_full<LSK, KA, KB>(ks, kps, kwrap, kbase, lane);
             else
-                dma_rows4<Sh::RBV / 4, LSV>(vg + t * sg.v_pos, vps, nkk, base, lane);
+                dma_rows4<Sh::RBK / 4, LSK, KA, KB>(ks, kps, nkk, kbase, lane);
+        } else if (rgl == 2) {
+            if (kfull_ok && whole)
+                dma_rows4_full<LSK, KB, LSK>(ks, kps, kwrap, kbase, lane);
+            else
+                dma_rows4<Sh::RBK / 4, LSK, KB, LSK>(ks, kps, nkk, kbase, lane);
+            if (vfull_ok && whole)
+                dma_rows4_full<LSV, 0, VA>(vs, vps, vwrap, vbase, lane);
+            else
+                dma_rows4<Sh::RBV / 4, LSV, 0, VA>(vs, vps, nkk, vbase, lane);
+        } else {
+            if (vfull_ok && whole)
+                dma_rows4_full<LSV, VA, LSV>(vs, vps, vwrap, vbase, lane);
+            else
+                dma_rows4<Sh::RBV / 4, LSV, VA, LSV>(vs, vps, nkk, vbase, lane);
         }
     };
 
@@ -165,7 +183,7 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
 
     for (; t0 < kend; t0 += kTile) {
         const int nk = nk_at(t0);
-        waitcnt_vm<0>();  // this wave's raw tile DMA (if any) has landed
+        waitcnt_vm<0>();  // this wave's share of the raw tile DMA has landed
         __syncthreads();  // the head's raw tiles are in LDS; every wave is done with the last tile's operands
 
         // ---- decode this wave's quarter of the head's operands
@@ -225,16 +243,10 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
             const int tl = limv[i] - (int)t0;
             kmx[i] = p.masked ? (tl < nk - 1 ? (tl < -1 ? -1 : tl) : nk - 1) : nk - 1;
         }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int key = 16 * kb + qi;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float x = sv[kb][i];
-                if (cap > 0.f) x = capl * tanh_from_exp2(x * two_over_cap);
-                sv[kb][i] = key <= kmx[i] ? x : -INFINITY;
-            }
-        }
+        if (cap > 0.f)
+            cap_mask_tile<true>(sv, kmx, qi, capl, two_over_cap);
+        else
+            cap_mask_tile<false>(sv, kmx, qi, capl, two_over_cap);
         float al[4], mex[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
