@@ -110,18 +110,18 @@ __device__ __forceinline__ float tanh_from_exp2(float two_y_log2)
     return fmaf(-2.f, __builtin_amdgcn_rcpf(t + 1.f), 1.f);
 }
 
-// Softcap (CAP) and causal mask of one 64-key score tile in the matrix-core
-// output layout: sv[kb][i] holds key 16 kb + qi of the lane's output row i
-// (scores in log2 units); keys past kmx[i] become -inf.  The cap is a template
-// argument: the caller branches once per tile on the uniform cap, so that a
-// tile without one carries no exp2 or reciprocal.
-template <bool CAP>
-__device__ __forceinline__ void cap_mask_tile(float (&sv)[4][4], const int (&kmx)[4], int qi, float capl,
+// Softcap (CAP) and causal mask of NKB 16-key blocks of a score tile in the
+// matrix-core output layout: sv[kb][i] holds tile key key0 + 16 kb of the
+// lane's output row i (scores in log2 units); keys past kmx[i] become -inf.
+// The cap is a template argument: the caller branches once per tile on the
+// uniform cap, so that a tile without one carries no exp2 or reciprocal.
+template <bool CAP, int NKB>
+__device__ __forceinline__ void cap_mask_tile(float (&sv)[NKB][4], const int (&kmx)[4], int key0, float capl,
                                               float two_over_cap)
 {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        const int key = 16 * kb + qi;
+    for (int kb = 0; kb < NKB; ++kb) {
+        const int key = key0 + 16 * kb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float x = sv[kb][i];
@@ -1343,9 +1343,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 }
             }
             if (cap > 0.f)
-                cap_mask_tile<true>(sv, kmx, lane & 15, capl, two_over_cap);
+                cap_mask_tile<true, 4>(sv, kmx, lane & 15, capl, two_over_cap);
             else
-                cap_mask_tile<false>(sv, kmx, lane & 15, capl, two_over_cap);
+                cap_mask_tile<false, 4>(sv, kmx, lane & 15, capl, two_over_cap);
             // ---- online softmax: per-lane rows, then the wave-uniform rescale
             // (a row that has seen no key yet keeps m = -inf, l = 0: its
             // exponents are taken against 0 so that they give 0, not NaN)

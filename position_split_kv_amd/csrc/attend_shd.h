@@ -180,6 +180,25 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
     const float capl = cap * kLog2e;
     const float two_over_cap = cap > 0.f ? 2.f / cap : 0.f;
     const int qi = lane & 15, gq = lane >> 4;
+    // LDS layouts free of bank conflicts.  V operands: wave rgl's key pair
+    // sits in dword (rgl + gq) mod 4 of a lane's 16-byte operand, so the four
+    // lane groups of one store hit different banks; the matrix core pairs A
+    // and B element by element within a lane group, so the probabilities of
+    // a group take the same rotated key order: 32-key block b, element
+    // 2 ((s + g) mod 4) + e of group g holds key 32 b + 8 s + 4 e + g.
+    // Probability rows: column c of row r is stored at c ^ swz(r), swz(r) =
+    // 4 ((2 (r / 4) + r) mod 4) + 16 (r / 4 mod 4), which keeps 4-column
+    // groups whole for the 16-byte reads and spreads both the stores and the
+    // reads over all banks.
+    const int vslot = (rgl + gq) & 3;
+    auto swz = [](int r) { return 4 * ((2 * (r >> 2) + r) & 3) + 16 * ((r >> 2) & 3); };
+    int pcol[4];  // rotated column of key 16 kb + qi
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int key = 16 * kb + qi, g = key & 3, e = (key >> 2) & 1, sk = (key >> 3) & 3;
+        pcol[kb] = 16 * g + 8 * (key >> 5) + 2 * ((sk + g) & 3) + e;
+    }
+    const int swr = swz(qi);
 
     for (; t0 < kend; t0 += kTile) {
         const int nk = nk_at(t0);
@@ -207,7 +226,7 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
                 const rkv_half2 h0 = d2 * x0, h1 = d2 * x1;
                 const rkv_half2 l0 = __builtin_elementwise_fma(d2, x0, -h0);
                 const rkv_half2 l1 = __builtin_elementwise_fma(d2, x1, -h1);
-                const int i0 = ((kb * 8 + 2 * p2) * 64 + lane) * 4 + rgl, i1 = i0 + 64 * 4;
+                const int i0 = ((kb * 8 + 2 * p2) * 64 + lane) * 4 + vslot, i1 = i0 + 64 * 4;
                 bVh[i0] = __builtin_bit_cast(uint32_t, h0);
                 bVh[i1] = __builtin_bit_cast(uint32_t, h1);
                 bVl[i0] = __builtin_bit_cast(uint32_t, l0);
@@ -270,8 +289,7 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
             for (int kb = 0; kb < 4; ++kb) {
                 const float pv = __builtin_amdgcn_exp2f(sv[kb][i] - mex[i]);
                 ps += pv;
-                const int key = 16 * kb + qi;
-                sPw[row * kTile + (key & 3) * 16 + (key >> 2)] = pv;
+                sPw[row * kTile + (pcol[kb] ^ swz(row))] = pv;
             }
             lrow[i] += ps;
         }
@@ -283,8 +301,8 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
         for (int kb = 0; kb < 2; ++kb) {
             rkv_half8 ph, pl;
             {
-                const float4 a = *(const float4 *)&sPw[qi * kTile + gq * 16 + 8 * kb];
-                const float4 b = *(const float4 *)&sPw[qi * kTile + gq * 16 + 8 * kb + 4];
+                const float4 a = *(const float4 *)&sPw[qi * kTile + ((gq * 16 + 8 * kb) ^ swr)];
+                const float4 b = *(const float4 *)&sPw[qi * kTile + ((gq * 16 + 8 * kb + 4) ^ swr)];
                 const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
