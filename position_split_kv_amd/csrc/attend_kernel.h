@@ -110,12 +110,14 @@ __device__ __forceinline__ float tanh_from_exp2(float two_y_log2)
     return fmaf(-2.f, __builtin_amdgcn_rcpf(t + 1.f), 1.f);
 }
 
-// Softcap (CAP) and causal mask of NKB 16-key blocks of a score tile in the
+// Softcap (CAP) and mask (MASK) of NKB 16-key blocks of a score tile in the
 // matrix-core output layout: sv[kb][i] holds tile key key0 + 16 kb of the
-// lane's output row i (scores in log2 units); keys past kmx[i] become -inf.
-// The cap is a template argument: the caller branches once per tile on the
-// uniform cap, so that a tile without one carries no exp2 or reciprocal.
-template <bool CAP, int NKB>
+// lane's output row i (scores in log2 units); with MASK, keys past kmx[i]
+// become -inf.  Both are template arguments: the caller branches once per
+// tile on the uniform cap and on whether the tile needs a mask (a causal
+// mask, or a tile shorter than kTile), so that a whole unmasked tile without
+// a cap costs nothing here.
+template <bool CAP, bool MASK, int NKB>
 __device__ __forceinline__ void cap_mask_tile(float (&sv)[NKB][4], const int (&kmx)[4], int key0, float capl,
                                               float two_over_cap)
 {
@@ -127,7 +129,8 @@ __device__ __forceinline__ void cap_mask_tile(float (&sv)[NKB][4], const int (&k
             float x = sv[kb][i];
             // (s/c = x/capl, and 2 (s/c) log2 e = x * 2/c)
             if constexpr (CAP) x = capl * tanh_from_exp2(x * two_over_cap);
-            sv[kb][i] = key <= kmx[i] ? x : -INFINITY;
+            if constexpr (MASK) x = key <= kmx[i] ? x : -INFINITY;
+            sv[kb][i] = x;
         }
     }
 }
@@ -1342,10 +1345,14 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                     kmx[i] = tl < nk - 1 ? (tl < -1 ? -1 : tl) : nk - 1;
                 }
             }
-            if (cap > 0.f)
-                cap_mask_tile<true, 4>(sv, kmx, lane & 15, capl, two_over_cap);
-            else
-                cap_mask_tile<false, 4>(sv, kmx, lane & 15, capl, two_over_cap);
+            if (p.masked || nk < kTile) {
+                if (cap > 0.f)
+                    cap_mask_tile<true, true>(sv, kmx, lane & 15, capl, two_over_cap);
+                else
+                    cap_mask_tile<false, true>(sv, kmx, lane & 15, capl, two_over_cap);
+            } else if (cap > 0.f) {
+                cap_mask_tile<true, false>(sv, kmx, lane & 15, capl, two_over_cap);
+            }
             // ---- online softmax: per-lane rows, then the wave-uniform rescale
             // (a row that has seen no key yet keeps m = -inf, l = 0: its
             // exponents are taken against 0 so that they give 0, not NaN)

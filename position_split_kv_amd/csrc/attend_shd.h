@@ -262,10 +262,14 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
             const int tl = limv[i] - (int)t0;
             kmx[i] = p.masked ? (tl < nk - 1 ? (tl < -1 ? -1 : tl) : nk - 1) : nk - 1;
         }
-        if (cap > 0.f)
-            cap_mask_tile<true>(sv, kmx, qi, capl, two_over_cap);
-        else
-            cap_mask_tile<false>(sv, kmx, qi, capl, two_over_cap);
+        if (p.masked || nk < kTile) {
+            if (cap > 0.f)
+                cap_mask_tile<true, true>(sv, kmx, qi, capl, two_over_cap);
+            else
+                cap_mask_tile<false, true>(sv, kmx, qi, capl, two_over_cap);
+        } else if (cap > 0.f) {
+            cap_mask_tile<true, false>(sv, kmx, qi, capl, two_over_cap);
+        }
         float al[4], mex[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
