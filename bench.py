@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE), each scaled
 # by that counter's reading for a plain 1 GiB copy; None once the kernel has
 # changed since the counters were taken.
-MEASURED_TRAFFIC_BYTES = 274_484_849
+MEASURED_TRAFFIC_BYTES = 274_503_862
 
 
 def log(msg):
