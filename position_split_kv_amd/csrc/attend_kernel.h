@@ -440,6 +440,35 @@ __device__ __forceinline__ void dma_rows4_full(const uint8_t *src, int P, uint64
     }
 }
 
+// The per-lane byte offsets (from the tile's first row) of loads [I0, I1) of
+// dma_rows4_full for position stride P, computed once so that a kernel with
+// registers to spare issues whole-tile copies with no address arithmetic:
+// off[i - I0] = i*(DJ*P + 4*DC) + 4*lane + (lane/LS + wraps before i)*(P - 4*LS).
+template <int LS, int I0, int I1>
+__device__ __forceinline__ void dma_plan_full(int P, uint64_t wrap, int lane, uint32_t *off)
+{
+    static_assert(0 <= I0 && I0 <= I1 && I1 <= LS, "load range");
+    constexpr int DJ = 64 / LS, DC = 64 % LS;
+    const uint32_t db = (uint32_t)(DJ * P + 4 * DC), xd = (uint32_t)(P - 4 * LS);
+    uint32_t wr0 = 0;
+    if constexpr (I0 > 0) wr0 = (uint32_t)__builtin_popcountll(wrap & ((1ull << I0) - 1ull));
+    uint32_t v = ((uint32_t)(lane / LS) + wr0) * xd + 4u * (uint32_t)lane + (uint32_t)I0 * db;
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+        off[i - I0] = v;
+        v += db + (uint32_t)((wrap >> i) & 1ull) * xd;
+    }
+}
+
+// Loads [I0, I0 + N) of a whole-tile copy from offsets planned by
+// dma_plan_full: one uniform base, one planned offset per load.
+template <int I0, int N>
+__device__ __forceinline__ void dma_issue_planned(const uint8_t *src, const uint32_t *off, uint32_t lds_base)
+{
+#pragma unroll
+    for (int j = 0; j < N; ++j) lds_dma4_s(src, off[j], lds_base + 256u * (I0 + j));
+}
+
 // s_waitcnt vmcnt(n) (0 <= n <= 63), other counters untouched.
 template <int N>
 __device__ __forceinline__ void waitcnt_vm()

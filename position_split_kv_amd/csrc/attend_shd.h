@@ -117,6 +117,28 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
     const uint64_t kwrap = dma_wraps<LSK>(lane), vwrap = dma_wraps<LSV>(lane);
     const bool kfull_ok = sg.k_pos >= 4 * LSK && sg.k_pos < (1 << 23);
     const bool vfull_ok = sg.v_pos >= 4 * LSV && sg.v_pos < (1 << 23);
+    // this wave's whole-tile load offsets, planned once: K loads first, then V
+    constexpr int NKW[4] = {KA, KB - KA, LSK - KB, 0}, NVW[4] = {0, 0, VA, LSV - VA};
+    constexpr int NW0 = NKW[0] + NVW[0], NW1 = NKW[1] + NVW[1], NW2 = NKW[2] + NVW[2], NW3 = NKW[3] + NVW[3];
+    constexpr int NPL = NW0 > NW1 ? (NW0 > NW2 ? (NW0 > NW3 ? NW0 : NW3) : (NW2 > NW3 ? NW2 : NW3))
+                                  : (NW1 > NW2 ? (NW1 > NW3 ? NW1 : NW3) : (NW2 > NW3 ? NW2 : NW3));
+    uint32_t doff[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) doff[j] = 0;
+    {
+        const int kp = (int)sg.k_pos, vp = (int)sg.v_pos;
+        if (rgl == 0) {
+            if (kfull_ok) dma_plan_full<LSK, 0, KA>(kp, kwrap, lane, doff);
+        } else if (rgl == 1) {
+            if (kfull_ok) dma_plan_full<LSK, KA, KB>(kp, kwrap, lane, doff);
+        } else if (rgl == 2) {
+            if (kfull_ok) dma_plan_full<LSK, KB, LSK>(kp, kwrap, lane, doff);
+            if (vfull_ok) dma_plan_full<LSV, 0, VA>(vp, vwrap, lane, doff + NKW[2]);
+        } else {
+            if (vfull_ok) dma_plan_full<LSV, VA, LSV>(vp, vwrap, lane, doff);
+        }
+    }
+    static_assert(NW0 + NW1 + NW2 + NW3 == LSK + LSV, "every load of a tile planned once");
     auto nk_at = [&](int64_t t) { return (int)(kend - t < kTile ? kend - t : kTile); };
     auto dma_raw = [&](int64_t t) {
         const int nkk = nk_at(t);
@@ -128,26 +150,26 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
         const uint32_t kbase = lds_addr(rawK), vbase = lds_addr(rawV);
         if (rgl == 0) {
             if (kfull_ok && whole)
-                dma_rows4_full<LSK, 0, KA>(ks, kps, kwrap, kbase, lane);
+                dma_issue_planned<0, KA>(ks, doff, kbase);
             else
                 dma_rows4<Sh::RBK / 4, LSK, 0, KA>(ks, kps, nkk, kbase, lane);
         } else if (rgl == 1) {
             if (kfull_ok && whole)
-                dma_rows4_full<LSK, KA, KB>(ks, kps, kwrap, kbase, lane);
+                dma_issue_planned<KA, KB - KA>(ks, doff, kbase);
             else
                 dma_rows4<Sh::RBK / 4, LSK, KA, KB>(ks, kps, nkk, kbase, lane);
         } else if (rgl == 2) {
             if (kfull_ok && whole)
-                dma_rows4_full<LSK, KB, LSK>(ks, kps, kwrap, kbase, lane);
+                dma_issue_planned<KB, LSK - KB>(ks, doff, kbase);
             else
                 dma_rows4<Sh::RBK / 4, LSK, KB, LSK>(ks, kps, nkk, kbase, lane);
             if (vfull_ok && whole)
-                dma_rows4_full<LSV, 0, VA>(vs, vps, vwrap, vbase, lane);
+                dma_issue_planned<0, VA>(vs, doff + NKW[2], vbase);
             else
                 dma_rows4<Sh::RBV / 4, LSV, 0, VA>(vs, vps, nkk, vbase, lane);
         } else {
             if (vfull_ok && whole)
-                dma_rows4_full<LSV, VA, LSV>(vs, vps, vwrap, vbase, lane);
+                dma_issue_planned<VA, LSV - VA>(vs, doff, vbase);
             else
                 dma_rows4<Sh::RBV / 4, LSV, VA, LSV>(vs, vps, nkk, vbase, lane);
         }
