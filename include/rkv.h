@@ -112,9 +112,10 @@ typedef struct rkv_kv_view {
  * n_seq * n_q_heads <= 65535.
  *
  * Several query rows of one sequence -- a prefill chunk or the draft tokens
- * of a verify step ("Rolling-KV: step/graph-level tail prefetch (design)": a
- * multi-row batch over the split cache, masked by absolute key position with
- * -inf for hidden keys) -- are passed as n_seq "sequences" over views with
+ * of a verify step ("F5 M7 -- Rolling KV", section "2026-07-12 -- #582-P2
+ * SHIPPED", bug-2161: the n_q > 1 path over window and tail; section
+ * "2026-07-14 -- bug-2172 SHIPPED": the mask is indexed by absolute key
+ * position, -inf for hidden keys) -- are passed as n_seq "sequences" over views with
  * sequence stride 0, each with its position in q_pos: the row at position p
  * sees the keys at absolute positions <= p (a key's absolute position is the
  * view's pos0 plus its index).  A row that sees no key of a call gets o = 0
@@ -394,8 +395,9 @@ int rkv_append_kv(int n_kv_heads, int head_dim, int n_tokens, int64_t pos0, int 
  *    spill costs more than the target drop; a smaller cache type should be
  *    chosen).
  *  - predicted_step_s = max(step compute, tail DMA) + c_engage_s, free zone =
- *    step compute * bw_eff, predicted_hidden = min(compute, DMA) / DMA ("F5
- *    M7 -- Rolling KV", section "Bounded win").
+ *    step compute * bw_eff, predicted_hidden = min(compute, DMA) / DMA
+ *    ("Rolling-KV: step/graph-level tail prefetch (design)", section "Bounded
+ *    win (be honest)").
  * Units: bytes, bytes per second, seconds.  Errors: RKV_E_INVAL (NULL,
  * non-positive or non-finite rates, a budget below two slots of one
  * position); the message is rkv_plan_last_error().

@@ -291,10 +291,12 @@ static int key_seen(const int64_t *q_pos, int b, int64_t t)
  *        written for the r-th listed row (or row r when rows is NULL).
  * q_to_kv: optional map query head -> KV head; NULL means contiguous groups
  *        h / (n_q_heads / n_kv_heads).
- * q_pos: optional causal mask by absolute key position ("Rolling-KV:
- *        step/graph-level tail prefetch (design)", the multi-row batch of a
- *        prefill chunk or a verify step, whose mask is indexed by absolute
- *        position with -inf for hidden keys).  Key t of the concatenation
+ * q_pos: optional causal mask by absolute key position for several query
+ *        rows ("F5 M7 -- Rolling KV", section "2026-07-14 -- bug-2172
+ *        SHIPPED": the streaming attention's mask is per cell and indexed by
+ *        absolute key position, -inf for hidden keys; section "2026-07-12 --
+ *        #582-P2 SHIPPED", bug-2161: the n_q > 1 prefill path over window and
+ *        tail).  Key t of the concatenation
  *        (t = 0, 1, ... over view 0's keys, then view 1's, ...) sits at
  *        absolute position t; sequence b's query sits at q_pos[b] and sees
  *        the keys with t <= q_pos[b].  NULL: every key is seen.

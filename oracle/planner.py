@@ -26,15 +26,17 @@ Written from the pages, step by step, in binary64:
    T* = (target_drop * t_resident - c_engage) * bw_eff, no spill when <= 0.
    A tail within T* is streamed; a larger one is rejected in favour of a
    smaller cache type ("quantize").
-7. Bounded win ("F5 M7 -- Rolling KV", section "Bounded win"): with perfect
+7. Bounded win ("Rolling-KV: step/graph-level tail prefetch (design)",
+   section "Bounded win (be honest)"): with perfect
    overlap a step takes max(step compute, tail DMA) instead of their sum;
    the free zone is step compute x bandwidth; the hidden fraction of the tail
    DMA is min(step compute, DMA) / DMA.  The fixed engagement cost c_engage
    is added to a step with a tail (the measured first-spill step).
 
-Parity unpinned: the weights term of t_resident.  The pages define
-t_resident as (active weights + resident KV) / device bandwidth but print no
-worked value of it, so no pin tells the sum from the KV term alone.
+The pages print no worked value of the weights term of t_resident; it is
+pinned by what the definition fixes (T* is affine in the weights with slope
+target_drop * bw_eff / vram_bw, and the drop falls with the weights in the
+ratio of the t_resident values), not by a printed number.
 """
 from __future__ import annotations
 

@@ -19,6 +19,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librkv.so")
+# the streaming-read probe the benchmark measures the read ceiling with (not
+# part of the attention library)
+PROBE_LIB = os.path.join(HERE, "librkvprobe.so")
 ARCH = os.environ.get("RKV_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -79,6 +82,12 @@ def build(jobs: int | None = None, verbose: bool = False, incremental: bool = Fa
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [_hipcc(), *FLAGS, "-shared", "-o", tmp, os.path.join(CSRC, "probe.hip")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -718,6 +718,12 @@ __device__ __forceinline__ float row16_sum(float x)
 // pre-multiplied by scale * log2(e) and split into binary16 high and low
 // parts (hi + lo keeps about 22 significant bits, so the products, exact in
 // the f32 accumulator, carry the f32 query).  Rows >= nr are zero.
+// Before the split every row is multiplied by a power of two 2^ex that puts
+// its largest magnitude in [2^14, 2^15): binary16 then neither overflows
+// (a query of any binary32 size) nor loses the low part to its subnormal
+// range (a tiny query); the scores of the row come out multiplied by 2^ex,
+// which unscale_rows takes off exactly.  ex is returned per lane (the
+// exponent of the lane's A-operand row).
 // Loads (mfma_q_load, issued early) and conversion (mfma_q_split).
 // (Unpredicated loads: a lane without a row reads a valid row and its values
 // are replaced by zero in mfma_q_split.)
@@ -734,18 +740,75 @@ __device__ __forceinline__ void mfma_q_load(const float *qrow, int lane, float (
     }
 }
 template <int D>
-__device__ __forceinline__ void mfma_q_split(const float (*x)[8], bool has, float sl2, rkv_half8 *qhi, rkv_half8 *qlo)
+__device__ __forceinline__ int mfma_q_split(const float (*x)[8], bool has, float sl2, rkv_half8 *qhi, rkv_half8 *qlo)
 {
+    float y[D / 32][8];
+    float mx = 0.f;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float y = has ? x[kk][e] * sl2 : 0.f;
-            const _Float16 h = (_Float16)y;
-            qhi[kk][e] = h;
-            qlo[kk][e] = (_Float16)(y - (float)h);
+            y[kk][e] = has ? x[kk][e] * sl2 : 0.f;
+            mx = fmaxf(mx, fabsf(y[kk][e]));
         }
+    // the row's values sit in lanes l, l ^ 16, l ^ 32, l ^ 48
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // mx = f 2^e with f in [0.5, 1): mx 2^(15 - e) is in [2^14, 2^15) (a zero row: any ex)
+    const int ex = 15 - __builtin_amdgcn_frexp_expf(mx);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float z = __builtin_amdgcn_ldexpf(y[kk][e], ex);
+            const _Float16 h = (_Float16)z;
+            qhi[kk][e] = h;
+            qlo[kk][e] = (_Float16)(z - (float)h);
+        }
+    return ex;
 }
+
+// The query-row exponents of a lane's four MFMA output rows (rows
+// 4*(lane/16) + i), from the lanes that hold those rows' A operands.
+__device__ __forceinline__ void mfma_out_row_exps(int ex, int lane, int (&oex)[4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oex[i] = __shfl(ex, 4 * (lane >> 4) + i, 64);
+}
+
+// Take the query rows' power-of-two factors off a score tile (exact).
+template <int NKB>
+__device__ __forceinline__ void unscale_rows(float (&sv)[NKB][4], const int (&oex)[4])
+{
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[kb][i] = __builtin_amdgcn_ldexpf(sv[kb][i], -oex[i]);
+}
+
+// Block-type V on the matrix cores takes d * code as a binary16 operand,
+// which overflows once |d * code| > 65504: q8_0 codes reach -128, so any
+// |d| >= 512 (binary16 exponent field >= 24) can; q4_0 codes reach -8, so
+// |d| >= 8192 (field >= 28).  The largest scale magnitude (bits without the
+// sign) of the blocks of this lane's key row in a staged V tile (row = lane,
+// NB blocks); keys past the segment's end repeat a real row.
+template <int VT, int NB>
+__device__ __forceinline__ uint32_t v_row_scale_max(const uint32_t *row)
+{
+    constexpr int BB = VT == kQ8 ? 34 : 18;
+    uint32_t m = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int o = BB * b;
+        const uint32_t w = row[o >> 2];
+        m = max(m, ((o & 2) ? (w >> 16) : w) & 0x7fffu);
+    }
+    return m;
+}
+template <int VT>
+__device__ __forceinline__ constexpr uint32_t v_scale_limit() { return VT == kQ8 ? 0x6000u : 0x7000u; }
+
+
 
 // Scores (log2 units) of the 64 keys of a DMA-staged f16 K tile against the
 // wave's query rows: sv[kb][i] = score of row 4*(lane/16) + i and key
@@ -939,6 +1002,30 @@ __device__ __forceinline__ float v_group_lds(const uint32_t *row, int dg, float 
     }
 }
 
+// P.V of one staged block-type V tile (64 keys, head_dim 128) in binary32 on
+// the VALU, accumulated into the matrix-core output layout (lane (g, n):
+// oc[c][i] = O[4g + i][8n + c]): the path for tiles whose scales would make
+// d * code overflow the binary16 operands.  Each product p * (d * code) is
+// one binary32 rounding (d * code is exact).  prob(r, k) is the probability
+// of row r and key k of the tile; rows >= rt are skipped.
+template <int VT, int LSV, typename ProbFn>
+__device__ __forceinline__ void pv_valu_tile(const uint32_t *sv_tile, ProbFn prob, int rt, int lane,
+                                             rkv_float4v (&oc)[8])
+{
+    const int g = lane >> 4, n = lane & 15;
+    for (int k = 0; k < kTile; ++k) {
+        float x[8];
+        const float dsc = v_group_lds<VT, 128>(sv_tile + k * LSV, n, x);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            const float pw = r < rt ? prob(r, k) : 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) oc[c][i] = fmaf(pw, dsc * x[c], oc[c][i]);
+        }
+    }
+}
+
 // Entry i of a 16-bit table in the kernel arguments, read as the aligned
 // 32-bit word that holds it: with a wave-uniform index that is a scalar load
 // (there are no 16-bit scalar loads), so its wait does not involve the vector
@@ -1111,6 +1198,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     static_assert(DS == 1 || MFMA_PVB, "dim slices need block-type K and V on the matrix cores");
     constexpr int NKQ = MFMA_S ? D / 32 : 1;
     rkv_half8 qhi[NKQ], qlo[NKQ];
+    int oex[4] = {0, 0, 0, 0};  // query-row exponents of the lane's MFMA output rows
     float mrow[4], lrow[4];
     const float capl = cap * kLog2e;                  // cap in log2 units
     const float two_over_cap = cap > 0.f ? 2.f / cap : 0.f;
@@ -1219,6 +1307,68 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     static_assert(2 * NV <= 63, "vmcnt range");
     const int sw = kswz<Sh::RBK>(lane);
 
+    // P.V of this wave's staged block-type V tile on the matrix cores
+    // (MFMA_PVB), for tiles whose block scales keep d * code inside binary16.
+    auto pv_blk = [&]() {
+        const int qi = lane & 15, gq = lane >> 4;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            rkv_half8 ph, pl;
+            if (qi < RT) {
+                const float4 a = *(const float4 *)&sPw[qi * kTile + gq * 16 + 8 * kb];
+                const float4 b = *(const float4 *)&sPw[qi * kTile + gq * 16 + 8 * kb + 4];
+                const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const _Float16 h = (_Float16)x[e];
+                    ph[e] = h;
+                    pl[e] = (_Float16)(x[e] - (float)h);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    ph[e] = (_Float16)0.f;
+                    pl[e] = (_Float16)0.f;
+                }
+            }
+            // B operands built two keys at a time: element e of bh[c] / bl[c]
+            // is d * code of dim 8n + c of key 4*(8kb + e) + g.  The codes are
+            // exact in binary16; hi = d * code rounded once (packed f16
+            // multiply) and lo = d * code - hi (packed f16 fma, exact while
+            // |d * code| <= 65504, which the scale test guarantees).
+            uint32_t hw[8][4], lw[8][4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                uint32_t ca[4], cb[4], da, db;
+                v_group_codes_f16<VT>(sV + (4 * (8 * kb + 2 * e2) + gq) * LSV, qi, ca, da);
+                v_group_codes_f16<VT>(sV + (4 * (8 * kb + 2 * e2 + 1) + gq) * LSV, qi, cb, db);
+                const rkv_half2 d2 = __builtin_bit_cast(rkv_half2, da | (db << 16));
+#pragma unroll
+                for (int p2 = 0; p2 < 4; ++p2) {
+                    // (key a, key b) of dims 2*p2 and 2*p2 + 1
+                    const rkv_half2 x0 = __builtin_bit_cast(rkv_half2, __builtin_amdgcn_perm(cb[p2], ca[p2], 0x05040100u));
+                    const rkv_half2 x1 = __builtin_bit_cast(rkv_half2, __builtin_amdgcn_perm(cb[p2], ca[p2], 0x07060302u));
+                    const rkv_half2 h0 = d2 * x0, h1 = d2 * x1;
+                    const rkv_half2 l0 = __builtin_elementwise_fma(d2, x0, -h0);
+                    const rkv_half2 l1 = __builtin_elementwise_fma(d2, x1, -h1);
+                    hw[2 * p2][e2] = __builtin_bit_cast(uint32_t, h0);
+                    hw[2 * p2 + 1][e2] = __builtin_bit_cast(uint32_t, h1);
+                    lw[2 * p2][e2] = __builtin_bit_cast(uint32_t, l0);
+                    lw[2 * p2 + 1][e2] = __builtin_bit_cast(uint32_t, l1);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const rkv_half8 bh = __builtin_bit_cast(rkv_half8, hw[c]);
+                const rkv_half8 bl = __builtin_bit_cast(rkv_half8, lw[c]);
+                oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bh, oc[c], 0, 0, 0);
+                oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bl, oc[c], 0, 0, 0);
+                oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bh, oc[c], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     // Query rows of the matrix-core path, loaded before the first tile's K / V
     // loads are issued.  The row of lane l is row l % 16 of the wave's group:
     // the row table is read with wave-uniform (scalar) loads and picked per
@@ -1268,7 +1418,8 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         // the pin keeps the conversion (and the waits for the query loads)
         // after the first tile's loads have been issued
         pin_v<8 * NKQ>(&qraw[0][0]);
-        mfma_q_split<D>(qraw, (lane & 15) < nr, sl2, qhi, qlo);
+        const int qex = mfma_q_split<D>(qraw, (lane & 15) < nr, sl2, qhi, qlo);
+        mfma_out_row_exps(qex, lane, oex);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             mrow[i] = -INFINITY;
@@ -1318,6 +1469,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             float sv[4][4];
             if constexpr (KT == kQ8 || KT == kQ4) mfma_scores_blk<KT, D, LSK>(sK, qhi, qlo, lane, sv);
             else mfma_scores<D, Sh::RBK>(sK, qhi, qlo, lane, sv);
+            // (before the slices exchange their partial scores: each slice
+            // scaled its query rows by its own power of two)
+            unscale_rows(sv, oex);
             if constexpr (BDMA) {
                 // this tile's V rows have landed (nothing else is in flight), so
                 // the next tile's K rows can load through the rest of the tile
@@ -1480,62 +1634,14 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
 
         if constexpr (MFMA_PVB) {
             // ---- P.V on the matrix cores, block-type V (see where MFMA_PVB is set)
-            const int qi = lane & 15, gq = lane >> 4;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                rkv_half8 ph, pl;
-                if (qi < RT) {
-                    const float4 a = *(const float4 *)&sPw[qi * kTile + gq * 16 + 8 * kb];
-                    const float4 b = *(const float4 *)&sPw[qi * kTile + gq * 16 + 8 * kb + 4];
-                    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const _Float16 h = (_Float16)x[e];
-                        ph[e] = h;
-                        pl[e] = (_Float16)(x[e] - (float)h);
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        ph[e] = (_Float16)0.f;
-                        pl[e] = (_Float16)0.f;
-                    }
-                }
-                // B operands built two keys at a time: element e of bh[c] / bl[c]
-                // is d * code of dim 8n + c of key 4*(8kb + e) + g.  The codes are
-                // exact in binary16; hi = d * code rounded once (packed f16
-                // multiply) and lo = d * code - hi (packed f16 fma, exact).
-                uint32_t hw[8][4], lw[8][4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    uint32_t ca[4], cb[4], da, db;
-                    v_group_codes_f16<VT>(sV + (4 * (8 * kb + 2 * e2) + gq) * LSV, qi, ca, da);
-                    v_group_codes_f16<VT>(sV + (4 * (8 * kb + 2 * e2 + 1) + gq) * LSV, qi, cb, db);
-                    const rkv_half2 d2 = __builtin_bit_cast(rkv_half2, da | (db << 16));
-#pragma unroll
-                    for (int p2 = 0; p2 < 4; ++p2) {
-                        // (key a, key b) of dims 2*p2 and 2*p2 + 1
-                        const rkv_half2 x0 = __builtin_bit_cast(rkv_half2, __builtin_amdgcn_perm(cb[p2], ca[p2], 0x05040100u));
-                        const rkv_half2 x1 = __builtin_bit_cast(rkv_half2, __builtin_amdgcn_perm(cb[p2], ca[p2], 0x07060302u));
-                        const rkv_half2 h0 = d2 * x0, h1 = d2 * x1;
-                        const rkv_half2 l0 = __builtin_elementwise_fma(d2, x0, -h0);
-                        const rkv_half2 l1 = __builtin_elementwise_fma(d2, x1, -h1);
-                        hw[2 * p2][e2] = __builtin_bit_cast(uint32_t, h0);
-                        hw[2 * p2 + 1][e2] = __builtin_bit_cast(uint32_t, h1);
-                        lw[2 * p2][e2] = __builtin_bit_cast(uint32_t, l0);
-                        lw[2 * p2 + 1][e2] = __builtin_bit_cast(uint32_t, l1);
-                    }
-                }
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const rkv_half8 bh = __builtin_bit_cast(rkv_half8, hw[c]);
-                    const rkv_half8 bl = __builtin_bit_cast(rkv_half8, lw[c]);
-                    oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bh, oc[c], 0, 0, 0);
-                    oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bl, oc[c], 0, 0, 0);
-                    oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bh, oc[c], 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            // A tile with a block scale large enough for d * code to overflow
+            // binary16 (rare) is multiplied out in binary32 on the VALU.
+            const uint32_t vmx = v_row_scale_max<VT, D / 32>(sV + lane * LSV);
+            if (__builtin_amdgcn_ballot_w64(vmx >= v_scale_limit<VT>()) == 0)
+                pv_blk();
+            else
+                pv_valu_tile<VT, LSV>(
+                    sV, [&](int r, int k) { return sPw[r * kTile + (k & 3) * 16 + (k >> 2)]; }, RT, lane, oc);
         } else if constexpr (MFMA_PV) {
             // ---- P.V on the matrix cores (layout described where MFMA_PV is set)
             const int qi = lane & 15, gq = lane >> 4;

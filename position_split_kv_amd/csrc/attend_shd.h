@@ -187,7 +187,8 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
     if (t0 < kend) dma_raw(t0);
     rkv_half8 qhi[D / 32], qlo[D / 32];
     pin_v<8 * (D / 32)>(&qraw[0][0]);
-    mfma_q_split<D>(qraw, (lane & 15) < nr, p.scale_log2, qhi, qlo);
+    int oex[4];  // query-row exponents of the lane's MFMA output rows
+    mfma_out_row_exps(mfma_q_split<D>(qraw, (lane & 15) < nr, p.scale_log2, qhi, qlo), lane, oex);
     float mrow[4], lrow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -227,6 +228,14 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
         waitcnt_vm<0>();  // this wave's share of the raw tile DMA has landed
         __syncthreads();  // the head's raw tiles are in LDS; every wave is done with the last tile's operands
 
+        // A tile with a V block scale large enough for d * code to overflow
+        // the binary16 operands (rare): every wave multiplies P.V out in
+        // binary32 from the raw V tile instead, which then stays in LDS until
+        // P.V is done (the next tile's DMA waits).  Every wave scans the whole
+        // tile, so all four take the same decision.
+        const bool vbig =
+            __builtin_amdgcn_ballot_w64(v_row_scale_max<VT, D / 32>(rawV + lane * LSV) >= v_scale_limit<VT>()) != 0;
+
         // ---- decode this wave's quarter of the head's operands
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -256,7 +265,7 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
             }
         }
         __syncthreads();  // the operands are in LDS; the raw tiles are free
-        if (t0 + kTile < kend) dma_raw(t0 + kTile);
+        if (!vbig && t0 + kTile < kend) dma_raw(t0 + kTile);
 
         // ---- scores on the matrix cores from the shared K operands
         float sv[4][4];
@@ -277,6 +286,7 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
                 for (int i = 0; i < 4; ++i) sv[kb][i] = fmaf(dsc, acc[i], sv[kb][i]);
             }
         }
+        unscale_rows(sv, oex);
         // ---- mask, cap, online softmax (as the general kernel)
         int kmx[4];
 #pragma unroll
@@ -322,6 +332,22 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
 
+        if (vbig) {
+            // ---- P.V in binary32 from the raw V tile (probability of row r,
+            // key k at its rotated, swizzled column), then the next tile's DMA
+            // once every wave is done with the raw tile
+            pv_valu_tile<VT, LSV>(
+                rawV,
+                [&](int r, int k) {
+                    const int kg4 = k & 3;
+                    const int col = 16 * kg4 + 8 * (k >> 5) + 2 * ((((k >> 3) & 3) + kg4) & 3) + ((k >> 2) & 1);
+                    return sPw[r * kTile + (col ^ swz(r))];
+                },
+                RT, lane, oc);
+            __syncthreads();
+            if (t0 + kTile < kend) dma_raw(t0 + kTile);
+            continue;
+        }
         // ---- P.V on the matrix cores from the shared V operands
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {

@@ -19,7 +19,8 @@
 //    a smaller cache type ("T*-aware auto rolling-KV spill", T* section).
 //  - Step time with perfect overlap max(step compute, tail DMA) + c_engage,
 //    free zone step compute x bw_eff, hidden fraction min(compute, DMA) / DMA
-//    ("F5 M7 -- Rolling KV", section "Bounded win").
+//    ("Rolling-KV: step/graph-level tail prefetch (design)", section
+//    "Bounded win (be honest)").
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>

@@ -206,3 +206,52 @@ def append_rows(n_tokens: int, n_kv_heads: int, head_dim: int, seed: int, device
         blocks[b, i] = top
         blocks[b, j] = top if kind[b] == 6 else -top
     return x.to(device)
+
+
+# Per-block magnitude factors of make_cache_wide (powers of two, so binary16
+# rounding of float data is unaffected apart from range).  "small" factors put
+# q8_0 / q4_0 block scales (amax/127, m/-8 of N(0,1) draws) in binary16's
+# subnormal range; "big" ones push q8_0 scales past 512 and q4_0 scales past
+# 8192, where d * code leaves binary16's range, while staying finite.
+WIDE_FACTORS = {
+    F32: ([2.0 ** -30, 2.0 ** -12, 1.0, 1.0], [2.0 ** 20, 2.0 ** 40]),
+    F16: ([2.0 ** -20, 2.0 ** -12, 1.0, 1.0], [2.0 ** 10, 2.0 ** 13]),
+    Q8_0: ([2.0 ** -18, 2.0 ** -12, 1.0, 1.0], [2.0 ** 14, 2.0 ** 16]),
+    Q4_0: ([2.0 ** -15, 2.0 ** -10, 1.0, 1.0], [2.0 ** 15, 2.0 ** 16]),
+}
+
+
+def make_cache_wide(n_keys: int, n_kv_heads: int, head_dim: int, dtype: int, seed: int, device="cpu",
+                    big_every: int = 3, neg128_frac: float = 1.0 / 16) -> Cache:
+    """A cache of N(0,1) draws whose 32-value blocks are scaled by powers of two
+    that span the storage type's range (WIDE_FACTORS): small factors anywhere,
+    big ones only in the keys of every ``big_every``-th run of 64 keys (so some
+    runs of keys hold only ordinary blocks).  For q8_0 a fraction
+    ``neg128_frac`` of the code bytes is then set to -128, a legal code the
+    quantiser never makes.  Generated on the CPU (bytes are then moved to
+    ``device``); the recipe is part of the data."""
+    g = generator(seed, "cpu")
+    x = torch.randn(n_keys, n_kv_heads, head_dim, generator=g, dtype=torch.float32)
+    small, big = WIDE_FACTORS[dtype]
+    nb = head_dim // 32
+    kind = torch.randint(0, len(small) + len(big), (n_keys, n_kv_heads, nb), generator=g)
+    keys = torch.arange(n_keys)
+    big_ok = ((keys // 64) % big_every == 0)[:, None, None]
+    table = torch.tensor(small + big, dtype=torch.float32)
+    kind = torch.where(big_ok | (kind < len(small)), kind, kind % len(small))
+    f = table[kind]  # [n][H][nb]
+    x = (x.view(n_keys, n_kv_heads, nb, 32) * f[..., None]).view(n_keys, n_kv_heads, head_dim)
+    data = encode(x, dtype)
+    if dtype == Q8_0 and neg128_frac > 0:
+        codes = data.view(n_keys, n_kv_heads, nb, 34)[..., 2:]
+        hit = torch.rand(codes.shape, generator=g) < neg128_frac
+        codes[hit] = 0x80
+    return Cache(data.to(device).contiguous(), dtype, n_keys, n_kv_heads, head_dim)
+
+
+def make_query_scaled(n_seq: int, n_q_heads: int, head_dim: int, seed: int, row_log2: list, device="cpu") -> torch.Tensor:
+    """make_query with row h of every sequence multiplied by 2^row_log2[h % len(row_log2)]."""
+    q = normal((n_seq, n_q_heads, head_dim), seed, "cpu")
+    f = torch.tensor([2.0 ** row_log2[h % len(row_log2)] for h in range(n_q_heads)], dtype=torch.float32)
+    return (q * f[None, :, None]).to(device)
+

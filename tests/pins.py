@@ -627,10 +627,11 @@ def pin_split_degenerate(orc):
 # ----------------------------------------------------------------------------- causal mask (several query rows)
 #
 # Rows of a prefill chunk or a verify step sit at absolute positions; a row at
-# position p sees the keys at positions 0 .. p and no later one ("Rolling-KV:
-# step/graph-level tail prefetch (design)": the multi-row batch is masked by
-# absolute key position, hidden keys at -inf).  Key t of the concatenated
-# views sits at position t.
+# position p sees the keys at positions 0 .. p and no later one ("F5 M7 --
+# Rolling KV", section "2026-07-14 -- bug-2172 SHIPPED": the mask is indexed by
+# absolute key position, hidden keys at -inf; section "2026-07-12 -- #582-P2
+# SHIPPED", bug-2161: the n_q > 1 path over window and tail).  Key t of the
+# concatenated views sits at position t.
 
 def _mask_case(seed, n=70, wc=40, hq=8, hkv=2, d=32, kt=synth.Q8_0, vt=synth.F16):
     kc, vc = host_pair(n, hkv, d, kt, vt, seed)

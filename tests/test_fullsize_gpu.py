@@ -11,7 +11,12 @@ oracle computes one by one (every sampled row still attends every key).
     the device, tail 65536 in pinned host memory in 8192-key tiles through a
     3-slot ring (2 layers);
   - shared prefix: 15 sequences x 32/8 heads; a 32768-key q8_0 / q4_0 prefix
-    stored once plus a private 2048-key f16 suffix per sequence.
+    stored once plus a private 2048-key f16 suffix per sequence, as one
+    rkv_attend_split call (the shared-decode launch over the prefix, the
+    suffix launch, one merge: the form the benchmark times) and as the
+    three-call form.
+
+Sampled rows cover every KV head.
 """
 import math
 
@@ -49,7 +54,9 @@ def test_qwen14b_f16_layer_full():
     o1, l1 = P.attend_split(desc, q, segs)
     o3, l3 = attend_views(desc, q, segs)
     torch.cuda.synchronize()
-    rows = [0, 4, 5, 13, 22, 26, 31, 39]  # every KV head's first or last row among them
+    # at least one row of every KV head (query head h attends KV head h // 5)
+    rows = [0, 4, 5, 13, 15, 19, 22, 26, 31, 39]
+    assert sorted({r // (Hq // Hkv) for r in rows}) == list(range(Hkv))
     views, _ = host_views(kc, vc)
     o_ref, l_ref = oracle.attend(q.cpu().numpy(), views, Hkv, 1.0 / math.sqrt(D), rows=rows)
     compare(o1, l1, o_ref, l_ref, rows=rows, what="one launch (bench step)")
@@ -106,7 +113,7 @@ def test_streamed_tail_full():
         torch.cuda.synchronize()
     finally:
         ring.close()
-    rows = [0, 9, 17, 24, 39]
+    rows = [0, 9, 10, 17, 24, 25, 30, 39]  # one row of every KV head or more
     for li, (kc, vc, q, _, _) in enumerate(layers):
         views = [P.view_of_cache(kc, vc, 0, wc)] + [P.view_of_cache(kc, vc, a, a + tile) for a in range(wc, n, tile)]
         o_r, l_r = attend_views(desc, q, views)
@@ -126,10 +133,15 @@ def test_shared_prefix_full():
     desc = P.Desc(S, Hq, Hkv, D, 1.0 / math.sqrt(D))
     prefix = P.view_of_cache(pk, pv)
     suffix = P.view_of_cache(sk, sv, 0, nsuf, nsuf * sk.pos_stride, nsuf * sv.pos_stride)
-    o, l = attend_views(desc, q, [prefix, suffix])
+    o1, l1 = P.attend_split(desc, q, [prefix, suffix])
+    o3, l3 = attend_views(desc, q, [prefix, suffix])
     torch.cuda.synchronize()
     pkh, pvh, skh, svh = pk.to("cpu"), pv.to("cpu"), sk.to("cpu"), sv.to("cpu")
     views = [oracle.view_of(pkh, pvh), oracle.view_of(skh, svh, 0, nsuf, nsuf * sk.pos_stride, nsuf * sv.pos_stride)]
-    rows = [0, 31, 32 * 7 + 5, 32 * 7 + 30, 32 * 14, 32 * 14 + 31]
+    # row b * Hq + h of sequence b attends KV head h // 4: one row of every KV head, spread over the
+    # sequences, plus the first and last rows
+    rows = [b * Hq + 4 * g + (g % 4) for g, b in zip(range(Hkv), (0, 3, 7, 11, 14, 1, 5, 9))] + [0, S * Hq - 1]
+    assert sorted({(r % Hq) // (Hq // Hkv) for r in rows}) == list(range(Hkv))
     o_ref, l_ref = oracle.attend(q.cpu().numpy(), views, Hkv, 1.0 / math.sqrt(D), rows=rows)
-    compare(o, l, o_ref, l_ref, rows=rows, what="prefix + suffix")
+    compare(o1, l1, o_ref, l_ref, rows=rows, what="one call (bench form): prefix + suffix")
+    compare(o3, l3, o_ref, l_ref, rows=rows, what="segment, segment, combine")

@@ -1,9 +1,10 @@
 """GPU: several query rows over the split cache with a causal mask.
 
 The rows of a prefill chunk or of a verify step sit at absolute positions and
-see the keys at positions up to their own ("Rolling-KV: step/graph-level tail
-prefetch (design)": the multi-row batch over the split cache, masked by
-absolute key position with -inf for hidden keys).  They are passed as n_seq
+see the keys at positions up to their own ("F5 M7 -- Rolling KV", section
+"2026-07-14 -- bug-2172 SHIPPED": the mask is indexed by absolute key
+position, -inf for hidden keys; section "2026-07-12 -- #582-P2 SHIPPED",
+bug-2161: the n_q > 1 path over window and tail).  They are passed as n_seq
 query rows over shared (sequence stride 0) window and tail views, each view
 carrying the absolute position of its first key.  Results must match the
 oracle's masked unsplit attention within the method's tolerances; a row

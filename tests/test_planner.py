@@ -168,7 +168,38 @@ def pin_plan_invariants(op):
         prev = p["window"]
 
 
-PINS = [pin_bw_eff_table, pin_drop_response, pin_bounded_win, pin_t5_verdict, pin_plan_invariants]
+def pin_weights_term(op):
+    """The weights term of t_resident ("T*-aware auto rolling-KV spill", T*
+    section: t_resident = (W_active + KV_resident) / vram_bw, the per-token
+    time with the cache resident).  The pages print no worked value of it, so
+    it is pinned by what the definition fixes: T* is affine in the weights
+    with slope target_drop * bw_eff / vram_bw (adding dW bytes of weights
+    raises T* by exactly that times dW); at a fixed tail the drop falls as the
+    weights grow, in the ratio t_resident(W1) / t_resident(W2); a step whose
+    weights alone already make 0.20 t_resident exceed c_engage may spill where
+    the same cache without weights may not (the page's short-context gate:
+    a tiny t_resident means T* <= 0)."""
+    L, n, bpk = 48, 16384, 4096
+    kv_total = L * n * bpk
+    vbw, lbw, c, comp = 1.8e12, 51.2e9, 8.2e-4, 5e-5
+    budget = kv_total // 2
+    base = op.plan(L, n, bpk, budget, 0, vbw, lbw, 0.0, c, comp, 0.2, 0.8)
+    for w in (1 << 30, 15 << 30, 60 << 30):
+        p = op.plan(L, n, bpk, budget, w, vbw, lbw, 0.0, c, comp, 0.2, 0.8)
+        assert abs(p["t_resident"] - (w + kv_total) / vbw) <= 1e-12 * p["t_resident"]
+        slope = (p["t_star"] - base["t_star"]) / w
+        assert abs(slope - 0.2 * lbw / vbw) <= 1e-9 * (0.2 * lbw / vbw), (w, slope)
+        assert p["drop"] < base["drop"]
+        assert abs(p["drop"] / base["drop"] - base["t_resident"] / p["t_resident"]) <= 1e-12
+    # short context: no weights -> T* <= 0 (quantize); 15 GiB of weights -> a spill is tolerable
+    small = op.plan(L, 256, bpk, L * 128 * bpk, 0, vbw, lbw, 0.0, c, comp, 0.2, 0.8)
+    heavy = op.plan(L, 256, bpk, L * 128 * bpk, 15 << 30, vbw, lbw, 0.0, c, comp, 0.2, 0.8)
+    assert small["t_star"] <= 0 and small["tactic"] == op.QUANTIZE
+    assert heavy["t_star"] > 0
+
+
+PINS = [pin_bw_eff_table, pin_drop_response, pin_bounded_win, pin_t5_verdict, pin_plan_invariants,
+        pin_weights_term]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -190,6 +221,9 @@ PLANNER_MUTANTS = {
                           "tactic=STREAM if tail_bytes >= out[\"t_star\"] else QUANTIZE"),
     "resident_strict": ("if kv_total <= kv_budget:", "if kv_total < kv_budget:"),
     "hidden_inverted": ("return min(step_compute, dma) / dma", "return min(step_compute, dma) / step_compute"),
+    "t_resident_no_weights": ("t_resident = (weights_bytes + kv_total) / vram_bw", "t_resident = kv_total / vram_bw"),
+    "t_resident_weights_twice": ("t_resident = (weights_bytes + kv_total) / vram_bw",
+                                 "t_resident = (2 * weights_bytes + kv_total) / vram_bw"),
 }
 
 
