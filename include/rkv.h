@@ -185,6 +185,29 @@ int rkv_attend_split(const rkv_attn_desc *desc, const float *q, int n_segments, 
                      float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * rkv_attend_split_noalloc -- rkv_attend_split for callers that cannot
+ * allocate device memory: code under stream or graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The same launches and arithmetic
+ * (the same bits as rkv_attend_split), with the per-split partials in a fixed
+ * array of the library's own instead of a caller's workspace: each GPU the
+ * library runs on holds one array of RKV_NOALLOC_MAX_BYTES, from module load
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * library allocation) and creates nothing; the caller passes q, o, lse and
+ * the segments as for rkv_attend_split.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it has to start at zero: every partial is written
+ * before it is read): calls that overlap in time on one GPU (on different
+ * streams, or from different threads without ordering) race and give wrong
+ * results.  A call whose partials need more than RKV_NOALLOC_MAX_BYTES (see
+ * rkv_attend_split_workspace_bytes) returns RKV_E_UNSUPPORTED and enqueues
+ * nothing.  Other errors as for rkv_attend_split.
+ */
+#define RKV_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+int rkv_attend_split_noalloc(const rkv_attn_desc *desc, const float *q, int n_segments, const rkv_kv_view *segs,
+                             float *o, float *lse, hipStream_t stream);
+
+/*
  * The two phases of rkv_attend_split as separate calls, for callers that
  * time them or put other work between them:
  *   rkv_attend_split_partials  the attention kernel: every key split writes

@@ -26,7 +26,10 @@ EXPORTS = (
     "rkv_ring_begin_step", "rkv_stream_tail_workspace_bytes", "rkv_stream_tail", "rkv_ring_end_step",
     "rkv_ring_schedule", "rkv_attend_split", "rkv_attend_split_workspace_bytes", "rkv_append_kv",
     "rkv_plan_residency", "rkv_plan_last_error", "rkv_attend_split_partials", "rkv_attend_split_merge",
+    "rkv_attend_split_noalloc",
 )
+# bytes of partials rkv_attend_split_noalloc can hold (RKV_NOALLOC_MAX_BYTES)
+RKV_NOALLOC_MAX_BYTES = 32 << 20
 RKV_RESIDENT, RKV_STREAM, RKV_QUANTIZE = 0, 1, 2
 RKV_LINK_BOUND, RKV_HOST_RAM_BOUND = 0, 1
 
@@ -106,6 +109,8 @@ def lib() -> ctypes.CDLL:
                                        vp, vp, vp, sz, vp]
         L.rkv_attend_split_partials.argtypes = [ctypes.POINTER(rkv_attn_desc), vp, ctypes.c_int,
                                                 ctypes.POINTER(rkv_kv_view), vp, vp, vp, sz, vp]
+        L.rkv_attend_split_noalloc.argtypes = [ctypes.POINTER(rkv_attn_desc), vp, ctypes.c_int,
+                                               ctypes.POINTER(rkv_kv_view), vp, vp, vp]
         L.rkv_attend_split_merge.argtypes = [ctypes.POINTER(rkv_attn_desc), ctypes.c_int, ctypes.POINTER(rkv_kv_view),
                                              vp, vp, vp, sz, vp]
         L.rkv_lse_combine.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i32, vp, vp, vp]
@@ -226,6 +231,12 @@ def rkv_attend_split(desc: Desc, q: torch.Tensor, segs, o: torch.Tensor, lse: to
     arr = _segs(segs)
     _check(lib().rkv_attend_split(ctypes.byref(desc.c), _addr(q), len(segs), arr, _addr(o), _addr(lse), _addr(ws),
                                   ws_bytes, _stream(stream)))
+
+
+def rkv_attend_split_noalloc(desc: Desc, q: torch.Tensor, segs, o: torch.Tensor, lse: torch.Tensor,
+                             stream=None) -> None:
+    _check(lib().rkv_attend_split_noalloc(ctypes.byref(desc.c), _addr(q), len(segs), _segs(segs), _addr(o),
+                                          _addr(lse), _stream(stream)))
 
 
 def rkv_attend_split_partials(desc: Desc, q: torch.Tensor, segs, o: torch.Tensor, lse: torch.Tensor,

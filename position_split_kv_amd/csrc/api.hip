@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <condition_variable>
 #include <deque>
@@ -463,6 +464,82 @@ int rkv_attend_split(const rkv_attn_desc *desc, const float *q, int n_segments, 
                      float *lse, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     return attend_split_phase(desc, q, n_segments, segs, o, lse, ws, ws_bytes, stream, 0);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free attention
+//
+// rkv_attend_split_noalloc keeps the per-split partials in this fixed device
+// array instead of a caller's workspace.  Every GPU the library runs on holds
+// its own copy (from module load until the process ends).  In host code the
+// name is only a stand-in: the device address of a GPU's copy comes from
+// hipGetSymbolAddress with that GPU current, taken once per device and kept.
+namespace {
+constexpr size_t kScratchBytes = RKV_NOALLOC_MAX_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+constexpr int kScratchDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_addr[kScratchDevices];
+
+// Device address of the current device's scratch array (looked up once per device).
+int scratch_of_current_device(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kScratchDevices) return fail(RKV_E_UNSUPPORTED, "device %d beyond %d", dev, kScratchDevices);
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (scratch)");
+            if (!p) return fail(RKV_E_HIP, "hipGetSymbolAddress (scratch) gave NULL");
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return RKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rkv_attend_split_noalloc(const rkv_attn_desc *desc, const float *q, int n_segments, const rkv_kv_view *segs,
+                             float *o, float *lse, hipStream_t stream)
+{
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if ((rc = check_segs(desc, n_segments, segs))) return rc;
+    if ((rc = check_out_args(q, o, lse))) return rc;
+    if ((rc = check_device(q, "q")) || (rc = check_device(o, "o")) || (rc = check_device(lse, "lse"))) return rc;
+    const rkv_kv_view *vp[kMaxSegs];
+    int64_t keys = 0;
+    for (int i = 0; i < n_segments; ++i) {
+        if (segs[i].n_keys > 0 && ((rc = check_device(segs[i].k, "K")) || (rc = check_device(segs[i].v, "V"))))
+            return rc;
+        vp[i] = &segs[i];
+        keys += segs[i].n_keys;
+    }
+    void *ws = nullptr;
+    if (keys > 0) {
+        CallPlan cp;
+        if ((rc = make_call_plan(desc, n_segments, vp, &cp, nullptr))) return rc;
+        if (cp.ws_bytes > kScratchBytes)
+            return fail(RKV_E_UNSUPPORTED, "the call needs %zu bytes of partials; the scratch array holds %zu",
+                        cp.ws_bytes, kScratchBytes);
+        if (cp.ws_bytes > 0 && (rc = scratch_of_current_device(&ws))) return rc;
+    }
+    return attend_impl(desc, q, n_segments, vp, o, lse, ws, kScratchBytes, stream);
 }
 
 int rkv_attend_split_partials(const rkv_attn_desc *desc, const float *q, int n_segments, const rkv_kv_view *segs,
