@@ -323,6 +323,32 @@ __device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds)
 #endif
 }
 
+// A raw buffer resource for loads at byte offsets (vector + scalar) from a
+// uniform base: no stride, no range limit (the offsets are the caller's to
+// keep inside the buffer), the data-format word of this GPU family.
+typedef uint32_t rkv_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
+}
+
+// The same with a uniform base and a per-lane 32-bit offset (global address
+// = sbase + voff): the address arithmetic of a whole tile stays scalar.
+__device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, uint32_t lds)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory");
+#else
+    (void)sbase;
+    (void)voff;
+    (void)lds;
+#endif
+}
+
 // The same for 4 bytes per lane (the dword lands at lds + 4 * lane).
 __device__ __forceinline__ void lds_dma4(const void *g, uint32_t lds)
 {
@@ -718,12 +744,15 @@ __device__ __forceinline__ float row16_sum(float x)
 // pre-multiplied by scale * log2(e) and split into binary16 high and low
 // parts (hi + lo keeps about 22 significant bits, so the products, exact in
 // the f32 accumulator, carry the f32 query).  Rows >= nr are zero.
-// Before the split every row is multiplied by a power of two 2^ex that puts
-// its largest magnitude in [2^14, 2^15): binary16 then neither overflows
-// (a query of any binary32 size) nor loses the low part to its subnormal
-// range (a tiny query); the scores of the row come out multiplied by 2^ex,
-// which unscale_rows takes off exactly.  ex is returned per lane (the
-// exponent of the lane's A-operand row).
+// A row whose largest magnitude lies outside [2^-2, 2^15) is first
+// multiplied by a power of two 2^ex that puts it in [2^14, 2^15): binary16
+// then neither overflows (a query of any binary32 size) nor loses the low
+// part to its subnormal range (a tiny query); the scores of such a row come
+// out multiplied by 2^ex, which unscale_rows takes off exactly.  Inside
+// [2^-2, 2^15) ex = 0: the high part of the largest values is normal and
+// their low part too, and a smaller value's error stays below 2^-24 of the
+// row's largest.  ex is returned per lane (the exponent of the lane's
+// A-operand row).
 // Loads (mfma_q_load, issued early) and conversion (mfma_q_split).
 // (Unpredicated loads: a lane without a row reads a valid row and its values
 // are replaced by zero in mfma_q_split.)
@@ -754,8 +783,9 @@ __device__ __forceinline__ int mfma_q_split(const float (*x)[8], bool has, float
     // the row's values sit in lanes l, l ^ 16, l ^ 32, l ^ 48
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // mx = f 2^e with f in [0.5, 1): mx 2^(15 - e) is in [2^14, 2^15) (a zero row: any ex)
-    const int ex = 15 - __builtin_amdgcn_frexp_expf(mx);
+    // mx = f 2^e with f in [0.5, 1): mx 2^(15 - e) is in [2^14, 2^15)
+    const int e = __builtin_amdgcn_frexp_expf(mx);
+    const int ex = (mx == 0.f || (e >= -1 && e <= 15)) ? 0 : 15 - e;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
@@ -823,14 +853,20 @@ __device__ __forceinline__ void mfma_scores(const uint32_t *tile, const rkv_half
     for (int kb = 0; kb < 4; ++kb) acc[kb] = rkv_float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
+        // the four B operands of the chunk are read together (one LDS wait per
+        // chunk), and the high-part products of the four key blocks go before
+        // the low-part ones, so consecutive MFMAs use different accumulators
+        rkv_half8 b[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int j = 16 * kb + (lane & 15);
             const int c = 4 * kk + (lane >> 4);
-            const rkv_half8 b = *(const rkv_half8 *)(tile + j * (RB / 4) + 4 * (c ^ kswz<RB>(j)));
-            acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi[kk], b, acc[kb], 0, 0, 0);
-            acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo[kk], b, acc[kb], 0, 0, 0);
+            b[kb] = *(const rkv_half8 *)(tile + j * (RB / 4) + 4 * (c ^ kswz<RB>(j)));
         }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi[kk], b[kb], acc[kb], 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo[kk], b[kb], acc[kb], 0, 0, 0);
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -929,16 +965,24 @@ __device__ __forceinline__ void mfma_scores_blk(const uint32_t *tile, const rkv_
         for (int i = 0; i < 4; ++i) sv[kb][i] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
+        // the four key blocks' operands of the chunk first, then the
+        // high-part products of all four, then the low-part ones
+        // (consecutive MFMAs use different accumulators)
+        rkv_half8 b[4];
+        float dsc[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            float dsc;
-            const rkv_half8 b = block_codes_f16<KT>(tile + (16 * kb + (lane & 15)) * LS, kk, lane >> 4, dsc);
-            rkv_float4v acc = rkv_float4v{0.f, 0.f, 0.f, 0.f};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi[kk], b, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo[kk], b, acc, 0, 0, 0);
+        for (int kb = 0; kb < 4; ++kb)
+            b[kb] = block_codes_f16<KT>(tile + (16 * kb + (lane & 15)) * LS, kk, lane >> 4, dsc[kb]);
+        rkv_float4v acc[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sv[kb][i] = fmaf(dsc, acc[i], sv[kb][i]);
-        }
+        for (int kb = 0; kb < 4; ++kb)
+            acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi[kk], b[kb], rkv_float4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo[kk], b[kb], acc[kb], 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[kb][i] = fmaf(dsc[kb], acc[kb][i], sv[kb][i]);
         // one block of 32 dims at a time: keeps the code reads of later blocks
         // from being hoisted (and held in registers) ahead of this one
         __builtin_amdgcn_sched_barrier(0);
@@ -1199,6 +1243,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     constexpr int NKQ = MFMA_S ? D / 32 : 1;
     rkv_half8 qhi[NKQ], qlo[NKQ];
     int oex[4] = {0, 0, 0, 0};  // query-row exponents of the lane's MFMA output rows
+    bool qscaled = false;         // some row of the wave has one (wave-uniform)
     float mrow[4], lrow[4];
     const float capl = cap * kLog2e;                  // cap in log2 units
     const float two_over_cap = cap > 0.f ? 2.f / cap : 0.f;
@@ -1226,9 +1271,28 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     uint32_t vreg[V_REG ? NSTEP : 1][VRW];
     int vps = (int)sg.v_pos;
     asm volatile("" : "+s"(vps));
+    // (whole tiles: lane offset ks * vps + dg * 4 VRW, computed once; the
+    // step's uniform part st * KPS * vps goes into the scalar base)
+    const uint32_t voff_lane = (uint32_t)ks * (uint32_t)vps + (uint32_t)(dg * (VRW * 4));
     auto load_v_into = [&](uint32_t (&dst)[V_REG ? NSTEP : 1][VRW], int64_t t, int nkk) {
         if constexpr (!V_REG) return;
         const uint8_t *vt = vg + t * sg.v_pos;
+        if (nkk == kTile) {
+            // buffer loads: the tile base in a scalar resource, the step in
+            // the scalar offset, the lane's offset in one vector register
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(vt);
+#pragma unroll
+            for (int st = 0; st < NSTEP; ++st) {
+                const rkv_u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_lane, st * KPS * vps, 0);
+                uint32_t *vr8 = &dst[st][0];
+                vr8[0] = a.x; vr8[1] = a.y; vr8[2] = a.z; vr8[3] = a.w;
+                if constexpr (VRW == 8) {
+                    const rkv_u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_lane + 16u, st * KPS * vps, 0);
+                    vr8[4] = b.x; vr8[5] = b.y; vr8[6] = b.z; vr8[7] = b.w;
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
             const int key = st * KPS + ks;
@@ -1247,6 +1311,18 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     auto nk_at = [&](int64_t t) { return (int)(kend - t < kTile ? kend - t : kTile); };
 
     constexpr bool KDMA = Sh::KDMA;
+    // Whole-tile K DMA offsets: load i covers rows R i + g (R = 64 / CPR,
+    // g = lane / CPR), chunk slot lane % CPR, whose chunk is swizzled by
+    // kswz(R i + g) = kswz(g) ^ kswz(R i) (no carries for these row counts),
+    // so the lane's offset is its row part plus (its chunk of load 0) ^ a
+    // constant of i; the rest of the address is uniform.
+    constexpr int KCPR = KDMA ? Sh::RBK / 16 : 16;
+    uint32_t krow = 0, kchunk = 0;
+    if constexpr (KDMA) {
+        static_assert(64 % KCPR == 0, "whole-tile DMA plan");
+        krow = (uint32_t)(lane / KCPR) * (uint32_t)sg.k_pos;
+        kchunk = 16u * (uint32_t)((lane % KCPR) ^ kswz<Sh::RBK>(lane / KCPR));
+    }
     // Issue the direct global -> LDS loads of a tile's K rows (rows past nkk
     // repeat row nkk-1).  Lane l of load i fills slot i*64 + l of the tile.
     auto dma_k = [&](int64_t t, int nkk) {
@@ -1258,6 +1334,13 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             const uint8_t *kt = kg + t * sg.k_pos;
             const uint32_t base = lds_addr(smem + w * Sh::STAGE_DW);
             waitcnt_lgkm0();  // this wave's earlier LDS reads of the buffer are done
+            if (nkk == kTile) {
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    lds_dma16_s(kt + (int64_t)i * (64 / CPR) * sg.k_pos,
+                                krow + (kchunk ^ (16u * (uint32_t)kswz<Sh::RBK>(i * (64 / CPR)))), base + 1024u * i);
+                return;
+            }
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int slot = i * 64 + lane;
@@ -1420,6 +1503,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         pin_v<8 * NKQ>(&qraw[0][0]);
         const int qex = mfma_q_split<D>(qraw, (lane & 15) < nr, sl2, qhi, qlo);
         mfma_out_row_exps(qex, lane, oex);
+        qscaled = __builtin_amdgcn_ballot_w64(qex != 0) != 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             mrow[i] = -INFINITY;
@@ -1471,7 +1555,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             else mfma_scores<D, Sh::RBK>(sK, qhi, qlo, lane, sv);
             // (before the slices exchange their partial scores: each slice
             // scaled its query rows by its own power of two)
-            unscale_rows(sv, oex);
+            if (qscaled) unscale_rows(sv, oex);
             if constexpr (BDMA) {
                 // this tile's V rows have landed (nothing else is in flight), so
                 // the next tile's K rows can load through the rest of the tile

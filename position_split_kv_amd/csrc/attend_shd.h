@@ -188,7 +188,9 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
     rkv_half8 qhi[D / 32], qlo[D / 32];
     pin_v<8 * (D / 32)>(&qraw[0][0]);
     int oex[4];  // query-row exponents of the lane's MFMA output rows
-    mfma_out_row_exps(mfma_q_split<D>(qraw, (lane & 15) < nr, p.scale_log2, qhi, qlo), lane, oex);
+    const int qex = mfma_q_split<D>(qraw, (lane & 15) < nr, p.scale_log2, qhi, qlo);
+    mfma_out_row_exps(qex, lane, oex);
+    const bool qscaled = __builtin_amdgcn_ballot_w64(qex != 0) != 0;  // some row has one (wave-uniform)
     float mrow[4], lrow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -275,18 +277,28 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
             for (int i = 0; i < 4; ++i) sv[kb][i] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+            // (the four key blocks' operands together, then the high-part
+            // products, then the low-part ones: consecutive MFMAs use
+            // different accumulators)
+            rkv_half8 b[4];
+            float dsc[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const rkv_half8 b = *(const rkv_half8 *)(bK + ((kb * 4 + kk) * 64 + lane) * 4);
-                const float dsc = dK[(kb * 4 + kk) * 16 + qi];
-                rkv_float4v acc = rkv_float4v{0.f, 0.f, 0.f, 0.f};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi[kk], b, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo[kk], b, acc, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sv[kb][i] = fmaf(dsc, acc[i], sv[kb][i]);
+                b[kb] = *(const rkv_half8 *)(bK + ((kb * 4 + kk) * 64 + lane) * 4);
+                dsc[kb] = dK[(kb * 4 + kk) * 16 + qi];
             }
+            rkv_float4v acc[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qhi[kk], b[kb], rkv_float4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qlo[kk], b[kb], acc[kb], 0, 0, 0);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[kb][i] = fmaf(dsc[kb], acc[kb][i], sv[kb][i]);
         }
-        unscale_rows(sv, oex);
+        if (qscaled) unscale_rows(sv, oex);
         // ---- mask, cap, online softmax (as the general kernel)
         int kmx[4];
 #pragma unroll
