@@ -115,7 +115,7 @@ def main():
                     help="skip the three-call comparison and the read-ceiling probe (profiling runs)")
     ap.add_argument("--no-streamed", action="store_true", help="skip the streamed-tail measurement")
     ap.add_argument("--no-others", action="store_true", help="skip the tiny, softcap-q8_0 and shared-prefix timings")
-    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "verify", "append", "ceiling"],
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c4-sweep", "c5", "verify", "append", "ceiling"],
                     help="run one workload alone and print its figures (profiling runs)")
     ap.add_argument("--reps", type=int, default=20, help="timed calls per workload of the other workloads")
     args = ap.parse_args()
@@ -144,6 +144,7 @@ def main():
               "c5": lambda: shared_prefix(P, synth, args.reps), "verify": lambda: verify_rows(P, synth, args.reps),
               "append": lambda: append_path(P, synth, args.reps),
               "c4": lambda: streamed_tail(P, synth, quick=True),
+              "c4-sweep": lambda: streamed_tail(P, synth),
               "ceiling": lambda: read_ceiling(None)}[args.only]
         print(json.dumps({args.only: fn(), "kernel_src": kernel_source_hash()}), flush=True)
         return
@@ -587,8 +588,9 @@ def streamed_tail(P, synth, L=48, steps=3, quick=False):
     a copy stream; between layers a dense-FFN stand-in (a 14336 x 4096 f16 GEMV,
     48 distinct matrices, repeated r times to about 0.2 ms).
 
-    T_c: the step with the tails already in HBM (same kernels: window, one
-    segment call per tile, combine; no copies).  T_d: the tile copies alone on
+    T_c: the step with the tails already in HBM (the same ring step with
+    device-resident tails, attended in place: the same tile cut, launches and
+    merge; no copies).  T_d: the tile copies alone on
     the copy stream.  T_p: the pipelined step through the ring.  Tail-hidden
     fraction h = (T_c + T_d - T_p) / T_d (clipped to [0, 1]); link fraction =
     (tail bytes / T_p) / R_link, with R_link the measured pinned H2D rate.
@@ -666,12 +668,12 @@ def streamed_tail(P, synth, L=48, steps=3, quick=False):
         n_t = (tail_keys + tile_keys - 1) // tile_keys
         kc0, vc0 = lay[0]["kc"], lay[0]["vc"]
         ring = P.Ring(B, tile_keys * kc0.pos_stride, tile_keys * vc0.pos_stride)
-        tails = [P.view_of_cache(l_["kh"], l_["vh"], 0, tail_keys) for l_ in lay]
+        ring_r = P.Ring(B, tile_keys * kc0.pos_stride, tile_keys * vc0.pos_stride)
+        tails = {"stream": [P.view_of_cache(l_["kh"], l_["vh"], 0, tail_keys, pos0=wc) for l_ in lay],
+                 "resident": [P.view_of_cache(l_["kc"], l_["vc"], wc, wc + tail_keys) for l_ in lay]}
+        rings = {"stream": ring, "resident": ring_r}
         slots = [(torch.empty(tile_keys * kc0.pos_stride, dtype=torch.uint8, device=dev),
                   torch.empty(tile_keys * vc0.pos_stride, dtype=torch.uint8, device=dev)) for _ in range(B)]
-        parts_o = [torch.empty(1, Hq, D, device=dev) for _ in range(n_t + 1)]
-        parts_l = [torch.empty(1, Hq, device=dev) for _ in range(n_t + 1)]
-        ws_t = P.workspace(P.rkv_attend_workspace_bytes(desc, P.view_of_cache(kc0, vc0, wc, wc + min(tile_keys, tail_keys))))
         ws_s = [None]
 
         def step(mode):
@@ -690,23 +692,15 @@ def streamed_tail(P, synth, L=48, steps=3, quick=False):
                             j += 1
                 cs.synchronize()
             else:
-                if mode == "stream":
-                    ring.rkv_ring_begin_step(tails, tile_keys)
-                    if ws_s[0] is None:
-                        ws_s[0] = P.workspace(ring.rkv_stream_tail_workspace_bytes(0, desc))
+                rg = rings[mode]
+                rg.rkv_ring_begin_step(tails[mode], tile_keys)
+                if ws_s[0] is None:
+                    ws_s[0] = P.workspace(rg.rkv_stream_tail_workspace_bytes(0, desc))
                 for li, l_ in enumerate(lay):
                     P.rkv_attend_segment(desc, l_["q"], P.view_of_cache(l_["kc"], l_["vc"], 0, wc), o_w, l_w, ws_w, stream)
-                    if mode == "stream":
-                        ring.rkv_stream_tail(li, desc, l_["q"], o_w, l_w, outs[li][0], outs[li][1], ws_s[0], stream)
-                    else:
-                        for t in range(n_t):
-                            a0, a1 = wc + t * tile_keys, wc + min(tail_keys, (t + 1) * tile_keys)
-                            P.rkv_attend_segment(desc, l_["q"], P.view_of_cache(l_["kc"], l_["vc"], a0, a1),
-                                                 parts_o[t + 1], parts_l[t + 1], ws_t, stream)
-                        P.rkv_lse_combine([o_w] + parts_o[1:], [l_w] + parts_l[1:], outs[li][0], outs[li][1], D, stream)
+                    rg.rkv_stream_tail(li, desc, l_["q"], o_w, l_w, outs[li][0], outs[li][1], ws_s[0], stream)
                     ffn(li)
-                if mode == "stream":
-                    ring.rkv_ring_end_step()
+                rg.rkv_ring_end_step()
                 torch.cuda.synchronize()
             return time.perf_counter() - t0
 
@@ -719,6 +713,7 @@ def streamed_tail(P, synth, L=48, steps=3, quick=False):
                         times[mode].append(dt)
         finally:
             ring.close()
+            ring_r.close()
         t_c, t_d, t_p = (statistics.median(times[m]) for m in ("resident", "copy", "stream"))
         tail_bytes = L * tail_keys * (kc0.pos_stride + vc0.pos_stride)
         h = min(1.0, max(0.0, (t_c + t_d - t_p) / t_d))

@@ -258,9 +258,9 @@ int rkv_dequant_q4_0(const void *blocks, int64_t n_values, float *out, hipStream
  * stream.  The copy into a slot waits until the attention of the slot's
  * previous tile has read it; the attention of a tile waits for its slot's
  * copy_done event ("F5 M7 -- Rolling KV", "CUDA stream graph").  The first of
- * these waits is taken on the host: the kernel after a tile's split kernel
- * (the partial merge, or a one-thread signal kernel) writes the tile's
- * sequence number to a per-slot word in pinned host memory, and a copier
+ * these waits is taken on the host: a one-thread kernel after a tile's
+ * attention kernel writes the tile's sequence number to a per-slot word in
+ * pinned host memory, and a copier
  * thread owned by the ring watches that word and then enqueues the slot's
  * copies (DMA-engine hipMemcpyAsync) and copy_done record.  So the copy
  * stream carries no wait on a compute-queue event (such a wait costs a
@@ -289,14 +289,18 @@ int rkv_ring_create(int n_slots, size_t slot_k_bytes, size_t slot_v_bytes, hipSt
  * NULL is a no-op. */
 int rkv_ring_destroy(rkv_ring *ring);
 
-/* Plan one step: the tails of n_layers layers (host_tails[l], each in pinned
- * host memory, one sequence or shared by all sequences), cut into tiles of
- * tile_keys keys (the last tile of a layer may be partial; an empty tail has
- * no tiles).  Hands the first n_slots copies to the copier (each waits for
- * the previous step's last use of its slot).  The host buffers must stay
- * alive and unchanged until the step's attention has completed.
- * Errors: RKV_E_INVAL (device pointer, tile larger than a slot, misaligned),
- * RKV_E_STATE (previous step not ended). */
+/* Plan one step: the tails of n_layers layers (host_tails[l], one sequence
+ * or shared by all sequences), cut into tiles of tile_keys keys (the last tile
+ * of a layer may be partial; an empty tail has no tiles; at most 63 tiles per
+ * layer).  A tail in pinned host memory is streamed through the slots; a tail
+ * in device memory is attended where it is, tile by tile, with the same
+ * launches and the same merge and no copies (the step's results are then the
+ * same bits as with that tail streamed).  Hands the first n_slots copies to
+ * the copier (each waits for the previous step's last use of its slot).  The
+ * tail buffers must stay alive and unchanged until the step's attention has
+ * completed.  Errors: RKV_E_INVAL (pageable host memory, a streamed tile
+ * larger than a slot, misaligned), RKV_E_UNSUPPORTED (more than 63 tiles in a
+ * layer), RKV_E_STATE (previous step not ended). */
 int rkv_ring_begin_step(rkv_ring *ring, int n_layers, const rkv_kv_view *host_tails, int64_t tile_keys);
 
 /* Workspace bytes rkv_stream_tail needs for a layer of the current plan. */
@@ -315,11 +319,15 @@ int rkv_stream_tail_workspace_bytes(const rkv_ring *ring, int layer, const rkv_a
  * streams.  A slot whose previous reader has not finished within 60 s of the
  * copier starting to wait fails the ring's copier (RKV_E_HIP at the next
  * call).
- * Finally (o_window, lse_window) and the tiles' results are merged with
- * rkv_lse_combine in the order window, tile 0, tile 1, ...  lse_window may be
- * NULL (no window; o_window is then ignored).  The result equals, bit for
- * bit, rkv_attend_segment on each tile resident in device memory followed by
- * that combine, whatever n_slots is.  Layers must be consumed in plan order.
+ * Each tile's key splits write their partials into one set for the layer,
+ * and one fixed-order merge (the S2 combine applied to the window's result
+ * and every split's partial, in the order window, tile 0's splits, tile 1's
+ * splits, ...) gives o and lse; lse_window may be NULL (no window; o_window is
+ * then ignored).  A slot is released by a one-thread kernel after the tile's
+ * attention kernel.  The result does not depend on n_slots, and equals, bit
+ * for bit, the same call with the layer's tail in device memory (attended in
+ * place); it agrees with rkv_attend_segment per tile + rkv_lse_combine to
+ * rounding.  Layers must be consumed in plan order.
  * Errors: RKV_E_STATE (layer out of order / no step), RKV_E_INVAL, RKV_E_HIP
  * (also a failure of the copier).  A failure once the tiles have started
  * aborts the step: later calls return RKV_E_STATE until the next begin_step.

@@ -306,10 +306,12 @@ class Ring:
         except Exception:
             pass
 
-    def rkv_ring_begin_step(self, host_tails, tile_keys: int) -> None:
-        arr = (rkv_kv_view * max(1, len(host_tails)))(*host_tails)
+    def rkv_ring_begin_step(self, tails, tile_keys: int) -> None:
+        """tails: one view per layer, in pinned host memory (streamed) or in
+        device memory (attended in place)."""
+        arr = (rkv_kv_view * max(1, len(tails)))(*tails)
         self._tails = arr
-        _check(lib().rkv_ring_begin_step(self.h, len(host_tails), arr, tile_keys))
+        _check(lib().rkv_ring_begin_step(self.h, len(tails), arr, tile_keys))
 
     def rkv_stream_tail_workspace_bytes(self, layer: int, desc: Desc) -> int:
         out = ctypes.c_size_t(0)

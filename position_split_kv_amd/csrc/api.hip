@@ -231,6 +231,7 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
         prm->n_splits = pl->n_splits;
         prm->split_off = 0;
         prm->n_splits_all = pl->n_splits;
+        prm->direct = pl->n_splits == 1;
         prm->n_rg = pl->n_rg;
         prm->rows_per_g = rmax;
         prm->n_rows_total = (int32_t)pl->n_rows_total;
@@ -304,11 +305,33 @@ int make_call_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, C
     if (off > 65535) return fail(RKV_E_UNSUPPORTED, "segments too long for one call");
     cp->n_splits_all = off;
     if (prm)
-        for (int j = 0; j < cp->g.n; ++j) prm[j].n_splits_all = off;
+        for (int j = 0; j < cp->g.n; ++j) {
+            prm[j].n_splits_all = off;
+            prm[j].direct = off == 1;
+        }
     const int64_t rows = (int64_t)d->n_seq * d->n_q_heads;
     cp->acc_bytes = off > 1 ? ((size_t)off * rows * d->head_dim * sizeof(float) + 255) & ~(size_t)255 : 0;
     cp->ml_bytes = off > 1 ? (size_t)off * rows * sizeof(float2) : 0;
     cp->ws_bytes = cp->acc_bytes + cp->ml_bytes;
+    return RKV_OK;
+}
+
+// The split-kernel launches of a call plan (one per group of segments).
+int launch_plan(const CallPlan &cp, const SplitParams *prm, const rkv_attn_desc *d, const float *q, float *part_acc,
+                float2 *part_ml, float *o, float *lse, hipStream_t stream)
+{
+    for (int j = 0; j < cp.g.n; ++j) {
+        const SplitPlan &pl = cp.pl[j];
+        if (!split_supported(cp.g.v[j][0]->k_type, cp.g.v[j][0]->v_type, d->head_dim, pl.rt))
+            return fail(RKV_E_UNSUPPORTED, "no kernel for this (type, head_dim, rows)");
+        const dim3 grid((unsigned)pl.n_splits, (unsigned)(pl.n_hg * pl.n_rg), (unsigned)pl.z);
+        if (pl.shd)
+            RKV_HIP(launch_split_shd(cp.g.v[j][0]->k_type, cp.g.v[j][0]->v_type, grid, q, part_acc, part_ml, o, lse,
+                                     prm[j], stream));
+        else
+            RKV_HIP(launch_split(cp.g.v[j][0]->k_type, cp.g.v[j][0]->v_type, d->head_dim, pl.rt, grid, q, part_acc,
+                                 part_ml, o, lse, prm[j], stream));
+    }
     return RKV_OK;
 }
 
@@ -343,17 +366,7 @@ int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view
             return fail(RKV_E_UNSUPPORTED, "no kernel for this (type, head_dim, rows)");
     float *part_acc = (float *)ws;
     float2 *part_ml = (float2 *)((char *)ws + cp.acc_bytes);
-    if (phase != 2)
-        for (int j = 0; j < cp.g.n; ++j) {
-            const SplitPlan &pl = cp.pl[j];
-            const dim3 grid((unsigned)pl.n_splits, (unsigned)(pl.n_hg * pl.n_rg), (unsigned)pl.z);
-            if (pl.shd)
-                RKV_HIP(launch_split_shd(cp.g.v[j][0]->k_type, cp.g.v[j][0]->v_type, grid, q, part_acc, part_ml, o, lse,
-                                         prm[j], stream));
-            else
-                RKV_HIP(launch_split(cp.g.v[j][0]->k_type, cp.g.v[j][0]->v_type, d->head_dim, pl.rt, grid, q,
-                                     part_acc, part_ml, o, lse, prm[j], stream));
-        }
+    if (phase != 2 && (rc = launch_plan(cp, prm, d, q, part_acc, part_ml, o, lse, stream))) return rc;
     if (phase == 1) return RKV_OK;
     if (cp.n_splits_all > 1)
         RKV_HIP(launch_reduce(d->head_dim, n_rows, cp.n_splits_all, part_acc, part_ml, o, lse, stream, done,
@@ -665,6 +678,7 @@ struct rkv_ring {
     // plan of the current step
     bool in_step = false;
     std::vector<rkv_kv_view> tails;
+    std::vector<char> inplace;  // per layer: the tail is in device memory and is attended where it is
     int64_t tile_keys = 0;
     struct Item {
         int layer;
@@ -813,10 +827,61 @@ void ring_free(rkv_ring *r)
     delete r;
 }
 
-// Bytes of the tile partials kept in the stream_tail workspace.
-size_t tile_parts_bytes(int64_t n_tiles, int64_t n_rows, int D)
+// The tiles of a layer's tail in the current step: how many, and tile t's
+// view -- the ring slot it is copied into (streamed tails; planning only
+// needs the sizes, so slot 0 stands in for a slot not yet known) or the tail
+// itself at the tile's keys (a tail in device memory, attended in place).
+// The sequence strides are 0: a tail is shared by all sequences or n_seq == 1.
+int64_t layer_tiles(const rkv_ring *r, int layer)
 {
-    return (((size_t)n_tiles * n_rows * (D + 1) * sizeof(float)) + 255) & ~(size_t)255;
+    if (r->inplace[layer]) return (r->tails[layer].n_keys + r->tile_keys - 1) / r->tile_keys;
+    return r->first_item[layer + 1] - r->first_item[layer];
+}
+
+rkv_kv_view tile_view(const rkv_ring *r, int layer, int64_t t, int slot)
+{
+    const rkv_kv_view &tail = r->tails[layer];
+    rkv_kv_view v = tail;
+    const int64_t k0 = t * r->tile_keys;
+    v.n_keys = std::min(r->tile_keys, tail.n_keys - k0);
+    v.pos0 = tail.pos0 + k0;
+    if (r->inplace[layer]) {
+        v.k = (const char *)tail.k + k0 * tail.k_pos_stride;
+        v.v = (const char *)tail.v + k0 * tail.v_pos_stride;
+    } else {
+        v.k = r->sk[slot];
+        v.v = r->sv[slot];
+    }
+    v.k_seq_stride = 0;
+    v.v_seq_stride = 0;
+    return v;
+}
+
+// Partials of a layer's tail: every tile's key splits, one set of per-split
+// partials for the whole layer (tile t's splits at offset off[t]); total
+// splits, and the workspace bytes they take.
+int layer_tail_plan(const rkv_ring *r, int layer, const rkv_attn_desc *d, std::vector<int> *off, int *total,
+                    size_t *acc_bytes, size_t *bytes)
+{
+    const int64_t nt = layer_tiles(r, layer);
+    off->assign((size_t)nt + 1, 0);
+    int64_t tot = 0;
+    for (int64_t t = 0; t < nt; ++t) {
+        const rkv_kv_view v = tile_view(r, layer, t, 0);
+        const rkv_kv_view *vp = &v;
+        CallPlan cp;
+        int rc = make_call_plan(d, 1, &vp, &cp, nullptr);
+        if (rc) return rc;
+        (*off)[t] = (int)tot;
+        tot += cp.n_splits_all;
+        if (tot > 65535) return fail(RKV_E_UNSUPPORTED, "layer %d: tail tiles need more than 65535 splits", layer);
+    }
+    (*off)[nt] = (int)tot;
+    const int64_t rows = (int64_t)d->n_seq * d->n_q_heads;
+    *total = (int)tot;
+    *acc_bytes = ((size_t)tot * rows * d->head_dim * sizeof(float) + 255) & ~(size_t)255;
+    *bytes = *acc_bytes + (size_t)tot * rows * sizeof(float2);
+    return RKV_OK;
 }
 
 }  // namespace
@@ -921,6 +986,7 @@ int rkv_ring_begin_step(rkv_ring *r, int n_layers, const rkv_kv_view *tails, int
     if (tile_keys < 1) return fail(RKV_E_INVAL, "tile_keys must be >= 1");
     std::vector<rkv_ring::Item> items;
     std::vector<int64_t> first(n_layers + 1, 0);
+    std::vector<char> inplace(n_layers, 0);
     for (int l = 0; l < n_layers; ++l) {
         const rkv_kv_view &t = tails[l];
         first[l] = (int64_t)items.size();
@@ -928,15 +994,20 @@ int rkv_ring_begin_step(rkv_ring *r, int n_layers, const rkv_kv_view *tails, int
         if (t.n_keys == 0) continue;
         if (!t.k || !t.v || t.k_pos_stride <= 0 || t.v_pos_stride <= 0)
             return fail(RKV_E_INVAL, "tail %d: bad pointers or strides", l);
+        if ((t.n_keys + tile_keys - 1) / tile_keys > kMaxParts - 1)
+            return fail(RKV_E_UNSUPPORTED, "tail %d: more than %d tiles", l, kMaxParts - 1);
+        const int mk = mem_kind(t.k), mv = mem_kind(t.v);
+        if (mk == 2 && mv == 2) {  // device memory: attended in place, no copies
+            inplace[l] = 1;
+            continue;
+        }
+        if (mk != 1 || mv != 1)
+            return fail(RKV_E_INVAL, "tail %d must be pinned host memory (or device memory, attended in place)", l);
         if ((size_t)(std::min(tile_keys, t.n_keys) * t.k_pos_stride) > r->slot_k ||
             (size_t)(std::min(tile_keys, t.n_keys) * t.v_pos_stride) > r->slot_v)
             return fail(RKV_E_INVAL, "tail %d: a tile does not fit a slot", l);
-        if (mem_kind(t.k) != 1 || mem_kind(t.v) != 1)
-            return fail(RKV_E_INVAL, "tail %d must be pinned host memory", l);
         for (int64_t k0 = 0; k0 < t.n_keys; k0 += tile_keys)
             items.push_back({l, k0, std::min(tile_keys, t.n_keys - k0), r->appends[l]});
-        if ((int64_t)items.size() - first[l] > kMaxParts - 1)
-            return fail(RKV_E_UNSUPPORTED, "tail %d: more than %d tiles", l, kMaxParts - 1);
     }
     first[n_layers] = (int64_t)items.size();
     {
@@ -948,6 +1019,7 @@ int rkv_ring_begin_step(rkv_ring *r, int n_layers, const rkv_kv_view *tails, int
         if (r->err != hipSuccess) return hip_fail(r->err, r->err_what);
         r->base += (int64_t)r->items.size();
         r->tails.assign(tails, tails + n_layers);
+        r->inplace.swap(inplace);
         r->items.swap(items);
         r->first_item.swap(first);
     }
@@ -966,18 +1038,13 @@ int rkv_stream_tail_workspace_bytes(const rkv_ring *r, int layer, const rkv_attn
     if (layer < 0 || layer >= (int)r->tails.size()) return fail(RKV_E_INVAL, "layer out of range");
     int rc = check_desc(desc);
     if (rc) return rc;
-    const int64_t n_tiles = r->first_item[layer + 1] - r->first_item[layer];
-    const int64_t n_rows = (int64_t)desc->n_seq * desc->n_q_heads;
-    size_t attend = 0;
-    if (n_tiles > 0) {
-        rkv_kv_view v = r->tails[layer];
-        v.n_keys = std::min<int64_t>(r->tile_keys, v.n_keys);
-        v.k = r->sk[0];
-        v.v = r->sv[0];
-        if ((rc = rkv_attend_workspace_bytes(desc, &v, &attend))) return rc;
+    if (layer_tiles(r, layer) > 0) {
+        if ((rc = check_view_fields(desc, &r->tails[layer]))) return rc;
     }
-    *bytes = tile_parts_bytes(n_tiles, n_rows, desc->head_dim) + attend;
-    return RKV_OK;
+    std::vector<int> off;
+    int total = 0;
+    size_t acc = 0;
+    return layer_tail_plan(r, layer, desc, &off, &total, &acc, bytes);
 }
 
 int rkv_stream_tail(rkv_ring *r, int layer, const rkv_attn_desc *desc, const float *q, const float *o_window,
@@ -992,8 +1059,8 @@ int rkv_stream_tail(rkv_ring *r, int layer, const rkv_attn_desc *desc, const flo
     if (lse_window && !o_window) return fail(RKV_E_INVAL, "o_window is NULL");
     const int D = desc->head_dim;
     const int64_t n_rows = (int64_t)desc->n_seq * desc->n_q_heads;
-    const int64_t j0 = r->first_item[layer], j1 = r->first_item[layer + 1];
-    const int64_t n_tiles = j1 - j0;
+    const int64_t j0 = r->first_item[layer];
+    const int64_t n_tiles = layer_tiles(r, layer);
     const rkv_kv_view &tail = r->tails[layer];
     if (n_tiles > 0) {
         if (desc->n_seq > 1 && (tail.k_seq_stride != 0 || tail.v_seq_stride != 0))
@@ -1012,61 +1079,75 @@ int rkv_stream_tail(rkv_ring *r, int layer, const rkv_attn_desc *desc, const flo
     if (lse_window && ((rc = check_device(o_window, "o_window")) || (rc = check_device(lse_window, "lse_window"))))
         return rc;
 
-    float *tile_o = (float *)ws;
-    float *tile_lse = tile_o + n_tiles * n_rows * D;
-    char *attend_ws = (char *)ws + tile_parts_bytes(n_tiles, n_rows, D);
-    const size_t attend_bytes = ws_bytes - tile_parts_bytes(n_tiles, n_rows, D);
-    for (int64_t j = j0; j < j1; ++j) {
-        const int s = (int)(j % r->B);
-        rkv_kv_view v = tail;
-        v.k = r->sk[s];
-        v.v = r->sv[s];
-        v.n_keys = r->items[j].nk;
-        v.pos0 = tail.pos0 + r->items[j].k0;
-        v.k_seq_stride = 0;
-        v.v_seq_stride = 0;
+    // Every tile's key splits write into one set of per-split partials for
+    // the layer (tile t at offset off[t]); one merge then takes the window's
+    // result and all of them, in that order.
+    std::vector<int> off;
+    int total = 0;
+    size_t acc_bytes = 0, plan_bytes = 0;
+    if ((rc = layer_tail_plan(r, layer, desc, &off, &total, &acc_bytes, &plan_bytes))) return rc;
+    float *part_acc = (float *)ws;
+    float2 *part_ml = (float2 *)((char *)ws + acc_bytes);
+    const bool inplace = r->inplace[layer] != 0;
+    for (int64_t t = 0; t < n_tiles; ++t) {
+        const int64_t j = j0 + t;
+        const int s = inplace ? 0 : (int)(j % r->B);
+        const rkv_kv_view v = tile_view(r, layer, t, s);
         // A failure from here on aborts the step (later calls: RKV_E_STATE),
         // so that nothing waits for a copy that will not be requested.
-        if ((rc = check_view_fields(desc, &v)) || (rc = wait_enqueued(r, j))) {
+        if ((rc = check_view_fields(desc, &v)) || (!inplace && (rc = wait_enqueued(r, j)))) {
             r->in_step = false;
             return rc;
         }
-        hipError_t e = hipStreamWaitEvent(cs, r->copy_done[s], 0);
-        if (e != hipSuccess) {
-            r->in_step = false;
-            return hip_fail(e, "hipStreamWaitEvent (copy_done)");
+        if (!inplace) {
+            hipError_t e = hipStreamWaitEvent(cs, r->copy_done[s], 0);
+            if (e != hipSuccess) {
+                r->in_step = false;
+                return hip_fail(e, "hipStreamWaitEvent (copy_done)");
+            }
         }
         const rkv_kv_view *vp = &v;
-        const int64_t g = r->base + j;
-        if ((rc = attend_impl(desc, q, 1, &vp, tile_o + (j - j0) * n_rows * D, tile_lse + (j - j0) * n_rows, attend_ws,
-                              attend_bytes, cs, r->progress + s, (uint64_t)(g + 1)))) {
+        CallPlan cp;
+        SplitParams prm[kMaxSegs];
+        rc = make_call_plan(desc, 1, &vp, &cp, prm);
+        if (!rc && (cp.g.n != 1 || cp.n_splits_all != off[t + 1] - off[t]))
+            rc = fail(RKV_E_STATE, "tile plan changed between the workspace query and the launch");
+        if (!rc) {
+            prm[0].split_off = off[t];
+            prm[0].n_splits_all = total;
+            prm[0].direct = 0;
+            rc = launch_plan(cp, prm, desc, q, part_acc, part_ml, o, lse, cs);
+        }
+        // the slot is free once the tile's split kernel has finished
+        if (!rc && !inplace) {
+            const int64_t g = r->base + j;
+            hipError_t e = launch_signal(r->progress + s, (uint64_t)(g + 1), cs);
+            if (e != hipSuccess) rc = hip_fail(e, "slot release signal");
+            else {
+                std::lock_guard<std::mutex> lk(r->mu);
+                r->last_user[s] = g;
+            }
+        }
+        if (rc) {
             // a kernel of the tile may have been launched: let it finish
             // before the slot can be refilled (its progress may never come)
             (void)hipStreamSynchronize(cs);
             r->in_step = false;
             return rc;
         }
-        {
-            std::lock_guard<std::mutex> lk(r->mu);
-            r->last_user[s] = g;
-        }
-        if (j + r->B < (int64_t)r->items.size()) request_copy(r, j + r->B);
+        if (!inplace && j + r->B < (int64_t)r->items.size()) request_copy(r, j + r->B);
     }
-    CombineParts parts;
-    memset(&parts, 0, sizeof parts);
-    int np = 0;
-    if (lse_window) {
-        parts.o[np] = o_window;
-        parts.lse[np++] = lse_window;
-    }
-    for (int64_t t = 0; t < n_tiles; ++t) {
-        parts.o[np] = tile_o + t * n_rows * D;
-        parts.lse[np++] = tile_lse + t * n_rows;
-    }
-    if (np == 0) {
-        RKV_HIP(launch_fill_empty(D, n_rows, o, lse, cs));
+    if (total > 0) {
+        RKV_HIP(launch_reduce(D, n_rows, total, part_acc, part_ml, o, lse, cs, nullptr, 0,
+                              lse_window ? o_window : nullptr, lse_window));
+    } else if (lse_window) {
+        CombineParts parts;
+        memset(&parts, 0, sizeof parts);
+        parts.o[0] = o_window;
+        parts.lse[0] = lse_window;
+        RKV_HIP(launch_combine(1, parts, n_rows, D, o, lse, cs));  // a single part: copied bit for bit
     } else {
-        RKV_HIP(launch_combine(np, parts, n_rows, D, o, lse, cs));
+        RKV_HIP(launch_fill_empty(D, n_rows, o, lse, cs));
     }
     r->next_layer++;
     return RKV_OK;

@@ -174,6 +174,9 @@ hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q
 // issued before the maximum is known.  If `done` is given, one thread writes
 // done_value there (host-visible memory, system scope) as the kernel starts:
 // the split kernel before it has then finished reading its key tiles.
+// o_x / lse_x (optional): a normalised part (O and natural-log LSE, i.e. the
+// partial acc = O, m = LSE log2 e, l = 1), merged first; lse = -inf gives it
+// weight 0.
 __device__ __forceinline__ float block_max256(float v, float *sw)
 {
 #pragma unroll
@@ -187,7 +190,7 @@ __device__ __forceinline__ float block_max256(float v, float *sw)
 __global__ void __launch_bounds__(256)
 rkv_reduce_kernel(const float *__restrict__ part_acc, const float2 *__restrict__ part_ml, int n_splits,
                   int64_t n_rows, int D, float *__restrict__ o, float *__restrict__ lse, uint64_t *done,
-                  uint64_t done_value)
+                  uint64_t done_value, const float *__restrict__ o_x, const float *__restrict__ lse_x)
 {
     if (done && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
         __hip_atomic_store(done, done_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -211,7 +214,8 @@ rkv_reduce_kernel(const float *__restrict__ part_acc, const float2 *__restrict__
     if (grp < n_splits) load(grp, ml, x);
     float mloc = -INFINITY;
     for (int sp = t; sp < n_splits; sp += 256) mloc = fmaxf(mloc, ml_row[sp].x);
-    const float M = block_max256(mloc, sW);
+    const float mx = lse_x ? lse_x[row] * 1.4426950408889634f : -INFINITY;  // the extra part, log2 units
+    const float M = fmaxf(block_max256(mloc, sW), mx);
     float l = 0.f;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int base = grp; base < n_splits; base += 32 * 8) {
@@ -234,6 +238,12 @@ rkv_reduce_kernel(const float *__restrict__ part_acc, const float2 *__restrict__
     if (grp == 0) {
         float L = 0.f;
         float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (mx != -INFINITY) {
+            const float w = __builtin_amdgcn_exp2f(mx - M);
+            const float4 x = *(const float4 *)(o_x + row * D + d0);
+            L = w;
+            s = make_float4(x.x * w, x.y * w, x.z * w, x.w * w);
+        }
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
             L += sL[j];
@@ -250,11 +260,13 @@ rkv_reduce_kernel(const float *__restrict__ part_acc, const float2 *__restrict__
 }
 
 hipError_t launch_reduce(int d, int64_t n_rows, int n_splits, const float *pa, const float2 *pm, float *o,
-                         float *lse, hipStream_t s, uint64_t *done, uint64_t done_value)
+                         float *lse, hipStream_t s, uint64_t *done, uint64_t done_value, const float *o_x,
+                         const float *lse_x)
 {
     if (d % 32 || n_rows <= 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)n_rows, (unsigned)(d / 32)), block(256);
-    hipLaunchKernelGGL(rkv_reduce_kernel, grid, block, 0, s, pa, pm, n_splits, n_rows, d, o, lse, done, done_value);
+    hipLaunchKernelGGL(rkv_reduce_kernel, grid, block, 0, s, pa, pm, n_splits, n_rows, d, o, lse, done, done_value,
+                       o_x, lse_x);
     return hipGetLastError();
 }
 

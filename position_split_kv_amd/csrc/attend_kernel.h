@@ -1836,7 +1836,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             // the wave writes its rows straight from the MFMA output layout
             // (lane (g, n) holds dims 8n .. 8n+7 of rows 4g .. 4g+3).  The
             // values are those the LDS merge would produce for one wave.
-            const bool single = p.n_splits_all == 1;
+            const bool single = p.direct != 0;
             const int64_t pbase = (int64_t)(p.split_off + (int)blockIdx.x) * p.n_rows_total;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1920,7 +1920,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     }
     // Thread t finalises (head slot, row, dim) triples, merging the waves of
     // the head slot; a wave with no keys has m = -inf and weight 0.
-    const bool single = p.n_splits_all == 1;
+    const bool single = p.direct != 0;
     const int64_t pbase = (int64_t)(p.split_off + (int)blockIdx.x) * p.n_rows_total;
     const int hpw = 1 << p.hpw_log2;
     for (int i = threadIdx.x; i < hpw * RT * D; i += 64 * NW) {

@@ -394,7 +394,7 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
         l[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), 16 * (r >> 2)));
         m[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mrow[r & 3]), 16 * (r >> 2)));
     }
-    const bool single = p.n_splits_all == 1;
+    const bool single = p.direct != 0;
     const int64_t pbase = (int64_t)(p.split_off + (int)blockIdx.x) * p.n_rows_total;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

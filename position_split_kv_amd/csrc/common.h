@@ -50,7 +50,8 @@ struct SplitParams {
     int32_t n_segs;
     int32_t n_splits;      // total key splits over all segments (grid x)
     int32_t split_off;     // index of this launch's first split among all partials of the call
-    int32_t n_splits_all;  // partials of the call (all its launches); 1: the result is written directly
+    int32_t n_splits_all;  // partials of the call (all its launches)
+    int32_t direct;        // 1: the launch is the call's only split and writes o / lse directly
     int32_t n_rg;          // row groups per KV head
     int32_t rows_per_g;    // stride of rowtab between KV heads
     int32_t n_rows_total;  // n_seq * n_q_heads
@@ -97,8 +98,11 @@ hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q
                         float2 *part_ml, float *o, float *lse, const SplitParams &p, hipStream_t stream);
 // done (optional): host-visible memory that receives done_value once the split
 // kernel before the merge has finished (a progress signal for the tail ring).
+// o_x / lse_x (optional): one more, already normalised part (an O and its
+// LSE, natural log) merged before the splits, e.g. a window's result.
 hipError_t launch_reduce(int d, int64_t n_rows, int n_splits, const float *part_acc, const float2 *part_ml,
-                         float *o, float *lse, hipStream_t stream, uint64_t *done = nullptr, uint64_t done_value = 0);
+                         float *o, float *lse, hipStream_t stream, uint64_t *done = nullptr, uint64_t done_value = 0,
+                         const float *o_x = nullptr, const float *lse_x = nullptr);
 // Write done_value to done (system scope) once the work before it on the stream has finished.
 hipError_t launch_signal(uint64_t *done, uint64_t done_value, hipStream_t stream);
 bool split_supported(int kt, int vt, int d, int rt);

@@ -98,27 +98,31 @@ def test_streamed_tail_full():
         vh.copy_(vc.data[wc:])
         layers.append((kc, vc, q, synth.Cache(kh, kc.dtype, n - wc, Hkv, D), synth.Cache(vh, vc.dtype, n - wc, Hkv, D)))
     torch.cuda.synchronize()
-    ring = P.Ring(B, tile * layers[0][0].pos_stride, tile * layers[0][1].pos_stride)
-    outs = []
-    try:
-        ring.rkv_ring_begin_step([P.view_of_cache(t[3], t[4]) for t in layers], tile)
-        for li, (kc, vc, q, _, _) in enumerate(layers):
-            o_w, l_w = P.attend(desc, q, P.view_of_cache(kc, vc, 0, wc))
-            ws = P.workspace(ring.rkv_stream_tail_workspace_bytes(li, desc))
-            o = torch.empty_like(q)
-            lse = torch.empty(S, Hq, device=DEV)
-            ring.rkv_stream_tail(li, desc, q, o_w, l_w, o, lse, ws)
-            outs.append((o, lse))
-        ring.rkv_ring_end_step()
-        torch.cuda.synchronize()
-    finally:
-        ring.close()
+
+    def ring_step(tails):
+        ring = P.Ring(B, tile * layers[0][0].pos_stride, tile * layers[0][1].pos_stride)
+        outs = []
+        try:
+            ring.rkv_ring_begin_step(tails, tile)
+            for li, (kc, vc, q, _, _) in enumerate(layers):
+                o_w, l_w = P.attend(desc, q, P.view_of_cache(kc, vc, 0, wc))
+                ws = P.workspace(ring.rkv_stream_tail_workspace_bytes(li, desc))
+                o = torch.empty_like(q)
+                lse = torch.empty(S, Hq, device=DEV)
+                ring.rkv_stream_tail(li, desc, q, o_w, l_w, o, lse, ws)
+                outs.append((o, lse))
+            ring.rkv_ring_end_step()
+            torch.cuda.synchronize()
+        finally:
+            ring.close()
+        return outs
+
+    outs = ring_step([P.view_of_cache(t[3], t[4], pos0=wc) for t in layers])
+    res = ring_step([P.view_of_cache(t[0], t[1], wc, n) for t in layers])
     rows = [0, 9, 10, 17, 24, 25, 30, 39]  # one row of every KV head or more
     for li, (kc, vc, q, _, _) in enumerate(layers):
-        views = [P.view_of_cache(kc, vc, 0, wc)] + [P.view_of_cache(kc, vc, a, a + tile) for a in range(wc, n, tile)]
-        o_r, l_r = attend_views(desc, q, views)
-        torch.cuda.synchronize()
-        assert torch.equal(outs[li][0], o_r) and torch.equal(outs[li][1], l_r), f"layer {li}: streamed != resident"
+        assert torch.equal(outs[li][0], res[li][0]) and torch.equal(outs[li][1], res[li][1]), \
+            f"layer {li}: streamed != resident"
         hv, _ = host_views(kc, vc)
         o_ref, l_ref = oracle.attend(q.cpu().numpy(), hv, Hkv, 1.0 / math.sqrt(D), rows=rows)
         compare(outs[li][0], outs[li][1], o_ref, l_ref, rows=rows, what=f"streamed layer {li}")

@@ -98,8 +98,9 @@ def test_masked_single_split_empty_rows():
 
 def test_masked_stream_tail():
     """A verify step of 6 rows with the tail in pinned host memory, streamed in
-    tiles: equal bit for bit to the same tiles attended resident (each tile's
-    view starting at its absolute position), and to the oracle."""
+    tiles: equal bit for bit to the same ring step with the tail resident in
+    device memory (attended in place, each tile at its absolute position), to
+    the segment calls per tile + combine to rounding, and to the oracle."""
     Hq, Hkv, D, n, wc, tile, B = 40, 8, 128, 3000, 1200, 512, 3
     pos = [wc - 3, wc + 2, 2000, n - 3, n - 2, n - 1]
     note(f"masked stream tail: n={n} wc={wc} tile={tile} q_pos={pos}")
@@ -114,23 +115,30 @@ def test_masked_stream_tail():
     vt = synth.Cache(vh, vc.dtype, n - wc, Hkv, D)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ring = P.Ring(B, tile * kc.pos_stride, tile * vc.pos_stride)
-    try:
-        ring.rkv_ring_begin_step([P.view_of_cache(kt, vt, pos0=wc)], tile)
-        o_w, l_w = P.attend(desc, q, P.view_of_cache(kc, vc, 0, wc), stream)
-        ws = P.workspace(ring.rkv_stream_tail_workspace_bytes(0, desc))
-        o = torch.empty_like(q)
-        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
-        ring.rkv_stream_tail(0, desc, q, o_w, l_w, o, lse, ws, stream)
-        ring.rkv_ring_end_step()
-        torch.cuda.synchronize()
-    finally:
-        ring.close()
+
+    def ring_step(tail):
+        ring = P.Ring(B, tile * kc.pos_stride, tile * vc.pos_stride)
+        try:
+            ring.rkv_ring_begin_step([tail], tile)
+            o_w, l_w = P.attend(desc, q, P.view_of_cache(kc, vc, 0, wc), stream)
+            ws = P.workspace(ring.rkv_stream_tail_workspace_bytes(0, desc))
+            o = torch.empty_like(q)
+            lse = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+            ring.rkv_stream_tail(0, desc, q, o_w, l_w, o, lse, ws, stream)
+            ring.rkv_ring_end_step()
+            torch.cuda.synchronize()
+        finally:
+            ring.close()
+        return o, lse
+
+    o, lse = ring_step(P.view_of_cache(kt, vt, pos0=wc))
+    o_res, l_res = ring_step(P.view_of_cache(kc, vc, wc, n))
+    assert torch.equal(o, o_res) and torch.equal(lse, l_res)
     views = [P.view_of_cache(kc, vc, 0, wc)] + [P.view_of_cache(kc, vc, a, min(n, a + tile))
                                                  for a in range(wc, n, tile)]
-    o_res, l_res = attend_views(desc, q, views)
+    o_seg, l_seg = attend_views(desc, q, views)
     torch.cuda.synchronize()
-    assert torch.equal(o, o_res) and torch.equal(lse, l_res)
+    assert torch.allclose(o, o_seg, rtol=0, atol=1e-5) and torch.allclose(lse, l_seg, rtol=1e-6, atol=1e-6)
     o_ref, l_ref = oracle.attend(q.cpu().numpy(), [oracle.view_of(kc.to("cpu"), vc.to("cpu"))], Hkv,
                                  default_scale(D), q_pos=pos)
     compare(o, lse, o_ref, l_ref, what="streamed")
