@@ -667,13 +667,16 @@ def streamed_tail(P, synth, L=48, steps=3, quick=False):
         the median over the reps (after one untimed rep)."""
         n_t = (tail_keys + tile_keys - 1) // tile_keys
         kc0, vc0 = lay[0]["kc"], lay[0]["vc"]
-        ring = P.Ring(B, tile_keys * kc0.pos_stride, tile_keys * vc0.pos_stride)
-        ring_r = P.Ring(B, tile_keys * kc0.pos_stride, tile_keys * vc0.pos_stride)
+        # the ring's device memory stays that of 3 slots of 8192 keys: shorter
+        # tiles get more slots (at most 16)
+        nb = min(16, B * tile // tile_keys)
+        ring = P.Ring(nb, tile_keys * kc0.pos_stride, tile_keys * vc0.pos_stride)
+        ring_r = P.Ring(nb, tile_keys * kc0.pos_stride, tile_keys * vc0.pos_stride)
         tails = {"stream": [P.view_of_cache(l_["kh"], l_["vh"], 0, tail_keys, pos0=wc) for l_ in lay],
                  "resident": [P.view_of_cache(l_["kc"], l_["vc"], wc, wc + tail_keys) for l_ in lay]}
         rings = {"stream": ring, "resident": ring_r}
         slots = [(torch.empty(tile_keys * kc0.pos_stride, dtype=torch.uint8, device=dev),
-                  torch.empty(tile_keys * vc0.pos_stride, dtype=torch.uint8, device=dev)) for _ in range(B)]
+                  torch.empty(tile_keys * vc0.pos_stride, dtype=torch.uint8, device=dev)) for _ in range(nb)]
         ws_s = [None]
 
         def step(mode):
@@ -686,7 +689,7 @@ def streamed_tail(P, synth, L=48, steps=3, quick=False):
                         kb, vb = l_["kh"].data.view(-1), l_["vh"].data.view(-1)
                         for t in range(n_t):
                             a0, a1 = t * tile_keys, min(tail_keys, (t + 1) * tile_keys)
-                            sk, sv = slots[j % B]
+                            sk, sv = slots[j % nb]
                             sk[: (a1 - a0) * kc0.pos_stride].copy_(kb[a0 * kc0.pos_stride: a1 * kc0.pos_stride], non_blocking=True)
                             sv[: (a1 - a0) * vc0.pos_stride].copy_(vb[a0 * vc0.pos_stride: a1 * vc0.pos_stride], non_blocking=True)
                             j += 1
@@ -718,14 +721,14 @@ def streamed_tail(P, synth, L=48, steps=3, quick=False):
         tail_bytes = L * tail_keys * (kc0.pos_stride + vc0.pos_stride)
         h = min(1.0, max(0.0, (t_c + t_d - t_p) / t_d))
         # The residency planner on the measured terms: the device memory this
-        # layout uses (L windows + a 3-slot ring), the measured link rate and
+        # layout uses (L windows + the ring), the measured link rate and
         # per-layer compute, the FFN weights the step reads; its window, tile,
         # slots and bounded-win prediction beside the measurement.
         bpk = kc0.pos_stride + vc0.pos_stride
-        plan = P.rkv_plan_residency(L, wc + tail_keys, bpk, L * wc * bpk + 3 * tile_keys * bpk,
+        plan = P.rkv_plan_residency(L, wc + tail_keys, bpk, L * wc * bpk + nb * tile_keys * bpk,
                                     L * reps_ffn * 14336 * 4096 * 2, HBM_PEAK_GBS * 1e9, r_link * 1e9, 0.0, 0.0,
                                     t_c / L)
-        return {"tail_keys": tail_keys, "tile_keys": tile_keys, "reps": reps, "T_c_ms": round(t_c * 1e3, 3),
+        return {"tail_keys": tail_keys, "tile_keys": tile_keys, "n_slots": nb, "reps": reps, "T_c_ms": round(t_c * 1e3, 3),
                 "T_d_ms": round(t_d * 1e3, 3), "T_p_ms": round(t_p * 1e3, 3), "tail_hidden_fraction": round(h, 4),
                 "tail_GBs": round(tail_bytes / t_p / 1e9, 2), "link_fraction": round(tail_bytes / t_p / 1e9 / r_link, 4),
                 "free_zone_keys_per_layer": round(t_c * r_link * 1e9 / L / bpk),

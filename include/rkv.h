@@ -258,10 +258,11 @@ int rkv_dequant_q4_0(const void *blocks, int64_t n_values, float *out, hipStream
  * stream.  The copy into a slot waits until the attention of the slot's
  * previous tile has read it; the attention of a tile waits for its slot's
  * copy_done event ("F5 M7 -- Rolling KV", "CUDA stream graph").  The first of
- * these waits is taken on the host: a one-thread kernel after a tile's
- * attention kernel writes the tile's sequence number to a per-slot word in
- * pinned host memory, and a copier
- * thread owned by the ring watches that word and then enqueues the slot's
+ * these waits is taken on the host: the kernel after a tile's attention
+ * kernel on the stream (the layer's next tile, or its merge) writes the
+ * tile's sequence number to a per-slot word in pinned host memory when it
+ * starts, and a copier thread owned by the ring watches that word and then
+ * enqueues the slot's
  * copies (DMA-engine hipMemcpyAsync) and copy_done record.  So the copy
  * stream carries no wait on a compute-queue event (such a wait costs a
  * DMA-engine copy tens of microseconds even when the event has long
@@ -323,8 +324,8 @@ int rkv_stream_tail_workspace_bytes(const rkv_ring *ring, int layer, const rkv_a
  * and one fixed-order merge (the S2 combine applied to the window's result
  * and every split's partial, in the order window, tile 0's splits, tile 1's
  * splits, ...) gives o and lse; lse_window may be NULL (no window; o_window is
- * then ignored).  A slot is released by a one-thread kernel after the tile's
- * attention kernel.  The result does not depend on n_slots, and equals, bit
+ * then ignored).  A slot is released when the kernel after the tile's
+ * attention kernel (the next tile's, or the merge) starts.  The result does not depend on n_slots, and equals, bit
  * for bit, the same call with the layer's tail in device memory (attended in
  * place); it agrees with rkv_attend_segment per tile + rkv_lse_combine to
  * rounding.  Layers must be consumed in plan order.

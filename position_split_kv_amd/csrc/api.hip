@@ -339,20 +339,16 @@ int launch_plan(const CallPlan &cp, const SplitParams *prm, const rkv_attn_desc 
 // validated): one split-kernel launch per group of segments (same K / V types
 // and sequence sharing), all writing into one set of per-split partials, then
 // one fixed-order merge.  All segments empty: o = 0, lse = -inf.
-// done (optional): host-visible memory that receives done_value once the
-// launches have finished reading their keys.
 // phase: 0 the whole call; 1 the split kernels alone (partials in ws, or o /
 // lse directly when the call has one split or no keys); 2 the merge alone.
 int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view *const *v, float *o, float *lse,
-                void *ws, size_t ws_bytes, hipStream_t stream, uint64_t *done = nullptr, uint64_t done_value = 0,
-                int phase = 0)
+                void *ws, size_t ws_bytes, hipStream_t stream, int phase = 0)
 {
     const int64_t n_rows = (int64_t)d->n_seq * d->n_q_heads;
     int64_t keys = 0;
     for (int i = 0; i < n; ++i) keys += v[i]->n_keys;
     if (keys == 0) {
         if (phase != 2) RKV_HIP(launch_fill_empty(d->head_dim, n_rows, o, lse, stream));
-        if (done) RKV_HIP(launch_signal(done, done_value, stream));
         return RKV_OK;
     }
     CallPlan cp;
@@ -369,10 +365,7 @@ int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view
     if (phase != 2 && (rc = launch_plan(cp, prm, d, q, part_acc, part_ml, o, lse, stream))) return rc;
     if (phase == 1) return RKV_OK;
     if (cp.n_splits_all > 1)
-        RKV_HIP(launch_reduce(d->head_dim, n_rows, cp.n_splits_all, part_acc, part_ml, o, lse, stream, done,
-                              done_value));
-    else if (done)
-        RKV_HIP(launch_signal(done, done_value, stream));
+        RKV_HIP(launch_reduce(d->head_dim, n_rows, cp.n_splits_all, part_acc, part_ml, o, lse, stream));
     return RKV_OK;
 }
 
@@ -470,7 +463,7 @@ static int attend_split_phase(const rkv_attn_desc *desc, const float *q, int n_s
     if (ws && (rc = check_device(ws, "workspace"))) return rc;
     const rkv_kv_view *vp[kMaxSegs];
     for (int i = 0; i < n_segments; ++i) vp[i] = &segs[i];
-    return attend_impl(desc, q, n_segments, vp, o, lse, ws, ws_bytes, stream, nullptr, 0, phase);
+    return attend_impl(desc, q, n_segments, vp, o, lse, ws, ws_bytes, stream, phase);
 }
 
 int rkv_attend_split(const rkv_attn_desc *desc, const float *q, int n_segments, const rkv_kv_view *segs, float *o,
@@ -659,9 +652,10 @@ struct rkv_ring {
     hipStream_t copy = nullptr;
     bool own_copy = false;
     hipEvent_t copy_done[16] = {};
-    // Slot release: the merge kernel after a tile's attention (it starts only
-    // once the split kernel has read the slot) writes the tile's sequence
-    // number + 1 to progress[slot], pinned and coherent host memory.  A slot's
+    // Slot release: the kernel after a tile's attention kernel (the layer's
+    // next tile or its merge; it starts only once the tile's kernel has read
+    // the slot) writes the tile's sequence number + 1 to progress[slot],
+    // pinned and coherent host memory.  A slot's
     // tiles run one after another (each waits for its copy, which waits for
     // the previous tile of the slot), so each word only grows, whatever
     // streams the tiles run on.  last_user[s]: sequence number of the tile that
@@ -724,8 +718,8 @@ bool wait_word(const uint64_t *w, int64_t need)
 
 // Enqueue the copy of item j (index in the step) into its slot, on the copy
 // stream, once the compute that last read the slot has finished: the copier
-// waits for that on the host, watching the ring's progress word (the merge
-// kernel after that tile's attention writes it).  A DMA-engine copy made to
+// waits for that on the host, watching the ring's progress word (the kernel
+// after that tile's attention kernel writes it).  A DMA-engine copy made to
 // wait on a compute-queue event on the GPU costs tens of microseconds per copy
 // even when the event has long completed, and an event record on the compute
 // queue costs it a few microseconds per tile; this way the copy goes out with
@@ -1089,22 +1083,31 @@ int rkv_stream_tail(rkv_ring *r, int layer, const rkv_attn_desc *desc, const flo
     float *part_acc = (float *)ws;
     float2 *part_ml = (float2 *)((char *)ws + acc_bytes);
     const bool inplace = r->inplace[layer] != 0;
+    // Slot release of the last streamed tile launched: written by the next
+    // kernel on the stream, the layer's next tile or its merge, when it
+    // starts (the tile's kernel has then finished reading the slot).
+    uint64_t *rel = nullptr;
+    uint64_t rel_value = 0;
+    // On a failure after a tile's launch: let the launched work finish, then
+    // release that tile's slot from the host (nothing on the GPU will), so no
+    // copy waits for a release that never comes; the step is aborted (later
+    // calls: RKV_E_STATE).
+    auto abort_step = [&](int code) {
+        if (rel) {
+            (void)hipStreamSynchronize(cs);
+            __atomic_store_n(rel, rel_value, __ATOMIC_RELEASE);
+        }
+        r->in_step = false;
+        return code;
+    };
     for (int64_t t = 0; t < n_tiles; ++t) {
         const int64_t j = j0 + t;
         const int s = inplace ? 0 : (int)(j % r->B);
         const rkv_kv_view v = tile_view(r, layer, t, s);
-        // A failure from here on aborts the step (later calls: RKV_E_STATE),
-        // so that nothing waits for a copy that will not be requested.
-        if ((rc = check_view_fields(desc, &v)) || (!inplace && (rc = wait_enqueued(r, j)))) {
-            r->in_step = false;
-            return rc;
-        }
+        if ((rc = check_view_fields(desc, &v)) || (!inplace && (rc = wait_enqueued(r, j)))) return abort_step(rc);
         if (!inplace) {
             hipError_t e = hipStreamWaitEvent(cs, r->copy_done[s], 0);
-            if (e != hipSuccess) {
-                r->in_step = false;
-                return hip_fail(e, "hipStreamWaitEvent (copy_done)");
-            }
+            if (e != hipSuccess) return abort_step(hip_fail(e, "hipStreamWaitEvent (copy_done)"));
         }
         const rkv_kv_view *vp = &v;
         CallPlan cp;
@@ -1112,34 +1115,29 @@ int rkv_stream_tail(rkv_ring *r, int layer, const rkv_attn_desc *desc, const flo
         rc = make_call_plan(desc, 1, &vp, &cp, prm);
         if (!rc && (cp.g.n != 1 || cp.n_splits_all != off[t + 1] - off[t]))
             rc = fail(RKV_E_STATE, "tile plan changed between the workspace query and the launch");
-        if (!rc) {
-            prm[0].split_off = off[t];
-            prm[0].n_splits_all = total;
-            prm[0].direct = 0;
-            rc = launch_plan(cp, prm, desc, q, part_acc, part_ml, o, lse, cs);
-        }
-        // the slot is free once the tile's split kernel has finished
-        if (!rc && !inplace) {
+        if (rc) return abort_step(rc);
+        prm[0].split_off = off[t];
+        prm[0].n_splits_all = total;
+        prm[0].direct = 0;
+        prm[0].release = rel;
+        prm[0].release_value = rel_value;
+        if ((rc = launch_plan(cp, prm, desc, q, part_acc, part_ml, o, lse, cs))) return abort_step(rc);
+        rel = nullptr;
+        if (!inplace) {
             const int64_t g = r->base + j;
-            hipError_t e = launch_signal(r->progress + s, (uint64_t)(g + 1), cs);
-            if (e != hipSuccess) rc = hip_fail(e, "slot release signal");
-            else {
+            rel = r->progress + s;
+            rel_value = (uint64_t)(g + 1);
+            {
                 std::lock_guard<std::mutex> lk(r->mu);
                 r->last_user[s] = g;
             }
+            if (j + r->B < (int64_t)r->items.size()) request_copy(r, j + r->B);
         }
-        if (rc) {
-            // a kernel of the tile may have been launched: let it finish
-            // before the slot can be refilled (its progress may never come)
-            (void)hipStreamSynchronize(cs);
-            r->in_step = false;
-            return rc;
-        }
-        if (!inplace && j + r->B < (int64_t)r->items.size()) request_copy(r, j + r->B);
     }
     if (total > 0) {
-        RKV_HIP(launch_reduce(D, n_rows, total, part_acc, part_ml, o, lse, cs, nullptr, 0,
-                              lse_window ? o_window : nullptr, lse_window));
+        hipError_t e = launch_reduce(D, n_rows, total, part_acc, part_ml, o, lse, cs, rel, rel_value,
+                                     lse_window ? o_window : nullptr, lse_window);
+        if (e != hipSuccess) return abort_step(hip_fail(e, "merge launch"));
     } else if (lse_window) {
         CombineParts parts;
         memset(&parts, 0, sizeof parts);

@@ -1117,6 +1117,8 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     __shared__ __attribute__((aligned(16))) float sP[NW][Sh::P_IN_K ? 4 : RTX * kTile];
     __shared__ int sRow[NW][RT];  // output row of each wave's rows (-1: none), for the epilogue
 
+    if (p.release && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+        __hip_atomic_store(p.release, p.release_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform in the wave
     uint32_t *sK = smem + w * Sh::STAGE_DW;

@@ -54,6 +54,8 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
     constexpr int LSK = SS::LSK, LSV = SS::LSV;
     __shared__ __attribute__((aligned(16))) uint32_t lds[SS::LDS_DW];
 
+    if (p.release && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+        __hip_atomic_store(p.release, p.release_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hs = w / kShdRG, rgl = w - hs * kShdRG;  // head slot, row group within the head

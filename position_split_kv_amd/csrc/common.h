@@ -64,6 +64,11 @@ struct SplitParams {
     int32_t wph_log2;      // log2 of the waves per KV head (waves per workgroup / heads per workgroup)
     int32_t n_q_heads;     // sequence of output row r: r / n_q_heads
     int32_t masked;        // qpos holds the absolute query position of each sequence
+    // Optional slot release: workgroup (0, 0, 0) writes release_value to
+    // *release (host-visible memory, system scope) when the kernel starts,
+    // i.e. once the kernel before it on the stream has finished.
+    uint64_t *release;
+    uint64_t release_value;
     int64_t qpos[kMaxMaskSeqs];
     uint16_t rowcnt[kMaxKvHeads];
     uint16_t rowtab[kMaxRowTable];
