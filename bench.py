@@ -115,7 +115,8 @@ def main():
                     help="skip the three-call comparison and the read-ceiling probe (profiling runs)")
     ap.add_argument("--no-streamed", action="store_true", help="skip the streamed-tail measurement")
     ap.add_argument("--no-others", action="store_true", help="skip the tiny, softcap-q8_0 and shared-prefix timings")
-    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c4-sweep", "c5", "verify", "append", "ceiling"],
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c4-sweep", "c4-window", "c5", "verify", "append",
+                                       "ceiling"],
                     help="run one workload alone and print its figures (profiling runs)")
     ap.add_argument("--reps", type=int, default=20, help="timed calls per workload of the other workloads")
     args = ap.parse_args()
@@ -145,6 +146,7 @@ def main():
               "append": lambda: append_path(P, synth, args.reps),
               "c4": lambda: streamed_tail(P, synth, quick=True),
               "c4-sweep": lambda: streamed_tail(P, synth),
+              "c4-window": lambda: window_q8q4(P, synth, args.reps),
               "ceiling": lambda: read_ceiling(None)}[args.only]
         print(json.dumps({args.only: fn(), "kernel_src": kernel_source_hash()}), flush=True)
         return
@@ -251,6 +253,7 @@ def main():
     others = None
     if not args.no_others:
         others = {"tiny_f32": tiny_f32(P, synth, args.reps), "softcap_q8_d512": softcap_q8_d512(P, synth, args.reps),
+                  "window_q8q4": window_q8q4(P, synth, args.reps),
                   "shared_prefix": shared_prefix(P, synth, args.reps),
                   "verify_8_rows_f16": verify_rows(P, synth, args.reps), **append_path(P, synth, args.reps)}
 
@@ -455,6 +458,44 @@ def softcap_q8_d512(P, synth, reps):
                         "mfma_frac_algorithmic": round(flops / tk / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}}
     c = measured("c3_counters")
     res["roofline"]["sq_counters"] = c
+    return res
+
+
+def window_q8q4(P, synth, reps):
+    """The window of the streamed-tail layers: q8_0 K / q4_0 V, 40/8 heads, D 128,
+    65536 keys (109 MB), one rkv_attend_segment call; four cache instances
+    alternated (436 MB, past the 256 MB last-level cache).  The roofline object
+    is the attention kernel alone (rkv_attend_split_partials over the one
+    segment)."""
+    import torch
+
+    Hq, Hkv, D, n = 40, 8, 128, 65536
+    inst = []
+    for i in range(4):
+        inst.append((synth.make_cache(n, Hkv, D, synth.Q8_0, synth.stream_seed(6, 1, i), "cuda"),
+                     synth.make_cache(n, Hkv, D, synth.Q4_0, synth.stream_seed(6, 2, i), "cuda")))
+    q = synth.make_query(1, Hq, D, synth.stream_seed(6, 3), "cuda")
+    d = P.Desc(1, Hq, Hkv, D, 1 / math.sqrt(D))
+    segs = [P.view_of_cache(kc, vc) for kc, vc in inst]
+    ws = P.workspace(max(P.rkv_attend_workspace_bytes(d, segs[0]), P.rkv_attend_split_workspace_bytes(d, segs[:1])))
+    o, l = torch.empty(1, Hq, D, device="cuda"), torch.empty(1, Hq, device="cuda")
+    k = [0]
+
+    def call():
+        P.rkv_attend_segment(d, q, segs[k[0] % 4], o, l, ws)
+        k[0] += 1
+
+    def part():
+        P.rkv_attend_split_partials(d, q, [segs[k[0] % 4]], o, l, ws)
+        k[0] += 1
+    t = timed(call, reps)
+    tk = timed(part, reps)
+    b = n * (inst[0][0].pos_stride + inst[0][1].pos_stride)  # 8 heads x (136 + 72) B per key
+    res = {"us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1), "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+           "bytes": b,
+           "roofline": {"bound": "hbm", "kernel": "rkv_split_kernel<q8_0,q4_0,128,5,1>",
+                        "achieved": round(b / tk / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(b / tk / 1e9 / HBM_PEAK_GBS, 4), "avg_launch_us": round(tk * 1e6, 2)}}
     return res
 
 
