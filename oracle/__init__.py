@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "oracle.c")
 
-F32, F16, Q8_0, Q4_0 = 0, 1, 2, 3
+F32, F16, Q8_0, Q4_0, TBQ3 = 0, 1, 2, 3, 4
 
 
 def build(force: bool = False) -> str:
@@ -73,6 +73,14 @@ class Oracle:
         L.orc_encode_row.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         L.orc_route.restype = ctypes.c_int
         L.orc_route.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
+        L.orc_dequant_tbq3.restype = ctypes.c_int
+        L.orc_dequant_tbq3.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        L.orc_tbq3_levels.restype = None
+        L.orc_tbq3_levels.argtypes = [ctypes.c_void_p]
+        L.orc_tbq3_signs.restype = None
+        L.orc_tbq3_signs.argtypes = [ctypes.c_void_p]
+        L.orc_splitmix64.restype = None
+        L.orc_splitmix64.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
         L.orc_max_threads.restype = ctypes.c_int
         L.orc_set_threads.argtypes = [ctypes.c_int]
         self.L = L
@@ -94,6 +102,30 @@ class Oracle:
         if self.L.orc_dequant_q4_0(_ptr(blocks), n_values, out.ctypes.data) != 0:
             raise ValueError("n_values must be a multiple of 32")
         return out
+
+    def dequant_tbq3(self, blocks, n_values: int) -> np.ndarray:
+        """Original-space values of TBQ3 blocks (binary64 rounded to binary32)."""
+        out = np.empty(n_values, dtype=np.float32)
+        if self.L.orc_dequant_tbq3(_ptr(blocks), n_values, out.ctypes.data) != 0:
+            raise ValueError("n_values must be a multiple of 128")
+        return out
+
+    def tbq3_levels(self) -> np.ndarray:
+        """The positive half of the 8-level Lloyd-Max codebook of N(0,1)."""
+        out = np.zeros(4, dtype=np.float64)
+        self.L.orc_tbq3_levels(out.ctypes.data)
+        return out
+
+    def tbq3_signs(self):
+        """(S1, S2): the rotation's two diagonal sign vectors (+-1, 128 each)."""
+        out = np.zeros(256, dtype=np.int32)
+        self.L.orc_tbq3_signs(out.ctypes.data)
+        return out[:128].copy(), out[128:].copy()
+
+    def splitmix64(self, seed: int, n: int) -> list:
+        out = np.zeros(n, dtype=np.uint64)
+        self.L.orc_splitmix64(seed, n, out.ctypes.data)
+        return [int(x) for x in out]
 
     def attend(self, q, views, n_kv_heads: int, scale: float, softcap: float = 0.0, q_to_kv=None, rows=None,
                q_pos=None):
@@ -199,6 +231,22 @@ def dequant_q8_0(blocks, n_values):
 
 def dequant_q4_0(blocks, n_values):
     return default().dequant_q4_0(blocks, n_values)
+
+
+def dequant_tbq3(blocks, n_values):
+    return default().dequant_tbq3(blocks, n_values)
+
+
+def tbq3_levels():
+    return default().tbq3_levels()
+
+
+def tbq3_signs():
+    return default().tbq3_signs()
+
+
+def splitmix64(seed, n):
+    return default().splitmix64(seed, n)
 
 
 def attend(q, views, n_kv_heads, scale, softcap=0.0, q_to_kv=None, rows=None, q_pos=None):

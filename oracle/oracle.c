@@ -45,6 +45,27 @@
  *    d (ties to even), the codes come from the binary32 d.  The codes are
  *    integers decided by binary32 arithmetic, so they are computed here in
  *    binary32, as the kernel computes them, and compared bit for bit.
+ *  - TBQ3, the 3-bit value tier ("F5 M6 -- PolyKV", section "S2 --
+ *    TurboQuant tier family (TBQ8_0 / TBQ4_0 / TBQ3_0)": a fast
+ *    Walsh-Hadamard rotation spreads a block's energy over its values, then
+ *    each value takes the nearest level of a Lloyd-Max (MSE-optimal)
+ *    codebook; the same page lists the 3-bit type's fields as a binary16
+ *    norm, 2-bit indices and one sign bit per value over a 128-value block,
+ *    and names seed 42 for the rotation; section "S2 perf-path Level B": the
+ *    rotation is a Q forward / O inverse pair, exact by Parseval).  The pages
+ *    print neither the codebook, nor the signs, nor a byte order; the
+ *    readings taken: the codebook is the 8-level Lloyd-Max quantiser of
+ *    N(0,1) (symmetric: a 2-bit index m picks the magnitude c_m, the sign
+ *    bit the sign), solved here from its two optimality conditions; the
+ *    rotation of a 128-value block is R = S2 H S1 / sqrt(128), H the
+ *    Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i & j)), S1 / S2
+ *    diagonal signs from bits 0..127 of the first two / next two outputs of
+ *    splitmix64 seeded with 42 (bit set = -1); a block stores
+ *    n = ||x||_2 of its original values (binary16, nearest even), two zero
+ *    bytes (alignment), the 2-bit magnitude index of value i at bits
+ *    2(i%4) of byte 4 + i/4 and its sign bit at bit i%8 of byte 36 + i/8
+ *    (52 bytes).  A stored block means y_i = +-c_m n / sqrt(128) in the
+ *    rotated space, and x = R^T y = S1 H S2 y / sqrt(128) in the original one.
  */
 #include <math.h>
 #include <stdint.h>
@@ -55,7 +76,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_F16 = 1, ORC_Q8_0 = 2, ORC_Q4_0 = 3 };
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_Q8_0 = 2, ORC_Q4_0 = 3, ORC_TBQ3 = 4 };
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
  * exponent 0 -> subnormal m * 2^-24; exponent 31 -> inf / nan. */
@@ -84,6 +105,7 @@ int64_t orc_row_bytes(int type, int64_t d)
     case ORC_F16: return 2 * d;
     case ORC_Q8_0: return (d % 32) ? 0 : (d / 32) * 34;
     case ORC_Q4_0: return (d % 32) ? 0 : (d / 32) * 18;
+    case ORC_TBQ3: return (d % 128) ? 0 : (d / 128) * 52;
     default: return 0;
     }
 }
@@ -106,6 +128,124 @@ static double q4_0_value(const uint8_t *blk, int i)
     return d * (double)(n - 8);
 }
 
+/* ---- TBQ3 (readings in the header) ---- */
+
+/* splitmix64: the state advances by 0x9e3779b97f4a7c15 and each output is
+ * the state passed through two xor-shift-multiply steps and a final
+ * xor-shift (Vigna's published generator). */
+void orc_splitmix64(uint64_t seed, int n, uint64_t *out)
+{
+    uint64_t s = seed;
+    int i;
+    for (i = 0; i < n; ++i) {
+        uint64_t z;
+        s += 0x9e3779b97f4a7c15ull;
+        z = s;
+        z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+        z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+        out[i] = z ^ (z >> 31);
+    }
+}
+
+static double std_normal_pdf(double x) { return isinf(x) ? 0.0 : exp(-0.5 * x * x) / sqrt(2.0 * acos(-1.0)); }
+static double std_normal_above(double x) { return isinf(x) ? 0.0 : 0.5 * erfc(x / sqrt(2.0)); } /* P(X > x) */
+
+/* The positive half c[0] < c[1] < c[2] < c[3] of the 8-level Lloyd-Max
+ * quantiser of N(0,1): Lloyd's iteration of its two conditions, thresholds
+ * t_j = (c_{j-1} + c_j) / 2 (t_0 = 0, t_4 = inf) and levels
+ * c_j = E[X | t_j < X < t_{j+1}] = (pdf(t_j) - pdf(t_{j+1})) / P(t_j < X < t_{j+1}),
+ * from a uniform start until no level moves. */
+static void tbq3_solve_levels(double c[4])
+{
+    int it, j;
+    c[0] = 0.5; c[1] = 1.0; c[2] = 1.5; c[3] = 2.0;
+    for (it = 0; it < 100000; ++it) {
+        double t[5], nc[4], moved = 0.0;
+        t[0] = 0.0;
+        for (j = 1; j < 4; ++j) t[j] = 0.5 * (c[j - 1] + c[j]);
+        t[4] = INFINITY;
+        for (j = 0; j < 4; ++j) {
+            const double mass = std_normal_above(t[j]) - std_normal_above(t[j + 1]);
+            nc[j] = (std_normal_pdf(t[j]) - std_normal_pdf(t[j + 1])) / mass;
+            if (fabs(nc[j] - c[j]) > moved) moved = fabs(nc[j] - c[j]);
+        }
+        for (j = 0; j < 4; ++j) c[j] = nc[j];
+        if (moved == 0.0) break;
+    }
+}
+
+static double tbq3_lv[4];
+static int tbq3_s1[128], tbq3_s2[128];
+static int tbq3_ready;
+
+/* Fill the codebook and the rotation signs (called outside parallel regions). */
+static void tbq3_init(void)
+{
+    uint64_t w[4];
+    int i;
+    if (tbq3_ready) return;
+    tbq3_solve_levels(tbq3_lv);
+    orc_splitmix64(42, 4, w);
+    for (i = 0; i < 128; ++i) {
+        tbq3_s1[i] = ((w[i >> 6] >> (i & 63)) & 1) ? -1 : 1;
+        tbq3_s2[i] = ((w[2 + (i >> 6)] >> (i & 63)) & 1) ? -1 : 1;
+    }
+    tbq3_ready = 1;
+}
+
+void orc_tbq3_levels(double out[4])
+{
+    tbq3_init();
+    memcpy(out, tbq3_lv, sizeof tbq3_lv);
+}
+
+void orc_tbq3_signs(int32_t out[256])
+{
+    int i;
+    tbq3_init();
+    for (i = 0; i < 128; ++i) {
+        out[i] = tbq3_s1[i];
+        out[128 + i] = tbq3_s2[i];
+    }
+}
+
+/* Entry (i, j) of the 128 x 128 Sylvester Hadamard matrix. */
+static int hadamard(int i, int j) { return (__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1; }
+
+/* One TBQ3 block: its 128 values in the original space, x = S1 H S2 y / sqrt(128). */
+static void tbq3_block_values(const uint8_t *blk, double *out)
+{
+    const double n = orc_f16_to_f64(rd_u16(blk));
+    double y[128];
+    int i, j;
+    for (i = 0; i < 128; ++i) {
+        const int m = (blk[4 + i / 4] >> (2 * (i % 4))) & 3;
+        const int neg = (blk[36 + i / 8] >> (i % 8)) & 1;
+        y[i] = (neg ? -1.0 : 1.0) * tbq3_lv[m] * n / sqrt(128.0);
+    }
+    for (i = 0; i < 128; ++i) {
+        double acc = 0.0;
+        for (j = 0; j < 128; ++j) acc += hadamard(i, j) * tbq3_s2[j] * y[j];
+        out[i] = tbq3_s1[i] * acc / sqrt(128.0);
+    }
+}
+
+/* Standalone TBQ3 dequantisation: n_values (a multiple of 128) original-space
+ * values, each the binary64 value rounded to binary32. */
+int orc_dequant_tbq3(const void *blocks, int64_t n_values, float *out)
+{
+    int64_t b;
+    double v[128];
+    int i;
+    if (n_values % 128) return -1;
+    tbq3_init();
+    for (b = 0; b < n_values / 128; ++b) {
+        tbq3_block_values((const uint8_t *)blocks + 52 * b, v);
+        for (i = 0; i < 128; ++i) out[128 * b + i] = (float)v[i];
+    }
+    return 0;
+}
+
 /* Dequantise one row of D values to binary64. */
 static void dequant_row(int type, const uint8_t *row, int d, double *out)
 {
@@ -126,6 +266,9 @@ static void dequant_row(int type, const uint8_t *row, int d, double *out)
         break;
     case ORC_Q4_0:
         for (i = 0; i < d; ++i) out[i] = q4_0_value(row + 18 * (i / 32), i % 32);
+        break;
+    case ORC_TBQ3:
+        for (i = 0; i < d; i += 128) tbq3_block_values(row + 52 * (i / 128), out + i);
         break;
     }
 }
@@ -155,9 +298,9 @@ int orc_dequant_q4_0(const void *blocks, int64_t n_values, float *out)
  * multiples of 2^-24; a normal result 2^e (1 + m / 1024) has 1024 + m the
  * nearest integer to |x| 2^(10 - e); |x| >= 65520 (the midpoint between the
  * largest finite value 65504 and 2^16) rounds to infinity. */
-uint16_t orc_f32_to_f16(float f)
+static uint16_t f64_to_f16(double f)
 {
-    const double v = fabs((double)f);
+    const double v = fabs(f);
     const uint16_t sign = signbit(f) ? 0x8000 : 0;
     double m;
     int ex, e;
@@ -174,6 +317,8 @@ uint16_t orc_f32_to_f16(float f)
     }
     return sign | (uint16_t)(((e + 15) << 10) | ((int)m - 1024));
 }
+
+uint16_t orc_f32_to_f16(float f) { return f64_to_f16((double)f); }
 
 static void wr_u16(uint8_t *p, uint16_t h)
 {
@@ -220,6 +365,36 @@ static void quant_q4_0_block(const float *x, uint8_t *blk)
     for (i = 0; i < 16; ++i) blk[2 + i] = (uint8_t)(n[i] | (n[i + 16] << 4));
 }
 
+/* One TBQ3 block from 128 binary32 values (readings in the header):
+ * n = ||x||_2, y = S2 H S1 x / sqrt(128), z = y sqrt(128) / n; value i takes
+ * the level nearest to z_i (magnitude index m = the number of thresholds
+ * (c_{j-1} + c_j) / 2 strictly below |z_i|; sign bit set when z_i < 0); a
+ * block of zeros stores n = 0 and index 0.  Used by the oracle's own tests
+ * (round trip, nearest level); the attention reads whatever bytes it gets. */
+static void quant_tbq3_block(const float *x, uint8_t *blk)
+{
+    double n = 0.0, y[128];
+    int i, j;
+    for (i = 0; i < 128; ++i) n += (double)x[i] * (double)x[i];
+    n = sqrt(n);
+    for (i = 0; i < 128; ++i) {
+        double acc = 0.0;
+        for (j = 0; j < 128; ++j) acc += hadamard(i, j) * tbq3_s1[j] * (double)x[j];
+        y[i] = tbq3_s2[i] * acc / sqrt(128.0);
+    }
+    memset(blk, 0, 52);
+    wr_u16(blk, f64_to_f16(n));
+    if (n == 0.0) return;
+    for (i = 0; i < 128; ++i) {
+        const double z = y[i] * sqrt(128.0) / n, a = fabs(z);
+        int m = 0;
+        for (j = 1; j < 4; ++j)
+            if (a > 0.5 * (tbq3_lv[j - 1] + tbq3_lv[j])) m = j;
+        blk[4 + i / 4] |= (uint8_t)(m << (2 * (i % 4)));
+        if (z < 0.0) blk[36 + i / 8] |= (uint8_t)(1 << (i % 8));
+    }
+}
+
 /* Store one row of D binary32 values in a cache type: binary32 bytes as
  * they are, binary16 rounded to nearest even, or D/32 blocks.  Returns 0, or
  * -1 for a bad type or a block type with D % 32 != 0. */
@@ -239,6 +414,10 @@ int orc_encode_row(int type, const float *x, int64_t d, uint8_t *out)
         break;
     case ORC_Q4_0:
         for (i = 0; i < d / 32; ++i) quant_q4_0_block(x + 32 * i, out + 18 * i);
+        break;
+    case ORC_TBQ3:
+        tbq3_init();
+        for (i = 0; i < d / 128; ++i) quant_tbq3_block(x + 128 * i, out + 52 * i);
         break;
     }
     return 0;
@@ -318,6 +497,7 @@ int orc_attend(int n_seq, int n_q_heads, int n_kv_heads, int head_dim,
         n_total += views[vi].n_keys;
     }
     if (!rows) n_rows = (int64_t)n_seq * n_q_heads;
+    tbq3_init();
 
 #pragma omp parallel for schedule(dynamic, 1)
     for (r = 0; r < n_rows; ++r) {

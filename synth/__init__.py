@@ -16,6 +16,12 @@ in the low nibble of byte i and element i >= 16 in the high nibble of byte
 i - 16.  The quantiser rule used to *generate* blocks from normal draws is not
 given by the pages; the one here (amax/127 for q8_0, signed-max/-8 for q4_0,
 scale stored round-to-nearest-even) only shapes the test data.
+
+TBQ3 (the 3-bit value tier) blocks are 128 values in 52 bytes: a binary16
+norm, two zero bytes, 32 bytes of 2-bit magnitude indices, 16 bytes of sign
+bits.  They are drawn here directly, without the tier's rotation or codebook:
+the norm is that of 128 N(0,1) draws (rounded to binary16) and the indices
+and sign bits are uniform random bytes.
 """
 from __future__ import annotations
 
@@ -23,8 +29,8 @@ from dataclasses import dataclass
 
 import torch
 
-F32, F16, Q8_0, Q4_0 = 0, 1, 2, 3
-TYPE_NAMES = {F32: "f32", F16: "f16", Q8_0: "q8_0", Q4_0: "q4_0"}
+F32, F16, Q8_0, Q4_0, TBQ3 = 0, 1, 2, 3, 4
+TYPE_NAMES = {F32: "f32", F16: "f16", Q8_0: "q8_0", Q4_0: "q4_0", TBQ3: "tbq3"}
 TYPE_BY_NAME = {v: k for k, v in TYPE_NAMES.items()}
 
 
@@ -34,6 +40,10 @@ def row_bytes(dtype: int, head_dim: int) -> int:
         return 4 * head_dim
     if dtype == F16:
         return 2 * head_dim
+    if dtype == TBQ3:
+        if head_dim % 128:
+            raise ValueError("tbq3 needs head_dim % 128 == 0")
+        return head_dim // 128 * 52
     if head_dim % 32:
         raise ValueError("block types need head_dim % 32 == 0")
     if dtype == Q8_0:
@@ -107,7 +117,19 @@ def encode(x: torch.Tensor, dtype: int) -> torch.Tensor:
         return pack_q8_0(x)
     if dtype == Q4_0:
         return pack_q4_0(x)
-    raise ValueError(dtype)
+    raise ValueError(f"no packer for dtype {dtype}")
+
+
+def draw_tbq3(n_keys: int, n_kv_heads: int, head_dim: int, g: torch.Generator, device) -> torch.Tensor:
+    """TBQ3 rows drawn directly: uint8 [n_keys][n_kv_heads][head_dim/128*52]."""
+    nb = head_dim // 128
+    x = torch.randn(n_keys, n_kv_heads, nb, 128, generator=g, device=device, dtype=torch.float32)
+    norm = x.double().norm(dim=-1).to(torch.float16)
+    del x
+    out = torch.zeros(n_keys, n_kv_heads, nb, 52, dtype=torch.uint8, device=device)
+    out[..., 0:2] = norm.view(torch.uint8).reshape(n_keys, n_kv_heads, nb, 2)
+    out[..., 4:52] = torch.randint(0, 256, (n_keys, n_kv_heads, nb, 48), generator=g, device=device, dtype=torch.uint8)
+    return out.reshape(n_keys, n_kv_heads, nb * 52)
 
 
 @dataclass
@@ -159,6 +181,9 @@ def make_cache(n_keys: int, n_kv_heads: int, head_dim: int, dtype: int, seed: in
     g = generator(seed, device)
     for c0 in range(0, n_keys, chunk_keys):
         c1 = min(n_keys, c0 + chunk_keys)
+        if dtype == TBQ3:
+            out[c0:c1] = draw_tbq3(c1 - c0, n_kv_heads, head_dim, g, device)
+            continue
         x = torch.randn(c1 - c0, n_kv_heads, head_dim, generator=g, device=device, dtype=torch.float32)
         out[c0:c1] = encode(x, dtype)
         del x

@@ -26,6 +26,14 @@ What pins what:
   - the causal mask of several query rows: bit-equality with the unmasked
     attention over the truncated key set, torch SDPA with a boolean mask,
     closed forms and pure-Python brute force, and the masked split merge.
+  - the TBQ3 tier: the codebook against the two Lloyd-Max optimality
+    conditions (conditional means by numerical quadrature, midpoint
+    thresholds) and Max's published 8-level table for N(0,1); splitmix64
+    against its author's published first outputs; the rotation against
+    scipy's Sylvester Hadamard matrix on hand-built blocks, orthogonality
+    (Parseval); the encoder against brute force over the 8 levels and the
+    codebook's distortion on Gaussian data; attention over TBQ3 values
+    against torch SDPA on values decoded here.
 """
 from __future__ import annotations
 
@@ -60,6 +68,8 @@ def values_f64(orc, cache) -> np.ndarray:
         return t.numpy().astype(np.float64)
     nval = cache.n_keys * cache.n_kv_heads * cache.head_dim
     raw = np.ascontiguousarray(t.numpy().reshape(-1))
+    if cache.dtype == synth.TBQ3:
+        return tbq3_values_f64(orc, raw).reshape(cache.n_keys, cache.n_kv_heads, cache.head_dim)
     f = orc.dequant_q8_0 if cache.dtype == synth.Q8_0 else orc.dequant_q4_0
     return f(raw, nval).astype(np.float64).reshape(cache.n_keys, cache.n_kv_heads, cache.head_dim)
 
@@ -726,6 +736,131 @@ def pin_mask_split_merge(orc):
         rows = slice(b * hq, (b + 1) * hq)
         if p < wc:
             assert np.all(np.isneginf(t[1][rows])) and np.array_equal(o[rows], w[0][rows])
+
+
+# ----------------------------------------------------------------------------- TBQ3
+
+# Max (1960), "Quantizing for minimum distortion", table for 8 output levels
+# of a unit Gaussian: the positive output levels and the mean squared error.
+MAX_1960_LEVELS = (0.2451, 0.7560, 1.3440, 2.1520)
+MAX_1960_MSE = 0.03455
+
+
+def _hadamard128():
+    import scipy.linalg
+    return scipy.linalg.hadamard(128).astype(np.float64)
+
+
+def tbq3_rotation(orc):
+    """R = S2 H S1 / sqrt(128) from the oracle's signs and scipy's Hadamard matrix."""
+    s1, s2 = orc.tbq3_signs()
+    return (s2[:, None] * _hadamard128() * s1[None, :]) / math.sqrt(128.0)
+
+
+def tbq3_values_f64(orc, raw) -> np.ndarray:
+    """Original-space binary64 values of TBQ3 blocks (bytes), decoded here:
+    y = +-c_m n / sqrt(128), x = R^T y."""
+    blk = np.asarray(raw, dtype=np.uint8).reshape(-1, 52)
+    lv = orc.tbq3_levels()
+    n = blk[:, 0:2].copy().view(np.float16).astype(np.float64)[:, 0]
+    i = np.arange(128)
+    m = (blk[:, 4 + i // 4] >> (2 * (i % 4))) & 3
+    neg = (blk[:, 36 + i // 8] >> (i % 8)) & 1
+    y = np.where(neg == 1, -1.0, 1.0) * lv[m] * n[:, None] / math.sqrt(128.0)
+    return (y @ tbq3_rotation(orc)).reshape(-1)  # row-vector form of R^T y
+
+
+def pin_tbq3_lloyd_max(orc):
+    from scipy import integrate, stats
+    c = orc.tbq3_levels()
+    assert np.all(np.diff(c) > 0) and c[0] > 0
+    t = [0.0] + [(c[j - 1] + c[j]) / 2 for j in range(1, 4)] + [np.inf]
+    mse = 0.0
+    for j in range(4):
+        mass = stats.norm.sf(t[j]) - stats.norm.sf(t[j + 1])
+        mean = integrate.quad(lambda x: x * stats.norm.pdf(x), t[j], t[j + 1], epsabs=1e-14, epsrel=1e-13)[0] / mass
+        assert abs(mean - c[j]) < 1e-9, (j, mean, c[j])
+        mse += 2 * integrate.quad(lambda x: (x - c[j]) ** 2 * stats.norm.pdf(x), t[j], t[j + 1], epsabs=1e-14)[0]
+    assert np.max(np.abs(c - np.array(MAX_1960_LEVELS))) < 1.5e-4, c
+    assert abs(mse - MAX_1960_MSE) < 1e-5, mse
+
+
+def pin_splitmix64_published(orc):
+    # the first outputs of splitmix64 seeded with 1234567, as its author publishes them
+    assert orc.splitmix64(1234567, 5) == [6457827717110365317, 3203168211198807973, 9817491932198370423,
+                                          4593380528125082431, 16408922859458223821]
+
+
+def pin_tbq3_signs_from_seed(orc):
+    w = orc.splitmix64(42, 4)
+    s1, s2 = orc.tbq3_signs()
+    bits = lambda a, b: np.array([((a if i < 64 else b) >> (i % 64)) & 1 for i in range(128)])
+    assert np.array_equal(s1, np.where(bits(w[0], w[1]) == 1, -1, 1))
+    assert np.array_equal(s2, np.where(bits(w[2], w[3]) == 1, -1, 1))
+    assert not np.array_equal(s1, s2)
+
+
+def _tbq3_block(norm_bits, mags, negs):
+    b = np.zeros(52, dtype=np.uint8)
+    b[0], b[1] = norm_bits & 0xFF, norm_bits >> 8
+    for i in range(128):
+        b[4 + i // 4] |= (mags[i] & 3) << (2 * (i % 4))
+        b[36 + i // 8] |= (negs[i] & 1) << (i % 8)
+    return b
+
+
+def pin_tbq3_hand_blocks(orc):
+    lv = orc.tbq3_levels()
+    R = tbq3_rotation(orc)
+    rng = np.random.default_rng(5)
+    cases = [(0x3C00, [1] * 128, [0] * 128),                      # n = 1, every value +c_1
+             (0x4900, [i % 4 for i in range(128)], [(i // 4) % 2 for i in range(128)]),
+             (0x0001, [3] * 128, [1] * 128),                      # subnormal norm
+             (0x0000, list(rng.integers(0, 4, 128)), list(rng.integers(0, 2, 128)))]
+    for nb, mags, negs in cases:
+        blk = _tbq3_block(nb, mags, negs)
+        n = float(np.array([nb], dtype=np.uint16).view(np.float16)[0])
+        y = np.array([(-1.0 if negs[i] else 1.0) * lv[mags[i]] * n / math.sqrt(128.0) for i in range(128)])
+        want = R.T @ y
+        got = orc.dequant_tbq3(blk, 128).astype(np.float64)
+        assert np.allclose(got, want, rtol=2e-7, atol=1e-30 + 1e-7 * np.max(np.abs(want))), (hex(nb),)
+        assert np.allclose(np.linalg.norm(got), np.linalg.norm(y), rtol=1e-6, atol=1e-30)
+    # a single index: value 0 at level 0, everything else at level 0 with the other sign pattern
+    assert np.allclose(R @ R.T, np.eye(128), atol=1e-12)
+
+
+def pin_tbq3_encoder(orc):
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((600, 128)).astype(np.float32)
+    x[0] = 0.0
+    x[1] *= 1e-3
+    enc = orc.encode_rows(x, synth.TBQ3)
+    lv = orc.tbq3_levels()
+    R = tbq3_rotation(orc)
+    levels = np.concatenate([lv, -lv])
+    for r in range(x.shape[0]):
+        blk = enc[r]
+        n = np.linalg.norm(x[r].astype(np.float64))
+        assert blk[:2].copy().view(np.float16)[0] == np.float16(n), r
+        assert blk[2] == 0 and blk[3] == 0
+        if n == 0:
+            assert not blk[4:].any()
+            continue
+        z = (R @ x[r].astype(np.float64)) * math.sqrt(128.0) / n
+        i = np.arange(128)
+        m = (blk[4 + i // 4] >> (2 * (i % 4))) & 3
+        neg = (blk[36 + i // 8] >> (i % 8)) & 1
+        best = np.argmin(np.abs(z[:, None] - levels[None, :]), axis=1)
+        assert np.array_equal(m, best % 4) and np.array_equal(neg, (best >= 4).astype(neg.dtype)), r
+    xd = orc.dequant_tbq3(np.ascontiguousarray(enc[2:].reshape(-1)), 598 * 128).reshape(598, 128).astype(np.float64)
+    x2 = x[2:].astype(np.float64)
+    rel = np.sum((xd - x2) ** 2) / np.sum(x2 ** 2)
+    assert abs(rel - MAX_1960_MSE) < 3e-3, rel
+
+
+def pin_sdpa_tbq3(orc):
+    _sdpa_case(orc, 150, 8, 2, 128, synth.Q8_0, synth.TBQ3, 71)
+    _sdpa_case(orc, 60, 4, 1, 256, synth.F16, synth.TBQ3, 72)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

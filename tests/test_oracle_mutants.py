@@ -55,6 +55,22 @@ MUTANTS = {
     "mask_first_seq": ("return !q_pos || t <= q_pos[b];", "return !q_pos || t <= q_pos[0];"),
     "mask_ignored_in_values": ("if (!key_seen(q_pos, b, t)) continue;\n                p = exp",
                                "p = exp"),
+    # TBQ3 tier
+    "tbq3_decode_signs_swapped": ("acc += hadamard(i, j) * tbq3_s2[j] * y[j];", "acc += hadamard(i, j) * tbq3_s1[j] * y[j];"),
+    "tbq3_decode_no_sqrt": ("out[i] = tbq3_s1[i] * acc / sqrt(128.0);", "out[i] = tbq3_s1[i] * acc;"),
+    "tbq3_qs_shift": ("const int m = (blk[4 + i / 4] >> (2 * (i % 4))) & 3;", "const int m = (blk[4 + i / 4] >> (i % 4)) & 3;"),
+    "tbq3_sign_bit_order": ("const int neg = (blk[36 + i / 8] >> (i % 8)) & 1;",
+                            "const int neg = (blk[36 + i / 8] >> (7 - i % 8)) & 1;"),
+    "tbq3_level_mean": ("nc[j] = (std_normal_pdf(t[j]) - std_normal_pdf(t[j + 1])) / mass;",
+                        "nc[j] = (std_normal_pdf(t[j]) - std_normal_pdf(t[j + 1])) / (2.0 * mass);"),
+    "tbq3_threshold": ("for (j = 1; j < 4; ++j) t[j] = 0.5 * (c[j - 1] + c[j]);", "for (j = 1; j < 4; ++j) t[j] = c[j - 1];"),
+    "tbq3_seed": ("orc_splitmix64(42, 4, w);", "orc_splitmix64(43, 4, w);"),
+    "splitmix_shift": ("z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;", "z = (z ^ (z >> 31)) * 0xbf58476d1ce4e5b9ull;"),
+    "tbq3_enc_threshold": ("if (a > 0.5 * (tbq3_lv[j - 1] + tbq3_lv[j])) m = j;", "if (a > tbq3_lv[j - 1]) m = j;"),
+    "tbq3_enc_norm_squared": ("    n = sqrt(n);\n", "\n"),
+    "tbq3_enc_rotation_order": ("acc += hadamard(i, j) * tbq3_s1[j] * (double)x[j];",
+                                "acc += hadamard(i, j) * tbq3_s2[j] * (double)x[j];"),
+    "tbq3_block_stride": ("tbq3_block_values(row + 52 * (i / 128), out + i);", "tbq3_block_values(row + 48 * (i / 128), out + i);"),
 }
 
 
