@@ -115,8 +115,8 @@ def main():
                     help="skip the three-call comparison and the read-ceiling probe (profiling runs)")
     ap.add_argument("--no-streamed", action="store_true", help="skip the streamed-tail measurement")
     ap.add_argument("--no-others", action="store_true", help="skip the tiny, softcap-q8_0 and shared-prefix timings")
-    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c4-sweep", "c4-window", "c5", "verify", "append",
-                                       "ceiling"],
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c4-sweep", "c4-window", "tbq3", "c5", "verify",
+                                       "append", "ceiling"],
                     help="run one workload alone and print its figures (profiling runs)")
     ap.add_argument("--reps", type=int, default=20, help="timed calls per workload of the other workloads")
     args = ap.parse_args()
@@ -147,6 +147,7 @@ def main():
               "c4": lambda: streamed_tail(P, synth, quick=True),
               "c4-sweep": lambda: streamed_tail(P, synth),
               "c4-window": lambda: window_q8q4(P, synth, args.reps),
+              "tbq3": lambda: window_q8q4(P, synth, args.reps, synth.TBQ3),
               "ceiling": lambda: read_ceiling(None)}[args.only]
         print(json.dumps({args.only: fn(), "kernel_src": kernel_source_hash()}), flush=True)
         return
@@ -254,6 +255,7 @@ def main():
     if not args.no_others:
         others = {"tiny_f32": tiny_f32(P, synth, args.reps), "softcap_q8_d512": softcap_q8_d512(P, synth, args.reps),
                   "window_q8q4": window_q8q4(P, synth, args.reps),
+                  "window_q8_tbq3": window_q8q4(P, synth, args.reps, synth.TBQ3),
                   "shared_prefix": shared_prefix(P, synth, args.reps),
                   "verify_8_rows_f16": verify_rows(P, synth, args.reps), **append_path(P, synth, args.reps)}
 
@@ -461,19 +463,21 @@ def softcap_q8_d512(P, synth, reps):
     return res
 
 
-def window_q8q4(P, synth, reps):
+def window_q8q4(P, synth, reps, vt=None):
     """The window of the streamed-tail layers: q8_0 K / q4_0 V, 40/8 heads, D 128,
     65536 keys (109 MB), one rkv_attend_segment call; four cache instances
     alternated (436 MB, past the 256 MB last-level cache).  The roofline object
     is the attention kernel alone (rkv_attend_split_partials over the one
-    segment)."""
+    segment).  vt: another value type (TBQ3: the 3-bit tier, 98.6 MB, whose
+    call also turns the output back from the rotated space)."""
     import torch
 
     Hq, Hkv, D, n = 40, 8, 128, 65536
+    vt = synth.Q4_0 if vt is None else vt
     inst = []
     for i in range(4):
         inst.append((synth.make_cache(n, Hkv, D, synth.Q8_0, synth.stream_seed(6, 1, i), "cuda"),
-                     synth.make_cache(n, Hkv, D, synth.Q4_0, synth.stream_seed(6, 2, i), "cuda")))
+                     synth.make_cache(n, Hkv, D, vt, synth.stream_seed(6, 2, i), "cuda")))
     q = synth.make_query(1, Hq, D, synth.stream_seed(6, 3), "cuda")
     d = P.Desc(1, Hq, Hkv, D, 1 / math.sqrt(D))
     segs = [P.view_of_cache(kc, vc) for kc, vc in inst]
@@ -490,10 +494,10 @@ def window_q8q4(P, synth, reps):
         k[0] += 1
     t = timed(call, reps)
     tk = timed(part, reps)
-    b = n * (inst[0][0].pos_stride + inst[0][1].pos_stride)  # 8 heads x (136 + 72) B per key
+    b = n * (inst[0][0].pos_stride + inst[0][1].pos_stride)  # 8 heads x (136 + 72 or 52) B per key
     res = {"us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1), "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
            "bytes": b,
-           "roofline": {"bound": "hbm", "kernel": "rkv_split_kernel<q8_0,q4_0,128,5,1>",
+           "roofline": {"bound": "hbm", "kernel": f"rkv_split_kernel<q8_0,{synth.TYPE_NAMES[vt]},128,5,1>",
                         "achieved": round(b / tk / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(b / tk / 1e9 / HBM_PEAK_GBS, 4), "avg_launch_us": round(tk * 1e6, 2)}}
     return res

@@ -68,8 +68,34 @@ const char *rkv_last_error(void);
  *             element i < 16 is the low nibble of byte i, element i >= 16
  *             the high nibble of byte i - 16.
  * Block types need head_dim % 32 == 0; a row of head_dim values is
- * head_dim/32 blocks back to back. */
-typedef enum rkv_dtype { RKV_F32 = 0, RKV_F16 = 1, RKV_Q8_0 = 2, RKV_Q4_0 = 3 } rkv_dtype;
+ * head_dim/32 blocks back to back.
+ *   RKV_TBQ3 (values only): the 3-bit tier of "F5 M6 -- PolyKV", section
+ *             "S2 -- TurboQuant tier family (TBQ8_0 / TBQ4_0 / TBQ3_0)": a
+ *             128-value block is rotated by a seeded fast Walsh-Hadamard
+ *             transform and each rotated value stored as the nearest level
+ *             of the 8-level Lloyd-Max codebook of N(0,1), with the block's
+ *             binary16 norm, 2-bit indices and one sign bit per value (the
+ *             fields that page lists).  52 bytes per block:
+ *               bytes 0-1  n, the block's L2 norm (binary16); bytes 2-3 zero;
+ *               bytes 4-35 magnitude index m_i of value i at bits 2(i%4) of
+ *                          byte 4 + i/4;
+ *               bytes 36-51 sign bit of value i at bit i%8 of byte 36 + i/8.
+ *             Rotated value y_i = (-1)^sign c_{m_i} n / sqrt(128), with
+ *             c_0..c_3 the positive levels of the codebook (about 0.2451,
+ *             0.7560, 1.3439, 2.1519); the value is x = R^T y with
+ *             R = S2 H S1 / sqrt(128), H the 128 x 128 Sylvester Hadamard
+ *             matrix, S1 / S2 diagonal signs from bits 0..127 of the first
+ *             two / next two outputs of splitmix64 seeded with 42 (bit set:
+ *             -1).  The pages print neither the levels, the signs nor the
+ *             byte order; these are this library's.  head_dim % 128 == 0.
+ *             Attention over TBQ3 values sums P.y in the rotated space and
+ *             applies R^T once to the output ("S2 perf-path Level B": the O
+ *             inverse rotation, exact by Parseval).  Limits: V only; a call
+ *             whose segments hold keys must have TBQ3 values in all of them
+ *             or in none (RKV_E_UNSUPPORTED), since partials of the two
+ *             spaces are not merged; not accepted as a streamed tail or as
+ *             an append destination (RKV_E_UNSUPPORTED). */
+typedef enum rkv_dtype { RKV_F32 = 0, RKV_F16 = 1, RKV_Q8_0 = 2, RKV_Q4_0 = 3, RKV_TBQ3 = 4 } rkv_dtype;
 
 /* Bytes of one row of head_dim values of a type (0 if invalid). */
 int64_t rkv_row_bytes(int32_t dtype, int32_t head_dim);
@@ -251,6 +277,14 @@ int rkv_lse_combine(int n_parts, const float *const *o_parts, const float *const
  */
 int rkv_dequant_q8_0(const void *blocks, int64_t n_values, float *out, hipStream_t stream);
 int rkv_dequant_q4_0(const void *blocks, int64_t n_values, float *out, hipStream_t stream);
+/*
+ * rkv_dequant_tbq3 -- TBQ3 blocks (device) to n_values binary32 values of the
+ * original space x = R^T y (device); n_values % 128 != 0 -> RKV_E_INVAL.
+ * Computed in binary32 (the levels, the norm product and the transform
+ * round), so the values agree with their binary64 definition to a few units
+ * in the last place of the block's largest value, not bit for bit.
+ */
+int rkv_dequant_tbq3(const void *blocks, int64_t n_values, float *out, hipStream_t stream);
 
 /* ---- streamed tail --------------------------------------------------------
  * A ring of n_slots device staging slots, each holding one tile of K and one

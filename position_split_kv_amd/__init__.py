@@ -16,13 +16,13 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("RKV_LIB") or os.path.join(_HERE, "librkv.so")
 
-RKV_F32, RKV_F16, RKV_Q8_0, RKV_Q4_0 = 0, 1, 2, 3
+RKV_F32, RKV_F16, RKV_Q8_0, RKV_Q4_0, RKV_TBQ3 = 0, 1, 2, 3, 4
 RKV_OK, RKV_E_INVAL, RKV_E_UNSUPPORTED, RKV_E_HIP, RKV_E_NOMEM, RKV_E_STATE = 0, -1, -2, -3, -4, -5
 
 # every symbol include/rkv.h declares
 EXPORTS = (
     "rkv_status_string", "rkv_last_error", "rkv_row_bytes", "rkv_attend_workspace_bytes", "rkv_attend_segment",
-    "rkv_lse_combine", "rkv_dequant_q8_0", "rkv_dequant_q4_0", "rkv_ring_create", "rkv_ring_destroy",
+    "rkv_lse_combine", "rkv_dequant_q8_0", "rkv_dequant_q4_0", "rkv_dequant_tbq3", "rkv_ring_create", "rkv_ring_destroy",
     "rkv_ring_begin_step", "rkv_stream_tail_workspace_bytes", "rkv_stream_tail", "rkv_ring_end_step",
     "rkv_ring_schedule", "rkv_attend_split", "rkv_attend_split_workspace_bytes", "rkv_append_kv",
     "rkv_plan_residency", "rkv_plan_last_error", "rkv_attend_split_partials", "rkv_attend_split_merge",
@@ -116,6 +116,7 @@ def lib() -> ctypes.CDLL:
         L.rkv_lse_combine.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), i64, i32, vp, vp, vp]
         L.rkv_dequant_q8_0.argtypes = [vp, i64, vp, vp]
         L.rkv_dequant_q4_0.argtypes = [vp, i64, vp, vp]
+        L.rkv_dequant_tbq3.argtypes = [vp, i64, vp, vp]
         L.rkv_ring_create.argtypes = [ctypes.c_int, sz, sz, vp, ctypes.POINTER(vp)]
         L.rkv_ring_destroy.argtypes = [vp]
         L.rkv_ring_begin_step.argtypes = [vp, ctypes.c_int, ctypes.POINTER(rkv_kv_view), i64]
@@ -268,6 +269,10 @@ def rkv_dequant_q8_0(blocks: torch.Tensor, n_values: int, out: torch.Tensor, str
 
 def rkv_dequant_q4_0(blocks: torch.Tensor, n_values: int, out: torch.Tensor, stream=None) -> None:
     _check(lib().rkv_dequant_q4_0(_addr(blocks), n_values, _addr(out), _stream(stream)))
+
+
+def rkv_dequant_tbq3(blocks: torch.Tensor, n_values: int, out: torch.Tensor, stream=None) -> None:
+    _check(lib().rkv_dequant_tbq3(_addr(blocks), n_values, _addr(out), _stream(stream)))
 
 
 def rkv_ring_schedule(tiles_per_layer, n_slots: int):

@@ -42,7 +42,7 @@ def _hipcc() -> str:
 def _units():
     units = []
     for kt in range(4):
-        for vt in range(4):
+        for vt in range(5):
             units.append((os.path.join(CSRC, "attend_inst.hip"), os.path.join(BUILD, f"attend_k{kt}_v{vt}.o"),
                           [f"-DRKV_KT={kt}", f"-DRKV_VT={vt}"]))
     for name in ("attend", "combine", "dequant", "append", "plan", "api"):

@@ -2,6 +2,7 @@
 // streamed-tail ring.  Every entry point validates its arguments on the host
 // before enqueuing anything and reports errors through status codes and a
 // thread-local message; nothing here aborts.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -19,6 +20,49 @@
 #include "common.h"
 
 using namespace rkv;
+
+// The TBQ3 tier's constants ("F5 M6 -- PolyKV", "S2 -- TurboQuant tier
+// family"; the choices are stated in rkv.h).  The codebook: the 8-level
+// minimum-MSE quantiser of a unit Gaussian is symmetric, so its positive
+// half c_0 < .. < c_3 is the fixed point of Lloyd's two conditions, each
+// level the mean of the Gaussian over its cell and each cell boundary the
+// midpoint of its two levels; iterated in double from an even spread until
+// the levels stop changing.  The signs: bits of splitmix64 (seed 42).
+const Tbq3Consts &rkv::tbq3_consts()
+{
+    static const Tbq3Consts c = [] {
+        Tbq3Consts k{};
+        auto pdf = [](double x) { return std::isinf(x) ? 0.0 : exp(-0.5 * x * x) * 0.39894228040143267794; };
+        auto tail = [](double x) { return std::isinf(x) ? 0.0 : 0.5 * erfc(x * 0.70710678118654752440); };
+        double lv[4] = {0.5, 1.0, 1.5, 2.0};
+        for (int it = 0; it < 100000; ++it) {
+            double edge[5] = {0.0, 0.5 * (lv[0] + lv[1]), 0.5 * (lv[1] + lv[2]), 0.5 * (lv[2] + lv[3]), INFINITY};
+            bool same = true;
+            double next[4];
+            for (int j = 0; j < 4; ++j) {
+                next[j] = (pdf(edge[j]) - pdf(edge[j + 1])) / (tail(edge[j]) - tail(edge[j + 1]));
+                same = same && next[j] == lv[j];
+            }
+            for (int j = 0; j < 4; ++j) lv[j] = next[j];
+            if (same) break;
+        }
+        for (int j = 0; j < 4; ++j) k.lv[j] = (float)lv[j];
+        uint64_t state = 42, out[4];
+        for (int i = 0; i < 4; ++i) {
+            state += 0x9e3779b97f4a7c15ull;
+            uint64_t z = state;
+            z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+            z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+            out[i] = z ^ (z >> 31);
+        }
+        for (int w = 0; w < 4; ++w) {
+            k.s1[w] = (uint32_t)(out[w >> 1] >> (32 * (w & 1)));
+            k.s2[w] = (uint32_t)(out[2 + (w >> 1)] >> (32 * (w & 1)));
+        }
+        return k;
+    }();
+    return c;
+}
 
 namespace {
 
@@ -61,7 +105,8 @@ int mem_kind(const void *p)
     return 0;
 }
 
-bool valid_type(int t) { return t >= RKV_F32 && t <= RKV_Q4_0; }
+bool valid_type(int t) { return t >= RKV_F32 && t <= RKV_Q4_0; }   // K, and values
+bool valid_v_type(int t) { return valid_type(t) || t == RKV_TBQ3; }  // values only
 bool valid_d(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
 int check_desc(const rkv_attn_desc *d)
@@ -96,7 +141,10 @@ int kv_of(const rkv_attn_desc *d, int h)
 int check_view_fields(const rkv_attn_desc *d, const rkv_kv_view *v)
 {
     if (!v) return fail(RKV_E_INVAL, "view is NULL");
-    if (!valid_type(v->k_type) || !valid_type(v->v_type)) return fail(RKV_E_INVAL, "bad K/V type");
+    if (v->k_type == RKV_TBQ3) return fail(RKV_E_UNSUPPORTED, "TBQ3 is a value type (K must be f32, f16, q8_0 or q4_0)");
+    if (!valid_type(v->k_type) || !valid_v_type(v->v_type)) return fail(RKV_E_INVAL, "bad K/V type");
+    if (v->v_type == RKV_TBQ3 && d->head_dim % 128)
+        return fail(RKV_E_UNSUPPORTED, "TBQ3 values need head_dim %% 128 == 0");
     if (v->n_keys < 0) return fail(RKV_E_INVAL, "n_keys < 0");
     if (v->n_keys > ((int64_t)1 << 40)) return fail(RKV_E_UNSUPPORTED, "n_keys too large");
     if (v->pos0 < 0 || v->pos0 > ((int64_t)1 << 40)) return fail(RKV_E_INVAL, "pos0 must be in [0, 2^40]");
@@ -239,6 +287,7 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
         prm->scale = d->scale;
         prm->scale_log2 = d->scale * 1.4426950408889634f;
         prm->softcap = d->softcap;
+        for (int j = 0; j < 4; ++j) prm->tbq_lv[j] = tbq3_consts().lv[j];
         prm->n_kv_heads = Hkv;
         int hl = 0, wl = 0;
         while ((1 << hl) < hpw) ++hl;
@@ -362,10 +411,18 @@ int attend_impl(const rkv_attn_desc *d, const float *q, int n, const rkv_kv_view
             return fail(RKV_E_UNSUPPORTED, "no kernel for this (type, head_dim, rows)");
     float *part_acc = (float *)ws;
     float2 *part_ml = (float2 *)((char *)ws + cp.acc_bytes);
+    // TBQ3 values (then in every segment with keys): the output is summed in
+    // the rotated space and turned back by the inverse rotation once final
+    bool t3 = false;
+    for (int i = 0; i < n; ++i) t3 = t3 || (v[i]->n_keys > 0 && v[i]->v_type == RKV_TBQ3);
     if (phase != 2 && (rc = launch_plan(cp, prm, d, q, part_acc, part_ml, o, lse, stream))) return rc;
+    if (cp.n_splits_all == 1) {
+        if (t3 && phase != 2) RKV_HIP(launch_unrotate(o, n_rows, d->head_dim, tbq3_consts(), stream));
+        return RKV_OK;
+    }
     if (phase == 1) return RKV_OK;
-    if (cp.n_splits_all > 1)
-        RKV_HIP(launch_reduce(d->head_dim, n_rows, cp.n_splits_all, part_acc, part_ml, o, lse, stream));
+    RKV_HIP(launch_reduce(d->head_dim, n_rows, cp.n_splits_all, part_acc, part_ml, o, lse, stream));
+    if (t3) RKV_HIP(launch_unrotate(o, n_rows, d->head_dim, tbq3_consts(), stream));
     return RKV_OK;
 }
 
@@ -390,8 +447,14 @@ int check_segs(const rkv_attn_desc *d, int n, const rkv_kv_view *segs)
     if (n < 1 || n > kMaxSegs) return fail(RKV_E_INVAL, "n_segments must be in [1, %d]", kMaxSegs);
     if (!segs) return fail(RKV_E_INVAL, "segments is NULL");
     int rc;
-    for (int i = 0; i < n; ++i)
+    int n_t3 = 0, n_other = 0;
+    for (int i = 0; i < n; ++i) {
         if ((rc = check_view_fields(d, &segs[i]))) return rc;
+        if (segs[i].n_keys > 0) (segs[i].v_type == RKV_TBQ3 ? n_t3 : n_other)++;
+    }
+    // partials over TBQ3 values are in the rotated space, the others are not
+    if (n_t3 && n_other)
+        return fail(RKV_E_UNSUPPORTED, "TBQ3 values in some segments of a call and not in others");
     return RKV_OK;
 }
 
@@ -416,8 +479,9 @@ const char *rkv_last_error(void) { return g_err.c_str(); }
 
 int64_t rkv_row_bytes(int32_t dtype, int32_t head_dim)
 {
-    if (!valid_type(dtype) || head_dim <= 0) return 0;
+    if (!valid_v_type(dtype) || head_dim <= 0) return 0;
     if ((dtype == RKV_Q8_0 || dtype == RKV_Q4_0) && head_dim % 32) return 0;
+    if (dtype == RKV_TBQ3 && head_dim % 128) return 0;
     return row_bytes_of(dtype, head_dim);
 }
 
@@ -618,6 +682,16 @@ int rkv_dequant_q4_0(const void *blocks, int64_t n_values, float *out, hipStream
     int rc = dequant_common(blocks, n_values, out);
     if (rc || n_values == 0) return rc;
     RKV_HIP(launch_dequant_q4_0(blocks, n_values, out, stream));
+    return RKV_OK;
+}
+
+int rkv_dequant_tbq3(const void *blocks, int64_t n_values, float *out, hipStream_t stream)
+{
+    if (n_values < 0 || n_values % 128) return fail(RKV_E_INVAL, "n_values must be a non-negative multiple of 128");
+    int rc = dequant_common(blocks, n_values, out);
+    if (rc || n_values == 0) return rc;
+    if (n_values / 128 > 0x7fffffff) return fail(RKV_E_UNSUPPORTED, "too many blocks");
+    RKV_HIP(launch_dequant_tbq3(blocks, n_values, out, tbq3_consts(), stream));
     return RKV_OK;
 }
 
@@ -988,6 +1062,8 @@ int rkv_ring_begin_step(rkv_ring *r, int n_layers, const rkv_kv_view *tails, int
         if (t.n_keys == 0) continue;
         if (!t.k || !t.v || t.k_pos_stride <= 0 || t.v_pos_stride <= 0)
             return fail(RKV_E_INVAL, "tail %d: bad pointers or strides", l);
+        // (its partials would be in the rotated space, the window's result is not)
+        if (t.v_type == RKV_TBQ3) return fail(RKV_E_UNSUPPORTED, "tail %d: TBQ3 values cannot be streamed", l);
         if ((t.n_keys + tile_keys - 1) / tile_keys > kMaxParts - 1)
             return fail(RKV_E_UNSUPPORTED, "tail %d: more than %d tiles", l, kMaxParts - 1);
         const int mk = mem_kind(t.k), mv = mem_kind(t.v);
@@ -1183,6 +1259,8 @@ int rkv_append_kv(int n_kv_heads, int head_dim, int n_tokens, int64_t pos0, int 
     // bit 1 device memory allowed, bit 0 pinned host memory allowed.
     auto add = [&](const rkv_kv_view *v, const char *name, int first, int count, int64_t row0, int kinds) -> int {
         if (count == 0) return RKV_OK;
+        if (v->k_type == RKV_TBQ3 || v->v_type == RKV_TBQ3)
+            return fail(RKV_E_UNSUPPORTED, "%s: appending to TBQ3 storage is not supported", name);
         if (!valid_type(v->k_type) || !valid_type(v->v_type)) return fail(RKV_E_INVAL, "%s: bad K/V type", name);
         if (!v->k || !v->v) return fail(RKV_E_INVAL, "%s: K or V pointer is NULL", name);
         const int64_t rbk = row_bytes_of(v->k_type, head_dim), rbv = row_bytes_of(v->v_type, head_dim);

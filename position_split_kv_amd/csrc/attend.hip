@@ -16,7 +16,7 @@ namespace rkv {
                                               float *lse, const SplitParams &p, hipStream_t s);           \
     int split_shd_occupancy_k##kt##_v##vt();                                                              \
     bool split_shd_supported_k##kt##_v##vt();
-#define RKV_DECL_K(kt) RKV_DECL(kt, 0) RKV_DECL(kt, 1) RKV_DECL(kt, 2) RKV_DECL(kt, 3)
+#define RKV_DECL_K(kt) RKV_DECL(kt, 0) RKV_DECL(kt, 1) RKV_DECL(kt, 2) RKV_DECL(kt, 3) RKV_DECL(kt, 4)
 RKV_DECL_K(0)
 RKV_DECL_K(1)
 RKV_DECL_K(2)
@@ -24,15 +24,15 @@ RKV_DECL_K(3)
 
 bool split_supported(int kt, int vt, int d, int rt)
 {
-    const bool t = kt >= 0 && kt <= 3 && vt >= 0 && vt <= 3;
-    const bool dd = d == 64 || d == 128 || d == 256 || (d == 512 && kt != kF32 && vt != kF32);
+    const bool t = kt >= 0 && kt <= 3 && vt >= 0 && vt <= 4;
+    const bool dd = (d == 64 && vt != kT3) || d == 128 || d == 256 || (d == 512 && kt != kF32 && vt != kF32);
     const bool r = rt == 1 || rt == 2 || rt == 4 || rt == 5 || rt == 8 || rt == 16;
     return t && dd && r;
 }
 
 int split_dim_slices(int kt, int vt, int d)
 {
-    const bool blk = (kt == kQ8 || kt == kQ4) && (vt == kQ8 || vt == kQ4);
+    const bool blk = (kt == kQ8 || kt == kQ4) && (vt == kQ8 || vt == kQ4 || vt == kT3);
     return blk && d > 128 ? d / 128 : 1;
 }
 
@@ -40,7 +40,7 @@ int split_waves(int kt, int vt, int d, int rt)
 {
 #define RKV_NW(kk, vv) \
     if (kt == kk && vt == vv) return split_waves_k##kk##_v##vv(d, rt);
-#define RKV_NW_K(kk) RKV_NW(kk, 0) RKV_NW(kk, 1) RKV_NW(kk, 2) RKV_NW(kk, 3)
+#define RKV_NW_K(kk) RKV_NW(kk, 0) RKV_NW(kk, 1) RKV_NW(kk, 2) RKV_NW(kk, 3) RKV_NW(kk, 4)
     RKV_NW_K(0)
     RKV_NW_K(1)
     RKV_NW_K(2)
@@ -52,7 +52,7 @@ int split_occupancy(int kt, int vt, int d, int rt)
 {
     // cached per instance and device (the first query on a device may be
     // slow); atomics, since calls may plan from several host threads
-    static std::atomic<int> cache[4][4][4][6][16];
+    static std::atomic<int> cache[4][5][4][6][16];
     static const int rts[6] = {1, 2, 4, 5, 8, 16};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
@@ -63,13 +63,13 @@ int split_occupancy(int kt, int vt, int d, int rt)
     for (int i = 0; i < 6; ++i)
         if (rts[i] == rt) ri = i;
     const int di = d == 64 ? 0 : d == 128 ? 1 : d == 256 ? 2 : d == 512 ? 3 : -1;
-    if (ri < 0 || di < 0 || kt < 0 || kt > 3 || vt < 0 || vt > 3 || dev < 0 || dev >= 16) return 0;
+    if (ri < 0 || di < 0 || kt < 0 || kt > 3 || vt < 0 || vt > 4 || dev < 0 || dev >= 16) return 0;
     std::atomic<int> &slot = cache[kt][vt][di][ri][dev];
     int c = slot.load(std::memory_order_relaxed);
     if (c == 0) {
 #define RKV_OCC(kk, vv) \
     if (kt == kk && vt == vv) c = split_occupancy_k##kk##_v##vv(d, rt);
-#define RKV_OCC_K(kk) RKV_OCC(kk, 0) RKV_OCC(kk, 1) RKV_OCC(kk, 2) RKV_OCC(kk, 3)
+#define RKV_OCC_K(kk) RKV_OCC(kk, 0) RKV_OCC(kk, 1) RKV_OCC(kk, 2) RKV_OCC(kk, 3) RKV_OCC(kk, 4)
         RKV_OCC_K(0)
         RKV_OCC_K(1)
         RKV_OCC_K(2)
@@ -103,7 +103,7 @@ bool split_shd_supported(int kt, int vt)
 {
 #define RKV_SOK(kk, vv) \
     if (kt == kk && vt == vv) return split_shd_supported_k##kk##_v##vv();
-#define RKV_SOK_K(kk) RKV_SOK(kk, 0) RKV_SOK(kk, 1) RKV_SOK(kk, 2) RKV_SOK(kk, 3)
+#define RKV_SOK_K(kk) RKV_SOK(kk, 0) RKV_SOK(kk, 1) RKV_SOK(kk, 2) RKV_SOK(kk, 3) RKV_SOK(kk, 4)
     RKV_SOK_K(0)
     RKV_SOK_K(1)
     RKV_SOK_K(2)
@@ -113,19 +113,19 @@ bool split_shd_supported(int kt, int vt)
 
 int split_shd_occupancy(int kt, int vt)
 {
-    static std::atomic<int> cache[4][4][16];
+    static std::atomic<int> cache[4][5][16];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();
         return 0;
     }
-    if (kt < 0 || kt > 3 || vt < 0 || vt > 3 || dev < 0 || dev >= 16) return 0;
+    if (kt < 0 || kt > 3 || vt < 0 || vt > 4 || dev < 0 || dev >= 16) return 0;
     std::atomic<int> &slot = cache[kt][vt][dev];
     int c = slot.load(std::memory_order_relaxed);
     if (c == 0) {
 #define RKV_SOCC(kk, vv) \
     if (kt == kk && vt == vv) c = split_shd_occupancy_k##kk##_v##vv();
-#define RKV_SOCC_K(kk) RKV_SOCC(kk, 0) RKV_SOCC(kk, 1) RKV_SOCC(kk, 2) RKV_SOCC(kk, 3)
+#define RKV_SOCC_K(kk) RKV_SOCC(kk, 0) RKV_SOCC(kk, 1) RKV_SOCC(kk, 2) RKV_SOCC(kk, 3) RKV_SOCC(kk, 4)
         RKV_SOCC_K(0)
         RKV_SOCC_K(1)
         RKV_SOCC_K(2)
@@ -141,7 +141,7 @@ hipError_t launch_split_shd(int kt, int vt, dim3 grid, const float *q, float *pa
 {
 #define RKV_SCASE(kk, vv) \
     if (kt == kk && vt == vv) return launch_split_shd_k##kk##_v##vv(grid, q, pa, pm, o, lse, p, s);
-#define RKV_SCASE_K(kk) RKV_SCASE(kk, 0) RKV_SCASE(kk, 1) RKV_SCASE(kk, 2) RKV_SCASE(kk, 3)
+#define RKV_SCASE_K(kk) RKV_SCASE(kk, 0) RKV_SCASE(kk, 1) RKV_SCASE(kk, 2) RKV_SCASE(kk, 3) RKV_SCASE(kk, 4)
     RKV_SCASE_K(0)
     RKV_SCASE_K(1)
     RKV_SCASE_K(2)
@@ -154,7 +154,7 @@ hipError_t launch_split(int kt, int vt, int d, int rt, dim3 grid, const float *q
 {
 #define RKV_CASE(kk, vv) \
     if (kt == kk && vt == vv) return launch_split_k##kk##_v##vv(d, rt, grid, q, pa, pm, o, lse, p, s);
-#define RKV_CASE_K(kk) RKV_CASE(kk, 0) RKV_CASE(kk, 1) RKV_CASE(kk, 2) RKV_CASE(kk, 3)
+#define RKV_CASE_K(kk) RKV_CASE(kk, 0) RKV_CASE(kk, 1) RKV_CASE(kk, 2) RKV_CASE(kk, 3) RKV_CASE(kk, 4)
     RKV_CASE_K(0)
     RKV_CASE_K(1)
     RKV_CASE_K(2)

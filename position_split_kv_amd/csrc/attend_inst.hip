@@ -15,16 +15,20 @@ namespace rkv {
 
 // Block-type K and V at head_dim 256 / 512 run as 2 / 4 dim slices of 128
 // (see rkv_split_kernel): the instance used for a requested head_dim.
-constexpr bool kBlockKV = (RKV_KT == kQ8 || RKV_KT == kQ4) && (RKV_VT == kQ8 || RKV_VT == kQ4);
+constexpr bool kBlockKV = (RKV_KT == kQ8 || RKV_KT == kQ4) && (RKV_VT == kQ8 || RKV_VT == kQ4 || RKV_VT == kT3);
 template <int D>
 constexpr int slices_of() { return kBlockKV && D > 128 ? D / 128 : 1; }
+// An instance exists for the head_dim (TBQ3 values come in blocks of 128;
+// an f32 row of 512 values does not fit the LDS tile).
+template <int D>
+constexpr bool has_instance() { return !(RKV_VT == kT3 && D % 128) && !(D == 512 && (RKV_KT == kF32 || RKV_VT == kF32)); }
 
 template <int D, int RT>
 static hipError_t go(dim3 grid, const float *q, float *pa, float2 *pm, float *o, float *lse, const SplitParams &p,
                      hipStream_t stream)
 {
-    if constexpr (D == 512 && (RKV_KT == kF32 || RKV_VT == kF32)) {
-        return hipErrorInvalidValue;  // an f32 row of 512 values does not fit the LDS tile
+    if constexpr (!has_instance<D>()) {
+        return hipErrorInvalidValue;
     } else if constexpr (slices_of<D>() > 1) {
         constexpr int DS = slices_of<D>();
         hipLaunchKernelGGL((rkv_split_kernel<RKV_KT, RKV_VT, 128, RT, DS>), grid,
@@ -67,7 +71,7 @@ hipError_t RKV_NAME(RKV_KT, RKV_VT)(int d, int rt, dim3 grid, const float *q, fl
 template <int D, int RT>
 static int occ_of()
 {
-    if constexpr (D == 512 && (RKV_KT == kF32 || RKV_VT == kF32)) {
+    if constexpr (!has_instance<D>()) {
         return 0;
     } else if constexpr (slices_of<D>() > 1) {
         constexpr int DS = slices_of<D>();
@@ -122,6 +126,7 @@ static int nw_by_rt(int rt)
 {
     constexpr int DS = slices_of<D>();
     using Sh = Shape<RKV_KT, RKV_VT, (DS > 1 ? 128 : D)>;
+    if (!has_instance<D>()) return 0;
     switch (rt) {
     case 1: return Sh::waves(sp_rows(1, DS));
     case 2: return Sh::waves(sp_rows(2, DS));

@@ -78,7 +78,7 @@ struct Shape {
     static constexpr int lds_bytes(int nw, int rt)
     {
         return 4 * (nw * STAGE_DW > nw * rt * (D + 2) ? nw * STAGE_DW : nw * rt * (D + 2)) +
-               (P_IN_K ? 0 : 4 * nw * rt * kTile);
+               (P_IN_K ? 0 : 4 * nw * rt * kTile) + (VT == kT3 ? 512 : 0);
     }
     // waves per workgroup: as many (up to 8) as fit 160 KiB of LDS
     static constexpr int waves(int rt)
@@ -993,8 +993,15 @@ __device__ __forceinline__ void mfma_scores_blk(const uint32_t *tile, const rkv_
 
 // 8 consecutive values (dims 8*dg .. 8*dg+7) of a V row held in LDS, as
 // floats, plus the block scale they must be multiplied by (1 for f32/f16).
+// A TBQ3 level by index m (0..3) from the four positive levels.
+__device__ __forceinline__ float tbq3_level(const float *lv, uint32_t m)
+{
+    const float lo = (m & 1u) ? lv[1] : lv[0], hi = (m & 1u) ? lv[3] : lv[2];
+    return (m & 2u) ? hi : lo;
+}
+
 template <int VT, int D>
-__device__ __forceinline__ float v_group_lds(const uint32_t *row, int dg, float *x)
+__device__ __forceinline__ float v_group_lds(const uint32_t *row, int dg, float *x, const float *lv = nullptr)
 {
     if constexpr (VT == kF32) {
         const uint4 a = *(const uint4 *)(row + 8 * dg), b = *(const uint4 *)(row + 8 * dg + 4);
@@ -1027,6 +1034,20 @@ __device__ __forceinline__ float v_group_lds(const uint32_t *row, int dg, float 
             x[4 + k] = sbyte(w1, k);
         }
         return dsc;
+    } else if constexpr (VT == kT3) {
+        // TBQ3: rotated values of dims 8n..8n+7 of block b (13 dwords per
+        // block: norm, 16 bits of magnitude indices at dword 1 + n/2, 8 sign
+        // bits at dword 9 + n/4); the block's n / sqrt(128) is the scale
+        const int b = dg >> 4, n = dg & 15;
+        const uint32_t *blk = row + 13 * b;
+        const uint32_t q16 = blk[1 + (n >> 1)] >> (16 * (n & 1));
+        const uint32_t s8 = blk[9 + (n >> 2)] >> (8 * (n & 3));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float c = tbq3_level(lv, (q16 >> (2 * e)) & 3u);
+            x[e] = ((s8 >> e) & 1u) ? -c : c;
+        }
+        return h2f(blk[0]) * 0.088388347648318440550f;
     } else {  // kQ4: dims 8h..8h+7 of the block = low (h < 2) or high nibbles of bytes 8(h&1) ..
         const int bb = dg >> 2, h = dg & 3;
         const int os = 18 * bb;
@@ -1116,9 +1137,25 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     __shared__ __attribute__((aligned(16))) uint32_t smem[SMEM_DW];
     __shared__ __attribute__((aligned(16))) float sP[NW][Sh::P_IN_K ? 4 : RTX * kTile];
     __shared__ int sRow[NW][RT];  // output row of each wave's rows (-1: none), for the epilogue
+    // TBQ3 values: entry m_a | m_b << 2 | sign_a << 4 | sign_b << 5 of
+    // two consecutive values, as the binary16 high parts (x) and low parts
+    // (y) of the two signed levels, packed as matrix-core operand pairs
+    __shared__ uint2 sT3[VT == kT3 ? 64 : 1];
 
     if (p.release && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)
         __hip_atomic_store(p.release, p.release_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if constexpr (VT == kT3) {
+        if (threadIdx.x < 64) {
+            const int e = threadIdx.x;
+            const float va = ((e >> 4) & 1) ? -tbq3_level(p.tbq_lv, e & 3) : tbq3_level(p.tbq_lv, e & 3);
+            const float vb = ((e >> 5) & 1) ? -tbq3_level(p.tbq_lv, (e >> 2) & 3) : tbq3_level(p.tbq_lv, (e >> 2) & 3);
+            const _Float16 ha = (_Float16)va, hb = (_Float16)vb;
+            const _Float16 la = (_Float16)(va - (float)ha), lb = (_Float16)(vb - (float)hb);
+            sT3[e] = make_uint2((uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16),
+                                (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16));
+        }
+        __syncthreads();
+    }
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform in the wave
     uint32_t *sK = smem + w * Sh::STAGE_DW;
@@ -1239,7 +1276,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // about 22 bits.  The MFMA cost does not depend on the row count (rows are
     // padded to 16), while the VALU form decodes and multiplies every value
     // once per row: even at 1 row the matrix cores leave the VALU far less.
-    constexpr bool MFMA_PVB = MFMA_S && (VT == kQ8 || VT == kQ4) && !Sh::V_REG && D == 128;
+    constexpr bool MFMA_PVB = MFMA_S && (VT == kQ8 || VT == kQ4 || VT == kT3) && !Sh::V_REG && D == 128;
     constexpr bool MFMA_O = MFMA_PV || MFMA_PVB;  // O held in the MFMA output layout
     static_assert(DS == 1 || MFMA_PVB, "dim slices need block-type K and V on the matrix cores");
     constexpr int NKQ = MFMA_S ? D / 32 : 1;
@@ -1265,7 +1302,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // LDS by dword DMA (no staging registers); a tile's K rows go out once
     // the previous tile's scores are done, its V rows after the previous P.V,
     // and the wait for K leaves V's loads in flight.
-    constexpr bool BDMA = MFMA_S && (KT == kQ8 || KT == kQ4) && (VT == kQ8 || VT == kQ4) && Sh::RBK % 4 == 0 &&
+    constexpr bool BDMA = MFMA_S && (KT == kQ8 || KT == kQ4) && (VT == kQ8 || VT == kQ4 || VT == kT3) && Sh::RBK % 4 == 0 &&
                           Sh::RBV % 4 == 0 && LSK <= 64 && LSV <= 64;
     constexpr int NVD = LSV < 63 ? LSV : 63;  // V loads a wait for K may leave outstanding
     KRegs kr;
@@ -1425,7 +1462,27 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             // exact in binary16; hi = d * code rounded once (packed f16
             // multiply) and lo = d * code - hi (packed f16 fma, exact while
             // |d * code| <= 65504, which the scale test guarantees).
+            // TBQ3: element e is the signed level of dim 8n + c of that key
+            // (the key's n / sqrt(128) is in P), high and low parts from the
+            // table, two values per lookup.
             uint32_t hw[8][4], lw[8][4];
+            if constexpr (VT == kT3) {
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const uint32_t *ra = sV + (4 * (8 * kb + 2 * e2) + gq) * LSV, *rb = ra + 4 * LSV;
+                    const uint32_t qa = ra[1 + (qi >> 1)] >> (16 * (qi & 1)), qb = rb[1 + (qi >> 1)] >> (16 * (qi & 1));
+                    const uint32_t sa = ra[9 + (qi >> 2)] >> (8 * (qi & 3)), sb = rb[9 + (qi >> 2)] >> (8 * (qi & 3));
+#pragma unroll
+                    for (int p2 = 0; p2 < 4; ++p2) {
+                        const uint2 ta = sT3[((qa >> (4 * p2)) & 15u) | (((sa >> (2 * p2)) & 3u) << 4)];
+                        const uint2 tb = sT3[((qb >> (4 * p2)) & 15u) | (((sb >> (2 * p2)) & 3u) << 4)];
+                        hw[2 * p2][e2] = __builtin_amdgcn_perm(tb.x, ta.x, 0x05040100u);
+                        hw[2 * p2 + 1][e2] = __builtin_amdgcn_perm(tb.x, ta.x, 0x07060302u);
+                        lw[2 * p2][e2] = __builtin_amdgcn_perm(tb.y, ta.y, 0x05040100u);
+                        lw[2 * p2 + 1][e2] = __builtin_amdgcn_perm(tb.y, ta.y, 0x07060302u);
+                    }
+                }
+            } else {
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
                 uint32_t ca[4], cb[4], da, db;
@@ -1445,6 +1502,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                     lw[2 * p2][e2] = __builtin_bit_cast(uint32_t, l0);
                     lw[2 * p2 + 1][e2] = __builtin_bit_cast(uint32_t, l1);
                 }
+            }
             }
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
@@ -1658,6 +1716,13 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                     }
                 }
             }
+            // TBQ3 values: P is stored times the key's n / sqrt(128) (the
+            // value scale; the denominator takes P itself)
+            float vs[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (VT == kT3) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) vs[kb] = h2f(sV[(16 * kb + (lane & 15)) * LSV]) * 0.088388347648318440550f;
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * (lane >> 4) + i;
@@ -1668,7 +1733,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                     ps += pv;
                     const int key = 16 * kb + (lane & 15);
                     const int at = MFMA_O ? (key & 3) * 16 + (key >> 2) : key;
-                    if (row < RT) sPw[row * kTile + at] = pv;
+                    if (row < RT) sPw[row * kTile + at] = VT == kT3 ? pv * vs[kb] : pv;
                 }
                 lrow[i] += ps;
             }
@@ -1726,12 +1791,17 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             // ---- P.V on the matrix cores, block-type V (see where MFMA_PVB is set)
             // A tile with a block scale large enough for d * code to overflow
             // binary16 (rare) is multiplied out in binary32 on the VALU.
-            const uint32_t vmx = v_row_scale_max<VT, D / 32>(sV + lane * LSV);
-            if (__builtin_amdgcn_ballot_w64(vmx >= v_scale_limit<VT>()) == 0)
+            // (TBQ3: levels below 2.2, P times n / sqrt(128) below 5800)
+            if constexpr (VT == kT3) {
                 pv_blk();
-            else
-                pv_valu_tile<VT, LSV>(
-                    sV, [&](int r, int k) { return sPw[r * kTile + (k & 3) * 16 + (k >> 2)]; }, RT, lane, oc);
+            } else {
+                const uint32_t vmx = v_row_scale_max<VT, D / 32>(sV + lane * LSV);
+                if (__builtin_amdgcn_ballot_w64(vmx >= v_scale_limit<VT>()) == 0)
+                    pv_blk();
+                else
+                    pv_valu_tile<VT, LSV>(
+                        sV, [&](int r, int k) { return sPw[r * kTile + (k & 3) * 16 + (k >> 2)]; }, RT, lane, oc);
+            }
         } else if constexpr (MFMA_PV) {
             // ---- P.V on the matrix cores (layout described where MFMA_PV is set)
             const int qi = lane & 15, gq = lane >> 4;
@@ -1789,11 +1859,11 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 }
                 dsc = 1.f;
             } else {
-                dsc = v_group_lds<VT, D>(sV + key * LSV, dg, x);
+                dsc = v_group_lds<VT, D>(sV + key * LSV, dg, x, p.tbq_lv);
             }
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
-                const float pw = (VT == kQ8 || VT == kQ4) ? sPw[r * kTile + key] * dsc : sPw[r * kTile + key];
+                const float pw = (VT == kQ8 || VT == kQ4 || VT == kT3) ? sPw[r * kTile + key] * dsc : sPw[r * kTile + key];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pw, x[e], acc[r][e]);
             }

@@ -10,12 +10,22 @@
 
 namespace rkv {
 
-constexpr int kF32 = RKV_F32, kF16 = RKV_F16, kQ8 = RKV_Q8_0, kQ4 = RKV_Q4_0;
+constexpr int kF32 = RKV_F32, kF16 = RKV_F16, kQ8 = RKV_Q8_0, kQ4 = RKV_Q4_0, kT3 = RKV_TBQ3;
 
 __host__ __device__ constexpr int row_bytes_of(int t, int d)
 {
-    return t == kF32 ? 4 * d : t == kF16 ? 2 * d : t == kQ8 ? (d / 32) * 34 : t == kQ4 ? (d / 32) * 18 : 0;
+    return t == kF32 ? 4 * d : t == kF16 ? 2 * d : t == kQ8 ? (d / 32) * 34 : t == kQ4 ? (d / 32) * 18
+         : t == kT3 ? (d % 128 ? 0 : (d / 128) * 52) : 0;
 }
+
+// The TBQ3 tier's constants, computed once on the host (api.hip): the
+// positive Lloyd-Max levels of N(0,1) and the rotation's sign masks (bit i
+// of s1 / s2 set: the sign of value i is -1).
+struct Tbq3Consts {
+    float lv[4];
+    uint32_t s1[4], s2[4];
+};
+const Tbq3Consts &tbq3_consts();
 
 // Width in bytes of the vector loads that stage a row: the largest of 16, 8, 4
 // dividing the row size.
@@ -69,6 +79,7 @@ struct SplitParams {
     // i.e. once the kernel before it on the stream has finished.
     uint64_t *release;
     uint64_t release_value;
+    float tbq_lv[4];       // TBQ3 values: the codebook's positive levels
     int64_t qpos[kMaxMaskSeqs];
     uint16_t rowcnt[kMaxKvHeads];
     uint16_t rowtab[kMaxRowTable];
@@ -161,6 +172,11 @@ hipError_t launch_append(int d, int n_tokens, int n_kv_heads, const float *k_new
                          const AppendParams &p, hipStream_t stream);
 
 hipError_t launch_dequant_q8_0(const void *blocks, int64_t n_values, float *out, hipStream_t stream);
+hipError_t launch_dequant_tbq3(const void *blocks, int64_t n_values, float *out, const Tbq3Consts &c,
+                               hipStream_t stream);
+// o [n_rows][d] (d % 128 == 0) in place: each 128-value block y -> R^T y, the
+// TBQ3 tier's inverse rotation (the output of attention over TBQ3 values).
+hipError_t launch_unrotate(float *o, int64_t n_rows, int d, const Tbq3Consts &c, hipStream_t stream);
 hipError_t launch_dequant_q4_0(const void *blocks, int64_t n_values, float *out, hipStream_t stream);
 
 }  // namespace rkv

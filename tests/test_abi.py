@@ -40,6 +40,9 @@ def test_row_bytes():
     assert P.row_bytes(P.RKV_Q4_0, 128) == 72
     assert P.row_bytes(P.RKV_Q8_0, 512) == 544
     assert P.row_bytes(P.RKV_Q8_0, 48) == 0
+    assert P.row_bytes(P.RKV_TBQ3, 128) == 52
+    assert P.row_bytes(P.RKV_TBQ3, 512) == 208
+    assert P.row_bytes(P.RKV_TBQ3, 64) == 0
     assert P.row_bytes(7, 128) == 0
 
 
