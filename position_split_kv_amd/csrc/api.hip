@@ -225,13 +225,23 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
     const int slots = Hkv * ds;
     int hpw = 1;
     if (ds > 1 && nw < ds) return fail(RKV_E_UNSUPPORTED, "too few waves per workgroup for %d dim slices", ds);
+    // Several row groups of a KV head on the matrix-core path (head_dim 128,
+    // no f32 operand): the waves of a head take its row groups, each over all
+    // the split's keys, so that one workgroup reads a tile for all of them
+    // at once (the copies after the first come from the compute unit's
+    // caches) rather than one workgroup per row group each reading it.
+    const bool rgw = !pl->shd && ds == 1 && D == 128 && kt != kF32 && vt != kF32 && pl->n_rg > 1 && nw >= 2;
+    int rg_per_wg = 1;
+    if (rgw)
+        while (rg_per_wg < pl->n_rg && 2 * rg_per_wg <= nw) rg_per_wg *= 2;
     if (pl->shd)
         hpw = 1;
     else if (ds > 1)
         hpw = nw;
     else
-        while (2 * hpw <= nw && 2 * hpw <= slots) hpw *= 2;
+        while (2 * hpw <= nw / rg_per_wg && 2 * hpw <= slots) hpw *= 2;
     if (pl->shd) pl->n_rg = (pl->n_rg + 3) / 4;
+    if (rgw) pl->n_rg = (pl->n_rg + nw / hpw - 1) / (nw / hpw);
     pl->nw = nw;
     pl->hpw = hpw;
     pl->n_hg = (slots + hpw - 1) / hpw;
@@ -243,7 +253,7 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
     if (cus <= 0) cus = 256;
     const int64_t want_groups = std::max<int64_t>(1, (int64_t)occ * cus / units);
     int64_t tps = std::max<int64_t>(1, (tiles_total + want_groups - 1) / want_groups);
-    tps = (tps + wph - 1) / wph * wph;
+    if (!rgw) tps = (tps + wph - 1) / wph * wph;  // (row-group waves each walk every tile)
     if (tps * kTile > (1 << 30)) tps = (1 << 30) / kTile;
     int64_t n_splits = 0;
     if (prm) memset(prm, 0, sizeof *prm);
@@ -296,6 +306,8 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
         prm->wph_log2 = wl;
         prm->n_q_heads = Hq;
         prm->masked = d->q_pos != nullptr;
+        prm->stream_once = pl->n_rg == 1 && !rgw;
+        prm->rg_waves = rgw;
         if (d->q_pos)
             for (int b = 0; b < S; ++b)  // (clamped so that position differences stay far from overflow)
                 prm->qpos[b] = std::min<int64_t>(std::max<int64_t>(d->q_pos[b], -1), (int64_t)1 << 42);

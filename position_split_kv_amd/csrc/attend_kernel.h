@@ -43,6 +43,8 @@
 // "CUDA stream graph": flash attention's exact math over rotating key chunks).
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace rkv {
@@ -304,19 +306,29 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 // inserts its own (conservative or missing) waits for it nor reorders memory
 // accesses across it; callers wait with waitcnt_vm() before reading the data
 // and wait for their LDS reads (lgkmcnt) before overwriting a buffer.  M0 is
-// saved and restored around the load.  Each 16-byte chunk is read exactly once
-// and every load takes whole cache lines, so it carries the non-temporal cache
-// policy (nt): on the 48-layer f16 step 2.5 % less time than the default
-// policy.  (The 4-byte loads below touch each line from several loads and
-// keep the default: with nt they were up to 15 % slower.)
+// saved and restored around the load.  When each 16-byte chunk is read
+// exactly once by the launch (one row group per KV head), every load takes
+// whole cache lines and carries the non-temporal cache policy (NT): on the
+// 48-layer f16 step 2.5 % less time than the default policy.  When several
+// row groups read the same tile, the default policy keeps it in L2 for the
+// others (a verify step of 40 rows per head: 106 -> 94 us).  (The 4-byte
+// loads below touch each line from several loads and keep the default: with
+// nt they were up to 15 % slower.)
+template <bool NT>
 __device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "v"(g), "s"(lds)
-                 : "memory");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "v"(g), "s"(lds)
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "v"(g), "s"(lds)
+                     : "memory");
 #else
     (void)g;
     (void)lds;
@@ -334,14 +346,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base)
 
 // The same with a uniform base and a per-lane 32-bit offset (global address
 // = sbase + voff): the address arithmetic of a whole tile stays scalar.
+template <bool NT>
 __device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, uint32_t lds)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "v"(voff), "s"(sbase), "s"(lds)
-                 : "memory");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "v"(voff), "s"(sbase), "s"(lds)
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "v"(voff), "s"(sbase), "s"(lds)
+                     : "memory");
 #else
     (void)sbase;
     (void)voff;
@@ -1163,12 +1182,14 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // this wave's score rows P [row][key] (in its K tile when that is free)
     float *const sPw = Sh::P_IN_K ? (float *)sK : &sP[w][0];
 
-    // this wave's head slot hs and its index ws among the head's waves
+    // this wave's head slot hs and its index ws among the head's waves; the
+    // waves of a head split its key tiles, or (rg_waves) each takes one of
+    // its row groups over all of them
     const int hg = blockIdx.y / p.n_rg;
-    const int rg = blockIdx.y - hg * p.n_rg;
     const int wph = 1 << p.wph_log2;
     const int hs = w >> p.wph_log2;
     const int ws = w - hs * wph;
+    const int rg = p.rg_waves ? (blockIdx.y - hg * p.n_rg) * wph + ws : blockIdx.y - hg * p.n_rg;
     // head slot -> KV head g and dim slice js (js = 0 and g the slot when DS = 1)
     const int vh = (hg << p.hpw_log2) + hs;
     const int g = vh / DS, js = vh - (vh / DS) * DS;
@@ -1186,7 +1207,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // meet at a barrier per tile)
     int64_t kend = (nr == 0 && DS == 1) ? kbeg
                    : kbeg + sg.keys_per_split < sg.n_keys ? kbeg + sg.keys_per_split : sg.n_keys;
-    const int64_t tstep = (int64_t)wph * kTile;  // tile stride of this wave
+    const int64_t tstep = (p.rg_waves ? 1 : (int64_t)wph) * kTile;  // tile stride of this wave
 
     const int gr = g < p.n_kv_heads ? g : p.n_kv_heads - 1;  // a slot past the heads reads a real one
     const uint8_t *kg = sg.k + z * sg.k_seq + gr * sg.k_head + js * Sh::RBK;
@@ -1319,21 +1340,28 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         if (nkk == kTile) {
             // buffer loads: the tile base in a scalar resource, the step in
             // the scalar offset, the lane's offset in one vector register;
-            // non-temporal like the K tile's DMA (each byte is read once, by
-            // whole lines: on the 48-layer f16 step 4.5 % less time for the
-            // attention kernel than the default cache policy)
+            // non-temporal like the K tile's DMA when each byte is read once
+            // by the launch (whole lines: on the 48-layer f16 step 4.5 % less
+            // time for the attention kernel than the default cache policy),
+            // the default policy when other row groups read the tile too
             const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(vt);
-            constexpr int kNt = 2;  // cache-policy bits of the buffer load: nt
+            auto issue = [&](auto policy) {
+                constexpr int kAux = decltype(policy)::value;  // cache-policy bits: 2 = nt
 #pragma unroll
-            for (int st = 0; st < NSTEP; ++st) {
-                const rkv_u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_lane, st * KPS * vps, kNt);
-                uint32_t *vr8 = &dst[st][0];
-                vr8[0] = a.x; vr8[1] = a.y; vr8[2] = a.z; vr8[3] = a.w;
-                if constexpr (VRW == 8) {
-                    const rkv_u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_lane + 16u, st * KPS * vps, kNt);
-                    vr8[4] = b.x; vr8[5] = b.y; vr8[6] = b.z; vr8[7] = b.w;
+                for (int st = 0; st < NSTEP; ++st) {
+                    const rkv_u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_lane, st * KPS * vps, kAux);
+                    uint32_t *vr8 = &dst[st][0];
+                    vr8[0] = a.x; vr8[1] = a.y; vr8[2] = a.z; vr8[3] = a.w;
+                    if constexpr (VRW == 8) {
+                        const rkv_u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_lane + 16u, st * KPS * vps, kAux);
+                        vr8[4] = b.x; vr8[5] = b.y; vr8[6] = b.z; vr8[7] = b.w;
+                    }
                 }
-            }
+            };
+            if (p.stream_once)
+                issue(std::integral_constant<int, 2>{});
+            else
+                issue(std::integral_constant<int, 0>{});
             return;
         }
 #pragma unroll
@@ -1377,21 +1405,29 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             const uint8_t *kt = kg + t * sg.k_pos;
             const uint32_t base = lds_addr(smem + w * Sh::STAGE_DW);
             waitcnt_lgkm0();  // this wave's earlier LDS reads of the buffer are done
-            if (nkk == kTile) {
+            auto issue = [&](auto policy) {
+                constexpr bool NT = decltype(policy)::value;
+                if (nkk == kTile) {
 #pragma unroll
-                for (int i = 0; i < NI; ++i)
-                    lds_dma16_s(kt + (int64_t)i * (64 / CPR) * sg.k_pos,
-                                krow + (kchunk ^ (16u * (uint32_t)kswz<Sh::RBK>(i * (64 / CPR)))), base + 1024u * i);
-                return;
-            }
+                    for (int i = 0; i < NI; ++i)
+                        lds_dma16_s<NT>(kt + (int64_t)i * (64 / CPR) * sg.k_pos,
+                                        krow + (kchunk ^ (16u * (uint32_t)kswz<Sh::RBK>(i * (64 / CPR)))),
+                                        base + 1024u * i);
+                    return;
+                }
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int slot = i * 64 + lane;
-                const int j = slot / CPR, cs = slot % CPR;
-                const int c = cs ^ kswz<Sh::RBK>(j);
-                const int jc = j < nkk ? j : nkk - 1;
-                lds_dma16(kt + (uint32_t)(jc * kps + 16 * c), base + 1024u * i);
-            }
+                for (int i = 0; i < NI; ++i) {
+                    const int slot = i * 64 + lane;
+                    const int j = slot / CPR, cs = slot % CPR;
+                    const int c = cs ^ kswz<Sh::RBK>(j);
+                    const int jc = j < nkk ? j : nkk - 1;
+                    lds_dma16<NT>(kt + (uint32_t)(jc * kps + 16 * c), base + 1024u * i);
+                }
+            };
+            if (p.stream_once)
+                issue(std::integral_constant<bool, true>{});
+            else
+                issue(std::integral_constant<bool, false>{});
         }
     };
     // Block-type K and V tiles by dword DMA, issued separately: a tile's K
@@ -1530,7 +1566,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         mfma_q_load<D>(q + (int64_t)rowi * DF + js * D, lane, qraw);
     }
 
-    int64_t t0 = kbeg + (int64_t)ws * kTile;
+    int64_t t0 = kbeg + (p.rg_waves ? 0 : (int64_t)ws * kTile);
     // VMEM loads issued after the K rows' DMA that may stay outstanding when
     // the scores start: 0 or NV.
     //
@@ -1903,8 +1939,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         }
     }
     if constexpr (MFMA_O) {
-        if (DS > 1 || wph == 1) {
-            // One wave per KV head (or dim slice): nothing to merge inside the workgroup, so
+        if (DS > 1 || wph == 1 || p.rg_waves) {
+            // One wave per KV head (or dim slice, or row group over all the
+            // split's keys): nothing to merge inside the workgroup, so
             // the wave writes its rows straight from the MFMA output layout
             // (lane (g, n) holds dims 8n .. 8n+7 of rows 4g .. 4g+3).  The
             // values are those the LDS merge would produce for one wave.

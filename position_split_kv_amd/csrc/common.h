@@ -74,6 +74,8 @@ struct SplitParams {
     int32_t wph_log2;      // log2 of the waves per KV head (waves per workgroup / heads per workgroup)
     int32_t n_q_heads;     // sequence of output row r: r / n_q_heads
     int32_t masked;        // qpos holds the absolute query position of each sequence
+    int32_t stream_once;   // every K / V byte is read once by the launch (one row group per KV head)
+    int32_t rg_waves;      // the waves of a head slot take its row groups (n_rg counts blocks of them), all tiles each
     // Optional slot release: workgroup (0, 0, 0) writes release_value to
     // *release (host-visible memory, system scope) when the kernel starts,
     // i.e. once the kernel before it on the stream has finished.
