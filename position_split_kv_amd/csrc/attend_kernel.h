@@ -1735,10 +1735,14 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 mrow[i] = mn;
             }
             if constexpr (MFMA_O) {
+                // (a row whose maximum did not move has al = 2^0 = 1 exactly:
+                // the rescale is skipped when no row of the wave moved)
+                if (__builtin_amdgcn_ballot_w64(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
 #pragma unroll
-                for (int c = 0; c < 8; ++c)
+                    for (int c = 0; c < 8; ++c)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) oc[c][i] *= al[i];
+                        for (int i = 0; i < 4; ++i) oc[c][i] *= al[i];
+                }
             } else {
 #pragma unroll
                 for (int r = 0; r < RT; ++r) {

@@ -327,10 +327,13 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
             lrow[i] *= al[i];
             mrow[i] = mn;
         }
+        // (skipped when no row's maximum moved: al = 2^0 = 1 exactly)
+        if (__builtin_amdgcn_ballot_w64(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
+            for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) oc[c][i] *= al[i];
+                for (int i = 0; i < 4; ++i) oc[c][i] *= al[i];
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 4 * (lane >> 4) + i;
