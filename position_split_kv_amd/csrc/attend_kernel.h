@@ -1672,7 +1672,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 float4 *xs = (float4 *)&sP[w][0];
                 if (lane < XL) {
 #pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) xs[4 * lane + kb] = make_float4(sv[kb][0], sv[kb][1], sv[kb][2], sv[kb][3]);
+                    for (int kb = 0; kb < 4; ++kb) xs[kb * XL + lane] = make_float4(sv[kb][0], sv[kb][1], sv[kb][2], sv[kb][3]);
                 }
                 __syncthreads();
                 if (lane < XL) {
@@ -1684,7 +1684,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                         const float4 *xo = (const float4 *)&sP[w - js + j][0];
 #pragma unroll
                         for (int kb = 0; kb < 4; ++kb) {
-                            const float4 x = xo[4 * lane + kb];
+                            const float4 x = xo[kb * XL + lane];
                             a4[kb].x += x.x;
                             a4[kb].y += x.y;
                             a4[kb].z += x.z;
