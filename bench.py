@@ -63,11 +63,15 @@ def kernel_source_hash() -> str:
 # on; a figure whose hash differs from the current sources is reported as null.
 #   c2_split_traffic: HBM bytes (FETCH_SIZE, then WRITE_SIZE, each scaled by the
 #     same counter's reading for a plain 1 GiB copy) per split-kernel launch.
-#   c3_counters / c5_counters: SQ busy fractions of the dominant kernel.
+#   c3_counters / c5_counters / c4_window_counters / tbq3_window_counters: SQ
+#     figures of the workload's attention kernel (VALU and MFMA busy fractions,
+#     instructions per wave; profiles/rkv_block_kernels_sq_counters.md).
 MEASURED = {
-    "c2_split_traffic": {"src": None, "bytes": None},
-    "c3_counters": {"src": None},
-    "c5_counters": {"src": None},
+    "c2_split_traffic": {"src": "3b59eafc55055ee7", "fetch_bytes": 269029469, "write_bytes": 5570587, "bytes": 274600056},
+    "c3_counters": {"valu_busy": 0.5122, "mfma_busy": 0.103, "valu_per_wave": 25456, "mfma_per_wave": 1280, "salu_per_wave": 10028, "lds_per_wave": 1960, "wait_frac": 0.343, "issue_frac": 0.442, "lds_conflict_per_lds_active": 1.838, "src": "3b59eafc55055ee7"},
+    "c5_counters": {"valu_busy": 0.3901, "mfma_busy": 0.1526, "valu_per_wave": 6543, "mfma_per_wave": 640, "salu_per_wave": 1538, "lds_per_wave": 982, "wait_frac": 0.395, "issue_frac": 0.407, "lds_conflict_per_lds_active": 0.557, "src": "3b59eafc55055ee7"},
+    "c4_window_counters": {"valu_busy": 0.4401, "mfma_busy": 0.0883, "valu_per_wave": 6379, "mfma_per_wave": 320, "salu_per_wave": 2369, "lds_per_wave": 417, "wait_frac": 0.327, "issue_frac": 0.457, "lds_conflict_per_lds_active": 1.623, "src": "3b59eafc55055ee7"},
+    "tbq3_window_counters": {"valu_busy": 0.4598, "mfma_busy": 0.0923, "valu_per_wave": 6375, "mfma_per_wave": 320, "salu_per_wave": 2205, "lds_per_wave": 609, "wait_frac": 0.316, "issue_frac": 0.483, "lds_conflict_per_lds_active": 1.725, "src": "3b59eafc55055ee7"},
 }
 
 
@@ -500,6 +504,7 @@ def window_q8q4(P, synth, reps, vt=None):
            "roofline": {"bound": "hbm", "kernel": f"rkv_split_kernel<q8_0,{synth.TYPE_NAMES[vt]},128,5,1>",
                         "achieved": round(b / tk / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(b / tk / 1e9 / HBM_PEAK_GBS, 4), "avg_launch_us": round(tk * 1e6, 2)}}
+    res["roofline"]["sq_counters"] = measured("tbq3_window_counters" if vt == synth.TBQ3 else "c4_window_counters")
     return res
 
 
