@@ -165,3 +165,30 @@ def test_tbq3_full_size_sampled_rows():
     o_ref, l_ref = oracle.attend(q.cpu().numpy(), [oracle.view_of(kc.to("cpu"), vc.to("cpu"))], Hkv,
                                  1.0 / math.sqrt(D), rows=rows)
     compare(o, l, o_ref, l_ref, rows=rows, what="full size, one call")
+
+
+@pytest.mark.parametrize("n", [50, 3000])
+def test_tbq3_phases_and_no_alloc(n):
+    """The split kernel and the merge enqueued apart (rkv_attend_split_partials,
+    then rkv_attend_split_merge), and the allocation-free entry point, give
+    rkv_attend_split's bits over TBQ3 values: with one split (the output
+    written directly, then turned back) and with many."""
+    D, Hq, Hkv = 128, 40, 8
+    note(f"tbq3 phases / no-alloc: n={n}")
+    kc, vc = pair(n, Hkv, D, synth.Q8_0, synth.TBQ3, 700 + n, DEV)
+    q = synth.make_query(1, Hq, D, 701 + n, DEV)
+    desc = P.Desc(1, Hq, Hkv, D, 1.0 / math.sqrt(D))
+    segs = [P.view_of_cache(kc, vc, 0, n // 2), P.view_of_cache(kc, vc, n // 2, n)]
+    ws = P.workspace(P.rkv_attend_split_workspace_bytes(desc, segs))
+    o1, l1 = P.attend_split(desc, q, segs, ws=ws)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    P.rkv_attend_split_partials(desc, q, segs, o2, l2, ws)
+    P.rkv_attend_split_merge(desc, segs, o2, l2, ws)
+    o3, l3 = torch.empty_like(o1), torch.empty_like(l1)
+    P.rkv_attend_split_noalloc(desc, q, segs, o3, l3)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    o_ref, l_ref = oracle.attend(q.cpu().numpy(), [oracle.view_of(kc.to("cpu"), vc.to("cpu"))], Hkv,
+                                 1.0 / math.sqrt(D))
+    compare(o1, l1, o_ref, l_ref, what=f"n={n}")
