@@ -221,7 +221,10 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
     // x 4 row groups that decode each tile once (n_rg then counts blocks of 4
     // row groups).
     pl->shd = ds == 1 && D == 128 && rt == 16 && pl->n_rg >= 2 && split_shd_supported(kt, vt);
-    const int nw = pl->shd ? 4 : std::max(1, split_waves(kt, vt, D, rt));
+    // The same over f16 K and V: the staged-tile kernel, whose workgroups hold
+    // one KV head x 4 row groups and stage each tile in LDS once for them.
+    pl->rgs = ds == 1 && D == 128 && rt == 16 && pl->n_rg >= 2 && kt == kF16 && vt == kF16;
+    const int nw = (pl->shd || pl->rgs) ? 4 : std::max(1, split_waves(kt, vt, D, rt));
     const int slots = Hkv * ds;
     int hpw = 1;
     if (ds > 1 && nw < ds) return fail(RKV_E_UNSUPPORTED, "too few waves per workgroup for %d dim slices", ds);
@@ -230,24 +233,24 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
     // the split's keys, so that one workgroup reads a tile for all of them
     // at once (the copies after the first come from the compute unit's
     // caches) rather than one workgroup per row group each reading it.
-    const bool rgw = !pl->shd && ds == 1 && D == 128 && kt != kF32 && vt != kF32 && pl->n_rg > 1 && nw >= 2;
+    const bool rgw = !pl->shd && !pl->rgs && ds == 1 && D == 128 && kt != kF32 && vt != kF32 && pl->n_rg > 1 && nw >= 2;
     int rg_per_wg = 1;
     if (rgw)
         while (rg_per_wg < pl->n_rg && 2 * rg_per_wg <= nw) rg_per_wg *= 2;
-    if (pl->shd)
+    if (pl->shd || pl->rgs)
         hpw = 1;
     else if (ds > 1)
         hpw = nw;
     else
         while (2 * hpw <= nw / rg_per_wg && 2 * hpw <= slots) hpw *= 2;
-    if (pl->shd) pl->n_rg = (pl->n_rg + 3) / 4;
+    if (pl->shd || pl->rgs) pl->n_rg = (pl->n_rg + 3) / 4;
     if (rgw) pl->n_rg = (pl->n_rg + nw / hpw - 1) / (nw / hpw);
     pl->nw = nw;
     pl->hpw = hpw;
     pl->n_hg = (slots + hpw - 1) / hpw;
-    const int64_t wph = pl->shd ? 1 : nw / hpw;
+    const int64_t wph = (pl->shd || pl->rgs) ? 1 : nw / hpw;
     const int64_t units = (int64_t)pl->n_hg * pl->n_rg * pl->z;
-    int occ = pl->shd ? split_shd_occupancy(kt, vt) : split_occupancy(kt, vt, D, rt);
+    int occ = pl->shd ? split_shd_occupancy(kt, vt) : pl->rgs ? split_rgs_occupancy() : split_occupancy(kt, vt, D, rt);
     int cus = compute_units();
     if (occ <= 0) occ = 2;
     if (cus <= 0) cus = 256;
@@ -306,7 +309,7 @@ int make_plan(const rkv_attn_desc *d, int n, const rkv_kv_view *const *v, SplitP
         prm->wph_log2 = wl;
         prm->n_q_heads = Hq;
         prm->masked = d->q_pos != nullptr;
-        prm->stream_once = pl->n_rg == 1 && !rgw;
+        prm->stream_once = pl->n_rg == 1 && !rgw;  // (with shd / rgs: one block of row groups per head)
         prm->rg_waves = rgw;
         if (d->q_pos)
             for (int b = 0; b < S; ++b)  // (clamped so that position differences stay far from overflow)
@@ -386,7 +389,9 @@ int launch_plan(const CallPlan &cp, const SplitParams *prm, const rkv_attn_desc 
         if (!split_supported(cp.g.v[j][0]->k_type, cp.g.v[j][0]->v_type, d->head_dim, pl.rt))
             return fail(RKV_E_UNSUPPORTED, "no kernel for this (type, head_dim, rows)");
         const dim3 grid((unsigned)pl.n_splits, (unsigned)(pl.n_hg * pl.n_rg), (unsigned)pl.z);
-        if (pl.shd)
+        if (pl.rgs)
+            RKV_HIP(launch_split_rgs(grid, q, part_acc, part_ml, o, lse, prm[j], stream));
+        else if (pl.shd)
             RKV_HIP(launch_split_shd(cp.g.v[j][0]->k_type, cp.g.v[j][0]->v_type, grid, q, part_acc, part_ml, o, lse,
                                      prm[j], stream));
         else

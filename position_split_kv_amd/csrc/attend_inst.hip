@@ -1,11 +1,14 @@
 // attend_inst.hip -- instances of the split kernel for one (K type, V type)
 // pair.  Built once per pair with -DRKV_KT=<t> -DRKV_VT=<t> (0 f32, 1 f16,
-// 2 q8_0, 3 q4_0) so that the instances compile in parallel.
+// 2 q8_0, 3 q4_0, 4 TBQ3) so that the instances compile in parallel.
 #include "attend_kernel.h"
 #include "attend_shd.h"
 
 #if !defined(RKV_KT) || !defined(RKV_VT)
 #error "RKV_KT and RKV_VT must be defined"
+#endif
+#if RKV_KT == 1 && RKV_VT == 1
+#include "attend_rgs.h"  // (its kernel is not a template: one unit defines it)
 #endif
 
 #define RKV_CAT4(a, b, c, d) a##b##c##d
@@ -185,5 +188,27 @@ int RKV_NAME_SHD_OCC(RKV_KT, RKV_VT)()
 
 #define RKV_NAME_SHD_OK(kt, vt) RKV_CAT4(split_shd_supported_k, kt, _v, vt)
 bool RKV_NAME_SHD_OK(RKV_KT, RKV_VT)() { return ShdShape<RKV_KT, RKV_VT>::OK; }
+
+
+// The staged-tile kernel for many rows per KV head (attend_rgs.h): f16 K and
+// V at head_dim 128, built with the f16 / f16 pair only.
+#if RKV_KT == 1 && RKV_VT == 1
+hipError_t launch_split_rgs(dim3 grid, const float *q, float *pa, float2 *pm, float *o, float *lse,
+                            const SplitParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL(rkv_split_rgs_kernel, grid, dim3(64 * kRgsRG), 0, s, q, pa, pm, o, lse, p);
+    return hipGetLastError();
+}
+
+int split_rgs_occupancy()
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rkv_split_rgs_kernel, 64 * kRgsRG, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return n;
+}
+#endif
 
 }  // namespace rkv

@@ -1151,7 +1151,21 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     constexpr int NSTEP = kTile / KPS;
     constexpr int VRW = VT == kF32 ? 8 : 4;  // dwords of one lane's 8 values, register path
     constexpr int MERGE_DW = NW * RT * (D + 2);
-    constexpr int SMEM_DW = NW * Sh::STAGE_DW > MERGE_DW ? NW * Sh::STAGE_DW : MERGE_DW;
+    constexpr int SMEM_DW1 = NW * Sh::STAGE_DW > MERGE_DW ? NW * Sh::STAGE_DW : MERGE_DW;
+    // Block-type K and V rows by DMA at head_dim 128 without dim slices (the
+    // BDMA path below): a second V buffer per wave (VDB) wherever it fits the
+    // compute unit's LDS without lowering the number of workgroups it holds.
+    // Tile i+1's V rows then go out together with its K rows once tile i's
+    // scores are done, instead of after tile i's P.V, and have the rest of
+    // tile i (softmax, P.V) and tile i+1's scores to land.
+    constexpr bool BDMA_SHAPE = (KT == kQ8 || KT == kQ4) && (VT == kQ8 || VT == kQ4 || VT == kT3) && D == 128 &&
+                                RT <= 16 && DS == 1 && Sh::RBK % 4 == 0 && Sh::RBV % 4 == 0 && LSK + LSV <= 63;
+    constexpr int LDS_REST = 4 * NW * (Sh::P_IN_K ? 4 : RTX * kTile) + 4 * NW * RT + (VT == kT3 ? 512 : 8);
+    constexpr int SMEM_DW2 = NW * Sh::STAGE_DW + NW * kTile * LSV > MERGE_DW ? NW * Sh::STAGE_DW + NW * kTile * LSV
+                                                                             : MERGE_DW;
+    constexpr int LDS1 = 4 * SMEM_DW1 + LDS_REST, LDS2 = 4 * SMEM_DW2 + LDS_REST;
+    constexpr bool VDB = BDMA_SHAPE && LDS2 <= 160 * 1024 && (160 * 1024) / LDS2 == (160 * 1024) / LDS1;
+    constexpr int SMEM_DW = VDB ? SMEM_DW2 : SMEM_DW1;
 
     __shared__ __attribute__((aligned(16))) uint32_t smem[SMEM_DW];
     __shared__ __attribute__((aligned(16))) float sP[NW][Sh::P_IN_K ? 4 : RTX * kTile];
@@ -1178,7 +1192,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform in the wave
     uint32_t *sK = smem + w * Sh::STAGE_DW;
-    uint32_t *sV = sK + kTile * LSK;
+    uint32_t *sV = sK + kTile * LSK;  // this tile's V rows (block-type V)
+    // the next tile's V rows with VDB (the buffers swap after each tile)
+    uint32_t *sVn = VDB ? smem + NW * Sh::STAGE_DW + w * kTile * LSV : sV;
     // this wave's score rows P [row][key] (in its K tile when that is free)
     float *const sPw = Sh::P_IN_K ? (float *)sK : &sP[w][0];
 
@@ -1243,7 +1259,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     // limits are clamped to [-1, 2^30])
     constexpr int kSeeAll = 1 << 30;
     int lim[RT];
-    int lim_max = -1;
+    int lim_max = -1, lim_min = kSeeAll;  // over the wave's real rows
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
         int x = kSeeAll;
@@ -1252,9 +1268,13 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             x = rel < -1 ? -1 : rel > kSeeAll ? kSeeAll : (int)rel;
         }
         lim[r] = x;
-        if (r < nr) lim_max = x > lim_max ? x : lim_max;
+        if (r < nr) {
+            lim_max = x > lim_max ? x : lim_max;
+            lim_min = x < lim_min ? x : lim_min;
+        }
     }
-    if (DS == 1 && p.masked && kend > kbeg + lim_max + 1) kend = kbeg + lim_max + 1 > kbeg ? kbeg + lim_max + 1 : kbeg;
+    // (limits, kbeg and kend all count keys from the segment's first one)
+    if (DS == 1 && p.masked && kend > (int64_t)lim_max + 1) kend = (int64_t)lim_max + 1 > kbeg ? (int64_t)lim_max + 1 : kbeg;
 
     float m[RT], l[RT], acc[RT][8];
 #pragma unroll
@@ -1326,6 +1346,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     constexpr bool BDMA = MFMA_S && (KT == kQ8 || KT == kQ4) && (VT == kQ8 || VT == kQ4 || VT == kT3) && Sh::RBK % 4 == 0 &&
                           Sh::RBV % 4 == 0 && LSK <= 64 && LSV <= 64;
     constexpr int NVD = LSV < 63 ? LSV : 63;  // V loads a wait for K may leave outstanding
+    static_assert(!VDB || BDMA, "the second V buffer belongs to the block-type DMA path");
     KRegs kr;
     VRegs vr;
     uint32_t vreg[V_REG ? NSTEP : 1][VRW];
@@ -1452,12 +1473,12 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 dma_rows4<Sh::RBK / 4, LSK>(kg + t * sg.k_pos, kps, nkk, base, lane);
         }
     };
-    auto dma_vb = [&](int64_t t, int nkk) {
+    auto dma_vb = [&](int64_t t, int nkk, const uint32_t *dst) {
         if constexpr (BDMA) {
             int vps2 = (int)sg.v_pos;
             asm volatile("" : "+s"(vps2));
             waitcnt_lgkm0();  // this wave's earlier LDS reads of the V buffer are done
-            const uint32_t base = lds_addr(smem + w * Sh::STAGE_DW) + 4u * kTile * LSK;
+            const uint32_t base = lds_addr(dst);
             if (vfull_ok && nkk == kTile && t + kTile < sg.n_keys)
                 dma_rows4_full<LSV1>(vg + t * sg.v_pos, vps2, vwrap, base, lane);
             else
@@ -1580,7 +1601,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     if constexpr (BDMA) {
         if (t0 < kend) {
             dma_kb(t0, nk_at(t0));
-            dma_vb(t0, nk_at(t0));
+            dma_vb(t0, nk_at(t0), sV);
         }
     } else if constexpr (KDMA) {
         if (t0 < kend) {
@@ -1624,8 +1645,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         const int nk = nk_at(t0);
         const int64_t tn = t0 + tstep;
         if constexpr (BDMA) {
-            // K went out before the previous tile's P.V and V after it: once
-            // at most V's loads are outstanding this tile's K rows have landed
+            // K went out before the previous tile's P.V and V after it (with
+            // VDB right after K): once at most V's loads are outstanding this
+            // tile's K rows have landed
             waitcnt_vm<NVD>();
         } else if constexpr (KDMA) {
             // K rows arrive by DMA issued one tile ahead (V rows in registers
@@ -1656,7 +1678,21 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             // (before the slices exchange their partial scores: each slice
             // scaled its query rows by its own power of two)
             if (qscaled) unscale_rows(sv, oex);
-            if constexpr (BDMA) {
+            if constexpr (VDB) {
+                // the next tile's K rows (its V rows into the other buffer)
+                // load through the rest of this tile; then this tile's V rows,
+                // issued before them, have landed once at most their loads
+                // are outstanding
+                __builtin_amdgcn_wave_barrier();
+                if (tn < kend) {
+                    dma_kb(tn, nk_at(tn));
+                    dma_vb(tn, nk_at(tn), sVn);
+                    waitcnt_vm<LSK + LSV>();
+                } else {
+                    waitcnt_vm<0>();
+                }
+                __builtin_amdgcn_wave_barrier();
+            } else if constexpr (BDMA) {
                 // this tile's V rows have landed (nothing else is in flight), so
                 // the next tile's K rows can load through the rest of the tile
                 waitcnt_vm<0>();
@@ -1701,18 +1737,20 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 }
                 __syncthreads();  // every slice has read the partials before P overwrites them
             }
-            // last key of the tile each output row sees
+            // last key of the tile each output row sees; a masked launch
+            // masks only the tiles that reach past some row's last key
+            const bool tile_masked = p.masked && t0 + nk - 1 > lim_min;
             int kmx[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) kmx[i] = nk - 1;
-            if (p.masked) {
+            if (tile_masked) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tl = limv[i] - (int)t0;
                     kmx[i] = tl < nk - 1 ? (tl < -1 ? -1 : tl) : nk - 1;
                 }
             }
-            if (p.masked || nk < kTile) {
+            if (tile_masked || nk < kTile) {
                 if (cap > 0.f)
                     cap_mask_tile<true, true>(sv, kmx, lane & 15, capl, two_over_cap);
                 else
@@ -1912,8 +1950,12 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
         if constexpr (PIPE && V_REG) {
             if (tn < kend) load_vreg(tn, nk_at(tn));
         }
-        if constexpr (BDMA) {
-            if (tn < kend) dma_vb(tn, nk_at(tn));
+        if constexpr (VDB) {
+            uint32_t *const sx = sV;
+            sV = sVn;
+            sVn = sx;
+        } else if constexpr (BDMA) {
+            if (tn < kend) dma_vb(tn, nk_at(tn), sV);
         }
         if constexpr (KDMA && V_REG) {
             v_after_dma = 0;

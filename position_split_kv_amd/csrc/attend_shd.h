@@ -108,6 +108,18 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
         }
         limv[i] = x;
     }
+    // the earliest limit of the wave's rows: tiles that end at or before it
+    // need no mask
+    int lim_min = kSeeAll;
+    if (p.masked) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+            if (tabrow[r] >= 0) {
+                const int64_t rel = p.qpos[tabrow[r] / p.n_q_heads] - sg.pos0;
+                const int x = rel < -1 ? -1 : rel > kSeeAll ? kSeeAll : (int)rel;
+                lim_min = x < lim_min ? x : lim_min;
+            }
+    }
 
     // raw tile DMA: the LSK K loads and LSV V loads of a tile, a quarter per
     // wave (wave 0: K loads [0, KA), 1: [KA, KB), 2: K [KB, LSK) and V [0, VA),
@@ -302,13 +314,14 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
         }
         if (qscaled) unscale_rows(sv, oex);
         // ---- mask, cap, online softmax (as the general kernel)
+        const bool tile_masked = p.masked && t0 + nk - 1 > lim_min;
         int kmx[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tl = limv[i] - (int)t0;
-            kmx[i] = p.masked ? (tl < nk - 1 ? (tl < -1 ? -1 : tl) : nk - 1) : nk - 1;
+            kmx[i] = tile_masked ? (tl < nk - 1 ? (tl < -1 ? -1 : tl) : nk - 1) : nk - 1;
         }
-        if (p.masked || nk < kTile) {
+        if (tile_masked || nk < kTile) {
             if (cap > 0.f)
                 cap_mask_tile<true, true>(sv, kmx, qi, capl, two_over_cap);
             else

@@ -102,6 +102,7 @@ struct SplitPlan {
     int z;           // grid z (sequences with own keys, or 1)
     int n_splits;    // grid x
     bool shd;        // the shared-decode kernel (n_rg then counts blocks of its row groups)
+    bool rgs;        // the staged-tile f16 kernel (n_rg then counts blocks of its row groups)
     int64_t n_rows_total;
     size_t acc_bytes, ml_bytes;
     size_t ws_bytes;
@@ -141,6 +142,12 @@ bool split_shd_supported(int kt, int vt);
 int split_shd_occupancy(int kt, int vt);
 hipError_t launch_split_shd(int kt, int vt, dim3 grid, const float *q, float *part_acc, float2 *part_ml, float *o,
                             float *lse, const SplitParams &p, hipStream_t stream);
+// The staged-tile split kernel (attend_rgs.h): many rows per KV head over f16
+// K and V at head_dim 128 (16 rows per wave, 4 row groups of one KV head per
+// workgroup, each tile staged once in LDS; grid y = KV heads x row-group blocks).
+int split_rgs_occupancy();
+hipError_t launch_split_rgs(dim3 grid, const float *q, float *part_acc, float2 *part_ml, float *o, float *lse,
+                            const SplitParams &p, hipStream_t stream);
 hipError_t launch_fill_empty(int d, int64_t n_rows, float *o, float *lse, hipStream_t stream);
 
 struct CombineParts {

@@ -86,6 +86,18 @@ CASES = [
     ("q4q4_shd_odd_heads", 1, 60, 3, 128, synth.Q4_0, synth.Q4_0, 777, 333, None, 0.0, None),
     ("q8q4_shd_rows40_cap", 1, 40, 1, 128, synth.Q8_0, synth.Q4_0, 500, 200, None, 20.0, None),
     ("q8q4_shd_rows120", 1, 240, 2, 128, synth.Q8_0, synth.Q4_0, 420, 70, None, 0.0, None),
+    # more than 16 rows per KV head over f16 K and V at head_dim 128: the staged-tile kernel (one KV head x four
+    # 16-row groups per workgroup, each tile staged once in LDS): 20 rows per head over an odd head count (two
+    # row groups without rows), 40 rows with a cap, 120 rows (two blocks of row groups, default cache policy),
+    # sequences with their own keys (32 rows per sequence and head), 64 rows over ragged tiles, a head map with
+    # 18 and 2 rows, and segments of one short tile (a single split: o and lse written directly)
+    ("f16_rgs_odd_heads", 1, 60, 3, 128, synth.F16, synth.F16, 777, 333, None, 0.0, None),
+    ("f16_rgs_rows40_cap", 1, 40, 1, 128, synth.F16, synth.F16, 500, 200, None, 20.0, None),
+    ("f16_rgs_rows120", 1, 240, 2, 128, synth.F16, synth.F16, 420, 70, None, 0.0, None),
+    ("f16_rgs_batch2_own_keys", 2, 64, 2, 128, synth.F16, synth.F16, 300, 130, None, 0.0, None),
+    ("f16_rgs_rows64_ragged", 1, 64, 1, 128, synth.F16, synth.F16, 129, 64, None, 0.0, None),
+    ("f16_rgs_map_18_2", 1, 20, 2, 128, synth.F16, synth.F16, 257, 128, None, 0.0, [0] * 18 + [1] * 2),
+    ("f16_rgs_one_tile", 1, 40, 2, 128, synth.F16, synth.F16, 50, 20, None, 0.0, None),
 ]
 
 

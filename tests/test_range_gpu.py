@@ -101,6 +101,10 @@ CASES = [
     ("q_tiny_f16", 1, 40, 8, 128, synth.F16, "big", synth.F16, False, 600, 250, 2.0 ** 14 / math.sqrt(128), 0.0,
      [-26, -26, -25, -26, -27]),
     ("q_big_q8q4", 1, 16, 2, 128, synth.Q8_0, "tiny", synth.Q4_0, False, 500, 200, None, 0.0, [19, 18, 0, 19]),
+    # the same query ranges with 40 rows per KV head over f16 K and V (the staged-tile kernel)
+    ("q_big_f16_rows40", 1, 40, 1, 128, synth.F16, "tiny", synth.F16, False, 600, 250, None, 0.0, [19, 0, 18, -3, 19]),
+    ("q_tiny_f16_rows40", 2, 40, 2, 128, synth.F16, "big", synth.F16, False, 600, 250, 2.0 ** 14 / math.sqrt(128),
+     0.0, [-26, -26, -25, -26, -27]),
 ]
 
 
