@@ -47,7 +47,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X published dense f16 matrix-core rate
 
 # Sources whose content decides the attention kernels: figures taken from
 # hardware counters are valid only for the kernels they were taken on.
-KERNEL_SOURCES = ["attend_kernel.h", "attend_shd.h", "attend_inst.hip", "attend.hip", "common.h"]
+KERNEL_SOURCES = ["attend_kernel.h", "attend_shd.h", "attend_rgs.h", "attend_inst.hip", "attend.hip", "common.h"]
 
 
 def kernel_source_hash() -> str:
@@ -63,21 +63,22 @@ def kernel_source_hash() -> str:
 # on; a figure whose hash differs from the current sources is reported as null.
 #   c2_split_traffic: HBM bytes (FETCH_SIZE, then WRITE_SIZE, each scaled by the
 #     same counter's reading for a plain 1 GiB copy) per split-kernel launch.
-#   c3_counters / c5_counters / c4_window_counters / tbq3_window_counters: SQ
-#     figures of the workload's attention kernel (VALU and MFMA busy fractions,
-#     instructions per wave; profiles/rkv_block_kernels_sq_counters.md).
+#   c3_counters / c5_counters / c4_window_counters / tbq3_window_counters /
+#     verify_counters: SQ figures of the workload's attention kernel (VALU and MFMA busy fractions,
+#     instructions per wave; profiles/rkv_split_kernels_sq_counters.md).
 MEASURED = {
-    "c2_split_traffic": {"src": "3b59eafc55055ee7", "fetch_bytes": 269029469, "write_bytes": 5570587, "bytes": 274600056},
-    "c3_counters": {"valu_busy": 0.5122, "mfma_busy": 0.103, "valu_per_wave": 25456, "mfma_per_wave": 1280, "salu_per_wave": 10028, "lds_per_wave": 1960, "wait_frac": 0.343, "issue_frac": 0.442, "lds_conflict_per_lds_active": 1.838, "src": "3b59eafc55055ee7"},
-    "c5_counters": {"valu_busy": 0.3901, "mfma_busy": 0.1526, "valu_per_wave": 6543, "mfma_per_wave": 640, "salu_per_wave": 1538, "lds_per_wave": 982, "wait_frac": 0.395, "issue_frac": 0.407, "lds_conflict_per_lds_active": 0.557, "src": "3b59eafc55055ee7"},
-    "c4_window_counters": {"valu_busy": 0.4401, "mfma_busy": 0.0883, "valu_per_wave": 6379, "mfma_per_wave": 320, "salu_per_wave": 2369, "lds_per_wave": 417, "wait_frac": 0.327, "issue_frac": 0.457, "lds_conflict_per_lds_active": 1.623, "src": "3b59eafc55055ee7"},
-    "tbq3_window_counters": {"valu_busy": 0.4598, "mfma_busy": 0.0923, "valu_per_wave": 6375, "mfma_per_wave": 320, "salu_per_wave": 2205, "lds_per_wave": 609, "wait_frac": 0.316, "issue_frac": 0.483, "lds_conflict_per_lds_active": 1.725, "src": "3b59eafc55055ee7"},
+    "c2_split_traffic": {"src": "b300c89a47c0221f", "fetch_bytes": 269015087, "write_bytes": 5570585, "bytes": 274585672},
+    "c3_counters": {"valu_busy": 0.5119, "mfma_busy": 0.1026, "valu_per_wave": 25538, "mfma_per_wave": 1280, "salu_per_wave": 10267, "lds_per_wave": 1960, "wait_frac": 0.337, "issue_frac": 0.442, "lds_conflict_per_lds_active": 1.834, "src": "b300c89a47c0221f"},
+    "c5_counters": {"valu_busy": 0.3881, "mfma_busy": 0.1514, "valu_per_wave": 6563, "mfma_per_wave": 640, "salu_per_wave": 1591, "lds_per_wave": 982, "wait_frac": 0.393, "issue_frac": 0.409, "lds_conflict_per_lds_active": 0.557, "src": "b300c89a47c0221f"},
+    "c4_window_counters": {"valu_busy": 0.4363, "mfma_busy": 0.0886, "valu_per_wave": 6304, "mfma_per_wave": 320, "salu_per_wave": 2453, "lds_per_wave": 417, "wait_frac": 0.298, "issue_frac": 0.464, "lds_conflict_per_lds_active": 1.621, "src": "b300c89a47c0221f"},
+    "tbq3_window_counters": {"valu_busy": 0.3625, "mfma_busy": 0.0725, "valu_per_wave": 6403, "mfma_per_wave": 320, "salu_per_wave": 2308, "lds_per_wave": 609, "wait_frac": 0.337, "issue_frac": 0.463, "lds_conflict_per_lds_active": 1.726, "src": "b300c89a47c0221f"},
+    "verify_counters": {"valu_busy": 0.3122, "mfma_busy": 0.1575, "valu_per_wave": 6089, "mfma_per_wave": 768, "salu_per_wave": 2785, "lds_per_wave": 582, "wait_frac": 0.467, "issue_frac": 0.365, "lds_conflict_per_lds_active": 0.705, "src": "b300c89a47c0221f"},
 }
 
 
 def measured(name):
-    m = MEASURED[name]
-    return m if m.get("src") == kernel_source_hash() else None
+    m = MEASURED.get(name)
+    return m if m and m.get("src") == kernel_source_hash() else None
 
 
 def log(msg):
@@ -588,10 +589,20 @@ def verify_rows(P, synth, reps):
     def ver():
         P.rkv_attend_split(d, q, segs[k[0] % 2], o, l, ws)
         k[0] += 1
+
+    def part():
+        P.rkv_attend_split_partials(d, q, segs[k[0] % 2], o, l, ws)
+        k[0] += 1
     t = timed(ver, reps)
+    tk = timed(part, reps)
     b = 2 * n * Hkv * D * 2
     return {"us": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1), "frac_of_hbm_peak": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes": b, "rows_per_kv_head": nq * Hq // Hkv}
+            "bytes": b, "rows_per_kv_head": nq * Hq // Hkv,
+            "roofline": {"bound": "hbm", "kernel": "rkv_split_rgs_kernel (f16, 40 rows per KV head: each tile staged once "
+                                                   "per head)",
+                         "achieved": round(b / tk / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(b / tk / 1e9 / HBM_PEAK_GBS, 4), "avg_launch_us": round(tk * 1e6, 2),
+                         "sq_counters": measured("verify_counters")}}
 
 
 def append_path(P, synth, reps):
