@@ -14,7 +14,9 @@ oracle computes one by one (every sampled row still attends every key).
     stored once plus a private 2048-key f16 suffix per sequence, as one
     rkv_attend_split call (the shared-decode launch over the prefix, the
     suffix launch, one merge: the form the benchmark times) and as the
-    three-call form.
+    three-call form;
+  - verify step: 8 draft rows under the causal mask over the f16 layer above,
+    one rkv_attend_split call (the staged-tile kernel).
 
 Sampled rows cover every KV head.
 """
@@ -61,6 +63,30 @@ def test_qwen14b_f16_layer_full():
     o_ref, l_ref = oracle.attend(q.cpu().numpy(), views, Hkv, 1.0 / math.sqrt(D), rows=rows)
     compare(o1, l1, o_ref, l_ref, rows=rows, what="one launch (bench step)")
     compare(o3, l3, o_ref, l_ref, rows=rows, what="segment, segment, combine")
+
+
+def test_verify_step_full():
+    """The verify step the benchmark times: 8 draft rows at positions 65528 ..
+    65535 over the 40/8-head, head_dim 128 f16 layer of 65536 keys (window 49152
+    + tail 16384), causal mask, one rkv_attend_split call (40 rows per KV head:
+    the staged-tile kernel)."""
+    Hq, Hkv, D, n, wc, nq = 40, 8, 128, 65536, 49152, 8
+    pos = list(range(n - nq, n))
+    note(f"full size verify step: {nq} rows x Hq={Hq} Hkv={Hkv} D={D} n={n} wc={wc}, q_pos={pos[0]}..{pos[-1]}")
+    kc, vc = pair(n, Hkv, D, synth.F16, synth.F16, 20011, DEV, outliers=round(0.01 * Hkv * D))
+    q = synth.make_query(nq, Hq, D, synth.stream_seed(20011, 3), DEV)
+    desc = P.Desc(nq, Hq, Hkv, D, 1.0 / math.sqrt(D), q_pos=pos)
+    segs = [P.view_of_cache(kc, vc, 0, wc), P.view_of_cache(kc, vc, wc, n)]
+    o1, l1 = P.attend_split(desc, q, segs)
+    torch.cuda.synchronize()
+    # rows b * Hq + h: every draft position and every KV head (h // 5)
+    rows = [b * Hq + h for b, h in [(0, 0), (1, 6), (2, 12), (3, 17), (4, 23), (5, 27), (6, 33), (7, 39), (7, 5),
+                                    (0, 38)]]
+    assert sorted({(r % Hq) // (Hq // Hkv) for r in rows}) == list(range(Hkv))
+    assert sorted({r // Hq for r in rows}) == list(range(nq))
+    views, _ = host_views(kc, vc)
+    o_ref, l_ref = oracle.attend(q.cpu().numpy(), views, Hkv, 1.0 / math.sqrt(D), rows=rows, q_pos=pos)
+    compare(o1, l1, o_ref, l_ref, rows=rows, what="verify step, one call (bench form)")
 
 
 @pytest.mark.parametrize("scale", [None, 1.0], ids=["scale_1_over_sqrt_d", "stress_scale_1"])
