@@ -96,15 +96,18 @@ def test_masked_single_split_empty_rows():
     assert not torch.any(o[:2]) and torch.all(torch.isneginf(lse[:2]))
 
 
-def test_masked_stream_tail():
-    """A verify step of 6 rows with the tail in pinned host memory, streamed in
-    tiles: equal bit for bit to the same ring step with the tail resident in
-    device memory (attended in place, each tile at its absolute position), to
-    the segment calls per tile + combine to rounding, and to the oracle."""
+@pytest.mark.parametrize("kt,vt", [(synth.Q8_0, synth.Q4_0), (synth.F16, synth.F16)], ids=["q8q4", "f16"])
+def test_masked_stream_tail(kt, vt):
+    """A verify step of 6 rows (30 per KV head: the shared-decode kernel for
+    q8_0 / q4_0, the staged-tile kernel for f16) with the tail in pinned host
+    memory, streamed in tiles: equal bit for bit to the same ring step with the
+    tail resident in device memory (attended in place, each tile at its
+    absolute position), to the segment calls per tile + combine to rounding,
+    and to the oracle."""
     Hq, Hkv, D, n, wc, tile, B = 40, 8, 128, 3000, 1200, 512, 3
     pos = [wc - 3, wc + 2, 2000, n - 3, n - 2, n - 1]
-    note(f"masked stream tail: n={n} wc={wc} tile={tile} q_pos={pos}")
-    kc, vc = pair(n, Hkv, D, synth.Q8_0, synth.Q4_0, 9, DEV)
+    note(f"masked stream tail {synth.TYPE_NAMES[kt]}/{synth.TYPE_NAMES[vt]}: n={n} wc={wc} tile={tile} q_pos={pos}")
+    kc, vc = pair(n, Hkv, D, kt, vt, 9, DEV)
     q = synth.make_query(len(pos), Hq, D, 10, DEV)
     desc = P.Desc(len(pos), Hq, Hkv, D, default_scale(D), q_pos=pos)
     kh = torch.empty(kc.data[wc:].shape, dtype=kc.data.dtype, pin_memory=True)
