@@ -436,19 +436,63 @@ __device__ __forceinline__ void lds_dma4_s(const void *sbase, uint32_t voff, uin
 // i+1 that offset grows by DJ*P + 4*DC (uniform) plus P - 4*LS when the slot
 // wraps past a row end; bit i of wrap holds that wrap for the lane, so that
 // offset_i = i*(DJ*P + 4*DC) + 4*lane + (lane/LS + wraps before i)*(P - 4*LS).
-template <int LS>
-__device__ __forceinline__ uint64_t dma_wraps(int lane)
+// Bit i of the plan is set iff (lane mod LS + i * DC) mod LS >= LS - DC.
+// Stepping i through every load costs a few VALU per load at the kernel's
+// start; when DC has an inverse modulo LS the loads whose column lands on a
+// given residue r are i = (r - lane mod LS) * DC^-1 mod LS, so only the
+// residues of the smaller class (the DC wrapping ones, or the LS - DC others)
+// are visited, each at one add and one conditional subtract.
+__host__ __device__ constexpr uint64_t dma_wraps_stepped(int LS, int lane)
 {
-    constexpr int DC = 64 % LS;
+    const int DC = 64 % LS;
     int c = lane % LS;
     uint64_t wrap = 0;
-#pragma unroll
     for (int i = 0; i + 1 < LS; ++i) {
         if (c >= LS - DC) wrap |= 1ull << i;
         c += DC;
         if (c >= LS) c -= LS;
     }
     return wrap;
+}
+__host__ __device__ constexpr int dma_wrap_inverse(int LS)
+{
+    const int DC = 64 % LS;
+    for (int x = 1; x < LS; ++x)
+        if (DC * x % LS == 1) return x;
+    return 0;
+}
+template <int LS>
+__host__ __device__ constexpr uint64_t dma_wraps_by_residue(int lane)
+{
+    constexpr int DC = 64 % LS, INV = dma_wrap_inverse(LS);
+    constexpr bool OTHERS = 2 * DC > LS;  // visit the non-wrapping residues and complement
+    constexpr int R0 = OTHERS ? 0 : LS - DC, NR = OTHERS ? LS - DC : DC;
+    const int c0 = lane % LS;
+    int i = (R0 - c0 + LS) % LS * INV % LS;  // load of residue R0
+    uint64_t m = 0;
+    for (int k = 0; k < NR; ++k) {
+        if (i < LS - 1) m |= 1ull << i;
+        i += INV;
+        if (i >= LS) i -= LS;
+    }
+    return OTHERS ? ~m & ((1ull << (LS - 1)) - 1) : m;
+}
+template <int LS>
+constexpr bool dma_wraps_agree()
+{
+    for (int lane = 0; lane < 64; ++lane)
+        if (dma_wraps_by_residue<LS>(lane) != dma_wraps_stepped(LS, lane)) return false;
+    return true;
+}
+template <int LS>
+__device__ __forceinline__ uint64_t dma_wraps(int lane)
+{
+    if constexpr (64 % LS != 0 && dma_wrap_inverse(LS) != 0) {
+        static_assert(dma_wraps_agree<LS>(), "the residue form of the wrap plan equals the stepped one for every lane");
+        return dma_wraps_by_residue<LS>(lane);
+    } else {
+        return dma_wraps_stepped(LS, lane);
+    }
 }
 
 // dma_rows4 for a whole tile (kTile rows) that is followed by at least one
@@ -805,14 +849,20 @@ __device__ __forceinline__ int mfma_q_split(const float (*x)[8], bool has, float
     // mx = f 2^e with f in [0.5, 1): mx 2^(15 - e) is in [2^14, 2^15)
     const int e = __builtin_amdgcn_frexp_expf(mx);
     const int ex = (mx == 0.f || (e >= -1 && e <= 15)) ? 0 : 15 - e;
+    // (the scaling pass only when some row of the wave needs it)
+    if (__builtin_amdgcn_ballot_w64(ex != 0)) {
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[kk][e] = __builtin_amdgcn_ldexpf(y[kk][e], ex);
+    }
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float z = __builtin_amdgcn_ldexpf(y[kk][e], ex);
-            const _Float16 h = (_Float16)z;
+            const _Float16 h = (_Float16)y[kk][e];
             qhi[kk][e] = h;
-            qlo[kk][e] = (_Float16)(z - (float)h);
+            qlo[kk][e] = (_Float16)(y[kk][e] - (float)h);
         }
     return ex;
 }
@@ -1166,6 +1216,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     constexpr int LDS1 = 4 * SMEM_DW1 + LDS_REST, LDS2 = 4 * SMEM_DW2 + LDS_REST;
     constexpr bool VDB = BDMA_SHAPE && LDS2 <= 160 * 1024 && (160 * 1024) / LDS2 == (160 * 1024) / LDS1;
     constexpr int SMEM_DW = VDB ? SMEM_DW2 : SMEM_DW1;
+    static_assert(4 * SMEM_DW + LDS_REST <= 160 * 1024, "a workgroup's LDS fits one compute unit");
 
     __shared__ __attribute__((aligned(16))) uint32_t smem[SMEM_DW];
     __shared__ __attribute__((aligned(16))) float sP[NW][Sh::P_IN_K ? 4 : RTX * kTile];
