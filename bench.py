@@ -67,12 +67,12 @@ def kernel_source_hash() -> str:
 #     verify_counters: SQ figures of the workload's attention kernel (VALU and MFMA busy fractions,
 #     instructions per wave; profiles/rkv_split_kernels_sq_counters.md).
 MEASURED = {
-    "c2_split_traffic": {"src": "b300c89a47c0221f", "fetch_bytes": 269015087, "write_bytes": 5570585, "bytes": 274585672},
-    "c3_counters": {"valu_busy": 0.5119, "mfma_busy": 0.1026, "valu_per_wave": 25538, "mfma_per_wave": 1280, "salu_per_wave": 10267, "lds_per_wave": 1960, "wait_frac": 0.337, "issue_frac": 0.442, "lds_conflict_per_lds_active": 1.834, "src": "b300c89a47c0221f"},
-    "c5_counters": {"valu_busy": 0.3881, "mfma_busy": 0.1514, "valu_per_wave": 6563, "mfma_per_wave": 640, "salu_per_wave": 1591, "lds_per_wave": 982, "wait_frac": 0.393, "issue_frac": 0.409, "lds_conflict_per_lds_active": 0.557, "src": "b300c89a47c0221f"},
-    "c4_window_counters": {"valu_busy": 0.4363, "mfma_busy": 0.0886, "valu_per_wave": 6304, "mfma_per_wave": 320, "salu_per_wave": 2453, "lds_per_wave": 417, "wait_frac": 0.298, "issue_frac": 0.464, "lds_conflict_per_lds_active": 1.621, "src": "b300c89a47c0221f"},
-    "tbq3_window_counters": {"valu_busy": 0.3625, "mfma_busy": 0.0725, "valu_per_wave": 6403, "mfma_per_wave": 320, "salu_per_wave": 2308, "lds_per_wave": 609, "wait_frac": 0.337, "issue_frac": 0.463, "lds_conflict_per_lds_active": 1.726, "src": "b300c89a47c0221f"},
-    "verify_counters": {"valu_busy": 0.3122, "mfma_busy": 0.1575, "valu_per_wave": 6089, "mfma_per_wave": 768, "salu_per_wave": 2785, "lds_per_wave": 582, "wait_frac": 0.467, "issue_frac": 0.365, "lds_conflict_per_lds_active": 0.705, "src": "b300c89a47c0221f"},
+    "c2_split_traffic": {"src": "6f6737aa47f44a25", "fetch_bytes": 269025156, "write_bytes": 5570584, "bytes": 274595739},
+    "c3_counters": {"valu_busy": 0.5149, "mfma_busy": 0.1038, "valu_per_wave": 25407, "mfma_per_wave": 1280, "salu_per_wave": 10267, "lds_per_wave": 1960, "wait_frac": 0.336, "issue_frac": 0.444, "lds_conflict_per_lds_active": 1.836, "src": "6f6737aa47f44a25"},
+    "c5_counters": {"valu_busy": 0.3858, "mfma_busy": 0.1523, "valu_per_wave": 6485, "mfma_per_wave": 640, "salu_per_wave": 1587, "lds_per_wave": 982, "wait_frac": 0.393, "issue_frac": 0.406, "lds_conflict_per_lds_active": 0.557, "src": "6f6737aa47f44a25"},
+    "c4_window_counters": {"valu_busy": 0.4292, "mfma_busy": 0.0902, "valu_per_wave": 6090, "mfma_per_wave": 320, "salu_per_wave": 2454, "lds_per_wave": 417, "wait_frac": 0.303, "issue_frac": 0.449, "lds_conflict_per_lds_active": 1.621, "src": "6f6737aa47f44a25"},
+    "tbq3_window_counters": {"valu_busy": 0.3297, "mfma_busy": 0.0683, "valu_per_wave": 6183, "mfma_per_wave": 320, "salu_per_wave": 2309, "lds_per_wave": 609, "wait_frac": 0.338, "issue_frac": 0.457, "lds_conflict_per_lds_active": 1.726, "src": "6f6737aa47f44a25"},
+    "verify_counters": {"valu_busy": 0.3134, "mfma_busy": 0.1589, "valu_per_wave": 6060, "mfma_per_wave": 768, "salu_per_wave": 2785, "lds_per_wave": 582, "wait_frac": 0.463, "issue_frac": 0.366, "lds_conflict_per_lds_active": 0.703, "src": "6f6737aa47f44a25"},
 }
 
 
