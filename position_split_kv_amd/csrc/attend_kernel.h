@@ -368,14 +368,18 @@ __device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, ui
 #endif
 }
 
-// The same for 4 bytes per lane (the dword lands at lds + 4 * lane).
+// The same for 4 bytes per lane: the dword lands at lds + OFF + 4 * lane.
+// The constant OFF is added to M0 inside the asm, so that the compiler does
+// not keep one precomputed LDS address per load of a tile in scalar
+// registers across the tile loop.
+template <uint32_t OFF>
 __device__ __forceinline__ void lds_dma4(const void *g, uint32_t lds)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+    asm volatile("s_mov_b32 %0, m0\n\ts_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved)
-                 : "v"(g), "s"(lds)
+                 : "v"(g), "s"(lds), "i"(OFF)
                  : "memory");
 #else
     (void)g;
@@ -391,6 +395,24 @@ __device__ __forceinline__ void lds_dma4(const void *g, uint32_t lds)
 // (The lane index passes through an empty asm so that the per-slot row and
 // column are recomputed here, by an add-and-carry recurrence, instead of being
 // hoisted out of the tile loop into registers.)
+template <int RBD, int LS, int I, int I1>
+__device__ __forceinline__ void dma_rows4_from(const uint8_t *src, int pos_stride, int nkk, uint32_t lds_base, int j,
+                                               int c)
+{
+    if constexpr (I < I1) {
+        constexpr int DJ = 64 / LS, DC = 64 % LS;  // slot advance of 64 per load
+        const int cc = c < RBD ? c : RBD - 1;
+        const int jc = j < nkk ? j : nkk - 1;
+        lds_dma4<256u * I>(src + (uint32_t)(jc * pos_stride + 4 * cc), lds_base);
+        j += DJ;
+        c += DC;
+        if (c >= LS) {
+            c -= LS;
+            ++j;
+        }
+        dma_rows4_from<RBD, LS, I + 1, I1>(src, pos_stride, nkk, lds_base, j, c);
+    }
+}
 template <int RBD, int LS, int I0 = 0, int I1 = LS>
 __device__ __forceinline__ void dma_rows4(const uint8_t *src, int pos_stride, int nkk, uint32_t lds_base, int lane)
 {
@@ -398,40 +420,10 @@ __device__ __forceinline__ void dma_rows4(const uint8_t *src, int pos_stride, in
     static_assert(0 <= I0 && I0 <= I1 && I1 <= LS, "load range");
     asm volatile("" : "+v"(lane));
     const int s0 = I0 * 64 + lane;
-    int j = s0 / LS, c = s0 - (s0 / LS) * LS;  // slot of load I0
-    constexpr int DJ = 64 / LS, DC = 64 % LS;  // slot advance of 64 per load
-#pragma unroll
-    for (int i = I0; i < I1; ++i) {
-        const int cc = c < RBD ? c : RBD - 1;
-        const int jc = j < nkk ? j : nkk - 1;
-        lds_dma4(src + (uint32_t)(jc * pos_stride + 4 * cc), lds_base + 256u * i);
-        j += DJ;
-        c += DC;
-        if (c >= LS) {
-            c -= LS;
-            ++j;
-        }
-    }
+    dma_rows4_from<RBD, LS, I0, I1>(src, pos_stride, nkk, lds_base, s0 / LS, s0 - (s0 / LS) * LS);  // slot of load I0
 }
 
-// The same copy with a uniform base and a per-lane 32-bit offset
-// (global address = sbase + voff).
-__device__ __forceinline__ void lds_dma4_s(const void *sbase, uint32_t voff, uint32_t lds)
-{
-#if defined(__HIP_DEVICE_COMPILE__)
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "v"(voff), "s"(sbase), "s"(lds)
-                 : "memory");
-#else
-    (void)sbase;
-    (void)voff;
-    (void)lds;
-#endif
-}
-
-// Lane plan of dma_rows4_full for rows of LS dwords: slot s = i*64 + lane of
+// Slot plan of a whole tile for rows of LS dwords: slot s = i*64 + lane of
 // load i sits at byte (s / LS) * P + 4 * (s % LS) of the tile.  From load i to
 // i+1 that offset grows by DJ*P + 4*DC (uniform) plus P - 4*LS when the slot
 // wraps past a row end; bit i of wrap holds that wrap for the lane, so that
@@ -495,46 +487,250 @@ __device__ __forceinline__ uint64_t dma_wraps(int lane)
     }
 }
 
-// dma_rows4 for a whole tile (kTile rows) that is followed by at least one
-// more position of the segment, with P >= 4*LS: no clamps; a row's padding
-// slots read the dwords after the row (inside the next row or position,
-// never used).  Per load: one bit test and one 24-bit multiply-add.  [I0, I1)
-// selects a range of the LS loads, as for dma_rows4.
-template <int LS, int I0 = 0, int I1 = LS>
-__device__ __forceinline__ void dma_rows4_full(const uint8_t *src, int P, uint64_t wrap, uint32_t lds_base, int lane)
-{
-    static_assert(LS <= 64, "one row per load at least");
-    static_assert(0 <= I0 && I0 <= I1 && I1 <= LS, "load range");
-    constexpr int DJ = 64 / LS, DC = 64 % LS;
-    const int db = DJ * P + 4 * DC;
-    const int xd = P - 4 * LS;  // >= 0, < 2^23
-    uint32_t wlo = (uint32_t)wrap, whi = (uint32_t)(wrap >> 32);
-    // (opaque to the compiler, so that the per-load offsets are recomputed
-    // here rather than hoisted out of the tile loop into registers)
-    asm volatile("" : "+v"(wlo), "+v"(whi), "+v"(lane));
-    // wraps before load I0: the low I0 bits of the plan
-    uint32_t wr0 = 0;
-    if constexpr (I0 > 0) {
-        constexpr uint64_t mask = (1ull << I0) - 1ull;
-        wr0 = (uint32_t)__builtin_popcountll(((uint64_t)whi << 32 | wlo) & mask);
+// Whole-row direct global -> LDS copy of a full tile (kTile rows of RBD
+// dwords, position stride P bytes) into LDS rows of LS >= RBD dwords.  One
+// load carries R = 64 / LS whole rows: lane l holds dword l % LS of the
+// load's row l / LS, and the lanes past a row's RBD dwords or past R rows are
+// switched off (EXEC), so nothing outside the tile's rows is read and the
+// padding slots are not written.  A lane's offset inside its load is the same
+// for every load, (l / LS) * P + 4 * (l % LS); load n starts at row R * n in
+// memory and at LDS dword R * n * LS.  The loads go out in groups under one
+// M0 / EXEC setting as buffer loads: the instruction's immediate offset
+// advances the LDS address and the memory address together by 4 * R * LS per
+// load, and the scalar offset, stepped by R * (P - 4 * LS) with one scalar
+// add per load, makes up the memory side's difference.  No per-lane
+// arithmetic per load.
+template <int RBD, int LS>
+struct RowDma {
+    static_assert(RBD <= LS && LS <= 64, "one row per load at least");
+    static constexpr int R = 64 / LS;                    // rows per load
+    static constexpr int NL = (kTile + R - 1) / R;       // loads per tile
+    static constexpr int STEP = 4 * R * LS;              // bytes per load (LDS side)
+    static constexpr int LAST_ROWS = kTile - R * (NL - 1);  // rows of the last load
+    static constexpr int GMAX = 4095 / STEP + 1 < 16 ? 4095 / STEP + 1 : 16;  // immediate offsets <= 4095
+    static constexpr uint64_t lanes(int rows)
+    {
+        uint64_t m = 0;
+        for (int l = 0; l < rows * LS; ++l)
+            if (l % LS < RBD) m |= 1ull << l;
+        return m;
     }
-    uint32_t voff = __umul24((uint32_t)(lane / LS) + wr0, (uint32_t)xd) + 4u * (uint32_t)lane;
-#pragma unroll
-    for (int i = I0; i < I1; ++i) {
-        lds_dma4_s(src + (int64_t)i * db, voff, lds_base + 256u * i);
-        if (i + 1 < LS) {
-            const uint32_t bit = ((i < 32 ? wlo >> i : whi >> (i - 32)) & 1u);
-            voff += __umul24(bit, (uint32_t)xd);
+    static constexpr uint64_t MASK = lanes(R), MASK_LAST = lanes(LAST_ROWS);
+};
+
+// One group of G loads (G = 1, 2, 4, 8 or 16) of the whole-row copy: M0 and
+// EXEC are set, the loads issued and both restored inside one asm statement,
+// so that no other instruction runs under the reduced EXEC.
+#define RKV_ROW_LD(j) "s_add_u32 %[so], %[so], %[st]\n\tbuffer_load_dword %[v], %[rs], %[so] offen offset:%[o" #j "] lds\n\t"
+#define RKV_ROW_LD2 RKV_ROW_LD(1)
+#define RKV_ROW_LD4 RKV_ROW_LD2 RKV_ROW_LD(2) RKV_ROW_LD(3)
+#define RKV_ROW_LD8 RKV_ROW_LD4 RKV_ROW_LD(4) RKV_ROW_LD(5) RKV_ROW_LD(6) RKV_ROW_LD(7)
+#define RKV_ROW_LD16 \
+    RKV_ROW_LD8 RKV_ROW_LD(8) RKV_ROW_LD(9) RKV_ROW_LD(10) RKV_ROW_LD(11) RKV_ROW_LD(12) RKV_ROW_LD(13) RKV_ROW_LD(14) RKV_ROW_LD(15)
+#define RKV_ROW_GRP(BODY)                                                                                              \
+    asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[ml]\n\ts_mov_b64 %[se], exec\n\ts_mov_b64 exec, %[mk]\n\t" \
+                 "s_nop 0\n\tbuffer_load_dword %[v], %[rs], %[so] offen lds\n\t" BODY                                  \
+                 "s_mov_b64 exec, %[se]\n\ts_mov_b32 m0, %[sv]"                                                        \
+                 : [sv] "=&s"(saved), [se] "=&s"(sexec), [so] "+&s"(so)                                                \
+                 : [v] "v"(voff), [rs] "s"(rs), [mk] "s"(mask), [ml] "s"(m0v), [st] "s"(st), [o1] "i"(S),              \
+                   [o2] "i"(2 * S), [o3] "i"(3 * S), [o4] "i"(4 * S), [o5] "i"(5 * S), [o6] "i"(6 * S),             \
+                   [o7] "i"(7 * S), [o8] "i"(8 * S), [o9] "i"(9 * S), [o10] "i"(10 * S), [o11] "i"(11 * S),        \
+                   [o12] "i"(12 * S), [o13] "i"(13 * S), [o14] "i"(14 * S), [o15] "i"(15 * S)                      \
+                 : "memory")
+template <int G, int S>
+__device__ __forceinline__ void lds_rows_grp(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t so, uint32_t st,
+                                             uint64_t mask, uint32_t m0v)
+{
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
+    static_assert((G - 1) * S <= 4095, "immediate offset range");
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t saved;
+    uint64_t sexec;
+    if constexpr (G == 1)
+        RKV_ROW_GRP("");
+    else if constexpr (G == 2)
+        RKV_ROW_GRP(RKV_ROW_LD2);
+    else if constexpr (G == 4)
+        RKV_ROW_GRP(RKV_ROW_LD4);
+    else if constexpr (G == 8)
+        RKV_ROW_GRP(RKV_ROW_LD8);
+    else
+        RKV_ROW_GRP(RKV_ROW_LD16);
+#else
+    (void)rs;
+    (void)voff;
+    (void)so;
+    (void)st;
+    (void)mask;
+    (void)m0v;
+#endif
+}
+#undef RKV_ROW_GRP
+#undef RKV_ROW_LD16
+#undef RKV_ROW_LD8
+#undef RKV_ROW_LD4
+#undef RKV_ROW_LD2
+#undef RKV_ROW_LD
+
+__host__ __device__ constexpr int row_grp_size(int n, int gmax)
+{
+    const int m = n < gmax ? n : gmax;
+    return m >= 16 ? 16 : m >= 8 ? 8 : m >= 4 ? 4 : m >= 2 ? 2 : 1;
+}
+
+// Loads [N0, N1) of the whole-row copy of a tile.  rs addresses the tile's
+// first row; voff = RowDma::voff(P, lane); st = R * (P - 4 * LS).
+template <int RBD, int LS, int N0, int N1>
+__device__ __forceinline__ void dma_rows_whole(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int P, uint32_t st,
+                                               uint32_t lds_base)
+{
+    using RD = RowDma<RBD, LS>;
+    static_assert(0 <= N0 && N0 <= N1 && N1 <= RD::NL, "load range");
+    if constexpr (N0 < N1) {
+        // the tile's last load (fewer rows when R does not divide the tile)
+        // goes on its own with its own lane mask
+        constexpr bool LASTG = N1 == RD::NL && RD::MASK_LAST != RD::MASK;
+        constexpr int NE = LASTG ? N1 - 1 : N1;
+        if constexpr (N0 < NE) {
+            constexpr int G = row_grp_size(NE - N0, RD::GMAX);
+            lds_rows_grp<G, RD::STEP>(rs, voff, (uint32_t)(N0 * RD::R) * (uint32_t)P, st, RD::MASK,
+                                      lds_base + (uint32_t)(RD::STEP * N0));
+            dma_rows_whole<RBD, LS, N0 + G, N1>(rs, voff, P, st, lds_base);
+        } else {
+            lds_rows_grp<1, RD::STEP>(rs, voff, (uint32_t)(N0 * RD::R) * (uint32_t)P, st, RD::MASK_LAST,
+                                      lds_base + (uint32_t)(RD::STEP * N0));
         }
     }
 }
+template <int LS>
+__device__ __forceinline__ uint32_t row_dma_voff(int P, int lane)
+{
+    return (uint32_t)(lane / LS) * (uint32_t)P + 4u * (uint32_t)(lane % LS);
+}
 
-// The per-lane byte offsets (from the tile's first row) of loads [I0, I1) of
-// dma_rows4_full for position stride P, computed once so that a kernel with
-// registers to spare issues whole-tile copies with no address arithmetic:
-// off[i - I0] = i*(DJ*P + 4*DC) + 4*lane + (lane/LS + wraps before i)*(P - 4*LS).
+// The slot plan of a whole tile (kTile rows followed by at least one more
+// position of the segment, P >= 4 * LS: a row's padding slots read the dwords
+// after the row, inside the next row or position, never used), issued as
+// buffer loads in groups under one M0 setting, with no clamps.
+// Load i of the plan reads at i * db + voff_i (db = DJ * P + 4 * DC,
+// voff_i the lane's offset, which grows by xd = P - 4 * LS after each load
+// whose slot wraps past a row end) and lands at LDS lds_base + 256 * i.  In a
+// group starting at load i0 the immediate offset 256 * (i - i0) advances both
+// addresses; the scalar offset starts at i0 * db and steps by db - 256 =
+// DJ * xd per load, and the lane's wrap is added in the asm between loads
+// (bit i of the plan, one bit extract and one 24-bit multiply-add).  All 64
+// lanes load, so EXEC is untouched.
+#define RKV_WRP_LD(j, jb)                                                                                     \
+    "v_bfe_u32 %[t], %[wg], " #jb ", 1\n\tv_mad_u32_u24 %[vo], %[t], %[xd], %[vo]\n\ts_add_u32 %[so], %[so], %[st]\n\t" \
+    "buffer_load_dword %[vo], %[rs], %[so] offen offset:%[o" #j "] lds\n\t"
+#define RKV_WRP_LD2 RKV_WRP_LD(1, 0)
+#define RKV_WRP_LD4 RKV_WRP_LD2 RKV_WRP_LD(2, 1) RKV_WRP_LD(3, 2)
+#define RKV_WRP_LD8 RKV_WRP_LD4 RKV_WRP_LD(4, 3) RKV_WRP_LD(5, 4) RKV_WRP_LD(6, 5) RKV_WRP_LD(7, 6)
+#define RKV_WRP_LD16                                                                                                 \
+    RKV_WRP_LD8 RKV_WRP_LD(8, 7) RKV_WRP_LD(9, 8) RKV_WRP_LD(10, 9) RKV_WRP_LD(11, 10) RKV_WRP_LD(12, 11) RKV_WRP_LD(13, 12) \
+        RKV_WRP_LD(14, 13) RKV_WRP_LD(15, 14)
+#define RKV_WRP_GRP(BODY)                                                                                          \
+    asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[ml]\n\ts_nop 0\n\t"                                        \
+                 "buffer_load_dword %[vo], %[rs], %[so] offen lds\n\t" BODY "s_mov_b32 m0, %[sv]"                   \
+                 : [sv] "=&s"(saved), [so] "+&s"(so), [vo] "+&v"(voff), [t] "=&v"(tmp)                              \
+                 : [wg] "v"(wg), [xd] "s"(xd), [rs] "s"(rs), [ml] "s"(m0v), [st] "s"(st), [o1] "i"(256),            \
+                   [o2] "i"(512), [o3] "i"(768), [o4] "i"(1024), [o5] "i"(1280), [o6] "i"(1536), [o7] "i"(1792),    \
+                   [o8] "i"(2048), [o9] "i"(2304), [o10] "i"(2560), [o11] "i"(2816), [o12] "i"(3072),              \
+                   [o13] "i"(3328), [o14] "i"(3584), [o15] "i"(3840)                                               \
+                 : "memory")
+template <int G>
+__device__ __forceinline__ void lds_wrap_grp(__amdgpu_buffer_rsrc_t rs, uint32_t &voff, uint32_t wg, uint32_t xd,
+                                             uint32_t so, uint32_t st, uint32_t m0v)
+{
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t saved, tmp;
+    if constexpr (G == 1)
+        RKV_WRP_GRP("");
+    else if constexpr (G == 2)
+        RKV_WRP_GRP(RKV_WRP_LD2);
+    else if constexpr (G == 4)
+        RKV_WRP_GRP(RKV_WRP_LD4);
+    else if constexpr (G == 8)
+        RKV_WRP_GRP(RKV_WRP_LD8);
+    else
+        RKV_WRP_GRP(RKV_WRP_LD16);
+    (void)tmp;
+#else
+    (void)rs;
+    (void)voff;
+    (void)wg;
+    (void)xd;
+    (void)so;
+    (void)st;
+    (void)m0v;
+#endif
+}
+#undef RKV_WRP_GRP
+#undef RKV_WRP_LD16
+#undef RKV_WRP_LD8
+#undef RKV_WRP_LD4
+#undef RKV_WRP_LD2
+#undef RKV_WRP_LD
+
+// The same loads from per-lane offsets planned once (dma_plan_grp below):
+// load j of a group reads at off[j] + 256 * j and lands at LDS m0 + 256 * j,
+// with no arithmetic between the loads.
+#define RKV_PLN_LD(j) "buffer_load_dword %[v" #j "], %[rs], %[so] offen offset:%[o" #j "] lds\n\t"
+#define RKV_PLN_LD2 RKV_PLN_LD(1)
+#define RKV_PLN_LD4 RKV_PLN_LD2 RKV_PLN_LD(2) RKV_PLN_LD(3)
+#define RKV_PLN_LD8 RKV_PLN_LD4 RKV_PLN_LD(4) RKV_PLN_LD(5) RKV_PLN_LD(6) RKV_PLN_LD(7)
+#define RKV_PLN_LD16 \
+    RKV_PLN_LD8 RKV_PLN_LD(8) RKV_PLN_LD(9) RKV_PLN_LD(10) RKV_PLN_LD(11) RKV_PLN_LD(12) RKV_PLN_LD(13) RKV_PLN_LD(14) RKV_PLN_LD(15)
+#define RKV_PLN_GRP(BODY)                                                                                           \
+    asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[ml]\n\ts_nop 0\n\t"                                         \
+                 "buffer_load_dword %[v0], %[rs], %[so] offen lds\n\t" BODY "s_mov_b32 m0, %[sv]"                    \
+                 : [sv] "=&s"(saved)                                                                                 \
+                 : [v0] "v"(off[0]), [v1] "v"(off[G > 1 ? 1 : 0]), [v2] "v"(off[G > 2 ? 2 : 0]),                   \
+                   [v3] "v"(off[G > 3 ? 3 : 0]), [v4] "v"(off[G > 4 ? 4 : 0]), [v5] "v"(off[G > 5 ? 5 : 0]),       \
+                   [v6] "v"(off[G > 6 ? 6 : 0]), [v7] "v"(off[G > 7 ? 7 : 0]), [v8] "v"(off[G > 8 ? 8 : 0]),       \
+                   [v9] "v"(off[G > 9 ? 9 : 0]), [v10] "v"(off[G > 10 ? 10 : 0]), [v11] "v"(off[G > 11 ? 11 : 0]), \
+                   [v12] "v"(off[G > 12 ? 12 : 0]), [v13] "v"(off[G > 13 ? 13 : 0]),                                \
+                   [v14] "v"(off[G > 14 ? 14 : 0]), [v15] "v"(off[G > 15 ? 15 : 0]), [so] "s"(0u), [rs] "s"(rs),    \
+                   [ml] "s"(m0v), [o1] "i"(256), [o2] "i"(512), [o3] "i"(768), [o4] "i"(1024), [o5] "i"(1280),      \
+                   [o6] "i"(1536), [o7] "i"(1792), [o8] "i"(2048), [o9] "i"(2304), [o10] "i"(2560),                \
+                   [o11] "i"(2816), [o12] "i"(3072), [o13] "i"(3328), [o14] "i"(3584), [o15] "i"(3840)             \
+                 : "memory")
+template <int G>
+__device__ __forceinline__ void lds_plan_grp(__amdgpu_buffer_rsrc_t rs, const uint32_t *off, uint32_t m0v)
+{
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t saved;
+    if constexpr (G == 1)
+        RKV_PLN_GRP("");
+    else if constexpr (G == 2)
+        RKV_PLN_GRP(RKV_PLN_LD2);
+    else if constexpr (G == 4)
+        RKV_PLN_GRP(RKV_PLN_LD4);
+    else if constexpr (G == 8)
+        RKV_PLN_GRP(RKV_PLN_LD8);
+    else
+        RKV_PLN_GRP(RKV_PLN_LD16);
+#else
+    (void)rs;
+    (void)off;
+    (void)m0v;
+#endif
+}
+#undef RKV_PLN_GRP
+#undef RKV_PLN_LD16
+#undef RKV_PLN_LD8
+#undef RKV_PLN_LD4
+#undef RKV_PLN_LD2
+#undef RKV_PLN_LD
+
+// The per-lane offsets of loads [I0, I1) of the slot plan of a whole tile,
+// computed once for the groups dma_issue_grp issues: off[i - I0] = i * db +
+// 4 * lane + (lane / LS + wraps before i) * xd - 256 * (position of load i in
+// its group).
 template <int LS, int I0, int I1>
-__device__ __forceinline__ void dma_plan_full(int P, uint64_t wrap, int lane, uint32_t *off)
+__device__ __forceinline__ void dma_plan_grp(int P, uint64_t wrap, int lane, uint32_t *off)
 {
     static_assert(0 <= I0 && I0 <= I1 && I1 <= LS, "load range");
     constexpr int DJ = 64 / LS, DC = 64 % LS;
@@ -542,20 +738,44 @@ __device__ __forceinline__ void dma_plan_full(int P, uint64_t wrap, int lane, ui
     uint32_t wr0 = 0;
     if constexpr (I0 > 0) wr0 = (uint32_t)__builtin_popcountll(wrap & ((1ull << I0) - 1ull));
     uint32_t v = ((uint32_t)(lane / LS) + wr0) * xd + 4u * (uint32_t)lane + (uint32_t)I0 * db;
+    int g0 = I0, gl = row_grp_size(I1 - I0, 16);  // current group's first load and size
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
-        off[i - I0] = v;
+        if (i == g0 + gl) {
+            g0 = i;
+            gl = row_grp_size(I1 - i, 16);
+        }
+        off[i - I0] = v - 256u * (uint32_t)(i - g0);
         v += db + (uint32_t)((wrap >> i) & 1ull) * xd;
     }
 }
-
-// Loads [I0, I0 + N) of a whole-tile copy from offsets planned by
-// dma_plan_full: one uniform base, one planned offset per load.
-template <int I0, int N>
-__device__ __forceinline__ void dma_issue_planned(const uint8_t *src, const uint32_t *off, uint32_t lds_base)
+template <int I0, int N, int J = 0>
+__device__ __forceinline__ void dma_issue_grp(__amdgpu_buffer_rsrc_t rs, const uint32_t *off, uint32_t lds_base)
 {
-#pragma unroll
-    for (int j = 0; j < N; ++j) lds_dma4_s(src, off[j], lds_base + 256u * (I0 + j));
+    if constexpr (J < N) {
+        constexpr int G = row_grp_size(N - J, 16);
+        lds_plan_grp<G>(rs, off + J, lds_base + 256u * (I0 + J));
+        dma_issue_grp<I0, N, J + G>(rs, off, lds_base);
+    }
+}
+
+// Loads [I0, I1) of the slot plan of a whole tile; voff is the lane's offset
+// for load I0 (it leaves holding the offset for load I1), rs addresses the
+// tile's first row.  The wrap after the group's last load is added here.
+template <int LS, int I0, int I1>
+__device__ __forceinline__ void dma_rows4_grp(__amdgpu_buffer_rsrc_t rs, uint32_t &voff, uint64_t wrap, int P,
+                                              uint32_t lds_base)
+{
+    static_assert(0 <= I0 && I0 <= I1 && I1 <= LS, "load range");
+    if constexpr (I0 < I1) {
+        constexpr int DJ = 64 / LS, DC = 64 % LS;
+        constexpr int G = row_grp_size(I1 - I0, 16);
+        const uint32_t db = (uint32_t)(DJ * P + 4 * DC), xd = (uint32_t)(P - 4 * LS);
+        const uint32_t wg = (uint32_t)(wrap >> I0);
+        lds_wrap_grp<G>(rs, voff, wg, xd, (uint32_t)I0 * db, (uint32_t)DJ * xd, lds_base + 256u * I0);
+        if constexpr (I0 + G < LS) voff += ((wg >> (G - 1)) & 1u) * xd;  // the wrap after the group's last load
+        dma_rows4_grp<LS, I0 + G, I1>(rs, voff, wrap, P, lds_base);
+    }
 }
 
 // s_waitcnt vmcnt(n) (0 <= n <= 63), other counters untouched.
@@ -1512,16 +1732,31 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     const uint64_t kwrap = BDMA ? dma_wraps<LSK1>(lane) : 0, vwrap = BDMA ? dma_wraps<LSV1>(lane) : 0;
     const bool kfull_ok = sg.k_pos >= 4 * LSK && sg.k_pos < (1 << 23);
     const bool vfull_ok = sg.v_pos >= 4 * LSV && sg.v_pos < (1 << 23);
+    // V rows short enough for several whole rows per load take the whole-row
+    // copy (no per-lane arithmetic per load); the others the slot plan.
+    // Either issues at least LSV loads, the count the waits below assume.
+    constexpr int LSVR = BDMA ? LSV1 : 1;  // (a placeholder shape off the DMA path)
+    constexpr int RBDV = BDMA ? Sh::RBV / 4 : 1;
+    using VRow = RowDma<RBDV, LSVR>;
+    constexpr bool V_ROWS = BDMA && VRow::R >= 2;
+    static_assert(!V_ROWS || VRow::NL >= LSV, "the whole-row V copy issues at least as many loads as the slot plan");
+    // lane offsets of load 0 of the slot plans (no wraps before it)
+    const uint32_t koff0 = BDMA ? (uint32_t)(lane / LSK1) * (uint32_t)(sg.k_pos - 4 * LSK1) + 4u * (uint32_t)lane : 0u;
+    const uint32_t voff0 = !BDMA ? 0u
+                           : V_ROWS ? row_dma_voff<LSV1>((int)sg.v_pos, lane)
+                                    : (uint32_t)(lane / LSV1) * (uint32_t)(sg.v_pos - 4 * LSV1) + 4u * (uint32_t)lane;
     auto dma_kb = [&](int64_t t, int nkk) {
         if constexpr (BDMA) {
             int kps = (int)sg.k_pos;
             asm volatile("" : "+s"(kps));
             waitcnt_lgkm0();  // this wave's earlier LDS reads of the K buffer are done
             const uint32_t base = lds_addr(smem + w * Sh::STAGE_DW);
-            if (kfull_ok && nkk == kTile && t + kTile < sg.n_keys)
-                dma_rows4_full<LSK1>(kg + t * sg.k_pos, kps, kwrap, base, lane);
-            else
+            if (kfull_ok && nkk == kTile && t + kTile < sg.n_keys) {
+                uint32_t vo = koff0;
+                dma_rows4_grp<LSK1, 0, LSK1>(buffer_rsrc(kg + t * sg.k_pos), vo, kwrap, kps, base);
+            } else {
                 dma_rows4<Sh::RBK / 4, LSK>(kg + t * sg.k_pos, kps, nkk, base, lane);
+            }
         }
     };
     auto dma_vb = [&](int64_t t, int nkk, const uint32_t *dst) {
@@ -1530,10 +1765,18 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             asm volatile("" : "+s"(vps2));
             waitcnt_lgkm0();  // this wave's earlier LDS reads of the V buffer are done
             const uint32_t base = lds_addr(dst);
-            if (vfull_ok && nkk == kTile && t + kTile < sg.n_keys)
-                dma_rows4_full<LSV1>(vg + t * sg.v_pos, vps2, vwrap, base, lane);
-            else
+            if (vfull_ok && nkk == kTile && t + kTile < sg.n_keys) {
+                const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(vg + t * sg.v_pos);
+                if constexpr (V_ROWS) {
+                    dma_rows_whole<RBDV, LSVR, 0, VRow::NL>(
+                        rs, voff0, vps2, (uint32_t)VRow::R * (uint32_t)(vps2 - 4 * LSVR), base);
+                } else {
+                    uint32_t vo = voff0;
+                    dma_rows4_grp<LSV1, 0, LSV1>(rs, vo, vwrap, vps2, base);
+                }
+            } else {
                 dma_rows4<Sh::RBV / 4, LSV>(vg + t * sg.v_pos, vps2, nkk, base, lane);
+            }
         }
     };
     // VMEM instructions one load_v_into issues (outstanding loads a wait may leave)
@@ -2042,18 +2285,17 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             // the wave writes its rows straight from the MFMA output layout
             // (lane (g, n) holds dims 8n .. 8n+7 of rows 4g .. 4g+3).  The
             // values are those the LDS merge would produce for one wave.
+            // (output rows from the wave's copy of the row table in LDS, so
+            // that the table does not hold scalar registers through the loop)
             const bool single = p.direct != 0;
             const int64_t pbase = (int64_t)(p.split_off + (int)blockIdx.x) * p.n_rows_total;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * (lane >> 4) + i;
-                int rr = -1;
+                const int rr = row < RT ? sRow[w][row] : -1;
                 float lr = 1.f;
 #pragma unroll
-                for (int r = 0; r < RT; ++r) {
-                    rr = row == r ? tabrow[r] : rr;
-                    lr = row == r ? l[r] : lr;
-                }
+                for (int r = 0; r < RT; ++r) lr = row == r ? l[r] : lr;
                 if (rr < 0) continue;
                 float v[8];
 #pragma unroll
@@ -2063,11 +2305,10 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 *(float4 *)(dst + 8 * (lane & 15) + 4) = make_float4(v[4], v[5], v[6], v[7]);
             }
             if (js == 0 && lane < RT) {
-                int rr = -1;
+                const int rr = sRow[w][lane];
                 float mr = 0.f, lr = 1.f;
 #pragma unroll
                 for (int r = 0; r < RT; ++r) {
-                    rr = lane == r ? tabrow[r] : rr;
                     mr = lane == r ? m[r] : mr;
                     lr = lane == r ? l[r] : lr;
                 }

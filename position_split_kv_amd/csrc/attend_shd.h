@@ -85,13 +85,16 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
     const uint8_t *kg = sg.k + z * sg.k_seq + gr * sg.k_head;
     const uint8_t *vg = sg.v + z * sg.v_seq + gr * sg.v_head;
 
-    int tabrow[RT];
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
+    // output row of the wave's row r (-1 past nr); read again after the tile
+    // loop rather than held in scalar registers through it
+    auto table_row = [&](int r, int nrx) {
         const int ti = g * p.rows_per_g + rg * RT + r;
         const int v = u16_at(p.rowtab, ti < kMaxRowTable ? ti : kMaxRowTable - 1);
-        tabrow[r] = r < nr ? z * p.z_row_step + v : -1;
-    }
+        return r < nrx ? z * p.z_row_step + v : -1;
+    };
+    int tabrow[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) tabrow[r] = table_row(r, nr);
     // causal mask: row r sees the segment's keys with index <= lim[r]
     constexpr int kSeeAll = 1 << 30;
     int limv[4];
@@ -121,38 +124,45 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
             }
     }
 
-    // raw tile DMA: the LSK K loads and LSV V loads of a tile, a quarter per
-    // wave (wave 0: K loads [0, KA), 1: [KA, KB), 2: K [KB, LSK) and V [0, VA),
-    // 3: V [VA, LSV))
+    // raw tile DMA: the tile's K rows by the slot plan (LSK loads) and its V
+    // rows by the whole-row copy (NLV loads, several rows per load), one
+    // sequence of loads shared out in quarters over the four waves: wave w
+    // issues loads [w * NQ, (w + 1) * NQ) of K's then V's
     static_assert(LSK > 0 && LSV > 0, "block K and V rows are staged in LDS");
-    constexpr int NQ = (LSK + LSV + 3) / 4;
-    constexpr int KA = NQ < LSK ? NQ : LSK, KB = 2 * NQ < LSK ? 2 * NQ : LSK;
-    constexpr int VA = 3 * NQ - LSK < 0 ? 0 : 3 * NQ - LSK < LSV ? 3 * NQ - LSK : LSV;
-    const uint64_t kwrap = dma_wraps<LSK>(lane), vwrap = dma_wraps<LSV>(lane);
+    using VRow = RowDma<Sh::RBV / 4, LSV>;
+    static_assert(VRow::R >= 2, "several V rows per load");
+    constexpr int NLV = VRow::NL, NQ = (LSK + NLV + 3) / 4;
+    const uint64_t kwrap = dma_wraps<LSK>(lane);
     const bool kfull_ok = sg.k_pos >= 4 * LSK && sg.k_pos < (1 << 23);
     const bool vfull_ok = sg.v_pos >= 4 * LSV && sg.v_pos < (1 << 23);
-    // this wave's whole-tile load offsets, planned once: K loads first, then V
-    constexpr int NKW[4] = {KA, KB - KA, LSK - KB, 0}, NVW[4] = {0, 0, VA, LSV - VA};
-    constexpr int NW0 = NKW[0] + NVW[0], NW1 = NKW[1] + NVW[1], NW2 = NKW[2] + NVW[2], NW3 = NKW[3] + NVW[3];
-    constexpr int NPL = NW0 > NW1 ? (NW0 > NW2 ? (NW0 > NW3 ? NW0 : NW3) : (NW2 > NW3 ? NW2 : NW3))
-                                  : (NW1 > NW2 ? (NW1 > NW3 ? NW1 : NW3) : (NW2 > NW3 ? NW2 : NW3));
-    uint32_t doff[NPL];
+    // loads [S0, S1) of the sequence for wave W: K's [K0, K1), V's [V0, V1)
+    auto wave_range = [](auto wc) {
+        constexpr int W = decltype(wc)::value;
+        constexpr int S0 = W * NQ, S1 = (W + 1) * NQ < LSK + NLV ? (W + 1) * NQ : LSK + NLV;
+        struct R {
+            int k0, k1, v0, v1;
+        };
+        return R{S0 < LSK ? S0 : LSK, S1 < LSK ? S1 : LSK, S0 > LSK ? S0 - LSK : 0, S1 > LSK ? S1 - LSK : 0};
+    };
+    // this wave's K load offsets, planned once (no per-load arithmetic), and
+    // the V rows' lane offset
+    uint32_t koffs[NQ];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) doff[j] = 0;
-    {
-        const int kp = (int)sg.k_pos, vp = (int)sg.v_pos;
-        if (rgl == 0) {
-            if (kfull_ok) dma_plan_full<LSK, 0, KA>(kp, kwrap, lane, doff);
-        } else if (rgl == 1) {
-            if (kfull_ok) dma_plan_full<LSK, KA, KB>(kp, kwrap, lane, doff);
-        } else if (rgl == 2) {
-            if (kfull_ok) dma_plan_full<LSK, KB, LSK>(kp, kwrap, lane, doff);
-            if (vfull_ok) dma_plan_full<LSV, 0, VA>(vp, vwrap, lane, doff + NKW[2]);
-        } else {
-            if (vfull_ok) dma_plan_full<LSV, VA, LSV>(vp, vwrap, lane, doff);
-        }
-    }
-    static_assert(NW0 + NW1 + NW2 + NW3 == LSK + LSV, "every load of a tile planned once");
+    for (int j = 0; j < NQ; ++j) koffs[j] = 0;
+    auto plan_wave = [&](auto wc) {
+        constexpr auto r = wave_range(wc);
+        if constexpr (r.k0 < r.k1)
+            if (kfull_ok) dma_plan_grp<LSK, r.k0, r.k1>((int)sg.k_pos, kwrap, lane, koffs);
+    };
+    if (rgl == 0)
+        plan_wave(std::integral_constant<int, 0>{});
+    else if (rgl == 1)
+        plan_wave(std::integral_constant<int, 1>{});
+    else if (rgl == 2)
+        plan_wave(std::integral_constant<int, 2>{});
+    else
+        plan_wave(std::integral_constant<int, 3>{});
+    const uint32_t voffr = row_dma_voff<LSV>((int)sg.v_pos, lane);
     auto nk_at = [&](int64_t t) { return (int)(kend - t < kTile ? kend - t : kTile); };
     auto dma_raw = [&](int64_t t) {
         const int nkk = nk_at(t);
@@ -162,31 +172,36 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
         waitcnt_lgkm0();
         const uint8_t *ks = kg + t * sg.k_pos, *vs = vg + t * sg.v_pos;
         const uint32_t kbase = lds_addr(rawK), vbase = lds_addr(rawV);
-        if (rgl == 0) {
-            if (kfull_ok && whole)
-                dma_issue_planned<0, KA>(ks, doff, kbase);
-            else
-                dma_rows4<Sh::RBK / 4, LSK, 0, KA>(ks, kps, nkk, kbase, lane);
-        } else if (rgl == 1) {
-            if (kfull_ok && whole)
-                dma_issue_planned<KA, KB - KA>(ks, doff, kbase);
-            else
-                dma_rows4<Sh::RBK / 4, LSK, KA, KB>(ks, kps, nkk, kbase, lane);
-        } else if (rgl == 2) {
-            if (kfull_ok && whole)
-                dma_issue_planned<KB, LSK - KB>(ks, doff, kbase);
-            else
-                dma_rows4<Sh::RBK / 4, LSK, KB, LSK>(ks, kps, nkk, kbase, lane);
-            if (vfull_ok && whole)
-                dma_issue_planned<0, VA>(vs, doff + NKW[2], vbase);
-            else
-                dma_rows4<Sh::RBV / 4, LSV, 0, VA>(vs, vps, nkk, vbase, lane);
-        } else {
-            if (vfull_ok && whole)
-                dma_issue_planned<VA, LSV - VA>(vs, doff, vbase);
-            else
-                dma_rows4<Sh::RBV / 4, LSV, VA, LSV>(vs, vps, nkk, vbase, lane);
-        }
+        auto wave_loads = [&](auto wc) {
+            constexpr auto r = wave_range(wc);
+            constexpr int K0 = r.k0, K1 = r.k1, V0 = r.v0, V1 = r.v1;
+            if constexpr (K0 < K1) {
+                if (kfull_ok && whole) {
+                    dma_issue_grp<K0, K1 - K0>(buffer_rsrc(ks), koffs, kbase);
+                } else {
+                    dma_rows4<Sh::RBK / 4, LSK, K0, K1>(ks, kps, nkk, kbase, lane);
+                }
+            }
+            if constexpr (V0 < V1) {
+                if (vfull_ok && whole) {
+                    dma_rows_whole<Sh::RBV / 4, LSV, V0, V1>(buffer_rsrc(vs), voffr, vps,
+                                                             (uint32_t)VRow::R * (uint32_t)(vps - 4 * LSV), vbase);
+                } else {
+                    // the clamped copy in the slot plan's units: the V loads
+                    // of this wave's share, scaled to LSV
+                    constexpr int C0 = V0 * LSV / NLV, C1 = V1 == NLV ? LSV : V1 * LSV / NLV;
+                    dma_rows4<Sh::RBV / 4, LSV, C0, C1>(vs, vps, nkk, vbase, lane);
+                }
+            }
+        };
+        if (rgl == 0)
+            wave_loads(std::integral_constant<int, 0>{});
+        else if (rgl == 1)
+            wave_loads(std::integral_constant<int, 1>{});
+        else if (rgl == 2)
+            wave_loads(std::integral_constant<int, 2>{});
+        else
+            wave_loads(std::integral_constant<int, 3>{});
     };
 
     float qraw[D / 32][8];
@@ -414,6 +429,11 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
     }
     const bool single = p.direct != 0;
     const int64_t pbase = (int64_t)(p.split_off + (int)blockIdx.x) * p.n_rows_total;
+    int orow[RT];
+    int nr_e = nr;
+    asm volatile("" : "+s"(nr_e));  // (not the loop-spanning copies of r < nr)
+#pragma unroll
+    for (int r = 0; r < RT; ++r) orow[r] = table_row(r, nr_e);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 4 * (lane >> 4) + i;
@@ -421,7 +441,7 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
         float lr = 1.f;
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
-            rr = row == r ? tabrow[r] : rr;
+            rr = row == r ? orow[r] : rr;
             lr = row == r ? l[r] : lr;
         }
         if (rr < 0) continue;
@@ -437,7 +457,7 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
         float mr = 0.f, lr = 1.f;
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
-            rr = lane == r ? tabrow[r] : rr;
+            rr = lane == r ? orow[r] : rr;
             mr = lane == r ? m[r] : mr;
             lr = lane == r ? l[r] : lr;
         }
