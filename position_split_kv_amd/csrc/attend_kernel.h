@@ -1178,36 +1178,119 @@ __device__ __forceinline__ uint32_t f16pair_of_bytes(uint32_t x, uint32_t sel, _
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// Signed byte B of x as an exact binary16 in the low half of a fresh dword
+// (upper half zero), and signed byte B of y into the high half of r (low
+// half kept): one sub-dword-addressed conversion each, no shifts or bias.
+template <int B>
+__device__ __forceinline__ uint32_t i8_f16_lo(uint32_t x)
+{
+    uint32_t r;
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (B == 0)
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(x));
+    else if constexpr (B == 1)
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(x));
+    else if constexpr (B == 2)
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(x));
+    else
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(x));
+#else
+    r = x;
+#endif
+    return r;
+}
+template <int B>
+__device__ __forceinline__ uint32_t i8_f16_hi(uint32_t r, uint32_t y)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (B == 0)
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0" : "+v"(r) : "v"(y));
+    else if constexpr (B == 1)
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1" : "+v"(r) : "v"(y));
+    else if constexpr (B == 2)
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_2" : "+v"(r) : "v"(y));
+    else
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3" : "+v"(r) : "v"(y));
+#else
+    (void)y;
+#endif
+    return r;
+}
+// (signed byte BA of x, signed byte BB of y) as a binary16 pair
+template <int BA, int BB>
+__device__ __forceinline__ uint32_t i8_f16_pair(uint32_t x, uint32_t y)
+{
+    return i8_f16_hi<BB>(i8_f16_lo<BA>(x), y);
+}
+
 // 8 codes of a q8_0 / q4_0 row in LDS (row = dword pointer) for dims
 // 32*kk + 8*g .. +7, as the f16 B operand; and the block scale of block kk.
-template <int KT>
+// (q8_0 with SDWA: the codes start 2 bytes into a dword when kk is even and
+// on a dword boundary when it is odd, so each pair is converted straight from
+// the dwords that hold it -- for a kk known at compile time after unrolling;
+// otherwise the codes are aligned by a funnel shift, biased into the
+// exponent-0x64 binade and the bias subtracted.)
+template <int KT, bool SDWA = true>
 __device__ __forceinline__ rkv_half8 block_codes_f16(const uint32_t *row, int kk, int g, float &dsc)
 {
     const int os = (KT == kQ8 ? 34 : 18) * kk;
     const uint32_t s0 = row[os >> 2];
     dsc = h2f((os & 2) ? (s0 >> 16) : s0);
     const int o = KT == kQ8 ? os + 2 + 8 * g : os + 2 + 8 * (g & 1);
-    const uint32_t sh = o & 3;
-    const uint32_t A = row[o >> 2], B = row[(o >> 2) + 1], C = row[(o >> 2) + 2];
-    uint32_t w0 = funnel(A, B, sh), w1 = funnel(B, C, sh);
     uint32_t out[4];
-    if constexpr (KT == kQ8) {
-        w0 ^= 0x80808080u;
-        w1 ^= 0x80808080u;
-        out[0] = f16pair_of_bytes(w0, 0x04010400u, (_Float16)1152.f);
-        out[1] = f16pair_of_bytes(w0, 0x04030402u, (_Float16)1152.f);
-        out[2] = f16pair_of_bytes(w1, 0x04010400u, (_Float16)1152.f);
-        out[3] = f16pair_of_bytes(w1, 0x04030402u, (_Float16)1152.f);
+    if constexpr (KT == kQ8 && SDWA) {
+        const uint32_t *w = row + (o >> 2);
+        if ((kk & 1) == 0) {  // codes at bytes 2, 3 of w[0], then w[1], then bytes 0, 1 of w[2]
+            const uint32_t A = w[0], B = w[1], C = w[2];
+            out[0] = i8_f16_pair<2, 3>(A, A);
+            out[1] = i8_f16_pair<0, 1>(B, B);
+            out[2] = i8_f16_pair<2, 3>(B, B);
+            out[3] = i8_f16_pair<0, 1>(C, C);
+        } else {  // codes at w[0], w[1]
+            const uint32_t A = w[0], B = w[1];
+            out[0] = i8_f16_pair<0, 1>(A, A);
+            out[1] = i8_f16_pair<2, 3>(A, A);
+            out[2] = i8_f16_pair<0, 1>(B, B);
+            out[3] = i8_f16_pair<2, 3>(B, B);
+        }
     } else {
-        const int shn = (g >> 1) * 4;  // dims 0..15 of the block: low nibbles; 16..31: high
-        w0 = (w0 >> shn) & 0x0f0f0f0fu;
-        w1 = (w1 >> shn) & 0x0f0f0f0fu;
-        out[0] = f16pair_of_bytes(w0, 0x04010400u, (_Float16)1032.f);
-        out[1] = f16pair_of_bytes(w0, 0x04030402u, (_Float16)1032.f);
-        out[2] = f16pair_of_bytes(w1, 0x04010400u, (_Float16)1032.f);
-        out[3] = f16pair_of_bytes(w1, 0x04030402u, (_Float16)1032.f);
+        const uint32_t sh = o & 3;
+        const uint32_t A = row[o >> 2], B = row[(o >> 2) + 1], C = row[(o >> 2) + 2];
+        uint32_t w0 = funnel(A, B, sh), w1 = funnel(B, C, sh);
+        if constexpr (KT == kQ8) {
+            w0 ^= 0x80808080u;
+            w1 ^= 0x80808080u;
+            out[0] = f16pair_of_bytes(w0, 0x04010400u, (_Float16)1152.f);
+            out[1] = f16pair_of_bytes(w0, 0x04030402u, (_Float16)1152.f);
+            out[2] = f16pair_of_bytes(w1, 0x04010400u, (_Float16)1152.f);
+            out[3] = f16pair_of_bytes(w1, 0x04030402u, (_Float16)1152.f);
+        } else {
+            const int shn = (g >> 1) * 4;  // dims 0..15 of the block: low nibbles; 16..31: high
+            w0 = (w0 >> shn) & 0x0f0f0f0fu;
+            w1 = (w1 >> shn) & 0x0f0f0f0fu;
+            out[0] = f16pair_of_bytes(w0, 0x04010400u, (_Float16)1032.f);
+            out[1] = f16pair_of_bytes(w0, 0x04030402u, (_Float16)1032.f);
+            out[2] = f16pair_of_bytes(w1, 0x04010400u, (_Float16)1032.f);
+            out[3] = f16pair_of_bytes(w1, 0x04030402u, (_Float16)1032.f);
+        }
     }
     return __builtin_bit_cast(rkv_half8, out);
+}
+
+// The 8 code bytes of dims 8*dg .. 8*dg+7 of a q8_0 row in LDS as two
+// dwords (dim 8*dg + j in byte j % 4 of w[j / 4]), and the block's binary16
+// scale bits.
+__device__ __forceinline__ void v_group_bytes_q8(const uint32_t *row, int dg, uint32_t *w, uint32_t &dbits)
+{
+    const int bb = dg >> 2, h = dg & 3;
+    const int os = 34 * bb;
+    const uint32_t s0 = row[os >> 2];
+    dbits = (os & 2) ? (s0 >> 16) : (s0 & 0xffffu);
+    const int o = os + 2 + 8 * h;
+    const uint32_t sh = o & 3;
+    const uint32_t A = row[o >> 2], B = row[(o >> 2) + 1], C = row[(o >> 2) + 2];
+    w[0] = funnel(A, B, sh);
+    w[1] = funnel(B, C, sh);
 }
 
 // The 8 codes of dims 8*dg .. 8*dg+7 of a q8_0 / q4_0 row in LDS as four
@@ -1831,6 +1914,32 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                         hw[2 * p2 + 1][e2] = __builtin_amdgcn_perm(tb.x, ta.x, 0x07060302u);
                         lw[2 * p2][e2] = __builtin_amdgcn_perm(tb.y, ta.y, 0x05040100u);
                         lw[2 * p2 + 1][e2] = __builtin_amdgcn_perm(tb.y, ta.y, 0x07060302u);
+                    }
+                }
+            } else if constexpr (VT == kQ8) {
+                // (key a, key b) pairs of each dim converted straight from
+                // the two keys' code bytes
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    uint32_t wa[2], wb[2], da, db;
+                    v_group_bytes_q8(sV + (4 * (8 * kb + 2 * e2) + gq) * LSV, qi, wa, da);
+                    v_group_bytes_q8(sV + (4 * (8 * kb + 2 * e2 + 1) + gq) * LSV, qi, wb, db);
+                    const rkv_half2 d2 = __builtin_bit_cast(rkv_half2, da | (db << 16));
+                    rkv_half2 x[8];
+                    x[0] = __builtin_bit_cast(rkv_half2, i8_f16_pair<0, 0>(wa[0], wb[0]));
+                    x[1] = __builtin_bit_cast(rkv_half2, i8_f16_pair<1, 1>(wa[0], wb[0]));
+                    x[2] = __builtin_bit_cast(rkv_half2, i8_f16_pair<2, 2>(wa[0], wb[0]));
+                    x[3] = __builtin_bit_cast(rkv_half2, i8_f16_pair<3, 3>(wa[0], wb[0]));
+                    x[4] = __builtin_bit_cast(rkv_half2, i8_f16_pair<0, 0>(wa[1], wb[1]));
+                    x[5] = __builtin_bit_cast(rkv_half2, i8_f16_pair<1, 1>(wa[1], wb[1]));
+                    x[6] = __builtin_bit_cast(rkv_half2, i8_f16_pair<2, 2>(wa[1], wb[1]));
+                    x[7] = __builtin_bit_cast(rkv_half2, i8_f16_pair<3, 3>(wa[1], wb[1]));
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        const rkv_half2 h = d2 * x[c];
+                        const rkv_half2 l = __builtin_elementwise_fma(d2, x[c], -h);
+                        hw[c][e2] = __builtin_bit_cast(uint32_t, h);
+                        lw[c][e2] = __builtin_bit_cast(uint32_t, l);
                     }
                 }
             } else {

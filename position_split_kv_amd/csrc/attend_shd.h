@@ -271,7 +271,7 @@ rkv_split_shd_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             float dsc;
-            const rkv_half8 b = block_codes_f16<KT>(rawK + (16 * kb + qi) * LSK, rgl, gq, dsc);
+            const rkv_half8 b = block_codes_f16<KT, false>(rawK + (16 * kb + qi) * LSK, rgl, gq, dsc);  // (kk = the wave's row group)
             *(rkv_half8 *)(bK + ((kb * 4 + rgl) * 64 + lane) * 4) = b;
             if (lane < 16) dK[(kb * 4 + rgl) * 16 + lane] = dsc;
         }
