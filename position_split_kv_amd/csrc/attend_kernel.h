@@ -2204,19 +2204,38 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) vs[kb] = h2f(sV[(16 * kb + (lane & 15)) * LSV]) * 0.088388347648318440550f;
             }
+            // (the probabilities first, then the stores of the lanes that
+            // hold real rows under as few lane tests as RT allows: one when
+            // every lane group holds whole rows)
+            float pvs[4][4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = 4 * (lane >> 4) + i;
                 float ps = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    const float pv = __builtin_amdgcn_exp2f(sv[kb][i] - mex[i]);
-                    ps += pv;
-                    const int key = 16 * kb + (lane & 15);
-                    const int at = MFMA_O ? (key & 3) * 16 + (key >> 2) : key;
-                    if (row < RT) sPw[row * kTile + at] = VT == kT3 ? pv * vs[kb] : pv;
+                    pvs[kb][i] = __builtin_amdgcn_exp2f(sv[kb][i] - mex[i]);
+                    ps += pvs[kb][i];
                 }
                 lrow[i] += ps;
+            }
+            auto store_row = [&](int i) {
+                const int row = 4 * (lane >> 4) + i;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const int key = 16 * kb + (lane & 15);
+                    const int at = MFMA_O ? (key & 3) * 16 + (key >> 2) : key;
+                    sPw[row * kTile + at] = VT == kT3 ? pvs[kb][i] * vs[kb] : pvs[kb][i];
+                }
+            };
+            if constexpr (RT % 4 == 0) {
+                if (4 * (lane >> 4) < RT) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) store_row(i);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * (lane >> 4) + i < RT) store_row(i);
             }
         } else {
         // ---- scores, one key per lane
