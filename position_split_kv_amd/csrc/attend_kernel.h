@@ -314,25 +314,96 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 // others (a verify step of 40 rows per head: 106 -> 94 us).  (The 4-byte
 // loads below touch each line from several loads and keep the default: with
 // nt they were up to 15 % slower.)
-template <bool NT>
+template <bool NT, uint32_t OFF = 0>
 __device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     uint32_t saved;
     if constexpr (NT)
-        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+        asm volatile("s_mov_b32 %0, m0\n\ts_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
                      : "=&s"(saved)
-                     : "v"(g), "s"(lds)
+                     : "v"(g), "s"(lds), "i"(OFF)
                      : "memory");
     else
-        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+        asm volatile("s_mov_b32 %0, m0\n\ts_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
                      : "=&s"(saved)
-                     : "v"(g), "s"(lds)
+                     : "v"(g), "s"(lds), "i"(OFF)
                      : "memory");
 #else
     (void)g;
     (void)lds;
 #endif
+}
+
+// f(std::integral_constant<int, i>) for i = I .. N-1 (an unrolled loop whose
+// index is a compile-time constant)
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Groups of G (1, 2 or 4) sixteen-byte direct-to-LDS buffer loads under one
+// M0 setting: load j of a group reads at voff[j] + so_j + 1024 j and lands at
+// LDS m0 + 1024 j + 16 lane (the immediate offset advances both addresses),
+// with so_0 = so and so_(j+1) = so_j + st (one scalar add per load).  The
+// per-load LDS addresses are immediates inside the asm, so none of them is
+// held in a scalar register across a loop.
+#define RKV_X4_GRP(NTS, BODY)                                                                                        \
+    asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[ml]\n\ts_nop 0\n\t"                                        \
+                 "buffer_load_dwordx4 %[v0], %[rs], %[so] offen" NTS " lds\n\t" BODY "s_mov_b32 m0, %[sv]"         \
+                 : [sv] "=&s"(saved), [so] "+&s"(so)                                                                 \
+                 : [v0] "v"(voff[0]), [v1] "v"(voff[G > 1 ? 1 : 0]), [v2] "v"(voff[G > 2 ? 2 : 0]),                \
+                   [v3] "v"(voff[G > 3 ? 3 : 0]), [rs] "s"(rs), [ml] "s"(m0v), [st] "s"(st), [o1] "i"(1024),       \
+                   [o2] "i"(2048), [o3] "i"(3072)                                                                    \
+                 : "memory")
+#define RKV_X4_LD(j, NTS) "s_add_u32 %[so], %[so], %[st]\n\tbuffer_load_dwordx4 %[v" #j "], %[rs], %[so] offen offset:%[o" #j "]" NTS " lds\n\t"
+template <int G, bool NT>
+__device__ __forceinline__ void lds_dma16_grp(__amdgpu_buffer_rsrc_t rs, const uint32_t *voff, uint32_t so, uint32_t st,
+                                              uint32_t m0v)
+{
+    static_assert(G == 1 || G == 2 || G == 4, "group size");
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t saved;
+    if constexpr (NT) {
+        if constexpr (G == 1)
+            RKV_X4_GRP(" nt", "");
+        else if constexpr (G == 2)
+            RKV_X4_GRP(" nt", RKV_X4_LD(1, " nt"));
+        else
+            RKV_X4_GRP(" nt", RKV_X4_LD(1, " nt") RKV_X4_LD(2, " nt") RKV_X4_LD(3, " nt"));
+    } else {
+        if constexpr (G == 1)
+            RKV_X4_GRP("", "");
+        else if constexpr (G == 2)
+            RKV_X4_GRP("", RKV_X4_LD(1, ""));
+        else
+            RKV_X4_GRP("", RKV_X4_LD(1, "") RKV_X4_LD(2, "") RKV_X4_LD(3, ""));
+    }
+#else
+    (void)rs;
+    (void)voff;
+    (void)so;
+    (void)st;
+    (void)m0v;
+#endif
+}
+#undef RKV_X4_LD
+#undef RKV_X4_GRP
+// Loads [J, N) of a tile copy by lds_dma16_grp: load i reads at
+// i * rstep + voff[i] and lands at LDS lds_base + 1024 i.
+template <bool NT, int N, int J = 0>
+__device__ __forceinline__ void dma16_groups(__amdgpu_buffer_rsrc_t rs, const uint32_t *voff, uint32_t rstep,
+                                             uint32_t lds_base)
+{
+    if constexpr (J < N) {
+        constexpr int G = N - J >= 4 ? 4 : N - J >= 2 ? 2 : 1;
+        lds_dma16_grp<G, NT>(rs, voff + J, (uint32_t)J * rstep, rstep - 1024u, lds_base + 1024u * J);
+        dma16_groups<NT, N, J + G>(rs, voff, rstep, lds_base);
+    }
 }
 
 // A raw buffer resource for loads at byte offsets (vector + scalar) from a
@@ -342,30 +413,6 @@ typedef uint32_t rkv_u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
-}
-
-// The same with a uniform base and a per-lane 32-bit offset (global address
-// = sbase + voff): the address arithmetic of a whole tile stays scalar.
-template <bool NT>
-__device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, uint32_t lds)
-{
-#if defined(__HIP_DEVICE_COMPILE__)
-    uint32_t saved;
-    if constexpr (NT)
-        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
-                     : "=&s"(saved)
-                     : "v"(voff), "s"(sbase), "s"(lds)
-                     : "memory");
-    else
-        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-                     : "=&s"(saved)
-                     : "v"(voff), "s"(sbase), "s"(lds)
-                     : "memory");
-#else
-    (void)sbase;
-    (void)voff;
-    (void)lds;
-#endif
 }
 
 // The same for 4 bytes per lane: the dword lands at lds + OFF + 4 * lane.
@@ -1783,21 +1830,22 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             auto issue = [&](auto policy) {
                 constexpr bool NT = decltype(policy)::value;
                 if (nkk == kTile) {
+                    // grouped buffer loads: load i at i * (64 / CPR) rows plus
+                    // the lane's swizzled chunk of its row
+                    uint32_t vo[NI];
 #pragma unroll
-                    for (int i = 0; i < NI; ++i)
-                        lds_dma16_s<NT>(kt + (int64_t)i * (64 / CPR) * sg.k_pos,
-                                        krow + (kchunk ^ (16u * (uint32_t)kswz<Sh::RBK>(i * (64 / CPR)))),
-                                        base + 1024u * i);
+                    for (int i = 0; i < NI; ++i) vo[i] = krow + (kchunk ^ (16u * (uint32_t)kswz<Sh::RBK>(i * (64 / CPR))));
+                    dma16_groups<NT, NI>(buffer_rsrc(kt), vo, (uint32_t)(64 / CPR) * (uint32_t)kps, base);
                     return;
                 }
-#pragma unroll
-                for (int i = 0; i < NI; ++i) {
+                static_for<0, NI>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
                     const int slot = i * 64 + lane;
                     const int j = slot / CPR, cs = slot % CPR;
                     const int c = cs ^ kswz<Sh::RBK>(j);
                     const int jc = j < nkk ? j : nkk - 1;
-                    lds_dma16<NT>(kt + (uint32_t)(jc * kps + 16 * c), base + 1024u * i);
-                }
+                    lds_dma16<NT, 1024u * i>(kt + (uint32_t)(jc * kps + 16 * c), base);
+                });
             };
             if (p.stream_once)
                 issue(std::integral_constant<bool, true>{});

@@ -119,26 +119,31 @@ rkv_split_rgs_kernel(const float *__restrict__ q, float *__restrict__ part_acc, 
         auto issue = [&](auto policy) {
             constexpr bool NT = decltype(policy)::value;
             if (nkk == kTile) {
-                const uint32_t voff = (uint32_t)lg * (uint32_t)vps + 16u * (uint32_t)lc;
+                // one group of four buffer loads each for K and V, starting
+                // at row 16 rgl (load j at row 4 (4 rgl + j) and LDS byte
+                // 1024 (4 rgl + j)); the K chunk swizzle of rows 4i .. 4i+3 is
+                // kswz(4i + lg) = (4i mod 16) | lg = 4 j | lg
+                uint32_t ko[4], vo[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int i = 4 * rgl + j;  // (rows 4i .. 4i+3: kswz(4i + lg) = (4i mod 16) | lg)
-                    const uint32_t koff = (uint32_t)lg * (uint32_t)kps +
-                                          16u * (uint32_t)(lc ^ ((4 * i) & 15) ^ lg);
-                    lds_dma16_s<NT>(kt + (int64_t)(4 * i) * sg.k_pos, koff, kb + 1024u * i);
-                    lds_dma16_s<NT>(vt + (int64_t)(4 * i) * sg.v_pos, voff, vb + 1024u * i);
+                    ko[j] = (uint32_t)lg * (uint32_t)kps + 16u * (uint32_t)(lc ^ (4 * j) ^ lg);
+                    vo[j] = (uint32_t)lg * (uint32_t)vps + 16u * (uint32_t)lc;
                 }
+                lds_dma16_grp<4, NT>(buffer_rsrc(kt), ko, 16u * (uint32_t)rgl * (uint32_t)kps, 4u * (uint32_t)kps - 1024u,
+                                     kb + 4096u * (uint32_t)rgl);
+                lds_dma16_grp<4, NT>(buffer_rsrc(vt), vo, 16u * (uint32_t)rgl * (uint32_t)vps, 4u * (uint32_t)vps - 1024u,
+                                     vb + 4096u * (uint32_t)rgl);
                 return;
             }
             // the segment's last, short tile: rows past nkk repeat row nkk - 1
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            static_for<0, 4>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
                 const int i = 4 * rgl + j;
                 const int row = 4 * i + lg;
                 const int rc = row < nkk ? row : nkk - 1;
-                lds_dma16<NT>(kt + (uint32_t)(rc * kps + 16 * (lc ^ kswz<RB>(row))), kb + 1024u * i);
-                lds_dma16<NT>(vt + (uint32_t)(rc * vps + 16 * lc), vb + 1024u * i);
-            }
+                lds_dma16<NT, 1024u * j>(kt + (uint32_t)(rc * kps + 16 * (lc ^ kswz<RB>(row))), kb + 4096u * (uint32_t)rgl);
+                lds_dma16<NT, 1024u * j>(vt + (uint32_t)(rc * vps + 16 * lc), vb + 4096u * (uint32_t)rgl);
+            });
         };
         if (p.stream_once)
             issue(std::integral_constant<bool, true>{});
