@@ -67,12 +67,12 @@ def kernel_source_hash() -> str:
 #     verify_counters: SQ figures of the workload's attention kernel (VALU and MFMA busy fractions,
 #     instructions per wave; profiles/rkv_split_kernels_sq_counters.md).
 MEASURED = {
-    "c2_split_traffic": {"src": "6f6737aa47f44a25", "fetch_bytes": 269025156, "write_bytes": 5570584, "bytes": 274595739},
-    "c3_counters": {"valu_busy": 0.5149, "mfma_busy": 0.1038, "valu_per_wave": 25407, "mfma_per_wave": 1280, "salu_per_wave": 10267, "lds_per_wave": 1960, "wait_frac": 0.336, "issue_frac": 0.444, "lds_conflict_per_lds_active": 1.836, "src": "6f6737aa47f44a25"},
-    "c5_counters": {"valu_busy": 0.3858, "mfma_busy": 0.1523, "valu_per_wave": 6485, "mfma_per_wave": 640, "salu_per_wave": 1587, "lds_per_wave": 982, "wait_frac": 0.393, "issue_frac": 0.406, "lds_conflict_per_lds_active": 0.557, "src": "6f6737aa47f44a25"},
-    "c4_window_counters": {"valu_busy": 0.4292, "mfma_busy": 0.0902, "valu_per_wave": 6090, "mfma_per_wave": 320, "salu_per_wave": 2454, "lds_per_wave": 417, "wait_frac": 0.303, "issue_frac": 0.449, "lds_conflict_per_lds_active": 1.621, "src": "6f6737aa47f44a25"},
-    "tbq3_window_counters": {"valu_busy": 0.3297, "mfma_busy": 0.0683, "valu_per_wave": 6183, "mfma_per_wave": 320, "salu_per_wave": 2309, "lds_per_wave": 609, "wait_frac": 0.338, "issue_frac": 0.457, "lds_conflict_per_lds_active": 1.726, "src": "6f6737aa47f44a25"},
-    "verify_counters": {"valu_busy": 0.3134, "mfma_busy": 0.1589, "valu_per_wave": 6060, "mfma_per_wave": 768, "salu_per_wave": 2785, "lds_per_wave": 582, "wait_frac": 0.463, "issue_frac": 0.366, "lds_conflict_per_lds_active": 0.703, "src": "6f6737aa47f44a25"},
+    "c2_split_traffic": {"src": "ed342c807606b0ec", "fetch_bytes": 268994869, "write_bytes": 5570662, "bytes": 274565531},
+    "c3_counters": {"valu_busy": 0.4591, "mfma_busy": 0.1123, "valu_per_wave": 20924, "mfma_per_wave": 1280, "salu_per_wave": 3470, "lds_per_wave": 1708, "wait_frac": 0.325, "issue_frac": 0.367, "lds_conflict_per_lds_active": 1.819, "src": "ed342c807606b0ec"},
+    "c5_counters": {"valu_busy": 0.3836, "mfma_busy": 0.1579, "valu_per_wave": 6217, "mfma_per_wave": 640, "salu_per_wave": 1663, "lds_per_wave": 982, "wait_frac": 0.353, "issue_frac": 0.427, "lds_conflict_per_lds_active": 0.556, "src": "ed342c807606b0ec"},
+    "c4_window_counters": {"valu_busy": 0.3924, "mfma_busy": 0.096, "valu_per_wave": 5229, "mfma_per_wave": 320, "salu_per_wave": 1172, "lds_per_wave": 358, "wait_frac": 0.288, "issue_frac": 0.413, "lds_conflict_per_lds_active": 1.681, "src": "ed342c807606b0ec"},
+    "tbq3_window_counters": {"valu_busy": 0.3296, "mfma_busy": 0.0779, "valu_per_wave": 5416, "mfma_per_wave": 320, "salu_per_wave": 1109, "lds_per_wave": 550, "wait_frac": 0.306, "issue_frac": 0.429, "lds_conflict_per_lds_active": 1.778, "src": "ed342c807606b0ec"},
+    "verify_counters": {"valu_busy": 0.3139, "mfma_busy": 0.1632, "valu_per_wave": 5908, "mfma_per_wave": 768, "salu_per_wave": 2330, "lds_per_wave": 582, "wait_frac": 0.456, "issue_frac": 0.36, "lds_conflict_per_lds_active": 0.701, "src": "ed342c807606b0ec"},
 }
 
 
