@@ -302,7 +302,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 }
 
 // One direct global -> LDS load: the 16 bytes at g (per lane) land at LDS
-// address lds + 16 * lane.  Written as asm so that the compiler neither
+// address lds + OFF + 16 * lane (the constant OFF is added to M0 inside the
+// asm, so that no per-load LDS address is held in a scalar register across a
+// tile loop).  Written as asm so that the compiler neither
 // inserts its own (conservative or missing) waits for it nor reorders memory
 // accesses across it; callers wait with waitcnt_vm() before reading the data
 // and wait for their LDS reads (lgkmcnt) before overwriting a buffer.  M0 is
