@@ -212,6 +212,24 @@ def main():
     torch.cuda.synchronize()
     call_s = sum(a.elapsed_time(b) for a, b in ev_step) * 1e-3 / (reps * L)
     call_gbs = kv_bytes_layer / call_s / 1e9
+
+    # The unsplit run (one segment [0, n), i.e. wc = n_kv), timed the same way:
+    # the split overhead is the two-segment call's time minus this one's.
+    segs1 = [[P.view_of_cache(kc, vc, 0, n)] for kc, vc, _ in layers]
+    ws1 = P.workspace(P.rkv_attend_split_workspace_bytes(desc, segs1[0]))
+
+    def step1():
+        for li in range(L):
+            P.rkv_attend_split(desc, layers[li][2], segs1[li], outs[li][0], outs[li][1], ws1, stream)
+
+    step1()
+    for a, b in ev_step:
+        a.record(stream)
+        step1()
+        b.record(stream)
+    torch.cuda.synchronize()
+    unsplit_s = sum(a.elapsed_time(b) for a, b in ev_step) * 1e-3 / (reps * L)
+    del ws1
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
     times = []
     for _ in range(reps):
@@ -293,6 +311,8 @@ def main():
             "us_per_layer": round(dt / L * 1e6, 3),
             "us_per_layer_call_p10_p50_p90": [round(pct(times, p) * 1e6, 2) for p in (10, 50, 90)],
             "us_per_layer_three_calls": three_us and round(three_us, 3),
+            "us_per_layer_unsplit": round(unsplit_s * 1e6, 3),
+            "split_overhead_us": round((call_s - unsplit_s) * 1e6, 3),
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "read_ceiling": ceiling,
             "frac_of_read_ceiling": ceiling and round(gbs / ceiling["per_layer_kv_GBs"], 4),
