@@ -211,3 +211,21 @@ def test_ring_consecutive_steps():
                     f"step {step} layer {li}"
     finally:
         ring.close()
+
+
+def test_stream_tail_tiny_f32():
+    """The tiny f32 configuration's streamed variant: 8 query heads / 2 KV
+    heads, head_dim 128, 4096 keys = window 3072 + a 1024-key tail in pinned
+    host memory, 256-key tiles through 3 slots, 2 layers: bit for bit the
+    resident-tail step, and the oracle over the whole unsplit cache."""
+    L, n, wc, Hq, Hkv, D, tile, B = 2, 4096, 3072, 8, 2, 128, 256, 3
+    note(f"ring tiny f32: {L} layers, n={n}, wc={wc}, tile={tile}, B={B}")
+    layers = make_layers(L, n, [wc] * L, Hq, Hkv, D, synth.F32, synth.F32, 9100)
+    desc = P.Desc(1, Hq, Hkv, D, 1.0 / math.sqrt(D))
+    outs = run_streamed(layers, desc, B, tile, n)
+    res = run_streamed(layers, desc, B, tile, n, inplace=True)
+    for li, L_ in enumerate(layers):
+        assert torch.equal(outs[li][0], res[li][0]) and torch.equal(outs[li][1], res[li][1]), f"layer {li}"
+        o_ref, l_ref = oracle.attend(L_["q"].cpu().numpy(), [oracle.view_of(L_["kc"].to("cpu"), L_["vc"].to("cpu"))],
+                                     Hkv, 1.0 / math.sqrt(D))
+        compare(outs[li][0], outs[li][1], o_ref, l_ref, what=f"ring tiny f32 layer {li} vs oracle")
