@@ -1892,22 +1892,33 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             }
         }
     };
-    auto dma_vb = [&](int64_t t, int nkk, const uint32_t *dst) {
+    // V rows of a whole tile can go out in two parts: the loads that touch rows
+    // 0..31 only (part 1: loads [0, LSV / 2) of the slot plan, [0, 32 / R) of
+    // the whole-row copy), once the first half of P.V has read those rows, and
+    // the rest (part 2) after P.V; part 0 is all of them.  vfull(t, nkk): the
+    // tile takes the whole-tile copy (a tile that does not goes out whole).
+    constexpr int VH1 = V_ROWS ? 32 / VRow::R : LSV1 / 2;
+    auto vfull = [&](int64_t t, int nkk) { return vfull_ok && nkk == kTile && t + kTile < sg.n_keys; };
+    uint32_t vo_part = 0;  // the slot plan's lane offset between the two parts
+    auto dma_vb = [&](int64_t t, int nkk, const uint32_t *dst, auto partc) {
         if constexpr (BDMA) {
+            constexpr int PART = decltype(partc)::value;
             int vps2 = (int)sg.v_pos;
             asm volatile("" : "+s"(vps2));
             waitcnt_lgkm0();  // this wave's earlier LDS reads of the V buffer are done
             const uint32_t base = lds_addr(dst);
-            if (vfull_ok && nkk == kTile && t + kTile < sg.n_keys) {
+            if (vfull(t, nkk)) {
                 const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(vg + t * sg.v_pos);
                 if constexpr (V_ROWS) {
-                    dma_rows_whole<RBDV, LSVR, 0, VRow::NL>(
-                        rs, voff0, vps2, (uint32_t)VRow::R * (uint32_t)(vps2 - 4 * LSVR), base);
+                    constexpr int I0 = PART == 2 ? VH1 : 0, I1 = PART == 1 ? VH1 : VRow::NL;
+                    dma_rows_whole<RBDV, LSVR, I0, I1>(rs, voff0, vps2, (uint32_t)VRow::R * (uint32_t)(vps2 - 4 * LSVR),
+                                                       base);
                 } else {
-                    uint32_t vo = voff0;
-                    dma_rows4_grp<LSV1, 0, LSV1>(rs, vo, vwrap, vps2, base);
+                    constexpr int I0 = PART == 2 ? VH1 : 0, I1 = PART == 1 ? VH1 : LSV1;
+                    if constexpr (PART != 2) vo_part = voff0;
+                    dma_rows4_grp<LSV1, I0, I1>(rs, vo_part, vwrap, vps2, base);
                 }
-            } else {
+            } else if constexpr (PART != 1) {
                 dma_rows4<Sh::RBV / 4, LSV>(vg + t * sg.v_pos, vps2, nkk, base, lane);
             }
         }
@@ -1919,7 +1930,9 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
 
     // P.V of this wave's staged block-type V tile on the matrix cores
     // (MFMA_PVB), for tiles whose block scales keep d * code inside binary16.
-    auto pv_blk = [&]() {
+    // mid() runs once the first 32-key half's products are issued (its V rows
+    // 0..31 are then no longer read by this tile).
+    auto pv_blk = [&](auto &&mid) {
         const int qi = lane & 15, gq = lane >> 4;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -2023,6 +2036,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 oc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bh, oc[c], 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
+            if (kb == 0) mid();
         }
     };
 
@@ -2054,7 +2068,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     if constexpr (BDMA) {
         if (t0 < kend) {
             dma_kb(t0, nk_at(t0));
-            dma_vb(t0, nk_at(t0), sV);
+            dma_vb(t0, nk_at(t0), sV, std::integral_constant<int, 0>{});
         }
     } else if constexpr (KDMA) {
         if (t0 < kend) {
@@ -2097,6 +2111,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
     for (; t0 < kend; t0 += tstep) {
         const int nk = nk_at(t0);
         const int64_t tn = t0 + tstep;
+        bool v_mid = false;  // the first part of the next tile's V rows went out during P.V
         if constexpr (BDMA) {
             // K went out before the previous tile's P.V and V after it (with
             // VDB right after K): once at most V's loads are outstanding this
@@ -2139,7 +2154,7 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
                 __builtin_amdgcn_wave_barrier();
                 if (tn < kend) {
                     dma_kb(tn, nk_at(tn));
-                    dma_vb(tn, nk_at(tn), sVn);
+                    dma_vb(tn, nk_at(tn), sVn, std::integral_constant<int, 0>{});
                     waitcnt_vm<LSK + LSV>();
                 } else {
                     waitcnt_vm<0>();
@@ -2342,12 +2357,22 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             // A tile with a block scale large enough for d * code to overflow
             // binary16 (rare) is multiplied out in binary32 on the VALU.
             // (TBQ3: levels below 2.2, P times n / sqrt(128) below 5800)
+            // (one buffer per wave: the next tile's V rows 0..31 go out once
+            // the first half of P.V has read them)
+            auto mid = [&]() {
+                if constexpr (BDMA && !VDB) {
+                    if (tn < kend) {
+                        dma_vb(tn, nk_at(tn), sV, std::integral_constant<int, 1>{});
+                        v_mid = true;
+                    }
+                }
+            };
             if constexpr (VT == kT3) {
-                pv_blk();
+                pv_blk(mid);
             } else {
                 const uint32_t vmx = v_row_scale_max<VT, D / 32>(sV + lane * LSV);
                 if (__builtin_amdgcn_ballot_w64(vmx >= v_scale_limit<VT>()) == 0)
-                    pv_blk();
+                    pv_blk(mid);
                 else
                     pv_valu_tile<VT, LSV>(
                         sV, [&](int r, int k) { return sPw[r * kTile + (k & 3) * 16 + (k >> 2)]; }, RT, lane, oc);
@@ -2427,7 +2452,12 @@ rkv_split_kernel(const float *__restrict__ q, float *__restrict__ part_acc, floa
             sV = sVn;
             sVn = sx;
         } else if constexpr (BDMA) {
-            if (tn < kend) dma_vb(tn, nk_at(tn), sV);
+            if (tn < kend) {
+                if (v_mid)
+                    dma_vb(tn, nk_at(tn), sV, std::integral_constant<int, 2>{});
+                else
+                    dma_vb(tn, nk_at(tn), sV, std::integral_constant<int, 0>{});
+            }
         }
         if constexpr (KDMA && V_REG) {
             v_after_dma = 0;
