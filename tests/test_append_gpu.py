@@ -276,3 +276,14 @@ def test_append_ring_decode(L, B, tile):
     for li in range(L):
         wins[li].check(f"window {li}")
         tails[li].check(f"tail {li}")
+
+
+def test_binding_stream_is_torch_current_stream():
+    """The binding's default stream (no stream argument) is torch's current
+    stream, also inside a stream context and after leaving it."""
+    s = torch.cuda.Stream()
+    assert P._stream(None) == torch.cuda.current_stream().cuda_stream
+    with torch.cuda.stream(s):
+        assert P._stream(None) == s.cuda_stream
+    assert P._stream(None) == torch.cuda.current_stream().cuda_stream
+    assert P._stream(s) == s.cuda_stream and P._stream(s.cuda_stream) == s.cuda_stream
