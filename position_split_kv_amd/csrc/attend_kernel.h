@@ -68,7 +68,13 @@ struct Shape {
     static constexpr bool KDMA = (KT == kF32 || KT == kF16) && RBK >= 128 && RBK <= 512 && is_pow2(RBK / 16);
     static constexpr int LSK = KDMA ? RBK / 4 : lds_row_dwords(RBK);
     static constexpr bool V_REG = (VT == kF16 && D <= 128) || (VT == kF32 && D <= 64);
-    static constexpr int LSV = V_REG ? 0 : lds_row_dwords(RBV);
+    // q4_0 V rows at 128 dims: 22 dwords instead of 19, so that the P.V
+    // operand reads (a block scale and three code words per lane, 16 lanes
+    // on each of two rows per half-wave) meet no bank twice.  (With q4_0 K
+    // the wider rows would cost workgroups per compute unit; kept at 19.)
+    static constexpr int LSV = V_REG                                      ? 0
+                               : (VT == kQ4 && D == 128 && KT != kQ4) ? 22
+                                                                          : lds_row_dwords(RBV);
     static constexpr int STAGE_DW = kTile * (LSK + LSV) + 8;  // per wave: K (+ V) rows plus read slack
     // With K rows by DMA and V rows in registers, a wave's K tile is not
     // needed between its scores and the next tile's DMA (issued after P.V),
