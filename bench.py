@@ -67,12 +67,12 @@ def kernel_source_hash() -> str:
 #     verify_counters: SQ figures of the workload's attention kernel (VALU and MFMA busy fractions,
 #     instructions per wave; profiles/rkv_split_kernels_sq_counters.md).
 MEASURED = {
-    "c2_split_traffic": {"src": "c142524526b6762e", "fetch_bytes": 268994095, "write_bytes": 5570662, "bytes": 274564756},
-    "c3_counters": {"valu_busy": 0.4678, "mfma_busy": 0.1144, "valu_per_wave": 20938, "mfma_per_wave": 1280, "salu_per_wave": 3895, "lds_per_wave": 1708, "wait_frac": 0.346, "issue_frac": 0.379, "lds_conflict_per_lds_active": 1.82, "src": "c142524526b6762e"},
-    "c5_counters": {"valu_busy": 0.3825, "mfma_busy": 0.1575, "valu_per_wave": 6217, "mfma_per_wave": 640, "salu_per_wave": 1663, "lds_per_wave": 982, "wait_frac": 0.35, "issue_frac": 0.428, "lds_conflict_per_lds_active": 0.556, "src": "c142524526b6762e"},
-    "c4_window_counters": {"valu_busy": 0.4004, "mfma_busy": 0.098, "valu_per_wave": 5229, "mfma_per_wave": 320, "salu_per_wave": 1172, "lds_per_wave": 358, "wait_frac": 0.291, "issue_frac": 0.422, "lds_conflict_per_lds_active": 1.68, "src": "c142524526b6762e"},
-    "tbq3_window_counters": {"valu_busy": 0.2848, "mfma_busy": 0.0673, "valu_per_wave": 5416, "mfma_per_wave": 320, "salu_per_wave": 1109, "lds_per_wave": 550, "wait_frac": 0.305, "issue_frac": 0.433, "lds_conflict_per_lds_active": 1.778, "src": "c142524526b6762e"},
-    "verify_counters": {"valu_busy": 0.3148, "mfma_busy": 0.1637, "valu_per_wave": 5908, "mfma_per_wave": 768, "salu_per_wave": 2330, "lds_per_wave": 582, "wait_frac": 0.455, "issue_frac": 0.362, "lds_conflict_per_lds_active": 0.703, "src": "c142524526b6762e"},
+    "c2_split_traffic": {"src": "9cd0940b1d0b2a29", "fetch_bytes": 268993041, "write_bytes": 5570659, "bytes": 274563700},
+    "c3_counters": {"valu_busy": 0.4675, "mfma_busy": 0.1143, "valu_per_wave": 20938, "mfma_per_wave": 1280, "salu_per_wave": 3895, "lds_per_wave": 1708, "wait_frac": 0.348, "issue_frac": 0.379, "lds_conflict_per_lds_active": 1.82, "src": "9cd0940b1d0b2a29"},
+    "c5_counters": {"valu_busy": 0.379, "mfma_busy": 0.1565, "valu_per_wave": 6202, "mfma_per_wave": 640, "salu_per_wave": 1592, "lds_per_wave": 982, "wait_frac": 0.36, "issue_frac": 0.423, "lds_conflict_per_lds_active": 0.555, "src": "9cd0940b1d0b2a29"},
+    "c4_window_counters": {"valu_busy": 0.3988, "mfma_busy": 0.0966, "valu_per_wave": 5283, "mfma_per_wave": 320, "salu_per_wave": 1232, "lds_per_wave": 358, "wait_frac": 0.305, "issue_frac": 0.43, "lds_conflict_per_lds_active": 1.459, "src": "9cd0940b1d0b2a29"},
+    "tbq3_window_counters": {"valu_busy": 0.329, "mfma_busy": 0.0778, "valu_per_wave": 5416, "mfma_per_wave": 320, "salu_per_wave": 1109, "lds_per_wave": 550, "wait_frac": 0.308, "issue_frac": 0.434, "lds_conflict_per_lds_active": 1.778, "src": "9cd0940b1d0b2a29"},
+    "verify_counters": {"valu_busy": 0.314, "mfma_busy": 0.1633, "valu_per_wave": 5908, "mfma_per_wave": 768, "salu_per_wave": 2330, "lds_per_wave": 582, "wait_frac": 0.454, "issue_frac": 0.361, "lds_conflict_per_lds_active": 0.704, "src": "9cd0940b1d0b2a29"},
 }
 
 
