@@ -203,10 +203,15 @@ rkv_reduce_kernel(const float *__restrict__ part_acc, const float2 *__restrict__
     auto load = [&](int base, float2 (&ml)[8], float4 (&x)[8]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            // (indices past the end repeat a valid split and are not added)
-            const int sp = base + 32 * u < n_splits ? base + 32 * u : base;
-            ml[u] = ml_row[sp];
-            x[u] = *(const float4 *)(part_acc + ((int64_t)sp * n_rows + row) * D + d0);
+            // (indices past the end are neither loaded nor added)
+            const int sp = base + 32 * u;
+            if (sp < n_splits) {
+                ml[u] = ml_row[sp];
+                x[u] = *(const float4 *)(part_acc + ((int64_t)sp * n_rows + row) * D + d0);
+            } else {
+                ml[u] = make_float2(-INFINITY, 0.f);
+                x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
     };
     float2 ml[8];
