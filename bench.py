@@ -67,12 +67,12 @@ def kernel_source_hash() -> str:
 #     verify_counters: SQ figures of the workload's attention kernel (VALU and MFMA busy fractions,
 #     instructions per wave; profiles/rkv_split_kernels_sq_counters.md).
 MEASURED = {
-    "c2_split_traffic": {"src": "9cd0940b1d0b2a29", "fetch_bytes": 268993041, "write_bytes": 5570659, "bytes": 274563700},
-    "c3_counters": {"valu_busy": 0.4675, "mfma_busy": 0.1143, "valu_per_wave": 20938, "mfma_per_wave": 1280, "salu_per_wave": 3895, "lds_per_wave": 1708, "wait_frac": 0.348, "issue_frac": 0.379, "lds_conflict_per_lds_active": 1.82, "src": "9cd0940b1d0b2a29"},
-    "c5_counters": {"valu_busy": 0.379, "mfma_busy": 0.1565, "valu_per_wave": 6202, "mfma_per_wave": 640, "salu_per_wave": 1592, "lds_per_wave": 982, "wait_frac": 0.36, "issue_frac": 0.423, "lds_conflict_per_lds_active": 0.555, "src": "9cd0940b1d0b2a29"},
-    "c4_window_counters": {"valu_busy": 0.3988, "mfma_busy": 0.0966, "valu_per_wave": 5283, "mfma_per_wave": 320, "salu_per_wave": 1232, "lds_per_wave": 358, "wait_frac": 0.305, "issue_frac": 0.43, "lds_conflict_per_lds_active": 1.459, "src": "9cd0940b1d0b2a29"},
-    "tbq3_window_counters": {"valu_busy": 0.329, "mfma_busy": 0.0778, "valu_per_wave": 5416, "mfma_per_wave": 320, "salu_per_wave": 1109, "lds_per_wave": 550, "wait_frac": 0.308, "issue_frac": 0.434, "lds_conflict_per_lds_active": 1.778, "src": "9cd0940b1d0b2a29"},
-    "verify_counters": {"valu_busy": 0.314, "mfma_busy": 0.1633, "valu_per_wave": 5908, "mfma_per_wave": 768, "salu_per_wave": 2330, "lds_per_wave": 582, "wait_frac": 0.454, "issue_frac": 0.361, "lds_conflict_per_lds_active": 0.704, "src": "9cd0940b1d0b2a29"},
+    "c2_split_traffic": {"src": "8c18b6b1c1b901a0", "fetch_bytes": 268994319, "write_bytes": 5570675, "bytes": 274564994},
+    "c3_counters": {"valu_busy": 0.4682, "mfma_busy": 0.1145, "valu_per_wave": 20938, "mfma_per_wave": 1280, "salu_per_wave": 3895, "lds_per_wave": 1708, "wait_frac": 0.347, "issue_frac": 0.378, "lds_conflict_per_lds_active": 1.82, "src": "8c18b6b1c1b901a0"},
+    "c5_counters": {"valu_busy": 0.3753, "mfma_busy": 0.1549, "valu_per_wave": 6202, "mfma_per_wave": 640, "salu_per_wave": 1592, "lds_per_wave": 982, "wait_frac": 0.361, "issue_frac": 0.421, "lds_conflict_per_lds_active": 0.555, "src": "8c18b6b1c1b901a0"},
+    "c4_window_counters": {"valu_busy": 0.3964, "mfma_busy": 0.096, "valu_per_wave": 5283, "mfma_per_wave": 320, "salu_per_wave": 1232, "lds_per_wave": 358, "wait_frac": 0.301, "issue_frac": 0.425, "lds_conflict_per_lds_active": 1.461, "src": "8c18b6b1c1b901a0"},
+    "tbq3_window_counters": {"valu_busy": 0.3287, "mfma_busy": 0.0777, "valu_per_wave": 5416, "mfma_per_wave": 320, "salu_per_wave": 1109, "lds_per_wave": 550, "wait_frac": 0.305, "issue_frac": 0.431, "lds_conflict_per_lds_active": 1.778, "src": "8c18b6b1c1b901a0"},
+    "verify_counters": {"valu_busy": 0.3131, "mfma_busy": 0.1628, "valu_per_wave": 5908, "mfma_per_wave": 768, "salu_per_wave": 2330, "lds_per_wave": 582, "wait_frac": 0.455, "issue_frac": 0.359, "lds_conflict_per_lds_active": 0.703, "src": "8c18b6b1c1b901a0"},
 }
 
 
