@@ -61,6 +61,9 @@ CASES = [
     ("q8q8_d512_cap", 1, 16, 2, 512, synth.Q8_0, synth.Q8_0, 777, 500, None, 30.0, None),
     ("q8q8_d512_cap_stress", 1, 16, 2, 512, synth.Q8_0, synth.Q8_0, 777, 500, 1.0, 30.0, None),
     ("q8q4_gqa5", 1, 40, 8, 128, synth.Q8_0, synth.Q4_0, 1100, 512, None, 0.0, None),
+    # binary32 / binary16 K beside q4_0 V rows at 128 dims (their 22-dword LDS stride), ragged tails
+    ("f32q4_gqa5_d128", 1, 40, 8, 128, synth.F32, synth.Q4_0, 701, 300, None, 0.0, None),
+    ("f16q4_gqa4_d128", 2, 16, 4, 128, synth.F16, synth.Q4_0, 517, 203, None, 0.0, None),
     ("q8q4_d512_wall", 1, 8, 1, 512, synth.Q8_0, synth.Q4_0, 300, 129, None, 0.0, None),
     ("q4q8_d64", 2, 6, 3, 64, synth.Q4_0, synth.Q8_0, 333, 65, None, 0.0, None),
     ("f16q4_d256_mha", 2, 4, 4, 256, synth.F16, synth.Q4_0, 257, 63, None, 0.0, None),
